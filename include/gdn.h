@@ -1,0 +1,145 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet (GDN) token mixer.
+ *
+ * The mixer (local-inference walkthrough, bjdmk.com.cn, section 2.1; hybrid-
+ * attention explainer, jianying88.com, section 3) keeps one fixed-size state
+ * matrix S (d_k x d_v, fp32) per (sequence, V head) and, for every token t:
+ *
+ *   1. short causal depthwise conv of width 4 over the raw q, k, v channels,
+ *      then SiLU; q^ and k^ are L2-normalised per (token, QK head), eps = 1e-6
+ *      inside the square root; v^ is not normalised;
+ *   2. beta_t = sigmoid(b_t) (write strength), alpha_t = exp(-gate_scale *
+ *      softplus(a_t)) (forget gate), one scalar each per (token, V head);
+ *   3. S_t = alpha_t (I - beta_t k^_t k^_t^T) S_{t-1} + beta_t k^_t v^_t^T;
+ *   4. o_t = q_scale * S_t^T q^_t.
+ *
+ * V head h reads QK head h / (Hv / Hqk): contiguous groups of Hv / Hqk V heads
+ * share one QK head (16 QK heads for 48 V heads in the explainer's config).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers, row-major, innermost last.
+ *    bf16 tensors are passed as uint16_t bit patterns.
+ *  - Conv channels are ordered q | k | v: C_tot = 2*Hqk*d_k + Hv*d_v.
+ *    conv_w is [C_tot][4] bf16; tap 3 multiplies the current token, taps
+ *    0..2 the three previous tokens.  Conv states are [.][3][C_tot] bf16 raw
+ *    (pre-conv) rows, oldest first.
+ *  - The library allocates nothing, keeps no pointer after it returns and
+ *    holds no global state.  All work is enqueued on `stream` (a hipStream_t;
+ *    NULL = the default stream); the call returns before the GPU finishes,
+ *    and every buffer must stay valid until the stream has passed the work.
+ *  - Arguments are validated before any HIP call: on an error status nothing
+ *    is launched and no output is touched.  Device faults are asynchronous
+ *    and surface at the caller's next stream synchronisation.
+ *  - Supported shapes: d_k = d_v = 128, Hv a multiple of Hqk, every pointer
+ *    16-byte aligned except a, b, cu_seqlens (4-byte).
+ *  - Numerics: bf16 I/O, fp32 state, fp32 accumulation; the chunked prefill
+ *    feeds its dense products to the matrix cores as fp16 operands (see the
+ *    repository's design notes for the error budget).
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARGUMENT = 1, /* NULL required pointer, size <= 0, misaligned */
+    GDN_ERR_UNSUPPORTED = 2,      /* d_k or d_v != 128, Hv % Hqk != 0 */
+    GDN_ERR_WORKSPACE_TOO_SMALL = 3,
+    GDN_ERR_HIP = 4               /* a HIP launch or query failed */
+};
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *gdn_status_string(int status);
+
+/* Bytes of device workspace gdn_prefill needs for these sizes. */
+size_t gdn_prefill_workspace_size(int B, int T, int Hqk, int Hv, int dk, int dv);
+
+/*
+ * Chunked prefill of B sequences of equal length T (the WY / chunk-parallel
+ * evaluation of the update that the walkthrough's section 2.1 names; exact up
+ * to rounding order).
+ *
+ *   q, k           [B][T][Hqk][dk] bf16, raw (pre-conv)
+ *   v              [B][T][Hv][dv]  bf16, raw (pre-conv)
+ *   a, b           [B][T][Hv] fp32 raw gate pre-activations (a -> alpha, b -> beta)
+ *   conv_w         [C_tot][4] bf16
+ *   conv_state_in  [B][3][C_tot] bf16 history rows, or NULL (zero history)
+ *   conv_state_out [B][3][C_tot] bf16, or NULL (not written): the last three
+ *                  raw rows of each sequence (reaching into conv_state_in when
+ *                  T < 3); must not overlap conv_state_in
+ *   state_in       [B][Hv][dk][dv] fp32 initial state, or NULL (zeros)
+ *   state_out      [B][Hv][dk][dv] fp32 final state; may equal state_in
+ *                  (in place), any other overlap is undefined
+ *   o              [B][T][Hv][dv] bf16 output (round to nearest even)
+ *   workspace      device scratch of >= gdn_prefill_workspace_size(...) bytes,
+ *                  256-byte aligned; its contents on entry are irrelevant
+ * T = 0 copies state_in to state_out (zeros if state_in is NULL).
+ */
+int gdn_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                const float *a, const float *b, const uint16_t *conv_w,
+                const uint16_t *conv_state_in, uint16_t *conv_state_out,
+                const float *state_in, float *state_out, uint16_t *o,
+                int B, int T, int Hqk, int Hv, int dk, int dv,
+                float gate_scale, float q_scale,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace gdn_prefill_varlen needs (any lengths summing to
+ * T_tot over N sequences). */
+size_t gdn_prefill_varlen_workspace_size(int N, int T_tot, int Hqk, int Hv, int dk, int dv);
+
+/*
+ * Packed variable-length prefill with state carry-in (continuation of a
+ * prefix: chunked prefill and prefix caching in serving engines hand over the
+ * state and the conv rows).  Same as gdn_prefill, except:
+ *
+ *   q, k           [T_tot][Hqk][dk], v [T_tot][Hv][dv], a, b [T_tot][Hv],
+ *                  o [T_tot][Hv][dv]: tokens of all sequences packed
+ *   cu_seqlens     DEVICE int32 [N+1], cu_seqlens[0] = 0, non-decreasing,
+ *                  cu_seqlens[N] = T_tot; read on the device only (no host
+ *                  synchronisation).  Values outside that contract are
+ *                  undefined behaviour.
+ *   conv_state_*   [N][3][C_tot];  state_*  [N][Hv][dk][dv]
+ * Sequences never see each other's tokens: each starts from its own
+ * state_in / conv_state_in row (or zeros).  Empty sequences copy their state.
+ */
+int gdn_prefill_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                       const float *a, const float *b, const uint16_t *conv_w,
+                       const uint16_t *conv_state_in, uint16_t *conv_state_out,
+                       const float *state_in, float *state_out, uint16_t *o,
+                       const int32_t *cu_seqlens, int N, int T_tot,
+                       int Hqk, int Hv, int dk, int dv,
+                       float gate_scale, float q_scale,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step: one new token for each of B independent sequences (the
+ * pages' constant-cost decode: a token only reads and updates the fixed-size
+ * memory; hybrid-attention explainer, section 3).
+ *
+ *   q, k        [B][Hqk][dk] bf16 raw;  v [B][Hv][dv] bf16 raw
+ *   a, b        [B][Hv] fp32
+ *   conv_state  [B][3][C_tot] bf16, updated IN PLACE: rows shift up by one
+ *               and the new raw token becomes row 2
+ *   state_in    [B][Hv][dk][dv] fp32
+ *   state_out   [B][Hv][dk][dv] fp32; may equal state_in (in place)
+ *   o           [B][Hv][dv] bf16
+ * No workspace.  B = 0 is a no-op.
+ */
+int gdn_decode_step(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                    const float *a, const float *b, const uint16_t *conv_w,
+                    uint16_t *conv_state, const float *state_in, float *state_out,
+                    uint16_t *o, int B, int Hqk, int Hv, int dk, int dv,
+                    float gate_scale, float q_scale, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

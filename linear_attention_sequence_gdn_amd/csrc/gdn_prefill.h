@@ -1,0 +1,62 @@
+// gdn_prefill.h -- internal interface of the chunked prefill (not the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gdn_common.h"
+
+namespace gdn {
+
+struct PrefillArgs {
+    const uint16_t *q, *k, *v;
+    const float *a, *b;
+    const uint16_t *conv_w;
+    const uint16_t *conv_state_in;
+    uint16_t *conv_state_out;
+    const float *state_in;
+    float *state_out;
+    uint16_t *o;
+    const int32_t *cu_seqlens;  // NULL: N sequences of T_uniform tokens
+    int N, T_uniform, T_tot;
+    int Hqk, Hv;
+    float gate_scale, q_scale;
+    int max_chunks;
+};
+
+// Upper bound of the number of 64-token chunks.
+inline int max_chunks_uniform(int B, int T) { return B * ((T + kChunk - 1) / kChunk); }
+inline int max_chunks_varlen(int N, int T_tot)
+{
+    return (int)(((long)T_tot + (long)(kChunk - 1) * N) / kChunk);
+}
+
+// Per-chunk hand-over from the parallel prep pass to the sequential pass, in
+// bytes.  Everything the sequential pass reads is stored in the exact
+// register order of the matrix-core operands that consume it.
+constexpr size_t kFragBytes = 64 * 16;               // one 16x32 fp16 operand
+constexpr size_t kQFragBytes = 16 * kFragBytes;      // q^ of a chunk     [64 x 128]
+constexpr size_t kKFragBytes = 16 * kFragBytes;      // k^T of a chunk    [128 x 64]
+constexpr size_t kWFragBytes = 16 * kFragBytes;      // -W of a chunk     [64 x 128]
+constexpr size_t kUBytes = 64 * 128 * 2;             // U' of a chunk     [64 x 128]
+constexpr size_t kPFragBytes = 8 * kFragBytes;       // P of a chunk      [64 x 64]
+constexpr size_t kGateFloats = 3 * 64;               // Gamma, r, {Gamma_n}
+
+struct Workspace {
+    int4 *chunk_info;   // [max_chunks] {seq, t0, n, first}
+    int4 *seq_info;     // [N] {chunk0, nchunks, t0, L}
+    int *order;         // [N] sequences, longest first
+    uint8_t *qfrag;     // [max_chunks][Hqk]
+    uint8_t *kfrag;     // [max_chunks][Hqk]
+    uint8_t *wfrag;     // [max_chunks][Hv]
+    uint8_t *ufrag;     // [max_chunks][Hv]
+    uint8_t *pfrag;     // [max_chunks][Hv]
+    float *gates;       // [max_chunks][Hv][3][64]
+};
+
+size_t prefill_workspace_bytes(int max_chunks, int N, int Hqk, int Hv);
+Workspace carve_workspace(void *base, int max_chunks, int N, int Hqk, int Hv);
+hipError_t launch_prefill(const PrefillArgs &p, void *workspace, hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,619 @@
+// gdn_prefill.hip -- chunked prefill of the GDN mixer on gfx950.
+//
+// The state update of the local-inference walkthrough (section 2.1) is
+// evaluated in its chunk-parallel (WY) form, which the same section names as
+// the way the method becomes GPU-friendly.  Per chunk of n <= 64 tokens of one
+// (sequence, V head), with in-chunk log decays gam_i = sum_{j<=i} log alpha_j,
+// Gam = e^gam and D_ij = e^{gam_i - gam_j}:
+//
+//   A    = strict_lower( diag(beta) (K K^T) * D )          (n x n)
+//   T'   = (I + A)^-1 diag(beta)
+//   W    = T' diag(Gam) K,   U' = T' V                     (n x d)
+//   Vnew = U' - W S                                        (S: state entering)
+//   O    = diag(Gam) Q S + (Q K^T * D, lower incl. diag) Vnew
+//   S   <- Gam_n S + (diag(Gam_n / Gam) K)^T Vnew
+//
+// which equals the token-by-token recurrence up to rounding order.
+//
+// Three launches:
+//   setup  -- chunk and sequence tables from cu_seqlens (device-side, no host
+//             sync), longest sequences first;
+//   prep   -- fully parallel over (chunk, QK group): conv + SiLU, L2 norm,
+//             gates, K K^T and K Q^T on the matrix cores, the blocked
+//             unit-lower-triangular inverse, W and U' on the matrix cores;
+//             writes every operand the sequential pass needs in the register
+//             order of the matrix-core instruction that consumes it;
+//   chain  -- sequential over the chunks of a sequence, parallel over
+//             (sequence, V head, 16-column slice of the state): the columns
+//             of S evolve independently, so each wave carries a 128 x 16
+//             fp32 slice of S in registers through the whole sequence with no
+//             synchronisation at all.
+#include "gdn_prefill.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kPrepThreads = 256;
+constexpr int kQ_LD = 136;  // fp16 row stride of the token-major q^ / k^ tiles
+constexpr int kT_LD = 72;   // fp16 row stride of 64-token rows (k^T, v^T, T')
+constexpr int kA_LD = 65;   // fp32 row stride of A and its inverse
+
+__host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------------------
+// operand loaders
+// ---------------------------------------------------------------------------
+
+// 16x32 fp16 operand fragment from a row-major LDS matrix M[row][k]:
+// lane l takes row r0 + l%16 and contraction indices k0 + kappa(l/16, 0..7).
+// Serves A operands (M = A) and B operands (M[col][k] = B[k][col]).
+__device__ __forceinline__ half8 lds_frag(const _Float16 *M, int ld, int r0, int k0, int lane)
+{
+    const _Float16 *row = M + (r0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
+    const half4 lo = *reinterpret_cast<const half4 *>(row);
+    const half4 hi = *reinterpret_cast<const half4 *>(row + 16);
+    half8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+}
+
+__device__ __forceinline__ uint32_t ld_pair(const uint16_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
+
+// Causal width-4 conv + SiLU of channels (2*pp, 2*pp+1) of one 128-channel
+// plane, rows r0 .. r0+15 of the chunk.  x points at the chunk's first token
+// (row stride ld); rows < 0 come from the previous chunk of the same sequence
+// (first == false), from the carried conv rows `hist` (row stride C_tot), or
+// are zero.  Rows >= n are padding and produce zeros.
+__device__ __forceinline__ void conv_plane(const uint16_t *__restrict__ x, long ld, int n, bool first,
+                                           const uint16_t *hist, long C_tot,
+                                           const uint16_t *__restrict__ w, int pp, int r0,
+                                           float (&z0)[16], float (&z1)[16])
+{
+    const uint2 wa = *reinterpret_cast<const uint2 *>(w + (2 * pp) * 4);
+    const uint2 wb = *reinterpret_cast<const uint2 *>(w + (2 * pp + 1) * 4);
+    const float a0 = bf16_lo(wa.x), a1 = bf16_hi(wa.x), a2 = bf16_lo(wa.y), a3 = bf16_hi(wa.y);
+    const float b0 = bf16_lo(wb.x), b1 = bf16_hi(wb.x), b2 = bf16_lo(wb.y), b3 = bf16_hi(wb.y);
+    uint32_t win[19];
+#pragma unroll
+    for (int i = 0; i < 19; ++i) {
+        const int r = r0 - 3 + i;
+        uint32_t val = 0;
+        if (r >= 0) {
+            if (r < n) val = ld_pair(x + (long)r * ld + 2 * pp);
+        } else if (!first) {
+            val = ld_pair(x + (long)r * ld + 2 * pp);
+        } else if (hist) {
+            val = ld_pair(hist + (long)(3 + r) * C_tot + 2 * pp);
+        }
+        win[i] = val;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float ya = a0 * bf16_lo(win[i]) + a1 * bf16_lo(win[i + 1]) + a2 * bf16_lo(win[i + 2]) +
+                         a3 * bf16_lo(win[i + 3]);
+        const float yb = b0 * bf16_hi(win[i]) + b1 * bf16_hi(win[i + 1]) + b2 * bf16_hi(win[i + 2]) +
+                         b3 * bf16_hi(win[i + 3]);
+        const bool valid = r0 + i < n;
+        z0[i] = valid ? silu_f(ya) : 0.0f;
+        z1[i] = valid ? silu_f(yb) : 0.0f;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// setup: chunk / sequence tables
+// ---------------------------------------------------------------------------
+// Sequence bounds, clamped into [0, T_tot] so that a malformed cu_seqlens
+// cannot send any kernel outside the caller's buffers.
+__device__ __forceinline__ int seq_start(const PrefillArgs &p, int s)
+{
+    return p.cu_seqlens ? min(max(p.cu_seqlens[s], 0), p.T_tot) : s * p.T_uniform;
+}
+__device__ __forceinline__ int seq_len(const PrefillArgs &p, int s)
+{
+    if (!p.cu_seqlens) return p.T_uniform;
+    const int t0 = seq_start(p, s);
+    return min(max(p.cu_seqlens[s + 1] - t0, 0), p.T_tot - t0);
+}
+
+__global__ __launch_bounds__(1024) void setup_kernel(PrefillArgs p, Workspace ws)
+{
+    __shared__ int s_scan[1024];
+    const int t = threadIdx.x;
+    const int per = (p.N + 1023) / 1024;
+    const int s0 = min(p.N, t * per), s1 = min(p.N, s0 + per);
+    int local = 0;
+    for (int s = s0; s < s1; ++s) local += (seq_len(p, s) + kChunk - 1) / kChunk;
+    s_scan[t] = local;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int add = t >= off ? s_scan[t - off] : 0;
+        __syncthreads();
+        s_scan[t] += add;
+        __syncthreads();
+    }
+    int base = s_scan[t] - local;
+    const int total = s_scan[1023];
+    for (int s = s0; s < s1; ++s) {
+        const int L = seq_len(p, s), t0 = seq_start(p, s);
+        // chunks beyond the workspace bound (only with a malformed cu_seqlens) are dropped
+        const int nch = max(0, min((L + kChunk - 1) / kChunk, p.max_chunks - base));
+        ws.seq_info[s] = make_int4(base, nch, t0, min(L, nch * kChunk));
+        for (int j = 0; j < nch; ++j)
+            ws.chunk_info[base + j] = make_int4(s, t0 + j * kChunk, min(kChunk, L - j * kChunk), j == 0);
+        base += nch;
+    }
+    for (int c = min(total, p.max_chunks) + t; c < p.max_chunks; c += 1024) ws.chunk_info[c] = make_int4(0, 0, 0, 0);
+    // longest first (ties by index): rank of each sequence
+    for (int s = t; s < p.N; s += 1024) {
+        const int Ls = seq_len(p, s);
+        int rank = 0;
+        for (int j2 = 0; j2 < p.N; ++j2) {
+            const int Lj = seq_len(p, j2);
+            rank += (Lj > Ls) || (Lj == Ls && j2 < s);
+        }
+        ws.order[rank] = s;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// prep: everything that does not depend on the carried state
+// ---------------------------------------------------------------------------
+
+// X_{bi,bj} = -X_{bi,bi} * sum_{k=bj}^{bi-1} A_{bi,k} X_{k,bj}   (16x16 blocks)
+// executed by one wave; M is a 16 x 17 fp32 scratch owned by the wave.
+__device__ __forceinline__ void inv_block_product(const float *As, float *Xs, float *M, int bi, int bj,
+                                                  int lane)
+{
+    const int r = lane >> 2, c0 = 4 * (lane & 3);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int kblk = bj; kblk < bi; ++kblk) {
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const float a = As[(16 * bi + r) * kA_LD + 16 * kblk + m];
+            const float *xr = Xs + (16 * kblk + m) * kA_LD + 16 * bj + c0;
+            acc[0] += a * xr[0];
+            acc[1] += a * xr[1];
+            acc[2] += a * xr[2];
+            acc[3] += a * xr[3];
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) M[r * 17 + c0 + e] = acc[e];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float out[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const float xv = Xs[(16 * bi + r) * kA_LD + 16 * bi + m];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] -= xv * M[m * 17 + c0 + e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Xs[(16 * bi + r) * kA_LD + 16 * bj + c0 + e] = out[e];
+}
+
+__global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillArgs p, Workspace ws)
+{
+    // LDS plan (bytes): [0, 34816) q^ and k^ token-major, later A and X;
+    // then k^T, v^T, T', T'Gam, inverse scratch, gates.
+    __shared__ __attribute__((aligned(16))) uint8_t smem[34816 + 2 * 18432 + 2 * 9216 + 3 * 1088 + 512];
+    _Float16 *Qs = reinterpret_cast<_Float16 *>(smem);
+    _Float16 *Ks = Qs + 64 * kQ_LD;
+    float *As = reinterpret_cast<float *>(smem);
+    float *Xs = As + 64 * kA_LD;
+    _Float16 *KTs = reinterpret_cast<_Float16 *>(smem + 34816);
+    _Float16 *VTs = KTs + 128 * kT_LD;
+    _Float16 *Th = VTs + 128 * kT_LD;
+    _Float16 *TGh = Th + 64 * kT_LD;
+    float *Mscr = reinterpret_cast<float *>(smem + 34816 + 2 * 18432 + 2 * 9216);
+    float *s_gam = Mscr + 3 * 272;
+    float *s_beta = s_gam + 64;
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int q4 = lane >> 4, c16 = lane & 15;
+    const int c = blockIdx.x / p.Hqk, g = blockIdx.x % p.Hqk;
+    const int4 ci = ws.chunk_info[c];
+    const int n = ci.z;
+    if (n == 0) return;  // empty chunk slot (whole workgroup)
+    const int s = ci.x, t0 = ci.y;
+    const bool first = ci.w != 0;
+    const int Hqk = p.Hqk, Hv = p.Hv, G = Hv / Hqk;
+    const long C_tot = 2L * Hqk * kD + (long)Hv * kD;
+    const uint16_t *hist = (first && p.conv_state_in) ? p.conv_state_in + (long)s * 3 * C_tot : nullptr;
+    const int r0 = 16 * wave;
+
+    // ---- 1. q^, k^: conv + SiLU + L2 norm -> LDS (token-major and k^T)
+    {
+        float z0[16], z1[16];
+        const long ldqk = (long)Hqk * kD;
+        const long cq = (long)g * kD, ck = (long)Hqk * kD + (long)g * kD;
+#pragma unroll
+        for (int plane = 0; plane < 2; ++plane) {
+            const uint16_t *x = (plane == 0 ? p.q : p.k) + (long)t0 * ldqk + (long)g * kD;
+            const long ch0 = plane == 0 ? cq : ck;
+            conv_plane(x, ldqk, n, first, hist ? hist + ch0 : nullptr, C_tot, p.conv_w + ch0 * 4, lane,
+                       r0, z0, z1);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float ss = wave_sum(z0[i] * z0[i] + z1[i] * z1[i]);
+                const float inv = rsqrtf(ss + 1e-6f);
+                const _Float16 h0 = (_Float16)(z0[i] * inv), h1 = (_Float16)(z1[i] * inv);
+                _Float16 *dst = (plane == 0 ? Qs : Ks) + (r0 + i) * kQ_LD + 2 * lane;
+                dst[0] = h0;
+                dst[1] = h1;
+                if (plane == 1) {
+                    KTs[(2 * lane) * kT_LD + r0 + i] = h0;
+                    KTs[(2 * lane + 1) * kT_LD + r0 + i] = h1;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- 2. q^ and k^T operands for the sequential pass; K K^T and K Q^T
+    f32x4 kk[4], kq[4];
+    {
+        half8 *qf = reinterpret_cast<half8 *>(ws.qfrag + ((long)c * Hqk + g) * kQFragBytes);
+        half8 *kf = reinterpret_cast<half8 *>(ws.kfrag + ((long)c * Hqk + g) * kKFragBytes);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) qf[(wave * 4 + kb) * 64 + lane] = lds_frag(Qs, kQ_LD, 16 * wave, 32 * kb, lane);
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int rt = 2 * wave + rr;
+                kf[(rt * 2 + kb) * 64 + lane] = lds_frag(KTs, kT_LD, 16 * rt, 32 * kb, lane);
+            }
+        // K K^T: rows 16*wave.., all four column tiles
+        half8 arow[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) arow[kb] = lds_frag(Ks, kQ_LD, 16 * wave, 32 * kb, lane);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) acc = mfma16(arow[kb], lds_frag(Ks, kQ_LD, 16 * ct, 32 * kb, lane), acc);
+            kk[ct] = acc;
+        }
+        // K Q^T: column tile `wave` (query tokens), key-token tiles jt <= wave
+        half8 bq[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) bq[kb] = lds_frag(Qs, kQ_LD, 16 * wave, 32 * kb, lane);
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (jt <= wave) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) acc = mfma16(lds_frag(Ks, kQ_LD, 16 * jt, 32 * kb, lane), bq[kb], acc);
+            }
+            kq[jt] = acc;
+        }
+    }
+    __syncthreads();  // q^ / k^ token-major tiles are dead from here on (A, X reuse them)
+
+    // ---- 3. per V head of the group
+    for (int j = 0; j < G; ++j) {
+        const int h = g * G + j;
+        const long hc = (long)c * Hv + h;
+        // gates (wave 0): gam = in-chunk cumulative log decay, beta
+        if (wave == 0) {
+            const bool valid = lane < n;
+            const long ti = (long)(t0 + lane) * Hv + h;
+            const float av = valid ? p.a[ti] : 0.f, bv = valid ? p.b[ti] : 0.f;
+            const float gl = valid ? -p.gate_scale * softplus_f(av) : 0.f;
+            const float be = valid ? sigmoid_f(bv) : 0.f;
+            float gam = gl;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(gam, off, 64);
+                if (lane >= off) gam += y;
+            }
+            const float gam_n = __shfl(gam, n - 1, 64);
+            s_gam[lane] = gam;
+            s_beta[lane] = be;
+            float *gt = ws.gates + hc * kGateFloats;
+            gt[lane] = __expf(gam);
+            gt[64 + lane] = valid ? __expf(gam_n - gam) : 0.f;
+            if (lane == 0) gt[128] = __expf(gam_n);
+        }
+        // v^ of head h: conv + SiLU -> v^T in LDS
+        {
+            float z0[16], z1[16];
+            const long ldv = (long)Hv * kD;
+            const long cv = 2L * Hqk * kD + (long)h * kD;
+            const uint16_t *x = p.v + (long)t0 * ldv + (long)h * kD;
+            conv_plane(x, ldv, n, first, hist ? hist + cv : nullptr, C_tot, p.conv_w + cv * 4, lane, r0,
+                       z0, z1);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                VTs[(2 * lane) * kT_LD + r0 + i] = (_Float16)z0[i];
+                VTs[(2 * lane + 1) * kT_LD + r0 + i] = (_Float16)z1[i];
+            }
+        }
+        __syncthreads();
+        // A = strict_lower(diag(beta) K K^T * D) -> LDS; P = (K Q^T)^T * D (lower) -> global
+        {
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * wave + 4 * q4 + e, jj = 16 * ct + c16;
+                    As[i * kA_LD + jj] = i > jj ? s_beta[i] * kk[ct][e] * __expf(s_gam[i] - s_gam[jj]) : 0.f;
+                }
+            half8 *pf = reinterpret_cast<half8 *>(ws.pfrag + hc * kPFragBytes);
+            const int i = 16 * wave + c16;
+            const float gi = s_gam[i];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                half8 fr;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int jt = 2 * kb + (e >> 2);
+                    const int jj = 16 * jt + 4 * q4 + (e & 3);
+                    const float val = i >= jj ? kq[jt][e & 3] * __expf(gi - s_gam[jj]) : 0.f;
+                    fr[e] = (_Float16)val;
+                }
+                pf[(wave * 2 + kb) * 64 + lane] = fr;
+            }
+        }
+        __syncthreads();
+        // (I + A)^-1, blocked by 16: diagonal blocks by forward substitution
+        {
+            const int cc = lane & 15;
+            const int bo = 16 * wave;
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float acc = i == cc ? 1.f : 0.f;
+#pragma unroll
+                for (int m = 0; m < i; ++m) acc -= As[(bo + i) * kA_LD + bo + m] * x[m];
+                x[i] = acc;
+            }
+            if (lane < 16) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) Xs[(bo + i) * kA_LD + bo + cc] = x[i];
+            }
+        }
+        __syncthreads();
+        if (wave < 3) inv_block_product(As, Xs, Mscr + wave * 272, wave + 1, wave, lane);
+        __syncthreads();
+        if (wave < 2) inv_block_product(As, Xs, Mscr + wave * 272, wave + 2, wave, lane);
+        __syncthreads();
+        if (wave == 0) inv_block_product(As, Xs, Mscr, 3, 0, lane);
+        __syncthreads();
+        // T' = X diag(beta), T'Gam = X diag(beta Gam) (fp16, lower)
+        for (int e = t; e < 64 * 64; e += kPrepThreads) {
+            const int i = e >> 6, jj = e & 63;
+            const float tv = jj <= i ? Xs[i * kA_LD + jj] * s_beta[jj] : 0.f;
+            Th[i * kT_LD + jj] = (_Float16)tv;
+            TGh[i * kT_LD + jj] = (_Float16)(tv * __expf(s_gam[jj]));
+        }
+        __syncthreads();
+        // U' = T' V: column tiles 2*wave, 2*wave+1; stored in accumulator order
+        {
+            half4 *uf = reinterpret_cast<half4 *>(ws.ufrag + hc * kUBytes);
+#pragma unroll
+            for (int cti = 0; cti < 2; ++cti) {
+                const int ct = 2 * wave + cti;
+                const half8 b0 = lds_frag(VTs, kT_LD, 16 * ct, 0, lane);
+                const half8 b1 = lds_frag(VTs, kT_LD, 16 * ct, 32, lane);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    acc = mfma16(lds_frag(Th, kT_LD, 16 * rt, 0, lane), b0, acc);
+                    if (rt >= 2) acc = mfma16(lds_frag(Th, kT_LD, 16 * rt, 32, lane), b1, acc);
+                    half4 hv;
+                    hv[0] = (_Float16)acc[0]; hv[1] = (_Float16)acc[1];
+                    hv[2] = (_Float16)acc[2]; hv[3] = (_Float16)acc[3];
+                    uf[(ct * 4 + rt) * 64 + lane] = hv;
+                }
+            }
+        }
+        // W^T = K^T diag(Gam) T'^T: token tile `wave`, all eight d tiles; -W stored as A operand
+        {
+            half8 *wf = reinterpret_cast<half8 *>(ws.wfrag + hc * kWFragBytes);
+            const half8 b0 = lds_frag(TGh, kT_LD, 16 * wave, 0, lane);
+            const half8 b1 = lds_frag(TGh, kT_LD, 16 * wave, 32, lane);
+            f32x4 wt[8];
+#pragma unroll
+            for (int rt = 0; rt < 8; ++rt) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                acc = mfma16(lds_frag(KTs, kT_LD, 16 * rt, 0, lane), b0, acc);
+                if (wave >= 2) acc = mfma16(lds_frag(KTs, kT_LD, 16 * rt, 32, lane), b1, acc);
+                wt[rt] = acc;
+            }
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) wf[(wave * 4 + kb) * 64 + lane] = pack_h8(-wt[2 * kb], -wt[2 * kb + 1]);
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// chain: the sequential state carry, one wave per (sequence, V head, 16 cols)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void chain_kernel(PrefillArgs p, Workspace ws)
+{
+    const int lane = threadIdx.x, q4 = lane >> 4, c16 = lane & 15;
+    const int Hqk = p.Hqk, Hv = p.Hv, G = Hv / Hqk;
+    // block -> (rank, group, head-in-group, column tile); the 8*G waves that
+    // share one (sequence, QK group) land on the same XCD (same L2)
+    const int bid = blockIdx.x;
+    const int gu = (bid / (64 * G)) * 8 + (bid & 7);
+    const int inner = (bid >> 3) % (8 * G);
+    if (gu >= p.N * Hqk) return;
+    const int rank = gu / Hqk, g = gu % Hqk;
+    const int j = inner >> 3, ct = inner & 7;
+    const int h = g * G + j;
+    const int s = ws.order[rank];
+    const int4 si = ws.seq_info[s];  // chunk0, nchunks, t0, L
+    const int col = 16 * ct + c16;
+
+    // state slice S[:, 16ct .. 16ct+15] in accumulator layout: tile rt holds rows 16rt + 4q4 + e
+    f32x4 S[8];
+    const long sbase = ((long)s * Hv + h) * kD * kD;
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            S[rt][e] = p.state_in ? p.state_in[sbase + (long)(16 * rt + 4 * q4 + e) * kD + col] : 0.f;
+
+    for (int cc = 0; cc < si.y; ++cc) {
+        const int c = si.x + cc;
+        const int n = min(kChunk, si.w - cc * kChunk);
+        const int tok0 = si.z + cc * kChunk;
+        const long hc = (long)c * Hv + h, gc = (long)c * Hqk + g;
+        const half8 *Wf = reinterpret_cast<const half8 *>(ws.wfrag + hc * kWFragBytes) + lane;
+        const half8 *Qf = reinterpret_cast<const half8 *>(ws.qfrag + gc * kQFragBytes) + lane;
+        const half8 *Kf = reinterpret_cast<const half8 *>(ws.kfrag + gc * kKFragBytes) + lane;
+        const half8 *Pf = reinterpret_cast<const half8 *>(ws.pfrag + hc * kPFragBytes) + lane;
+        const half4 *Uf = reinterpret_cast<const half4 *>(ws.ufrag + hc * kUBytes) + ct * 4 * 64 + lane;
+        const float *gt = ws.gates + hc * kGateFloats;
+
+        // state as the B operand (fp16), contraction over d_k
+        half8 Sb[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) Sb[kb] = pack_h8(S[2 * kb], S[2 * kb + 1]);
+
+        // Vnew = U' - W S ;  QS = Q S
+        f32x4 Vn[4], QS[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const half4 u = Uf[rt * 64];
+            f32x4 acc = {(float)u[0], (float)u[1], (float)u[2], (float)u[3]};
+            f32x4 qacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                acc = mfma16(Wf[(rt * 4 + kb) * 64], Sb[kb], acc);
+                qacc = mfma16(Qf[(rt * 4 + kb) * 64], Sb[kb], qacc);
+            }
+            Vn[rt] = acc;
+            QS[rt] = qacc;
+        }
+        // Vnew as B operands: plain (for P Vnew) and scaled by Gam_n / Gam (for the state)
+        half8 Vb[2], Vr[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const f32x4 r_lo = *reinterpret_cast<const f32x4 *>(gt + 64 + 32 * kb + 4 * q4);
+            const f32x4 r_hi = *reinterpret_cast<const f32x4 *>(gt + 64 + 32 * kb + 16 + 4 * q4);
+            Vb[kb] = pack_h8(Vn[2 * kb], Vn[2 * kb + 1]);
+            Vr[kb] = pack_h8(Vn[2 * kb] * r_lo, Vn[2 * kb + 1] * r_hi);
+        }
+        // O = diag(Gam) Q S + P Vnew
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const f32x4 gam = *reinterpret_cast<const f32x4 *>(gt + 16 * rt + 4 * q4);
+            f32x4 acc = QS[rt] * gam;
+            acc = mfma16(Pf[(rt * 2 + 0) * 64], Vb[0], acc);
+            if (rt >= 2) acc = mfma16(Pf[(rt * 2 + 1) * 64], Vb[1], acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int tok = 16 * rt + 4 * q4 + e;
+                if (tok < n)
+                    p.o[((long)(tok0 + tok) * Hv + h) * kD + col] = (uint16_t)f32_to_bf16(acc[e] * p.q_scale);
+            }
+        }
+        // S <- Gam_n S + K^T (r * Vnew)
+        const float gn = gt[128];
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt) {
+            f32x4 acc = S[rt] * gn;
+            acc = mfma16(Kf[(rt * 2 + 0) * 64], Vr[0], acc);
+            acc = mfma16(Kf[(rt * 2 + 1) * 64], Vr[1], acc);
+            S[rt] = acc;
+        }
+    }
+
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p.state_out[sbase + (long)(16 * rt + 4 * q4 + e) * kD + col] = S[rt][e];
+
+    // carried conv rows: the last three raw rows of the sequence (v channels of
+    // head h; the first head of the group also writes the q and k channels)
+    if (p.conv_state_out && ct == 0) {
+        const long C_tot = 2L * Hqk * kD + (long)Hv * kD;
+        const int L = si.w, t0 = si.z;
+        for (int plane = (j == 0 ? 0 : 2); plane < 3; ++plane) {
+            const long ch0 = plane == 0 ? (long)g * kD : plane == 1 ? (long)Hqk * kD + (long)g * kD
+                                                                  : 2L * Hqk * kD + (long)h * kD;
+            const uint16_t *src = plane == 0 ? p.q + (long)g * kD : plane == 1 ? p.k + (long)g * kD
+                                                                              : p.v + (long)h * kD;
+            const long ld = plane == 2 ? (long)Hv * kD : (long)Hqk * kD;
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {
+                const int tau = L - 3 + r;
+                uint32_t val = 0;
+                if (tau >= 0)
+                    val = ld_pair(src + (long)(t0 + tau) * ld + 2 * lane);
+                else if (p.conv_state_in)
+                    val = ld_pair(p.conv_state_in + ((long)s * 3 + 3 + tau) * C_tot + ch0 + 2 * lane);
+                *reinterpret_cast<uint32_t *>(p.conv_state_out + ((long)s * 3 + r) * C_tot + ch0 + 2 * lane) = val;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+size_t prefill_workspace_bytes(int max_chunks, int N, int Hqk, int Hv)
+{
+    const size_t C = (size_t)max_chunks;
+    size_t total = 0;
+    total += align256(C * sizeof(int4));
+    total += align256((size_t)N * sizeof(int4));
+    total += align256((size_t)N * sizeof(int));
+    total += align256(C * Hqk * kQFragBytes);
+    total += align256(C * Hqk * kKFragBytes);
+    total += align256(C * Hv * kWFragBytes);
+    total += align256(C * Hv * kUBytes);
+    total += align256(C * Hv * kPFragBytes);
+    total += align256(C * Hv * kGateFloats * sizeof(float));
+    return total;
+}
+
+Workspace carve_workspace(void *base, int max_chunks, int N, int Hqk, int Hv)
+{
+    const size_t C = (size_t)max_chunks;
+    uint8_t *ptr = static_cast<uint8_t *>(base);
+    Workspace ws;
+    auto take = [&](size_t bytes) {
+        uint8_t *r = ptr;
+        ptr += align256(bytes);
+        return r;
+    };
+    ws.chunk_info = reinterpret_cast<int4 *>(take(C * sizeof(int4)));
+    ws.seq_info = reinterpret_cast<int4 *>(take((size_t)N * sizeof(int4)));
+    ws.order = reinterpret_cast<int *>(take((size_t)N * sizeof(int)));
+    ws.qfrag = take(C * Hqk * kQFragBytes);
+    ws.kfrag = take(C * Hqk * kKFragBytes);
+    ws.wfrag = take(C * Hv * kWFragBytes);
+    ws.ufrag = take(C * Hv * kUBytes);
+    ws.pfrag = take(C * Hv * kPFragBytes);
+    ws.gates = reinterpret_cast<float *>(take(C * Hv * kGateFloats * sizeof(float)));
+    return ws;
+}
+
+hipError_t launch_prefill(const PrefillArgs &p, void *workspace, hipStream_t stream)
+{
+    const Workspace ws = carve_workspace(workspace, p.max_chunks, p.N, p.Hqk, p.Hv);
+    hipLaunchKernelGGL(setup_kernel, dim3(1), dim3(1024), 0, stream, p, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (p.max_chunks > 0) {
+        hipLaunchKernelGGL(prep_kernel, dim3((unsigned)((long)p.max_chunks * p.Hqk)), dim3(kPrepThreads), 0,
+                           stream, p, ws);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int G = p.Hv / p.Hqk;
+    const long groups = (long)p.N * p.Hqk;
+    const long blocks = ((groups + 7) / 8) * 64L * G;
+    hipLaunchKernelGGL(chain_kernel, dim3((unsigned)blocks), dim3(64), 0, stream, p, ws);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,121 @@
+"""The C ABI library loads, exports every entry point the header declares and
+rejects bad arguments with the documented status before touching the GPU.
+
+These tests run without a GPU: every call here fails validation (or is a
+documented no-op), and validation happens before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_sequence_gdn_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(gdn.LIB_PATH):
+        from linear_attention_sequence_gdn_amd import build
+        build.build()
+    return gdn.lib()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) >= {"gdn_prefill", "gdn_prefill_varlen", "gdn_decode_step",
+                          "gdn_prefill_workspace_size", "gdn_prefill_varlen_workspace_size",
+                          "gdn_status_string"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    assert gdn.gdn_status_string(0) == "GDN_OK"
+    assert gdn.gdn_status_string(1) == "GDN_ERR_INVALID_ARGUMENT"
+    assert gdn.gdn_status_string(2) == "GDN_ERR_UNSUPPORTED"
+    assert gdn.gdn_status_string(3) == "GDN_ERR_WORKSPACE_TOO_SMALL"
+    assert gdn.gdn_status_string(4) == "GDN_ERR_HIP"
+    assert gdn.gdn_status_string(99) == "GDN_ERR_UNKNOWN"
+
+
+def test_workspace_sizes(L):
+    assert gdn.gdn_prefill_workspace_size(1, 8192, 16, 48) > 0
+    assert gdn.gdn_prefill_workspace_size(1, 8192, 16, 48) < gdn.gdn_prefill_workspace_size(1, 8193, 16, 48)
+    assert gdn.gdn_prefill_workspace_size(1, 64, 16, 48, 64, 128) == 0  # unsupported dims
+    assert gdn.gdn_prefill_workspace_size(1, 64, 16, 47) == 0
+    # varlen bound covers any split of T_tot into N sequences
+    assert gdn.gdn_prefill_varlen_workspace_size(4, 256, 2, 6) >= gdn.gdn_prefill_workspace_size(4, 64, 2, 6)
+
+
+FAKE = 0x10000  # 64 KiB-aligned, never dereferenced: validation fails first
+
+
+def _p(v=FAKE):
+    return ctypes.c_void_p(v) if v else None
+
+
+def call_decode(L, q=FAKE, B=2, Hqk=2, Hv=6, dk=128, dv=128, state=FAKE):
+    return L.gdn_decode_step(_p(q), _p(), _p(), _p(), _p(), _p(), _p(), _p(state), _p(state), _p(),
+                             B, Hqk, Hv, dk, dv, 0.1, 1.0, None)
+
+
+def test_decode_validation(L):
+    assert call_decode(L, q=0) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call_decode(L, B=-1) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call_decode(L, dk=64) == gdn.GDN_ERR_UNSUPPORTED
+    assert call_decode(L, dv=96) == gdn.GDN_ERR_UNSUPPORTED
+    assert call_decode(L, Hv=7) == gdn.GDN_ERR_UNSUPPORTED
+    assert call_decode(L, Hqk=0) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call_decode(L, Hqk=1, Hv=17) == gdn.GDN_ERR_UNSUPPORTED  # group wider than one workgroup
+    assert call_decode(L, state=FAKE + 4) == gdn.GDN_ERR_INVALID_ARGUMENT  # misaligned state
+    assert call_decode(L, B=0) == gdn.GDN_OK  # no-op, nothing launched
+
+
+def call_prefill(L, B=1, T=64, Hqk=2, Hv=6, dk=128, dv=128, q=FAKE, ws=FAKE, ws_bytes=None,
+                 cs_in=0, cs_out=0):
+    if ws_bytes is None:
+        ws_bytes = gdn.gdn_prefill_workspace_size(B, T, Hqk, Hv, dk, dv)
+    return L.gdn_prefill(_p(q), _p(), _p(), _p(), _p(), _p(), _p(cs_in), _p(cs_out), None, _p(), _p(),
+                         B, T, Hqk, Hv, dk, dv, 0.1, 1.0, _p(ws), ws_bytes, None)
+
+
+def test_prefill_validation(L):
+    assert call_prefill(L, q=0) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call_prefill(L, T=-1) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call_prefill(L, dk=64) == gdn.GDN_ERR_UNSUPPORTED
+    assert call_prefill(L, Hv=5) == gdn.GDN_ERR_UNSUPPORTED
+    assert call_prefill(L, q=FAKE + 2) == gdn.GDN_ERR_INVALID_ARGUMENT
+    need = gdn.gdn_prefill_workspace_size(1, 64, 2, 6)
+    assert call_prefill(L, ws_bytes=need - 1) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL
+    assert call_prefill(L, ws=0) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL
+    assert call_prefill(L, cs_in=FAKE, cs_out=FAKE) == gdn.GDN_ERR_INVALID_ARGUMENT  # aliasing conv rows
+    assert call_prefill(L, B=0, T=0, ws=0, ws_bytes=0) == gdn.GDN_OK  # empty batch: nothing to do
+
+
+def test_varlen_validation(L):
+    def call(cu=FAKE, N=2, T_tot=100, Hv=6, ws_bytes=None):
+        if ws_bytes is None:
+            ws_bytes = gdn.gdn_prefill_varlen_workspace_size(N, T_tot, 2, Hv)
+        return L.gdn_prefill_varlen(_p(), _p(), _p(), _p(), _p(), _p(), None, None, None, _p(), _p(),
+                                    _p(cu), N, T_tot, 2, Hv, 128, 128, 0.1, 1.0, _p(), ws_bytes, None)
+    assert call(cu=0) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(N=-1) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(Hv=9) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(ws_bytes=10) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL
+    assert call(cu=FAKE + 1) == gdn.GDN_ERR_INVALID_ARGUMENT
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(gdn, "_lib", None)
+    monkeypatch.setattr(gdn, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        gdn.lib()
