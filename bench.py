@@ -1,0 +1,312 @@
+#!/usr/bin/env python3
+"""GDN token mixer benchmark on one MI355X.
+
+A step is one chunked prefill of the model-layer workload (B = 1, T = 8192,
+16 QK / 48 V heads, d = 128, seeded synthetic bf16 inputs already resident in
+HBM).  The decode workload (B = 256 sequences, 64 consecutive in-place steps)
+is timed in the same run and reported under "decode".  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Timing: HIP events on the stream the library launches on.  The prefill goes
+through gdn_prefill_with_events, so each of its three kernels is timed per
+launch; the decode step is one kernel per call.  The CPU baseline is the fp64
+oracle, as it stands, on a bounded sample of the same prefill workload.
+"""
+import argparse
+import ctypes
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN prefill tokens/s (T=8192, 16QK/48V heads, d=128); decode μs/step at B=256"
+PEAK_MFMA_F16 = 2.5e15      # dense fp16/bf16 matrix-core FLOP/s
+PEAK_HBM = 8.0e12           # bytes/s
+D = 128
+CHUNK = 64
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (chunk form, C = 64, counted per full chunk)
+# ---------------------------------------------------------------------------
+def prefill_flops(T, Hqk, Hv, n=CHUNK, d=D):
+    """(prep, chain) algorithmic FLOP of one prefill of T tokens (T % 64 == 0)."""
+    chunks = T // n
+    prep = chunks * (Hqk * 4 * n * n * d + Hv * (n ** 3 / 3 + 4 * n * n * d))
+    chain = chunks * Hv * (6 * n * d * d + 2 * n * n * d)
+    return prep, chain
+
+
+def prefill_bytes(T, Hqk, Hv, d=D):
+    """Compulsory HBM bytes of one prefill (zero initial state, no conv carry)."""
+    per_tok = 2 * (2 * Hqk * d + Hv * d) + 2 * 4 * Hv + 2 * Hv * d
+    return T * per_tok + Hv * d * d * 4 + (2 * Hqk * d + Hv * d) * 4 * 2
+
+
+def decode_bytes(B, Hqk, Hv, d=D):
+    """Compulsory HBM bytes of one decode step (state read + write dominate)."""
+    C_tot = 2 * Hqk * d + Hv * d
+    state = 2 * B * Hv * d * d * 4
+    per_seq = 2 * (2 * Hqk * d + Hv * d) + 2 * Hv * d + 2 * 4 * Hv + 2 * 3 * C_tot * 2
+    return state + B * per_seq
+
+
+# ---------------------------------------------------------------------------
+# HIP events through the runtime torch already loaded
+# ---------------------------------------------------------------------------
+class Hip:
+    def __init__(self):
+        import torch
+        cands = glob.glob(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so*"))
+        self.L = ctypes.CDLL(cands[0] if cands else "libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        rc = self.L.hipEventCreate(ctypes.byref(e))
+        assert rc == 0, f"hipEventCreate failed ({rc})"
+        return e
+
+    def record(self, e, stream):
+        assert self.L.hipEventRecord(e, stream) == 0
+
+    def ms(self, a, b):
+        self.L.hipEventSynchronize(b)
+        out = ctypes.c_float()
+        assert self.L.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
+        return float(out.value)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "linear_attention_sequence_gdn_amd", "csrc", "*"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name, digest):
+    """HBM traffic measured by rocprofv3 counters for `name`, if the committed
+    measurement was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(name)
+    except (ValueError, AttributeError):
+        return None
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+def bench_prefill(hip, steps, warmup):
+    import torch
+    import linear_attention_sequence_gdn_amd as gdn
+    from linear_attention_sequence_gdn_amd import inputs
+
+    x = inputs.make_config(1)
+    T, Hqk, Hv = 8192, 16, 48
+
+    def dev(a, bf):
+        import numpy as np
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if bf else np.ascontiguousarray(a))
+        return (t.view(torch.bfloat16) if bf else t).cuda()
+
+    q = dev(x["q"].reshape(1, T, Hqk, D), True)
+    k = dev(x["k"].reshape(1, T, Hqk, D), True)
+    v = dev(x["v"].reshape(1, T, Hv, D), True)
+    a = dev(x["a"].reshape(1, T, Hv), False)
+    b = dev(x["b"].reshape(1, T, Hv), False)
+    w = dev(x["conv_w"], True)
+    o = torch.empty((1, T, Hv, D), dtype=torch.bfloat16, device="cuda")
+    so = torch.empty((1, Hv, D, D), dtype=torch.float32, device="cuda")
+    need = gdn.gdn_prefill_workspace_size(1, T, Hqk, Hv)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    L = gdn.lib()
+    L.gdn_prefill_with_events.restype = ctypes.c_int
+    L.gdn_prefill_with_events.argtypes = [ctypes.c_void_p] * 11 + [ctypes.c_int] * 6 + \
+        [ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    evs = [[hip.event() for _ in range(4)] for _ in range(steps)]
+    arrs = [(ctypes.c_void_p * 4)(*[e.value for e in ev]) for ev in evs]
+    warm = (ctypes.c_void_p * 4)(*[hip.event().value for _ in range(4)])
+
+    def run(arr):
+        rc = L.gdn_prefill_with_events(P(q), P(k), P(v), P(a), P(b), P(w), None, None, None, P(so), P(o),
+                                       1, T, Hqk, Hv, D, D, 0.1, 1.0, P(ws), need, sp, arr)
+        assert rc == 0, gdn.gdn_status_string(rc)
+
+    for _ in range(warmup):
+        run(warm)
+    torch.cuda.synchronize()
+    t0, t1 = hip.event(), hip.event()
+    hip.record(t0, sp)
+    for i in range(steps):
+        run(arrs[i])
+    hip.record(t1, sp)
+    torch.cuda.synchronize()
+    total_ms = hip.ms(t0, t1)
+    stage = {"setup": 0.0, "prep": 0.0, "chain": 0.0}
+    for ev in evs:
+        stage["setup"] += hip.ms(ev[0], ev[1])
+        stage["prep"] += hip.ms(ev[1], ev[2])
+        stage["chain"] += hip.ms(ev[2], ev[3])
+    stage = {k_: v_ / steps for k_, v_ in stage.items()}
+    return dict(ms_per_step=total_ms / steps, stage_ms=stage, T=T, Hqk=Hqk, Hv=Hv)
+
+
+def bench_decode(hip, steps=64):
+    import numpy as np
+    import torch
+    import linear_attention_sequence_gdn_amd as gdn
+    from linear_attention_sequence_gdn_amd import inputs
+
+    x = inputs.make_config(3)
+    B, Hqk, Hv = x["B"], x["Hqk"], x["Hv"]
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v = bf(x["q"]), bf(x["k"]), bf(x["v"])
+    a = torch.from_numpy(x["a"]).cuda()
+    b = torch.from_numpy(x["b"]).cuda()
+    w = bf(x["conv_w"])
+    conv0 = bf(x["conv_state"])
+    st0 = torch.from_numpy(x["state"]).cuda()
+    conv, st = conv0.clone(), st0.clone()
+    o = torch.empty((B, Hv, D), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    L = gdn.lib()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def step(i):
+        rc = L.gdn_decode_step(P(q[i]), P(k[i]), P(v[i]), P(a[i]), P(b[i]), P(w), P(conv), P(st), P(st),
+                               P(o), B, Hqk, Hv, D, D, 0.1, 1.0, sp)
+        assert rc == 0, gdn.gdn_status_string(rc)
+
+    for i in range(4):  # warm-up, then restore the initial state
+        step(i)
+    torch.cuda.synchronize()
+    conv.copy_(conv0)
+    st.copy_(st0)
+    torch.cuda.synchronize()
+    ev = [hip.event() for _ in range(steps + 1)]
+    for i in range(steps):
+        hip.record(ev[i], sp)
+        step(i)
+    hip.record(ev[steps], sp)
+    torch.cuda.synchronize()
+    per = [hip.ms(ev[i], ev[i + 1]) for i in range(steps)]
+    total = hip.ms(ev[0], ev[steps])
+    return dict(us_per_step=total * 1e3 / steps, kernel_us=sum(per) * 1e3 / steps, B=B, Hqk=Hqk, Hv=Hv,
+                steps=steps)
+
+
+def cpu_baseline(min_seconds=10.0, max_reps=3):
+    import oracle
+    from linear_attention_sequence_gdn_amd import inputs
+    x = inputs.make_config(1)
+    oracle.build(force=False)
+    reps, t0 = 0, time.perf_counter()
+    while reps < max_reps:
+        oracle.prefill(x["q"], x["k"], x["v"], x["a"], x["b"], x["conv_w"], x["cu_seqlens"],
+                       Hqk=16, Hv=48, gate_scale=0.1)
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": 8192 * reps / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 token-by-token oracle on the full T=8192, 16QK/48V workload, "
+                      f"{reps} run(s) in {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import linear_attention_sequence_gdn_amd as gdn
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    gdn.lib()
+    hip = Hip()
+    digest = source_digest()
+
+    pf = bench_prefill(hip, args.steps, args.warmup)
+    dc = bench_decode(hip)
+    T, Hqk, Hv = pf["T"], pf["Hqk"], pf["Hv"]
+    flop_prep, flop_chain = prefill_flops(T, Hqk, Hv)
+    tok_s = T / (pf["ms_per_step"] * 1e-3)
+
+    # dominant prefill kernel, priced against the fp16 matrix-core peak
+    dom = "chain" if pf["stage_ms"]["chain"] >= pf["stage_ms"]["prep"] else "prep"
+    dom_flop = flop_chain if dom == "chain" else flop_prep
+    dom_ms = pf["stage_ms"][dom]
+    achieved = dom_flop / (dom_ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "kernel": f"{dom}_kernel", "achieved": achieved,
+            "peak": PEAK_MFMA_F16 / 1e12, "unit": "TFLOP/s", "frac": achieved * 1e12 / PEAK_MFMA_F16,
+            "traffic": load_traffic(f"prefill_{dom}", digest),
+            "algorithmic_flop_per_launch": dom_flop, "avg_launch_ms": dom_ms}
+    path_flop = flop_prep + flop_chain
+    dec_bytes = decode_bytes(dc["B"], dc["Hqk"], dc["Hv"])
+    dec_gbs = dec_bytes / (dc["kernel_us"] * 1e-6) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pf["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 MFMA operands, f32 accumulate/state, bf16 I/O",
+        "data": "synthetic (seeded, inputs resident in HBM)",
+        "config": {"workload": "layer_prefill_T8192_16qk_48v", "B": 1, "T": T, "Hqk": Hqk, "Hv": Hv,
+                   "d": D, "chunk": CHUNK, "seed": 1001},
+        "roofline": roof,
+        "path": {"algorithmic_flop": path_flop,
+                 "mfma_frac": path_flop / (pf["ms_per_step"] * 1e-3) / PEAK_MFMA_F16,
+                 "compulsory_bytes": prefill_bytes(T, Hqk, Hv),
+                 "hbm_frac": prefill_bytes(T, Hqk, Hv) / (pf["ms_per_step"] * 1e-3) / PEAK_HBM,
+                 "stage_ms": pf["stage_ms"]},
+        "decode": {"metric": "decode us/step (B=256, 16QK/48V, 64 in-place steps)",
+                   "value": dc["us_per_step"], "unit": "us/step", "higher_is_better": False,
+                   "kernel_us": dc["kernel_us"],
+                   "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": dec_gbs,
+                                "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": dec_gbs * 1e9 / PEAK_HBM,
+                                "traffic": load_traffic("decode", digest),
+                                "algorithmic_bytes_per_launch": dec_bytes}},
+        "source_digest": digest,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

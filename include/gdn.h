@@ -90,6 +90,23 @@ int gdn_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                 float gate_scale, float q_scale,
                 void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Measurement variant of gdn_prefill: the same work on the same stream, and
+ * additionally records four caller-created HIP events (events[i] is a
+ * hipEvent_t): events[0] before the first kernel, events[1] after the
+ * chunk-table setup, events[2] after the parallel per-chunk pass and
+ * events[3] after the sequential state pass, so that the caller can time each
+ * stage with hipEventElapsedTime.  events must not be NULL.
+ */
+int gdn_prefill_with_events(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                            const float *a, const float *b, const uint16_t *conv_w,
+                            const uint16_t *conv_state_in, uint16_t *conv_state_out,
+                            const float *state_in, float *state_out, uint16_t *o,
+                            int B, int T, int Hqk, int Hv, int dk, int dv,
+                            float gate_scale, float q_scale,
+                            void *workspace, size_t workspace_bytes, void *stream,
+                            void *const *events);
+
 /* Bytes of device workspace gdn_prefill_varlen needs (any lengths summing to
  * T_tot over N sequences). */
 size_t gdn_prefill_varlen_workspace_size(int N, int T_tot, int Hqk, int Hv, int dk, int dv);

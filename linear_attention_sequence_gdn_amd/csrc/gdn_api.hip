@@ -84,7 +84,8 @@ static int prefill_common(const uint16_t *q, const uint16_t *k, const uint16_t *
                           uint16_t *conv_state_out, const float *state_in, float *state_out,
                           uint16_t *o, const int32_t *cu_seqlens, int N, int T_uniform,
                           int T_tot, int Hqk, int Hv, float gate_scale, float q_scale,
-                          void *workspace, size_t workspace_bytes, void *stream)
+                          void *workspace, size_t workspace_bytes, void *stream,
+                          void *const *events = nullptr)
 {
     if (!state_out || !conv_w) return GDN_ERR_INVALID_ARGUMENT;
     if (T_tot > 0 && (!q || !k || !v || !a || !b || !o)) return GDN_ERR_INVALID_ARGUMENT;
@@ -108,7 +109,8 @@ static int prefill_common(const uint16_t *q, const uint16_t *k, const uint16_t *
     p.cu_seqlens = cu_seqlens; p.N = N; p.T_uniform = T_uniform; p.T_tot = T_tot;
     p.Hqk = Hqk; p.Hv = Hv; p.gate_scale = gate_scale; p.q_scale = q_scale;
     p.max_chunks = max_chunks;
-    hipError_t e = gdn::launch_prefill(p, workspace, reinterpret_cast<hipStream_t>(stream));
+    hipError_t e = gdn::launch_prefill(p, workspace, reinterpret_cast<hipStream_t>(stream),
+                                       reinterpret_cast<hipEvent_t const *>(events));
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
@@ -125,6 +127,25 @@ int gdn_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v, const f
     return prefill_common(q, k, v, a, b, conv_w, conv_state_in, conv_state_out, state_in,
                           state_out, o, nullptr, B, T, B * T, Hqk, Hv, gate_scale, q_scale,
                           workspace, workspace_bytes, stream);
+}
+
+int gdn_prefill_with_events(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
+                            const float *b, const uint16_t *conv_w, const uint16_t *conv_state_in,
+                            uint16_t *conv_state_out, const float *state_in, float *state_out,
+                            uint16_t *o, int B, int T, int Hqk, int Hv, int dk, int dv,
+                            float gate_scale, float q_scale, void *workspace,
+                            size_t workspace_bytes, void *stream, void *const *events)
+{
+    if (!events) return GDN_ERR_INVALID_ARGUMENT;
+    for (int i = 0; i < 4; ++i)
+        if (!events[i]) return GDN_ERR_INVALID_ARGUMENT;
+    if (B < 0 || T < 0) return GDN_ERR_INVALID_ARGUMENT;
+    int rc = check_dims(Hqk, Hv, dk, dv);
+    if (rc != GDN_OK) return rc;
+    if ((long)B * T > 0x7fffffffL) return GDN_ERR_UNSUPPORTED;
+    return prefill_common(q, k, v, a, b, conv_w, conv_state_in, conv_state_out, state_in,
+                          state_out, o, nullptr, B, T, B * T, Hqk, Hv, gate_scale, q_scale,
+                          workspace, workspace_bytes, stream, events);
 }
 
 int gdn_prefill_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,

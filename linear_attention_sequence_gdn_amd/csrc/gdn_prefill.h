@@ -41,7 +41,7 @@ constexpr size_t kKFragBytes = 16 * kFragBytes;      // k^T of a chunk    [128 x
 constexpr size_t kWFragBytes = 16 * kFragBytes;      // -W of a chunk     [64 x 128]
 constexpr size_t kUBytes = 64 * 128 * 2;             // U' of a chunk     [64 x 128]
 constexpr size_t kPFragBytes = 8 * kFragBytes;       // P of a chunk      [64 x 64]
-constexpr size_t kGateFloats = 3 * 64;               // Gamma, r, {Gamma_n}
+constexpr size_t kGateFloats = 256;                 // Gamma[64], r[64], Gamma_n, pad (1 KiB)
 
 struct Workspace {
     int4 *chunk_info;   // [max_chunks] {seq, t0, n, first}
@@ -57,6 +57,9 @@ struct Workspace {
 
 size_t prefill_workspace_bytes(int max_chunks, int N, int Hqk, int Hv);
 Workspace carve_workspace(void *base, int max_chunks, int N, int Hqk, int Hv);
-hipError_t launch_prefill(const PrefillArgs &p, void *workspace, hipStream_t stream);
+// events: NULL, or four events recorded before setup, after setup, after
+// prep and after the chain kernel.
+hipError_t launch_prefill(const PrefillArgs &p, void *workspace, hipStream_t stream,
+                          hipEvent_t const *events = nullptr);
 
 }  // namespace gdn

@@ -433,24 +433,81 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillArgs p, Works
 }
 
 // ---------------------------------------------------------------------------
-// chain: the sequential state carry, one wave per (sequence, V head, 16 cols)
+// chain: the sequential state carry
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void chain_kernel(PrefillArgs p, Workspace ws)
+// Workgroup = kChainWaves waves = one (sequence, V head) and 16*kChainWaves
+// columns of its state; each wave carries a 128 x 16 fp32 slice of S in its
+// accumulators through the whole sequence.  The operands of a chunk that
+// every wave needs (-W, q^, k^T, P, gates) and the waves' U' tiles are
+// brought into LDS with direct-to-LDS loads, double-buffered: chunk c+1 is in
+// flight while chunk c is computed, with one workgroup barrier per chunk.
+constexpr int kChainWaves = 2;
+
+template <int NW>
+struct ChainStage {
+    static constexpr int kW = 0, kQ = 16 * 1024, kK = 32 * 1024, kP = 48 * 1024, kG = 56 * 1024,
+                         kU = 57 * 1024;
+    static constexpr int kBlocks = 57 + 2 * NW;  // 1-KiB blocks per stage
+    static constexpr int kBytes = kBlocks * 1024;
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Issue the direct-to-LDS loads of chunk c into `stage`.  Every region is a
+// whole number of 1-KiB blocks; wave w (uniform) moves blocks w, w+NW, ... of
+// each region (lane l: bytes 16l .. 16l+15 of a block).
+template <int NW, int kBlocks>
+__device__ __forceinline__ void issue_region(const uint8_t *src, uint8_t *dst, int wave)
 {
-    const int lane = threadIdx.x, q4 = lane >> 4, c16 = lane & 15;
+#pragma unroll
+    for (int i = 0; i < kBlocks / NW; ++i) {
+        const int blk = i * NW + wave;
+        __builtin_amdgcn_global_load_lds(src + blk * 1024, (lds_void *)(dst + blk * 1024), 16, 0, 0);
+    }
+}
+
+template <int NW>
+__device__ __forceinline__ void chain_issue(const Workspace &ws, uint8_t *stage, long c, int h, int g,
+                                            int Hqk, int Hv, int cb, int wave, int lane)
+{
+    using St = ChainStage<NW>;
+    const long hc = c * Hv + h, gc = c * Hqk + g;
+    issue_region<NW, 16>(ws.wfrag + hc * kWFragBytes + lane * 16, stage + St::kW, wave);
+    issue_region<NW, 16>(ws.qfrag + gc * kQFragBytes + lane * 16, stage + St::kQ, wave);
+    issue_region<NW, 16>(ws.kfrag + gc * kKFragBytes + lane * 16, stage + St::kK, wave);
+    issue_region<NW, 8>(ws.pfrag + hc * kPFragBytes + lane * 16, stage + St::kP, wave);
+    issue_region<NW, 2 * NW>(ws.ufrag + hc * kUBytes + (long)cb * NW * 2048 + lane * 16, stage + St::kU, wave);
+    if (wave == 0)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t *>(ws.gates + hc * kGateFloats) + lane * 16,
+                                         (lds_void *)(stage + St::kG), 16, 0, 0);
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void chain_kernel(PrefillArgs p, Workspace ws)
+{
+    using St = ChainStage<NW>;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * St::kBytes + NW * 2048];
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int q4 = lane >> 4, c16 = lane & 15;
     const int Hqk = p.Hqk, Hv = p.Hv, G = Hv / Hqk;
-    // block -> (rank, group, head-in-group, column tile); the 8*G waves that
-    // share one (sequence, QK group) land on the same XCD (same L2)
+    constexpr int kBlocksPerHead = 8 / NW;
+    // block -> (rank, group, head-in-group, column block); all workgroups of
+    // one (sequence, QK group) land on the same XCD (same L2)
+    const int per_group = G * kBlocksPerHead;
     const int bid = blockIdx.x;
-    const int gu = (bid / (64 * G)) * 8 + (bid & 7);
-    const int inner = (bid >> 3) % (8 * G);
+    const int gu = (bid / (8 * per_group)) * 8 + (bid & 7);
+    const int inner = (bid >> 3) % per_group;
     if (gu >= p.N * Hqk) return;
     const int rank = gu / Hqk, g = gu % Hqk;
-    const int j = inner >> 3, ct = inner & 7;
+    const int j = inner / kBlocksPerHead, cb = inner % kBlocksPerHead;
     const int h = g * G + j;
+    const int ct = cb * NW + wave;
     const int s = ws.order[rank];
     const int4 si = ws.seq_info[s];  // chunk0, nchunks, t0, L
     const int col = 16 * ct + c16;
+    uint16_t *ostage = reinterpret_cast<uint16_t *>(smem + 2 * St::kBytes + wave * 2048);
 
     // state slice S[:, 16ct .. 16ct+15] in accumulator layout: tile rt holds rows 16rt + 4q4 + e
     f32x4 S[8];
@@ -461,17 +518,45 @@ __global__ __launch_bounds__(64) void chain_kernel(PrefillArgs p, Workspace ws)
         for (int e = 0; e < 4; ++e)
             S[rt][e] = p.state_in ? p.state_in[sbase + (long)(16 * rt + 4 * q4 + e) * kD + col] : 0.f;
 
+    if (si.y > 0) chain_issue<NW>(ws, smem, si.x, h, g, Hqk, Hv, cb, wave, lane);
     for (int cc = 0; cc < si.y; ++cc) {
-        const int c = si.x + cc;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (cc + 1 < si.y)
+            chain_issue<NW>(ws, smem + ((cc + 1) & 1) * St::kBytes, si.x + cc + 1, h, g, Hqk, Hv, cb, wave, lane);
+        const uint8_t *st = smem + (cc & 1) * St::kBytes;
+        const half8 *Wf = reinterpret_cast<const half8 *>(st + St::kW) + lane;
+        const half8 *Qf = reinterpret_cast<const half8 *>(st + St::kQ) + lane;
+        const half8 *Kf = reinterpret_cast<const half8 *>(st + St::kK) + lane;
+        const half8 *Pf = reinterpret_cast<const half8 *>(st + St::kP) + lane;
+        const float *gt = reinterpret_cast<const float *>(st + St::kG);
+        const half4 *Uf = reinterpret_cast<const half4 *>(st + St::kU) + wave * 4 * 64 + lane;
         const int n = min(kChunk, si.w - cc * kChunk);
         const int tok0 = si.z + cc * kChunk;
-        const long hc = (long)c * Hv + h, gc = (long)c * Hqk + g;
-        const half8 *Wf = reinterpret_cast<const half8 *>(ws.wfrag + hc * kWFragBytes) + lane;
-        const half8 *Qf = reinterpret_cast<const half8 *>(ws.qfrag + gc * kQFragBytes) + lane;
-        const half8 *Kf = reinterpret_cast<const half8 *>(ws.kfrag + gc * kKFragBytes) + lane;
-        const half8 *Pf = reinterpret_cast<const half8 *>(ws.pfrag + hc * kPFragBytes) + lane;
-        const half4 *Uf = reinterpret_cast<const half4 *>(ws.ufrag + hc * kUBytes) + ct * 4 * 64 + lane;
-        const float *gt = ws.gates + hc * kGateFloats;
+
+        // every operand of this chunk into registers first (one LDS round trip)
+        half8 wA[16], qA[16], kA[16], pA[8];
+        half4 uC[4];
+        f32x4 gam[4], r_lo[2], r_hi[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) wA[i] = Wf[i * 64];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) qA[i] = Qf[i * 64];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) uC[rt] = Uf[rt * 64];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) kA[i] = Kf[i * 64];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pA[i] = Pf[i * 64];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) gam[rt] = *reinterpret_cast<const f32x4 *>(gt + 16 * rt + 4 * q4);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            r_lo[kb] = *reinterpret_cast<const f32x4 *>(gt + 64 + 32 * kb + 4 * q4);
+            r_hi[kb] = *reinterpret_cast<const f32x4 *>(gt + 64 + 32 * kb + 16 + 4 * q4);
+        }
+        const float gn = gt[128];
+        __builtin_amdgcn_sched_barrier(0);
 
         // state as the B operand (fp16), contraction over d_k
         half8 Sb[4];
@@ -482,49 +567,54 @@ __global__ __launch_bounds__(64) void chain_kernel(PrefillArgs p, Workspace ws)
         f32x4 Vn[4], QS[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            const half4 u = Uf[rt * 64];
-            f32x4 acc = {(float)u[0], (float)u[1], (float)u[2], (float)u[3]};
+            f32x4 acc = {(float)uC[rt][0], (float)uC[rt][1], (float)uC[rt][2], (float)uC[rt][3]};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) acc = mfma16(wA[rt * 4 + kb], Sb[kb], acc);
+            Vn[rt] = acc;
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
             f32x4 qacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                acc = mfma16(Wf[(rt * 4 + kb) * 64], Sb[kb], acc);
-                qacc = mfma16(Qf[(rt * 4 + kb) * 64], Sb[kb], qacc);
-            }
-            Vn[rt] = acc;
+            for (int kb = 0; kb < 4; ++kb) qacc = mfma16(qA[rt * 4 + kb], Sb[kb], qacc);
             QS[rt] = qacc;
         }
         // Vnew as B operands: plain (for P Vnew) and scaled by Gam_n / Gam (for the state)
         half8 Vb[2], Vr[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const f32x4 r_lo = *reinterpret_cast<const f32x4 *>(gt + 64 + 32 * kb + 4 * q4);
-            const f32x4 r_hi = *reinterpret_cast<const f32x4 *>(gt + 64 + 32 * kb + 16 + 4 * q4);
             Vb[kb] = pack_h8(Vn[2 * kb], Vn[2 * kb + 1]);
-            Vr[kb] = pack_h8(Vn[2 * kb] * r_lo, Vn[2 * kb + 1] * r_hi);
+            Vr[kb] = pack_h8(Vn[2 * kb] * r_lo[kb], Vn[2 * kb + 1] * r_hi[kb]);
         }
-        // O = diag(Gam) Q S + P Vnew
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            const f32x4 gam = *reinterpret_cast<const f32x4 *>(gt + 16 * rt + 4 * q4);
-            f32x4 acc = QS[rt] * gam;
-            acc = mfma16(Pf[(rt * 2 + 0) * 64], Vb[0], acc);
-            if (rt >= 2) acc = mfma16(Pf[(rt * 2 + 1) * 64], Vb[1], acc);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int tok = 16 * rt + 4 * q4 + e;
-                if (tok < n)
-                    p.o[((long)(tok0 + tok) * Hv + h) * kD + col] = (uint16_t)f32_to_bf16(acc[e] * p.q_scale);
-            }
-        }
-        // S <- Gam_n S + K^T (r * Vnew)
-        const float gn = gt[128];
+        // S <- Gam_n S + K^T (r * Vnew)   (the dependency chain into the next chunk)
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt) {
             f32x4 acc = S[rt] * gn;
-            acc = mfma16(Kf[(rt * 2 + 0) * 64], Vr[0], acc);
-            acc = mfma16(Kf[(rt * 2 + 1) * 64], Vr[1], acc);
+            acc = mfma16(kA[rt * 2 + 0], Vr[0], acc);
+            acc = mfma16(kA[rt * 2 + 1], Vr[1], acc);
             S[rt] = acc;
         }
+        // O = diag(Gam) Q S + P Vnew, staged through LDS for 16-byte row stores
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            f32x4 acc = QS[rt] * gam[rt];
+            acc = mfma16(pA[rt * 2 + 0], Vb[0], acc);
+            if (rt >= 2) acc = mfma16(pA[rt * 2 + 1], Vb[1], acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ostage[(16 * rt + 4 * q4 + e) * 16 + c16] = (uint16_t)f32_to_bf16(acc[e] * p.q_scale);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane < n) {
+            const uint4 *srow = reinterpret_cast<const uint4 *>(ostage + lane * 16);
+            uint4 *drow = reinterpret_cast<uint4 *>(p.o + ((long)(tok0 + lane) * Hv + h) * kD + 16 * ct);
+            drow[0] = srow[0];
+            drow[1] = srow[1];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
     }
 
 #pragma unroll
@@ -534,7 +624,7 @@ __global__ __launch_bounds__(64) void chain_kernel(PrefillArgs p, Workspace ws)
 
     // carried conv rows: the last three raw rows of the sequence (v channels of
     // head h; the first head of the group also writes the q and k channels)
-    if (p.conv_state_out && ct == 0) {
+    if (p.conv_state_out && cb == 0 && wave == 0) {
         const long C_tot = 2L * Hqk * kD + (long)Hv * kD;
         const int L = si.w, t0 = si.z;
         for (int plane = (j == 0 ? 0 : 2); plane < 3; ++plane) {
@@ -597,23 +687,29 @@ Workspace carve_workspace(void *base, int max_chunks, int N, int Hqk, int Hv)
     return ws;
 }
 
-hipError_t launch_prefill(const PrefillArgs &p, void *workspace, hipStream_t stream)
+hipError_t launch_prefill(const PrefillArgs &p, void *workspace, hipStream_t stream,
+                          hipEvent_t const *events)
 {
     const Workspace ws = carve_workspace(workspace, p.max_chunks, p.N, p.Hqk, p.Hv);
+    hipError_t e;
+    auto mark = [&](int i) { return events ? hipEventRecord(events[i], stream) : hipSuccess; };
+    if ((e = mark(0)) != hipSuccess) return e;
     hipLaunchKernelGGL(setup_kernel, dim3(1), dim3(1024), 0, stream, p, ws);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = mark(1)) != hipSuccess) return e;
     if (p.max_chunks > 0) {
         hipLaunchKernelGGL(prep_kernel, dim3((unsigned)((long)p.max_chunks * p.Hqk)), dim3(kPrepThreads), 0,
                            stream, p, ws);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
+    if ((e = mark(2)) != hipSuccess) return e;
     const int G = p.Hv / p.Hqk;
     const long groups = (long)p.N * p.Hqk;
-    const long blocks = ((groups + 7) / 8) * 64L * G;
-    hipLaunchKernelGGL(chain_kernel, dim3((unsigned)blocks), dim3(64), 0, stream, p, ws);
-    return hipGetLastError();
+    const long blocks = ((groups + 7) / 8) * 8L * G * (8 / kChainWaves);
+    hipLaunchKernelGGL(chain_kernel<kChainWaves>, dim3((unsigned)blocks), dim3(64 * kChainWaves), 0, stream, p,
+                       ws);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return mark(3);
 }
 
 }  // namespace gdn
