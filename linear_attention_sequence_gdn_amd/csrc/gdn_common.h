@@ -21,12 +21,10 @@ __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+// fp32 -> bf16 bits, round to nearest even (gfx950 converts in hardware).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
@@ -35,10 +33,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 
 // ---- scalar activations -----------------------------------------------------
 
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + __expf(-x)); }
-__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+// 1 / (1 + e^-x) and x / (1 + e^-x) with the hardware reciprocal (about 1 ulp)
+__device__ __forceinline__ float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+__device__ __forceinline__ float silu_f(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 // softplus(x) = max(x, 0) + log1p(exp(-|x|))
 __device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.0f) + log1pf(__expf(-fabsf(x))); }
+
+constexpr float kLog2e = 1.4426950408889634f;
 
 // ---- wave reductions (wave64) ----------------------------------------------
 

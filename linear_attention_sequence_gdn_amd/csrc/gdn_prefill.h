@@ -38,6 +38,7 @@ inline int max_chunks_varlen(int N, int T_tot)
 constexpr size_t kFragBytes = 64 * 16;               // one 16x32 fp16 operand
 constexpr size_t kQFragBytes = 16 * kFragBytes;      // q^ of a chunk     [64 x 128]
 constexpr size_t kKFragBytes = 16 * kFragBytes;      // k^T of a chunk    [128 x 64]
+constexpr size_t kKTokFragBytes = 16 * kFragBytes;   // k^ of a chunk     [64 x 128]
 constexpr size_t kWFragBytes = 16 * kFragBytes;      // -W of a chunk     [64 x 128]
 constexpr size_t kUBytes = 64 * 128 * 2;             // U' of a chunk     [64 x 128]
 constexpr size_t kPFragBytes = 8 * kFragBytes;       // P of a chunk      [64 x 64]
@@ -48,7 +49,8 @@ struct Workspace {
     int4 *seq_info;     // [N] {chunk0, nchunks, t0, L}
     int *order;         // [N] sequences, longest first
     uint8_t *qfrag;     // [max_chunks][Hqk]
-    uint8_t *kfrag;     // [max_chunks][Hqk]
+    uint8_t *kfrag;     // [max_chunks][Hqk]  k^T, d-major (sequential pass)
+    uint8_t *ktok;      // [max_chunks][Hqk]  k^, token-major (per-head pass)
     uint8_t *wfrag;     // [max_chunks][Hv]
     uint8_t *ufrag;     // [max_chunks][Hv]
     uint8_t *pfrag;     // [max_chunks][Hv]

@@ -37,7 +37,6 @@ namespace {
 constexpr int kPrepThreads = 256;
 constexpr int kQ_LD = 136;  // fp16 row stride of the token-major q^ / k^ tiles
 constexpr int kT_LD = 72;   // fp16 row stride of 64-token rows (k^T, v^T, T')
-constexpr int kA_LD = 65;   // fp32 row stride of A and its inverse
 
 __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -160,90 +159,75 @@ __global__ __launch_bounds__(1024) void setup_kernel(PrefillArgs p, Workspace ws
 // ---------------------------------------------------------------------------
 // prep: everything that does not depend on the carried state
 // ---------------------------------------------------------------------------
+constexpr int kAL = 68;        // fp32 row stride of A (16-byte aligned rows)
 
-// X_{bi,bj} = -X_{bi,bi} * sum_{k=bj}^{bi-1} A_{bi,k} X_{k,bj}   (16x16 blocks)
-// executed by one wave; M is a 16 x 17 fp32 scratch owned by the wave.
-__device__ __forceinline__ void inv_block_product(const float *As, float *Xs, float *M, int bi, int bj,
-                                                  int lane)
+// Sum over the 64 lanes of each of 16 per-lane values, by recursive halving
+// (reduce-scatter): 17 lane exchanges instead of 16 separate all-reduces.
+// Lanes 4r .. 4r+3 end up holding the total of value r.
+__device__ __forceinline__ float reduce_scatter16(const float (&v)[16], int lane)
 {
-    const int r = lane >> 2, c0 = 4 * (lane & 3);
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int kblk = bj; kblk < bi; ++kblk) {
+    float u[8], w4[4], w2[2];
+    const bool hi32 = lane & 32, hi16 = lane & 16, hi8 = lane & 8, hi4 = lane & 4;
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            const float a = As[(16 * bi + r) * kA_LD + 16 * kblk + m];
-            const float *xr = Xs + (16 * kblk + m) * kA_LD + 16 * bj + c0;
-            acc[0] += a * xr[0];
-            acc[1] += a * xr[1];
-            acc[2] += a * xr[2];
-            acc[3] += a * xr[3];
-        }
+    for (int i = 0; i < 8; ++i) {
+        const float keep = hi32 ? v[8 + i] : v[i], send = hi32 ? v[i] : v[8 + i];
+        u[i] = keep + __shfl_xor(send, 32, 64);
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) M[r * 17 + c0 + e] = acc[e];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    float out[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const float xv = Xs[(16 * bi + r) * kA_LD + 16 * bi + m];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) out[e] -= xv * M[m * 17 + c0 + e];
+    for (int i = 0; i < 4; ++i) {
+        const float keep = hi16 ? u[4 + i] : u[i], send = hi16 ? u[i] : u[4 + i];
+        w4[i] = keep + __shfl_xor(send, 16, 64);
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) Xs[(16 * bi + r) * kA_LD + 16 * bj + c0 + e] = out[e];
+    for (int i = 0; i < 2; ++i) {
+        const float keep = hi8 ? w4[2 + i] : w4[i], send = hi8 ? w4[i] : w4[2 + i];
+        w2[i] = keep + __shfl_xor(send, 8, 64);
+    }
+    float x = (hi4 ? w2[1] : w2[0]) + __shfl_xor(hi4 ? w2[0] : w2[1], 4, 64);
+    x += __shfl_xor(x, 2, 64);
+    x += __shfl_xor(x, 1, 64);
+    return x;
 }
 
-__global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillArgs p, Workspace ws)
+// prepA: per (chunk, QK group) -- conv + SiLU + L2 norm of q and k, written
+// as matrix-core operands: q^ and k^ token-major, k^T d-major.
+__global__ __launch_bounds__(kPrepThreads) void prep_qk_kernel(PrefillArgs p, Workspace ws)
 {
-    // LDS plan (bytes): [0, 34816) q^ and k^ token-major, later A and X;
-    // then k^T, v^T, T', T'Gam, inverse scratch, gates.
-    __shared__ __attribute__((aligned(16))) uint8_t smem[34816 + 2 * 18432 + 2 * 9216 + 3 * 1088 + 512];
-    _Float16 *Qs = reinterpret_cast<_Float16 *>(smem);
-    _Float16 *Ks = Qs + 64 * kQ_LD;
-    float *As = reinterpret_cast<float *>(smem);
-    float *Xs = As + 64 * kA_LD;
-    _Float16 *KTs = reinterpret_cast<_Float16 *>(smem + 34816);
-    _Float16 *VTs = KTs + 128 * kT_LD;
-    _Float16 *Th = VTs + 128 * kT_LD;
-    _Float16 *TGh = Th + 64 * kT_LD;
-    float *Mscr = reinterpret_cast<float *>(smem + 34816 + 2 * 18432 + 2 * 9216);
-    float *s_gam = Mscr + 3 * 272;
-    float *s_beta = s_gam + 64;
-
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int q4 = lane >> 4, c16 = lane & 15;
+    __shared__ __attribute__((aligned(16))) _Float16 Qs[64 * kQ_LD];
+    __shared__ __attribute__((aligned(16))) _Float16 Ks[64 * kQ_LD];
+    __shared__ __attribute__((aligned(16))) _Float16 KTs[128 * kT_LD];
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int c = blockIdx.x / p.Hqk, g = blockIdx.x % p.Hqk;
     const int4 ci = ws.chunk_info[c];
     const int n = ci.z;
     if (n == 0) return;  // empty chunk slot (whole workgroup)
     const int s = ci.x, t0 = ci.y;
     const bool first = ci.w != 0;
-    const int Hqk = p.Hqk, Hv = p.Hv, G = Hv / Hqk;
-    const long C_tot = 2L * Hqk * kD + (long)Hv * kD;
+    const int Hqk = p.Hqk;
+    const long C_tot = 2L * Hqk * kD + (long)p.Hv * kD;
     const uint16_t *hist = (first && p.conv_state_in) ? p.conv_state_in + (long)s * 3 * C_tot : nullptr;
     const int r0 = 16 * wave;
-
-    // ---- 1. q^, k^: conv + SiLU + L2 norm -> LDS (token-major and k^T)
     {
         float z0[16], z1[16];
         const long ldqk = (long)Hqk * kD;
-        const long cq = (long)g * kD, ck = (long)Hqk * kD + (long)g * kD;
 #pragma unroll
         for (int plane = 0; plane < 2; ++plane) {
+            const long ch0 = plane == 0 ? (long)g * kD : (long)Hqk * kD + (long)g * kD;
             const uint16_t *x = (plane == 0 ? p.q : p.k) + (long)t0 * ldqk + (long)g * kD;
-            const long ch0 = plane == 0 ? cq : ck;
-            conv_plane(x, ldqk, n, first, hist ? hist + ch0 : nullptr, C_tot, p.conv_w + ch0 * 4, lane,
-                       r0, z0, z1);
+            conv_plane(x, ldqk, n, first, hist ? hist + ch0 : nullptr, C_tot, p.conv_w + ch0 * 4, lane, r0,
+                       z0, z1);
+            float ss[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ss[i] = z0[i] * z0[i] + z1[i] * z1[i];
+            const float inv_mine = rsqrtf(reduce_scatter16(ss, lane) + 1e-6f);  // row (lane >> 2)
+            _Float16 *dst = plane == 0 ? Qs : Ks;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float ss = wave_sum(z0[i] * z0[i] + z1[i] * z1[i]);
-                const float inv = rsqrtf(ss + 1e-6f);
+                const float inv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inv_mine), 4 * i));
                 const _Float16 h0 = (_Float16)(z0[i] * inv), h1 = (_Float16)(z1[i] * inv);
-                _Float16 *dst = (plane == 0 ? Qs : Ks) + (r0 + i) * kQ_LD + 2 * lane;
-                dst[0] = h0;
-                dst[1] = h1;
+                dst[(r0 + i) * kQ_LD + 2 * lane] = h0;
+                dst[(r0 + i) * kQ_LD + 2 * lane + 1] = h1;
                 if (plane == 1) {
                     KTs[(2 * lane) * kT_LD + r0 + i] = h0;
                     KTs[(2 * lane + 1) * kT_LD + r0 + i] = h1;
@@ -252,183 +236,240 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillArgs p, Works
         }
     }
     __syncthreads();
-
-    // ---- 2. q^ and k^T operands for the sequential pass; K K^T and K Q^T
-    f32x4 kk[4], kq[4];
-    {
-        half8 *qf = reinterpret_cast<half8 *>(ws.qfrag + ((long)c * Hqk + g) * kQFragBytes);
-        half8 *kf = reinterpret_cast<half8 *>(ws.kfrag + ((long)c * Hqk + g) * kKFragBytes);
+    const long gc = (long)c * Hqk + g;
+    half8 *qf = reinterpret_cast<half8 *>(ws.qfrag + gc * kQFragBytes);
+    half8 *kt = reinterpret_cast<half8 *>(ws.ktok + gc * kKTokFragBytes);
+    half8 *kf = reinterpret_cast<half8 *>(ws.kfrag + gc * kKFragBytes);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) qf[(wave * 4 + kb) * 64 + lane] = lds_frag(Qs, kQ_LD, 16 * wave, 32 * kb, lane);
+    for (int kb = 0; kb < 4; ++kb) {
+        qf[(wave * 4 + kb) * 64 + lane] = lds_frag(Qs, kQ_LD, 16 * wave, 32 * kb, lane);
+        kt[(wave * 4 + kb) * 64 + lane] = lds_frag(Ks, kQ_LD, 16 * wave, 32 * kb, lane);
+    }
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr)
+    for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const int rt = 2 * wave + rr;
-                kf[(rt * 2 + kb) * 64 + lane] = lds_frag(KTs, kT_LD, 16 * rt, 32 * kb, lane);
-            }
-        // K K^T: rows 16*wave.., all four column tiles
-        half8 arow[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) arow[kb] = lds_frag(Ks, kQ_LD, 16 * wave, 32 * kb, lane);
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) acc = mfma16(arow[kb], lds_frag(Ks, kQ_LD, 16 * ct, 32 * kb, lane), acc);
-            kk[ct] = acc;
+        for (int kb = 0; kb < 2; ++kb) {
+            const int rt = 2 * wave + rr;
+            kf[(rt * 2 + kb) * 64 + lane] = lds_frag(KTs, kT_LD, 16 * rt, 32 * kb, lane);
         }
-        // K Q^T: column tile `wave` (query tokens), key-token tiles jt <= wave
-        half8 bq[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) bq[kb] = lds_frag(Qs, kQ_LD, 16 * wave, 32 * kb, lane);
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (jt <= wave) {
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb) acc = mfma16(lds_frag(Ks, kQ_LD, 16 * jt, 32 * kb, lane), bq[kb], acc);
-            }
-            kq[jt] = acc;
+}
+
+// Forward substitution for column `lane` of X = (I + A)^-1, A strictly lower
+// (row stride kAL): x_i = delta(i, lane) - sum_{m<i} A[i][m] x_m.  Expanded at
+// compile time so that x stays in registers.
+template <int I, int M0>
+struct SolveDot {
+    static __device__ __forceinline__ void run(float &acc, const float (&x)[64], const float *Arow)
+    {
+        if constexpr (M0 < I) {
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(Arow + M0);
+            if constexpr (M0 + 0 < I) acc -= a[0] * x[M0 + 0];
+            if constexpr (M0 + 1 < I) acc -= a[1] * x[M0 + 1];
+            if constexpr (M0 + 2 < I) acc -= a[2] * x[M0 + 2];
+            if constexpr (M0 + 3 < I) acc -= a[3] * x[M0 + 3];
+            SolveDot<I, M0 + 4>::run(acc, x, Arow);
         }
     }
-    __syncthreads();  // q^ / k^ token-major tiles are dead from here on (A, X reuse them)
+};
+template <int I>
+struct SolveRow {
+    static __device__ __forceinline__ void run(float (&x)[64], const float *As, int lane)
+    {
+        if constexpr (I < 64) {
+            float acc = I == lane ? 1.f : 0.f;
+            SolveDot<I, 0>::run(acc, x, As + I * kAL);
+            x[I] = acc;
+            SolveRow<I + 1>::run(x, As, lane);
+        }
+    }
+};
 
-    // ---- 3. per V head of the group
-    for (int j = 0; j < G; ++j) {
-        const int h = g * G + j;
-        const long hc = (long)c * Hv + h;
-        // gates (wave 0): gam = in-chunk cumulative log decay, beta
-        if (wave == 0) {
-            const bool valid = lane < n;
-            const long ti = (long)(t0 + lane) * Hv + h;
-            const float av = valid ? p.a[ti] : 0.f, bv = valid ? p.b[ti] : 0.f;
-            const float gl = valid ? -p.gate_scale * softplus_f(av) : 0.f;
-            const float be = valid ? sigmoid_f(bv) : 0.f;
-            float gam = gl;
+// prepB: per (chunk, V head) -- gates, conv + SiLU of v, K K^T and K Q^T,
+// A, P, the unit-lower-triangular solve, T', U' = T' V and -W.
+constexpr int kH_LD = 68;  // fp16 row stride of v^T, T', T' diag(Gam) (8-byte aligned rows)
+
+__global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, Workspace ws)
+{
+    __shared__ __attribute__((aligned(16))) float As[64 * kAL];
+    __shared__ __attribute__((aligned(16))) _Float16 VTs[128 * kH_LD];
+    __shared__ __attribute__((aligned(16))) _Float16 Th[64 * kH_LD];
+    __shared__ __attribute__((aligned(16))) _Float16 TGh[64 * kH_LD];
+    __shared__ float s_gam2[64], s_beta[64];
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int q4 = lane >> 4, c16 = lane & 15;
+    const int Hqk = p.Hqk, Hv = p.Hv, G = Hv / Hqk;
+    // block -> (chunk, group, head in group); the G heads of one (chunk, group)
+    // share an XCD, so the q^ / k^ operands they all read come from one L2
+    const int bid = blockIdx.x;
+    const int u = (bid / (8 * G)) * 8 + (bid & 7);
+    const int j = (bid >> 3) % G;
+    if (u >= p.max_chunks * Hqk) return;
+    const int c = u / Hqk, g = u % Hqk;
+    const int h = g * G + j;
+    const int4 ci = ws.chunk_info[c];
+    const int n = ci.z;
+    if (n == 0) return;
+    const int s = ci.x, t0 = ci.y;
+    const bool first = ci.w != 0;
+    const long C_tot = 2L * Hqk * kD + (long)Hv * kD;
+    const uint16_t *hist = (first && p.conv_state_in) ? p.conv_state_in + (long)s * 3 * C_tot : nullptr;
+    const long hc = (long)c * Hv + h, gc = (long)c * Hqk + g;
+    const int r0 = 16 * wave;
+
+    // operands from the q/k pass (straight into registers)
+    const half8 *qf = reinterpret_cast<const half8 *>(ws.qfrag + gc * kQFragBytes) + lane;
+    const half8 *kt = reinterpret_cast<const half8 *>(ws.ktok + gc * kKTokFragBytes) + lane;
+    const half8 *kf = reinterpret_cast<const half8 *>(ws.kfrag + gc * kKFragBytes) + lane;
+    half8 ktA[4][4], kOwn[4], qB[4];
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(gam, off, 64);
-                if (lane >= off) gam += y;
-            }
-            const float gam_n = __shfl(gam, n - 1, 64);
-            s_gam[lane] = gam;
-            s_beta[lane] = be;
-            float *gt = ws.gates + hc * kGateFloats;
-            gt[lane] = __expf(gam);
-            gt[64 + lane] = valid ? __expf(gam_n - gam) : 0.f;
-            if (lane == 0) gt[128] = __expf(gam_n);
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) ktA[rt][kb] = kt[(rt * 4 + kb) * 64];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        kOwn[kb] = kt[(wave * 4 + kb) * 64];
+        qB[kb] = qf[(wave * 4 + kb) * 64];
+    }
+
+    // gates (wave 0): gam = in-chunk cumulative log decay (log2 units), beta
+    if (wave == 0) {
+        const bool valid = lane < n;
+        const long ti = (long)(t0 + lane) * Hv + h;
+        const float av = valid ? p.a[ti] : 0.f, bv = valid ? p.b[ti] : 0.f;
+        const float gl = valid ? -p.gate_scale * kLog2e * softplus_f(av) : 0.f;
+        const float be = valid ? sigmoid_f(bv) : 0.f;
+        float gam = gl;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(gam, off, 64);
+            if (lane >= off) gam += y;
         }
-        // v^ of head h: conv + SiLU -> v^T in LDS
-        {
-            float z0[16], z1[16];
-            const long ldv = (long)Hv * kD;
-            const long cv = 2L * Hqk * kD + (long)h * kD;
-            const uint16_t *x = p.v + (long)t0 * ldv + (long)h * kD;
-            conv_plane(x, ldv, n, first, hist ? hist + cv : nullptr, C_tot, p.conv_w + cv * 4, lane, r0,
-                       z0, z1);
+        const float gam_n = __shfl(gam, n - 1, 64);
+        s_gam2[lane] = gam;
+        s_beta[lane] = be;
+        float *gt = ws.gates + hc * kGateFloats;
+        gt[lane] = __builtin_amdgcn_exp2f(gam);
+        gt[64 + lane] = valid ? __builtin_amdgcn_exp2f(gam_n - gam) : 0.f;
+        if (lane == 0) gt[128] = __builtin_amdgcn_exp2f(gam_n);
+    }
+    // v^ of head h: conv + SiLU -> v^T in LDS
+    {
+        float z0[16], z1[16];
+        const long ldv = (long)Hv * kD;
+        const long cv = 2L * Hqk * kD + (long)h * kD;
+        const uint16_t *xv = p.v + (long)t0 * ldv + (long)h * kD;
+        conv_plane(xv, ldv, n, first, hist ? hist + cv : nullptr, C_tot, p.conv_w + cv * 4, lane, r0, z0, z1);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                VTs[(2 * lane) * kT_LD + r0 + i] = (_Float16)z0[i];
-                VTs[(2 * lane + 1) * kT_LD + r0 + i] = (_Float16)z1[i];
-            }
+        for (int i = 0; i < 16; ++i) {
+            VTs[(2 * lane) * kH_LD + r0 + i] = (_Float16)z0[i];
+            VTs[(2 * lane + 1) * kH_LD + r0 + i] = (_Float16)z1[i];
         }
-        __syncthreads();
-        // A = strict_lower(diag(beta) K K^T * D) -> LDS; P = (K Q^T)^T * D (lower) -> global
-        {
+    }
+    // K K^T (rows 16*wave.., column tiles ct <= wave) and K Q^T (query tile
+    // `wave`, key tiles jt <= wave)
+    f32x4 kk[4], kq[4];
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
+    for (int ct = 0; ct < 4; ++ct) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acq = {0.f, 0.f, 0.f, 0.f};
+        if (ct <= wave) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 16 * wave + 4 * q4 + e, jj = 16 * ct + c16;
-                    As[i * kA_LD + jj] = i > jj ? s_beta[i] * kk[ct][e] * __expf(s_gam[i] - s_gam[jj]) : 0.f;
-                }
-            half8 *pf = reinterpret_cast<half8 *>(ws.pfrag + hc * kPFragBytes);
-            const int i = 16 * wave + c16;
-            const float gi = s_gam[i];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                half8 fr;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int jt = 2 * kb + (e >> 2);
-                    const int jj = 16 * jt + 4 * q4 + (e & 3);
-                    const float val = i >= jj ? kq[jt][e & 3] * __expf(gi - s_gam[jj]) : 0.f;
-                    fr[e] = (_Float16)val;
-                }
-                pf[(wave * 2 + kb) * 64 + lane] = fr;
-            }
-        }
-        __syncthreads();
-        // (I + A)^-1, blocked by 16: diagonal blocks by forward substitution
-        {
-            const int cc = lane & 15;
-            const int bo = 16 * wave;
-            float x[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float acc = i == cc ? 1.f : 0.f;
-#pragma unroll
-                for (int m = 0; m < i; ++m) acc -= As[(bo + i) * kA_LD + bo + m] * x[m];
-                x[i] = acc;
-            }
-            if (lane < 16) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) Xs[(bo + i) * kA_LD + bo + cc] = x[i];
-            }
-        }
-        __syncthreads();
-        if (wave < 3) inv_block_product(As, Xs, Mscr + wave * 272, wave + 1, wave, lane);
-        __syncthreads();
-        if (wave < 2) inv_block_product(As, Xs, Mscr + wave * 272, wave + 2, wave, lane);
-        __syncthreads();
-        if (wave == 0) inv_block_product(As, Xs, Mscr, 3, 0, lane);
-        __syncthreads();
-        // T' = X diag(beta), T'Gam = X diag(beta Gam) (fp16, lower)
-        for (int e = t; e < 64 * 64; e += kPrepThreads) {
-            const int i = e >> 6, jj = e & 63;
-            const float tv = jj <= i ? Xs[i * kA_LD + jj] * s_beta[jj] : 0.f;
-            Th[i * kT_LD + jj] = (_Float16)tv;
-            TGh[i * kT_LD + jj] = (_Float16)(tv * __expf(s_gam[jj]));
-        }
-        __syncthreads();
-        // U' = T' V: column tiles 2*wave, 2*wave+1; stored in accumulator order
-        {
-            half4 *uf = reinterpret_cast<half4 *>(ws.ufrag + hc * kUBytes);
-#pragma unroll
-            for (int cti = 0; cti < 2; ++cti) {
-                const int ct = 2 * wave + cti;
-                const half8 b0 = lds_frag(VTs, kT_LD, 16 * ct, 0, lane);
-                const half8 b1 = lds_frag(VTs, kT_LD, 16 * ct, 32, lane);
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                    acc = mfma16(lds_frag(Th, kT_LD, 16 * rt, 0, lane), b0, acc);
-                    if (rt >= 2) acc = mfma16(lds_frag(Th, kT_LD, 16 * rt, 32, lane), b1, acc);
-                    half4 hv;
-                    hv[0] = (_Float16)acc[0]; hv[1] = (_Float16)acc[1];
-                    hv[2] = (_Float16)acc[2]; hv[3] = (_Float16)acc[3];
-                    uf[(ct * 4 + rt) * 64 + lane] = hv;
-                }
+            for (int kb = 0; kb < 4; ++kb) {
+                acc = mfma16(kOwn[kb], ktA[ct][kb], acc);
+                acq = mfma16(ktA[ct][kb], qB[kb], acq);
             }
         }
-        // W^T = K^T diag(Gam) T'^T: token tile `wave`, all eight d tiles; -W stored as A operand
-        {
-            half8 *wf = reinterpret_cast<half8 *>(ws.wfrag + hc * kWFragBytes);
-            const half8 b0 = lds_frag(TGh, kT_LD, 16 * wave, 0, lane);
-            const half8 b1 = lds_frag(TGh, kT_LD, 16 * wave, 32, lane);
-            f32x4 wt[8];
+        kk[ct] = acc;
+        kq[ct] = acq;
+    }
+    __syncthreads();
+    // A = strict_lower(diag(beta) K K^T * D) -> LDS; P = (K Q^T)^T * D (lower) -> global
+    {
 #pragma unroll
-            for (int rt = 0; rt < 8; ++rt) {
+        for (int ct = 0; ct < 4; ++ct) {
+            if (ct > wave) continue;
+            const int jj = 16 * ct + c16;
+            const float gj = s_gam2[jj];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * wave + 4 * q4 + e;
+                if (i > jj) As[i * kAL + jj] = s_beta[i] * kk[ct][e] * __builtin_amdgcn_exp2f(s_gam2[i] - gj);
+            }
+        }
+        half8 *pf = reinterpret_cast<half8 *>(ws.pfrag + hc * kPFragBytes);
+        const int i = 16 * wave + c16;
+        const float gi = s_gam2[i];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            half8 fr;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int jt = 2 * kb + (e >> 2);
+                const int jj = 16 * jt + 4 * q4 + (e & 3);
+                float val = 0.f;
+                if (jt <= wave && i >= jj) val = kq[jt][e & 3] * __builtin_amdgcn_exp2f(gi - s_gam2[jj]);
+                fr[e] = (_Float16)val;
+            }
+            pf[(wave * 2 + kb) * 64 + lane] = fr;
+        }
+    }
+    __syncthreads();
+    // (I + A) X = I by forward substitution (wave 0; lane = column of X, X in
+    // registers), then T' = X diag(beta) and T' diag(Gam) into LDS
+    if (wave == 0) {
+        float x[64];
+        SolveRow<0>::run(x, As, lane);
+        const float bc = s_beta[lane];
+        const float gcl = bc * __builtin_amdgcn_exp2f(s_gam2[lane]);
+#pragma unroll
+        for (int i = 0; i < 64; ++i) {
+            Th[i * kH_LD + lane] = (_Float16)(x[i] * bc);
+            TGh[i * kH_LD + lane] = (_Float16)(x[i] * gcl);
+        }
+    }
+    __syncthreads();
+    // U' = T' V: column tiles 2*wave, 2*wave+1; stored in accumulator order
+    {
+        half4 *uf = reinterpret_cast<half4 *>(ws.ufrag + hc * kUBytes);
+        half8 ta[4][2];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            ta[rt][0] = lds_frag(Th, kH_LD, 16 * rt, 0, lane);
+            ta[rt][1] = lds_frag(Th, kH_LD, 16 * rt, 32, lane);
+        }
+#pragma unroll
+        for (int cti = 0; cti < 2; ++cti) {
+            const int ct = 2 * wave + cti;
+            const half8 b0 = lds_frag(VTs, kH_LD, 16 * ct, 0, lane);
+            const half8 b1 = lds_frag(VTs, kH_LD, 16 * ct, 32, lane);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mfma16(lds_frag(KTs, kT_LD, 16 * rt, 0, lane), b0, acc);
-                if (wave >= 2) acc = mfma16(lds_frag(KTs, kT_LD, 16 * rt, 32, lane), b1, acc);
-                wt[rt] = acc;
+                acc = mfma16(ta[rt][0], b0, acc);
+                if (rt >= 2) acc = mfma16(ta[rt][1], b1, acc);
+                half4 hv;
+                hv[0] = (_Float16)acc[0]; hv[1] = (_Float16)acc[1];
+                hv[2] = (_Float16)acc[2]; hv[3] = (_Float16)acc[3];
+                uf[(ct * 4 + rt) * 64 + lane] = hv;
             }
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) wf[(wave * 4 + kb) * 64 + lane] = pack_h8(-wt[2 * kb], -wt[2 * kb + 1]);
         }
-        __syncthreads();
+    }
+    // W^T = K^T diag(Gam) T'^T: token tile `wave`, all eight d tiles; -W stored as A operand
+    {
+        half8 *wf = reinterpret_cast<half8 *>(ws.wfrag + hc * kWFragBytes);
+        const half8 b0 = lds_frag(TGh, kH_LD, 16 * wave, 0, lane);
+        const half8 b1 = lds_frag(TGh, kH_LD, 16 * wave, 32, lane);
+        f32x4 wt[8];
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mfma16(kf[(rt * 2 + 0) * 64], b0, acc);
+            if (wave >= 2) acc = mfma16(kf[(rt * 2 + 1) * 64], b1, acc);
+            wt[rt] = acc;
+        }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) wf[(wave * 4 + kb) * 64 + lane] = pack_h8(-wt[2 * kb], -wt[2 * kb + 1]);
     }
 }
 
@@ -534,7 +575,7 @@ void chain_kernel(PrefillArgs p, Workspace ws)
         const int n = min(kChunk, si.w - cc * kChunk);
         const int tok0 = si.z + cc * kChunk;
 
-        // every operand of this chunk into registers first (one LDS round trip)
+        // operands of the first products (W, q^, U', gates) into registers
         half8 wA[16], qA[16], kA[16], pA[8];
         half4 uC[4];
         f32x4 gam[4], r_lo[2], r_hi[2];
@@ -544,10 +585,6 @@ void chain_kernel(PrefillArgs p, Workspace ws)
         for (int i = 0; i < 16; ++i) qA[i] = Qf[i * 64];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) uC[rt] = Uf[rt * 64];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) kA[i] = Kf[i * 64];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pA[i] = Pf[i * 64];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) gam[rt] = *reinterpret_cast<const f32x4 *>(gt + 16 * rt + 4 * q4);
 #pragma unroll
@@ -563,21 +600,29 @@ void chain_kernel(PrefillArgs p, Workspace ws)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) Sb[kb] = pack_h8(S[2 * kb], S[2 * kb + 1]);
 
-        // Vnew = U' - W S ;  QS = Q S
+        // Vnew = U' - W S ;  QS = Q S   (eight independent accumulators per
+        // k-block); the k^T and P reads are issued behind the first k-block
         f32x4 Vn[4], QS[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            f32x4 acc = {(float)uC[rt][0], (float)uC[rt][1], (float)uC[rt][2], (float)uC[rt][3]};
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) acc = mfma16(wA[rt * 4 + kb], Sb[kb], acc);
-            Vn[rt] = acc;
+            Vn[rt] = f32x4{(float)uC[rt][0], (float)uC[rt][1], (float)uC[rt][2], (float)uC[rt][3]};
+            QS[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            f32x4 qacc = {0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) qacc = mfma16(qA[rt * 4 + kb], Sb[kb], qacc);
-            QS[rt] = qacc;
+            for (int rt = 0; rt < 4; ++rt) {
+                Vn[rt] = mfma16(wA[rt * 4 + kb], Sb[kb], Vn[rt]);
+                QS[rt] = mfma16(qA[rt * 4 + kb], Sb[kb], QS[rt]);
+            }
+            if (kb == 0) {
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) kA[i] = Kf[i * 64];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pA[i] = Pf[i * 64];
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         // Vnew as B operands: plain (for P Vnew) and scaled by Gam_n / Gam (for the state)
         half8 Vb[2], Vr[2];
@@ -588,12 +633,11 @@ void chain_kernel(PrefillArgs p, Workspace ws)
         }
         // S <- Gam_n S + K^T (r * Vnew)   (the dependency chain into the next chunk)
 #pragma unroll
-        for (int rt = 0; rt < 8; ++rt) {
-            f32x4 acc = S[rt] * gn;
-            acc = mfma16(kA[rt * 2 + 0], Vr[0], acc);
-            acc = mfma16(kA[rt * 2 + 1], Vr[1], acc);
-            S[rt] = acc;
-        }
+        for (int rt = 0; rt < 8; ++rt) S[rt] = S[rt] * gn;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int rt = 0; rt < 8; ++rt) S[rt] = mfma16(kA[rt * 2 + kb], Vr[kb], S[rt]);
         // O = diag(Gam) Q S + P Vnew, staged through LDS for 16-byte row stores
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
@@ -658,6 +702,7 @@ size_t prefill_workspace_bytes(int max_chunks, int N, int Hqk, int Hv)
     total += align256((size_t)N * sizeof(int));
     total += align256(C * Hqk * kQFragBytes);
     total += align256(C * Hqk * kKFragBytes);
+    total += align256(C * Hqk * kKTokFragBytes);
     total += align256(C * Hv * kWFragBytes);
     total += align256(C * Hv * kUBytes);
     total += align256(C * Hv * kPFragBytes);
@@ -680,6 +725,7 @@ Workspace carve_workspace(void *base, int max_chunks, int N, int Hqk, int Hv)
     ws.order = reinterpret_cast<int *>(take((size_t)N * sizeof(int)));
     ws.qfrag = take(C * Hqk * kQFragBytes);
     ws.kfrag = take(C * Hqk * kKFragBytes);
+    ws.ktok = take(C * Hqk * kKTokFragBytes);
     ws.wfrag = take(C * Hv * kWFragBytes);
     ws.ufrag = take(C * Hv * kUBytes);
     ws.pfrag = take(C * Hv * kPFragBytes);
@@ -698,8 +744,11 @@ hipError_t launch_prefill(const PrefillArgs &p, void *workspace, hipStream_t str
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(1)) != hipSuccess) return e;
     if (p.max_chunks > 0) {
-        hipLaunchKernelGGL(prep_kernel, dim3((unsigned)((long)p.max_chunks * p.Hqk)), dim3(kPrepThreads), 0,
-                           stream, p, ws);
+        const long units = (long)p.max_chunks * p.Hqk;
+        hipLaunchKernelGGL(prep_qk_kernel, dim3((unsigned)units), dim3(kPrepThreads), 0, stream, p, ws);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const long blocks = ((units + 7) / 8) * 8L * (p.Hv / p.Hqk);
+        hipLaunchKernelGGL(prep_head_kernel, dim3((unsigned)blocks), dim3(kPrepThreads), 0, stream, p, ws);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if ((e = mark(2)) != hipSuccess) return e;
