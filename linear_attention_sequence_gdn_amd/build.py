@@ -22,6 +22,9 @@ HIPCC_FLAGS = [
     "-shared",
     # keep the compiler from forming packed-fp32 vector instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep matrix-core accumulators in ordinary VGPRs, so that the vector
+    # ALU can scale them without copies to and from the accumulator file
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
 ]
 

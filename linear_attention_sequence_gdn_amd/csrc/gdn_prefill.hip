@@ -349,8 +349,9 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
         const float gam_n = __shfl(gam, n - 1, 64);
         s_gam2[lane] = gam;
         s_beta[lane] = be;
+        // slot 0: q_scale * Gam (only the output uses it); slot 1: Gam_n / Gam; slot 2: Gam_n
         float *gt = ws.gates + hc * kGateFloats;
-        gt[lane] = __builtin_amdgcn_exp2f(gam);
+        gt[lane] = p.q_scale * __builtin_amdgcn_exp2f(gam);
         gt[64 + lane] = valid ? __builtin_amdgcn_exp2f(gam_n - gam) : 0.f;
         if (lane == 0) gt[128] = __builtin_amdgcn_exp2f(gam_n);
     }
@@ -408,7 +409,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
                 const int jt = 2 * kb + (e >> 2);
                 const int jj = 16 * jt + 4 * q4 + (e & 3);
                 float val = 0.f;
-                if (jt <= wave && i >= jj) val = kq[jt][e & 3] * __builtin_amdgcn_exp2f(gi - s_gam2[jj]);
+                if (jt <= wave && i >= jj)
+                    val = p.q_scale * kq[jt][e & 3] * __builtin_amdgcn_exp2f(gi - s_gam2[jj]);
                 fr[e] = (_Float16)val;
             }
             pf[(wave * 2 + kb) * 64 + lane] = fr;
@@ -492,18 +494,26 @@ struct ChainStage {
     static constexpr int kBytes = kBlocks * 1024;
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Issue the direct-to-LDS loads of chunk c into `stage`.  Every region is a
 // whole number of 1-KiB blocks; wave w (uniform) moves blocks w, w+NW, ... of
-// each region (lane l: bytes 16l .. 16l+15 of a block).
-template <int NW, int kBlocks>
-__device__ __forceinline__ void issue_region(const uint8_t *src, uint8_t *dst, int wave)
+// each region (lane l: bytes 16l .. 16l+15 of a block).  Buffer loads carry
+// the block offset in a scalar register, so issuing costs no vector ALU work.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t region_rsrc(const void *base)
 {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, 0x00020000);
+}
+
+template <int NW, int kBlocks>
+__device__ __forceinline__ void issue_region(const void *src, uint8_t *dst, int wave, int lane)
+{
+    const __amdgpu_buffer_rsrc_t r = region_rsrc(src);
 #pragma unroll
     for (int i = 0; i < kBlocks / NW; ++i) {
         const int blk = i * NW + wave;
-        __builtin_amdgcn_global_load_lds(src + blk * 1024, (lds_void *)(dst + blk * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(dst + blk * 1024), 16, lane * 16, blk * 1024, 0, 0);
     }
 }
 
@@ -513,14 +523,14 @@ __device__ __forceinline__ void chain_issue(const Workspace &ws, uint8_t *stage,
 {
     using St = ChainStage<NW>;
     const long hc = c * Hv + h, gc = c * Hqk + g;
-    issue_region<NW, 16>(ws.wfrag + hc * kWFragBytes + lane * 16, stage + St::kW, wave);
-    issue_region<NW, 16>(ws.qfrag + gc * kQFragBytes + lane * 16, stage + St::kQ, wave);
-    issue_region<NW, 16>(ws.kfrag + gc * kKFragBytes + lane * 16, stage + St::kK, wave);
-    issue_region<NW, 8>(ws.pfrag + hc * kPFragBytes + lane * 16, stage + St::kP, wave);
-    issue_region<NW, 2 * NW>(ws.ufrag + hc * kUBytes + (long)cb * NW * 2048 + lane * 16, stage + St::kU, wave);
+    issue_region<NW, 16>(ws.wfrag + hc * kWFragBytes, stage + St::kW, wave, lane);
+    issue_region<NW, 16>(ws.qfrag + gc * kQFragBytes, stage + St::kQ, wave, lane);
+    issue_region<NW, 16>(ws.kfrag + gc * kKFragBytes, stage + St::kK, wave, lane);
+    issue_region<NW, 8>(ws.pfrag + hc * kPFragBytes, stage + St::kP, wave, lane);
+    issue_region<NW, 2 * NW>(ws.ufrag + hc * kUBytes + (long)cb * NW * 2048, stage + St::kU, wave, lane);
     if (wave == 0)
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t *>(ws.gates + hc * kGateFloats) + lane * 16,
-                                         (lds_void *)(stage + St::kG), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(region_rsrc(ws.gates + hc * kGateFloats),
+                                                 (lds_void_t *)(stage + St::kG), 16, lane * 16, 0, 0, 0);
 }
 
 template <int NW>
@@ -575,78 +585,68 @@ void chain_kernel(PrefillArgs p, Workspace ws)
         const int n = min(kChunk, si.w - cc * kChunk);
         const int tok0 = si.z + cc * kChunk;
 
-        // operands of the first products (W, q^, U', gates) into registers
-        half8 wA[16], qA[16], kA[16], pA[8];
-        half4 uC[4];
-        f32x4 gam[4], r_lo[2], r_hi[2];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) wA[i] = Wf[i * 64];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) qA[i] = Qf[i * 64];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) uC[rt] = Uf[rt * 64];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) gam[rt] = *reinterpret_cast<const f32x4 *>(gt + 16 * rt + 4 * q4);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            r_lo[kb] = *reinterpret_cast<const f32x4 *>(gt + 64 + 32 * kb + 4 * q4);
-            r_hi[kb] = *reinterpret_cast<const f32x4 *>(gt + 64 + 32 * kb + 16 + 4 * q4);
-        }
-        const float gn = gt[128];
-        __builtin_amdgcn_sched_barrier(0);
-
         // state as the B operand (fp16), contraction over d_k
         half8 Sb[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) Sb[kb] = pack_h8(S[2 * kb], S[2 * kb + 1]);
 
         // Vnew = U' - W S ;  QS = Q S   (eight independent accumulators per
-        // k-block); the k^T and P reads are issued behind the first k-block
+        // k-block, operands read one k-block ahead)
         f32x4 Vn[4], QS[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            Vn[rt] = f32x4{(float)uC[rt][0], (float)uC[rt][1], (float)uC[rt][2], (float)uC[rt][3]};
+            const half4 u = Uf[rt * 64];
+            Vn[rt] = f32x4{(float)u[0], (float)u[1], (float)u[2], (float)u[3]};
             QS[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        half8 wA[4], qA[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            wA[rt] = Wf[(rt * 4) * 64];
+            qA[rt] = Qf[(rt * 4) * 64];
         }
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
+            half8 wN[4], qN[4];
+            if (kb < 3) {
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    wN[rt] = Wf[(rt * 4 + kb + 1) * 64];
+                    qN[rt] = Qf[(rt * 4 + kb + 1) * 64];
+                }
+            }
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                Vn[rt] = mfma16(wA[rt * 4 + kb], Sb[kb], Vn[rt]);
-                QS[rt] = mfma16(qA[rt * 4 + kb], Sb[kb], QS[rt]);
+                Vn[rt] = mfma16(wA[rt], Sb[kb], Vn[rt]);
+                QS[rt] = mfma16(qA[rt], Sb[kb], QS[rt]);
             }
-            if (kb == 0) {
-                __builtin_amdgcn_sched_barrier(0);
+            if (kb < 3) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) kA[i] = Kf[i * 64];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) pA[i] = Pf[i * 64];
-                __builtin_amdgcn_sched_barrier(0);
+                for (int rt = 0; rt < 4; ++rt) {
+                    wA[rt] = wN[rt];
+                    qA[rt] = qN[rt];
+                }
             }
         }
         // Vnew as B operands: plain (for P Vnew) and scaled by Gam_n / Gam (for the state)
         half8 Vb[2], Vr[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+            const f32x4 r_lo = *reinterpret_cast<const f32x4 *>(gt + 64 + 32 * kb + 4 * q4);
+            const f32x4 r_hi = *reinterpret_cast<const f32x4 *>(gt + 64 + 32 * kb + 16 + 4 * q4);
             Vb[kb] = pack_h8(Vn[2 * kb], Vn[2 * kb + 1]);
-            Vr[kb] = pack_h8(Vn[2 * kb] * r_lo[kb], Vn[2 * kb + 1] * r_hi[kb]);
+            Vr[kb] = pack_h8(Vn[2 * kb] * r_lo, Vn[2 * kb + 1] * r_hi);
         }
-        // S <- Gam_n S + K^T (r * Vnew)   (the dependency chain into the next chunk)
-#pragma unroll
-        for (int rt = 0; rt < 8; ++rt) S[rt] = S[rt] * gn;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int rt = 0; rt < 8; ++rt) S[rt] = mfma16(kA[rt * 2 + kb], Vr[kb], S[rt]);
-        // O = diag(Gam) Q S + P Vnew, staged through LDS for 16-byte row stores
+        // O = q_scale (diag(Gam) Q S + P Vnew) (q_scale is folded into Gam and
+        // P), staged through LDS for 16-byte row stores
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            f32x4 acc = QS[rt] * gam[rt];
-            acc = mfma16(pA[rt * 2 + 0], Vb[0], acc);
-            if (rt >= 2) acc = mfma16(pA[rt * 2 + 1], Vb[1], acc);
+            const f32x4 gam = *reinterpret_cast<const f32x4 *>(gt + 16 * rt + 4 * q4);
+            f32x4 acc = QS[rt] * gam;
+            acc = mfma16(Pf[(rt * 2 + 0) * 64], Vb[0], acc);
+            if (rt >= 2) acc = mfma16(Pf[(rt * 2 + 1) * 64], Vb[1], acc);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                ostage[(16 * rt + 4 * q4 + e) * 16 + c16] = (uint16_t)f32_to_bf16(acc[e] * p.q_scale);
+            for (int e = 0; e < 4; ++e) ostage[(16 * rt + 4 * q4 + e) * 16 + c16] = (uint16_t)f32_to_bf16(acc[e]);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -657,6 +657,15 @@ void chain_kernel(PrefillArgs p, Workspace ws)
             drow[0] = srow[0];
             drow[1] = srow[1];
         }
+        // S <- Gam_n S + K^T (r * Vnew): the dependency into the next chunk,
+        // last so that its matrix-core work overlaps the next chunk's wait
+        const float gn = gt[128];
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt) S[rt] = S[rt] * gn;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int rt = 0; rt < 8; ++rt) S[rt] = mfma16(Kf[(rt * 2 + kb) * 64], Vr[kb], S[rt]);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
     }
