@@ -40,6 +40,15 @@ constexpr int kT_LD = 72;   // fp16 row stride of 64-token rows (k^T, v^T, T')
 
 __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// raw buffer resource over `base` (offsets are bounds-checked against 2^31 - 1)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t region_rsrc(const void *base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, 0x00020000);
+}
+
 // ---------------------------------------------------------------------------
 // operand loaders
 // ---------------------------------------------------------------------------
@@ -254,47 +263,73 @@ __global__ __launch_bounds__(kPrepThreads) void prep_qk_kernel(PrefillArgs p, Wo
         }
 }
 
-// Forward substitution for column `lane` of X = (I + A)^-1, A strictly lower
-// (row stride kAL): x_i = delta(i, lane) - sum_{m<i} A[i][m] x_m.  Expanded at
-// compile time so that x stays in registers.
+// Forward substitution for column c of the inverse of a 16 x 16 unit
+// lower-triangular block I + A (A strictly lower, row stride kAL):
+// y_i = delta(i, c) - sum_{m<i} A[i][m] y_m.  Expanded at compile time so that
+// y stays in registers.
 template <int I, int M0>
-struct SolveDot {
-    static __device__ __forceinline__ void run(float &acc, const float (&x)[64], const float *Arow)
+struct SolveDot16 {
+    static __device__ __forceinline__ void run(float &acc, const float (&y)[16], const float *Arow)
     {
         if constexpr (M0 < I) {
             const f32x4 a = *reinterpret_cast<const f32x4 *>(Arow + M0);
-            if constexpr (M0 + 0 < I) acc -= a[0] * x[M0 + 0];
-            if constexpr (M0 + 1 < I) acc -= a[1] * x[M0 + 1];
-            if constexpr (M0 + 2 < I) acc -= a[2] * x[M0 + 2];
-            if constexpr (M0 + 3 < I) acc -= a[3] * x[M0 + 3];
-            SolveDot<I, M0 + 4>::run(acc, x, Arow);
+            if constexpr (M0 + 0 < I) acc -= a[0] * y[M0 + 0];
+            if constexpr (M0 + 1 < I) acc -= a[1] * y[M0 + 1];
+            if constexpr (M0 + 2 < I) acc -= a[2] * y[M0 + 2];
+            if constexpr (M0 + 3 < I) acc -= a[3] * y[M0 + 3];
+            SolveDot16<I, M0 + 4>::run(acc, y, Arow);
         }
     }
 };
 template <int I>
-struct SolveRow {
-    static __device__ __forceinline__ void run(float (&x)[64], const float *As, int lane)
+struct SolveRow16 {
+    static __device__ __forceinline__ void run(float (&y)[16], const float *A, int c)
     {
-        if constexpr (I < 64) {
-            float acc = I == lane ? 1.f : 0.f;
-            SolveDot<I, 0>::run(acc, x, As + I * kAL);
-            x[I] = acc;
-            SolveRow<I + 1>::run(x, As, lane);
+        if constexpr (I < 16) {
+            float acc = I == c ? 1.f : 0.f;
+            SolveDot16<I, 0>::run(acc, y, A + I * kAL);
+            y[I] = acc;
+            SolveRow16<I + 1>::run(y, A, c);
         }
     }
 };
 
+// acc += A_blk @ B_blk for 16 x 16 fp32 blocks of row-major LDS matrices, on
+// the fp32 matrix cores (four 16x16x4 steps).  Lane l supplies A[l%16][k] and
+// B[k][l%16] for k = 4kb + l/16; acc is in accumulator layout.
+__device__ __forceinline__ f32x4 mm16_f32(const float *Ab, int lda, const float *Bb, int ldb, f32x4 acc, int lane)
+{
+    const int r = lane & 15, k = lane >> 4;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Ab[r * lda + 4 * kb + k], Bb[(4 * kb + k) * ldb + r], acc, 0, 0, 0);
+    return acc;
+}
+__device__ __forceinline__ void st16_f32(float *Db, int ldd, f32x4 v, int lane)
+{
+    const int c = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Db[(4 * q + e) * ldd + c] = v[e];
+}
+
 // prepB: per (chunk, V head) -- gates, conv + SiLU of v, K K^T and K Q^T,
-// A, P, the unit-lower-triangular solve, T', U' = T' V and -W.
+// A, P, the unit-lower-triangular inverse, T', U' = T' V and -W.
 constexpr int kH_LD = 68;  // fp16 row stride of v^T, T', T' diag(Gam) (8-byte aligned rows)
 
 __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, Workspace ws)
 {
-    __shared__ __attribute__((aligned(16))) float As[64 * kAL];
+    // LDS plan: [F] k^ / q^ operands (20 KiB), later X = (I+A)^-1 (fp32);
+    //           [A] A (fp32), later T' and T' diag(Gam) (fp16); v^T; scratch; gates
+    __shared__ __attribute__((aligned(16))) uint8_t regF[20 * 1024];
+    __shared__ __attribute__((aligned(16))) uint8_t regA[64 * kAL * 4];
     __shared__ __attribute__((aligned(16))) _Float16 VTs[128 * kH_LD];
-    __shared__ __attribute__((aligned(16))) _Float16 Th[64 * kH_LD];
-    __shared__ __attribute__((aligned(16))) _Float16 TGh[64 * kH_LD];
+    __shared__ __attribute__((aligned(16))) float Msc[3][256];
     __shared__ float s_gam2[64], s_beta[64];
+    const half8 *Fk = reinterpret_cast<const half8 *>(regF);             // k^ tok-major: [rt*4+kb][lane]
+    float *Xs = reinterpret_cast<float *>(regF);
+    float *As = reinterpret_cast<float *>(regA);
+    _Float16 *Th = reinterpret_cast<_Float16 *>(regA);
+    _Float16 *TGh = Th + 64 * kH_LD;
 
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -318,19 +353,26 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
     const long hc = (long)c * Hv + h, gc = (long)c * Hqk + g;
     const int r0 = 16 * wave;
 
-    // operands from the q/k pass (straight into registers)
-    const half8 *qf = reinterpret_cast<const half8 *>(ws.qfrag + gc * kQFragBytes) + lane;
-    const half8 *kt = reinterpret_cast<const half8 *>(ws.ktok + gc * kKTokFragBytes) + lane;
-    const half8 *kf = reinterpret_cast<const half8 *>(ws.kfrag + gc * kKFragBytes) + lane;
-    half8 ktA[4][4], kOwn[4], qB[4];
+    // operands from the q/k pass: k^ (16 KiB) and this tile's... q^ row tile
+    // `wave` is only needed by this wave, k^ by all: k^ into LDS, q^ and the
+    // k^T rows this wave multiplies into registers
+    {
+        const __amdgpu_buffer_rsrc_t rk = region_rsrc(ws.ktok + gc * kKTokFragBytes);
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+        for (int i = 0; i < 4; ++i) {
+            const int blk = i * 4 + wave;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t *)(regF + blk * 1024), 16, lane * 16, blk * 1024, 0, 0);
+        }
+    }
+    half8 qB[4], kT[4];
+    {
+        const half8 *qf = reinterpret_cast<const half8 *>(ws.qfrag + gc * kQFragBytes) + lane;
+        const half8 *kf = reinterpret_cast<const half8 *>(ws.kfrag + gc * kKFragBytes) + lane;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) ktA[rt][kb] = kt[(rt * 4 + kb) * 64];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        kOwn[kb] = kt[(wave * 4 + kb) * 64];
-        qB[kb] = qf[(wave * 4 + kb) * 64];
+        for (int kb = 0; kb < 4; ++kb) {
+            qB[kb] = qf[(wave * 4 + kb) * 64];
+            kT[kb] = kf[(wave * 4 + kb) * 64];  // k^T row tiles 2w, 2w+1, k-blocks 0..1
+        }
     }
 
     // gates (wave 0): gam = in-chunk cumulative log decay (log2 units), beta
@@ -368,23 +410,30 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
             VTs[(2 * lane + 1) * kH_LD + r0 + i] = (_Float16)z1[i];
         }
     }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     // K K^T (rows 16*wave.., column tiles ct <= wave) and K Q^T (query tile
     // `wave`, key tiles jt <= wave)
     f32x4 kk[4], kq[4];
+    {
+        half8 kOwn[4];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acq = {0.f, 0.f, 0.f, 0.f};
-        if (ct <= wave) {
+        for (int kb = 0; kb < 4; ++kb) kOwn[kb] = Fk[(wave * 4 + kb) * 64 + lane];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                acc = mfma16(kOwn[kb], ktA[ct][kb], acc);
-                acq = mfma16(ktA[ct][kb], qB[kb], acq);
+        for (int ct = 0; ct < 4; ++ct) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acq = {0.f, 0.f, 0.f, 0.f};
+            if (ct <= wave) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    const half8 kc = Fk[(ct * 4 + kb) * 64 + lane];
+                    acc = mfma16(kOwn[kb], kc, acc);
+                    acq = mfma16(kc, qB[kb], acq);
+                }
             }
+            kk[ct] = acc;
+            kq[ct] = acq;
         }
-        kk[ct] = acc;
-        kq[ct] = acq;
     }
-    __syncthreads();
     // A = strict_lower(diag(beta) K K^T * D) -> LDS; P = (K Q^T)^T * D (lower) -> global
     {
 #pragma unroll
@@ -417,18 +466,43 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
         }
     }
     __syncthreads();
-    // (I + A) X = I by forward substitution (wave 0; lane = column of X, X in
-    // registers), then T' = X diag(beta) and T' diag(Gam) into LDS
-    if (wave == 0) {
-        float x[64];
-        SolveRow<0>::run(x, As, lane);
-        const float bc = s_beta[lane];
-        const float gcl = bc * __builtin_amdgcn_exp2f(s_gam2[lane]);
+    // X = (I + A)^-1, blocked by 16: diagonal blocks by forward substitution
+    // (wave b, block b), then the blocks below the diagonal level by level,
+    //   X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj,
+    // on the fp32 matrix cores
+    {
+        float y[16];
+        const int bo = 16 * wave;
+        SolveRow16<0>::run(y, As + bo * kAL + bo, c16);
+        if (lane < 16) {
 #pragma unroll
-        for (int i = 0; i < 64; ++i) {
-            Th[i * kH_LD + lane] = (_Float16)(x[i] * bc);
-            TGh[i * kH_LD + lane] = (_Float16)(x[i] * gcl);
+            for (int i = 0; i < 16; ++i) Xs[(bo + i) * kAL + bo + c16] = y[i];
         }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int lvl = 1; lvl <= 3; ++lvl) {
+        if (wave < 4 - lvl) {
+            const int bi = wave + lvl, bj = wave;
+            f32x4 m = {0.f, 0.f, 0.f, 0.f};
+            for (int bk = bj; bk < bi; ++bk)
+                m = mm16_f32(As + 16 * bi * kAL + 16 * bk, kAL, Xs + 16 * bk * kAL + 16 * bj, kAL, m, lane);
+            st16_f32(Msc[wave], 16, m, lane);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            x = mm16_f32(Xs + 16 * bi * kAL + 16 * bi, kAL, Msc[wave], 16, x, lane);
+            st16_f32(Xs + 16 * bi * kAL + 16 * bj, kAL, -x, lane);
+        }
+        __syncthreads();
+    }
+    // T' = X diag(beta) and T' diag(Gam) (fp16, lower), over A's storage
+    for (int e = t; e < 64 * 64; e += kPrepThreads) {
+        const int i = e >> 6, jj = e & 63;
+        const float tv = jj <= i ? Xs[i * kAL + jj] * s_beta[jj] : 0.f;
+        Th[i * kH_LD + jj] = (_Float16)tv;
+        TGh[i * kH_LD + jj] = (_Float16)(tv * __builtin_amdgcn_exp2f(s_gam2[jj]));
     }
     __syncthreads();
     // U' = T' V: column tiles 2*wave, 2*wave+1; stored in accumulator order
@@ -457,229 +531,250 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
             }
         }
     }
-    // W^T = K^T diag(Gam) T'^T: token tile `wave`, all eight d tiles; -W stored as A operand
+    // W^T = K^T diag(Gam) T'^T: d tiles 2*wave, 2*wave+1 (k-block `wave` of
+    // -W), all four token tiles; -W stored as A operand
     {
         half8 *wf = reinterpret_cast<half8 *>(ws.wfrag + hc * kWFragBytes);
-        const half8 b0 = lds_frag(TGh, kH_LD, 16 * wave, 0, lane);
-        const half8 b1 = lds_frag(TGh, kH_LD, 16 * wave, 32, lane);
-        f32x4 wt[8];
 #pragma unroll
-        for (int rt = 0; rt < 8; ++rt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mfma16(kf[(rt * 2 + 0) * 64], b0, acc);
-            if (wave >= 2) acc = mfma16(kf[(rt * 2 + 1) * 64], b1, acc);
-            wt[rt] = acc;
+        for (int ct = 0; ct < 4; ++ct) {
+            const half8 b0 = lds_frag(TGh, kH_LD, 16 * ct, 0, lane);
+            const half8 b1 = lds_frag(TGh, kH_LD, 16 * ct, 32, lane);
+            f32x4 w2[2];
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                acc = mfma16(kT[2 * rr + 0], b0, acc);
+                if (ct >= 2) acc = mfma16(kT[2 * rr + 1], b1, acc);
+                w2[rr] = acc;
+            }
+            wf[(ct * 4 + wave) * 64 + lane] = pack_h8(-w2[0], -w2[1]);
         }
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) wf[(wave * 4 + kb) * 64 + lane] = pack_h8(-wt[2 * kb], -wt[2 * kb + 1]);
     }
 }
 
 // ---------------------------------------------------------------------------
 // chain: the sequential state carry
 // ---------------------------------------------------------------------------
-// Workgroup = kChainWaves waves = one (sequence, V head) and 16*kChainWaves
-// columns of its state; each wave carries a 128 x 16 fp32 slice of S in its
-// accumulators through the whole sequence.  The operands of a chunk that
-// every wave needs (-W, q^, k^T, P, gates) and the waves' U' tiles are
-// brought into LDS with direct-to-LDS loads, double-buffered: chunk c+1 is in
-// flight while chunk c is computed, with one workgroup barrier per chunk.
-constexpr int kChainWaves = 2;
+// Workgroup = 4 waves = one (sequence, V head) and 16*kChainTiles columns of
+// its state.  Every product of a chunk is split over the four waves by rows:
+//   wave w computes Vnew and Q S for the chunk's tokens 16w .. 16w+15, owns
+//   (and updates) the state rows 32w .. 32w+31, and writes the outputs of
+//   its 16 tokens,
+// so each wave reads only its quarter of -W, q^, k^T and P.  Those operands
+// come straight from L2/HBM into registers, prefetched two chunks ahead; the
+// only exchanges are the fp16 copy of the state (B operand of W S and Q S)
+// and the two fp16 copies of Vnew (B operands of P Vnew and of the state
+// update), through small LDS buffers, with two barriers per chunk.
+constexpr int kChainTiles = 2;                         // 16-column tiles per workgroup
+constexpr int kChainBlocksPerHead = 8 / kChainTiles;   // workgroups per (sequence, V head)
+constexpr int kChainPrefetch = 2;                      // chunks in flight ahead of the one computed
 
-template <int NW>
-struct ChainStage {
-    static constexpr int kW = 0, kQ = 16 * 1024, kK = 32 * 1024, kP = 48 * 1024, kG = 56 * 1024,
-                         kU = 57 * 1024;
-    static constexpr int kBlocks = 57 + 2 * NW;  // 1-KiB blocks per stage
-    static constexpr int kBytes = kBlocks * 1024;
-};
-
-
-// Issue the direct-to-LDS loads of chunk c into `stage`.  Every region is a
-// whole number of 1-KiB blocks; wave w (uniform) moves blocks w, w+NW, ... of
-// each region (lane l: bytes 16l .. 16l+15 of a block).  Buffer loads carry
-// the block offset in a scalar register, so issuing costs no vector ALU work.
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t region_rsrc(const void *base)
+__device__ __forceinline__ half8 ld_frag(__amdgpu_buffer_rsrc_t r, int voff, int soff)
 {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, 0x00020000);
+    return __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-template <int NW, int kBlocks>
-__device__ __forceinline__ void issue_region(const void *src, uint8_t *dst, int wave, int lane)
+// this wave's operands of one chunk
+template <int CT>
+struct ChainOps {
+    half8 W[4];   // -W  rows 16w.., k-blocks 0..3 over d_k
+    half8 Q[4];   // q^  rows 16w.., k-blocks 0..3 over d_k
+    half8 K[4];   // k^T rows 32w + 16rr.., k-blocks 0..1 over tokens: index 2rr + kb
+    half8 P[2];   // P   rows 16w.., k-blocks 0..1 over tokens
+    half4 U[CT];  // U'  rows 16w.., column tiles of the workgroup
+    f32x4 gam;    // q_scale * Gam of rows 16w + 4q4 + e
+    f32x4 r;      // Gam_n / Gam of the same rows
+    float gn;     // Gam_n
+};
+
+template <int CT>
+__device__ __forceinline__ void chain_load(ChainOps<CT> &op, const Workspace &ws, long c, int h, int g, int Hqk,
+                                           int Hv, int ct0, int wave, int lane)
 {
-    const __amdgpu_buffer_rsrc_t r = region_rsrc(src);
+    const long hc = c * Hv + h, gc = c * Hqk + g;
+    const __amdgpu_buffer_rsrc_t rw = region_rsrc(ws.wfrag + hc * kWFragBytes);
+    const __amdgpu_buffer_rsrc_t rq = region_rsrc(ws.qfrag + gc * kQFragBytes);
+    const __amdgpu_buffer_rsrc_t rk = region_rsrc(ws.kfrag + gc * kKFragBytes);
+    const __amdgpu_buffer_rsrc_t rp = region_rsrc(ws.pfrag + hc * kPFragBytes);
+    const __amdgpu_buffer_rsrc_t ru = region_rsrc(ws.ufrag + hc * kUBytes);
+    const __amdgpu_buffer_rsrc_t rg = region_rsrc(ws.gates + hc * kGateFloats);
+    const int v16 = lane * 16;
 #pragma unroll
-    for (int i = 0; i < kBlocks / NW; ++i) {
-        const int blk = i * NW + wave;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(dst + blk * 1024), 16, lane * 16, blk * 1024, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+        op.W[i] = ld_frag(rw, v16, (wave * 4 + i) * 1024);
+        op.Q[i] = ld_frag(rq, v16, (wave * 4 + i) * 1024);
+        op.K[i] = ld_frag(rk, v16, (wave * 4 + i) * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) op.P[i] = ld_frag(rp, v16, (wave * 2 + i) * 1024);
+#pragma unroll
+    for (int x = 0; x < CT; ++x)
+        op.U[x] = __builtin_bit_cast(half4, __builtin_amdgcn_raw_buffer_load_b64(ru, lane * 8, ((ct0 + x) * 4 + wave) * 512, 0));
+    const int row4 = (16 * wave + 4 * (lane >> 4)) * 4;
+    op.gam = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, row4, 0, 0));
+    op.r = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, row4, 256, 0));
+    op.gn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, 0, 512, 0));
+}
+
+template <int CT>
+struct ChainLds {
+    half8 sx[4 * CT * 64];      // state as B operand: [k-block over d_k][tile][lane]
+    half8 vb[2 * CT * 64];      // Vnew as B operand:  [k-block over tokens][tile][lane]
+    half8 vr[2 * CT * 64];      // (Gam_n / Gam) Vnew as B operand
+    uint16_t os[4][16 * 16 * CT];  // output rows of each wave, bf16
+};
+
+// one chunk: consumes `op`, and issues the loads of chunk c + kChainPrefetch into `nxt`
+template <int CT>
+__device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace &ws, ChainLds<CT> &L,
+                                           f32x4 (&S)[CT][2], const ChainOps<CT> &op, ChainOps<CT> &nxt,
+                                           const int4 &si, int cc, int h, int g, int ct0, int wave, int lane)
+{
+    const int Hqk = p.Hqk, Hv = p.Hv;
+    const int q4 = lane >> 4, c16 = lane & 15;
+    // always issued (past the end it re-reads the last chunk), so that every
+    // chunk has the same memory operations in flight and the waits stay exact
+    chain_load<CT>(nxt, ws, si.x + min(cc + kChainPrefetch, si.y - 1), h, g, Hqk, Hv, ct0, wave, lane);
+
+    // 1. this wave's state rows 32w .. 32w+31 are k-block w of the B operand
+#pragma unroll
+    for (int x = 0; x < CT; ++x) L.sx[(wave * CT + x) * 64 + lane] = pack_h8(S[x][0], S[x][1]);
+    __syncthreads();
+    // 2. Vnew = U' - W S and Q S for tokens 16w .. 16w+15
+    f32x4 Vn[CT], QS[CT];
+#pragma unroll
+    for (int x = 0; x < CT; ++x) {
+        Vn[x] = f32x4{(float)op.U[x][0], (float)op.U[x][1], (float)op.U[x][2], (float)op.U[x][3]};
+        QS[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int x = 0; x < CT; ++x) {
+            const half8 sb = L.sx[(kb * CT + x) * 64 + lane];
+            Vn[x] = mfma16(op.W[kb], sb, Vn[x]);
+            QS[x] = mfma16(op.Q[kb], sb, QS[x]);
+        }
+    // 3. publish Vnew (plain and scaled) as half of a token k-block of the B operands
+    {
+        const int kbt = wave >> 1, half = wave & 1;
+#pragma unroll
+        for (int x = 0; x < CT; ++x) {
+            const f32x4 vs = Vn[x] * op.r;
+            half4 hb, hr;
+            hb[0] = (_Float16)Vn[x][0]; hb[1] = (_Float16)Vn[x][1]; hb[2] = (_Float16)Vn[x][2]; hb[3] = (_Float16)Vn[x][3];
+            hr[0] = (_Float16)vs[0]; hr[1] = (_Float16)vs[1]; hr[2] = (_Float16)vs[2]; hr[3] = (_Float16)vs[3];
+            reinterpret_cast<half4 *>(&L.vb[(kbt * CT + x) * 64 + lane])[half] = hb;
+            reinterpret_cast<half4 *>(&L.vr[(kbt * CT + x) * 64 + lane])[half] = hr;
+        }
+    }
+    __syncthreads();
+    // 4. state rows 32w + 16rr: S <- Gam_n S + k^T (r Vnew)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int x = 0; x < CT; ++x) {
+            const half8 vr = L.vr[(kb * CT + x) * 64 + lane];
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                if (kb == 0) S[x][rr] = S[x][rr] * op.gn;
+                S[x][rr] = mfma16(op.K[2 * rr + kb], vr, S[x][rr]);
+            }
+        }
+    // 5. outputs of tokens 16w .. 16w+15: q_scale (diag(Gam) Q S + P Vnew)
+    const int tok0 = si.z + cc * kChunk;
+    const int n = min(kChunk, si.w - cc * kChunk);
+#pragma unroll
+    for (int x = 0; x < CT; ++x) {
+        f32x4 acc = QS[x] * op.gam;
+        acc = mfma16(op.P[0], L.vb[(0 * CT + x) * 64 + lane], acc);
+        if (wave >= 2) acc = mfma16(op.P[1], L.vb[(1 * CT + x) * 64 + lane], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) L.os[wave][(4 * q4 + e) * (16 * CT) + 16 * x + c16] = (uint16_t)f32_to_bf16(acc[e]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    {
+        // 16 rows x (32 CT bytes): lane -> (row, 16-byte piece).  A buffer
+        // store whose range ends at the chunk's last valid token drops the
+        // rows of a partial chunk without a branch.
+        static_assert(CT == 2, "one 16-byte piece per lane");
+        constexpr int kPieces = 2 * CT;
+        const int row = lane / kPieces, piece = lane % kPieces;
+        const i32x4 v = reinterpret_cast<const i32x4 *>(&L.os[wave][row * 16 * CT])[piece];
+        const int rowb = Hv * kD * 2;  // bytes per token row of o
+        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+            p.o + ((long)tok0 * Hv + h) * kD + 16 * ct0, 0, n * rowb, 0x00020000);
+        __builtin_amdgcn_raw_buffer_store_b128(v, ro, (16 * wave + row) * rowb + piece * 16, 0, 0);
     }
 }
 
-template <int NW>
-__device__ __forceinline__ void chain_issue(const Workspace &ws, uint8_t *stage, long c, int h, int g,
-                                            int Hqk, int Hv, int cb, int wave, int lane)
-{
-    using St = ChainStage<NW>;
-    const long hc = c * Hv + h, gc = c * Hqk + g;
-    issue_region<NW, 16>(ws.wfrag + hc * kWFragBytes, stage + St::kW, wave, lane);
-    issue_region<NW, 16>(ws.qfrag + gc * kQFragBytes, stage + St::kQ, wave, lane);
-    issue_region<NW, 16>(ws.kfrag + gc * kKFragBytes, stage + St::kK, wave, lane);
-    issue_region<NW, 8>(ws.pfrag + hc * kPFragBytes, stage + St::kP, wave, lane);
-    issue_region<NW, 2 * NW>(ws.ufrag + hc * kUBytes + (long)cb * NW * 2048, stage + St::kU, wave, lane);
-    if (wave == 0)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(region_rsrc(ws.gates + hc * kGateFloats),
-                                                 (lds_void_t *)(stage + St::kG), 16, lane * 16, 0, 0, 0);
-}
-
-template <int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int CT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void chain_kernel(PrefillArgs p, Workspace ws)
 {
-    using St = ChainStage<NW>;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * St::kBytes + NW * 2048];
+    __shared__ ChainLds<CT> L;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int q4 = lane >> 4, c16 = lane & 15;
     const int Hqk = p.Hqk, Hv = p.Hv, G = Hv / Hqk;
-    constexpr int kBlocksPerHead = 8 / NW;
+    constexpr int kPerHead = 8 / CT;
     // block -> (rank, group, head-in-group, column block); all workgroups of
     // one (sequence, QK group) land on the same XCD (same L2)
-    const int per_group = G * kBlocksPerHead;
+    const int per_group = G * kPerHead;
     const int bid = blockIdx.x;
     const int gu = (bid / (8 * per_group)) * 8 + (bid & 7);
     const int inner = (bid >> 3) % per_group;
     if (gu >= p.N * Hqk) return;
     const int rank = gu / Hqk, g = gu % Hqk;
-    const int j = inner / kBlocksPerHead, cb = inner % kBlocksPerHead;
+    const int j = inner / kPerHead, cb = inner % kPerHead;
     const int h = g * G + j;
-    const int ct = cb * NW + wave;
+    const int ct0 = cb * CT;
     const int s = ws.order[rank];
     const int4 si = ws.seq_info[s];  // chunk0, nchunks, t0, L
-    const int col = 16 * ct + c16;
-    uint16_t *ostage = reinterpret_cast<uint16_t *>(smem + 2 * St::kBytes + wave * 2048);
 
-    // state slice S[:, 16ct .. 16ct+15] in accumulator layout: tile rt holds rows 16rt + 4q4 + e
-    f32x4 S[8];
+    // state rows 32w + 16rr + 4q4 + e, columns 16(ct0 + x) + c16
+    f32x4 S[CT][2];
     const long sbase = ((long)s * Hv + h) * kD * kD;
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
+    for (int x = 0; x < CT; ++x)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            S[rt][e] = p.state_in ? p.state_in[sbase + (long)(16 * rt + 4 * q4 + e) * kD + col] : 0.f;
+        for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                S[x][rr][e] = p.state_in ? p.state_in[sbase + (long)(32 * wave + 16 * rr + 4 * q4 + e) * kD +
+                                                      16 * (ct0 + x) + c16]
+                                         : 0.f;
 
-    if (si.y > 0) chain_issue<NW>(ws, smem, si.x, h, g, Hqk, Hv, cb, wave, lane);
-    for (int cc = 0; cc < si.y; ++cc) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (cc + 1 < si.y)
-            chain_issue<NW>(ws, smem + ((cc + 1) & 1) * St::kBytes, si.x + cc + 1, h, g, Hqk, Hv, cb, wave, lane);
-        const uint8_t *st = smem + (cc & 1) * St::kBytes;
-        const half8 *Wf = reinterpret_cast<const half8 *>(st + St::kW) + lane;
-        const half8 *Qf = reinterpret_cast<const half8 *>(st + St::kQ) + lane;
-        const half8 *Kf = reinterpret_cast<const half8 *>(st + St::kK) + lane;
-        const half8 *Pf = reinterpret_cast<const half8 *>(st + St::kP) + lane;
-        const float *gt = reinterpret_cast<const float *>(st + St::kG);
-        const half4 *Uf = reinterpret_cast<const half4 *>(st + St::kU) + wave * 4 * 64 + lane;
-        const int n = min(kChunk, si.w - cc * kChunk);
-        const int tok0 = si.z + cc * kChunk;
-
-        // state as the B operand (fp16), contraction over d_k
-        half8 Sb[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) Sb[kb] = pack_h8(S[2 * kb], S[2 * kb + 1]);
-
-        // Vnew = U' - W S ;  QS = Q S   (eight independent accumulators per
-        // k-block, operands read one k-block ahead)
-        f32x4 Vn[4], QS[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            const half4 u = Uf[rt * 64];
-            Vn[rt] = f32x4{(float)u[0], (float)u[1], (float)u[2], (float)u[3]};
-            QS[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (si.y > 0) {
+        // three operand sets rotate: chunk cc is computed while cc+1 and cc+2 load
+        ChainOps<CT> o0, o1, o2;
+        chain_load<CT>(o0, ws, si.x, h, g, Hqk, Hv, ct0, wave, lane);
+        chain_load<CT>(o1, ws, si.x + min(1, si.y - 1), h, g, Hqk, Hv, ct0, wave, lane);
+        int cc = 0;
+        for (; cc + 3 <= si.y; cc += 3) {
+            chain_step<CT>(p, ws, L, S, o0, o2, si, cc, h, g, ct0, wave, lane);
+            chain_step<CT>(p, ws, L, S, o1, o0, si, cc + 1, h, g, ct0, wave, lane);
+            chain_step<CT>(p, ws, L, S, o2, o1, si, cc + 2, h, g, ct0, wave, lane);
         }
-        half8 wA[4], qA[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            wA[rt] = Wf[(rt * 4) * 64];
-            qA[rt] = Qf[(rt * 4) * 64];
-        }
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            half8 wN[4], qN[4];
-            if (kb < 3) {
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    wN[rt] = Wf[(rt * 4 + kb + 1) * 64];
-                    qN[rt] = Qf[(rt * 4 + kb + 1) * 64];
-                }
-            }
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                Vn[rt] = mfma16(wA[rt], Sb[kb], Vn[rt]);
-                QS[rt] = mfma16(qA[rt], Sb[kb], QS[rt]);
-            }
-            if (kb < 3) {
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    wA[rt] = wN[rt];
-                    qA[rt] = qN[rt];
-                }
-            }
-        }
-        // Vnew as B operands: plain (for P Vnew) and scaled by Gam_n / Gam (for the state)
-        half8 Vb[2], Vr[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const f32x4 r_lo = *reinterpret_cast<const f32x4 *>(gt + 64 + 32 * kb + 4 * q4);
-            const f32x4 r_hi = *reinterpret_cast<const f32x4 *>(gt + 64 + 32 * kb + 16 + 4 * q4);
-            Vb[kb] = pack_h8(Vn[2 * kb], Vn[2 * kb + 1]);
-            Vr[kb] = pack_h8(Vn[2 * kb] * r_lo, Vn[2 * kb + 1] * r_hi);
-        }
-        // O = q_scale (diag(Gam) Q S + P Vnew) (q_scale is folded into Gam and
-        // P), staged through LDS for 16-byte row stores
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            const f32x4 gam = *reinterpret_cast<const f32x4 *>(gt + 16 * rt + 4 * q4);
-            f32x4 acc = QS[rt] * gam;
-            acc = mfma16(Pf[(rt * 2 + 0) * 64], Vb[0], acc);
-            if (rt >= 2) acc = mfma16(Pf[(rt * 2 + 1) * 64], Vb[1], acc);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ostage[(16 * rt + 4 * q4 + e) * 16 + c16] = (uint16_t)f32_to_bf16(acc[e]);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (lane < n) {
-            const uint4 *srow = reinterpret_cast<const uint4 *>(ostage + lane * 16);
-            uint4 *drow = reinterpret_cast<uint4 *>(p.o + ((long)(tok0 + lane) * Hv + h) * kD + 16 * ct);
-            drow[0] = srow[0];
-            drow[1] = srow[1];
-        }
-        // S <- Gam_n S + K^T (r * Vnew): the dependency into the next chunk,
-        // last so that its matrix-core work overlaps the next chunk's wait
-        const float gn = gt[128];
-#pragma unroll
-        for (int rt = 0; rt < 8; ++rt) S[rt] = S[rt] * gn;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int rt = 0; rt < 8; ++rt) S[rt] = mfma16(Kf[(rt * 2 + kb) * 64], Vr[kb], S[rt]);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
+        if (cc < si.y) chain_step<CT>(p, ws, L, S, o0, o2, si, cc, h, g, ct0, wave, lane);
+        if (cc + 1 < si.y) chain_step<CT>(p, ws, L, S, o1, o0, si, cc + 1, h, g, ct0, wave, lane);
     }
 
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
+    for (int x = 0; x < CT; ++x)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p.state_out[sbase + (long)(16 * rt + 4 * q4 + e) * kD + col] = S[rt][e];
+        for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                p.state_out[sbase + (long)(32 * wave + 16 * rr + 4 * q4 + e) * kD + 16 * (ct0 + x) + c16] = S[x][rr][e];
 
     // carried conv rows: the last three raw rows of the sequence (v channels of
     // head h; the first head of the group also writes the q and k channels)
     if (p.conv_state_out && cb == 0 && wave == 0) {
         const long C_tot = 2L * Hqk * kD + (long)Hv * kD;
-        const int L = si.w, t0 = si.z;
+        const int Ls = si.w, t0 = si.z;
         for (int plane = (j == 0 ? 0 : 2); plane < 3; ++plane) {
             const long ch0 = plane == 0 ? (long)g * kD : plane == 1 ? (long)Hqk * kD + (long)g * kD
                                                                   : 2L * Hqk * kD + (long)h * kD;
@@ -688,7 +783,7 @@ void chain_kernel(PrefillArgs p, Workspace ws)
             const long ld = plane == 2 ? (long)Hv * kD : (long)Hqk * kD;
 #pragma unroll
             for (int r = 0; r < 3; ++r) {
-                const int tau = L - 3 + r;
+                const int tau = Ls - 3 + r;
                 uint32_t val = 0;
                 if (tau >= 0)
                     val = ld_pair(src + (long)(t0 + tau) * ld + 2 * lane);
@@ -763,9 +858,8 @@ hipError_t launch_prefill(const PrefillArgs &p, void *workspace, hipStream_t str
     if ((e = mark(2)) != hipSuccess) return e;
     const int G = p.Hv / p.Hqk;
     const long groups = (long)p.N * p.Hqk;
-    const long blocks = ((groups + 7) / 8) * 8L * G * (8 / kChainWaves);
-    hipLaunchKernelGGL(chain_kernel<kChainWaves>, dim3((unsigned)blocks), dim3(64 * kChainWaves), 0, stream, p,
-                       ws);
+    const long blocks = ((groups + 7) / 8) * 8L * G * kChainBlocksPerHead;
+    hipLaunchKernelGGL(chain_kernel<kChainTiles>, dim3((unsigned)blocks), dim3(256), 0, stream, p, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return mark(3);
 }
