@@ -69,21 +69,14 @@ __device__ __forceinline__ half8 lds_frag(const _Float16 *M, int ld, int r0, int
 
 __device__ __forceinline__ uint32_t ld_pair(const uint16_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
 
-// Causal width-4 conv + SiLU of channels (2*pp, 2*pp+1) of one 128-channel
-// plane, rows r0 .. r0+15 of the chunk.  x points at the chunk's first token
-// (row stride ld); rows < 0 come from the previous chunk of the same sequence
+// Raw rows r0-3 .. r0+15 of channels (2*pp, 2*pp+1) of one 128-channel plane
+// for the causal width-4 conv.  x points at the chunk's first token (row
+// stride ld); rows < 0 come from the previous chunk of the same sequence
 // (first == false), from the carried conv rows `hist` (row stride C_tot), or
-// are zero.  Rows >= n are padding and produce zeros.
-__device__ __forceinline__ void conv_plane(const uint16_t *__restrict__ x, long ld, int n, bool first,
-                                           const uint16_t *hist, long C_tot,
-                                           const uint16_t *__restrict__ w, int pp, int r0,
-                                           float (&z0)[16], float (&z1)[16])
+// are zero.  Rows >= n are padding and read as zero.
+__device__ __forceinline__ void conv_window(const uint16_t *__restrict__ x, long ld, int n, bool first,
+                                            const uint16_t *hist, long C_tot, int pp, int r0, uint32_t (&win)[19])
 {
-    const uint2 wa = *reinterpret_cast<const uint2 *>(w + (2 * pp) * 4);
-    const uint2 wb = *reinterpret_cast<const uint2 *>(w + (2 * pp + 1) * 4);
-    const float a0 = bf16_lo(wa.x), a1 = bf16_hi(wa.x), a2 = bf16_lo(wa.y), a3 = bf16_hi(wa.y);
-    const float b0 = bf16_lo(wb.x), b1 = bf16_hi(wb.x), b2 = bf16_lo(wb.y), b3 = bf16_hi(wb.y);
-    uint32_t win[19];
 #pragma unroll
     for (int i = 0; i < 19; ++i) {
         const int r = r0 - 3 + i;
@@ -97,6 +90,16 @@ __device__ __forceinline__ void conv_plane(const uint16_t *__restrict__ x, long 
         }
         win[i] = val;
     }
+}
+
+// Conv (tap 3 = current token) + SiLU over a loaded window; rows >= n give 0.
+__device__ __forceinline__ void conv_silu(const uint32_t (&win)[19], const uint16_t *__restrict__ w, int pp, int r0,
+                                          int n, float (&z0)[16], float (&z1)[16])
+{
+    const uint2 wa = *reinterpret_cast<const uint2 *>(w + (2 * pp) * 4);
+    const uint2 wb = *reinterpret_cast<const uint2 *>(w + (2 * pp + 1) * 4);
+    const float a0 = bf16_lo(wa.x), a1 = bf16_hi(wa.x), a2 = bf16_lo(wa.y), a3 = bf16_hi(wa.y);
+    const float b0 = bf16_lo(wb.x), b1 = bf16_hi(wb.x), b2 = bf16_lo(wb.y), b3 = bf16_hi(wb.y);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const float ya = a0 * bf16_lo(win[i]) + a1 * bf16_lo(win[i + 1]) + a2 * bf16_lo(win[i + 2]) +
@@ -107,6 +110,16 @@ __device__ __forceinline__ void conv_plane(const uint16_t *__restrict__ x, long 
         z0[i] = valid ? silu_f(ya) : 0.0f;
         z1[i] = valid ? silu_f(yb) : 0.0f;
     }
+}
+
+__device__ __forceinline__ void conv_plane(const uint16_t *__restrict__ x, long ld, int n, bool first,
+                                           const uint16_t *hist, long C_tot,
+                                           const uint16_t *__restrict__ w, int pp, int r0,
+                                           float (&z0)[16], float (&z1)[16])
+{
+    uint32_t win[19];
+    conv_window(x, ld, n, first, hist, C_tot, pp, r0, win);
+    conv_silu(win, w, pp, r0, n, z0, z1);
 }
 
 // ---------------------------------------------------------------------------
@@ -318,18 +331,20 @@ constexpr int kH_LD = 68;  // fp16 row stride of v^T, T', T' diag(Gam) (8-byte a
 
 __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, Workspace ws)
 {
-    // LDS plan: [F] k^ / q^ operands (20 KiB), later X = (I+A)^-1 (fp32);
-    //           [A] A (fp32), later T' and T' diag(Gam) (fp16); v^T; scratch; gates
-    __shared__ __attribute__((aligned(16))) uint8_t regF[20 * 1024];
+    // LDS plan: [F] k^ operands (16 KiB) -> X = (I+A)^-1 (fp32) -> v^T (fp16);
+    //           [A] A (fp32) -> T' and T' diag(Gam) (fp16); scratch; gates
+    __shared__ __attribute__((aligned(16))) uint8_t regF[64 * kAL * 4];
     __shared__ __attribute__((aligned(16))) uint8_t regA[64 * kAL * 4];
-    __shared__ __attribute__((aligned(16))) _Float16 VTs[128 * kH_LD];
     __shared__ __attribute__((aligned(16))) float Msc[3][256];
-    __shared__ float s_gam2[64], s_beta[64];
-    const half8 *Fk = reinterpret_cast<const half8 *>(regF);             // k^ tok-major: [rt*4+kb][lane]
+    __shared__ float s_gam2[64], s_beta[64], s_bg[64];
+    const half8 *Fk = reinterpret_cast<const half8 *>(regF);  // k^ token-major: [rt*4+kb][lane]
     float *Xs = reinterpret_cast<float *>(regF);
+    _Float16 *VTs = reinterpret_cast<_Float16 *>(regF);
     float *As = reinterpret_cast<float *>(regA);
     _Float16 *Th = reinterpret_cast<_Float16 *>(regA);
     _Float16 *TGh = Th + 64 * kH_LD;
+    static_assert(128 * kH_LD * 2 <= 64 * kAL * 4, "v^T fits over X");
+    static_assert(2 * 64 * kH_LD * 2 <= 64 * kAL * 4, "T' and T' diag(Gam) fit over A");
 
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -352,10 +367,10 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
     const uint16_t *hist = (first && p.conv_state_in) ? p.conv_state_in + (long)s * 3 * C_tot : nullptr;
     const long hc = (long)c * Hv + h, gc = (long)c * Hqk + g;
     const int r0 = 16 * wave;
+    const long ldv = (long)Hv * kD;
+    const long cv = 2L * Hqk * kD + (long)h * kD;
 
-    // operands from the q/k pass: k^ (16 KiB) and this tile's... q^ row tile
-    // `wave` is only needed by this wave, k^ by all: k^ into LDS, q^ and the
-    // k^T rows this wave multiplies into registers
+    // ---- every global read of the workgroup is issued first
     {
         const __amdgpu_buffer_rsrc_t rk = region_rsrc(ws.ktok + gc * kKTokFragBytes);
 #pragma unroll
@@ -374,12 +389,18 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
             kT[kb] = kf[(wave * 4 + kb) * 64];  // k^T row tiles 2w, 2w+1, k-blocks 0..1
         }
     }
+    uint32_t vwin[19];
+    conv_window(p.v + (long)t0 * ldv + (long)h * kD, ldv, n, first, hist ? hist + cv : nullptr, C_tot, lane, r0, vwin);
+    float av = 0.f, bv = 0.f;
+    if (wave == 0 && lane < n) {
+        const long ti = (long)(t0 + lane) * Hv + h;
+        av = p.a[ti];
+        bv = p.b[ti];
+    }
 
-    // gates (wave 0): gam = in-chunk cumulative log decay (log2 units), beta
+    // ---- gates (wave 0): gam = in-chunk cumulative log decay (log2 units), beta
     if (wave == 0) {
         const bool valid = lane < n;
-        const long ti = (long)(t0 + lane) * Hv + h;
-        const float av = valid ? p.a[ti] : 0.f, bv = valid ? p.b[ti] : 0.f;
         const float gl = valid ? -p.gate_scale * kLog2e * softplus_f(av) : 0.f;
         const float be = valid ? sigmoid_f(bv) : 0.f;
         float gam = gl;
@@ -389,31 +410,20 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
             if (lane >= off) gam += y;
         }
         const float gam_n = __shfl(gam, n - 1, 64);
+        const float Gam = __builtin_amdgcn_exp2f(gam);
         s_gam2[lane] = gam;
         s_beta[lane] = be;
+        s_bg[lane] = be * Gam;
         // slot 0: q_scale * Gam (only the output uses it); slot 1: Gam_n / Gam; slot 2: Gam_n
         float *gt = ws.gates + hc * kGateFloats;
-        gt[lane] = p.q_scale * __builtin_amdgcn_exp2f(gam);
+        gt[lane] = p.q_scale * Gam;
         gt[64 + lane] = valid ? __builtin_amdgcn_exp2f(gam_n - gam) : 0.f;
         if (lane == 0) gt[128] = __builtin_amdgcn_exp2f(gam_n);
     }
-    // v^ of head h: conv + SiLU -> v^T in LDS
-    {
-        float z0[16], z1[16];
-        const long ldv = (long)Hv * kD;
-        const long cv = 2L * Hqk * kD + (long)h * kD;
-        const uint16_t *xv = p.v + (long)t0 * ldv + (long)h * kD;
-        conv_plane(xv, ldv, n, first, hist ? hist + cv : nullptr, C_tot, p.conv_w + cv * 4, lane, r0, z0, z1);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            VTs[(2 * lane) * kH_LD + r0 + i] = (_Float16)z0[i];
-            VTs[(2 * lane + 1) * kH_LD + r0 + i] = (_Float16)z1[i];
-        }
-    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // K K^T (rows 16*wave.., column tiles ct <= wave) and K Q^T (query tile
-    // `wave`, key tiles jt <= wave)
+    // ---- K K^T (rows 16*wave.., column tiles ct <= wave) and K Q^T (query
+    //      tile `wave`, key tiles jt <= wave)
     f32x4 kk[4], kq[4];
     {
         half8 kOwn[4];
@@ -434,7 +444,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
             kq[ct] = acq;
         }
     }
-    // A = strict_lower(diag(beta) K K^T * D) -> LDS; P = (K Q^T)^T * D (lower) -> global
+    // ---- A = strict_lower(diag(beta) K K^T * D) -> LDS; P = (K Q^T)^T * D (lower) -> global
     {
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
@@ -466,10 +476,10 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
         }
     }
     __syncthreads();
-    // X = (I + A)^-1, blocked by 16: diagonal blocks by forward substitution
-    // (wave b, block b), then the blocks below the diagonal level by level,
-    //   X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj,
-    // on the fp32 matrix cores
+    // ---- X = (I + A)^-1, blocked by 16: diagonal blocks by forward
+    //      substitution (wave b, block b), then the blocks below the diagonal
+    //      level by level, X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj, on the fp32
+    //      matrix cores
     {
         float y[16];
         const int bo = 16 * wave;
@@ -497,15 +507,38 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
         }
         __syncthreads();
     }
-    // T' = X diag(beta) and T' diag(Gam) (fp16, lower), over A's storage
-    for (int e = t; e < 64 * 64; e += kPrepThreads) {
-        const int i = e >> 6, jj = e & 63;
-        const float tv = jj <= i ? Xs[i * kAL + jj] * s_beta[jj] : 0.f;
-        Th[i * kH_LD + jj] = (_Float16)tv;
-        TGh[i * kH_LD + jj] = (_Float16)(tv * __builtin_amdgcn_exp2f(s_gam2[jj]));
+    // ---- T' = X diag(beta) and T' diag(Gam) (fp16, lower) over A's storage
+    {
+        float tv[16], tg[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int e = t + k * kPrepThreads;
+            const int i = e >> 6, jj = e & 63;
+            const float xv = jj <= i ? Xs[i * kAL + jj] : 0.f;
+            tv[k] = xv * s_beta[jj];
+            tg[k] = xv * s_bg[jj];
+        }
+        __syncthreads();  // A and X are dead from here on
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int e = t + k * kPrepThreads;
+            const int i = e >> 6, jj = e & 63;
+            Th[i * kH_LD + jj] = (_Float16)tv[k];
+            TGh[i * kH_LD + jj] = (_Float16)tg[k];
+        }
+    }
+    // ---- v^ of head h: conv + SiLU from the window loaded at the start -> v^T over X
+    {
+        float z0[16], z1[16];
+        conv_silu(vwin, p.conv_w + cv * 4, lane, r0, n, z0, z1);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            VTs[(2 * lane) * kH_LD + r0 + i] = (_Float16)z0[i];
+            VTs[(2 * lane + 1) * kH_LD + r0 + i] = (_Float16)z1[i];
+        }
     }
     __syncthreads();
-    // U' = T' V: column tiles 2*wave, 2*wave+1; stored in accumulator order
+    // ---- U' = T' V: column tiles 2*wave, 2*wave+1; stored in accumulator order
     {
         half4 *uf = reinterpret_cast<half4 *>(ws.ufrag + hc * kUBytes);
         half8 ta[4][2];
@@ -531,8 +564,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
             }
         }
     }
-    // W^T = K^T diag(Gam) T'^T: d tiles 2*wave, 2*wave+1 (k-block `wave` of
-    // -W), all four token tiles; -W stored as A operand
+    // ---- W^T = K^T diag(Gam) T'^T: d tiles 2*wave, 2*wave+1 (k-block `wave`
+    //      of -W), all four token tiles; -W stored as A operand
     {
         half8 *wf = reinterpret_cast<half8 *>(ws.wfrag + hc * kWFragBytes);
 #pragma unroll
