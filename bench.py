@@ -7,6 +7,16 @@ HBM).  The decode workload (B = 256 sequences, 64 consecutive in-place steps)
 is timed in the same run and reported under "decode".  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                  [--calibrate-copy]
+  python bench.py --traffic-report FETCH_CSV WRITE_CSV
+
+--calibrate-copy ends the run with a plain 256 MiB device-to-device copy, so
+that a rocprofv3 --pmc pass over this command also reads its counters for a
+transfer of known size.  --traffic-report turns two such passes (FETCH_SIZE,
+then WRITE_SIZE; rocprofv3's counter_collection.csv files) into HBM bytes per
+launch of each kernel, scaled by what the counters read for the copy, and
+writes them to profiles/traffic.json tagged with the digest of the kernel
+sources they were taken on.
 
 Timing: HIP events on the stream the library launches on.  The prefill goes
 through gdn_prefill_with_events, so each of its three kernels is timed per
@@ -92,6 +102,60 @@ def source_digest():
     for f in sorted(glob.glob(os.path.join(ROOT, "linear_attention_sequence_gdn_amd", "csrc", "*"))):
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
+
+
+COPY_BYTES = 256 << 20
+TRAFFIC_KERNELS = {"prefill_chain": "chain_kernel", "prefill_prep_head": "prep_head_kernel",
+                   "prefill_prep_qk": "prep_qk_kernel", "prefill_setup": "setup_kernel",
+                   "decode": "decode_kernel"}
+
+
+def _counter_rows(path, counter):
+    """(dispatch id, value) rows of `counter` by kernel name, from a rocprofv3
+    counter_collection.csv."""
+    import csv
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            acc.setdefault(r["Kernel_Name"], []).append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    return acc
+
+
+def traffic_report(fetch_csv, write_csv):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) -> calibrated bytes per launch.
+    The calibration copy is the run's last device-to-device copy dispatch."""
+    fetch = _counter_rows(fetch_csv, "FETCH_SIZE")
+    write = _counter_rows(write_csv, "WRITE_SIZE")
+
+    def rows(table, sub):
+        hits = [v_ for k_, v_ in table.items() if sub in k_]
+        if len(hits) != 1:
+            raise SystemExit(f"traffic report: {len(hits)} kernels match {sub!r}")
+        return hits[0]
+
+    def mean(table, sub):
+        r = rows(table, sub)
+        return sum(v_ for _, v_ in r) / len(r)
+
+    f_copy = max(rows(fetch, "copyBuffer"))[1] * 1024
+    w_copy = max(rows(write, "copyBuffer"))[1] * 1024
+    f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
+    digest = source_digest()
+    out = {"_calibration": {"copy_bytes": COPY_BYTES, "fetch_counter_bytes": f_copy,
+                            "write_counter_bytes": w_copy, "fetch_scale": f_scale,
+                            "write_scale": w_scale}}
+    for name, sub in TRAFFIC_KERNELS.items():
+        rd = mean(fetch, sub) * 1024 * f_scale
+        wr = mean(write, sub) * 1024 * w_scale
+        out[name] = {"kernel": sub, "read_bytes": rd, "write_bytes": wr, "bytes_per_launch": rd + wr,
+                     "source_digest": digest}
+        print(f"{sub:18s} read {rd / 2**20:10.2f} MiB  write {wr / 2**20:10.2f} MiB per launch")
+    print(f"copy calibration: FETCH_SIZE x{f_scale:.3f}, WRITE_SIZE x{w_scale:.3f}")
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print("wrote", path)
 
 
 def load_traffic(name, digest):
@@ -216,7 +280,7 @@ def bench_decode(hip, steps=64):
                 steps=steps)
 
 
-def cpu_baseline(min_seconds=10.0, max_reps=3):
+def cpu_baseline(min_seconds=12.0, max_reps=60):
     import oracle
     from linear_attention_sequence_gdn_amd import inputs
     x = inputs.make_config(1)
@@ -241,7 +305,12 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--traffic-report", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
+    if args.traffic_report:
+        traffic_report(*args.traffic_report)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
@@ -303,6 +372,11 @@ def main():
                                 "algorithmic_bytes_per_launch": dec_bytes}},
         "source_digest": digest,
     }
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

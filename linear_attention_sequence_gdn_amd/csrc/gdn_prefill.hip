@@ -155,17 +155,38 @@ __global__ __launch_bounds__(1024) void setup_kernel(PrefillArgs p, Workspace ws
         __syncthreads();
     }
     int base = s_scan[t] - local;
-    const int total = s_scan[1023];
     for (int s = s0; s < s1; ++s) {
         const int L = seq_len(p, s), t0 = seq_start(p, s);
         // chunks beyond the workspace bound (only with a malformed cu_seqlens) are dropped
         const int nch = max(0, min((L + kChunk - 1) / kChunk, p.max_chunks - base));
         ws.seq_info[s] = make_int4(base, nch, t0, min(L, nch * kChunk));
-        for (int j = 0; j < nch; ++j)
-            ws.chunk_info[base + j] = make_int4(s, t0 + j * kChunk, min(kChunk, L - j * kChunk), j == 0);
         base += nch;
     }
-    for (int c = min(total, p.max_chunks) + t; c < p.max_chunks; c += 1024) ws.chunk_info[c] = make_int4(0, 0, 0, 0);
+    // chunk table, one chunk per thread: chunk c lies in the sequence range of
+    // the first thread whose inclusive count exceeds c
+    const int total = min(s_scan[1023], p.max_chunks);
+    for (int c = t; c < p.max_chunks; c += 1024) {
+        int4 info = make_int4(0, 0, 0, 0);
+        if (c < total) {
+            int lo = 0, hi = 1023;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (s_scan[mid] > c) hi = mid;
+                else lo = mid + 1;
+            }
+            int b = lo > 0 ? s_scan[lo - 1] : 0;
+            for (int s = lo * per; s < min(p.N, lo * per + per); ++s) {
+                const int L = seq_len(p, s), nch = (L + kChunk - 1) / kChunk;
+                if (c < b + nch) {
+                    const int j = c - b;
+                    info = make_int4(s, seq_start(p, s) + j * kChunk, min(kChunk, L - j * kChunk), j == 0);
+                    break;
+                }
+                b += nch;
+            }
+        }
+        ws.chunk_info[c] = info;
+    }
     // longest first (ties by index): rank of each sequence
     for (int s = t; s < p.N; s += 1024) {
         const int Ls = seq_len(p, s);
