@@ -109,6 +109,8 @@ static int prefill_common(const uint16_t *q, const uint16_t *k, const uint16_t *
     p.cu_seqlens = cu_seqlens; p.N = N; p.T_uniform = T_uniform; p.T_tot = T_tot;
     p.Hqk = Hqk; p.Hv = Hv; p.gate_scale = gate_scale; p.q_scale = q_scale;
     p.max_chunks = max_chunks;
+    p.seg_chunks = gdn::choose_seg_chunks(max_chunks, N, Hv);
+    p.max_segs = gdn::max_segments(max_chunks, N, p.seg_chunks);
     hipError_t e = gdn::launch_prefill(p, workspace, reinterpret_cast<hipStream_t>(stream),
                                        reinterpret_cast<hipEvent_t const *>(events));
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;

@@ -23,6 +23,8 @@ struct PrefillArgs {
     int Hqk, Hv;
     float gate_scale, q_scale;
     int max_chunks;
+    int seg_chunks;  // chunks per segment of the sequential pass
+    int max_segs;    // bound of the number of segments
 };
 
 // Upper bound of the number of 64-token chunks.
@@ -42,7 +44,8 @@ constexpr size_t kKTokFragBytes = 16 * kFragBytes;   // k^ of a chunk     [64 x 
 constexpr size_t kWFragBytes = 16 * kFragBytes;      // -W of a chunk     [64 x 128]
 constexpr size_t kUBytes = 64 * 128 * 2;             // U' of a chunk     [64 x 128]
 constexpr size_t kPFragBytes = 8 * kFragBytes;       // P of a chunk      [64 x 64]
-constexpr size_t kGateFloats = 256;                 // Gamma[64], r[64], Gamma_n, pad (1 KiB)
+constexpr size_t kGateFloats = 256;                 // Gamma[64], r[64], Gamma_n, log2 Gamma_n, pad (1 KiB)
+constexpr size_t kStateFloats = 128 * 128;          // one fp32 state
 
 struct Workspace {
     int4 *chunk_info;   // [max_chunks] {seq, t0, n, first}
@@ -54,8 +57,18 @@ struct Workspace {
     uint8_t *wfrag;     // [max_chunks][Hv]
     uint8_t *ufrag;     // [max_chunks][Hv]
     uint8_t *pfrag;     // [max_chunks][Hv]
-    float *gates;       // [max_chunks][Hv][3][64]
+    float *gates;       // [max_chunks][Hv][256]
+    int4 *seg_info;     // [max_segs] {seq, first chunk, end chunk, 1: first of seq | 2: last of seq}; seq -1 = unused
+    int4 *seq_seg;      // [N] {first segment, segments, -, -}
+    int *seg_bad;       // [max_segs][Hv] warm-up bound not met: the segment is recomputed in order
+    float *bstate;      // [max_segs][Hv][128][128] final state of a segment whose successor is recomputed
 };
+
+// Segments of the sequential pass: each sequence's chunks are cut into runs of
+// seg_chunks that proceed in parallel (chosen from the sizes alone, so that the
+// workspace size is a function of the arguments).
+int choose_seg_chunks(int max_chunks, int N, int Hv);
+inline int max_segments(int max_chunks, int N, int seg_chunks) { return max_chunks / seg_chunks + N; }
 
 size_t prefill_workspace_bytes(int max_chunks, int N, int Hqk, int Hv);
 Workspace carve_workspace(void *base, int max_chunks, int N, int Hqk, int Hv);

@@ -155,12 +155,15 @@ __global__ __launch_bounds__(1024) void setup_kernel(PrefillArgs p, Workspace ws
         __syncthreads();
     }
     int base = s_scan[t] - local;
+    const int Lseg = p.seg_chunks;
+    int segs_local = 0;
     for (int s = s0; s < s1; ++s) {
         const int L = seq_len(p, s), t0 = seq_start(p, s);
         // chunks beyond the workspace bound (only with a malformed cu_seqlens) are dropped
         const int nch = max(0, min((L + kChunk - 1) / kChunk, p.max_chunks - base));
         ws.seq_info[s] = make_int4(base, nch, t0, min(L, nch * kChunk));
         base += nch;
+        segs_local += max(1, (nch + Lseg - 1) / Lseg);
     }
     // chunk table, one chunk per thread: chunk c lies in the sequence range of
     // the first thread whose inclusive count exceeds c
@@ -187,6 +190,29 @@ __global__ __launch_bounds__(1024) void setup_kernel(PrefillArgs p, Workspace ws
         }
         ws.chunk_info[c] = info;
     }
+    // segments of the sequential pass: max(1, ceil(chunks / Lseg)) per
+    // sequence, in sequence order
+    __syncthreads();
+    s_scan[t] = segs_local;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int add = t >= off ? s_scan[t - off] : 0;
+        __syncthreads();
+        s_scan[t] += add;
+        __syncthreads();
+    }
+    int sb = s_scan[t] - segs_local;
+    for (int s = s0; s < s1; ++s) {
+        const int4 si = ws.seq_info[s];
+        const int ns = max(1, (si.y + Lseg - 1) / Lseg);
+        ws.seq_seg[s] = make_int4(sb, ns, 0, 0);
+        for (int i = 0; i < ns && sb + i < p.max_segs; ++i) {
+            const int cb = si.x + i * Lseg, ce = min(si.x + si.y, cb + Lseg);
+            ws.seg_info[sb + i] = make_int4(s, cb, ce, (i == 0 ? 1 : 0) | (i == ns - 1 ? 2 : 0));
+        }
+        sb += ns;
+    }
+    for (int k = min(s_scan[1023], p.max_segs) + t; k < p.max_segs; k += 1024) ws.seg_info[k] = make_int4(-1, 0, 0, 0);
     // longest first (ties by index): rank of each sequence
     for (int s = t; s < p.N; s += 1024) {
         const int Ls = seq_len(p, s);
@@ -435,11 +461,14 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
         s_gam2[lane] = gam;
         s_beta[lane] = be;
         s_bg[lane] = be * Gam;
-        // slot 0: q_scale * Gam (only the output uses it); slot 1: Gam_n / Gam; slot 2: Gam_n
+        // [0,64): q_scale * Gam (only the output uses it); [64,128): Gam_n / Gam; 128: Gam_n; 129: log2 Gam_n
         float *gt = ws.gates + hc * kGateFloats;
         gt[lane] = p.q_scale * Gam;
         gt[64 + lane] = valid ? __builtin_amdgcn_exp2f(gam_n - gam) : 0.f;
-        if (lane == 0) gt[128] = __builtin_amdgcn_exp2f(gam_n);
+        if (lane == 0) {
+            gt[128] = __builtin_amdgcn_exp2f(gam_n);
+            gt[129] = gam_n;
+        }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -609,251 +638,530 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
 // ---------------------------------------------------------------------------
 // chain: the sequential state carry
 // ---------------------------------------------------------------------------
-// Workgroup = 4 waves = one (sequence, V head) and 16*kChainTiles columns of
-// its state.  Every product of a chunk is split over the four waves by rows:
-//   wave w computes Vnew and Q S for the chunk's tokens 16w .. 16w+15, owns
-//   (and updates) the state rows 32w .. 32w+31, and writes the outputs of
-//   its 16 tokens,
-// so each wave reads only its quarter of -W, q^, k^T and P.  Those operands
-// come straight from L2/HBM into registers, prefetched two chunks ahead; the
-// only exchanges are the fp16 copy of the state (B operand of W S and Q S)
-// and the two fp16 copies of Vnew (B operands of P Vnew and of the state
-// update), through small LDS buffers, with two barriers per chunk.
-constexpr int kChainTiles = 2;                         // 16-column tiles per workgroup
-constexpr int kChainBlocksPerHead = 8 / kChainTiles;   // workgroups per (sequence, V head)
-constexpr int kChainPrefetch = 2;                      // chunks in flight ahead of the one computed
+// Workgroup = one (segment, V head), 4 waves; wave w owns the state columns
+// 32w .. 32w+31 (two 16-column tiles) in every product of a chunk:
+//   Vnew = U' - W S                    64 tokens x 32 columns, over d_k
+//   Q S                                64 tokens x 32 columns, over d_k
+//   S <- Gam_n S + k^T (r Vnew)        d_k x 32 columns, over the chunk's tokens
+//   O = diag(q_scale Gam) Q S + P Vnew
+// The B operands of these products are the wave's own accumulators: with the
+// kappa k-mapping, a lane's accumulator rows 4q..4q+3 of two vertically
+// adjacent 16-row tiles are exactly its eight B-operand elements of the
+// 32-deep block they form, so the state and Vnew never leave the wave.  The
+// waves share only the chunk's A operands (-W, q^, k^T, P) and gates, which
+// the workgroup stages in LDS with direct-to-LDS loads into two buffers (one
+// barrier per chunk); U' goes straight to each wave's registers, and the chunk
+// after the next one is touched into L2 a step ahead.
+constexpr int kChainBlocksPerHead = 1;
+struct ChainBuf {
+    static constexpr int kW = 0, kQ = 16384, kK = 32768, kP = 49152, kG = 57344, kBytes = 58368;
+};
+constexpr int kChainStage = 64 * 32 * 2;  // output rows of one wave: 64 tokens x 32 columns bf16
 
-__device__ __forceinline__ half8 ld_frag(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+// raw buffer resource over `bytes` bytes at `base`: reads past the end return 0
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sized_rsrc(const void *base, int bytes)
 {
-    return __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
 }
 
-// this wave's operands of one chunk
-template <int CT>
-struct ChainOps {
-    half8 W[4];   // -W  rows 16w.., k-blocks 0..3 over d_k
-    half8 Q[4];   // q^  rows 16w.., k-blocks 0..3 over d_k
-    half8 K[4];   // k^T rows 32w + 16rr.., k-blocks 0..1 over tokens: index 2rr + kb
-    half8 P[2];   // P   rows 16w.., k-blocks 0..1 over tokens
-    half4 U[CT];  // U'  rows 16w.., column tiles of the workgroup
-    f32x4 gam;    // q_scale * Gam of rows 16w + 4q4 + e
-    f32x4 r;      // Gam_n / Gam of the same rows
-    float gn;     // Gam_n
-};
-
-template <int CT>
-__device__ __forceinline__ void chain_load(ChainOps<CT> &op, const Workspace &ws, long c, int h, int g, int Hqk,
-                                           int Hv, int ct0, int wave, int lane)
+// Chunk c's shared operands into one LDS buffer: 57 pieces of 1 KiB, piece
+// 4i + w by wave w (gates by wave 0).
+__device__ __forceinline__ void chain_dma(const Workspace &ws, uint8_t *buf, long c, int h, int g, int Hqk,
+                                          int Hv, int wave, int lane)
 {
     const long hc = c * Hv + h, gc = c * Hqk + g;
     const __amdgpu_buffer_rsrc_t rw = region_rsrc(ws.wfrag + hc * kWFragBytes);
     const __amdgpu_buffer_rsrc_t rq = region_rsrc(ws.qfrag + gc * kQFragBytes);
     const __amdgpu_buffer_rsrc_t rk = region_rsrc(ws.kfrag + gc * kKFragBytes);
     const __amdgpu_buffer_rsrc_t rp = region_rsrc(ws.pfrag + hc * kPFragBytes);
-    const __amdgpu_buffer_rsrc_t ru = region_rsrc(ws.ufrag + hc * kUBytes);
-    const __amdgpu_buffer_rsrc_t rg = region_rsrc(ws.gates + hc * kGateFloats);
     const int v16 = lane * 16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        op.W[i] = ld_frag(rw, v16, (wave * 4 + i) * 1024);
-        op.Q[i] = ld_frag(rq, v16, (wave * 4 + i) * 1024);
-        op.K[i] = ld_frag(rk, v16, (wave * 4 + i) * 1024);
+        const int f = 4 * i + wave;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)(buf + ChainBuf::kW + f * 1024), 16, v16, f * 1024, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void_t *)(buf + ChainBuf::kQ + f * 1024), 16, v16, f * 1024, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t *)(buf + ChainBuf::kK + f * 1024), 16, v16, f * 1024, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) op.P[i] = ld_frag(rp, v16, (wave * 2 + i) * 1024);
-#pragma unroll
-    for (int x = 0; x < CT; ++x)
-        op.U[x] = __builtin_bit_cast(half4, __builtin_amdgcn_raw_buffer_load_b64(ru, lane * 8, ((ct0 + x) * 4 + wave) * 512, 0));
-    const int row4 = (16 * wave + 4 * (lane >> 4)) * 4;
-    op.gam = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, row4, 0, 0));
-    op.r = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, row4, 256, 0));
-    op.gn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, 0, 512, 0));
+    for (int i = 0; i < 2; ++i) {
+        const int f = 4 * i + wave;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (lds_void_t *)(buf + ChainBuf::kP + f * 1024), 16, v16, f * 1024, 0, 0);
+    }
+    if (wave == 0) {
+        const __amdgpu_buffer_rsrc_t rg = region_rsrc(ws.gates + hc * kGateFloats);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (lds_void_t *)(buf + ChainBuf::kG), 16, v16, 0, 0, 0);
+    }
 }
 
-template <int CT>
-struct ChainLds {
-    half8 sx[4 * CT * 64];      // state as B operand: [k-block over d_k][tile][lane]
-    half8 vb[2 * CT * 64];      // Vnew as B operand:  [k-block over tokens][tile][lane]
-    half8 vr[2 * CT * 64];      // (Gam_n / Gam) Vnew as B operand
-    uint16_t os[4][16 * 16 * CT];  // output rows of each wave, bf16
+// U' of chunk c, this wave's two column tiles, all four token tiles (accumulator order)
+__device__ __forceinline__ void chain_load_u(half4 (&U)[4][2], const Workspace &ws, long c, int h, int Hv, int wave,
+                                             int lane)
+{
+    const __amdgpu_buffer_rsrc_t ru = region_rsrc(ws.ufrag + (c * Hv + h) * kUBytes);
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+            U[rt][x] = __builtin_bit_cast(half4, __builtin_amdgcn_raw_buffer_load_b64(ru, lane * 8, ((2 * wave + x) * 4 + rt) * 512, 0));
+}
+
+// One line in 128 bytes of a chunk's operands is read ahead into registers,
+// so that the data sits in L2 when the chunk's real loads are issued: ten
+// 8 KiB pieces (-W, q^, k^T, U' two each; P; gates), three per wave (wave 3
+// repeats two).  The values are folded into a junk word two steps later,
+// which keeps the loads alive without making anything wait for them early.
+// Piece i of chunk c starts at base[i] + c * stride[i].
+struct ChainTouch {
+    const uint8_t *base[3];
+    long stride[3];
+    int bytes[3];
 };
 
-// one chunk: consumes `op`, and issues the loads of chunk c + kChainPrefetch into `nxt`
-template <int CT>
-__device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace &ws, ChainLds<CT> &L,
-                                           f32x4 (&S)[CT][2], const ChainOps<CT> &op, ChainOps<CT> &nxt,
-                                           const int4 &si, int cc, int h, int g, int ct0, int wave, int lane)
+__device__ __forceinline__ ChainTouch chain_touch_plan(const Workspace &ws, int h, int g, int Hqk, int Hv, int wave)
+{
+    ChainTouch tp;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        int item = 4 * i + wave;
+        if (item >= 10) item -= 10;
+        const uint8_t *base;
+        long stride;
+        int bytes = 8192;
+        if (item < 2) {
+            base = ws.wfrag + (long)h * kWFragBytes + item * 8192;
+            stride = (long)Hv * kWFragBytes;
+        } else if (item < 4) {
+            base = ws.qfrag + (long)g * kQFragBytes + (item - 2) * 8192;
+            stride = (long)Hqk * kQFragBytes;
+        } else if (item < 6) {
+            base = ws.kfrag + (long)g * kKFragBytes + (item - 4) * 8192;
+            stride = (long)Hqk * kKFragBytes;
+        } else if (item < 8) {
+            base = ws.ufrag + (long)h * kUBytes + (item - 6) * 8192;
+            stride = (long)Hv * kUBytes;
+        } else if (item == 8) {
+            base = ws.pfrag + (long)h * kPFragBytes;
+            stride = (long)Hv * kPFragBytes;
+        } else {
+            base = reinterpret_cast<const uint8_t *>(ws.gates + (long)h * kGateFloats);
+            stride = (long)Hv * kGateFloats * 4;
+            bytes = kGateFloats * 4;
+        }
+        tp.base[i] = base;
+        tp.stride[i] = stride;
+        tp.bytes[i] = bytes;
+    }
+    return tp;
+}
+
+__device__ __forceinline__ void chain_touch(const ChainTouch &tp, long c, int lane, uint32_t (&tv)[3], uint32_t &junk)
+{
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        junk ^= tv[i];
+        tv[i] = __builtin_amdgcn_raw_buffer_load_b32(sized_rsrc(tp.base[i] + c * tp.stride[i], tp.bytes[i]),
+                                                     lane * 128, 0, 0);
+    }
+}
+
+// Chunk range of one run of the sequential pass: chunks [c_from, c_to) of a
+// sequence whose chunk 0 is c0 (first token t0, L tokens); chunks before c_out
+// only advance the state (their output stores are dropped).
+struct ChainRun {
+    int c0, t0, L;
+    int c_from, c_to, c_out;
+};
+
+// VMEM operations a wave issues after a chunk's operand DMA and before the
+// step that consumes it, not counting the output stores that may follow:
+// U' of that chunk (8) and the L2 touch (3).  Waiting down to this count
+// waits for the DMA (vector memory operations complete in issue order).
+constexpr int kChainVmemAfterDma = 8 + 3;
+constexpr int kChainTouchAhead = 2;  // chunks between the touch of a chunk and its use (the
+                                     // prologue and the two-step rotation assume 2)
+
+// s_waitcnt immediate that waits for vector memory operations only, until at
+// most n (< 64) are outstanding: vmcnt in bits 3:0 and 15:14, expcnt and
+// lgkmcnt at their no-wait maxima
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
+
+// One chunk from buffer `cur`; issues the next chunk's DMA into `nxt`, the
+// next chunk's U' into Un and the touch of the chunk kChainTouchAhead ahead.
+__device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace &ws, const uint8_t *cur,
+                                           uint8_t *nxt, uint8_t *stage, const ChainTouch &tp,
+                                           uint32_t (&tv)[3], uint32_t &junk, f32x4 (&S)[8][2],
+                                           const half4 (&U)[4][2], half4 (&Un)[4][2], const ChainRun &run,
+                                           int cc, int h, int g, int wave, int lane)
 {
     const int Hqk = p.Hqk, Hv = p.Hv;
     const int q4 = lane >> 4, c16 = lane & 15;
-    // always issued (past the end it re-reads the last chunk), so that every
-    // chunk has the same memory operations in flight and the waits stay exact
-    chain_load<CT>(nxt, ws, si.x + min(cc + kChainPrefetch, si.y - 1), h, g, Hqk, Hv, ct0, wave, lane);
+    // chunk cc's operands (DMA'd a step ago) have landed for every wave, and
+    // every wave is done with the buffer the next DMA overwrites
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kChainVmemAfterDma));
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    const int cn = min(cc + 1, run.c_to - 1);
+    chain_dma(ws, nxt, cn, h, g, Hqk, Hv, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    chain_load_u(Un, ws, cn, h, Hv, wave, lane);
+    chain_touch(tp, min(cc + kChainTouchAhead, run.c_to - 1), lane, tv, junk);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // 1. this wave's state rows 32w .. 32w+31 are k-block w of the B operand
+    const half8 *Wf = reinterpret_cast<const half8 *>(cur + ChainBuf::kW) + lane;
+    const half8 *Qf = reinterpret_cast<const half8 *>(cur + ChainBuf::kQ) + lane;
+    const half8 *Kf = reinterpret_cast<const half8 *>(cur + ChainBuf::kK) + lane;
+    const half8 *Pf = reinterpret_cast<const half8 *>(cur + ChainBuf::kP) + lane;
+    const float *gt = reinterpret_cast<const float *>(cur + ChainBuf::kG);
+
+    // Vnew = U' - W S and Q S over the four 32-row blocks of the state; the
+    // LDS fragments of block kb+1 are read while block kb multiplies
+    f32x4 Vn[4][2], QS[4][2];
 #pragma unroll
-    for (int x = 0; x < CT; ++x) L.sx[(wave * CT + x) * 64 + lane] = pack_h8(S[x][0], S[x][1]);
-    __syncthreads();
-    // 2. Vnew = U' - W S and Q S for tokens 16w .. 16w+15
-    f32x4 Vn[CT], QS[CT];
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int x = 0; x < CT; ++x) {
-        Vn[x] = f32x4{(float)op.U[x][0], (float)op.U[x][1], (float)op.U[x][2], (float)op.U[x][3]};
-        QS[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int x = 0; x < 2; ++x) {
+            Vn[rt][x] = f32x4{(float)U[rt][x][0], (float)U[rt][x][1], (float)U[rt][x][2], (float)U[rt][x][3]};
+            QS[rt][x] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    half8 aw[2][4], aq[2][4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        aw[0][rt] = Wf[(rt * 4) * 64];
+        aq[0][rt] = Qf[(rt * 4) * 64];
     }
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb) {
+        const int cb = kb & 1;
+        if (kb < 3) {
 #pragma unroll
-        for (int x = 0; x < CT; ++x) {
-            const half8 sb = L.sx[(kb * CT + x) * 64 + lane];
-            Vn[x] = mfma16(op.W[kb], sb, Vn[x]);
-            QS[x] = mfma16(op.Q[kb], sb, QS[x]);
-        }
-    // 3. publish Vnew (plain and scaled) as half of a token k-block of the B operands
-    {
-        const int kbt = wave >> 1, half = wave & 1;
-#pragma unroll
-        for (int x = 0; x < CT; ++x) {
-            const f32x4 vs = Vn[x] * op.r;
-            half4 hb, hr;
-            hb[0] = (_Float16)Vn[x][0]; hb[1] = (_Float16)Vn[x][1]; hb[2] = (_Float16)Vn[x][2]; hb[3] = (_Float16)Vn[x][3];
-            hr[0] = (_Float16)vs[0]; hr[1] = (_Float16)vs[1]; hr[2] = (_Float16)vs[2]; hr[3] = (_Float16)vs[3];
-            reinterpret_cast<half4 *>(&L.vb[(kbt * CT + x) * 64 + lane])[half] = hb;
-            reinterpret_cast<half4 *>(&L.vr[(kbt * CT + x) * 64 + lane])[half] = hr;
-        }
-    }
-    __syncthreads();
-    // 4. state rows 32w + 16rr: S <- Gam_n S + k^T (r Vnew)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int x = 0; x < CT; ++x) {
-            const half8 vr = L.vr[(kb * CT + x) * 64 + lane];
-#pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {
-                if (kb == 0) S[x][rr] = S[x][rr] * op.gn;
-                S[x][rr] = mfma16(op.K[2 * rr + kb], vr, S[x][rr]);
+            for (int rt = 0; rt < 4; ++rt) {
+                aw[cb ^ 1][rt] = Wf[(rt * 4 + kb + 1) * 64];
+                aq[cb ^ 1][rt] = Qf[(rt * 4 + kb + 1) * 64];
             }
         }
-    // 5. outputs of tokens 16w .. 16w+15: q_scale (diag(Gam) Q S + P Vnew)
-    const int tok0 = si.z + cc * kChunk;
-    const int n = min(kChunk, si.w - cc * kChunk);
+        __builtin_amdgcn_sched_barrier(0);
+        const half8 sb0 = pack_h8(S[2 * kb][0], S[2 * kb + 1][0]);
+        const half8 sb1 = pack_h8(S[2 * kb][1], S[2 * kb + 1][1]);
 #pragma unroll
-    for (int x = 0; x < CT; ++x) {
-        f32x4 acc = QS[x] * op.gam;
-        acc = mfma16(op.P[0], L.vb[(0 * CT + x) * 64 + lane], acc);
-        if (wave >= 2) acc = mfma16(op.P[1], L.vb[(1 * CT + x) * 64 + lane], acc);
+        for (int rt = 0; rt < 4; ++rt) {
+            Vn[rt][0] = mfma16(aw[cb][rt], sb0, Vn[rt][0]);
+            Vn[rt][1] = mfma16(aw[cb][rt], sb1, Vn[rt][1]);
+            QS[rt][0] = mfma16(aq[cb][rt], sb0, QS[rt][0]);
+            QS[rt][1] = mfma16(aq[cb][rt], sb1, QS[rt][1]);
+        }
+    }
+    // k^T fragments of the first two 16-row state tiles, P, and the gates
+    half8 kf[2][2][2];  // [buffer][tile in pair][token block]
 #pragma unroll
-        for (int e = 0; e < 4; ++e) L.os[wave][(4 * q4 + e) * (16 * CT) + 16 * x + c16] = (uint16_t)f32_to_bf16(acc[e]);
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) kf[0][i][tb] = Kf[(2 * i + tb) * 64];
+    half8 pf[6];  // P: row tiles 0, 1 (token block 0), 2, 3 (token blocks 0, 1)
+    pf[0] = Pf[0 * 64];
+    pf[1] = Pf[2 * 64];
+    pf[2] = Pf[4 * 64];
+    pf[3] = Pf[5 * 64];
+    pf[4] = Pf[6 * 64];
+    pf[5] = Pf[7 * 64];
+    f32x4 rg[4], gm[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        rg[rt] = *reinterpret_cast<const f32x4 *>(gt + 64 + 16 * rt + 4 * q4);
+        gm[rt] = *reinterpret_cast<const f32x4 *>(gt + 16 * rt + 4 * q4);
+    }
+    const float gn = gt[128];
+    __builtin_amdgcn_sched_barrier(0);
+    // Vnew and (Gam_n / Gam) Vnew as B operands over the chunk's two 32-token blocks
+    half8 vb[2][2], vr[2][2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            vb[tb][x] = pack_h8(Vn[2 * tb][x], Vn[2 * tb + 1][x]);
+            vr[tb][x] = pack_h8(Vn[2 * tb][x] * rg[2 * tb], Vn[2 * tb + 1][x] * rg[2 * tb + 1]);
+        }
+    // S <- Gam_n S + k^T (r Vnew), two state tiles at a time, the next pair's
+    // fragments read while this pair multiplies
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr) {
+        const int cb = pr & 1;
+        if (pr < 3) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) kf[cb ^ 1][i][tb] = Kf[(2 * (2 * pr + 2 + i) + tb) * 64];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int dt = 2 * pr + i;
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                S[dt][x] = mfma16(kf[cb][i][0], vr[0][x], S[dt][x] * gn);
+                S[dt][x] = mfma16(kf[cb][i][1], vr[1][x], S[dt][x]);
+            }
+        }
+    }
+    // O = diag(q_scale Gam) Q S + P Vnew (P lower triangular), staged as bf16 rows
+    uint16_t *os = reinterpret_cast<uint16_t *>(stage);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        const half8 p0 = pf[rt < 2 ? rt : 2 * rt - 2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            f32x4 acc = mfma16(p0, vb[0][x], QS[rt][x] * gm[rt]);
+            if (rt >= 2) acc = mfma16(pf[2 * rt - 1], vb[1][x], acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) os[(16 * rt + 4 * q4 + e) * 32 + 16 * x + c16] = (uint16_t)f32_to_bf16(acc[e]);
+        }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     {
-        // 16 rows x (32 CT bytes): lane -> (row, 16-byte piece).  A buffer
-        // store whose range ends at the chunk's last valid token drops the
-        // rows of a partial chunk without a branch.
-        static_assert(CT == 2, "one 16-byte piece per lane");
-        constexpr int kPieces = 2 * CT;
-        const int row = lane / kPieces, piece = lane % kPieces;
-        const i32x4 v = reinterpret_cast<const i32x4 *>(&L.os[wave][row * 16 * CT])[piece];
+        // 64 rows of 64 bytes: lane -> (row 16i + lane/4, 16-byte piece lane%4).
+        // The buffer range ends at the chunk's last valid token, so the rows
+        // of a partial chunk and every row of a warm-up chunk (n = 0) are
+        // dropped without a branch.
+        const int rel = (cc - run.c0) * kChunk;
+        const int n = cc >= run.c_out ? min(kChunk, run.L - rel) : 0;
         const int rowb = Hv * kD * 2;  // bytes per token row of o
         const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-            p.o + ((long)tok0 * Hv + h) * kD + 16 * ct0, 0, n * rowb, 0x00020000);
-        __builtin_amdgcn_raw_buffer_store_b128(v, ro, (16 * wave + row) * rowb + piece * 16, 0, 0);
+            p.o + ((long)(run.t0 + rel) * Hv + h) * kD + 32 * wave, 0, n * rowb, 0x00020000);
+        const int row = lane >> 2, piece = lane & 3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const i32x4 v = *reinterpret_cast<const i32x4 *>(stage + (16 * i + row) * 64 + piece * 16);
+            __builtin_amdgcn_raw_buffer_store_b128(v, ro, (16 * i + row) * rowb + piece * 16, 0, 0);
+        }
     }
 }
 
-template <int CT>
+// The chunks of one run, the state carried in registers.
+__device__ __forceinline__ void chain_run(const PrefillArgs &p, const Workspace &ws, uint8_t *buf0, uint8_t *buf1,
+                                          uint8_t *stage, f32x4 (&S)[8][2], const ChainRun &run, int h, int g,
+                                          int wave, int lane, uint32_t &junk)
+{
+    if (run.c_to <= run.c_from) return;
+    half4 U0[4][2], U1[4][2];
+    uint32_t T0[3] = {0, 0, 0}, T1[3] = {0, 0, 0};
+    const ChainTouch tp = chain_touch_plan(ws, h, g, p.Hqk, p.Hv, wave);
+    // prologue: the touch of the second chunk, the first chunk's operands
+    chain_touch(tp, min(run.c_from + 1, run.c_to - 1), lane, T1, junk);
+    chain_dma(ws, buf0, run.c_from, h, g, p.Hqk, p.Hv, wave, lane);
+    chain_load_u(U0, ws, run.c_from, h, p.Hv, wave, lane);
+    int cc = run.c_from;
+    for (; cc + 2 <= run.c_to; cc += 2) {
+        chain_step(p, ws, buf0, buf1, stage, tp, T0, junk, S, U0, U1, run, cc, h, g, wave, lane);
+        chain_step(p, ws, buf1, buf0, stage, tp, T1, junk, S, U1, U0, run, cc + 1, h, g, wave, lane);
+    }
+    if (cc < run.c_to) chain_step(p, ws, buf0, buf1, stage, tp, T0, junk, S, U0, U1, run, cc, h, g, wave, lane);
+    junk ^= T0[0] ^ T0[1] ^ T0[2] ^ T1[0] ^ T1[1] ^ T1[2];
+    // the last step's DMA into the other buffer is still in flight
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+}
+
+// Warm-up bound of the segmented sequential pass.  Every token's transition
+// alpha (I - beta k k^T) has spectral norm <= alpha (beta in (0,1), |k| <= 1),
+// so a state that enters w chunks before a segment reaches the segment's start
+// scaled by at most the product of those chunks' gates.  A segment therefore
+// starts from a zero state at the latest chunk w for which that product is
+// <= 2^-24 -- what it drops is below single-precision resolution of the state
+// it came from -- or from the sequence's own initial state when the sequence
+// start is within reach.
+constexpr float kWarmLog2 = -24.0f;
+constexpr int kMaxWarm = 64;  // chunks a segment looks back at most (one per lane)
+
+// First chunk of the run of the segment that starts at chunk cb (sequence
+// chunk 0 = c0): c0 (exact start from the initial state), a chunk in
+// (c0, cb) (start from zero), or -1 when the bound is not met within
+// kMaxWarm chunks.  Wave-uniform, and identical in every block that asks.
+__device__ __forceinline__ int warm_start(const Workspace &ws, int h, int Hv, int cb, int c0, int lane)
+{
+    if (cb <= c0) return c0;
+    const int c = cb - 1 - lane;
+    const bool in = c >= c0;
+    float gsum = in ? ws.gates[((long)c * Hv + h) * kGateFloats + 129] : 0.f;
+    // inclusive prefix over lanes: log2 of the decay of chunks cb-1-lane .. cb-1
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(gsum, off, 64);
+        if (lane >= off) gsum += y;
+    }
+    const unsigned long long hit = __ballot(in && gsum <= kWarmLog2);
+    int w;
+    if (hit) w = cb - 1 - __builtin_ctzll(hit);
+    else w = (cb - c0 <= kMaxWarm) ? c0 : -1;
+    return __builtin_amdgcn_readfirstlane(w);
+}
+
+// state columns 32w .. 32w+31 of one (sequence, head): tile (dt, x) element e
+// is row 16dt + 4q + e, column 32w + 16x + c16
+__device__ __forceinline__ void state_load(f32x4 (&S)[8][2], const float *src, int wave, int lane)
+{
+    const int q4 = lane >> 4, c16 = lane & 15;
+    if (!src) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int x = 0; x < 2; ++x) S[dt][x] = f32x4{0.f, 0.f, 0.f, 0.f};
+        return;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                S[dt][x][e] = src[(long)(16 * dt + 4 * q4 + e) * kD + 32 * wave + 16 * x + c16];
+}
+__device__ __forceinline__ void state_store(const f32x4 (&S)[8][2], float *dst, int wave, int lane)
+{
+    const int q4 = lane >> 4, c16 = lane & 15;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                dst[(long)(16 * dt + 4 * q4 + e) * kD + 32 * wave + 16 * x + c16] = S[dt][x][e];
+}
+
+// Sequential pass.  kRepair = false: one workgroup per (segment, V head);
+// segments run in parallel, each from its warm-up start.  kRepair = true: one
+// workgroup per (sequence, V head), which walks the sequence's segments in
+// order and recomputes, exactly from the state the previous segment handed
+// over, those whose warm-up bound was not met; it also hands each sequence of
+// several segments its final state.
+template <bool kRepair>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void chain_kernel(PrefillArgs p, Workspace ws)
 {
-    __shared__ ChainLds<CT> L;
+    __shared__ __attribute__((aligned(16))) uint8_t buf0[ChainBuf::kBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t buf1[ChainBuf::kBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_all[4 * kChainStage];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int q4 = lane >> 4, c16 = lane & 15;
+    uint8_t *stage = stage_all + wave * kChainStage;
+    uint32_t junk = 0;
     const int Hqk = p.Hqk, Hv = p.Hv, G = Hv / Hqk;
-    constexpr int kPerHead = 8 / CT;
-    // block -> (rank, group, head-in-group, column block); all workgroups of
-    // one (sequence, QK group) land on the same XCD (same L2)
-    const int per_group = G * kPerHead;
+    // block -> (segment or rank, group, head in group); the G heads of one
+    // (segment, QK group) land on the same XCD (same L2)
     const int bid = blockIdx.x;
-    const int gu = (bid / (8 * per_group)) * 8 + (bid & 7);
-    const int inner = (bid >> 3) % per_group;
-    if (gu >= p.N * Hqk) return;
-    const int rank = gu / Hqk, g = gu % Hqk;
-    const int j = inner / kPerHead, cb = inner % kPerHead;
+    const int gu = (bid / (8 * G)) * 8 + (bid & 7);
+    const int j = (bid >> 3) % G;
+    if (gu >= (kRepair ? p.N : p.max_segs) * Hqk) return;
+    const int unit = gu / Hqk, g = gu % Hqk;
     const int h = g * G + j;
-    const int ct0 = cb * CT;
-    const int s = ws.order[rank];
-    const int4 si = ws.seq_info[s];  // chunk0, nchunks, t0, L
+    f32x4 S[8][2];
 
-    // state rows 32w + 16rr + 4q4 + e, columns 16(ct0 + x) + c16
-    f32x4 S[CT][2];
-    const long sbase = ((long)s * Hv + h) * kD * kD;
+    if (!kRepair) {
+        const int k = unit;
+        const int4 sg = ws.seg_info[k];  // seq, first chunk, end chunk, flags
+        if (sg.x < 0) return;
+        const int s = sg.x;
+        const int4 si = ws.seq_info[s];  // chunk0, nchunks, t0, L
+        const bool first = sg.w & 1, last = sg.w & 2;
+        const int w = first ? sg.y : warm_start(ws, h, Hv, sg.y, si.x, lane);
+        if (!first && t == 0) ws.seg_bad[(long)k * Hv + h] = w < 0;
+        if (w < 0) return;  // recomputed in order by the repair pass
+        const long sbase = ((long)s * Hv + h) * kD * kD;
+        state_load(S, w == si.x && p.state_in ? p.state_in + sbase : nullptr, wave, lane);
+        chain_run(p, ws, buf0, buf1, stage, S, ChainRun{si.x, si.z, si.w, w, sg.z, sg.y}, h, g, wave, lane, junk);
+        // Final states: a sequence of one segment writes state_out itself.
+        // Otherwise other blocks of this sequence may still read state_in
+        // (which state_out may alias), so every segment parks its final state
+        // and the repair pass, which runs after this one, hands it to the
+        // next segment if that one is recomputed, and moves the last one.
+        state_store(S, last && first ? p.state_out + sbase : ws.bstate + ((long)k * Hv + h) * kStateFloats, wave, lane);
+        // carried conv rows: the last three raw rows of the sequence (v
+        // channels of head h; the first head of the group also writes the q
+        // and k channels)
+        if (first && p.conv_state_out && wave == 0) {
+            const long C_tot = 2L * Hqk * kD + (long)Hv * kD;
+            const int Ls = si.w, t0 = si.z;
+            for (int plane = (j == 0 ? 0 : 2); plane < 3; ++plane) {
+                const long ch0 = plane == 0 ? (long)g * kD : plane == 1 ? (long)Hqk * kD + (long)g * kD
+                                                                      : 2L * Hqk * kD + (long)h * kD;
+                const uint16_t *src = plane == 0 ? p.q + (long)g * kD : plane == 1 ? p.k + (long)g * kD
+                                                                                  : p.v + (long)h * kD;
+                const long ld = plane == 2 ? (long)Hv * kD : (long)Hqk * kD;
 #pragma unroll
-    for (int x = 0; x < CT; ++x)
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                S[x][rr][e] = p.state_in ? p.state_in[sbase + (long)(32 * wave + 16 * rr + 4 * q4 + e) * kD +
-                                                      16 * (ct0 + x) + c16]
-                                         : 0.f;
-
-    if (si.y > 0) {
-        // three operand sets rotate: chunk cc is computed while cc+1 and cc+2 load
-        ChainOps<CT> o0, o1, o2;
-        chain_load<CT>(o0, ws, si.x, h, g, Hqk, Hv, ct0, wave, lane);
-        chain_load<CT>(o1, ws, si.x + min(1, si.y - 1), h, g, Hqk, Hv, ct0, wave, lane);
-        int cc = 0;
-        for (; cc + 3 <= si.y; cc += 3) {
-            chain_step<CT>(p, ws, L, S, o0, o2, si, cc, h, g, ct0, wave, lane);
-            chain_step<CT>(p, ws, L, S, o1, o0, si, cc + 1, h, g, ct0, wave, lane);
-            chain_step<CT>(p, ws, L, S, o2, o1, si, cc + 2, h, g, ct0, wave, lane);
-        }
-        if (cc < si.y) chain_step<CT>(p, ws, L, S, o0, o2, si, cc, h, g, ct0, wave, lane);
-        if (cc + 1 < si.y) chain_step<CT>(p, ws, L, S, o1, o0, si, cc + 1, h, g, ct0, wave, lane);
-    }
-
-#pragma unroll
-    for (int x = 0; x < CT; ++x)
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                p.state_out[sbase + (long)(32 * wave + 16 * rr + 4 * q4 + e) * kD + 16 * (ct0 + x) + c16] = S[x][rr][e];
-
-    // carried conv rows: the last three raw rows of the sequence (v channels of
-    // head h; the first head of the group also writes the q and k channels)
-    if (p.conv_state_out && cb == 0 && wave == 0) {
-        const long C_tot = 2L * Hqk * kD + (long)Hv * kD;
-        const int Ls = si.w, t0 = si.z;
-        for (int plane = (j == 0 ? 0 : 2); plane < 3; ++plane) {
-            const long ch0 = plane == 0 ? (long)g * kD : plane == 1 ? (long)Hqk * kD + (long)g * kD
-                                                                  : 2L * Hqk * kD + (long)h * kD;
-            const uint16_t *src = plane == 0 ? p.q + (long)g * kD : plane == 1 ? p.k + (long)g * kD
-                                                                              : p.v + (long)h * kD;
-            const long ld = plane == 2 ? (long)Hv * kD : (long)Hqk * kD;
-#pragma unroll
-            for (int r = 0; r < 3; ++r) {
-                const int tau = Ls - 3 + r;
-                uint32_t val = 0;
-                if (tau >= 0)
-                    val = ld_pair(src + (long)(t0 + tau) * ld + 2 * lane);
-                else if (p.conv_state_in)
-                    val = ld_pair(p.conv_state_in + ((long)s * 3 + 3 + tau) * C_tot + ch0 + 2 * lane);
-                *reinterpret_cast<uint32_t *>(p.conv_state_out + ((long)s * 3 + r) * C_tot + ch0 + 2 * lane) = val;
+                for (int r = 0; r < 3; ++r) {
+                    const int tau = Ls - 3 + r;
+                    uint32_t val = 0;
+                    if (tau >= 0)
+                        val = ld_pair(src + (long)(t0 + tau) * ld + 2 * lane);
+                    else if (p.conv_state_in)
+                        val = ld_pair(p.conv_state_in + ((long)s * 3 + 3 + tau) * C_tot + ch0 + 2 * lane);
+                    *reinterpret_cast<uint32_t *>(p.conv_state_out + ((long)s * 3 + r) * C_tot + ch0 + 2 * lane) = val;
+                }
             }
         }
+    } else {
+        const int s = ws.order[unit];
+        const int4 si = ws.seq_info[s];
+        const int4 ss = ws.seq_seg[s];  // first segment, segments
+        const long sbase = ((long)s * Hv + h) * kD * kD;
+        const int nseg = min(ss.y, p.max_segs - ss.x);
+        bool carry = false;  // S holds the final state of the previous segment
+        for (int i = 1; i < nseg; ++i) {  // a sequence's first segment is never recomputed
+            const int k = ss.x + i;
+            if (!ws.seg_bad[(long)k * Hv + h]) {
+                carry = false;
+                continue;
+            }
+            if (!carry) state_load(S, ws.bstate + ((long)(k - 1) * Hv + h) * kStateFloats, wave, lane);
+            const int4 sg = ws.seg_info[k];
+            chain_run(p, ws, buf0, buf1, stage, S, ChainRun{si.x, si.z, si.w, sg.y, sg.z, sg.y}, h, g, wave, lane, junk);
+            carry = true;
+        }
+        // the final state of a sequence of several segments
+        if (nseg > 1) {
+            if (!carry) state_load(S, ws.bstate + ((long)(ss.x + nseg - 1) * Hv + h) * kStateFloats, wave, lane);
+            state_store(S, p.state_out + sbase, wave, lane);
+        }
     }
+    // consumes the touch values under a condition no valid call meets (N >= 0)
+    if (p.N < 0 && junk == 1u) ws.seg_bad[0] = 0;
 }
 
 }  // namespace
 
+int choose_seg_chunks(int max_chunks, int N, int Hv)
+{
+    // Makespan model of the segmented sequential pass, for sequences of the
+    // mean length: blocks = segments x Hv, run in rounds of kSlots resident
+    // blocks (256 CUs, one block each), each round as long as a segment plus
+    // a few warm-up chunks.  The cheapest cut wins; ties go to
+    // longer segments.
+    constexpr long kSlots = 256;
+    constexpr int kWarmGuess = 4, kMinSeg = 8;
+    if (N <= 0 || max_chunks <= 0) return kMinSeg;
+    const int nch = (max_chunks + N - 1) / N;
+    if (nch <= kMinSeg) return kMinSeg;
+    const long units = (long)N * Hv * kChainBlocksPerHead;
+    long best_cost = -1;
+    int best = nch;
+    // for a given number of segments the shortest even cut is the best one
+    for (int nseg = 1;; ++nseg) {
+        const int Ls = (nch + nseg - 1) / nseg;
+        if (nseg > 1 && Ls < kMinSeg) break;
+        const long rounds = (units * nseg + kSlots - 1) / kSlots;
+        const long cost = rounds * (Ls + (nseg > 1 ? kWarmGuess : 0));
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best = Ls;
+        }
+    }
+    return best;
+}
+
 size_t prefill_workspace_bytes(int max_chunks, int N, int Hqk, int Hv)
 {
     const size_t C = (size_t)max_chunks;
+    const size_t M = (size_t)max_segments(max_chunks, N, choose_seg_chunks(max_chunks, N, Hv));
     size_t total = 0;
     total += align256(C * sizeof(int4));
     total += align256((size_t)N * sizeof(int4));
@@ -865,12 +1173,17 @@ size_t prefill_workspace_bytes(int max_chunks, int N, int Hqk, int Hv)
     total += align256(C * Hv * kUBytes);
     total += align256(C * Hv * kPFragBytes);
     total += align256(C * Hv * kGateFloats * sizeof(float));
+    total += align256(M * sizeof(int4));
+    total += align256((size_t)N * sizeof(int4));
+    total += align256(M * Hv * sizeof(int));
+    total += align256(M * Hv * kStateFloats * sizeof(float));
     return total;
 }
 
 Workspace carve_workspace(void *base, int max_chunks, int N, int Hqk, int Hv)
 {
     const size_t C = (size_t)max_chunks;
+    const size_t M = (size_t)max_segments(max_chunks, N, choose_seg_chunks(max_chunks, N, Hv));
     uint8_t *ptr = static_cast<uint8_t *>(base);
     Workspace ws;
     auto take = [&](size_t bytes) {
@@ -888,6 +1201,10 @@ Workspace carve_workspace(void *base, int max_chunks, int N, int Hqk, int Hv)
     ws.ufrag = take(C * Hv * kUBytes);
     ws.pfrag = take(C * Hv * kPFragBytes);
     ws.gates = reinterpret_cast<float *>(take(C * Hv * kGateFloats * sizeof(float)));
+    ws.seg_info = reinterpret_cast<int4 *>(take(M * sizeof(int4)));
+    ws.seq_seg = reinterpret_cast<int4 *>(take((size_t)N * sizeof(int4)));
+    ws.seg_bad = reinterpret_cast<int *>(take(M * Hv * sizeof(int)));
+    ws.bstate = reinterpret_cast<float *>(take(M * Hv * kStateFloats * sizeof(float)));
     return ws;
 }
 
@@ -911,9 +1228,13 @@ hipError_t launch_prefill(const PrefillArgs &p, void *workspace, hipStream_t str
     }
     if ((e = mark(2)) != hipSuccess) return e;
     const int G = p.Hv / p.Hqk;
+    const long seg_groups = (long)p.max_segs * p.Hqk;
+    const long seg_blocks = ((seg_groups + 7) / 8) * 8L * G;
+    hipLaunchKernelGGL(chain_kernel<false>, dim3((unsigned)seg_blocks), dim3(256), 0, stream, p, ws);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     const long groups = (long)p.N * p.Hqk;
-    const long blocks = ((groups + 7) / 8) * 8L * G * kChainBlocksPerHead;
-    hipLaunchKernelGGL(chain_kernel<kChainTiles>, dim3((unsigned)blocks), dim3(256), 0, stream, p, ws);
+    const long blocks = ((groups + 7) / 8) * 8L * G;
+    hipLaunchKernelGGL(chain_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, p, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return mark(3);
 }

@@ -89,6 +89,31 @@ def test_varlen_small_with_empty_sequences(oracle_lib):
     np.testing.assert_array_equal(so.cpu().numpy()[[0, 3]], x["state_in"][[0, 3]])
 
 
+def test_segmented_pass_weak_and_strong_decay(oracle_lib):
+    """A sequence long enough for the sequential pass to be cut into segments.
+    V heads 0-2 barely decay (alpha ~ 1), except over tokens 4000-4399 where
+    they decay hard: their segments within 64 chunks of the start restart
+    from the initial state, those just after the strong stretch start from a
+    truncated warm-up, and the rest miss the warm-up bound and are recomputed
+    in order from the state handed over.  Heads 3-5 decay as usual."""
+    T = 8192 + 37
+    x = inputs.make_prefill(T_list=[T], Hqk=2, Hv=6, seed=510, state_std=0.05, conv_state_std=1.0)
+    x["a"][:, :3] = -9.0
+    x["a"][4000:4400, :3] = 5.0
+    o, so, cso = gpu_prefill(x, uniform_T=T)
+    compare(x, o, so, cso)
+
+
+def test_segmented_varlen_mixed_decay(oracle_lib):
+    """Packed sequences of several lengths cut into segments, two V heads
+    without decay (recomputed in order) beside normally decaying ones."""
+    x = inputs.make_prefill(T_list=[5000, 300, 9001, 0, 4500], Hqk=2, Hv=6, seed=511, state_std=0.05)
+    x["a"][:, 1] = -9.0
+    x["a"][:, 4] = -9.0
+    o, so, cso = gpu_prefill(x)
+    compare(x, o, so, cso)
+
+
 def test_zero_length_batch_copies_state(oracle_lib):
     x = inputs.make_prefill(T_list=[0, 0], Hqk=2, Hv=6, seed=501, state_std=0.05, conv_state_std=1.0)
     o, so, cso = gpu_prefill(x, uniform_T=0)
