@@ -588,9 +588,11 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
         }
     }
     __syncthreads();
-    // ---- U' = T' V: column tiles 2*wave, 2*wave+1; stored in accumulator order
+    // ---- U' = T' V: column tiles 2*wave, 2*wave+1; stored as B operands over
+    //      the chunk's two 32-token blocks (the accumulator rows of token tiles
+    //      2tb and 2tb+1 side by side): fragment ct*2 + tb
     {
-        half4 *uf = reinterpret_cast<half4 *>(ws.ufrag + hc * kUBytes);
+        half8 *uf = reinterpret_cast<half8 *>(ws.ufrag + hc * kUBytes);
         half8 ta[4][2];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
@@ -602,16 +604,15 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
             const int ct = 2 * wave + cti;
             const half8 b0 = lds_frag(VTs, kH_LD, 16 * ct, 0, lane);
             const half8 b1 = lds_frag(VTs, kH_LD, 16 * ct, 32, lane);
+            f32x4 acc[4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mfma16(ta[rt][0], b0, acc);
-                if (rt >= 2) acc = mfma16(ta[rt][1], b1, acc);
-                half4 hv;
-                hv[0] = (_Float16)acc[0]; hv[1] = (_Float16)acc[1];
-                hv[2] = (_Float16)acc[2]; hv[3] = (_Float16)acc[3];
-                uf[(ct * 4 + rt) * 64 + lane] = hv;
+                acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                acc[rt] = mfma16(ta[rt][0], b0, acc[rt]);
+                if (rt >= 2) acc[rt] = mfma16(ta[rt][1], b1, acc[rt]);
             }
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) uf[(ct * 2 + tb) * 64 + lane] = pack_h8(acc[2 * tb], acc[2 * tb + 1]);
         }
     }
     // ---- W^T = K^T diag(Gam) T'^T: d tiles 2*wave, 2*wave+1 (k-block `wave`
@@ -648,15 +649,15 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
 // kappa k-mapping, a lane's accumulator rows 4q..4q+3 of two vertically
 // adjacent 16-row tiles are exactly its eight B-operand elements of the
 // 32-deep block they form, so the state and Vnew never leave the wave.  The
-// waves share only the chunk's A operands (-W, q^, k^T, P) and gates, which
-// the workgroup stages in LDS with direct-to-LDS loads into two buffers (one
-// barrier per chunk); U' goes straight to each wave's registers, and the chunk
-// after the next one is touched into L2 a step ahead.
+// waves share only the chunk's operands (-W, q^, k^T, P, U', gates), which the
+// workgroup stages in LDS with direct-to-LDS loads into two buffers, one
+// barrier per chunk; the only other memory operations are the output stores,
+// so waiting for a chunk's operands never waits for the stores.
 constexpr int kChainBlocksPerHead = 1;
+constexpr int kChainStage = 32 * 32 * 2;  // output staging of one wave: 32 tokens x 32 columns bf16
 struct ChainBuf {
-    static constexpr int kW = 0, kQ = 16384, kK = 32768, kP = 49152, kG = 57344, kBytes = 58368;
+    static constexpr int kW = 0, kQ = 16384, kK = 32768, kP = 49152, kU = 57344, kG = 73728, kBytes = 74752;
 };
-constexpr int kChainStage = 64 * 32 * 2;  // output rows of one wave: 64 tokens x 32 columns bf16
 
 // raw buffer resource over `bytes` bytes at `base`: reads past the end return 0
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t sized_rsrc(const void *base, int bytes)
@@ -664,104 +665,47 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t sized_rsrc(const void *base, i
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
 }
 
-// Chunk c's shared operands into one LDS buffer: 57 pieces of 1 KiB, piece
-// 4i + w by wave w (gates by wave 0).
+// Chunk c's operands into one LDS buffer: 73 pieces of 1 KiB; wave w moves
+// pieces 4i + w of -W, q^, k^T (i < 4) and P (i < 2), pieces 4w + i of U'
+// (its own two column tiles), and wave 0 the gates.  Issued in four groups
+// (i = 0..3), spread through a chunk step so that the memory unit takes them
+// while the matrix cores work.
+struct ChainDma {
+    __amdgpu_buffer_rsrc_t rw, rq, rk, rp, ru, rg;
+};
+
+__device__ __forceinline__ ChainDma chain_dma_plan(const Workspace &ws, long c, int h, int g, int Hqk, int Hv)
+{
+    const long hc = c * Hv + h, gc = c * Hqk + g;
+    return ChainDma{region_rsrc(ws.wfrag + hc * kWFragBytes), region_rsrc(ws.qfrag + gc * kQFragBytes),
+                    region_rsrc(ws.kfrag + gc * kKFragBytes), region_rsrc(ws.pfrag + hc * kPFragBytes),
+                    region_rsrc(ws.ufrag + hc * kUBytes), region_rsrc(ws.gates + hc * kGateFloats)};
+}
+
+template <int I>
+__device__ __forceinline__ void chain_dma_group(const ChainDma &d, uint8_t *buf, int wave, int lane)
+{
+    const int f = 4 * I + wave, v16 = lane * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rw, (lds_void_t *)(buf + ChainBuf::kW + f * 1024), 16, v16, f * 1024, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rq, (lds_void_t *)(buf + ChainBuf::kQ + f * 1024), 16, v16, f * 1024, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rk, (lds_void_t *)(buf + ChainBuf::kK + f * 1024), 16, v16, f * 1024, 0, 0);
+    if (I < 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rp, (lds_void_t *)(buf + ChainBuf::kP + f * 1024), 16, v16, f * 1024, 0, 0);
+    if (I == 2 && wave == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rg, (lds_void_t *)(buf + ChainBuf::kG), 16, v16, 0, 0, 0);
+    // U': the wave's own 4 KiB (its two column tiles)
+    const int fu = 4 * wave + I;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ru, (lds_void_t *)(buf + ChainBuf::kU + fu * 1024), 16, v16, fu * 1024, 0, 0);
+}
+
 __device__ __forceinline__ void chain_dma(const Workspace &ws, uint8_t *buf, long c, int h, int g, int Hqk,
                                           int Hv, int wave, int lane)
 {
-    const long hc = c * Hv + h, gc = c * Hqk + g;
-    const __amdgpu_buffer_rsrc_t rw = region_rsrc(ws.wfrag + hc * kWFragBytes);
-    const __amdgpu_buffer_rsrc_t rq = region_rsrc(ws.qfrag + gc * kQFragBytes);
-    const __amdgpu_buffer_rsrc_t rk = region_rsrc(ws.kfrag + gc * kKFragBytes);
-    const __amdgpu_buffer_rsrc_t rp = region_rsrc(ws.pfrag + hc * kPFragBytes);
-    const int v16 = lane * 16;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int f = 4 * i + wave;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)(buf + ChainBuf::kW + f * 1024), 16, v16, f * 1024, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void_t *)(buf + ChainBuf::kQ + f * 1024), 16, v16, f * 1024, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t *)(buf + ChainBuf::kK + f * 1024), 16, v16, f * 1024, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int f = 4 * i + wave;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (lds_void_t *)(buf + ChainBuf::kP + f * 1024), 16, v16, f * 1024, 0, 0);
-    }
-    if (wave == 0) {
-        const __amdgpu_buffer_rsrc_t rg = region_rsrc(ws.gates + hc * kGateFloats);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (lds_void_t *)(buf + ChainBuf::kG), 16, v16, 0, 0, 0);
-    }
-}
-
-// U' of chunk c, this wave's two column tiles, all four token tiles (accumulator order)
-__device__ __forceinline__ void chain_load_u(half4 (&U)[4][2], const Workspace &ws, long c, int h, int Hv, int wave,
-                                             int lane)
-{
-    const __amdgpu_buffer_rsrc_t ru = region_rsrc(ws.ufrag + (c * Hv + h) * kUBytes);
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-            U[rt][x] = __builtin_bit_cast(half4, __builtin_amdgcn_raw_buffer_load_b64(ru, lane * 8, ((2 * wave + x) * 4 + rt) * 512, 0));
-}
-
-// One line in 128 bytes of a chunk's operands is read ahead into registers,
-// so that the data sits in L2 when the chunk's real loads are issued: ten
-// 8 KiB pieces (-W, q^, k^T, U' two each; P; gates), three per wave (wave 3
-// repeats two).  The values are folded into a junk word two steps later,
-// which keeps the loads alive without making anything wait for them early.
-// Piece i of chunk c starts at base[i] + c * stride[i].
-struct ChainTouch {
-    const uint8_t *base[3];
-    long stride[3];
-    int bytes[3];
-};
-
-__device__ __forceinline__ ChainTouch chain_touch_plan(const Workspace &ws, int h, int g, int Hqk, int Hv, int wave)
-{
-    ChainTouch tp;
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-        int item = 4 * i + wave;
-        if (item >= 10) item -= 10;
-        const uint8_t *base;
-        long stride;
-        int bytes = 8192;
-        if (item < 2) {
-            base = ws.wfrag + (long)h * kWFragBytes + item * 8192;
-            stride = (long)Hv * kWFragBytes;
-        } else if (item < 4) {
-            base = ws.qfrag + (long)g * kQFragBytes + (item - 2) * 8192;
-            stride = (long)Hqk * kQFragBytes;
-        } else if (item < 6) {
-            base = ws.kfrag + (long)g * kKFragBytes + (item - 4) * 8192;
-            stride = (long)Hqk * kKFragBytes;
-        } else if (item < 8) {
-            base = ws.ufrag + (long)h * kUBytes + (item - 6) * 8192;
-            stride = (long)Hv * kUBytes;
-        } else if (item == 8) {
-            base = ws.pfrag + (long)h * kPFragBytes;
-            stride = (long)Hv * kPFragBytes;
-        } else {
-            base = reinterpret_cast<const uint8_t *>(ws.gates + (long)h * kGateFloats);
-            stride = (long)Hv * kGateFloats * 4;
-            bytes = kGateFloats * 4;
-        }
-        tp.base[i] = base;
-        tp.stride[i] = stride;
-        tp.bytes[i] = bytes;
-    }
-    return tp;
-}
-
-__device__ __forceinline__ void chain_touch(const ChainTouch &tp, long c, int lane, uint32_t (&tv)[3], uint32_t &junk)
-{
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-        junk ^= tv[i];
-        tv[i] = __builtin_amdgcn_raw_buffer_load_b32(sized_rsrc(tp.base[i] + c * tp.stride[i], tp.bytes[i]),
-                                                     lane * 128, 0, 0);
-    }
+    const ChainDma d = chain_dma_plan(ws, c, h, g, Hqk, Hv);
+    chain_dma_group<0>(d, buf, wave, lane);
+    chain_dma_group<1>(d, buf, wave, lane);
+    chain_dma_group<2>(d, buf, wave, lane);
+    chain_dma_group<3>(d, buf, wave, lane);
 }
 
 // Chunk range of one run of the sequential pass: chunks [c_from, c_to) of a
@@ -773,25 +717,37 @@ struct ChainRun {
 };
 
 // VMEM operations a wave issues after a chunk's operand DMA and before the
-// step that consumes it, not counting the output stores that may follow:
-// U' of that chunk (8) and the L2 touch (3).  Waiting down to this count
-// waits for the DMA (vector memory operations complete in issue order).
-constexpr int kChainVmemAfterDma = 8 + 3;
-constexpr int kChainTouchAhead = 2;  // chunks between the touch of a chunk and its use (the
-                                     // prologue and the two-step rotation assume 2)
+// step that consumes it: the previous chunk's output stores (4).  Waiting
+// down to this count waits for the DMA (vector memory operations complete in
+// issue order) and leaves the stores in flight.
+constexpr int kChainVmemAfterDma = 4;
 
 // s_waitcnt immediate that waits for vector memory operations only, until at
 // most n (< 64) are outstanding: vmcnt in bits 3:0 and 15:14, expcnt and
 // lgkmcnt at their no-wait maxima
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
 
-// One chunk from buffer `cur`; issues the next chunk's DMA into `nxt`, the
-// next chunk's U' into Un and the touch of the chunk kChainTouchAhead ahead.
-__device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace &ws, const uint8_t *cur,
-                                           uint8_t *nxt, uint8_t *stage, const ChainTouch &tp,
-                                           uint32_t (&tv)[3], uint32_t &junk, f32x4 (&S)[8][2],
-                                           const half4 (&U)[4][2], half4 (&Un)[4][2], const ChainRun &run,
-                                           int cc, int h, int g, int wave, int lane)
+// Identity operand that copies rows 16*odd .. 16*odd+15 of a 32-deep B block
+// into a 16-row accumulator: lane (q, c) holds A[c][kappa(q, i)].
+__device__ __forceinline__ half8 eye_frag(int odd, int lane)
+{
+    const int q4 = lane >> 4, c16 = lane & 15;
+    half8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (_Float16)((q4 == (c16 >> 2) && i == 4 * odd + (c16 & 3)) ? 1.0f : 0.0f);
+    return r;
+}
+
+// One chunk from buffer `cur`; issues the next chunk's DMA into `nxt`.
+//   Vn  [rt][x]  Vnew, tokens 16rt.. x columns 16x..  (accumulator rows = tokens)
+//   QST [x][rt]  (Q S)^T, columns 16x.. x tokens 16rt.. (accumulator rows = columns)
+// The output is formed transposed, O^T = S^T Q^T diag(q_scale Gam) + Vnew^T P^T,
+// so that a lane holds four adjacent columns of one token (8-byte LDS writes
+// into the row staging).  The fragment layout is the same for A and B
+// operands, so the packed state and Vnew serve as A operands unchanged.
+__device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace &ws, uint8_t *cur, uint8_t *nxt,
+                                           uint8_t *stage, f32x4 (&S)[8][2], const half8 (&eye)[2],
+                                           const ChainRun &run, int cc, int h, int g, int wave, int lane)
 {
     const int Hqk = p.Hqk, Hv = p.Hv;
     const int q4 = lane >> 4, c16 = lane & 15;
@@ -801,27 +757,25 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     const int cn = min(cc + 1, run.c_to - 1);
-    chain_dma(ws, nxt, cn, h, g, Hqk, Hv, wave, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    chain_load_u(Un, ws, cn, h, Hv, wave, lane);
-    chain_touch(tp, min(cc + kChainTouchAhead, run.c_to - 1), lane, tv, junk);
-    __builtin_amdgcn_sched_barrier(0);
+    const ChainDma dn = chain_dma_plan(ws, cn, h, g, Hqk, Hv);
 
     const half8 *Wf = reinterpret_cast<const half8 *>(cur + ChainBuf::kW) + lane;
     const half8 *Qf = reinterpret_cast<const half8 *>(cur + ChainBuf::kQ) + lane;
     const half8 *Kf = reinterpret_cast<const half8 *>(cur + ChainBuf::kK) + lane;
     const half8 *Pf = reinterpret_cast<const half8 *>(cur + ChainBuf::kP) + lane;
+    const half8 *Uf = reinterpret_cast<const half8 *>(cur + ChainBuf::kU) + (4 * wave) * 64 + lane;
     const float *gt = reinterpret_cast<const float *>(cur + ChainBuf::kG);
 
-    // Vnew = U' - W S and Q S over the four 32-row blocks of the state; the
-    // LDS fragments of block kb+1 are read while block kb multiplies
-    f32x4 Vn[4][2], QS[4][2];
+    // W S and (Q S)^T over the four 32-row blocks of the state; the LDS
+    // fragments of block kb+1 are read while block kb multiplies, and the
+    // next chunk's DMA goes out one group per block
+    f32x4 Vn[4][2], QST[2][4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
-            Vn[rt][x] = f32x4{(float)U[rt][x][0], (float)U[rt][x][1], (float)U[rt][x][2], (float)U[rt][x][3]};
-            QS[rt][x] = f32x4{0.f, 0.f, 0.f, 0.f};
+            Vn[rt][x] = f32x4{0.f, 0.f, 0.f, 0.f};
+            QST[x][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     half8 aw[2][4], aq[2][4];
 #pragma unroll
@@ -839,6 +793,10 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
                 aq[cb ^ 1][rt] = Qf[(rt * 4 + kb + 1) * 64];
             }
         }
+        if (kb == 0) chain_dma_group<0>(dn, nxt, wave, lane);
+        if (kb == 1) chain_dma_group<1>(dn, nxt, wave, lane);
+        if (kb == 2) chain_dma_group<2>(dn, nxt, wave, lane);
+        if (kb == 3) chain_dma_group<3>(dn, nxt, wave, lane);
         __builtin_amdgcn_sched_barrier(0);
         const half8 sb0 = pack_h8(S[2 * kb][0], S[2 * kb + 1][0]);
         const half8 sb1 = pack_h8(S[2 * kb][1], S[2 * kb + 1][1]);
@@ -846,9 +804,22 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
         for (int rt = 0; rt < 4; ++rt) {
             Vn[rt][0] = mfma16(aw[cb][rt], sb0, Vn[rt][0]);
             Vn[rt][1] = mfma16(aw[cb][rt], sb1, Vn[rt][1]);
-            QS[rt][0] = mfma16(aq[cb][rt], sb0, QS[rt][0]);
-            QS[rt][1] = mfma16(aq[cb][rt], sb1, QS[rt][1]);
+            QST[0][rt] = mfma16(sb0, aq[cb][rt], QST[0][rt]);
+            QST[1][rt] = mfma16(sb1, aq[cb][rt], QST[1][rt]);
         }
+    }
+    // + U' (exact: an identity product of its fp16 values, B operand over
+    // token block rt / 2)
+    {
+        half8 ub[2][2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) ub[x][tb] = Uf[(2 * x + tb) * 64];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int x = 0; x < 2; ++x) Vn[rt][x] = mfma16(eye[rt & 1], ub[x][rt >> 1], Vn[rt][x]);
     }
     // k^T fragments of the first two 16-row state tiles, P, and the gates
     half8 kf[2][2][2];  // [buffer][tile in pair][token block]
@@ -863,15 +834,16 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
     pf[3] = Pf[5 * 64];
     pf[4] = Pf[6 * 64];
     pf[5] = Pf[7 * 64];
-    f32x4 rg[4], gm[4];
+    f32x4 rg[4];
+    float gm[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
         rg[rt] = *reinterpret_cast<const f32x4 *>(gt + 64 + 16 * rt + 4 * q4);
-        gm[rt] = *reinterpret_cast<const f32x4 *>(gt + 16 * rt + 4 * q4);
+        gm[rt] = gt[16 * rt + c16];
     }
     const float gn = gt[128];
     __builtin_amdgcn_sched_barrier(0);
-    // Vnew and (Gam_n / Gam) Vnew as B operands over the chunk's two 32-token blocks
+    // Vnew and (Gam_n / Gam) Vnew as operands over the chunk's two 32-token blocks
     half8 vb[2][2], vr[2][2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
@@ -902,61 +874,62 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
             }
         }
     }
-    // O = diag(q_scale Gam) Q S + P Vnew (P lower triangular), staged as bf16 rows
+    // O = diag(q_scale Gam) Q S + P Vnew (P lower triangular), through a
+    // per-wave LDS staging of 32 token rows at a time: (Q S)^T tile (x, rt)
+    // lane (q, c) holds columns 16x + 4q .. +3 of token 16rt + c.  The buffer
+    // range of the stores ends at the chunk's last valid token, so the rows of
+    // a partial chunk and every row of a warm-up chunk (n = 0) are dropped
+    // without a branch.
+    const int rel = (cc - run.c0) * kChunk;
+    const int n = cc >= run.c_out ? min(kChunk, run.L - rel) : 0;
+    const int rowb = Hv * kD * 2;  // bytes per token row of o
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        p.o + ((long)(run.t0 + rel) * Hv + h) * kD + 32 * wave, 0, n * rowb, 0x00020000);
     uint16_t *os = reinterpret_cast<uint16_t *>(stage);
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        const half8 p0 = pf[rt < 2 ? rt : 2 * rt - 2];
+    for (int half = 0; half < 2; ++half) {
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            f32x4 acc = mfma16(p0, vb[0][x], QS[rt][x] * gm[rt]);
-            if (rt >= 2) acc = mfma16(pf[2 * rt - 1], vb[1][x], acc);
+        for (int r2 = 0; r2 < 2; ++r2) {
+            const int rt = 2 * half + r2;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) os[(16 * rt + 4 * q4 + e) * 32 + 16 * x + c16] = (uint16_t)f32_to_bf16(acc[e]);
+            for (int x = 0; x < 2; ++x) {
+                f32x4 acc = mfma16(vb[0][x], pf[rt < 2 ? rt : 2 * rt - 2], QST[x][rt] * gm[rt]);
+                if (rt >= 2) acc = mfma16(vb[1][x], pf[2 * rt - 1], acc);
+                typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+                const u32x2 v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+                *reinterpret_cast<u32x2 *>(os + (16 * r2 + c16) * 32 + 16 * x + 4 * q4) = v;
+            }
         }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    {
-        // 64 rows of 64 bytes: lane -> (row 16i + lane/4, 16-byte piece lane%4).
-        // The buffer range ends at the chunk's last valid token, so the rows
-        // of a partial chunk and every row of a warm-up chunk (n = 0) are
-        // dropped without a branch.
-        const int rel = (cc - run.c0) * kChunk;
-        const int n = cc >= run.c_out ? min(kChunk, run.L - rel) : 0;
-        const int rowb = Hv * kD * 2;  // bytes per token row of o
-        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-            p.o + ((long)(run.t0 + rel) * Hv + h) * kD + 32 * wave, 0, n * rowb, 0x00020000);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // 32 rows of 64 bytes: lane -> (row 16i + lane/4, 16-byte piece lane%4)
         const int row = lane >> 2, piece = lane & 3;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2; ++i) {
             const i32x4 v = *reinterpret_cast<const i32x4 *>(stage + (16 * i + row) * 64 + piece * 16);
-            __builtin_amdgcn_raw_buffer_store_b128(v, ro, (16 * i + row) * rowb + piece * 16, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(v, ro, (32 * half + 16 * i + row) * rowb + piece * 16, 0, 0);
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
 // The chunks of one run, the state carried in registers.
 __device__ __forceinline__ void chain_run(const PrefillArgs &p, const Workspace &ws, uint8_t *buf0, uint8_t *buf1,
-                                          uint8_t *stage, f32x4 (&S)[8][2], const ChainRun &run, int h, int g,
-                                          int wave, int lane, uint32_t &junk)
+                                          uint8_t *stage, f32x4 (&S)[8][2], const half8 (&eye)[2],
+                                          const ChainRun &run, int h, int g, int wave, int lane)
 {
     if (run.c_to <= run.c_from) return;
-    half4 U0[4][2], U1[4][2];
-    uint32_t T0[3] = {0, 0, 0}, T1[3] = {0, 0, 0};
-    const ChainTouch tp = chain_touch_plan(ws, h, g, p.Hqk, p.Hv, wave);
-    // prologue: the touch of the second chunk, the first chunk's operands
-    chain_touch(tp, min(run.c_from + 1, run.c_to - 1), lane, T1, junk);
     chain_dma(ws, buf0, run.c_from, h, g, p.Hqk, p.Hv, wave, lane);
-    chain_load_u(U0, ws, run.c_from, h, p.Hv, wave, lane);
+    __builtin_amdgcn_s_waitcnt(0);
     int cc = run.c_from;
     for (; cc + 2 <= run.c_to; cc += 2) {
-        chain_step(p, ws, buf0, buf1, stage, tp, T0, junk, S, U0, U1, run, cc, h, g, wave, lane);
-        chain_step(p, ws, buf1, buf0, stage, tp, T1, junk, S, U1, U0, run, cc + 1, h, g, wave, lane);
+        chain_step(p, ws, buf0, buf1, stage, S, eye, run, cc, h, g, wave, lane);
+        chain_step(p, ws, buf1, buf0, stage, S, eye, run, cc + 1, h, g, wave, lane);
     }
-    if (cc < run.c_to) chain_step(p, ws, buf0, buf1, stage, tp, T0, junk, S, U0, U1, run, cc, h, g, wave, lane);
-    junk ^= T0[0] ^ T0[1] ^ T0[2] ^ T1[0] ^ T1[1] ^ T1[2];
+    if (cc < run.c_to) chain_step(p, ws, buf0, buf1, stage, S, eye, run, cc, h, g, wave, lane);
     // the last step's DMA into the other buffer is still in flight
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -1043,8 +1016,8 @@ void chain_kernel(PrefillArgs p, Workspace ws)
     __shared__ __attribute__((aligned(16))) uint8_t stage_all[4 * kChainStage];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const half8 eye[2] = {eye_frag(0, lane), eye_frag(1, lane)};
     uint8_t *stage = stage_all + wave * kChainStage;
-    uint32_t junk = 0;
     const int Hqk = p.Hqk, Hv = p.Hv, G = Hv / Hqk;
     // block -> (segment or rank, group, head in group); the G heads of one
     // (segment, QK group) land on the same XCD (same L2)
@@ -1068,7 +1041,7 @@ void chain_kernel(PrefillArgs p, Workspace ws)
         if (w < 0) return;  // recomputed in order by the repair pass
         const long sbase = ((long)s * Hv + h) * kD * kD;
         state_load(S, w == si.x && p.state_in ? p.state_in + sbase : nullptr, wave, lane);
-        chain_run(p, ws, buf0, buf1, stage, S, ChainRun{si.x, si.z, si.w, w, sg.z, sg.y}, h, g, wave, lane, junk);
+        chain_run(p, ws, buf0, buf1, stage, S, eye, ChainRun{si.x, si.z, si.w, w, sg.z, sg.y}, h, g, wave, lane);
         // Final states: a sequence of one segment writes state_out itself.
         // Otherwise other blocks of this sequence may still read state_in
         // (which state_out may alias), so every segment parks its final state
@@ -1114,7 +1087,7 @@ void chain_kernel(PrefillArgs p, Workspace ws)
             }
             if (!carry) state_load(S, ws.bstate + ((long)(k - 1) * Hv + h) * kStateFloats, wave, lane);
             const int4 sg = ws.seg_info[k];
-            chain_run(p, ws, buf0, buf1, stage, S, ChainRun{si.x, si.z, si.w, sg.y, sg.z, sg.y}, h, g, wave, lane, junk);
+            chain_run(p, ws, buf0, buf1, stage, S, eye, ChainRun{si.x, si.z, si.w, sg.y, sg.z, sg.y}, h, g, wave, lane);
             carry = true;
         }
         // the final state of a sequence of several segments
@@ -1123,8 +1096,6 @@ void chain_kernel(PrefillArgs p, Workspace ws)
             state_store(S, p.state_out + sbase, wave, lane);
         }
     }
-    // consumes the touch values under a condition no valid call meets (N >= 0)
-    if (p.N < 0 && junk == 1u) ws.seg_bad[0] = 0;
 }
 
 }  // namespace
