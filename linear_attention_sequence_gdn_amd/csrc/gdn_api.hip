@@ -10,7 +10,6 @@
 #include "gdn_prefill.h"
 
 namespace gdn {
-int max_decode_group();
 hipError_t launch_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
                          const float *b, const uint16_t *conv_w, uint16_t *conv_state,
                          const float *state_in, float *state_out, uint16_t *o, int B, int Hqk,
@@ -53,13 +52,12 @@ int gdn_decode_step(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
     if (B < 0) return GDN_ERR_INVALID_ARGUMENT;
     int rc = check_dims(Hqk, Hv, dk, dv);
     if (rc != GDN_OK) return rc;
-    if (Hv / Hqk > gdn::max_decode_group()) return GDN_ERR_UNSUPPORTED;
     if (B == 0) return GDN_OK;
     if (!q || !k || !v || !a || !b || !conv_w || !conv_state || !state_in || !state_out || !o)
         return GDN_ERR_INVALID_ARGUMENT;
     if (!aligned(state_in, 16) || !aligned(state_out, 16) || !aligned(conv_w, 8) ||
-        !aligned(o, 8) || !aligned(q, 2) || !aligned(k, 2) || !aligned(v, 2) ||
-        !aligned(conv_state, 2) || !aligned(a, 4) || !aligned(b, 4))
+        !aligned(o, 8) || !aligned(q, 4) || !aligned(k, 4) || !aligned(v, 2) ||
+        !aligned(conv_state, 4) || !aligned(a, 4) || !aligned(b, 4))
         return GDN_ERR_INVALID_ARGUMENT;
     hipError_t e = gdn::launch_decode(q, k, v, a, b, conv_w, conv_state, state_in, state_out, o,
                                       B, Hqk, Hv, gate_scale, q_scale,

@@ -75,7 +75,7 @@ def test_decode_validation(L):
     assert call_decode(L, dv=96) == gdn.GDN_ERR_UNSUPPORTED
     assert call_decode(L, Hv=7) == gdn.GDN_ERR_UNSUPPORTED
     assert call_decode(L, Hqk=0) == gdn.GDN_ERR_INVALID_ARGUMENT
-    assert call_decode(L, Hqk=1, Hv=17) == gdn.GDN_ERR_UNSUPPORTED  # group wider than one workgroup
+    assert call_decode(L, q=FAKE + 2) == gdn.GDN_ERR_INVALID_ARGUMENT  # q rows are read 4 bytes at a time
     assert call_decode(L, state=FAKE + 4) == gdn.GDN_ERR_INVALID_ARGUMENT  # misaligned state
     assert call_decode(L, B=0) == gdn.GDN_OK  # no-op, nothing launched
 

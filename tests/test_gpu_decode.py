@@ -38,7 +38,7 @@ def _oracle_steps(oracle_lib, x, steps, B_sub):
     return np.stack(outs), st, conv
 
 
-@pytest.mark.parametrize("B,Hqk,Hv,steps", [(1, 2, 6, 3), (5, 2, 6, 7), (3, 4, 4, 4), (2, 1, 16, 3)])
+@pytest.mark.parametrize("B,Hqk,Hv,steps", [(1, 2, 6, 3), (5, 2, 6, 7), (3, 4, 4, 4), (2, 1, 16, 3), (2, 1, 20, 2)])
 def test_decode_small(oracle_lib, B, Hqk, Hv, steps):
     x = inputs.make_decode(B=B, steps=steps, Hqk=Hqk, Hv=Hv, seed=77 + B)
     o, st, conv = _run_steps(x, steps)
