@@ -18,9 +18,11 @@ launch of each kernel, scaled by what the counters read for the copy, and
 writes them to profiles/traffic.json tagged with the digest of the kernel
 sources they were taken on.
 
-Timing: HIP events on the stream the library launches on.  The prefill goes
-through gdn_prefill_with_events, so each of its three kernels is timed per
-launch; the decode step is one kernel per call.  The CPU baseline is the fp64
+Timing: HIP events on the stream the library launches on.  The step time is
+K plain gdn_prefill calls between two events; the same K steps are then run
+through gdn_prefill_with_events, which records an event after each of the
+five kernels, for the per-kernel times the roofline uses.  A decode step (two
+kernels) is timed per call.  The CPU baseline is the fp64
 oracle, as it stands, on a bounded sample of the same prefill workload.
 """
 import argparse
@@ -45,6 +47,12 @@ CHUNK = 64
 # ---------------------------------------------------------------------------
 # algorithmic work (chunk form, C = 64, counted per full chunk)
 # ---------------------------------------------------------------------------
+# gdn_prefill_with_events records an event before the first kernel and after
+# each of these, in launch order
+PREFILL_KERNELS = ("setup_kernel", "prep_qk_kernel", "prep_head_kernel", "chain_kernel", "chain_repair_kernel")
+N_EVENTS = len(PREFILL_KERNELS) + 1
+
+
 def prefill_flops(T, Hqk, Hv, n=CHUNK, d=D):
     """(prep, chain) algorithmic FLOP of one prefill of T tokens (T % 64 == 0)."""
     chunks = T // n
@@ -105,9 +113,10 @@ def source_digest():
 
 
 COPY_BYTES = 256 << 20
-TRAFFIC_KERNELS = {"prefill_chain": "chain_kernel", "prefill_prep_head": "prep_head_kernel",
-                   "prefill_prep_qk": "prep_qk_kernel", "prefill_setup": "setup_kernel",
-                   "decode": "decode_kernel"}
+TRAFFIC_KERNELS = {"prefill_chain": "chain_kernel<false>", "prefill_chain_repair": "chain_kernel<true>",
+                   "prefill_prep_head": "prep_head_kernel", "prefill_prep_qk": "prep_qk_kernel",
+                   "prefill_setup": "setup_kernel", "decode": "decode_head_kernel",
+                   "decode_conv_shift": "conv_shift_qk_kernel"}
 
 
 def _counter_rows(path, counter):
@@ -145,17 +154,24 @@ def traffic_report(fetch_csv, write_csv):
                             "write_counter_bytes": w_copy, "fetch_scale": f_scale,
                             "write_scale": w_scale}}
     for name, sub in TRAFFIC_KERNELS.items():
+        if not any(sub in k_ for k_ in fetch):
+            print(f"{sub:22s} not launched in this run")
+            continue
         rd = mean(fetch, sub) * 1024 * f_scale
         wr = mean(write, sub) * 1024 * w_scale
         out[name] = {"kernel": sub, "read_bytes": rd, "write_bytes": wr, "bytes_per_launch": rd + wr,
                      "source_digest": digest}
-        print(f"{sub:18s} read {rd / 2**20:10.2f} MiB  write {wr / 2**20:10.2f} MiB per launch")
+        print(f"{sub:22s} read {rd / 2**20:10.2f} MiB  write {wr / 2**20:10.2f} MiB per launch")
     print(f"copy calibration: FETCH_SIZE x{f_scale:.3f}, WRITE_SIZE x{w_scale:.3f}")
     path = os.path.join(ROOT, "profiles", "traffic.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
     print("wrote", path)
+
+
+def _sum_or_none(*xs):
+    return None if any(x_ is None for x_ in xs) else sum(xs)
 
 
 def load_traffic(name, digest):
@@ -200,34 +216,48 @@ def bench_prefill(hip, steps, warmup):
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     L = gdn.lib()
+    L.gdn_prefill.restype = ctypes.c_int
+    L.gdn_prefill.argtypes = [ctypes.c_void_p] * 11 + [ctypes.c_int] * 6 + \
+        [ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     L.gdn_prefill_with_events.restype = ctypes.c_int
     L.gdn_prefill_with_events.argtypes = [ctypes.c_void_p] * 11 + [ctypes.c_int] * 6 + \
         [ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
     P = lambda t: ctypes.c_void_p(t.data_ptr())
-    evs = [[hip.event() for _ in range(4)] for _ in range(steps)]
-    arrs = [(ctypes.c_void_p * 4)(*[e.value for e in ev]) for ev in evs]
-    warm = (ctypes.c_void_p * 4)(*[hip.event().value for _ in range(4)])
+    evs = [[hip.event() for _ in range(N_EVENTS)] for _ in range(steps)]
+    arrs = [(ctypes.c_void_p * N_EVENTS)(*[e.value for e in ev]) for ev in evs]
+    warm = (ctypes.c_void_p * N_EVENTS)(*[hip.event().value for _ in range(N_EVENTS)])
 
-    def run(arr):
-        rc = L.gdn_prefill_with_events(P(q), P(k), P(v), P(a), P(b), P(w), None, None, None, P(so), P(o),
-                                       1, T, Hqk, Hv, D, D, 0.1, 1.0, P(ws), need, sp, arr)
+    def run(arr=None):
+        if arr is None:
+            rc = L.gdn_prefill(P(q), P(k), P(v), P(a), P(b), P(w), None, None, None, P(so), P(o),
+                               1, T, Hqk, Hv, D, D, 0.1, 1.0, P(ws), need, sp)
+        else:
+            rc = L.gdn_prefill_with_events(P(q), P(k), P(v), P(a), P(b), P(w), None, None, None, P(so), P(o),
+                                           1, T, Hqk, Hv, D, D, 0.1, 1.0, P(ws), need, sp, arr)
         assert rc == 0, gdn.gdn_status_string(rc)
 
     for _ in range(warmup):
+        run()
         run(warm)
     torch.cuda.synchronize()
+    # the step time: plain calls, nothing recorded between the kernels
     t0, t1 = hip.event(), hip.event()
     hip.record(t0, sp)
     for i in range(steps):
-        run(arrs[i])
+        run()
     hip.record(t1, sp)
     torch.cuda.synchronize()
     total_ms = hip.ms(t0, t1)
-    stage = {"setup": 0.0, "prep": 0.0, "chain": 0.0}
+    # per-kernel times: the same steps again with an event after every kernel
+    # (each recorded event costs the stream a few microseconds, which these
+    # intervals include)
+    for i in range(steps):
+        run(arrs[i])
+    torch.cuda.synchronize()
+    stage = {name: 0.0 for name in PREFILL_KERNELS}
     for ev in evs:
-        stage["setup"] += hip.ms(ev[0], ev[1])
-        stage["prep"] += hip.ms(ev[1], ev[2])
-        stage["chain"] += hip.ms(ev[2], ev[3])
+        for i, name in enumerate(PREFILL_KERNELS):
+            stage[name] += hip.ms(ev[i], ev[i + 1])
     stage = {k_: v_ / steps for k_, v_ in stage.items()}
     return dict(ms_per_step=total_ms / steps, stage_ms=stage, T=T, Hqk=Hqk, Hv=Hv)
 
@@ -303,7 +333,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--traffic-report", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
@@ -330,14 +360,16 @@ def main():
     flop_prep, flop_chain = prefill_flops(T, Hqk, Hv)
     tok_s = T / (pf["ms_per_step"] * 1e-3)
 
-    # dominant prefill kernel, priced against the fp16 matrix-core peak
-    dom = "chain" if pf["stage_ms"]["chain"] >= pf["stage_ms"]["prep"] else "prep"
-    dom_flop = flop_chain if dom == "chain" else flop_prep
-    dom_ms = pf["stage_ms"][dom]
+    # dominant prefill kernel (the longer of the two that carry the matrix
+    # products), priced against the fp16 dense matrix-core peak
+    km = pf["stage_ms"]
+    dom = "chain_kernel" if km["chain_kernel"] >= km["prep_head_kernel"] else "prep_head_kernel"
+    dom_flop = flop_chain if dom == "chain_kernel" else flop_prep
+    dom_ms = km[dom]
     achieved = dom_flop / (dom_ms * 1e-3) / 1e12
-    roof = {"bound": "mfma", "kernel": f"{dom}_kernel", "achieved": achieved,
+    roof = {"bound": "mfma", "kernel": dom, "achieved": achieved,
             "peak": PEAK_MFMA_F16 / 1e12, "unit": "TFLOP/s", "frac": achieved * 1e12 / PEAK_MFMA_F16,
-            "traffic": load_traffic(f"prefill_{dom}", digest),
+            "traffic": load_traffic("prefill_chain" if dom == "chain_kernel" else "prefill_prep_head", digest),
             "algorithmic_flop_per_launch": dom_flop, "avg_launch_ms": dom_ms}
     path_flop = flop_prep + flop_chain
     dec_bytes = decode_bytes(dc["B"], dc["Hqk"], dc["Hv"])
@@ -362,13 +394,18 @@ def main():
                  "mfma_frac": path_flop / (pf["ms_per_step"] * 1e-3) / PEAK_MFMA_F16,
                  "compulsory_bytes": prefill_bytes(T, Hqk, Hv),
                  "hbm_frac": prefill_bytes(T, Hqk, Hv) / (pf["ms_per_step"] * 1e-3) / PEAK_HBM,
-                 "stage_ms": pf["stage_ms"]},
+                 "kernel_ms": pf["stage_ms"],
+                 "other_kernel": {"kernel": "prep_head_kernel" if dom == "chain_kernel" else "chain_kernel",
+                                  "tflops": (flop_prep if dom == "chain_kernel" else flop_chain) /
+                                  (km["prep_head_kernel" if dom == "chain_kernel" else "chain_kernel"] * 1e-3) / 1e12}},
         "decode": {"metric": "decode us/step (B=256, 16QK/48V, 64 in-place steps)",
                    "value": dc["us_per_step"], "unit": "us/step", "higher_is_better": False,
                    "kernel_us": dc["kernel_us"],
-                   "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": dec_gbs,
-                                "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": dec_gbs * 1e9 / PEAK_HBM,
-                                "traffic": load_traffic("decode", digest),
+                   "roofline": {"bound": "hbm", "kernel": "decode step (decode_head_kernel + conv_shift_qk_kernel)",
+                                "achieved": dec_gbs, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                                "frac": dec_gbs * 1e9 / PEAK_HBM,
+                                "traffic": _sum_or_none(load_traffic("decode", digest),
+                                                        load_traffic("decode_conv_shift", digest)),
                                 "algorithmic_bytes_per_launch": dec_bytes}},
         "source_digest": digest,
     }

@@ -92,11 +92,12 @@ int gdn_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 
 /*
  * Measurement variant of gdn_prefill: the same work on the same stream, and
- * additionally records four caller-created HIP events (events[i] is a
- * hipEvent_t): events[0] before the first kernel, events[1] after the
- * chunk-table setup, events[2] after the parallel per-chunk pass and
- * events[3] after the sequential state pass, so that the caller can time each
- * stage with hipEventElapsedTime.  events must not be NULL.
+ * additionally records six caller-created HIP events (events[i] is a
+ * hipEvent_t), so that the caller can time each of the five kernels with
+ * hipEventElapsedTime: events[0] before the first kernel, then one after each
+ * of the chunk-table setup, the q/k prologue, the per-head chunk pass, the
+ * segmented sequential pass and its in-order repair pass.  events must not be
+ * NULL and must hold six events.
  */
 int gdn_prefill_with_events(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                             const float *a, const float *b, const uint16_t *conv_w,

@@ -109,6 +109,7 @@ static int prefill_common(const uint16_t *q, const uint16_t *k, const uint16_t *
     p.max_chunks = max_chunks;
     p.seg_chunks = gdn::choose_seg_chunks(max_chunks, N, Hv);
     p.max_segs = gdn::max_segments(max_chunks, N, p.seg_chunks);
+    p.defer_final = state_in != nullptr && state_in == state_out;
     hipError_t e = gdn::launch_prefill(p, workspace, reinterpret_cast<hipStream_t>(stream),
                                        reinterpret_cast<hipEvent_t const *>(events));
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
@@ -137,7 +138,7 @@ int gdn_prefill_with_events(const uint16_t *q, const uint16_t *k, const uint16_t
                             size_t workspace_bytes, void *stream, void *const *events)
 {
     if (!events) return GDN_ERR_INVALID_ARGUMENT;
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < gdn::kPrefillEvents; ++i)
         if (!events[i]) return GDN_ERR_INVALID_ARGUMENT;
     if (B < 0 || T < 0) return GDN_ERR_INVALID_ARGUMENT;
     int rc = check_dims(Hqk, Hv, dk, dv);

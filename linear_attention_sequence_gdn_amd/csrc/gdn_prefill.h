@@ -25,6 +25,7 @@ struct PrefillArgs {
     int max_chunks;
     int seg_chunks;  // chunks per segment of the sequential pass
     int max_segs;    // bound of the number of segments
+    int defer_final; // state_out is state_in: final states go through the repair pass
 };
 
 // Upper bound of the number of 64-token chunks.
@@ -72,8 +73,9 @@ inline int max_segments(int max_chunks, int N, int seg_chunks) { return max_chun
 
 size_t prefill_workspace_bytes(int max_chunks, int N, int Hqk, int Hv);
 Workspace carve_workspace(void *base, int max_chunks, int N, int Hqk, int Hv);
-// events: NULL, or four events recorded before setup, after setup, after
-// prep and after the chain kernel.
+// events: NULL, or kPrefillEvents events recorded before the first kernel and
+// after each of the five (setup, prep_qk, prep_head, chain, chain repair).
+constexpr int kPrefillEvents = 6;
 hipError_t launch_prefill(const PrefillArgs &p, void *workspace, hipStream_t stream,
                           hipEvent_t const *events = nullptr);
 

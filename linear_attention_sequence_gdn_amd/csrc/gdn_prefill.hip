@@ -138,22 +138,35 @@ __device__ __forceinline__ int seq_len(const PrefillArgs &p, int s)
     return min(max(p.cu_seqlens[s + 1] - t0, 0), p.T_tot - t0);
 }
 
+// Inclusive prefix sum over the 1024 threads of the block: within each wave by
+// lane shifts, then across the 16 wave totals.
+__device__ __forceinline__ int block_scan1024(int x, int *s_wsum)
+{
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) s_wsum[w] = x;
+    __syncthreads();
+    int pre = 0;
+    for (int i = 0; i < w; ++i) pre += s_wsum[i];
+    __syncthreads();  // s_wsum may be reused
+    return x + pre;
+}
+
 __global__ __launch_bounds__(1024) void setup_kernel(PrefillArgs p, Workspace ws)
 {
     __shared__ int s_scan[1024];
+    __shared__ int s_wsum[16];
     const int t = threadIdx.x;
     const int per = (p.N + 1023) / 1024;
     const int s0 = min(p.N, t * per), s1 = min(p.N, s0 + per);
     int local = 0;
     for (int s = s0; s < s1; ++s) local += (seq_len(p, s) + kChunk - 1) / kChunk;
-    s_scan[t] = local;
+    s_scan[t] = block_scan1024(local, s_wsum);
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int add = t >= off ? s_scan[t - off] : 0;
-        __syncthreads();
-        s_scan[t] += add;
-        __syncthreads();
-    }
     int base = s_scan[t] - local;
     const int Lseg = p.seg_chunks;
     int segs_local = 0;
@@ -192,16 +205,11 @@ __global__ __launch_bounds__(1024) void setup_kernel(PrefillArgs p, Workspace ws
     }
     // segments of the sequential pass: max(1, ceil(chunks / Lseg)) per
     // sequence, in sequence order
+    const int segs_incl = block_scan1024(segs_local, s_wsum);
+    if (t == 1023) s_wsum[0] = segs_incl;
     __syncthreads();
-    s_scan[t] = segs_local;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int add = t >= off ? s_scan[t - off] : 0;
-        __syncthreads();
-        s_scan[t] += add;
-        __syncthreads();
-    }
-    int sb = s_scan[t] - segs_local;
+    const int segs_total = s_wsum[0];
+    int sb = segs_incl - segs_local;
     for (int s = s0; s < s1; ++s) {
         const int4 si = ws.seq_info[s];
         const int ns = max(1, (si.y + Lseg - 1) / Lseg);
@@ -212,7 +220,7 @@ __global__ __launch_bounds__(1024) void setup_kernel(PrefillArgs p, Workspace ws
         }
         sb += ns;
     }
-    for (int k = min(s_scan[1023], p.max_segs) + t; k < p.max_segs; k += 1024) ws.seg_info[k] = make_int4(-1, 0, 0, 0);
+    for (int k = min(segs_total, p.max_segs) + t; k < p.max_segs; k += 1024) ws.seg_info[k] = make_int4(-1, 0, 0, 0);
     // longest first (ties by index): rank of each sequence
     for (int s = t; s < p.N; s += 1024) {
         const int Ls = seq_len(p, s);
@@ -224,6 +232,53 @@ __global__ __launch_bounds__(1024) void setup_kernel(PrefillArgs p, Workspace ws
         ws.order[rank] = s;
     }
 }
+
+// Table lookups.  Packed (varlen) calls read the tables setup_kernel built;
+// uniform batches (B sequences of T tokens) compute the same entries directly,
+// so that they need no setup launch.
+struct Tables {
+    static __device__ __forceinline__ int chunks_per_seq(const PrefillArgs &p) { return (p.T_uniform + kChunk - 1) / kChunk; }
+    static __device__ __forceinline__ int segs_per_seq(const PrefillArgs &p)
+    {
+        return max(1, (chunks_per_seq(p) + p.seg_chunks - 1) / p.seg_chunks);
+    }
+    // {sequence, first token, length, is-first}
+    static __device__ __forceinline__ int4 chunk(const PrefillArgs &p, const Workspace &ws, int c)
+    {
+        if (p.cu_seqlens) return ws.chunk_info[c];
+        const int per = chunks_per_seq(p), s = c / per, j = c % per;
+        return make_int4(s, s * p.T_uniform + j * kChunk, min(kChunk, p.T_uniform - j * kChunk), j == 0);
+    }
+    // {first chunk, chunks, first token, length}
+    static __device__ __forceinline__ int4 seq(const PrefillArgs &p, const Workspace &ws, int s)
+    {
+        if (p.cu_seqlens) return ws.seq_info[s];
+        const int per = chunks_per_seq(p);
+        return make_int4(s * per, per, s * p.T_uniform, p.T_uniform);
+    }
+    // {sequence or -1, first chunk, end chunk, 1: first of sequence | 2: last}
+    static __device__ __forceinline__ int4 seg(const PrefillArgs &p, const Workspace &ws, int k)
+    {
+        if (p.cu_seqlens) return ws.seg_info[k];
+        const int per = chunks_per_seq(p), ns = segs_per_seq(p);
+        const int s = k / ns, i = k % ns;
+        if (s >= p.N) return make_int4(-1, 0, 0, 0);
+        const int cb = s * per + i * p.seg_chunks, ce = min(s * per + per, cb + p.seg_chunks);
+        return make_int4(s, cb, ce, (i == 0 ? 1 : 0) | (i == ns - 1 ? 2 : 0));
+    }
+    // {first segment, segments}
+    static __device__ __forceinline__ int2 seq_segs(const PrefillArgs &p, const Workspace &ws, int s)
+    {
+        if (p.cu_seqlens) return make_int2(ws.seq_seg[s].x, ws.seq_seg[s].y);
+        const int ns = segs_per_seq(p);
+        return make_int2(s * ns, ns);
+    }
+    // sequences, longest first
+    static __device__ __forceinline__ int order(const PrefillArgs &p, const Workspace &ws, int rank)
+    {
+        return p.cu_seqlens ? ws.order[rank] : rank;
+    }
+};
 
 // ---------------------------------------------------------------------------
 // prep: everything that does not depend on the carried state
@@ -268,7 +323,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_qk_kernel(PrefillArgs p, Wo
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int c = blockIdx.x / p.Hqk, g = blockIdx.x % p.Hqk;
-    const int4 ci = ws.chunk_info[c];
+    const int4 ci = Tables::chunk(p, ws, c);
     const int n = ci.z;
     if (n == 0) return;  // empty chunk slot (whole workgroup)
     const int s = ci.x, t0 = ci.y;
@@ -405,7 +460,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
     if (u >= p.max_chunks * Hqk) return;
     const int c = u / Hqk, g = u % Hqk;
     const int h = g * G + j;
-    const int4 ci = ws.chunk_info[c];
+    const int4 ci = Tables::chunk(p, ws, c);
     const int n = ci.z;
     if (n == 0) return;
     const int s = ci.x, t0 = ci.y;
@@ -512,6 +567,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
         const float gi = s_gam2[i];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+            if (kb > wave / 2) continue;  // query tiles 0, 1 see only key block 0
             half8 fr;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -689,7 +745,8 @@ __device__ __forceinline__ void chain_dma_group(const ChainDma &d, uint8_t *buf,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rw, (lds_void_t *)(buf + ChainBuf::kW + f * 1024), 16, v16, f * 1024, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rq, (lds_void_t *)(buf + ChainBuf::kQ + f * 1024), 16, v16, f * 1024, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rk, (lds_void_t *)(buf + ChainBuf::kK + f * 1024), 16, v16, f * 1024, 0, 0);
-    if (I < 2)
+    // P: fragments 1 and 3 (query tiles 0, 1 against key block 1) are zero and never stored
+    if (I == 1 || (I == 0 && (wave & 1) == 0))
         __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rp, (lds_void_t *)(buf + ChainBuf::kP + f * 1024), 16, v16, f * 1024, 0, 0);
     if (I == 2 && wave == 0)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rg, (lds_void_t *)(buf + ChainBuf::kG), 16, v16, 0, 0, 0);
@@ -1005,8 +1062,8 @@ __device__ __forceinline__ void state_store(const f32x4 (&S)[8][2], float *dst, 
 // segments run in parallel, each from its warm-up start.  kRepair = true: one
 // workgroup per (sequence, V head), which walks the sequence's segments in
 // order and recomputes, exactly from the state the previous segment handed
-// over, those whose warm-up bound was not met; it also hands each sequence of
-// several segments its final state.
+// over, those whose warm-up bound was not met; for in-place calls it also
+// hands each sequence of several segments its final state.
 template <bool kRepair>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void chain_kernel(PrefillArgs p, Workspace ws)
@@ -1031,10 +1088,10 @@ void chain_kernel(PrefillArgs p, Workspace ws)
 
     if (!kRepair) {
         const int k = unit;
-        const int4 sg = ws.seg_info[k];  // seq, first chunk, end chunk, flags
+        const int4 sg = Tables::seg(p, ws, k);  // seq, first chunk, end chunk, flags
         if (sg.x < 0) return;
         const int s = sg.x;
-        const int4 si = ws.seq_info[s];  // chunk0, nchunks, t0, L
+        const int4 si = Tables::seq(p, ws, s);  // chunk0, nchunks, t0, L
         const bool first = sg.w & 1, last = sg.w & 2;
         const int w = first ? sg.y : warm_start(ws, h, Hv, sg.y, si.x, lane);
         if (!first && t == 0) ws.seg_bad[(long)k * Hv + h] = w < 0;
@@ -1042,12 +1099,14 @@ void chain_kernel(PrefillArgs p, Workspace ws)
         const long sbase = ((long)s * Hv + h) * kD * kD;
         state_load(S, w == si.x && p.state_in ? p.state_in + sbase : nullptr, wave, lane);
         chain_run(p, ws, buf0, buf1, stage, S, eye, ChainRun{si.x, si.z, si.w, w, sg.z, sg.y}, h, g, wave, lane);
-        // Final states: a sequence of one segment writes state_out itself.
-        // Otherwise other blocks of this sequence may still read state_in
-        // (which state_out may alias), so every segment parks its final state
-        // and the repair pass, which runs after this one, hands it to the
-        // next segment if that one is recomputed, and moves the last one.
-        state_store(S, last && first ? p.state_out + sbase : ws.bstate + ((long)k * Hv + h) * kStateFloats, wave, lane);
+        // Final states.  Every segment but the last parks its final state for
+        // the repair pass, which runs after this one and hands it to the next
+        // segment if that one is recomputed.  The last segment writes
+        // state_out, unless state_out is state_in and other blocks of the
+        // sequence may still be reading it: then it parks its state as well
+        // and the repair pass moves it.
+        const bool direct = last && (first || !p.defer_final);
+        state_store(S, direct ? p.state_out + sbase : ws.bstate + ((long)k * Hv + h) * kStateFloats, wave, lane);
         // carried conv rows: the last three raw rows of the sequence (v
         // channels of head h; the first head of the group also writes the q
         // and k channels)
@@ -1073,9 +1132,9 @@ void chain_kernel(PrefillArgs p, Workspace ws)
             }
         }
     } else {
-        const int s = ws.order[unit];
-        const int4 si = ws.seq_info[s];
-        const int4 ss = ws.seq_seg[s];  // first segment, segments
+        const int s = Tables::order(p, ws, unit);
+        const int4 si = Tables::seq(p, ws, s);
+        const int2 ss = Tables::seq_segs(p, ws, s);  // first segment, segments
         const long sbase = ((long)s * Hv + h) * kD * kD;
         const int nseg = min(ss.y, p.max_segs - ss.x);
         bool carry = false;  // S holds the final state of the previous segment
@@ -1086,12 +1145,13 @@ void chain_kernel(PrefillArgs p, Workspace ws)
                 continue;
             }
             if (!carry) state_load(S, ws.bstate + ((long)(k - 1) * Hv + h) * kStateFloats, wave, lane);
-            const int4 sg = ws.seg_info[k];
+            const int4 sg = Tables::seg(p, ws, k);
             chain_run(p, ws, buf0, buf1, stage, S, eye, ChainRun{si.x, si.z, si.w, sg.y, sg.z, sg.y}, h, g, wave, lane);
             carry = true;
         }
-        // the final state of a sequence of several segments
-        if (nseg > 1) {
+        // the final state of a sequence of several segments, when its last
+        // segment was recomputed here or parked its state
+        if (nseg > 1 && (carry || p.defer_final)) {
             if (!carry) state_load(S, ws.bstate + ((long)(ss.x + nseg - 1) * Hv + h) * kStateFloats, wave, lane);
             state_store(S, p.state_out + sbase, wave, lane);
         }
@@ -1186,28 +1246,34 @@ hipError_t launch_prefill(const PrefillArgs &p, void *workspace, hipStream_t str
     hipError_t e;
     auto mark = [&](int i) { return events ? hipEventRecord(events[i], stream) : hipSuccess; };
     if ((e = mark(0)) != hipSuccess) return e;
-    hipLaunchKernelGGL(setup_kernel, dim3(1), dim3(1024), 0, stream, p, ws);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (p.cu_seqlens) {
+        hipLaunchKernelGGL(setup_kernel, dim3(1), dim3(1024), 0, stream, p, ws);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if ((e = mark(1)) != hipSuccess) return e;
     if (p.max_chunks > 0) {
         const long units = (long)p.max_chunks * p.Hqk;
         hipLaunchKernelGGL(prep_qk_kernel, dim3((unsigned)units), dim3(kPrepThreads), 0, stream, p, ws);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = mark(2)) != hipSuccess) return e;
         const long blocks = ((units + 7) / 8) * 8L * (p.Hv / p.Hqk);
         hipLaunchKernelGGL(prep_head_kernel, dim3((unsigned)blocks), dim3(kPrepThreads), 0, stream, p, ws);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else if ((e = mark(2)) != hipSuccess) {
+        return e;
     }
-    if ((e = mark(2)) != hipSuccess) return e;
+    if ((e = mark(3)) != hipSuccess) return e;
     const int G = p.Hv / p.Hqk;
     const long seg_groups = (long)p.max_segs * p.Hqk;
     const long seg_blocks = ((seg_groups + 7) / 8) * 8L * G;
     hipLaunchKernelGGL(chain_kernel<false>, dim3((unsigned)seg_blocks), dim3(256), 0, stream, p, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = mark(4)) != hipSuccess) return e;
     const long groups = (long)p.N * p.Hqk;
     const long blocks = ((groups + 7) / 8) * 8L * G;
     hipLaunchKernelGGL(chain_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, p, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    return mark(3);
+    return mark(5);
 }
 
 }  // namespace gdn

@@ -114,6 +114,27 @@ def test_segmented_varlen_mixed_decay(oracle_lib):
     compare(x, o, so, cso)
 
 
+def test_in_place_state_with_segments():
+    """state_out == state_in on a sequence cut into many segments (some of
+    them recomputed in order) gives exactly the out-of-place result."""
+    import torch
+    import linear_attention_sequence_gdn_amd as gdn
+    T = 8192 + 37
+    x = inputs.make_prefill(T_list=[T], Hqk=2, Hv=6, seed=512, state_std=0.05)
+    x["a"][:, :2] = -9.0  # two heads without decay: their later segments are recomputed
+    o1, s1, _ = gpu_prefill(x, uniform_T=T, conv_out=False)
+    d = x["d"]
+    st = dev_f32(x["state_in"])
+    o2, s2, _ = gdn.gdn_prefill(dev_bf16(x["q"].reshape(1, T, 2, d)), dev_bf16(x["k"].reshape(1, T, 2, d)),
+                                dev_bf16(x["v"].reshape(1, T, 6, d)), dev_f32(x["a"].reshape(1, T, 6)),
+                                dev_f32(x["b"].reshape(1, T, 6)), dev_bf16(x["conv_w"]),
+                                gate_scale=x["gate_scale"], state_in=st, state_out=st)
+    torch.cuda.synchronize()
+    assert s2.data_ptr() == st.data_ptr()
+    np.testing.assert_array_equal(host_u16(o2.reshape(T, 6, d)), host_u16(o1))
+    np.testing.assert_array_equal(st.cpu().numpy(), s1.cpu().numpy())
+
+
 def test_zero_length_batch_copies_state(oracle_lib):
     x = inputs.make_prefill(T_list=[0, 0], Hqk=2, Hv=6, seed=501, state_std=0.05, conv_state_std=1.0)
     o, so, cso = gpu_prefill(x, uniform_T=0)
