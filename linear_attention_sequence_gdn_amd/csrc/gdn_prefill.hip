@@ -378,33 +378,19 @@ __global__ __launch_bounds__(kPrepThreads) void prep_qk_kernel(PrefillArgs p, Wo
         }
 }
 
-// Forward substitution for column c of the inverse of a 16 x 16 unit
-// lower-triangular block I + A (A strictly lower, row stride kAL):
-// y_i = delta(i, c) - sum_{m<i} A[i][m] y_m.  Expanded at compile time so that
-// y stays in registers.
-template <int I, int M0>
-struct SolveDot16 {
-    static __device__ __forceinline__ void run(float &acc, const float (&y)[16], const float *Arow)
+// Column c of the inverse of a 16 x 16 unit lower-triangular block I + A (A
+// strictly lower, row stride kAL), by right-looking substitution: once y_m is
+// final it is removed from every later row, y_i -= A[i][m] y_m, so the chain
+// of dependent operations is one multiply-add per row.  Expanded at compile
+// time so that y stays in registers.
+template <int M>
+struct SolveCol16 {
+    static __device__ __forceinline__ void run(float (&y)[16], const float *A)
     {
-        if constexpr (M0 < I) {
-            const f32x4 a = *reinterpret_cast<const f32x4 *>(Arow + M0);
-            if constexpr (M0 + 0 < I) acc -= a[0] * y[M0 + 0];
-            if constexpr (M0 + 1 < I) acc -= a[1] * y[M0 + 1];
-            if constexpr (M0 + 2 < I) acc -= a[2] * y[M0 + 2];
-            if constexpr (M0 + 3 < I) acc -= a[3] * y[M0 + 3];
-            SolveDot16<I, M0 + 4>::run(acc, y, Arow);
-        }
-    }
-};
-template <int I>
-struct SolveRow16 {
-    static __device__ __forceinline__ void run(float (&y)[16], const float *A, int c)
-    {
-        if constexpr (I < 16) {
-            float acc = I == c ? 1.f : 0.f;
-            SolveDot16<I, 0>::run(acc, y, A + I * kAL);
-            y[I] = acc;
-            SolveRow16<I + 1>::run(y, A, c);
+        if constexpr (M < 15) {
+#pragma unroll
+            for (int i = M + 1; i < 16; ++i) y[i] -= A[i * kAL + M] * y[M];
+            SolveCol16<M + 1>::run(y, A);
         }
     }
 };
@@ -589,7 +575,9 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
     {
         float y[16];
         const int bo = 16 * wave;
-        SolveRow16<0>::run(y, As + bo * kAL + bo, c16);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) y[i] = i == c16 ? 1.f : 0.f;
+        SolveCol16<0>::run(y, As + bo * kAL + bo);
         if (lane < 16) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) Xs[(bo + i) * kAL + bo + c16] = y[i];
@@ -633,14 +621,17 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
             TGh[i * kH_LD + jj] = (_Float16)tg[k];
         }
     }
-    // ---- v^ of head h: conv + SiLU from the window loaded at the start -> v^T over X
+    // ---- v^ of head h: conv + SiLU from the window loaded at the start -> v^T
+    //      over X; each lane writes 16 consecutive rows of two channels
     {
         float z0[16], z1[16];
         conv_silu(vwin, p.conv_w + cv * 4, lane, r0, n, z0, z1);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            VTs[(2 * lane) * kH_LD + r0 + i] = (_Float16)z0[i];
-            VTs[(2 * lane + 1) * kH_LD + r0 + i] = (_Float16)z1[i];
+        for (int i = 0; i < 16; i += 4) {
+            *reinterpret_cast<half4 *>(VTs + (2 * lane) * kH_LD + r0 + i) =
+                half4{(_Float16)z0[i], (_Float16)z0[i + 1], (_Float16)z0[i + 2], (_Float16)z0[i + 3]};
+            *reinterpret_cast<half4 *>(VTs + (2 * lane + 1) * kH_LD + r0 + i) =
+                half4{(_Float16)z1[i], (_Float16)z1[i + 1], (_Float16)z1[i + 2], (_Float16)z1[i + 3]};
         }
     }
     __syncthreads();
