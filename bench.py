@@ -310,6 +310,43 @@ def bench_decode(hip, steps=64):
                 steps=steps)
 
 
+def bench_decode_multi(hip, T=4, steps=32):
+    """B = 256 sequences, T tokens each per call (multi-token decode): the
+    state is read and written once per call, so the per-token cost falls."""
+    import numpy as np
+    import torch
+    import linear_attention_sequence_gdn_amd as gdn
+    from linear_attention_sequence_gdn_amd import inputs
+
+    c = inputs.CONFIGS[3]
+    B, Hqk, Hv = c["B"], c["Hqk"], c["Hv"]
+    x = inputs.make_decode(B=B, steps=T, Hqk=Hqk, Hv=Hv, seed=1003, gate_scale=c["gate_scale"])
+
+    def dev(arr, bf):
+        t = torch.from_numpy(np.ascontiguousarray(np.swapaxes(arr, 0, 1)))
+        return (t.view(torch.int16).view(torch.bfloat16) if bf else t).cuda()
+
+    q, k, v = dev(x["q"].view(np.int16), True), dev(x["k"].view(np.int16), True), dev(x["v"].view(np.int16), True)
+    a, b = dev(x["a"], False), dev(x["b"], False)
+    w = torch.from_numpy(x["conv_w"].view(np.int16)).view(torch.bfloat16).cuda()
+    conv = torch.from_numpy(x["conv_state"].view(np.int16)).view(torch.bfloat16).cuda()
+    st = torch.from_numpy(x["state"]).cuda()
+    o = torch.empty((B, T, Hv, D), dtype=torch.bfloat16, device="cuda")
+    for _ in range(4):
+        gdn.gdn_decode_multi(q, k, v, a, b, w, conv, st, o=o, gate_scale=c["gate_scale"])
+    torch.cuda.synchronize()
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    t0, t1 = hip.event(), hip.event()
+    hip.record(t0, sp)
+    for _ in range(steps):
+        gdn.gdn_decode_multi(q, k, v, a, b, w, conv, st, o=o, gate_scale=c["gate_scale"])
+    hip.record(t1, sp)
+    torch.cuda.synchronize()
+    us = hip.ms(t0, t1) * 1e3 / steps
+    return {"metric": f"multi-token decode (B=256, T={T} tokens per sequence per call, 16QK/48V)",
+            "us_per_call": us, "us_per_token_step": us / T, "tokens_per_s": B * T / (us * 1e-6)}
+
+
 def cpu_baseline(min_seconds=12.0, max_reps=60):
     import oracle
     from linear_attention_sequence_gdn_amd import inputs
@@ -356,6 +393,7 @@ def main():
 
     pf = bench_prefill(hip, args.steps, args.warmup)
     dc = bench_decode(hip)
+    dm = bench_decode_multi(hip)
     T, Hqk, Hv = pf["T"], pf["Hqk"], pf["Hv"]
     flop_prep, flop_chain = prefill_flops(T, Hqk, Hv)
     tok_s = T / (pf["ms_per_step"] * 1e-3)
@@ -407,6 +445,7 @@ def main():
                                 "traffic": _sum_or_none(load_traffic("decode", digest),
                                                         load_traffic("decode_conv_shift", digest)),
                                 "algorithmic_bytes_per_launch": dec_bytes}},
+        "decode_multi": dm,
         "source_digest": digest,
     }
     if args.calibrate_copy:

@@ -156,6 +156,38 @@ int gdn_decode_step(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                     uint16_t *o, int B, int Hqk, int Hv, int dk, int dv,
                     float gate_scale, float q_scale, void *stream);
 
+/*
+ * Multi-token decode with an optional slot table: T = 1..4 new tokens for
+ * each of B sequences, processed in order, the state read once and written
+ * once (multi-token decoding and the verification of tokens proposed by a
+ * multi-token-prediction head; the pages name MTP speculative decoding as part
+ * of the model's serving path).  Same computation as T successive calls of
+ * gdn_decode_step.
+ *
+ *   q, k        [B][T][Hqk][dk] bf16 raw;  v [B][T][Hv][dv] bf16 raw
+ *   a, b        [B][T][Hv] fp32
+ *   o           [B][T][Hv][dv] bf16: the output of every token
+ *   slots       DEVICE int32 [B], or NULL.  With a table, sequence b reads and
+ *               writes row slots[b] of state_in / state_out ([n_rows][Hv][dk][dv])
+ *               and of conv_state ([n_rows][3][C_tot]), the state cache of a
+ *               serving engine; a sequence whose slot lies outside
+ *               [0, n_rows) is skipped (its outputs are not written).  Two
+ *               sequences must not share a slot.  Without a table, row b and
+ *               n_rows is ignored.
+ *   conv_state  updated IN PLACE: its rows become the last three raw rows
+ *   state_out   may equal state_in (in place).  To take back the tokens a
+ *               verifier rejects, keep state_in and conv rows separate from the
+ *               outputs (state_out != state_in and a copy of the conv rows),
+ *               then advance the accepted prefix with a second call.
+ * T < 1 is invalid; T > 4 is unsupported.
+ */
+int gdn_decode_multi(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                     const float *a, const float *b, const uint16_t *conv_w,
+                     uint16_t *conv_state, const float *state_in, float *state_out,
+                     uint16_t *o, const int32_t *slots, int n_rows,
+                     int B, int T, int Hqk, int Hv, int dk, int dv,
+                     float gate_scale, float q_scale, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,6 +11,7 @@ Functions mirror the ABI names:
 * ``gdn_prefill``        -- B sequences of equal length T
 * ``gdn_prefill_varlen`` -- packed sequences addressed by ``cu_seqlens``
 * ``gdn_decode_step``    -- one new token for each of B sequences
+* ``gdn_decode_multi``   -- 1..4 new tokens per sequence, optional state-cache slots
 * ``gdn_prefill_workspace_size`` / ``gdn_prefill_varlen_workspace_size``
 * ``gdn_status_string``
 
@@ -69,6 +70,8 @@ def lib():
         L.gdn_prefill_varlen.argtypes = [_P] * 12 + [_I] * 6 + [_F, _F, _P, _SZ, _P]
         L.gdn_decode_step.restype = _I
         L.gdn_decode_step.argtypes = [_P] * 10 + [_I] * 5 + [_F, _F, _P]
+        L.gdn_decode_multi.restype = _I
+        L.gdn_decode_multi.argtypes = [_P] * 11 + [_I] * 7 + [_F, _F, _P]
         _lib = L
     return _lib
 
@@ -240,7 +243,49 @@ def gdn_decode_step(q, k, v, a, b, conv_w, conv_state, state_in, *, gate_scale, 
     return o, state_out
 
 
+def gdn_decode_multi(q, k, v, a, b, conv_w, conv_state, state_in, *, gate_scale, q_scale=1.0,
+                     state_out=None, o=None, slots=None, stream=None):
+    """T = 1..4 decode tokens per sequence.  q, k: [B][T][Hqk][128]; v:
+    [B][T][Hv][128] bf16; a, b: [B][T][Hv] fp32; conv_state: [rows][3][C_tot]
+    bf16 (updated in place); state_in: [rows][Hv][128][128] fp32 with rows = B,
+    or the pool size when ``slots`` (int32 [B] on the GPU) maps sequence b to
+    row slots[b]; state_out defaults to state_in (in place).
+    Returns (o [B][T][Hv][128], state_out)."""
+    torch = _torch()
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    C_tot = 2 * Hqk * dk + Hv * dv
+    bf, f32 = torch.bfloat16, torch.float32
+    rows = state_in.shape[0]
+    _check(q, "q", bf, (B, T, Hqk, dk))
+    _check(k, "k", bf, (B, T, Hqk, dk))
+    _check(v, "v", bf, (B, T, Hv, dv))
+    _check(a, "a", f32, (B, T, Hv))
+    _check(b, "b", f32, (B, T, Hv))
+    _check(conv_w, "conv_w", bf, (C_tot, 4))
+    _check(conv_state, "conv_state", bf, (rows, 3, C_tot))
+    _check(state_in, "state_in", f32, (rows, Hv, dk, dv))
+    if slots is None and rows != B:
+        raise ValueError(f"state_in has {rows} rows for {B} sequences and no slot table")
+    if slots is not None:
+        _check(slots, "slots", torch.int32, (B,))
+    if state_out is None:
+        state_out = state_in
+    if o is None:
+        o = torch.empty((B, T, Hv, dv), dtype=bf, device=q.device)
+    _check(state_out, "state_out", f32, (rows, Hv, dk, dv))
+    _check(o, "o", bf, (B, T, Hv, dv))
+    rc = lib().gdn_decode_multi(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(conv_w),
+                                _ptr(conv_state), _ptr(state_in), _ptr(state_out), _ptr(o),
+                                _ptr(slots), rows, B, T, Hqk, Hv, dk, dv, float(gate_scale),
+                                float(q_scale), _stream(stream))
+    if rc != GDN_OK:
+        raise GDNError("gdn_decode_multi", rc)
+    return o, state_out
+
+
 # short aliases
 prefill = gdn_prefill
 prefill_varlen = gdn_prefill_varlen
 decode_step = gdn_decode_step
+decode_multi = gdn_decode_multi

@@ -12,8 +12,9 @@
 namespace gdn {
 hipError_t launch_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
                          const float *b, const uint16_t *conv_w, uint16_t *conv_state,
-                         const float *state_in, float *state_out, uint16_t *o, int B, int Hqk,
-                         int Hv, float gate_scale, float q_scale, hipStream_t stream);
+                         const float *state_in, float *state_out, uint16_t *o, const int32_t *slots,
+                         int n_rows, int B, int T, int Hqk, int Hv, float gate_scale, float q_scale,
+                         hipStream_t stream);
 }  // namespace gdn
 
 namespace {
@@ -44,25 +45,37 @@ const char *gdn_status_string(int status)
     }
 }
 
-int gdn_decode_step(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
-                    const float *b, const uint16_t *conv_w, uint16_t *conv_state,
-                    const float *state_in, float *state_out, uint16_t *o, int B, int Hqk, int Hv,
-                    int dk, int dv, float gate_scale, float q_scale, void *stream)
+int gdn_decode_multi(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
+                     const float *b, const uint16_t *conv_w, uint16_t *conv_state,
+                     const float *state_in, float *state_out, uint16_t *o, const int32_t *slots,
+                     int n_rows, int B, int T, int Hqk, int Hv, int dk, int dv, float gate_scale,
+                     float q_scale, void *stream)
 {
-    if (B < 0) return GDN_ERR_INVALID_ARGUMENT;
+    if (B < 0 || T < 1) return GDN_ERR_INVALID_ARGUMENT;
+    if (T > gdn::kMaxDecodeTokens) return GDN_ERR_UNSUPPORTED;
     int rc = check_dims(Hqk, Hv, dk, dv);
     if (rc != GDN_OK) return rc;
+    if (slots && n_rows < 0) return GDN_ERR_INVALID_ARGUMENT;
     if (B == 0) return GDN_OK;
     if (!q || !k || !v || !a || !b || !conv_w || !conv_state || !state_in || !state_out || !o)
         return GDN_ERR_INVALID_ARGUMENT;
     if (!aligned(state_in, 16) || !aligned(state_out, 16) || !aligned(conv_w, 8) ||
         !aligned(o, 8) || !aligned(q, 4) || !aligned(k, 4) || !aligned(v, 2) ||
-        !aligned(conv_state, 4) || !aligned(a, 4) || !aligned(b, 4))
+        !aligned(conv_state, 4) || !aligned(a, 4) || !aligned(b, 4) || (slots && !aligned(slots, 4)))
         return GDN_ERR_INVALID_ARGUMENT;
-    hipError_t e = gdn::launch_decode(q, k, v, a, b, conv_w, conv_state, state_in, state_out, o,
-                                      B, Hqk, Hv, gate_scale, q_scale,
+    hipError_t e = gdn::launch_decode(q, k, v, a, b, conv_w, conv_state, state_in, state_out, o, slots,
+                                      slots ? n_rows : B, B, T, Hqk, Hv, gate_scale, q_scale,
                                       reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+int gdn_decode_step(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
+                    const float *b, const uint16_t *conv_w, uint16_t *conv_state,
+                    const float *state_in, float *state_out, uint16_t *o, int B, int Hqk, int Hv,
+                    int dk, int dv, float gate_scale, float q_scale, void *stream)
+{
+    return gdn_decode_multi(q, k, v, a, b, conv_w, conv_state, state_in, state_out, o, nullptr, 0, B, 1,
+                            Hqk, Hv, dk, dv, gate_scale, q_scale, stream);
 }
 
 size_t gdn_prefill_workspace_size(int B, int T, int Hqk, int Hv, int dk, int dv)

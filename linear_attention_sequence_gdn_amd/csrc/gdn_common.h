@@ -14,6 +14,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;     // head dim (d_k = d_v)
 constexpr int kChunk = 64;  // tokens per chunk of the chunked prefill
+constexpr int kMaxDecodeTokens = 4;  // tokens per sequence in one multi-token decode step
 
 // ---- number formats --------------------------------------------------------
 

@@ -119,3 +119,23 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(gdn, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         gdn.lib()
+
+
+def call_decode_multi(L, q=FAKE, slots=None, n_rows=0, B=2, T=2, Hqk=2, Hv=6, dk=128, dv=128):
+    return L.gdn_decode_multi(_p(q), _p(), _p(), _p(), _p(), _p(), _p(), _p(), _p(), _p(),
+                              None if slots is None else _p(slots), n_rows, B, T, Hqk, Hv, dk, dv, 0.1, 1.0, None)
+
+
+def test_decode_multi_validation(L):
+    L.gdn_decode_multi.restype = ctypes.c_int
+    L.gdn_decode_multi.argtypes = [ctypes.c_void_p] * 11 + [ctypes.c_int] * 7 + \
+        [ctypes.c_float, ctypes.c_float, ctypes.c_void_p]
+    assert call_decode_multi(L, T=0) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call_decode_multi(L, T=5) == gdn.GDN_ERR_UNSUPPORTED
+    assert call_decode_multi(L, B=-1) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call_decode_multi(L, dk=64) == gdn.GDN_ERR_UNSUPPORTED
+    assert call_decode_multi(L, slots=FAKE, n_rows=-1) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call_decode_multi(L, slots=FAKE + 2, n_rows=8) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call_decode_multi(L, q=0) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call_decode_multi(L, B=0) == gdn.GDN_OK
+
