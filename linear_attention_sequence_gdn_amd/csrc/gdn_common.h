@@ -27,9 +27,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f)
 {
     return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
+// two fp32 -> bf16 pair (lo in bits 15:0), one conversion instruction
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // ---- scalar activations -----------------------------------------------------

@@ -42,10 +42,14 @@ constexpr size_t kFragBytes = 64 * 16;               // one 16x32 fp16 operand
 constexpr size_t kQFragBytes = 16 * kFragBytes;      // q^ of a chunk     [64 x 128]
 constexpr size_t kKFragBytes = 16 * kFragBytes;      // k^T of a chunk    [128 x 64]
 constexpr size_t kKTokFragBytes = 16 * kFragBytes;   // k^ of a chunk     [64 x 128]
-constexpr size_t kWFragBytes = 16 * kFragBytes;      // -W of a chunk     [64 x 128]
-constexpr size_t kUBytes = 64 * 128 * 2;             // U' of a chunk     [64 x 128]
-constexpr size_t kPFragBytes = 8 * kFragBytes;       // P of a chunk      [64 x 64]
-constexpr size_t kGateFloats = 256;                 // Gamma[64], r[64], Gamma_n, log2 Gamma_n, pad (1 KiB)
+// The two lower-triangular 64 x 64 matrices keep the six 16x32 fragments that
+// are not structurally zero: (row tile, key block) (0,0) (1,0) (2,0) (2,1)
+// (3,0) (3,1), in that order.
+constexpr size_t kPFragBytes = 6 * kFragBytes;       // P of a chunk      [64 x 64]
+constexpr size_t kTFragBytes = 6 * kFragBytes;       // T' of a chunk     [64 x 64]
+// Per (chunk, V head) floats: [0,64) q_scale Gamma, [64,128) Gamma_n / Gamma,
+// 128 Gamma_n, 129 log2 Gamma_n, [192,256) Gamma (1 KiB)
+constexpr size_t kGateFloats = 256;
 constexpr size_t kStateFloats = 128 * 128;          // one fp32 state
 
 struct Workspace {
@@ -54,10 +58,9 @@ struct Workspace {
     int *order;         // [N] sequences, longest first
     uint8_t *qfrag;     // [max_chunks][Hqk]
     uint8_t *kfrag;     // [max_chunks][Hqk]  k^T, d-major (sequential pass)
-    uint8_t *ktok;      // [max_chunks][Hqk]  k^, token-major (per-head pass)
-    uint8_t *wfrag;     // [max_chunks][Hv]
-    uint8_t *ufrag;     // [max_chunks][Hv]
+    uint8_t *ktok;      // [max_chunks][Hqk]  k^, token-major (both passes)
     uint8_t *pfrag;     // [max_chunks][Hv]
+    uint8_t *tfrag;     // [max_chunks][Hv]
     float *gates;       // [max_chunks][Hv][256]
     int4 *seg_info;     // [max_segs] {seq, first chunk, end chunk, 1: first of seq | 2: last of seq}; seq -1 = unused
     int4 *seq_seg;      // [N] {first segment, segments, -, -}

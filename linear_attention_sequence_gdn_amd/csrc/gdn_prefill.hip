@@ -8,26 +8,27 @@
 //
 //   A    = strict_lower( diag(beta) (K K^T) * D )          (n x n)
 //   T'   = (I + A)^-1 diag(beta)
-//   W    = T' diag(Gam) K,   U' = T' V                     (n x d)
-//   Vnew = U' - W S                                        (S: state entering)
+//   Vnew = T' (V - diag(Gam) K S)                          (S: state entering)
 //   O    = diag(Gam) Q S + (Q K^T * D, lower incl. diag) Vnew
 //   S   <- Gam_n S + (diag(Gam_n / Gam) K)^T Vnew
 //
-// which equals the token-by-token recurrence up to rounding order.
+// which equals the token-by-token recurrence up to rounding order.  (The
+// usual W = T' diag(Gam) K and U' = T' V are never formed: Vnew is one more
+// 64 x 64 product of the sequential pass, which spares writing both to HBM
+// and reading them back.)
 //
-// Three launches:
-//   setup  -- chunk and sequence tables from cu_seqlens (device-side, no host
-//             sync), longest sequences first;
-//   prep   -- fully parallel over (chunk, QK group): conv + SiLU, L2 norm,
-//             gates, K K^T and K Q^T on the matrix cores, the blocked
-//             unit-lower-triangular inverse, W and U' on the matrix cores;
-//             writes every operand the sequential pass needs in the register
-//             order of the matrix-core instruction that consumes it;
-//   chain  -- sequential over the chunks of a sequence, parallel over
-//             (sequence, V head, 16-column slice of the state): the columns
-//             of S evolve independently, so each wave carries a 128 x 16
-//             fp32 slice of S in registers through the whole sequence with no
-//             synchronisation at all.
+// Launches:
+//   setup     -- chunk, sequence and segment tables from cu_seqlens
+//                (device-side, no host sync); uniform batches compute the
+//                same entries arithmetically and skip it;
+//   prep_qk   -- per (chunk, QK group): conv + SiLU + L2 norm of q and k,
+//                written as matrix-core operands;
+//   prep_head -- per (chunk, V head): gates, K K^T and K Q^T on the matrix
+//                cores, A, P, the blocked unit-lower-triangular inverse, T';
+//   chain     -- the sequential pass over (segment, V head): conv + SiLU of v
+//                and every product that involves the state; each wave
+//                carries 32 columns of S in registers;
+//   repair    -- segments whose warm-up bound failed, recomputed in order.
 #include "gdn_prefill.h"
 
 namespace gdn {
@@ -92,20 +93,28 @@ __device__ __forceinline__ void conv_window(const uint16_t *__restrict__ x, long
     }
 }
 
-// Conv (tap 3 = current token) + SiLU over a loaded window; rows >= n give 0.
-__device__ __forceinline__ void conv_silu(const uint32_t (&win)[19], const uint16_t *__restrict__ w, int pp, int r0,
-                                          int n, float (&z0)[16], float (&z1)[16])
+// Conv taps of channels (2*pp, 2*pp+1), tap 3 = current token, times `scale`
+struct ConvW {
+    float a[4], b[4];
+};
+__device__ __forceinline__ ConvW conv_weights(const uint16_t *__restrict__ w, int pp, float scale = 1.0f)
 {
     const uint2 wa = *reinterpret_cast<const uint2 *>(w + (2 * pp) * 4);
     const uint2 wb = *reinterpret_cast<const uint2 *>(w + (2 * pp + 1) * 4);
-    const float a0 = bf16_lo(wa.x), a1 = bf16_hi(wa.x), a2 = bf16_lo(wa.y), a3 = bf16_hi(wa.y);
-    const float b0 = bf16_lo(wb.x), b1 = bf16_hi(wb.x), b2 = bf16_lo(wb.y), b3 = bf16_hi(wb.y);
+    return ConvW{{scale * bf16_lo(wa.x), scale * bf16_hi(wa.x), scale * bf16_lo(wa.y), scale * bf16_hi(wa.y)},
+                 {scale * bf16_lo(wb.x), scale * bf16_hi(wb.x), scale * bf16_lo(wb.y), scale * bf16_hi(wb.y)}};
+}
+
+// Conv + SiLU over a loaded window; rows >= n give 0.
+__device__ __forceinline__ void conv_silu(const uint32_t (&win)[19], const ConvW &cw, int r0, int n,
+                                          float (&z0)[16], float (&z1)[16])
+{
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const float ya = a0 * bf16_lo(win[i]) + a1 * bf16_lo(win[i + 1]) + a2 * bf16_lo(win[i + 2]) +
-                         a3 * bf16_lo(win[i + 3]);
-        const float yb = b0 * bf16_hi(win[i]) + b1 * bf16_hi(win[i + 1]) + b2 * bf16_hi(win[i + 2]) +
-                         b3 * bf16_hi(win[i + 3]);
+        const float ya = cw.a[0] * bf16_lo(win[i]) + cw.a[1] * bf16_lo(win[i + 1]) +
+                         cw.a[2] * bf16_lo(win[i + 2]) + cw.a[3] * bf16_lo(win[i + 3]);
+        const float yb = cw.b[0] * bf16_hi(win[i]) + cw.b[1] * bf16_hi(win[i + 1]) +
+                         cw.b[2] * bf16_hi(win[i + 2]) + cw.b[3] * bf16_hi(win[i + 3]);
         const bool valid = r0 + i < n;
         z0[i] = valid ? silu_f(ya) : 0.0f;
         z1[i] = valid ? silu_f(yb) : 0.0f;
@@ -119,7 +128,7 @@ __device__ __forceinline__ void conv_plane(const uint16_t *__restrict__ x, long 
 {
     uint32_t win[19];
     conv_window(x, ld, n, first, hist, C_tot, pp, r0, win);
-    conv_silu(win, w, pp, r0, n, z0, z1);
+    conv_silu(win, conv_weights(w, pp), r0, n, z0, z1);
 }
 
 // ---------------------------------------------------------------------------
@@ -413,26 +422,23 @@ __device__ __forceinline__ void st16_f32(float *Db, int ldd, f32x4 v, int lane)
     for (int e = 0; e < 4; ++e) Db[(4 * q + e) * ldd + c] = v[e];
 }
 
-// prepB: per (chunk, V head) -- gates, conv + SiLU of v, K K^T and K Q^T,
-// A, P, the unit-lower-triangular inverse, T', U' = T' V and -W.
-constexpr int kH_LD = 68;  // fp16 row stride of v^T, T', T' diag(Gam) (8-byte aligned rows)
+// Index of fragment (row tile rt, key block kb <= rt / 2) of a lower-triangular
+// 64 x 64 operand in its compact order
+__host__ __device__ constexpr int tri_frag(int rt, int kb) { return rt < 2 ? rt : 2 * rt - 2 + kb; }
 
+// prepB: per (chunk, V head) -- gates, K K^T and K Q^T, A, P, the
+// unit-lower-triangular inverse and T'.
 __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, Workspace ws)
 {
-    // LDS plan: [F] k^ operands (16 KiB) -> X = (I+A)^-1 (fp32) -> v^T (fp16);
-    //           [A] A (fp32) -> T' and T' diag(Gam) (fp16); scratch; gates
+    // LDS plan: [F] k^ operands (16 KiB) -> X = (I+A)^-1 (fp32); [A] A (fp32); scratch
     __shared__ __attribute__((aligned(16))) uint8_t regF[64 * kAL * 4];
     __shared__ __attribute__((aligned(16))) uint8_t regA[64 * kAL * 4];
     __shared__ __attribute__((aligned(16))) float Msc[3][256];
-    __shared__ float s_gam2[64], s_beta[64], s_bg[64];
+    __shared__ float s_gam2[64];
+    __shared__ __attribute__((aligned(16))) float s_beta[64];
     const half8 *Fk = reinterpret_cast<const half8 *>(regF);  // k^ token-major: [rt*4+kb][lane]
     float *Xs = reinterpret_cast<float *>(regF);
-    _Float16 *VTs = reinterpret_cast<_Float16 *>(regF);
     float *As = reinterpret_cast<float *>(regA);
-    _Float16 *Th = reinterpret_cast<_Float16 *>(regA);
-    _Float16 *TGh = Th + 64 * kH_LD;
-    static_assert(128 * kH_LD * 2 <= 64 * kAL * 4, "v^T fits over X");
-    static_assert(2 * 64 * kH_LD * 2 <= 64 * kAL * 4, "T' and T' diag(Gam) fit over A");
 
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -449,14 +455,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
     const int4 ci = Tables::chunk(p, ws, c);
     const int n = ci.z;
     if (n == 0) return;
-    const int s = ci.x, t0 = ci.y;
-    const bool first = ci.w != 0;
-    const long C_tot = 2L * Hqk * kD + (long)Hv * kD;
-    const uint16_t *hist = (first && p.conv_state_in) ? p.conv_state_in + (long)s * 3 * C_tot : nullptr;
+    const int t0 = ci.y;
     const long hc = (long)c * Hv + h, gc = (long)c * Hqk + g;
-    const int r0 = 16 * wave;
-    const long ldv = (long)Hv * kD;
-    const long cv = 2L * Hqk * kD + (long)h * kD;
 
     // ---- every global read of the workgroup is issued first
     {
@@ -467,18 +467,12 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t *)(regF + blk * 1024), 16, lane * 16, blk * 1024, 0, 0);
         }
     }
-    half8 qB[4], kT[4];
+    half8 qB[4];
     {
         const half8 *qf = reinterpret_cast<const half8 *>(ws.qfrag + gc * kQFragBytes) + lane;
-        const half8 *kf = reinterpret_cast<const half8 *>(ws.kfrag + gc * kKFragBytes) + lane;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            qB[kb] = qf[(wave * 4 + kb) * 64];
-            kT[kb] = kf[(wave * 4 + kb) * 64];  // k^T row tiles 2w, 2w+1, k-blocks 0..1
-        }
+        for (int kb = 0; kb < 4; ++kb) qB[kb] = qf[(wave * 4 + kb) * 64];
     }
-    uint32_t vwin[19];
-    conv_window(p.v + (long)t0 * ldv + (long)h * kD, ldv, n, first, hist ? hist + cv : nullptr, C_tot, lane, r0, vwin);
     float av = 0.f, bv = 0.f;
     if (wave == 0 && lane < n) {
         const long ti = (long)(t0 + lane) * Hv + h;
@@ -501,11 +495,10 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
         const float Gam = __builtin_amdgcn_exp2f(gam);
         s_gam2[lane] = gam;
         s_beta[lane] = be;
-        s_bg[lane] = be * Gam;
-        // [0,64): q_scale * Gam (only the output uses it); [64,128): Gam_n / Gam; 128: Gam_n; 129: log2 Gam_n
         float *gt = ws.gates + hc * kGateFloats;
         gt[lane] = p.q_scale * Gam;
         gt[64 + lane] = valid ? __builtin_amdgcn_exp2f(gam_n - gam) : 0.f;
+        gt[192 + lane] = Gam;
         if (lane == 0) {
             gt[128] = __builtin_amdgcn_exp2f(gam_n);
             gt[129] = gam_n;
@@ -564,7 +557,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
                     val = p.q_scale * kq[jt][e & 3] * __builtin_amdgcn_exp2f(gi - s_gam2[jj]);
                 fr[e] = (_Float16)val;
             }
-            pf[(wave * 2 + kb) * 64 + lane] = fr;
+            pf[tri_frag(wave, kb) * 64 + lane] = fr;
         }
     }
     __syncthreads();
@@ -601,84 +594,26 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
         }
         __syncthreads();
     }
-    // ---- T' = X diag(beta) and T' diag(Gam) (fp16, lower) over A's storage
+    // ---- T' = X diag(beta), lower triangle, as A operands (rows = tokens i,
+    //      contraction = tokens j): wave w writes fragments w and w + 4
     {
-        float tv[16], tg[16];
+        half8 *tf = reinterpret_cast<half8 *>(ws.tfrag + hc * kTFragBytes);
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int e = t + k * kPrepThreads;
-            const int i = e >> 6, jj = e & 63;
-            const float xv = jj <= i ? Xs[i * kAL + jj] : 0.f;
-            tv[k] = xv * s_beta[jj];
-            tg[k] = xv * s_bg[jj];
-        }
-        __syncthreads();  // A and X are dead from here on
+        for (int f2 = 0; f2 < 2; ++f2) {
+            const int f = wave + 4 * f2;
+            if (f >= 6) continue;
+            const int rt = f < 2 ? f : (f + 2) >> 1, kb = f < 2 ? 0 : f & 1;
+            const int i = 16 * rt + c16;
+            half8 fr;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int e = t + k * kPrepThreads;
-            const int i = e >> 6, jj = e & 63;
-            Th[i * kH_LD + jj] = (_Float16)tv[k];
-            TGh[i * kH_LD + jj] = (_Float16)tg[k];
-        }
-    }
-    // ---- v^ of head h: conv + SiLU from the window loaded at the start -> v^T
-    //      over X; each lane writes 16 consecutive rows of two channels
-    {
-        float z0[16], z1[16];
-        conv_silu(vwin, p.conv_w + cv * 4, lane, r0, n, z0, z1);
+            for (int hb = 0; hb < 2; ++hb) {
+                const int j0 = 32 * kb + 16 * hb + 4 * q4;
+                const f32x4 xv = *reinterpret_cast<const f32x4 *>(Xs + i * kAL + j0);
+                const f32x4 bb = *reinterpret_cast<const f32x4 *>(s_beta + j0);
 #pragma unroll
-        for (int i = 0; i < 16; i += 4) {
-            *reinterpret_cast<half4 *>(VTs + (2 * lane) * kH_LD + r0 + i) =
-                half4{(_Float16)z0[i], (_Float16)z0[i + 1], (_Float16)z0[i + 2], (_Float16)z0[i + 3]};
-            *reinterpret_cast<half4 *>(VTs + (2 * lane + 1) * kH_LD + r0 + i) =
-                half4{(_Float16)z1[i], (_Float16)z1[i + 1], (_Float16)z1[i + 2], (_Float16)z1[i + 3]};
-        }
-    }
-    __syncthreads();
-    // ---- U' = T' V: column tiles 2*wave, 2*wave+1; stored as B operands over
-    //      the chunk's two 32-token blocks (the accumulator rows of token tiles
-    //      2tb and 2tb+1 side by side): fragment ct*2 + tb
-    {
-        half8 *uf = reinterpret_cast<half8 *>(ws.ufrag + hc * kUBytes);
-        half8 ta[4][2];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            ta[rt][0] = lds_frag(Th, kH_LD, 16 * rt, 0, lane);
-            ta[rt][1] = lds_frag(Th, kH_LD, 16 * rt, 32, lane);
-        }
-#pragma unroll
-        for (int cti = 0; cti < 2; ++cti) {
-            const int ct = 2 * wave + cti;
-            const half8 b0 = lds_frag(VTs, kH_LD, 16 * ct, 0, lane);
-            const half8 b1 = lds_frag(VTs, kH_LD, 16 * ct, 32, lane);
-            f32x4 acc[4];
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                acc[rt] = mfma16(ta[rt][0], b0, acc[rt]);
-                if (rt >= 2) acc[rt] = mfma16(ta[rt][1], b1, acc[rt]);
+                for (int e = 0; e < 4; ++e) fr[4 * hb + e] = (_Float16)(j0 + e <= i ? xv[e] * bb[e] : 0.f);
             }
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) uf[(ct * 2 + tb) * 64 + lane] = pack_h8(acc[2 * tb], acc[2 * tb + 1]);
-        }
-    }
-    // ---- W^T = K^T diag(Gam) T'^T: d tiles 2*wave, 2*wave+1 (k-block `wave`
-    //      of -W), all four token tiles; -W stored as A operand
-    {
-        half8 *wf = reinterpret_cast<half8 *>(ws.wfrag + hc * kWFragBytes);
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            const half8 b0 = lds_frag(TGh, kH_LD, 16 * ct, 0, lane);
-            const half8 b1 = lds_frag(TGh, kH_LD, 16 * ct, 32, lane);
-            f32x4 w2[2];
-#pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mfma16(kT[2 * rr + 0], b0, acc);
-                if (ct >= 2) acc = mfma16(kT[2 * rr + 1], b1, acc);
-                w2[rr] = acc;
-            }
-            wf[(ct * 4 + wave) * 64 + lane] = pack_h8(-w2[0], -w2[1]);
+            tf[f * 64 + lane] = fr;
         }
     }
 }
@@ -688,62 +623,62 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
 // ---------------------------------------------------------------------------
 // Workgroup = one (segment, V head), 4 waves; wave w owns the state columns
 // 32w .. 32w+31 (two 16-column tiles) in every product of a chunk:
-//   Vnew = U' - W S                    64 tokens x 32 columns, over d_k
-//   Q S                                64 tokens x 32 columns, over d_k
-//   S <- Gam_n S + k^T (r Vnew)        d_k x 32 columns, over the chunk's tokens
+//   X = K S,  Q S                      64 tokens x 32 columns, over d_k
+//   Vnew = T' (V - diag(Gam) X)        64 tokens x 32 columns, over the chunk
+//   S <- Gam_n S + k^T (r Vnew)        d_k x 32 columns, over the chunk
 //   O = diag(q_scale Gam) Q S + P Vnew
 // The B operands of these products are the wave's own accumulators: with the
 // kappa k-mapping, a lane's accumulator rows 4q..4q+3 of two vertically
 // adjacent 16-row tiles are exactly its eight B-operand elements of the
-// 32-deep block they form, so the state and Vnew never leave the wave.  The
-// waves share only the chunk's operands (-W, q^, k^T, P, U', gates), which the
-// workgroup stages in LDS with direct-to-LDS loads into two buffers, one
-// barrier per chunk; the only other memory operations are the output stores,
-// so waiting for a chunk's operands never waits for the stores.
+// 32-deep block they form, so the state, X and Vnew never leave the wave.
+// The waves share the chunk's operands (k^, q^, k^T, P, T', gates), which the
+// workgroup stages in LDS with direct-to-LDS loads into two buffers, and v^
+// (conv + SiLU of the chunk's v rows), which each wave computes one chunk
+// ahead for 16 tokens of every channel and leaves transposed in LDS, also in
+// two buffers; one barrier per chunk.  Waiting for a chunk's operands never
+// waits for the output stores: they are the only memory operations issued
+// after the operand loads.
 constexpr int kChainBlocksPerHead = 1;
-constexpr int kChainStage = 32 * 32 * 2;  // output staging of one wave: 32 tokens x 32 columns bf16
 struct ChainBuf {
-    static constexpr int kW = 0, kQ = 16384, kK = 32768, kP = 49152, kU = 57344, kG = 73728, kBytes = 74752;
+    // k^ (token-major), q^, k^T, P, T', gates
+    static constexpr int kK = 0, kQ = 16384, kKT = 32768, kP = 49152, kT = 55296, kG = 61440, kBytes = 62464;
 };
+constexpr int kVT_LD = 68;                 // fp16 row stride of v^T (one channel: 64 tokens + pad)
+constexpr int kVTHalfs = kD * kVT_LD;
+// The output of a wave goes out through an LDS staging of 32 tokens x 32
+// columns (bf16) in the wave's own channel rows of the current v^T buffer,
+// which no other wave reads.
+static_assert(32 * kVT_LD * 2 >= 32 * 32 * 2, "output staging fits in a wave's v^T rows");
 
-// raw buffer resource over `bytes` bytes at `base`: reads past the end return 0
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t sized_rsrc(const void *base, int bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
-}
-
-// Chunk c's operands into one LDS buffer: 73 pieces of 1 KiB; wave w moves
-// pieces 4i + w of -W, q^, k^T (i < 4) and P (i < 2), pieces 4w + i of U'
-// (its own two column tiles), and wave 0 the gates.  Issued in four groups
-// (i = 0..3), spread through a chunk step so that the memory unit takes them
-// while the matrix cores work.
+// Chunk c's operands into one LDS buffer: 61 pieces of 1 KiB; wave w moves
+// pieces 4i + w of k^, q^, k^T (i < 4) and of P and T' (4i + w < 6), and wave
+// 0 the gates.  Issued in four groups (i = 0..3), spread through a chunk step
+// so that the memory unit takes them while the matrix cores work.
 struct ChainDma {
-    __amdgpu_buffer_rsrc_t rw, rq, rk, rp, ru, rg;
+    __amdgpu_buffer_rsrc_t rk, rq, rkt, rp, rt, rg;
 };
 
 __device__ __forceinline__ ChainDma chain_dma_plan(const Workspace &ws, long c, int h, int g, int Hqk, int Hv)
 {
     const long hc = c * Hv + h, gc = c * Hqk + g;
-    return ChainDma{region_rsrc(ws.wfrag + hc * kWFragBytes), region_rsrc(ws.qfrag + gc * kQFragBytes),
+    return ChainDma{region_rsrc(ws.ktok + gc * kKTokFragBytes), region_rsrc(ws.qfrag + gc * kQFragBytes),
                     region_rsrc(ws.kfrag + gc * kKFragBytes), region_rsrc(ws.pfrag + hc * kPFragBytes),
-                    region_rsrc(ws.ufrag + hc * kUBytes), region_rsrc(ws.gates + hc * kGateFloats)};
+                    region_rsrc(ws.tfrag + hc * kTFragBytes), region_rsrc(ws.gates + hc * kGateFloats)};
 }
 
 template <int I>
 __device__ __forceinline__ void chain_dma_group(const ChainDma &d, uint8_t *buf, int wave, int lane)
 {
     const int f = 4 * I + wave, v16 = lane * 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rw, (lds_void_t *)(buf + ChainBuf::kW + f * 1024), 16, v16, f * 1024, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rq, (lds_void_t *)(buf + ChainBuf::kQ + f * 1024), 16, v16, f * 1024, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rk, (lds_void_t *)(buf + ChainBuf::kK + f * 1024), 16, v16, f * 1024, 0, 0);
-    // P: fragments 1 and 3 (query tiles 0, 1 against key block 1) are zero and never stored
-    if (I == 1 || (I == 0 && (wave & 1) == 0))
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rq, (lds_void_t *)(buf + ChainBuf::kQ + f * 1024), 16, v16, f * 1024, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rkt, (lds_void_t *)(buf + ChainBuf::kKT + f * 1024), 16, v16, f * 1024, 0, 0);
+    if (I == 0 || (I == 1 && wave < 2)) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rp, (lds_void_t *)(buf + ChainBuf::kP + f * 1024), 16, v16, f * 1024, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rt, (lds_void_t *)(buf + ChainBuf::kT + f * 1024), 16, v16, f * 1024, 0, 0);
+    }
     if (I == 2 && wave == 0)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rg, (lds_void_t *)(buf + ChainBuf::kG), 16, v16, 0, 0, 0);
-    // U': the wave's own 4 KiB (its two column tiles)
-    const int fu = 4 * wave + I;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ru, (lds_void_t *)(buf + ChainBuf::kU + fu * 1024), 16, v16, fu * 1024, 0, 0);
 }
 
 __device__ __forceinline__ void chain_dma(const Workspace &ws, uint8_t *buf, long c, int h, int g, int Hqk,
@@ -758,11 +693,114 @@ __device__ __forceinline__ void chain_dma(const Workspace &ws, uint8_t *buf, lon
 
 // Chunk range of one run of the sequential pass: chunks [c_from, c_to) of a
 // sequence whose chunk 0 is c0 (first token t0, L tokens); chunks before c_out
-// only advance the state (their output stores are dropped).
+// only advance the state (their output stores are dropped).  v is the head's
+// v at the sequence's first token, hist its carried conv rows (or NULL).
 struct ChainRun {
     int c0, t0, L;
     int c_from, c_to, c_out;
+    const uint16_t *v, *hist;
 };
+
+// Raw v rows of chunk cc for tokens 16w .. 16w+15 and the three before, of
+// channels 2*lane, 2*lane+1 -- without branches: one buffer range covers the
+// rows that come from v (the chunk's n rows, and the three before unless the
+// chunk starts the sequence), and everything outside it reads as zero; the
+// carried conv rows of a sequence's first chunk are a second range.
+__device__ __forceinline__ void chain_vload(const PrefillArgs &p, const ChainRun &run, int cc, int wave, int lane,
+                                            uint32_t (&win)[19])
+{
+    const int rel = (cc - run.c0) * kChunk;
+    const int n = min(kChunk, run.L - rel);
+    const bool first = cc == run.c0;
+    const int lo = first ? 0 : -3;  // first row taken from v
+    const int ldb = p.Hv * kD * 2;  // bytes per token row of v
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(run.v + (long)(rel + lo) * (ldb / 2)), 0, (n - lo) * ldb, 0x00020000);
+    // row r0 - 3 + i sits at (r0 - 3 + i - lo) rows into the range; rows
+    // before it give a negative offset, which the range check rejects too
+    const int voff = (16 * wave - 3 - lo) * ldb + 4 * lane;
+#pragma unroll
+    for (int i = 0; i < 19; ++i) win[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff + i * ldb, 0, 0);
+    if (first && wave == 0 && run.hist) {
+        const int ldh = (2 * p.Hqk * kD + p.Hv * kD) * 2;  // bytes per carried row
+        const __amdgpu_buffer_rsrc_t rh =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(run.hist), 0, 3 * ldh, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) win[i] = __builtin_amdgcn_raw_buffer_load_b32(rh, 4 * lane + i * ldh, 0, 0);
+    }
+}
+
+// v^ = SiLU(conv) of four of those rows (tokens 16w + 4P .. +3) into v^T:
+// channel rows 2*lane, 2*lane+1.  The taps come pre-scaled by -log2(e), so
+// the conv gives u = -y log2(e) and SiLU(y) = y / (1 + 2^u) = u / (-log2(e) (1 + 2^u)).
+// Tokens past the chunk's end are not masked: they come out finite (their raw
+// rows read as zero) and meet only zero columns of T'.
+constexpr float kNegLog2e = -kLog2e;
+__device__ __forceinline__ float silu_scaled(float u)
+{
+    return u * __builtin_amdgcn_rcpf(__builtin_fmaf(__builtin_amdgcn_exp2f(u), kNegLog2e, kNegLog2e));
+}
+template <int P>
+__device__ __forceinline__ void chain_vconv(const ConvW &cw, const uint32_t (&win)[19], _Float16 *vt, int wave,
+                                            int lane)
+{
+    float xa[7], xb[7];
+#pragma unroll
+    for (int m = 0; m < 7; ++m) {
+        xa[m] = bf16_lo(win[4 * P + m]);
+        xb[m] = bf16_hi(win[4 * P + m]);
+    }
+    half4 ha, hb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float ya = cw.a[0] * xa[e] + cw.a[1] * xa[e + 1] + cw.a[2] * xa[e + 2] + cw.a[3] * xa[e + 3];
+        const float yb = cw.b[0] * xb[e] + cw.b[1] * xb[e + 1] + cw.b[2] * xb[e + 2] + cw.b[3] * xb[e + 3];
+        ha[e] = (_Float16)silu_scaled(ya);
+        hb[e] = (_Float16)silu_scaled(yb);
+    }
+    *reinterpret_cast<half4 *>(vt + (2 * lane) * kVT_LD + 16 * wave + 4 * P) = ha;
+    *reinterpret_cast<half4 *>(vt + (2 * lane + 1) * kVT_LD + 16 * wave + 4 * P) = hb;
+}
+__device__ __forceinline__ void chain_vconv_all(const ConvW &cw, const uint32_t (&win)[19], _Float16 *vt, int wave,
+                                                int lane)
+{
+    chain_vconv<0>(cw, win, vt, wave, lane);
+    chain_vconv<1>(cw, win, vt, wave, lane);
+    chain_vconv<2>(cw, win, vt, wave, lane);
+    chain_vconv<3>(cw, win, vt, wave, lane);
+}
+
+// The same four rows in eleven slices, to be spread between matrix-core
+// instructions: slices 0-1 unpack the window, 2-9 form one output each,
+// 10 writes the two rows.
+struct VConvSlices {
+    float xa[7], xb[7];
+    half4 ha, hb;
+};
+__device__ __forceinline__ void chain_vconv_slice(int sl, int P, VConvSlices &st, const ConvW &cw,
+                                                  const uint32_t (&win)[19], _Float16 *vt, int wave, int lane)
+{
+    if (sl == 0 || sl == 1) {
+#pragma unroll
+        for (int m = 0; m < 7; ++m)
+            if ((m < 4) == (sl == 0)) {
+                st.xa[m] = bf16_lo(win[4 * P + m]);
+                st.xb[m] = bf16_hi(win[4 * P + m]);
+            }
+    } else if (sl < 10) {
+        const int e = (sl - 2) >> 1;
+        if (((sl - 2) & 1) == 0) {
+            const float u = cw.a[0] * st.xa[e] + cw.a[1] * st.xa[e + 1] + cw.a[2] * st.xa[e + 2] + cw.a[3] * st.xa[e + 3];
+            st.ha[e] = (_Float16)silu_scaled(u);
+        } else {
+            const float u = cw.b[0] * st.xb[e] + cw.b[1] * st.xb[e + 1] + cw.b[2] * st.xb[e + 2] + cw.b[3] * st.xb[e + 3];
+            st.hb[e] = (_Float16)silu_scaled(u);
+        }
+    } else if (sl == 10) {
+        *reinterpret_cast<half4 *>(vt + (2 * lane) * kVT_LD + 16 * wave + 4 * P) = st.ha;
+        *reinterpret_cast<half4 *>(vt + (2 * lane + 1) * kVT_LD + 16 * wave + 4 * P) = st.hb;
+    }
+}
 
 // VMEM operations a wave issues after a chunk's operand DMA and before the
 // step that consumes it: the previous chunk's output stores (4).  Waiting
@@ -775,60 +813,62 @@ constexpr int kChainVmemAfterDma = 4;
 // lgkmcnt at their no-wait maxima
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
 
-// Identity operand that copies rows 16*odd .. 16*odd+15 of a 32-deep B block
-// into a 16-row accumulator: lane (q, c) holds A[c][kappa(q, i)].
-__device__ __forceinline__ half8 eye_frag(int odd, int lane)
-{
-    const int q4 = lane >> 4, c16 = lane & 15;
-    half8 r;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = (_Float16)((q4 == (c16 >> 2) && i == 4 * odd + (c16 & 3)) ? 1.0f : 0.0f);
-    return r;
-}
-
-// One chunk from buffer `cur`; issues the next chunk's DMA into `nxt`.
-//   Vn  [rt][x]  Vnew, tokens 16rt.. x columns 16x..  (accumulator rows = tokens)
-//   QST [x][rt]  (Q S)^T, columns 16x.. x tokens 16rt.. (accumulator rows = columns)
+// One chunk from operand buffer `cur` and v^T buffer `vtc`; loads the next
+// chunk's operands into `nxt`, converts its raw v rows (`win`, loaded a step
+// ago) into `vtn`, and loads the raw v rows of the chunk after it into `win`.
+//   X, Vn [rt][x]  tokens 16rt.. x columns 16x..  (accumulator rows = tokens)
+//   QST   [x][rt]  (Q S)^T, columns 16x.. x tokens 16rt.. (accumulator rows = columns)
 // The output is formed transposed, O^T = S^T Q^T diag(q_scale Gam) + Vnew^T P^T,
 // so that a lane holds four adjacent columns of one token (8-byte LDS writes
 // into the row staging).  The fragment layout is the same for A and B
 // operands, so the packed state and Vnew serve as A operands unchanged.
 __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace &ws, uint8_t *cur, uint8_t *nxt,
-                                           uint8_t *stage, f32x4 (&S)[8][2], const half8 (&eye)[2],
-                                           const ChainRun &run, int cc, int h, int g, int wave, int lane)
+                                           _Float16 *vtc, _Float16 *vtn, uint32_t (&win)[19], f32x4 (&S)[8][2],
+                                           const ConvW &cw, const ChainRun &run, int cc, int h, int g, int wave,
+                                           int lane)
 {
     const int Hqk = p.Hqk, Hv = p.Hv;
     const int q4 = lane >> 4, c16 = lane & 15;
-    // chunk cc's operands (DMA'd a step ago) have landed for every wave, and
-    // every wave is done with the buffer the next DMA overwrites
+    // chunk cc's operands and v^ have landed for every wave, and every wave is
+    // done with the buffers the next chunk's loads overwrite
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kChainVmemAfterDma));
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    const int cn = min(cc + 1, run.c_to - 1);
+    // the next chunk and the one after (the last steps repeat the run's last)
+    const int cn = min(cc + 1, run.c_to - 1), cn2 = min(cc + 2, run.c_to - 1);
     const ChainDma dn = chain_dma_plan(ws, cn, h, g, Hqk, Hv);
 
-    const half8 *Wf = reinterpret_cast<const half8 *>(cur + ChainBuf::kW) + lane;
-    const half8 *Qf = reinterpret_cast<const half8 *>(cur + ChainBuf::kQ) + lane;
     const half8 *Kf = reinterpret_cast<const half8 *>(cur + ChainBuf::kK) + lane;
+    const half8 *Qf = reinterpret_cast<const half8 *>(cur + ChainBuf::kQ) + lane;
+    const half8 *KTf = reinterpret_cast<const half8 *>(cur + ChainBuf::kKT) + lane;
     const half8 *Pf = reinterpret_cast<const half8 *>(cur + ChainBuf::kP) + lane;
-    const half8 *Uf = reinterpret_cast<const half8 *>(cur + ChainBuf::kU) + (4 * wave) * 64 + lane;
+    const half8 *Tf = reinterpret_cast<const half8 *>(cur + ChainBuf::kT) + lane;
     const float *gt = reinterpret_cast<const float *>(cur + ChainBuf::kG);
 
-    // W S and (Q S)^T over the four 32-row blocks of the state; the LDS
+    // v^ at the wave's columns in accumulator layout: tile (rt, x) lane (q, c)
+    // holds tokens 16rt + 4q .. +3 of column 32w + 16x + c
+    half4 vh[4][2];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+            vh[rt][x] = *reinterpret_cast<const half4 *>(vtc + (32 * wave + 16 * x + c16) * kVT_LD + 16 * rt + 4 * q4);
+
+    // K S and (Q S)^T over the four 32-row blocks of the state; the LDS
     // fragments of block kb+1 are read while block kb multiplies, and the
     // next chunk's DMA goes out one group per block
-    f32x4 Vn[4][2], QST[2][4];
+    f32x4 X[4][2], QST[2][4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
-            Vn[rt][x] = f32x4{0.f, 0.f, 0.f, 0.f};
+            X[rt][x] = f32x4{0.f, 0.f, 0.f, 0.f};
             QST[x][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-    half8 aw[2][4], aq[2][4];
+    half8 ak[2][4], aq[2][4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-        aw[0][rt] = Wf[(rt * 4) * 64];
+        ak[0][rt] = Kf[(rt * 4) * 64];
         aq[0][rt] = Qf[(rt * 4) * 64];
     }
 #pragma unroll
@@ -837,7 +877,7 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
         if (kb < 3) {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                aw[cb ^ 1][rt] = Wf[(rt * 4 + kb + 1) * 64];
+                ak[cb ^ 1][rt] = Kf[(rt * 4 + kb + 1) * 64];
                 aq[cb ^ 1][rt] = Qf[(rt * 4 + kb + 1) * 64];
             }
         }
@@ -848,40 +888,66 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
         __builtin_amdgcn_sched_barrier(0);
         const half8 sb0 = pack_h8(S[2 * kb][0], S[2 * kb + 1][0]);
         const half8 sb1 = pack_h8(S[2 * kb][1], S[2 * kb + 1][1]);
+        // a quarter of the next chunk's v^ on the vector ALUs, one slice
+        // after each matrix-core instruction
+        VConvSlices vs;
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            Vn[rt][0] = mfma16(aw[cb][rt], sb0, Vn[rt][0]);
-            Vn[rt][1] = mfma16(aw[cb][rt], sb1, Vn[rt][1]);
-            QST[0][rt] = mfma16(sb0, aq[cb][rt], QST[0][rt]);
-            QST[1][rt] = mfma16(sb1, aq[cb][rt], QST[1][rt]);
+        for (int sl = 0; sl < 16; ++sl) {
+            const int rt = sl >> 2;
+            switch (sl & 3) {
+            case 0: X[rt][0] = mfma16(ak[cb][rt], sb0, X[rt][0]); break;
+            case 1: X[rt][1] = mfma16(ak[cb][rt], sb1, X[rt][1]); break;
+            case 2: QST[0][rt] = mfma16(sb0, aq[cb][rt], QST[0][rt]); break;
+            default: QST[1][rt] = mfma16(sb1, aq[cb][rt], QST[1][rt]); break;
+            }
+            chain_vconv_slice(sl, kb, vs, cw, win, vtn, wave, lane);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
-    // + U' (exact: an identity product of its fp16 values, B operand over
-    // token block rt / 2)
+    // raw v rows of the chunk after the next, converted in the next step
+    __builtin_amdgcn_sched_barrier(0);
+    chain_vload(p, run, cn2, wave, lane, win);
+    __builtin_amdgcn_sched_barrier(0);
+    // Vnew = T' (V - diag(Gam) X): the bracket as B operands over the chunk's
+    // two 32-token blocks, T' lower triangular
+    half8 tf[6];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) tf[i] = Tf[i * 64];
+    f32x4 Vn[4][2];
     {
-        half8 ub[2][2];
+        f32x4 gg[4];
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
+        for (int rt = 0; rt < 4; ++rt) gg[rt] = *reinterpret_cast<const f32x4 *>(gt + 192 + 16 * rt + 4 * q4);
+        half8 yb[2][2];
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) ub[x][tb] = Uf[(2 * x + tb) * 64];
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                f32x4 y[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        y[i][e] = (float)vh[2 * tb + i][x][e] - gg[2 * tb + i][e] * X[2 * tb + i][x][e];
+                yb[tb][x] = pack_h8(y[0], y[1]);
+            }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-            for (int x = 0; x < 2; ++x) Vn[rt][x] = mfma16(eye[rt & 1], ub[x][rt >> 1], Vn[rt][x]);
+            for (int x = 0; x < 2; ++x) {
+                Vn[rt][x] = mfma16(tf[tri_frag(rt, 0)], yb[0][x], f32x4{0.f, 0.f, 0.f, 0.f});
+                if (rt >= 2) Vn[rt][x] = mfma16(tf[tri_frag(rt, 1)], yb[1][x], Vn[rt][x]);
+            }
     }
     // k^T fragments of the first two 16-row state tiles, P, and the gates
     half8 kf[2][2][2];  // [buffer][tile in pair][token block]
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) kf[0][i][tb] = Kf[(2 * i + tb) * 64];
-    half8 pf[6];  // P: row tiles 0, 1 (token block 0), 2, 3 (token blocks 0, 1)
-    pf[0] = Pf[0 * 64];
-    pf[1] = Pf[2 * 64];
-    pf[2] = Pf[4 * 64];
-    pf[3] = Pf[5 * 64];
-    pf[4] = Pf[6 * 64];
-    pf[5] = Pf[7 * 64];
+        for (int tb = 0; tb < 2; ++tb) kf[0][i][tb] = KTf[(2 * i + tb) * 64];
+    half8 pf[6];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) pf[i] = Pf[i * 64];
     f32x4 rg[4];
     float gm[4];
 #pragma unroll
@@ -909,7 +975,7 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int tb = 0; tb < 2; ++tb) kf[cb ^ 1][i][tb] = Kf[(2 * (2 * pr + 2 + i) + tb) * 64];
+                for (int tb = 0; tb < 2; ++tb) kf[cb ^ 1][i][tb] = KTf[(2 * (2 * pr + 2 + i) + tb) * 64];
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -922,17 +988,18 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
             }
         }
     }
-    // O = diag(q_scale Gam) Q S + P Vnew (P lower triangular), through a
-    // per-wave LDS staging of 32 token rows at a time: (Q S)^T tile (x, rt)
-    // lane (q, c) holds columns 16x + 4q .. +3 of token 16rt + c.  The buffer
-    // range of the stores ends at the chunk's last valid token, so the rows of
-    // a partial chunk and every row of a warm-up chunk (n = 0) are dropped
-    // without a branch.
+    // O = diag(q_scale Gam) Q S + P Vnew (P lower triangular), through the
+    // wave's staging 32 token rows at a time: (Q S)^T tile (x, rt) lane (q, c)
+    // holds columns 16x + 4q .. +3 of token 16rt + c.  The buffer range of the
+    // stores ends at the chunk's last valid token, so the rows of a partial
+    // chunk and every row of a warm-up chunk (n = 0) are dropped without a
+    // branch.
     const int rel = (cc - run.c0) * kChunk;
     const int n = cc >= run.c_out ? min(kChunk, run.L - rel) : 0;
     const int rowb = Hv * kD * 2;  // bytes per token row of o
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
         p.o + ((long)(run.t0 + rel) * Hv + h) * kD + 32 * wave, 0, n * rowb, 0x00020000);
+    uint8_t *stage = reinterpret_cast<uint8_t *>(vtc + 32 * wave * kVT_LD);
     uint16_t *os = reinterpret_cast<uint16_t *>(stage);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -941,8 +1008,8 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
             const int rt = 2 * half + r2;
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
-                f32x4 acc = mfma16(vb[0][x], pf[rt < 2 ? rt : 2 * rt - 2], QST[x][rt] * gm[rt]);
-                if (rt >= 2) acc = mfma16(vb[1][x], pf[2 * rt - 1], acc);
+                f32x4 acc = mfma16(vb[0][x], pf[tri_frag(rt, 0)], QST[x][rt] * gm[rt]);
+                if (rt >= 2) acc = mfma16(vb[1][x], pf[tri_frag(rt, 1)], acc);
                 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
                 const u32x2 v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
                 *reinterpret_cast<u32x2 *>(os + (16 * r2 + c16) * 32 + 16 * x + 4 * q4) = v;
@@ -966,18 +1033,22 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
 
 // The chunks of one run, the state carried in registers.
 __device__ __forceinline__ void chain_run(const PrefillArgs &p, const Workspace &ws, uint8_t *buf0, uint8_t *buf1,
-                                          uint8_t *stage, f32x4 (&S)[8][2], const half8 (&eye)[2],
+                                          _Float16 *vt0, _Float16 *vt1, f32x4 (&S)[8][2], const ConvW &cw,
                                           const ChainRun &run, int h, int g, int wave, int lane)
 {
     if (run.c_to <= run.c_from) return;
     chain_dma(ws, buf0, run.c_from, h, g, p.Hqk, p.Hv, wave, lane);
+    uint32_t win[19];
+    chain_vload(p, run, run.c_from, wave, lane, win);
+    chain_vconv_all(cw, win, vt0, wave, lane);
+    chain_vload(p, run, min(run.c_from + 1, run.c_to - 1), wave, lane, win);
     __builtin_amdgcn_s_waitcnt(0);
     int cc = run.c_from;
     for (; cc + 2 <= run.c_to; cc += 2) {
-        chain_step(p, ws, buf0, buf1, stage, S, eye, run, cc, h, g, wave, lane);
-        chain_step(p, ws, buf1, buf0, stage, S, eye, run, cc + 1, h, g, wave, lane);
+        chain_step(p, ws, buf0, buf1, vt0, vt1, win, S, cw, run, cc, h, g, wave, lane);
+        chain_step(p, ws, buf1, buf0, vt1, vt0, win, S, cw, run, cc + 1, h, g, wave, lane);
     }
-    if (cc < run.c_to) chain_step(p, ws, buf0, buf1, stage, S, eye, run, cc, h, g, wave, lane);
+    if (cc < run.c_to) chain_step(p, ws, buf0, buf1, vt0, vt1, win, S, cw, run, cc, h, g, wave, lane);
     // the last step's DMA into the other buffer is still in flight
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -1061,11 +1132,10 @@ void chain_kernel(PrefillArgs p, Workspace ws)
 {
     __shared__ __attribute__((aligned(16))) uint8_t buf0[ChainBuf::kBytes];
     __shared__ __attribute__((aligned(16))) uint8_t buf1[ChainBuf::kBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t stage_all[4 * kChainStage];
+    __shared__ __attribute__((aligned(16))) _Float16 vt0[kVTHalfs];
+    __shared__ __attribute__((aligned(16))) _Float16 vt1[kVTHalfs];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const half8 eye[2] = {eye_frag(0, lane), eye_frag(1, lane)};
-    uint8_t *stage = stage_all + wave * kChainStage;
     const int Hqk = p.Hqk, Hv = p.Hv, G = Hv / Hqk;
     // block -> (segment or rank, group, head in group); the G heads of one
     // (segment, QK group) land on the same XCD (same L2)
@@ -1075,6 +1145,8 @@ void chain_kernel(PrefillArgs p, Workspace ws)
     if (gu >= (kRepair ? p.N : p.max_segs) * Hqk) return;
     const int unit = gu / Hqk, g = gu % Hqk;
     const int h = g * G + j;
+    const long C_tot = 2L * Hqk * kD + (long)Hv * kD, cv = 2L * Hqk * kD + (long)h * kD;
+    const ConvW cw = conv_weights(p.conv_w + cv * 4, lane, kNegLog2e);
     f32x4 S[8][2];
 
     if (!kRepair) {
@@ -1089,7 +1161,10 @@ void chain_kernel(PrefillArgs p, Workspace ws)
         if (w < 0) return;  // recomputed in order by the repair pass
         const long sbase = ((long)s * Hv + h) * kD * kD;
         state_load(S, w == si.x && p.state_in ? p.state_in + sbase : nullptr, wave, lane);
-        chain_run(p, ws, buf0, buf1, stage, S, eye, ChainRun{si.x, si.z, si.w, w, sg.z, sg.y}, h, g, wave, lane);
+        const uint16_t *hist = p.conv_state_in ? p.conv_state_in + (long)s * 3 * C_tot + cv : nullptr;
+        const uint16_t *vs = p.v + (long)si.z * Hv * kD + (long)h * kD;
+        chain_run(p, ws, buf0, buf1, vt0, vt1, S, cw, ChainRun{si.x, si.z, si.w, w, sg.z, sg.y, vs, hist}, h, g, wave,
+                  lane);
         // Final states.  Every segment but the last parks its final state for
         // the repair pass, which runs after this one and hands it to the next
         // segment if that one is recomputed.  The last segment writes
@@ -1102,7 +1177,6 @@ void chain_kernel(PrefillArgs p, Workspace ws)
         // channels of head h; the first head of the group also writes the q
         // and k channels)
         if (first && p.conv_state_out && wave == 0) {
-            const long C_tot = 2L * Hqk * kD + (long)Hv * kD;
             const int Ls = si.w, t0 = si.z;
             for (int plane = (j == 0 ? 0 : 2); plane < 3; ++plane) {
                 const long ch0 = plane == 0 ? (long)g * kD : plane == 1 ? (long)Hqk * kD + (long)g * kD
@@ -1127,6 +1201,8 @@ void chain_kernel(PrefillArgs p, Workspace ws)
         const int4 si = Tables::seq(p, ws, s);
         const int2 ss = Tables::seq_segs(p, ws, s);  // first segment, segments
         const long sbase = ((long)s * Hv + h) * kD * kD;
+        const uint16_t *hist = p.conv_state_in ? p.conv_state_in + (long)s * 3 * C_tot + cv : nullptr;
+        const uint16_t *vs = p.v + (long)si.z * Hv * kD + (long)h * kD;
         const int nseg = min(ss.y, p.max_segs - ss.x);
         bool carry = false;  // S holds the final state of the previous segment
         for (int i = 1; i < nseg; ++i) {  // a sequence's first segment is never recomputed
@@ -1137,7 +1213,8 @@ void chain_kernel(PrefillArgs p, Workspace ws)
             }
             if (!carry) state_load(S, ws.bstate + ((long)(k - 1) * Hv + h) * kStateFloats, wave, lane);
             const int4 sg = Tables::seg(p, ws, k);
-            chain_run(p, ws, buf0, buf1, stage, S, eye, ChainRun{si.x, si.z, si.w, sg.y, sg.z, sg.y}, h, g, wave, lane);
+            chain_run(p, ws, buf0, buf1, vt0, vt1, S, cw, ChainRun{si.x, si.z, si.w, sg.y, sg.z, sg.y, vs, hist}, h, g,
+                      wave, lane);
             carry = true;
         }
         // the final state of a sequence of several segments, when its last
@@ -1191,9 +1268,8 @@ size_t prefill_workspace_bytes(int max_chunks, int N, int Hqk, int Hv)
     total += align256(C * Hqk * kQFragBytes);
     total += align256(C * Hqk * kKFragBytes);
     total += align256(C * Hqk * kKTokFragBytes);
-    total += align256(C * Hv * kWFragBytes);
-    total += align256(C * Hv * kUBytes);
     total += align256(C * Hv * kPFragBytes);
+    total += align256(C * Hv * kTFragBytes);
     total += align256(C * Hv * kGateFloats * sizeof(float));
     total += align256(M * sizeof(int4));
     total += align256((size_t)N * sizeof(int4));
@@ -1219,9 +1295,8 @@ Workspace carve_workspace(void *base, int max_chunks, int N, int Hqk, int Hv)
     ws.qfrag = take(C * Hqk * kQFragBytes);
     ws.kfrag = take(C * Hqk * kKFragBytes);
     ws.ktok = take(C * Hqk * kKTokFragBytes);
-    ws.wfrag = take(C * Hv * kWFragBytes);
-    ws.ufrag = take(C * Hv * kUBytes);
     ws.pfrag = take(C * Hv * kPFragBytes);
+    ws.tfrag = take(C * Hv * kTFragBytes);
     ws.gates = reinterpret_cast<float *>(take(C * Hv * kGateFloats * sizeof(float)));
     ws.seg_info = reinterpret_cast<int4 *>(take(M * sizeof(int4)));
     ws.seq_seg = reinterpret_cast<int4 *>(take((size_t)N * sizeof(int4)));
