@@ -49,15 +49,19 @@ CHUNK = 64
 # ---------------------------------------------------------------------------
 # gdn_prefill_with_events records an event before the first kernel and after
 # each of these, in launch order
-PREFILL_KERNELS = ("setup_kernel", "prep_qk_kernel", "prep_head_kernel", "chain_kernel", "chain_repair_kernel")
+PREFILL_KERNELS = ("setup_kernel", "prep_kernel", "chain_kernel", "chain_repair_kernel")
 N_EVENTS = len(PREFILL_KERNELS) + 1
 
 
 def prefill_flops(T, Hqk, Hv, n=CHUNK, d=D):
-    """(prep, chain) algorithmic FLOP of one prefill of T tokens (T % 64 == 0)."""
+    """(prep, chain) algorithmic FLOP of one prefill of T tokens (T % 64 == 0).
+
+    prep: K K^T and K Q^T per QK head (2 x 2 n^2 d), the triangular inverse
+    per V head (n^3 / 3); chain, per V head: K S, Q S and the state update
+    (3 x 2 n d^2), T' times the bracket and P Vnew (2 x 2 n^2 d)."""
     chunks = T // n
-    prep = chunks * (Hqk * 4 * n * n * d + Hv * (n ** 3 / 3 + 4 * n * n * d))
-    chain = chunks * Hv * (6 * n * d * d + 2 * n * n * d)
+    prep = chunks * (Hqk * 4 * n * n * d + Hv * n ** 3 / 3)
+    chain = chunks * Hv * (6 * n * d * d + 4 * n * n * d)
     return prep, chain
 
 
@@ -114,7 +118,7 @@ def source_digest():
 
 COPY_BYTES = 256 << 20
 TRAFFIC_KERNELS = {"prefill_chain": "chain_kernel<false>", "prefill_chain_repair": "chain_kernel<true>",
-                   "prefill_prep_head": "prep_head_kernel", "prefill_prep_qk": "prep_qk_kernel",
+                   "prefill_prep": "prep_kernel",
                    "prefill_setup": "setup_kernel", "decode": "decode_head_kernel",
                    "decode_conv_shift": "conv_shift_qk_kernel"}
 
@@ -401,13 +405,13 @@ def main():
     # dominant prefill kernel (the longer of the two that carry the matrix
     # products), priced against the fp16 dense matrix-core peak
     km = pf["stage_ms"]
-    dom = "chain_kernel" if km["chain_kernel"] >= km["prep_head_kernel"] else "prep_head_kernel"
+    dom = "chain_kernel" if km["chain_kernel"] >= km["prep_kernel"] else "prep_kernel"
     dom_flop = flop_chain if dom == "chain_kernel" else flop_prep
     dom_ms = km[dom]
     achieved = dom_flop / (dom_ms * 1e-3) / 1e12
     roof = {"bound": "mfma", "kernel": dom, "achieved": achieved,
             "peak": PEAK_MFMA_F16 / 1e12, "unit": "TFLOP/s", "frac": achieved * 1e12 / PEAK_MFMA_F16,
-            "traffic": load_traffic("prefill_chain" if dom == "chain_kernel" else "prefill_prep_head", digest),
+            "traffic": load_traffic("prefill_chain" if dom == "chain_kernel" else "prefill_prep", digest),
             "algorithmic_flop_per_launch": dom_flop, "avg_launch_ms": dom_ms}
     path_flop = flop_prep + flop_chain
     dec_bytes = decode_bytes(dc["B"], dc["Hqk"], dc["Hv"])
@@ -433,9 +437,9 @@ def main():
                  "compulsory_bytes": prefill_bytes(T, Hqk, Hv),
                  "hbm_frac": prefill_bytes(T, Hqk, Hv) / (pf["ms_per_step"] * 1e-3) / PEAK_HBM,
                  "kernel_ms": pf["stage_ms"],
-                 "other_kernel": {"kernel": "prep_head_kernel" if dom == "chain_kernel" else "chain_kernel",
+                 "other_kernel": {"kernel": "prep_kernel" if dom == "chain_kernel" else "chain_kernel",
                                   "tflops": (flop_prep if dom == "chain_kernel" else flop_chain) /
-                                  (km["prep_head_kernel" if dom == "chain_kernel" else "chain_kernel"] * 1e-3) / 1e12}},
+                                  (km["prep_kernel" if dom == "chain_kernel" else "chain_kernel"] * 1e-3) / 1e12}},
         "decode": {"metric": "decode us/step (B=256, 16QK/48V, 64 in-place steps)",
                    "value": dc["us_per_step"], "unit": "us/step", "higher_is_better": False,
                    "kernel_us": dc["kernel_us"],

@@ -36,20 +36,21 @@ inline int max_chunks_varlen(int N, int T_tot)
 }
 
 // Per-chunk hand-over from the parallel prep pass to the sequential pass, in
-// bytes.  Everything the sequential pass reads is stored in the exact
-// register order of the matrix-core operands that consume it.
+// bytes.  The fp16 operands are stored in the register order of the
+// matrix-core instruction that consumes them, k^ as plain rows.
 constexpr size_t kFragBytes = 64 * 16;               // one 16x32 fp16 operand
 constexpr size_t kQFragBytes = 16 * kFragBytes;      // q^ of a chunk     [64 x 128]
-constexpr size_t kKFragBytes = 16 * kFragBytes;      // k^T of a chunk    [128 x 64]
-constexpr size_t kKTokFragBytes = 16 * kFragBytes;   // k^ of a chunk     [64 x 128]
-// The two lower-triangular 64 x 64 matrices keep the six 16x32 fragments that
-// are not structurally zero: (row tile, key block) (0,0) (1,0) (2,0) (2,1)
-// (3,0) (3,1), in that order.
+constexpr size_t kKRowBytes = 64 * 128 * 2;         // k^ of a chunk     [64 x 128], row-major
+// Per (chunk, V head) record: P, T', gates.  The two lower-triangular 64 x 64
+// matrices keep the six 16x32 fragments that are not structurally zero: (row
+// tile, key block) (0,0) (1,0) (2,0) (2,1) (3,0) (3,1), in that order.  Gate
+// floats: [0,64) q_scale Gamma, [64,128) Gamma_n / Gamma, 128 Gamma_n,
+// 129 log2 Gamma_n, [192,256) Gamma.
 constexpr size_t kPFragBytes = 6 * kFragBytes;       // P of a chunk      [64 x 64]
 constexpr size_t kTFragBytes = 6 * kFragBytes;       // T' of a chunk     [64 x 64]
-// Per (chunk, V head) floats: [0,64) q_scale Gamma, [64,128) Gamma_n / Gamma,
-// 128 Gamma_n, 129 log2 Gamma_n, [192,256) Gamma (1 KiB)
 constexpr size_t kGateFloats = 256;
+constexpr size_t kRecP = 0, kRecT = kPFragBytes, kRecG = kPFragBytes + kTFragBytes;
+constexpr size_t kRecBytes = kRecG + kGateFloats * 4;  // 13 KiB
 constexpr size_t kStateFloats = 128 * 128;          // one fp32 state
 
 struct Workspace {
@@ -57,11 +58,8 @@ struct Workspace {
     int4 *seq_info;     // [N] {chunk0, nchunks, t0, L}
     int *order;         // [N] sequences, longest first
     uint8_t *qfrag;     // [max_chunks][Hqk]
-    uint8_t *kfrag;     // [max_chunks][Hqk]  k^T, d-major (sequential pass)
-    uint8_t *ktok;      // [max_chunks][Hqk]  k^, token-major (both passes)
-    uint8_t *pfrag;     // [max_chunks][Hv]
-    uint8_t *tfrag;     // [max_chunks][Hv]
-    float *gates;       // [max_chunks][Hv][256]
+    uint8_t *krow;      // [max_chunks][Hqk]  k^, token rows of 128 fp16
+    uint8_t *hrec;      // [max_chunks][Hv] P, T', gates
     int4 *seg_info;     // [max_segs] {seq, first chunk, end chunk, 1: first of seq | 2: last of seq}; seq -1 = unused
     int4 *seq_seg;      // [N] {first segment, segments, -, -}
     int *seg_bad;       // [max_segs][Hv] warm-up bound not met: the segment is recomputed in order
@@ -77,8 +75,8 @@ inline int max_segments(int max_chunks, int N, int seg_chunks) { return max_chun
 size_t prefill_workspace_bytes(int max_chunks, int N, int Hqk, int Hv);
 Workspace carve_workspace(void *base, int max_chunks, int N, int Hqk, int Hv);
 // events: NULL, or kPrefillEvents events recorded before the first kernel and
-// after each of the five (setup, prep_qk, prep_head, chain, chain repair).
-constexpr int kPrefillEvents = 6;
+// after each of the four (setup, prep, chain, chain repair).
+constexpr int kPrefillEvents = 5;
 hipError_t launch_prefill(const PrefillArgs &p, void *workspace, hipStream_t stream,
                           hipEvent_t const *events = nullptr);
 

@@ -21,10 +21,10 @@
 //   setup     -- chunk, sequence and segment tables from cu_seqlens
 //                (device-side, no host sync); uniform batches compute the
 //                same entries arithmetically and skip it;
-//   prep_qk   -- per (chunk, QK group): conv + SiLU + L2 norm of q and k,
-//                written as matrix-core operands;
-//   prep_head -- per (chunk, V head): gates, K K^T and K Q^T on the matrix
-//                cores, A, P, the blocked unit-lower-triangular inverse, T';
+//   prep      -- per (chunk, QK group): conv + SiLU + L2 norm of q and k,
+//                written as matrix-core operands; K K^T and K Q^T on the
+//                matrix cores; per V head of the group: gates, A, P, the
+//                blocked unit-lower-triangular inverse, T';
 //   chain     -- the sequential pass over (segment, V head): conv + SiLU of v
 //                and every product that involves the state; each wave
 //                carries 32 columns of S in registers;
@@ -37,7 +37,6 @@ namespace {
 
 constexpr int kPrepThreads = 256;
 constexpr int kQ_LD = 136;  // fp16 row stride of the token-major q^ / k^ tiles
-constexpr int kT_LD = 72;   // fp16 row stride of 64-token rows (k^T, v^T, T')
 
 __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -93,16 +92,16 @@ __device__ __forceinline__ void conv_window(const uint16_t *__restrict__ x, long
     }
 }
 
-// Conv taps of channels (2*pp, 2*pp+1), tap 3 = current token, times `scale`
+// Conv taps of channels (2*pp, 2*pp+1), tap 3 = current token
 struct ConvW {
     float a[4], b[4];
 };
-__device__ __forceinline__ ConvW conv_weights(const uint16_t *__restrict__ w, int pp, float scale = 1.0f)
+__device__ __forceinline__ ConvW conv_weights(const uint16_t *__restrict__ w, int pp)
 {
     const uint2 wa = *reinterpret_cast<const uint2 *>(w + (2 * pp) * 4);
     const uint2 wb = *reinterpret_cast<const uint2 *>(w + (2 * pp + 1) * 4);
-    return ConvW{{scale * bf16_lo(wa.x), scale * bf16_hi(wa.x), scale * bf16_lo(wa.y), scale * bf16_hi(wa.y)},
-                 {scale * bf16_lo(wb.x), scale * bf16_hi(wb.x), scale * bf16_lo(wb.y), scale * bf16_hi(wb.y)}};
+    return ConvW{{bf16_lo(wa.x), bf16_hi(wa.x), bf16_lo(wa.y), bf16_hi(wa.y)},
+                 {bf16_lo(wb.x), bf16_hi(wb.x), bf16_lo(wb.y), bf16_hi(wb.y)}};
 }
 
 // Conv + SiLU over a loaded window; rows >= n give 0.
@@ -322,71 +321,6 @@ __device__ __forceinline__ float reduce_scatter16(const float (&v)[16], int lane
     return x;
 }
 
-// prepA: per (chunk, QK group) -- conv + SiLU + L2 norm of q and k, written
-// as matrix-core operands: q^ and k^ token-major, k^T d-major.
-__global__ __launch_bounds__(kPrepThreads) void prep_qk_kernel(PrefillArgs p, Workspace ws)
-{
-    __shared__ __attribute__((aligned(16))) _Float16 Qs[64 * kQ_LD];
-    __shared__ __attribute__((aligned(16))) _Float16 Ks[64 * kQ_LD];
-    __shared__ __attribute__((aligned(16))) _Float16 KTs[128 * kT_LD];
-    const int t = threadIdx.x, lane = t & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int c = blockIdx.x / p.Hqk, g = blockIdx.x % p.Hqk;
-    const int4 ci = Tables::chunk(p, ws, c);
-    const int n = ci.z;
-    if (n == 0) return;  // empty chunk slot (whole workgroup)
-    const int s = ci.x, t0 = ci.y;
-    const bool first = ci.w != 0;
-    const int Hqk = p.Hqk;
-    const long C_tot = 2L * Hqk * kD + (long)p.Hv * kD;
-    const uint16_t *hist = (first && p.conv_state_in) ? p.conv_state_in + (long)s * 3 * C_tot : nullptr;
-    const int r0 = 16 * wave;
-    {
-        float z0[16], z1[16];
-        const long ldqk = (long)Hqk * kD;
-#pragma unroll
-        for (int plane = 0; plane < 2; ++plane) {
-            const long ch0 = plane == 0 ? (long)g * kD : (long)Hqk * kD + (long)g * kD;
-            const uint16_t *x = (plane == 0 ? p.q : p.k) + (long)t0 * ldqk + (long)g * kD;
-            conv_plane(x, ldqk, n, first, hist ? hist + ch0 : nullptr, C_tot, p.conv_w + ch0 * 4, lane, r0,
-                       z0, z1);
-            float ss[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) ss[i] = z0[i] * z0[i] + z1[i] * z1[i];
-            const float inv_mine = rsqrtf(reduce_scatter16(ss, lane) + 1e-6f);  // row (lane >> 2)
-            _Float16 *dst = plane == 0 ? Qs : Ks;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float inv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inv_mine), 4 * i));
-                const _Float16 h0 = (_Float16)(z0[i] * inv), h1 = (_Float16)(z1[i] * inv);
-                dst[(r0 + i) * kQ_LD + 2 * lane] = h0;
-                dst[(r0 + i) * kQ_LD + 2 * lane + 1] = h1;
-                if (plane == 1) {
-                    KTs[(2 * lane) * kT_LD + r0 + i] = h0;
-                    KTs[(2 * lane + 1) * kT_LD + r0 + i] = h1;
-                }
-            }
-        }
-    }
-    __syncthreads();
-    const long gc = (long)c * Hqk + g;
-    half8 *qf = reinterpret_cast<half8 *>(ws.qfrag + gc * kQFragBytes);
-    half8 *kt = reinterpret_cast<half8 *>(ws.ktok + gc * kKTokFragBytes);
-    half8 *kf = reinterpret_cast<half8 *>(ws.kfrag + gc * kKFragBytes);
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        qf[(wave * 4 + kb) * 64 + lane] = lds_frag(Qs, kQ_LD, 16 * wave, 32 * kb, lane);
-        kt[(wave * 4 + kb) * 64 + lane] = lds_frag(Ks, kQ_LD, 16 * wave, 32 * kb, lane);
-    }
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const int rt = 2 * wave + rr;
-            kf[(rt * 2 + kb) * 64 + lane] = lds_frag(KTs, kT_LD, 16 * rt, 32 * kb, lane);
-        }
-}
-
 // Column c of the inverse of a 16 x 16 unit lower-triangular block I + A (A
 // strictly lower, row stride kAL), by right-looking substitution: once y_m is
 // final it is removed from every later row, y_i -= A[i][m] y_m, so the chain
@@ -426,194 +360,250 @@ __device__ __forceinline__ void st16_f32(float *Db, int ldd, f32x4 v, int lane)
 // 64 x 64 operand in its compact order
 __host__ __device__ constexpr int tri_frag(int rt, int kb) { return rt < 2 ? rt : 2 * rt - 2 + kb; }
 
-// prepB: per (chunk, V head) -- gates, K K^T and K Q^T, A, P, the
-// unit-lower-triangular inverse and T'.
-__global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, Workspace ws)
+// Gates of one (chunk, V head), by one wave (lane = token): gam = in-chunk
+// cumulative log decay (log2 units) and beta into LDS; the sequential pass's
+// per-chunk floats into the workspace
+__device__ __forceinline__ void prep_gates(const PrefillArgs &p, float av, float bv, int n, float *gt,
+                                           float *s_gam2, float *s_beta, int lane)
 {
-    // LDS plan: [F] k^ operands (16 KiB) -> X = (I+A)^-1 (fp32); [A] A (fp32); scratch
-    __shared__ __attribute__((aligned(16))) uint8_t regF[64 * kAL * 4];
-    __shared__ __attribute__((aligned(16))) uint8_t regA[64 * kAL * 4];
-    __shared__ __attribute__((aligned(16))) float Msc[3][256];
-    __shared__ float s_gam2[64];
-    __shared__ __attribute__((aligned(16))) float s_beta[64];
-    const half8 *Fk = reinterpret_cast<const half8 *>(regF);  // k^ token-major: [rt*4+kb][lane]
-    float *Xs = reinterpret_cast<float *>(regF);
-    float *As = reinterpret_cast<float *>(regA);
+    const bool valid = lane < n;
+    const float gl = valid ? -p.gate_scale * kLog2e * softplus_f(av) : 0.f;
+    const float be = valid ? sigmoid_f(bv) : 0.f;
+    float gam = gl;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(gam, off, 64);
+        if (lane >= off) gam += y;
+    }
+    const float gam_n = __shfl(gam, n - 1, 64);
+    const float Gam = __builtin_amdgcn_exp2f(gam);
+    s_gam2[lane] = gam;
+    s_beta[lane] = be;
+    gt[lane] = p.q_scale * Gam;
+    gt[64 + lane] = valid ? __builtin_amdgcn_exp2f(gam_n - gam) : 0.f;
+    gt[192 + lane] = Gam;
+    if (lane == 0) {
+        gt[128] = __builtin_amdgcn_exp2f(gam_n);
+        gt[129] = gam_n;
+    }
+}
+
+// prep: per (chunk, QK group), everything that does not depend on the carried
+// state.  q and k: conv + SiLU + L2 norm, written as matrix-core operands (q^
+// and k^ token-major, k^T d-major); K K^T and K Q^T once, on the matrix cores;
+// then for each V head of the group: gates, A, P, the unit-lower-triangular
+// inverse and T'.
+constexpr int kPrepTile = 64 * kAL * 4;  // one fp32 64 x 64 tile (row stride kAL)
+static_assert(64 * kQ_LD * 2 <= kPrepTile, "a token-major q^ / k^ tile fits in an fp32 tile");
+
+
+__global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillArgs p, Workspace ws)
+{
+    // LDS plan: [R0] q^ (fp16) -> A (fp32); [R1] k^ (fp16) -> X = (I+A)^-1
+    // (fp32); scratch of the inverse; the gates of four heads
+    __shared__ __attribute__((aligned(16))) uint8_t R0[kPrepTile];
+    __shared__ __attribute__((aligned(16))) uint8_t R1[kPrepTile];
+    __shared__ __attribute__((aligned(16))) float Msc[3 * 256];
+    __shared__ float s_gam2[4 * 64];
+    __shared__ __attribute__((aligned(16))) float s_beta[4 * 64];
+    _Float16 *Qs = reinterpret_cast<_Float16 *>(R0), *Ks = reinterpret_cast<_Float16 *>(R1);
+    float *As = reinterpret_cast<float *>(R0), *Xs = reinterpret_cast<float *>(R1);
 
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int q4 = lane >> 4, c16 = lane & 15;
     const int Hqk = p.Hqk, Hv = p.Hv, G = Hv / Hqk;
-    // block -> (chunk, group, head in group); the G heads of one (chunk, group)
-    // share an XCD, so the q^ / k^ operands they all read come from one L2
-    const int bid = blockIdx.x;
-    const int u = (bid / (8 * G)) * 8 + (bid & 7);
-    const int j = (bid >> 3) % G;
-    if (u >= p.max_chunks * Hqk) return;
-    const int c = u / Hqk, g = u % Hqk;
-    const int h = g * G + j;
+    const int c = blockIdx.x / Hqk, g = blockIdx.x % Hqk;
     const int4 ci = Tables::chunk(p, ws, c);
     const int n = ci.z;
-    if (n == 0) return;
-    const int t0 = ci.y;
-    const long hc = (long)c * Hv + h, gc = (long)c * Hqk + g;
+    if (n == 0) return;  // empty chunk slot (whole workgroup)
+    const int s = ci.x, t0 = ci.y;
+    const bool first = ci.w != 0;
+    const long C_tot = 2L * Hqk * kD + (long)Hv * kD;
+    const uint16_t *hist = (first && p.conv_state_in) ? p.conv_state_in + (long)s * 3 * C_tot : nullptr;
+    const int r0 = 16 * wave;
+    const long gc = (long)c * Hqk + g;
 
-    // ---- every global read of the workgroup is issued first
-    {
-        const __amdgpu_buffer_rsrc_t rk = region_rsrc(ws.ktok + gc * kKTokFragBytes);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int blk = i * 4 + wave;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t *)(regF + blk * 1024), 16, lane * 16, blk * 1024, 0, 0);
-        }
-    }
-    half8 qB[4];
-    {
-        const half8 *qf = reinterpret_cast<const half8 *>(ws.qfrag + gc * kQFragBytes) + lane;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) qB[kb] = qf[(wave * 4 + kb) * 64];
-    }
+    // gate inputs of the group's first four V heads (wave w: head w, lane = token)
     float av = 0.f, bv = 0.f;
-    if (wave == 0 && lane < n) {
-        const long ti = (long)(t0 + lane) * Hv + h;
+    if (wave < G && lane < n) {
+        const long ti = (long)(t0 + lane) * Hv + g * G + wave;
         av = p.a[ti];
         bv = p.b[ti];
     }
-
-    // ---- gates (wave 0): gam = in-chunk cumulative log decay (log2 units), beta
-    if (wave == 0) {
-        const bool valid = lane < n;
-        const float gl = valid ? -p.gate_scale * kLog2e * softplus_f(av) : 0.f;
-        const float be = valid ? sigmoid_f(bv) : 0.f;
-        float gam = gl;
+    // ---- q^, k^ of the chunk: conv + SiLU, L2 norm per token
+    {
+        float z0[16], z1[16];
+        const long ldqk = (long)Hqk * kD;
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(gam, off, 64);
-            if (lane >= off) gam += y;
-        }
-        const float gam_n = __shfl(gam, n - 1, 64);
-        const float Gam = __builtin_amdgcn_exp2f(gam);
-        s_gam2[lane] = gam;
-        s_beta[lane] = be;
-        float *gt = ws.gates + hc * kGateFloats;
-        gt[lane] = p.q_scale * Gam;
-        gt[64 + lane] = valid ? __builtin_amdgcn_exp2f(gam_n - gam) : 0.f;
-        gt[192 + lane] = Gam;
-        if (lane == 0) {
-            gt[128] = __builtin_amdgcn_exp2f(gam_n);
-            gt[129] = gam_n;
+        for (int plane = 0; plane < 2; ++plane) {
+            const long ch0 = plane == 0 ? (long)g * kD : (long)Hqk * kD + (long)g * kD;
+            const uint16_t *x = (plane == 0 ? p.q : p.k) + (long)t0 * ldqk + (long)g * kD;
+            conv_plane(x, ldqk, n, first, hist ? hist + ch0 : nullptr, C_tot, p.conv_w + ch0 * 4, lane, r0,
+                       z0, z1);
+            float ss[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ss[i] = z0[i] * z0[i] + z1[i] * z1[i];
+            const float inv_mine = rsqrtf(reduce_scatter16(ss, lane) + 1e-6f);  // row (lane >> 2)
+            _Float16 *dst = plane == 0 ? Qs : Ks;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float inv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inv_mine), 4 * i));
+                const _Float16 h0 = (_Float16)(z0[i] * inv), h1 = (_Float16)(z1[i] * inv);
+                dst[(r0 + i) * kQ_LD + 2 * lane] = h0;
+                dst[(r0 + i) * kQ_LD + 2 * lane + 1] = h1;
+            }
         }
     }
-    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // ---- K K^T (rows 16*wave.., column tiles ct <= wave) and K Q^T (query
-    //      tile `wave`, key tiles jt <= wave)
+    // ---- operands of the sequential pass, and K K^T (rows 16*wave.., column
+    //      tiles ct <= wave) and K Q^T (query tile `wave`, key tiles jt <= wave)
     f32x4 kk[4], kq[4];
     {
-        half8 kOwn[4];
+        half8 *qf = reinterpret_cast<half8 *>(ws.qfrag + gc * kQFragBytes);
+        half8 qOwn[4], kOwn[4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) kOwn[kb] = Fk[(wave * 4 + kb) * 64 + lane];
+        for (int kb = 0; kb < 4; ++kb) {
+            qOwn[kb] = lds_frag(Qs, kQ_LD, 16 * wave, 32 * kb, lane);
+            kOwn[kb] = lds_frag(Ks, kQ_LD, 16 * wave, 32 * kb, lane);
+            qf[(wave * 4 + kb) * 64 + lane] = qOwn[kb];
+        }
+        // k^ rows: 64 rows of 256 bytes, 16 bytes per thread and pass
+        uint8_t *kr = ws.krow + gc * kKRowBytes;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int piece = t + kPrepThreads * i, row = piece >> 4, col = piece & 15;
+            *reinterpret_cast<i32x4 *>(kr + row * 256 + col * 16) =
+                *reinterpret_cast<const i32x4 *>(Ks + row * kQ_LD + col * 8);
+        }
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acq = {0.f, 0.f, 0.f, 0.f};
             if (ct <= wave) {
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
-                    const half8 kc = Fk[(ct * 4 + kb) * 64 + lane];
+                    const half8 kc = lds_frag(Ks, kQ_LD, 16 * ct, 32 * kb, lane);
                     acc = mfma16(kOwn[kb], kc, acc);
-                    acq = mfma16(kc, qB[kb], acq);
+                    acq = mfma16(kc, qOwn[kb], acq);
                 }
             }
             kk[ct] = acc;
             kq[ct] = acq;
         }
     }
-    // ---- A = strict_lower(diag(beta) K K^T * D) -> LDS; P = (K Q^T)^T * D (lower) -> global
-    {
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            if (ct > wave) continue;
-            const int jj = 16 * ct + c16;
-            const float gj = s_gam2[jj];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * wave + 4 * q4 + e;
-                if (i > jj) As[i * kAL + jj] = s_beta[i] * kk[ct][e] * __builtin_amdgcn_exp2f(s_gam2[i] - gj);
+    __syncthreads();  // the q^ / k^ / k^T tiles are dead from here on
+
+    for (int j0 = 0; j0 < G; j0 += 4) {
+        // gates of heads j0 .. j0+3 of the group (wave w: head j0 + w)
+        if (j0 + wave < G) {
+            if (j0 > 0) {
+                av = bv = 0.f;
+                if (lane < n) {
+                    const long ti = (long)(t0 + lane) * Hv + g * G + j0 + wave;
+                    av = p.a[ti];
+                    bv = p.b[ti];
+                }
             }
-        }
-        half8 *pf = reinterpret_cast<half8 *>(ws.pfrag + hc * kPFragBytes);
-        const int i = 16 * wave + c16;
-        const float gi = s_gam2[i];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            if (kb > wave / 2) continue;  // query tiles 0, 1 see only key block 0
-            half8 fr;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int jt = 2 * kb + (e >> 2);
-                const int jj = 16 * jt + 4 * q4 + (e & 3);
-                float val = 0.f;
-                if (jt <= wave && i >= jj)
-                    val = p.q_scale * kq[jt][e & 3] * __builtin_amdgcn_exp2f(gi - s_gam2[jj]);
-                fr[e] = (_Float16)val;
-            }
-            pf[tri_frag(wave, kb) * 64 + lane] = fr;
-        }
-    }
-    __syncthreads();
-    // ---- X = (I + A)^-1, blocked by 16: diagonal blocks by forward
-    //      substitution (wave b, block b), then the blocks below the diagonal
-    //      level by level, X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj, on the fp32
-    //      matrix cores
-    {
-        float y[16];
-        const int bo = 16 * wave;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) y[i] = i == c16 ? 1.f : 0.f;
-        SolveCol16<0>::run(y, As + bo * kAL + bo);
-        if (lane < 16) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) Xs[(bo + i) * kAL + bo + c16] = y[i];
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int lvl = 1; lvl <= 3; ++lvl) {
-        if (wave < 4 - lvl) {
-            const int bi = wave + lvl, bj = wave;
-            f32x4 m = {0.f, 0.f, 0.f, 0.f};
-            for (int bk = bj; bk < bi; ++bk)
-                m = mm16_f32(As + 16 * bi * kAL + 16 * bk, kAL, Xs + 16 * bk * kAL + 16 * bj, kAL, m, lane);
-            st16_f32(Msc[wave], 16, m, lane);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            f32x4 x = {0.f, 0.f, 0.f, 0.f};
-            x = mm16_f32(Xs + 16 * bi * kAL + 16 * bi, kAL, Msc[wave], 16, x, lane);
-            st16_f32(Xs + 16 * bi * kAL + 16 * bj, kAL, -x, lane);
+            const long hc = (long)c * Hv + g * G + j0 + wave;
+            prep_gates(p, av, bv, n, reinterpret_cast<float *>(ws.hrec + hc * kRecBytes + kRecG), s_gam2 + 64 * wave,
+                       s_beta + 64 * wave, lane);
         }
         __syncthreads();
-    }
-    // ---- T' = X diag(beta), lower triangle, as A operands (rows = tokens i,
-    //      contraction = tokens j): wave w writes fragments w and w + 4
-    {
-        half8 *tf = reinterpret_cast<half8 *>(ws.tfrag + hc * kTFragBytes);
+        const int jn = min(4, G - j0);
+        for (int jj = 0; jj < jn; ++jj) {
+            const long hc = (long)c * Hv + g * G + j0 + jj;
+            const float *gam2 = s_gam2 + 64 * jj, *beta = s_beta + 64 * jj;
+            // ---- A = strict_lower(diag(beta) K K^T * D) -> LDS; P = (K Q^T)^T * D (lower) -> global
+            {
 #pragma unroll
-        for (int f2 = 0; f2 < 2; ++f2) {
-            const int f = wave + 4 * f2;
-            if (f >= 6) continue;
-            const int rt = f < 2 ? f : (f + 2) >> 1, kb = f < 2 ? 0 : f & 1;
-            const int i = 16 * rt + c16;
-            half8 fr;
+                for (int ct = 0; ct < 4; ++ct) {
+                    if (ct > wave) continue;
+                    const int jc = 16 * ct + c16;
+                    const float gj = gam2[jc];
 #pragma unroll
-            for (int hb = 0; hb < 2; ++hb) {
-                const int j0 = 32 * kb + 16 * hb + 4 * q4;
-                const f32x4 xv = *reinterpret_cast<const f32x4 *>(Xs + i * kAL + j0);
-                const f32x4 bb = *reinterpret_cast<const f32x4 *>(s_beta + j0);
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 16 * wave + 4 * q4 + e;
+                        if (i > jc) As[i * kAL + jc] = beta[i] * kk[ct][e] * __builtin_amdgcn_exp2f(gam2[i] - gj);
+                    }
+                }
+                half8 *pf = reinterpret_cast<half8 *>(ws.hrec + hc * kRecBytes + kRecP);
+                const int i = 16 * wave + c16;
+                const float gi = gam2[i];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) fr[4 * hb + e] = (_Float16)(j0 + e <= i ? xv[e] * bb[e] : 0.f);
+                for (int kb = 0; kb < 2; ++kb) {
+                    if (kb > wave / 2) continue;  // query tiles 0, 1 see only key block 0
+                    half8 fr;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int jt = 2 * kb + (e >> 2);
+                        const int jc = 16 * jt + 4 * q4 + (e & 3);
+                        float val = 0.f;
+                        if (jt <= wave && i >= jc)
+                            val = p.q_scale * kq[jt][e & 3] * __builtin_amdgcn_exp2f(gi - gam2[jc]);
+                        fr[e] = (_Float16)val;
+                    }
+                    pf[tri_frag(wave, kb) * 64 + lane] = fr;
+                }
             }
-            tf[f * 64 + lane] = fr;
+            __syncthreads();
+            // ---- X = (I + A)^-1, blocked by 16: diagonal blocks by forward
+            //      substitution (wave b, block b), then the blocks below the
+            //      diagonal level by level, X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj,
+            //      on the fp32 matrix cores
+            {
+                float y[16];
+                const int bo = 16 * wave;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) y[i] = i == c16 ? 1.f : 0.f;
+                SolveCol16<0>::run(y, As + bo * kAL + bo);
+                if (lane < 16) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) Xs[(bo + i) * kAL + bo + c16] = y[i];
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int lvl = 1; lvl <= 3; ++lvl) {
+                if (wave < 4 - lvl) {
+                    const int bi = wave + lvl, bj = wave;
+                    f32x4 m = {0.f, 0.f, 0.f, 0.f};
+                    for (int bk = bj; bk < bi; ++bk)
+                        m = mm16_f32(As + 16 * bi * kAL + 16 * bk, kAL, Xs + 16 * bk * kAL + 16 * bj, kAL, m, lane);
+                    st16_f32(Msc + 256 * wave, 16, m, lane);
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+                    x = mm16_f32(Xs + 16 * bi * kAL + 16 * bi, kAL, Msc + 256 * wave, 16, x, lane);
+                    st16_f32(Xs + 16 * bi * kAL + 16 * bj, kAL, -x, lane);
+                }
+                __syncthreads();
+            }
+            // ---- T' = X diag(beta), lower triangle, as A operands (rows =
+            //      tokens i, contraction = tokens j): wave w writes fragments
+            //      w and w + 4.  Entries above the diagonal blocks of X were
+            //      never written and are selected away.
+            {
+                half8 *tf = reinterpret_cast<half8 *>(ws.hrec + hc * kRecBytes + kRecT);
+#pragma unroll
+                for (int f2 = 0; f2 < 2; ++f2) {
+                    const int f = wave + 4 * f2;
+                    if (f >= 6) continue;
+                    const int rt = f < 2 ? f : (f + 2) >> 1, kb = f < 2 ? 0 : f & 1;
+                    const int i = 16 * rt + c16;
+                    half8 fr;
+#pragma unroll
+                    for (int hb = 0; hb < 2; ++hb) {
+                        const int j0c = 32 * kb + 16 * hb + 4 * q4;
+                        const f32x4 xv = *reinterpret_cast<const f32x4 *>(Xs + i * kAL + j0c);
+                        const f32x4 bb = *reinterpret_cast<const f32x4 *>(beta + j0c);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) fr[4 * hb + e] = (_Float16)(j0c + e <= i ? xv[e] * bb[e] : 0.f);
+                    }
+                    tf[f * 64 + lane] = fr;
+                }
+            }
+            __syncthreads();  // A and X are rebuilt for the next head
         }
     }
 }
@@ -623,73 +613,67 @@ __global__ __launch_bounds__(kPrepThreads) void prep_head_kernel(PrefillArgs p, 
 // ---------------------------------------------------------------------------
 // Workgroup = one (segment, V head), 4 waves; wave w owns the state columns
 // 32w .. 32w+31 (two 16-column tiles) in every product of a chunk:
+//   v^ = SiLU(conv v)                  64 tokens x 32 channels, over 4 taps
 //   X = K S,  Q S                      64 tokens x 32 columns, over d_k
-//   Vnew = T' (V - diag(Gam) X)        64 tokens x 32 columns, over the chunk
+//   Vnew = T' (v^ - diag(Gam) X)       64 tokens x 32 columns, over the chunk
 //   S <- Gam_n S + k^T (r Vnew)        d_k x 32 columns, over the chunk
 //   O = diag(q_scale Gam) Q S + P Vnew
 // The B operands of these products are the wave's own accumulators: with the
 // kappa k-mapping, a lane's accumulator rows 4q..4q+3 of two vertically
 // adjacent 16-row tiles are exactly its eight B-operand elements of the
 // 32-deep block they form, so the state, X and Vnew never leave the wave.
-// The waves share the chunk's operands (k^, q^, k^T, P, T', gates), which the
-// workgroup stages in LDS with direct-to-LDS loads into two buffers, and v^
-// (conv + SiLU of the chunk's v rows), which each wave computes one chunk
-// ahead for 16 tokens of every channel and leaves transposed in LDS, also in
-// two buffers; one barrier per chunk.  Waiting for a chunk's operands never
+// The width-4 causal conv of v runs on the matrix cores as well, as a product
+// with a block-diagonal tap matrix, which leaves v^ in the accumulator layout
+// of X.  The waves share the chunk's operands (k^, q^, k^T, P, T', gates, raw
+// v rows), which the workgroup stages in LDS with direct-to-LDS loads into
+// two buffers, one barrier per chunk.  Waiting for a chunk's operands never
 // waits for the output stores: they are the only memory operations issued
 // after the operand loads.
 constexpr int kChainBlocksPerHead = 1;
+constexpr int kVTileRows = 68;  // raw v rows of a chunk: 1 unused, 3 before the chunk, 64
 struct ChainBuf {
-    // k^ (token-major), q^, k^T, P, T', gates
-    static constexpr int kK = 0, kQ = 16384, kKT = 32768, kP = 49152, kT = 55296, kG = 61440, kBytes = 62464;
+    // k^ rows, q^ (operand order), the head record (P, T', gates), raw v
+    static constexpr int kK = 0, kQ = 16384, kRec = 32768;
+    static constexpr int kP = kRec + (int)kRecP, kT = kRec + (int)kRecT, kG = kRec + (int)kRecG;
+    static constexpr int kV = kRec + (int)kRecBytes;
+    static constexpr int kBytes = kV + kVTileRows * kD * 2;
 };
-constexpr int kVT_LD = 68;                 // fp16 row stride of v^T (one channel: 64 tokens + pad)
-constexpr int kVTHalfs = kD * kVT_LD;
-// The output of a wave goes out through an LDS staging of 32 tokens x 32
-// columns (bf16) in the wave's own channel rows of the current v^T buffer,
-// which no other wave reads.
-static_assert(32 * kVT_LD * 2 >= 32 * 32 * 2, "output staging fits in a wave's v^T rows");
+constexpr int kChainStageRows = 16;                    // token rows per output staging round
+constexpr int kChainStage = kChainStageRows * 32 * 2;  // output staging of one wave (bf16)
 
-// Chunk c's operands into one LDS buffer: 61 pieces of 1 KiB; wave w moves
-// pieces 4i + w of k^, q^, k^T (i < 4) and of P and T' (4i + w < 6), and wave
-// 0 the gates.  Issued in four groups (i = 0..3), spread through a chunk step
-// so that the memory unit takes them while the matrix cores work.
+// k^ tile: 64 token rows of 256 bytes whose 16-byte pieces are stored
+// permuted by a bit shuffle of the row index, ksw(R) = (r3, r1, r0, r2).  It
+// is a bijection on R mod 16, so the sixteen consecutive rows of a token-major
+// operand hit sixteen bank groups; and for four consecutive rows (r0, r1 free)
+// and two adjacent pieces (bit 0 free) it is one-to-one as well, which is
+// what the transposed reads of the d-major operand touch at once.
+__device__ __forceinline__ int ksw(int R)
+{
+    return (R & 8) | ((R & 2) << 1) | ((R & 1) << 1) | ((R >> 2) & 1);
+}
+__device__ __forceinline__ int ktile_offset(int R, int byte_in_row)
+{
+    return R * (kD * 2) + ((((byte_in_row >> 4) ^ ksw(R)) & 15) << 4) + (byte_in_row & 15);
+}
+
+// Raw v tile: tile row R holds chunk row R - 4 (rows 1..3: the three rows
+// before the chunk); its 16-byte pieces are stored XOR-swizzled by R mod 16,
+// so that the sixteen lanes of a conv operand, which read sixteen consecutive
+// rows at the same channels, hit sixteen different bank groups.
+__device__ __forceinline__ int vtile_offset(int R, int byte_in_row)
+{
+    return R * (kD * 2) + ((((byte_in_row >> 4) ^ R) & 15) << 4) + (byte_in_row & 15);
+}
+
+// Chunk c's operands into one LDS buffer: 62 pieces of 1 KiB; wave w moves
+// pieces 4i + w of k^, q^ and of the raw v tile (i < 4) and of the head
+// record (4i + w < 13), and wave 3 the last piece of the v tile.
+// Issued in four groups (i = 0..3), spread through a chunk step so that the
+// memory unit takes them while the matrix cores work.
 struct ChainDma {
-    __amdgpu_buffer_rsrc_t rk, rq, rkt, rp, rt, rg;
+    __amdgpu_buffer_rsrc_t rk, rq, rh, rv, rvh;
+    int ldb, ldh;  // bytes per row of v and of the rows before the chunk
 };
-
-__device__ __forceinline__ ChainDma chain_dma_plan(const Workspace &ws, long c, int h, int g, int Hqk, int Hv)
-{
-    const long hc = c * Hv + h, gc = c * Hqk + g;
-    return ChainDma{region_rsrc(ws.ktok + gc * kKTokFragBytes), region_rsrc(ws.qfrag + gc * kQFragBytes),
-                    region_rsrc(ws.kfrag + gc * kKFragBytes), region_rsrc(ws.pfrag + hc * kPFragBytes),
-                    region_rsrc(ws.tfrag + hc * kTFragBytes), region_rsrc(ws.gates + hc * kGateFloats)};
-}
-
-template <int I>
-__device__ __forceinline__ void chain_dma_group(const ChainDma &d, uint8_t *buf, int wave, int lane)
-{
-    const int f = 4 * I + wave, v16 = lane * 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rk, (lds_void_t *)(buf + ChainBuf::kK + f * 1024), 16, v16, f * 1024, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rq, (lds_void_t *)(buf + ChainBuf::kQ + f * 1024), 16, v16, f * 1024, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rkt, (lds_void_t *)(buf + ChainBuf::kKT + f * 1024), 16, v16, f * 1024, 0, 0);
-    if (I == 0 || (I == 1 && wave < 2)) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rp, (lds_void_t *)(buf + ChainBuf::kP + f * 1024), 16, v16, f * 1024, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rt, (lds_void_t *)(buf + ChainBuf::kT + f * 1024), 16, v16, f * 1024, 0, 0);
-    }
-    if (I == 2 && wave == 0)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rg, (lds_void_t *)(buf + ChainBuf::kG), 16, v16, 0, 0, 0);
-}
-
-__device__ __forceinline__ void chain_dma(const Workspace &ws, uint8_t *buf, long c, int h, int g, int Hqk,
-                                          int Hv, int wave, int lane)
-{
-    const ChainDma d = chain_dma_plan(ws, c, h, g, Hqk, Hv);
-    chain_dma_group<0>(d, buf, wave, lane);
-    chain_dma_group<1>(d, buf, wave, lane);
-    chain_dma_group<2>(d, buf, wave, lane);
-    chain_dma_group<3>(d, buf, wave, lane);
-}
 
 // Chunk range of one run of the sequential pass: chunks [c_from, c_to) of a
 // sequence whose chunk 0 is c0 (first token t0, L tokens); chunks before c_out
@@ -701,105 +685,130 @@ struct ChainRun {
     const uint16_t *v, *hist;
 };
 
-// Raw v rows of chunk cc for tokens 16w .. 16w+15 and the three before, of
-// channels 2*lane, 2*lane+1 -- without branches: one buffer range covers the
-// rows that come from v (the chunk's n rows, and the three before unless the
-// chunk starts the sequence), and everything outside it reads as zero; the
-// carried conv rows of a sequence's first chunk are a second range.
-__device__ __forceinline__ void chain_vload(const PrefillArgs &p, const ChainRun &run, int cc, int wave, int lane,
-                                            uint32_t (&win)[19])
+__device__ __forceinline__ ChainDma chain_dma_plan(const PrefillArgs &p, const Workspace &ws, const ChainRun &run,
+                                                   long c, int h, int g)
 {
-    const int rel = (cc - run.c0) * kChunk;
+    const int Hqk = p.Hqk, Hv = p.Hv;
+    const long hc = c * Hv + h, gc = c * Hqk + g;
+    // raw v: the chunk's n rows (rows past its end read as zero), and the three
+    // rows before it -- of v, or the carried rows of the sequence (zeros
+    // without them) for its first chunk
+    const int rel = ((int)c - run.c0) * kChunk;
     const int n = min(kChunk, run.L - rel);
-    const bool first = cc == run.c0;
-    const int lo = first ? 0 : -3;  // first row taken from v
-    const int ldb = p.Hv * kD * 2;  // bytes per token row of v
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(run.v + (long)(rel + lo) * (ldb / 2)), 0, (n - lo) * ldb, 0x00020000);
-    // row r0 - 3 + i sits at (r0 - 3 + i - lo) rows into the range; rows
-    // before it give a negative offset, which the range check rejects too
-    const int voff = (16 * wave - 3 - lo) * ldb + 4 * lane;
-#pragma unroll
-    for (int i = 0; i < 19; ++i) win[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff + i * ldb, 0, 0);
-    if (first && wave == 0 && run.hist) {
-        const int ldh = (2 * p.Hqk * kD + p.Hv * kD) * 2;  // bytes per carried row
-        const __amdgpu_buffer_rsrc_t rh =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(run.hist), 0, 3 * ldh, 0x00020000);
-#pragma unroll
-        for (int i = 0; i < 3; ++i) win[i] = __builtin_amdgcn_raw_buffer_load_b32(rh, 4 * lane + i * ldh, 0, 0);
-    }
+    const int ldb = Hv * kD * 2, ldc = (2 * Hqk * kD + Hv * kD) * 2;
+    const bool first = (int)c == run.c0;
+    uint16_t *vc = const_cast<uint16_t *>(run.v) + (long)rel * (ldb / 2);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(vc, 0, n * ldb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rvh =
+        first ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(run.hist), 0, run.hist ? 3 * ldc : 0,
+                                                  0x00020000)
+              : __builtin_amdgcn_make_buffer_rsrc(vc - 3 * (ldb / 2), 0, 3 * ldb, 0x00020000);
+    return ChainDma{region_rsrc(ws.krow + gc * kKRowBytes), region_rsrc(ws.qfrag + gc * kQFragBytes),
+                    region_rsrc(ws.hrec + hc * kRecBytes), rv, rvh, ldb, first ? ldc : ldb};
 }
 
-// v^ = SiLU(conv) of four of those rows (tokens 16w + 4P .. +3) into v^T:
-// channel rows 2*lane, 2*lane+1.  The taps come pre-scaled by -log2(e), so
-// the conv gives u = -y log2(e) and SiLU(y) = y / (1 + 2^u) = u / (-log2(e) (1 + 2^u)).
-// Tokens past the chunk's end are not masked: they come out finite (their raw
-// rows read as zero) and meet only zero columns of T'.
-constexpr float kNegLog2e = -kLog2e;
-__device__ __forceinline__ float silu_scaled(float u)
+// Piece f of the raw v tile (tile rows 4f .. 4f+3): lane L fills 16-byte slot
+// L % 16 of tile row 4f + L / 16, i.e. the row's logical piece (L % 16) ^ R.
+__device__ __forceinline__ void chain_dma_v(const ChainDma &d, uint8_t *buf, int f, int lane)
 {
-    return u * __builtin_amdgcn_rcpf(__builtin_fmaf(__builtin_amdgcn_exp2f(u), kNegLog2e, kNegLog2e));
-}
-template <int P>
-__device__ __forceinline__ void chain_vconv(const ConvW &cw, const uint32_t (&win)[19], _Float16 *vt, int wave,
-                                            int lane)
-{
-    float xa[7], xb[7];
-#pragma unroll
-    for (int m = 0; m < 7; ++m) {
-        xa[m] = bf16_lo(win[4 * P + m]);
-        xb[m] = bf16_hi(win[4 * P + m]);
-    }
-    half4 ha, hb;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const float ya = cw.a[0] * xa[e] + cw.a[1] * xa[e + 1] + cw.a[2] * xa[e + 2] + cw.a[3] * xa[e + 3];
-        const float yb = cw.b[0] * xb[e] + cw.b[1] * xb[e + 1] + cw.b[2] * xb[e + 2] + cw.b[3] * xb[e + 3];
-        ha[e] = (_Float16)silu_scaled(ya);
-        hb[e] = (_Float16)silu_scaled(yb);
-    }
-    *reinterpret_cast<half4 *>(vt + (2 * lane) * kVT_LD + 16 * wave + 4 * P) = ha;
-    *reinterpret_cast<half4 *>(vt + (2 * lane + 1) * kVT_LD + 16 * wave + 4 * P) = hb;
-}
-__device__ __forceinline__ void chain_vconv_all(const ConvW &cw, const uint32_t (&win)[19], _Float16 *vt, int wave,
-                                                int lane)
-{
-    chain_vconv<0>(cw, win, vt, wave, lane);
-    chain_vconv<1>(cw, win, vt, wave, lane);
-    chain_vconv<2>(cw, win, vt, wave, lane);
-    chain_vconv<3>(cw, win, vt, wave, lane);
+    const int R = 4 * f + (lane >> 4), piece = (lane ^ R) & 15;
+    uint8_t *dst = buf + ChainBuf::kV + f * 1024;
+    if (f == 0)  // tile row 0 is unused: a negative offset reads zero
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rvh, (lds_void_t *)dst, 16, (R - 1) * d.ldh + piece * 16, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rv, (lds_void_t *)dst, 16, (R - 4) * d.ldb + piece * 16, 0, 0, 0);
 }
 
-// The same four rows in eleven slices, to be spread between matrix-core
-// instructions: slices 0-1 unpack the window, 2-9 form one output each,
-// 10 writes the two rows.
-struct VConvSlices {
-    float xa[7], xb[7];
-    half4 ha, hb;
-};
-__device__ __forceinline__ void chain_vconv_slice(int sl, int P, VConvSlices &st, const ConvW &cw,
-                                                  const uint32_t (&win)[19], _Float16 *vt, int wave, int lane)
+template <int I>
+__device__ __forceinline__ void chain_dma_group(const ChainDma &d, uint8_t *buf, int wave, int lane)
 {
-    if (sl == 0 || sl == 1) {
-#pragma unroll
-        for (int m = 0; m < 7; ++m)
-            if ((m < 4) == (sl == 0)) {
-                st.xa[m] = bf16_lo(win[4 * P + m]);
-                st.xb[m] = bf16_hi(win[4 * P + m]);
-            }
-    } else if (sl < 10) {
-        const int e = (sl - 2) >> 1;
-        if (((sl - 2) & 1) == 0) {
-            const float u = cw.a[0] * st.xa[e] + cw.a[1] * st.xa[e + 1] + cw.a[2] * st.xa[e + 2] + cw.a[3] * st.xa[e + 3];
-            st.ha[e] = (_Float16)silu_scaled(u);
-        } else {
-            const float u = cw.b[0] * st.xb[e] + cw.b[1] * st.xb[e + 1] + cw.b[2] * st.xb[e + 2] + cw.b[3] * st.xb[e + 3];
-            st.hb[e] = (_Float16)silu_scaled(u);
-        }
-    } else if (sl == 10) {
-        *reinterpret_cast<half4 *>(vt + (2 * lane) * kVT_LD + 16 * wave + 4 * P) = st.ha;
-        *reinterpret_cast<half4 *>(vt + (2 * lane + 1) * kVT_LD + 16 * wave + 4 * P) = st.hb;
+    const int f = 4 * I + wave, v16 = lane * 16;
+    {
+        // k^ rows 4f .. 4f+3: lane L fills slot L % 16 of row R = 4f + L / 16
+        const int R = 4 * f + (lane >> 4), piece = ((lane & 15) ^ ksw(R)) & 15;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rk, (lds_void_t *)(buf + ChainBuf::kK + f * 1024), 16,
+                                                 R * 256 + piece * 16, 0, 0, 0);
     }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rq, (lds_void_t *)(buf + ChainBuf::kQ + f * 1024), 16, v16, f * 1024, 0, 0);
+    chain_dma_v(d, buf, f, lane);
+    // head record: 13 pieces (P 0-5, T' 6-11, gates 12)
+    if (I < 3 || wave == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rh, (lds_void_t *)(buf + ChainBuf::kRec + f * 1024), 16, v16, f * 1024, 0, 0);
+    if (I == 1 && wave == 3) chain_dma_v(d, buf, 16, lane);
+}
+
+__device__ __forceinline__ void chain_dma(const PrefillArgs &p, const Workspace &ws, const ChainRun &run,
+                                          uint8_t *buf, long c, int h, int g, int wave, int lane)
+{
+    const ChainDma d = chain_dma_plan(p, ws, run, c, h, g);
+    chain_dma_group<0>(d, buf, wave, lane);
+    chain_dma_group<1>(d, buf, wave, lane);
+    chain_dma_group<2>(d, buf, wave, lane);
+    chain_dma_group<3>(d, buf, wave, lane);
+}
+
+// Conv tap operands (B) of the wave's channel tile x and tap pair m: the
+// contraction index kappa(q, i) stands for (tap 2m + (i >= 4), channel
+// 4q + i % 4) of the tile, so lane (q, c) holds tap 2m / 2m+1 of channel c
+// where 4q + i % 4 == c and zero elsewhere.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8 conv_tap_frag(const uint16_t *__restrict__ w, int ch, int m, int lane)
+{
+    const int q4 = lane >> 4, c16 = lane & 15;
+    const uint16_t *wc = w + (long)ch * 4;  // taps of channel ch (= the tile's channel c16)
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const bool on = 4 * q4 + (i & 3) == c16;
+        const uint16_t bits = on ? wc[2 * m + (i >> 2)] : (uint16_t)0;
+        r[i] = __builtin_bit_cast(__bf16, bits);
+    }
+    return r;
+}
+
+// Conv operand (A) of token tile rt, channel tile x, tap pair m: lane (q, r)
+// takes the raw rows of token 16rt + r shifted by taps 2m and 2m+1 (tile rows
+// 16rt + r + 1 + 2m and + 2 + 2m), channels 4q .. 4q+3 of the tile.
+__device__ __forceinline__ bf16x8 conv_row_frag(const uint8_t *vt, int rt, int x, int m, int wave, int lane)
+{
+    const int q4 = lane >> 4, r = lane & 15;
+    const int byte = (32 * wave + 16 * x + 4 * q4) * 2;
+    const int R = 16 * rt + r + 1 + 2 * m;
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 lo = *reinterpret_cast<const u32x2 *>(vt + vtile_offset(R, byte));
+    const u32x2 hi = *reinterpret_cast<const u32x2 *>(vt + vtile_offset(R + 1, byte));
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], hi[0], hi[1]});
+}
+
+// k^ as the A operand of K S (token tile rt, d block kb): lane (q, r) takes
+// token 16rt + r, d = 32kb + 4q .. +3 and 32kb + 16 + 4q .. +3
+__device__ __forceinline__ half8 ktile_frag(const uint8_t *kt, int rt, int kb, int lane)
+{
+    const int q4 = lane >> 4, r = lane & 15, R = 16 * rt + r;
+    const half4 lo = *reinterpret_cast<const half4 *>(kt + ktile_offset(R, (32 * kb + 4 * q4) * 2));
+    const half4 hi = *reinterpret_cast<const half4 *>(kt + ktile_offset(R, (32 * kb + 16 + 4 * q4) * 2));
+    return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// k^T as the A operand of the state update (d tile dt, token block tb):
+// lane (q, r) needs d = 16dt + r at tokens 32tb + 4q .. +3 and 32tb + 16 + 4q
+// .. +3.  A transposed read hands lane i of each 16-lane group element i % 4
+// of the 8 bytes that lane 4j + i / 4 of the group addressed, as its element
+// j; so lane s of group q addresses token row 32tb + 4q + s / 4, d columns
+// 16dt + 4 (s % 4) .. +3.
+__device__ __forceinline__ half8 ktile_frag_t(const uint8_t *kt, int dt, int tb, int lane)
+{
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const int q4 = lane >> 4, s = lane & 15;
+    const int R = 32 * tb + 4 * q4 + (s >> 2), byte = (16 * dt + 4 * (s & 3)) * 2;
+    const uint8_t *p0 = kt + ktile_offset(R, byte), *p1 = kt + ktile_offset(R + 16, byte);
+    const half4 lo = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                   (lds_s16x4 *)(__attribute__((address_space(3))) uint8_t *)(p0)));
+    const half4 hi = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                   (lds_s16x4 *)(__attribute__((address_space(3))) uint8_t *)(p1)));
+    return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
 // VMEM operations a wave issues after a chunk's operand DMA and before the
@@ -813,50 +822,50 @@ constexpr int kChainVmemAfterDma = 4;
 // lgkmcnt at their no-wait maxima
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
 
-// One chunk from operand buffer `cur` and v^T buffer `vtc`; loads the next
-// chunk's operands into `nxt`, converts its raw v rows (`win`, loaded a step
-// ago) into `vtn`, and loads the raw v rows of the chunk after it into `win`.
-//   X, Vn [rt][x]  tokens 16rt.. x columns 16x..  (accumulator rows = tokens)
-//   QST   [x][rt]  (Q S)^T, columns 16x.. x tokens 16rt.. (accumulator rows = columns)
+// One chunk from operand buffer `cur`; loads the next chunk's operands into `nxt`.
+//   Z, X, Vn [rt][x]  tokens 16rt.. x columns 16x..  (accumulator rows = tokens)
+//   QST      [x][rt]  (Q S)^T, columns 16x.. x tokens 16rt.. (accumulator rows = columns)
 // The output is formed transposed, O^T = S^T Q^T diag(q_scale Gam) + Vnew^T P^T,
 // so that a lane holds four adjacent columns of one token (8-byte LDS writes
 // into the row staging).  The fragment layout is the same for A and B
 // operands, so the packed state and Vnew serve as A operands unchanged.
 __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace &ws, uint8_t *cur, uint8_t *nxt,
-                                           _Float16 *vtc, _Float16 *vtn, uint32_t (&win)[19], f32x4 (&S)[8][2],
-                                           const ConvW &cw, const ChainRun &run, int cc, int h, int g, int wave,
-                                           int lane)
+                                           uint8_t *stage, f32x4 (&S)[8][2], const bf16x8 (&wb)[2][2],
+                                           const ChainRun &run, int cc, int h, int g, int wave, int lane)
 {
-    const int Hqk = p.Hqk, Hv = p.Hv;
+    const int Hv = p.Hv;
     const int q4 = lane >> 4, c16 = lane & 15;
-    // chunk cc's operands and v^ have landed for every wave, and every wave is
-    // done with the buffers the next chunk's loads overwrite
+    // chunk cc's operands have landed for every wave, and every wave is done
+    // with the buffer the next chunk's DMA overwrites
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kChainVmemAfterDma));
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    // the next chunk and the one after (the last steps repeat the run's last)
-    const int cn = min(cc + 1, run.c_to - 1), cn2 = min(cc + 2, run.c_to - 1);
-    const ChainDma dn = chain_dma_plan(ws, cn, h, g, Hqk, Hv);
+    const int cn = min(cc + 1, run.c_to - 1);  // the last step repeats its own chunk
+    const ChainDma dn = chain_dma_plan(p, ws, run, cn, h, g);
 
-    const half8 *Kf = reinterpret_cast<const half8 *>(cur + ChainBuf::kK) + lane;
+    const uint8_t *kt = cur + ChainBuf::kK;
     const half8 *Qf = reinterpret_cast<const half8 *>(cur + ChainBuf::kQ) + lane;
-    const half8 *KTf = reinterpret_cast<const half8 *>(cur + ChainBuf::kKT) + lane;
     const half8 *Pf = reinterpret_cast<const half8 *>(cur + ChainBuf::kP) + lane;
     const half8 *Tf = reinterpret_cast<const half8 *>(cur + ChainBuf::kT) + lane;
     const float *gt = reinterpret_cast<const float *>(cur + ChainBuf::kG);
+    const uint8_t *vt = cur + ChainBuf::kV;
 
-    // v^ at the wave's columns in accumulator layout: tile (rt, x) lane (q, c)
-    // holds tokens 16rt + 4q .. +3 of column 32w + 16x + c
-    half4 vh[4][2];
+    // conv of v at the wave's channels (pre-activation), on the matrix cores
+    f32x4 Z[4][2];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
-            vh[rt][x] = *reinterpret_cast<const half4 *>(vtc + (32 * wave + 16 * x + c16) * kVT_LD + 16 * rt + 4 * q4);
+        for (int x = 0; x < 2; ++x) {
+            Z[rt][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(conv_row_frag(vt, rt, x, 0, wave, lane), wb[x][0],
+                                                               f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            Z[rt][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(conv_row_frag(vt, rt, x, 1, wave, lane), wb[x][1],
+                                                               Z[rt][x], 0, 0, 0);
+        }
 
     // K S and (Q S)^T over the four 32-row blocks of the state; the LDS
-    // fragments of block kb+1 are read while block kb multiplies, and the
-    // next chunk's DMA goes out one group per block
+    // fragments of block kb+1 are read while block kb multiplies, the next
+    // chunk's DMA goes out one group per block, and SiLU of a quarter of the
+    // conv runs on the vector ALUs meanwhile
     f32x4 X[4][2], QST[2][4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
@@ -865,21 +874,13 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
             X[rt][x] = f32x4{0.f, 0.f, 0.f, 0.f};
             QST[x][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-    half8 ak[2][4], aq[2][4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        ak[0][rt] = Kf[(rt * 4) * 64];
-        aq[0][rt] = Qf[(rt * 4) * 64];
-    }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        const int cb = kb & 1;
-        if (kb < 3) {
+        half8 ak[4], aq[4];
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                ak[cb ^ 1][rt] = Kf[(rt * 4 + kb + 1) * 64];
-                aq[cb ^ 1][rt] = Qf[(rt * 4 + kb + 1) * 64];
-            }
+        for (int rt = 0; rt < 4; ++rt) {
+            ak[rt] = ktile_frag(kt, rt, kb, lane);
+            aq[rt] = Qf[(rt * 4 + kb) * 64];
         }
         if (kb == 0) chain_dma_group<0>(dn, nxt, wave, lane);
         if (kb == 1) chain_dma_group<1>(dn, nxt, wave, lane);
@@ -888,27 +889,21 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
         __builtin_amdgcn_sched_barrier(0);
         const half8 sb0 = pack_h8(S[2 * kb][0], S[2 * kb + 1][0]);
         const half8 sb1 = pack_h8(S[2 * kb][1], S[2 * kb + 1][1]);
-        // a quarter of the next chunk's v^ on the vector ALUs, one slice
-        // after each matrix-core instruction
-        VConvSlices vs;
 #pragma unroll
         for (int sl = 0; sl < 16; ++sl) {
             const int rt = sl >> 2;
             switch (sl & 3) {
-            case 0: X[rt][0] = mfma16(ak[cb][rt], sb0, X[rt][0]); break;
-            case 1: X[rt][1] = mfma16(ak[cb][rt], sb1, X[rt][1]); break;
-            case 2: QST[0][rt] = mfma16(sb0, aq[cb][rt], QST[0][rt]); break;
-            default: QST[1][rt] = mfma16(sb1, aq[cb][rt], QST[1][rt]); break;
+            case 0: X[rt][0] = mfma16(ak[rt], sb0, X[rt][0]); break;
+            case 1: X[rt][1] = mfma16(ak[rt], sb1, X[rt][1]); break;
+            case 2: QST[0][rt] = mfma16(sb0, aq[rt], QST[0][rt]); break;
+            default: QST[1][rt] = mfma16(sb1, aq[rt], QST[1][rt]); break;
             }
-            chain_vconv_slice(sl, kb, vs, cw, win, vtn, wave, lane);
+            // SiLU of conv tile (kb, x = sl / 8), one value per slot
+            if (sl < 8) Z[kb][sl >> 2][sl & 3] = silu_f(Z[kb][sl >> 2][sl & 3]);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    // raw v rows of the chunk after the next, converted in the next step
-    __builtin_amdgcn_sched_barrier(0);
-    chain_vload(p, run, cn2, wave, lane, win);
-    __builtin_amdgcn_sched_barrier(0);
-    // Vnew = T' (V - diag(Gam) X): the bracket as B operands over the chunk's
+    // Vnew = T' (v^ - diag(Gam) X): the bracket as B operands over the chunk's
     // two 32-token blocks, T' lower triangular
     half8 tf[6];
 #pragma unroll
@@ -922,15 +917,9 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                f32x4 y[2];
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        y[i][e] = (float)vh[2 * tb + i][x][e] - gg[2 * tb + i][e] * X[2 * tb + i][x][e];
-                yb[tb][x] = pack_h8(y[0], y[1]);
-            }
+            for (int x = 0; x < 2; ++x)
+                yb[tb][x] = pack_h8(Z[2 * tb][x] - gg[2 * tb] * X[2 * tb][x],
+                                    Z[2 * tb + 1][x] - gg[2 * tb + 1] * X[2 * tb + 1][x]);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -944,7 +933,7 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) kf[0][i][tb] = KTf[(2 * i + tb) * 64];
+        for (int tb = 0; tb < 2; ++tb) kf[0][i][tb] = ktile_frag_t(kt, i, tb, lane);
     half8 pf[6];
 #pragma unroll
     for (int i = 0; i < 6; ++i) pf[i] = Pf[i * 64];
@@ -975,7 +964,7 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int tb = 0; tb < 2; ++tb) kf[cb ^ 1][i][tb] = KTf[(2 * (2 * pr + 2 + i) + tb) * 64];
+                for (int tb = 0; tb < 2; ++tb) kf[cb ^ 1][i][tb] = ktile_frag_t(kt, 2 * pr + 2 + i, tb, lane);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -989,7 +978,7 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
         }
     }
     // O = diag(q_scale Gam) Q S + P Vnew (P lower triangular), through the
-    // wave's staging 32 token rows at a time: (Q S)^T tile (x, rt) lane (q, c)
+    // wave's staging 16 token rows at a time: (Q S)^T tile (x, rt) lane (q, c)
     // holds columns 16x + 4q .. +3 of token 16rt + c.  The buffer range of the
     // stores ends at the chunk's last valid token, so the rows of a partial
     // chunk and every row of a warm-up chunk (n = 0) are dropped without a
@@ -999,32 +988,25 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
     const int rowb = Hv * kD * 2;  // bytes per token row of o
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
         p.o + ((long)(run.t0 + rel) * Hv + h) * kD + 32 * wave, 0, n * rowb, 0x00020000);
-    uint8_t *stage = reinterpret_cast<uint8_t *>(vtc + 32 * wave * kVT_LD);
     uint16_t *os = reinterpret_cast<uint16_t *>(stage);
+    static_assert(kChainStageRows == 16, "one token tile per staging round");
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
-        for (int r2 = 0; r2 < 2; ++r2) {
-            const int rt = 2 * half + r2;
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                f32x4 acc = mfma16(vb[0][x], pf[tri_frag(rt, 0)], QST[x][rt] * gm[rt]);
-                if (rt >= 2) acc = mfma16(vb[1][x], pf[tri_frag(rt, 1)], acc);
-                typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-                const u32x2 v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-                *reinterpret_cast<u32x2 *>(os + (16 * r2 + c16) * 32 + 16 * x + 4 * q4) = v;
-            }
+        for (int x = 0; x < 2; ++x) {
+            f32x4 acc = mfma16(vb[0][x], pf[tri_frag(rt, 0)], QST[x][rt] * gm[rt]);
+            if (rt >= 2) acc = mfma16(vb[1][x], pf[tri_frag(rt, 1)], acc);
+            typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+            *reinterpret_cast<u32x2 *>(os + c16 * 32 + 16 * x + 4 * q4) = v;
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // 32 rows of 64 bytes: lane -> (row 16i + lane/4, 16-byte piece lane%4)
+        // 16 rows of 64 bytes: lane -> (row lane/4, 16-byte piece lane%4)
         const int row = lane >> 2, piece = lane & 3;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const i32x4 v = *reinterpret_cast<const i32x4 *>(stage + (16 * i + row) * 64 + piece * 16);
-            __builtin_amdgcn_raw_buffer_store_b128(v, ro, (32 * half + 16 * i + row) * rowb + piece * 16, 0, 0);
-        }
+        const i32x4 v = *reinterpret_cast<const i32x4 *>(stage + row * 64 + piece * 16);
+        __builtin_amdgcn_raw_buffer_store_b128(v, ro, (16 * rt + row) * rowb + piece * 16, 0, 0);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -1033,22 +1015,18 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
 
 // The chunks of one run, the state carried in registers.
 __device__ __forceinline__ void chain_run(const PrefillArgs &p, const Workspace &ws, uint8_t *buf0, uint8_t *buf1,
-                                          _Float16 *vt0, _Float16 *vt1, f32x4 (&S)[8][2], const ConvW &cw,
+                                          uint8_t *stage, f32x4 (&S)[8][2], const bf16x8 (&wb)[2][2],
                                           const ChainRun &run, int h, int g, int wave, int lane)
 {
     if (run.c_to <= run.c_from) return;
-    chain_dma(ws, buf0, run.c_from, h, g, p.Hqk, p.Hv, wave, lane);
-    uint32_t win[19];
-    chain_vload(p, run, run.c_from, wave, lane, win);
-    chain_vconv_all(cw, win, vt0, wave, lane);
-    chain_vload(p, run, min(run.c_from + 1, run.c_to - 1), wave, lane, win);
+    chain_dma(p, ws, run, buf0, run.c_from, h, g, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     int cc = run.c_from;
     for (; cc + 2 <= run.c_to; cc += 2) {
-        chain_step(p, ws, buf0, buf1, vt0, vt1, win, S, cw, run, cc, h, g, wave, lane);
-        chain_step(p, ws, buf1, buf0, vt1, vt0, win, S, cw, run, cc + 1, h, g, wave, lane);
+        chain_step(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
+        chain_step(p, ws, buf1, buf0, stage, S, wb, run, cc + 1, h, g, wave, lane);
     }
-    if (cc < run.c_to) chain_step(p, ws, buf0, buf1, vt0, vt1, win, S, cw, run, cc, h, g, wave, lane);
+    if (cc < run.c_to) chain_step(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
     // the last step's DMA into the other buffer is still in flight
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -1074,7 +1052,7 @@ __device__ __forceinline__ int warm_start(const Workspace &ws, int h, int Hv, in
     if (cb <= c0) return c0;
     const int c = cb - 1 - lane;
     const bool in = c >= c0;
-    float gsum = in ? ws.gates[((long)c * Hv + h) * kGateFloats + 129] : 0.f;
+    float gsum = in ? reinterpret_cast<const float *>(ws.hrec + ((long)c * Hv + h) * kRecBytes + kRecG)[129] : 0.f;
     // inclusive prefix over lanes: log2 of the decay of chunks cb-1-lane .. cb-1
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -1132,10 +1110,10 @@ void chain_kernel(PrefillArgs p, Workspace ws)
 {
     __shared__ __attribute__((aligned(16))) uint8_t buf0[ChainBuf::kBytes];
     __shared__ __attribute__((aligned(16))) uint8_t buf1[ChainBuf::kBytes];
-    __shared__ __attribute__((aligned(16))) _Float16 vt0[kVTHalfs];
-    __shared__ __attribute__((aligned(16))) _Float16 vt1[kVTHalfs];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_all[4 * kChainStage];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    uint8_t *stage = stage_all + wave * kChainStage;
     const int Hqk = p.Hqk, Hv = p.Hv, G = Hv / Hqk;
     // block -> (segment or rank, group, head in group); the G heads of one
     // (segment, QK group) land on the same XCD (same L2)
@@ -1146,7 +1124,11 @@ void chain_kernel(PrefillArgs p, Workspace ws)
     const int unit = gu / Hqk, g = gu % Hqk;
     const int h = g * G + j;
     const long C_tot = 2L * Hqk * kD + (long)Hv * kD, cv = 2L * Hqk * kD + (long)h * kD;
-    const ConvW cw = conv_weights(p.conv_w + cv * 4, lane, kNegLog2e);
+    // conv taps of the wave's two channel tiles
+    const bf16x8 wb[2][2] = {{conv_tap_frag(p.conv_w, cv + 32 * wave + (lane & 15), 0, lane),
+                              conv_tap_frag(p.conv_w, cv + 32 * wave + (lane & 15), 1, lane)},
+                             {conv_tap_frag(p.conv_w, cv + 32 * wave + 16 + (lane & 15), 0, lane),
+                              conv_tap_frag(p.conv_w, cv + 32 * wave + 16 + (lane & 15), 1, lane)}};
     f32x4 S[8][2];
 
     if (!kRepair) {
@@ -1163,7 +1145,7 @@ void chain_kernel(PrefillArgs p, Workspace ws)
         state_load(S, w == si.x && p.state_in ? p.state_in + sbase : nullptr, wave, lane);
         const uint16_t *hist = p.conv_state_in ? p.conv_state_in + (long)s * 3 * C_tot + cv : nullptr;
         const uint16_t *vs = p.v + (long)si.z * Hv * kD + (long)h * kD;
-        chain_run(p, ws, buf0, buf1, vt0, vt1, S, cw, ChainRun{si.x, si.z, si.w, w, sg.z, sg.y, vs, hist}, h, g, wave,
+        chain_run(p, ws, buf0, buf1, stage, S, wb, ChainRun{si.x, si.z, si.w, w, sg.z, sg.y, vs, hist}, h, g, wave,
                   lane);
         // Final states.  Every segment but the last parks its final state for
         // the repair pass, which runs after this one and hands it to the next
@@ -1213,7 +1195,7 @@ void chain_kernel(PrefillArgs p, Workspace ws)
             }
             if (!carry) state_load(S, ws.bstate + ((long)(k - 1) * Hv + h) * kStateFloats, wave, lane);
             const int4 sg = Tables::seg(p, ws, k);
-            chain_run(p, ws, buf0, buf1, vt0, vt1, S, cw, ChainRun{si.x, si.z, si.w, sg.y, sg.z, sg.y, vs, hist}, h, g,
+            chain_run(p, ws, buf0, buf1, stage, S, wb, ChainRun{si.x, si.z, si.w, sg.y, sg.z, sg.y, vs, hist}, h, g,
                       wave, lane);
             carry = true;
         }
@@ -1266,11 +1248,8 @@ size_t prefill_workspace_bytes(int max_chunks, int N, int Hqk, int Hv)
     total += align256((size_t)N * sizeof(int4));
     total += align256((size_t)N * sizeof(int));
     total += align256(C * Hqk * kQFragBytes);
-    total += align256(C * Hqk * kKFragBytes);
-    total += align256(C * Hqk * kKTokFragBytes);
-    total += align256(C * Hv * kPFragBytes);
-    total += align256(C * Hv * kTFragBytes);
-    total += align256(C * Hv * kGateFloats * sizeof(float));
+    total += align256(C * Hqk * kKRowBytes);
+    total += align256(C * Hv * kRecBytes);
     total += align256(M * sizeof(int4));
     total += align256((size_t)N * sizeof(int4));
     total += align256(M * Hv * sizeof(int));
@@ -1293,11 +1272,8 @@ Workspace carve_workspace(void *base, int max_chunks, int N, int Hqk, int Hv)
     ws.seq_info = reinterpret_cast<int4 *>(take((size_t)N * sizeof(int4)));
     ws.order = reinterpret_cast<int *>(take((size_t)N * sizeof(int)));
     ws.qfrag = take(C * Hqk * kQFragBytes);
-    ws.kfrag = take(C * Hqk * kKFragBytes);
-    ws.ktok = take(C * Hqk * kKTokFragBytes);
-    ws.pfrag = take(C * Hv * kPFragBytes);
-    ws.tfrag = take(C * Hv * kTFragBytes);
-    ws.gates = reinterpret_cast<float *>(take(C * Hv * kGateFloats * sizeof(float)));
+    ws.krow = take(C * Hqk * kKRowBytes);
+    ws.hrec = take(C * Hv * kRecBytes);
     ws.seg_info = reinterpret_cast<int4 *>(take(M * sizeof(int4)));
     ws.seq_seg = reinterpret_cast<int4 *>(take((size_t)N * sizeof(int4)));
     ws.seg_bad = reinterpret_cast<int *>(take(M * Hv * sizeof(int)));
@@ -1319,27 +1295,21 @@ hipError_t launch_prefill(const PrefillArgs &p, void *workspace, hipStream_t str
     if ((e = mark(1)) != hipSuccess) return e;
     if (p.max_chunks > 0) {
         const long units = (long)p.max_chunks * p.Hqk;
-        hipLaunchKernelGGL(prep_qk_kernel, dim3((unsigned)units), dim3(kPrepThreads), 0, stream, p, ws);
+        hipLaunchKernelGGL(prep_kernel, dim3((unsigned)units), dim3(kPrepThreads), 0, stream, p, ws);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = mark(2)) != hipSuccess) return e;
-        const long blocks = ((units + 7) / 8) * 8L * (p.Hv / p.Hqk);
-        hipLaunchKernelGGL(prep_head_kernel, dim3((unsigned)blocks), dim3(kPrepThreads), 0, stream, p, ws);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    } else if ((e = mark(2)) != hipSuccess) {
-        return e;
     }
-    if ((e = mark(3)) != hipSuccess) return e;
+    if ((e = mark(2)) != hipSuccess) return e;
     const int G = p.Hv / p.Hqk;
     const long seg_groups = (long)p.max_segs * p.Hqk;
     const long seg_blocks = ((seg_groups + 7) / 8) * 8L * G;
     hipLaunchKernelGGL(chain_kernel<false>, dim3((unsigned)seg_blocks), dim3(256), 0, stream, p, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = mark(4)) != hipSuccess) return e;
+    if ((e = mark(3)) != hipSuccess) return e;
     const long groups = (long)p.N * p.Hqk;
     const long blocks = ((groups + 7) / 8) * 8L * G;
     hipLaunchKernelGGL(chain_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, p, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    return mark(5);
+    return mark(4);
 }
 
 }  // namespace gdn
