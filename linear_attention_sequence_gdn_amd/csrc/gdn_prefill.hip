@@ -397,13 +397,25 @@ constexpr int kPrepTile = 64 * kAL * 4;  // one fp32 64 x 64 tile (row stride kA
 static_assert(64 * kQ_LD * 2 <= kPrepTile, "a token-major q^ / k^ tile fits in an fp32 tile");
 
 
-__global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillArgs p, Workspace ws)
+// Lower 16 x 16 tiles of K K^T (row tile, column tile) and of K Q^T (query
+// tile, key tile) computed by each wave: five per wave.  The K Q^T tiles of a
+// P fragment (query tile rt, key block kb) stay within one wave, except for
+// fragment (3, 1), whose two halves come from waves 2 and 3.
+__device__ constexpr int kPrepKK[4][3][2] = {{{0, 0}, {2, 1}, {3, 2}}, {{1, 0}, {2, 2}, {3, 3}},
+                                             {{1, 1}, {3, 0}, {0, 0}}, {{2, 0}, {3, 1}, {0, 0}}};
+__device__ constexpr int kPrepKQ[4][3][2] = {{{0, 0}, {2, 2}, {0, 0}}, {{1, 0}, {1, 1}, {0, 0}},
+                                             {{2, 0}, {2, 1}, {3, 2}}, {{3, 0}, {3, 1}, {3, 3}}};
+
+// Four resident workgroups per CU (at most 128 VGPRs): the per-head phases
+// are short stretches between barriers, and other workgroups fill the waits.
+__global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void prep_kernel(PrefillArgs p, Workspace ws)
 {
     // LDS plan: [R0] q^ (fp16) -> A (fp32); [R1] k^ (fp16) -> X = (I+A)^-1
-    // (fp32); scratch of the inverse; the gates of four heads
+    // (fp32); product slots of the inverse; the gates of four heads
     __shared__ __attribute__((aligned(16))) uint8_t R0[kPrepTile];
     __shared__ __attribute__((aligned(16))) uint8_t R1[kPrepTile];
-    __shared__ __attribute__((aligned(16))) float Msc[3 * 256];
+    __shared__ __attribute__((aligned(16))) float Msc[4 * 256];
     __shared__ float s_gam2[4 * 64];
     __shared__ __attribute__((aligned(16))) float s_beta[4 * 64];
     _Float16 *Qs = reinterpret_cast<_Float16 *>(R0), *Ks = reinterpret_cast<_Float16 *>(R1);
@@ -456,18 +468,16 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillArgs p, Works
         }
     }
     __syncthreads();
-    // ---- operands of the sequential pass, and K K^T (rows 16*wave.., column
-    //      tiles ct <= wave) and K Q^T (query tile `wave`, key tiles jt <= wave)
-    f32x4 kk[4], kq[4];
+    // ---- operands of the sequential pass (q^ fragments of row tile `wave`,
+    //      k^ rows), then the lower 16 x 16 tiles of K K^T and K Q^T, five per
+    //      wave: K K^T tile (rt, ct) with ct <= rt, and K Q^T tile (query rt,
+    //      key jt) with jt <= rt, kept in registers for every head
+    f32x4 kk[3], kq[3];
+    const int nkk = wave < 2 ? 3 : 2, nkq = wave < 2 ? 2 : 3;
     {
         half8 *qf = reinterpret_cast<half8 *>(ws.qfrag + gc * kQFragBytes);
-        half8 qOwn[4], kOwn[4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            qOwn[kb] = lds_frag(Qs, kQ_LD, 16 * wave, 32 * kb, lane);
-            kOwn[kb] = lds_frag(Ks, kQ_LD, 16 * wave, 32 * kb, lane);
-            qf[(wave * 4 + kb) * 64 + lane] = qOwn[kb];
-        }
+        for (int kb = 0; kb < 4; ++kb) qf[(wave * 4 + kb) * 64 + lane] = lds_frag(Qs, kQ_LD, 16 * wave, 32 * kb, lane);
         // k^ rows: 64 rows of 256 bytes, 16 bytes per thread and pass
         uint8_t *kr = ws.krow + gc * kKRowBytes;
 #pragma unroll
@@ -477,21 +487,28 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillArgs p, Works
                 *reinterpret_cast<const i32x4 *>(Ks + row * kQ_LD + col * 8);
         }
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
+        for (int i = 0; i < 3; ++i) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acq = {0.f, 0.f, 0.f, 0.f};
-            if (ct <= wave) {
+            if (i < nkk) {
+                const int rt = kPrepKK[wave][i][0], ct = kPrepKK[wave][i][1];
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
-                    const half8 kc = lds_frag(Ks, kQ_LD, 16 * ct, 32 * kb, lane);
-                    acc = mfma16(kOwn[kb], kc, acc);
-                    acq = mfma16(kc, qOwn[kb], acq);
-                }
+                for (int kb = 0; kb < 4; ++kb)
+                    acc = mfma16(lds_frag(Ks, kQ_LD, 16 * rt, 32 * kb, lane), lds_frag(Ks, kQ_LD, 16 * ct, 32 * kb, lane),
+                                 acc);
             }
-            kk[ct] = acc;
-            kq[ct] = acq;
+            if (i < nkq) {
+                const int rt = kPrepKQ[wave][i][0], jt = kPrepKQ[wave][i][1];
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    acq = mfma16(lds_frag(Ks, kQ_LD, 16 * jt, 32 * kb, lane), lds_frag(Qs, kQ_LD, 16 * rt, 32 * kb, lane),
+                                 acq);
+            }
+            kk[i] = acc;
+            kq[i] = acq;
+            __builtin_amdgcn_sched_barrier(0);  // one tile's operands in flight at a time
         }
     }
-    __syncthreads();  // the q^ / k^ / k^T tiles are dead from here on
+    __syncthreads();  // the q^ / k^ tiles are dead from here on
 
     for (int j0 = 0; j0 < G; j0 += 4) {
         // gates of heads j0 .. j0+3 of the group (wave w: head j0 + w)
@@ -513,44 +530,53 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillArgs p, Works
         for (int jj = 0; jj < jn; ++jj) {
             const long hc = (long)c * Hv + g * G + j0 + jj;
             const float *gam2 = s_gam2 + 64 * jj, *beta = s_beta + 64 * jj;
-            // ---- A = strict_lower(diag(beta) K K^T * D) -> LDS; P = (K Q^T)^T * D (lower) -> global
-            {
+            // ---- A = strict_lower(diag(beta) K K^T * D) -> LDS
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) {
-                    if (ct > wave) continue;
-                    const int jc = 16 * ct + c16;
-                    const float gj = gam2[jc];
+            for (int i = 0; i < 3; ++i) {
+                if (i >= nkk) continue;
+                const int rt = kPrepKK[wave][i][0], ct = kPrepKK[wave][i][1];
+                const int jc = 16 * ct + c16;
+                const float gj = gam2[jc];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * rt + 4 * q4 + e;
+                    if (r > jc) As[r * kAL + jc] = beta[r] * kk[i][e] * __builtin_amdgcn_exp2f(gam2[r] - gj);
+                }
+            }
+            // ---- P = (K Q^T)^T * D, lower incl. the diagonal -> global: each
+            //      K Q^T tile gives half of a fragment (key tile jt: elements
+            //      4 (jt % 2) .. +3); wave 0 also writes the zero halves of
+            //      fragments (0, 0) and (2, 1)
+            {
+                uint8_t *pf = ws.hrec + hc * kRecBytes + kRecP;
+#pragma unroll
+                for (int i = 0; i < 3; ++i) {
+                    if (i >= nkq) continue;
+                    const int rt = kPrepKQ[wave][i][0], jt = kPrepKQ[wave][i][1];
+                    const int qi = 16 * rt + c16;
+                    const float gi = gam2[qi];
+                    half4 hv;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int i = 16 * wave + 4 * q4 + e;
-                        if (i > jc) As[i * kAL + jc] = beta[i] * kk[ct][e] * __builtin_amdgcn_exp2f(gam2[i] - gj);
+                        const int jc = 16 * jt + 4 * q4 + e;
+                        hv[e] = (_Float16)(qi >= jc ? p.q_scale * kq[i][e] * __builtin_amdgcn_exp2f(gi - gam2[jc]) : 0.f);
                     }
-                }
-                half8 *pf = reinterpret_cast<half8 *>(ws.hrec + hc * kRecBytes + kRecP);
-                const int i = 16 * wave + c16;
-                const float gi = gam2[i];
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    if (kb > wave / 2) continue;  // query tiles 0, 1 see only key block 0
-                    half8 fr;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int jt = 2 * kb + (e >> 2);
-                        const int jc = 16 * jt + 4 * q4 + (e & 3);
-                        float val = 0.f;
-                        if (jt <= wave && i >= jc)
-                            val = p.q_scale * kq[jt][e & 3] * __builtin_amdgcn_exp2f(gi - gam2[jc]);
-                        fr[e] = (_Float16)val;
-                    }
-                    pf[tri_frag(wave, kb) * 64 + lane] = fr;
+                    uint8_t *dst = pf + (tri_frag(rt, jt >> 1) * 64 + lane) * 16 + 8 * (jt & 1);
+                    *reinterpret_cast<half4 *>(dst) = hv;
+                    if (wave == 0) *reinterpret_cast<half4 *>(dst + 8) = half4{0, 0, 0, 0};
                 }
             }
             __syncthreads();
-            // ---- X = (I + A)^-1, blocked by 16: diagonal blocks by forward
-            //      substitution (wave b, block b), then the blocks below the
-            //      diagonal level by level, X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj,
-            //      on the fp32 matrix cores
-            {
+            // ---- X = (I + A)^-1, blocked by 16.  Diagonal blocks by forward
+            //      substitution (wave b, block b).  Then, with L = I + A in
+            //      32 x 32 blocks, L^-1 = [[X_a, 0], [-X_b L_ba X_a, X_b]]:
+            //      first the two 32 x 32 diagonal blocks (X_10, X_32) and, at
+            //      the same time, the products that need only diagonal
+            //      blocks (M_21 = A_21 X_11, M_31 = A_31 X_11); then M_20,
+            //      M_30 and X_21, X_31; then X_20, X_30 -- three rounds of at
+            //      most two dependent 16 x 16 products, on the fp32 matrix
+            //      cores, with M kept in LDS between rounds.
+            {  // wave b: diagonal block b, lane c (< 16): its column c
                 float y[16];
                 const int bo = 16 * wave;
 #pragma unroll
@@ -562,20 +588,49 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillArgs p, Works
                 }
             }
             __syncthreads();
-#pragma unroll
-            for (int lvl = 1; lvl <= 3; ++lvl) {
-                if (wave < 4 - lvl) {
-                    const int bi = wave + lvl, bj = wave;
-                    f32x4 m = {0.f, 0.f, 0.f, 0.f};
-                    for (int bk = bj; bk < bi; ++bk)
-                        m = mm16_f32(As + 16 * bi * kAL + 16 * bk, kAL, Xs + 16 * bk * kAL + 16 * bj, kAL, m, lane);
-                    st16_f32(Msc + 256 * wave, 16, m, lane);
+            {
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                auto At = [&](int i, int j) { return As + 16 * i * kAL + 16 * j; };
+                auto Xt = [&](int i, int j) { return Xs + 16 * i * kAL + 16 * j; };
+                float *Ms = Msc + 256 * wave;  // this wave's product slot
+                auto wave_sync = [] {
                     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                     __builtin_amdgcn_wave_barrier();
                     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                    f32x4 x = {0.f, 0.f, 0.f, 0.f};
-                    x = mm16_f32(Xs + 16 * bi * kAL + 16 * bi, kAL, Msc + 256 * wave, 16, x, lane);
-                    st16_f32(Xs + 16 * bi * kAL + 16 * bj, kAL, -x, lane);
+                };
+                // round 1: X_10 = -X_11 (A_10 X_00), X_32 = -X_33 (A_32 X_22);
+                //          M_21 = A_21 X_11 (slot 2), M_31 = A_31 X_11 (slot 3)
+                if (wave < 2) {
+                    const int i = 2 * wave;  // (1, 0) or (3, 2)
+                    st16_f32(Ms, 16, mm16_f32(At(i + 1, i), kAL, Xt(i, i), kAL, z, lane), lane);
+                    wave_sync();
+                    st16_f32(Xt(i + 1, i), kAL, -mm16_f32(Xt(i + 1, i + 1), kAL, Ms, 16, z, lane), lane);
+                } else {
+                    st16_f32(Ms, 16, mm16_f32(At(wave, 1), kAL, Xt(1, 1), kAL, z, lane), lane);
+                }
+                __syncthreads();
+                // round 2: M_20 (slot 0), M_30 (slot 1); X_21 = -X_22 M_21,
+                //          X_31 = -(X_32 M_21 + X_33 M_31)
+                if (wave < 2) {
+                    const int i = 2 + wave;
+                    f32x4 m = mm16_f32(At(i, 0), kAL, Xt(0, 0), kAL, z, lane);
+                    m = mm16_f32(At(i, 1), kAL, Xt(1, 0), kAL, m, lane);
+                    st16_f32(Ms, 16, m, lane);
+                } else if (wave == 2) {
+                    st16_f32(Xt(2, 1), kAL, -mm16_f32(Xt(2, 2), kAL, Msc + 512, 16, z, lane), lane);
+                } else {
+                    f32x4 x = mm16_f32(Xt(3, 2), kAL, Msc + 512, 16, z, lane);
+                    x = mm16_f32(Xt(3, 3), kAL, Msc + 768, 16, x, lane);
+                    st16_f32(Xt(3, 1), kAL, -x, lane);
+                }
+                __syncthreads();
+                // round 3: X_20 = -X_22 M_20, X_30 = -(X_32 M_20 + X_33 M_30)
+                if (wave == 0) {
+                    st16_f32(Xt(2, 0), kAL, -mm16_f32(Xt(2, 2), kAL, Msc, 16, z, lane), lane);
+                } else if (wave == 1) {
+                    f32x4 x = mm16_f32(Xt(3, 2), kAL, Msc, 16, z, lane);
+                    x = mm16_f32(Xt(3, 3), kAL, Msc + 256, 16, x, lane);
+                    st16_f32(Xt(3, 0), kAL, -x, lane);
                 }
                 __syncthreads();
             }
