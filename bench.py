@@ -119,8 +119,9 @@ def source_digest():
 COPY_BYTES = 256 << 20
 TRAFFIC_KERNELS = {"prefill_chain": "chain_kernel<false>", "prefill_chain_repair": "chain_kernel<true>",
                    "prefill_prep": "prep_kernel",
-                   "prefill_setup": "setup_kernel", "decode": "decode_head_kernel",
-                   "decode_conv_shift": "conv_shift_qk_kernel"}
+                   "prefill_setup": "setup_kernel", "decode": "decode_step_kernel",
+                   "decode_conv_shift": "conv_shift_qk_kernel<1>",
+                   "decode_multi": "decode_head_kernel<4>", "decode_multi_conv_shift": "conv_shift_qk_kernel<4>"}
 
 
 def _counter_rows(path, counter):
@@ -443,7 +444,7 @@ def main():
         "decode": {"metric": "decode us/step (B=256, 16QK/48V, 64 in-place steps)",
                    "value": dc["us_per_step"], "unit": "us/step", "higher_is_better": False,
                    "kernel_us": dc["kernel_us"],
-                   "roofline": {"bound": "hbm", "kernel": "decode step (decode_head_kernel + conv_shift_qk_kernel)",
+                   "roofline": {"bound": "hbm", "kernel": "decode step (decode_step_kernel + conv_shift_qk_kernel<1>)",
                                 "achieved": dec_gbs, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                                 "frac": dec_gbs * 1e9 / PEAK_HBM,
                                 "traffic": _sum_or_none(load_traffic("decode", digest),
