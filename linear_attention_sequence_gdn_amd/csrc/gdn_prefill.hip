@@ -693,8 +693,14 @@ struct ChainBuf {
     static constexpr int kV = kRec + (int)kRecBytes;
     static constexpr int kBytes = kV + kVTileRows * kD * 2;
 };
+// 16-column tiles of the state per wave: 1 gives eight waves of 16 columns
+// (two per SIMD, which hide each other's latencies), 2 gives four waves of 32.
+constexpr int kChainCT = 1;
+constexpr int kChainWaves = 8 / kChainCT;
+constexpr int kChainThreads = 64 * kChainWaves;
+constexpr int kCW = 16 * kChainCT;                      // state columns (and v channels) per wave
 constexpr int kChainStageRows = 16;                    // token rows per output staging round
-constexpr int kChainStage = kChainStageRows * 32 * 2;  // output staging of one wave (bf16)
+constexpr int kChainStage = kChainStageRows * kCW * 2;  // output staging of one wave (bf16)
 
 // k^ tile: 64 token rows of 256 bytes whose 16-byte pieces are stored
 // permuted by a bit shuffle of the row index, ksw(R) = (r3, r1, r0, r2).  It
@@ -774,22 +780,42 @@ __device__ __forceinline__ void chain_dma_v(const ChainDma &d, uint8_t *buf, int
         __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rv, (lds_void_t *)dst, 16, (R - 4) * d.ldb + piece * 16, 0, 0, 0);
 }
 
+// k^ rows 4f .. 4f+3: lane L fills slot L % 16 of row R = 4f + L / 16
+__device__ __forceinline__ void chain_dma_k(const ChainDma &d, uint8_t *buf, int f, int lane)
+{
+    const int R = 4 * f + (lane >> 4), piece = ((lane & 15) ^ ksw(R)) & 15;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rk, (lds_void_t *)(buf + ChainBuf::kK + f * 1024), 16,
+                                             R * 256 + piece * 16, 0, 0, 0);
+}
+
 template <int I>
 __device__ __forceinline__ void chain_dma_group(const ChainDma &d, uint8_t *buf, int wave, int lane)
 {
-    const int f = 4 * I + wave, v16 = lane * 16;
-    {
-        // k^ rows 4f .. 4f+3: lane L fills slot L % 16 of row R = 4f + L / 16
-        const int R = 4 * f + (lane >> 4), piece = ((lane & 15) ^ ksw(R)) & 15;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rk, (lds_void_t *)(buf + ChainBuf::kK + f * 1024), 16,
-                                                 R * 256 + piece * 16, 0, 0, 0);
+    const int v16 = lane * 16;
+    if constexpr (kChainWaves == 4) {
+        const int f = 4 * I + wave;
+        chain_dma_k(d, buf, f, lane);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rq, (lds_void_t *)(buf + ChainBuf::kQ + f * 1024), 16, v16, f * 1024, 0, 0);
+        chain_dma_v(d, buf, f, lane);
+        // head record: 13 pieces (P 0-5, T' 6-11, gates 12)
+        if (I < 3 || wave == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rh, (lds_void_t *)(buf + ChainBuf::kRec + f * 1024), 16, v16, f * 1024, 0, 0);
+        if (I == 1 && wave == 3) chain_dma_v(d, buf, 16, lane);
+    } else {
+        // eight waves: group 0 k^, 1 q^, 2 raw v, 3 the head record; pieces
+        // wave and wave + 8 of each
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int f = 8 * jj + wave;
+            if (I == 0) chain_dma_k(d, buf, f, lane);
+            if (I == 1)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rq, (lds_void_t *)(buf + ChainBuf::kQ + f * 1024), 16, v16, f * 1024, 0, 0);
+            if (I == 2) chain_dma_v(d, buf, f, lane);
+            if (I == 3 && f < 13)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rh, (lds_void_t *)(buf + ChainBuf::kRec + f * 1024), 16, v16, f * 1024, 0, 0);
+        }
+        if (I == 2 && wave == 0) chain_dma_v(d, buf, 16, lane);
     }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rq, (lds_void_t *)(buf + ChainBuf::kQ + f * 1024), 16, v16, f * 1024, 0, 0);
-    chain_dma_v(d, buf, f, lane);
-    // head record: 13 pieces (P 0-5, T' 6-11, gates 12)
-    if (I < 3 || wave == 0)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rh, (lds_void_t *)(buf + ChainBuf::kRec + f * 1024), 16, v16, f * 1024, 0, 0);
-    if (I == 1 && wave == 3) chain_dma_v(d, buf, 16, lane);
 }
 
 __device__ __forceinline__ void chain_dma(const PrefillArgs &p, const Workspace &ws, const ChainRun &run,
@@ -827,7 +853,7 @@ __device__ __forceinline__ bf16x8 conv_tap_frag(const uint16_t *__restrict__ w, 
 __device__ __forceinline__ bf16x8 conv_row_frag(const uint8_t *vt, int rt, int x, int m, int wave, int lane)
 {
     const int q4 = lane >> 4, r = lane & 15;
-    const int byte = (32 * wave + 16 * x + 4 * q4) * 2;
+    const int byte = (kCW * wave + 16 * x + 4 * q4) * 2;
     const int R = 16 * rt + r + 1 + 2 * m;
     typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
     const u32x2 lo = *reinterpret_cast<const u32x2 *>(vt + vtile_offset(R, byte));
@@ -885,7 +911,7 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4)
 // into the row staging).  The fragment layout is the same for A and B
 // operands, so the packed state and Vnew serve as A operands unchanged.
 __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace &ws, uint8_t *cur, uint8_t *nxt,
-                                           uint8_t *stage, f32x4 (&S)[8][2], const bf16x8 (&wb)[2][2],
+                                           uint8_t *stage, f32x4 (&S)[8][kChainCT], const bf16x8 (&wb)[kChainCT][2],
                                            const ChainRun &run, int cc, int h, int g, int wave, int lane)
 {
     const int Hv = p.Hv;
@@ -906,11 +932,11 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
     const uint8_t *vt = cur + ChainBuf::kV;
 
     // conv of v at the wave's channels (pre-activation), on the matrix cores
-    f32x4 Z[4][2];
+    f32x4 Z[4][kChainCT];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
+        for (int x = 0; x < kChainCT; ++x) {
             Z[rt][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(conv_row_frag(vt, rt, x, 0, wave, lane), wb[x][0],
                                                                f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             Z[rt][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(conv_row_frag(vt, rt, x, 1, wave, lane), wb[x][1],
@@ -921,11 +947,11 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
     // fragments of block kb+1 are read while block kb multiplies, the next
     // chunk's DMA goes out one group per block, and SiLU of a quarter of the
     // conv runs on the vector ALUs meanwhile
-    f32x4 X[4][2], QST[2][4];
+    f32x4 X[4][kChainCT], QST[kChainCT][4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
+        for (int x = 0; x < kChainCT; ++x) {
             X[rt][x] = f32x4{0.f, 0.f, 0.f, 0.f};
             QST[x][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
@@ -942,19 +968,17 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
         if (kb == 2) chain_dma_group<2>(dn, nxt, wave, lane);
         if (kb == 3) chain_dma_group<3>(dn, nxt, wave, lane);
         __builtin_amdgcn_sched_barrier(0);
-        const half8 sb0 = pack_h8(S[2 * kb][0], S[2 * kb + 1][0]);
-        const half8 sb1 = pack_h8(S[2 * kb][1], S[2 * kb + 1][1]);
+        half8 sb[kChainCT];
 #pragma unroll
-        for (int sl = 0; sl < 16; ++sl) {
-            const int rt = sl >> 2;
-            switch (sl & 3) {
-            case 0: X[rt][0] = mfma16(ak[rt], sb0, X[rt][0]); break;
-            case 1: X[rt][1] = mfma16(ak[rt], sb1, X[rt][1]); break;
-            case 2: QST[0][rt] = mfma16(sb0, aq[rt], QST[0][rt]); break;
-            default: QST[1][rt] = mfma16(sb1, aq[rt], QST[1][rt]); break;
-            }
-            // SiLU of conv tile (kb, x = sl / 8), one value per slot
-            if (sl < 8) Z[kb][sl >> 2][sl & 3] = silu_f(Z[kb][sl >> 2][sl & 3]);
+        for (int x = 0; x < kChainCT; ++x) sb[x] = pack_h8(S[2 * kb][x], S[2 * kb + 1][x]);
+        // per token tile: the X products of the wave's column tiles, then the
+        // (Q S)^T ones; SiLU of conv tile kb, one value per slot
+#pragma unroll
+        for (int sl = 0; sl < 8 * kChainCT; ++sl) {
+            const int rt = sl / (2 * kChainCT), r = sl % (2 * kChainCT);
+            if (r < kChainCT) X[rt][r] = mfma16(ak[rt], sb[r], X[rt][r]);
+            else QST[r - kChainCT][rt] = mfma16(sb[r - kChainCT], aq[rt], QST[r - kChainCT][rt]);
+            if (sl < 4 * kChainCT) Z[kb][sl >> 2][sl & 3] = silu_f(Z[kb][sl >> 2][sl & 3]);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -963,22 +987,22 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
     half8 tf[6];
 #pragma unroll
     for (int i = 0; i < 6; ++i) tf[i] = Tf[i * 64];
-    f32x4 Vn[4][2];
+    f32x4 Vn[4][kChainCT];
     {
         f32x4 gg[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) gg[rt] = *reinterpret_cast<const f32x4 *>(gt + 192 + 16 * rt + 4 * q4);
-        half8 yb[2][2];
+        half8 yb[2][kChainCT];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
+            for (int x = 0; x < kChainCT; ++x)
                 yb[tb][x] = pack_h8(Z[2 * tb][x] - gg[2 * tb] * X[2 * tb][x],
                                     Z[2 * tb + 1][x] - gg[2 * tb + 1] * X[2 * tb + 1][x]);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-            for (int x = 0; x < 2; ++x) {
+            for (int x = 0; x < kChainCT; ++x) {
                 Vn[rt][x] = mfma16(tf[tri_frag(rt, 0)], yb[0][x], f32x4{0.f, 0.f, 0.f, 0.f});
                 if (rt >= 2) Vn[rt][x] = mfma16(tf[tri_frag(rt, 1)], yb[1][x], Vn[rt][x]);
             }
@@ -1002,11 +1026,11 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
     const float gn = gt[128];
     __builtin_amdgcn_sched_barrier(0);
     // Vnew and (Gam_n / Gam) Vnew as operands over the chunk's two 32-token blocks
-    half8 vb[2][2], vr[2][2];
+    half8 vb[2][kChainCT], vr[2][kChainCT];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
+        for (int x = 0; x < kChainCT; ++x) {
             vb[tb][x] = pack_h8(Vn[2 * tb][x], Vn[2 * tb + 1][x]);
             vr[tb][x] = pack_h8(Vn[2 * tb][x] * rg[2 * tb], Vn[2 * tb + 1][x] * rg[2 * tb + 1]);
         }
@@ -1026,7 +1050,7 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
         for (int i = 0; i < 2; ++i) {
             const int dt = 2 * pr + i;
 #pragma unroll
-            for (int x = 0; x < 2; ++x) {
+            for (int x = 0; x < kChainCT; ++x) {
                 S[dt][x] = mfma16(kf[cb][i][0], vr[0][x], S[dt][x] * gn);
                 S[dt][x] = mfma16(kf[cb][i][1], vr[1][x], S[dt][x]);
             }
@@ -1042,26 +1066,32 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
     const int n = cc >= run.c_out ? min(kChunk, run.L - rel) : 0;
     const int rowb = Hv * kD * 2;  // bytes per token row of o
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-        p.o + ((long)(run.t0 + rel) * Hv + h) * kD + 32 * wave, 0, n * rowb, 0x00020000);
+        p.o + ((long)(run.t0 + rel) * Hv + h) * kD + kCW * wave, 0, n * rowb, 0x00020000);
     uint16_t *os = reinterpret_cast<uint16_t *>(stage);
     static_assert(kChainStageRows == 16, "one token tile per staging round");
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
+        for (int x = 0; x < kChainCT; ++x) {
             f32x4 acc = mfma16(vb[0][x], pf[tri_frag(rt, 0)], QST[x][rt] * gm[rt]);
             if (rt >= 2) acc = mfma16(vb[1][x], pf[tri_frag(rt, 1)], acc);
             typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
             const u32x2 v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-            *reinterpret_cast<u32x2 *>(os + c16 * 32 + 16 * x + 4 * q4) = v;
+            *reinterpret_cast<u32x2 *>(os + c16 * kCW + 16 * x + 4 * q4) = v;
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // 16 rows of 64 bytes: lane -> (row lane/4, 16-byte piece lane%4)
+        // 16 rows of 2 kCW bytes: lane -> (row lane/4, piece lane%4 of kCW/2 bytes)
         const int row = lane >> 2, piece = lane & 3;
-        const i32x4 v = *reinterpret_cast<const i32x4 *>(stage + row * 64 + piece * 16);
-        __builtin_amdgcn_raw_buffer_store_b128(v, ro, (16 * rt + row) * rowb + piece * 16, 0, 0);
+        if constexpr (kChainCT == 2) {
+            const i32x4 v = *reinterpret_cast<const i32x4 *>(stage + row * 64 + piece * 16);
+            __builtin_amdgcn_raw_buffer_store_b128(v, ro, (16 * rt + row) * rowb + piece * 16, 0, 0);
+        } else {
+            typedef int i32x2 __attribute__((ext_vector_type(2)));
+            const i32x2 v = *reinterpret_cast<const i32x2 *>(stage + row * 32 + piece * 8);
+            __builtin_amdgcn_raw_buffer_store_b64(v, ro, (16 * rt + row) * rowb + piece * 8, 0, 0);
+        }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -1070,8 +1100,9 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
 
 // The chunks of one run, the state carried in registers.
 __device__ __forceinline__ void chain_run(const PrefillArgs &p, const Workspace &ws, uint8_t *buf0, uint8_t *buf1,
-                                          uint8_t *stage, f32x4 (&S)[8][2], const bf16x8 (&wb)[2][2],
-                                          const ChainRun &run, int h, int g, int wave, int lane)
+                                          uint8_t *stage, f32x4 (&S)[8][kChainCT],
+                                          const bf16x8 (&wb)[kChainCT][2], const ChainRun &run, int h, int g, int wave,
+                                          int lane)
 {
     if (run.c_to <= run.c_from) return;
     chain_dma(p, ws, run, buf0, run.c_from, h, g, wave, lane);
@@ -1123,34 +1154,34 @@ __device__ __forceinline__ int warm_start(const Workspace &ws, int h, int Hv, in
 
 // state columns 32w .. 32w+31 of one (sequence, head): tile (dt, x) element e
 // is row 16dt + 4q + e, column 32w + 16x + c16
-__device__ __forceinline__ void state_load(f32x4 (&S)[8][2], const float *src, int wave, int lane)
+__device__ __forceinline__ void state_load(f32x4 (&S)[8][kChainCT], const float *src, int wave, int lane)
 {
     const int q4 = lane >> 4, c16 = lane & 15;
     if (!src) {
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-            for (int x = 0; x < 2; ++x) S[dt][x] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int x = 0; x < kChainCT; ++x) S[dt][x] = f32x4{0.f, 0.f, 0.f, 0.f};
         return;
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
+        for (int x = 0; x < kChainCT; ++x)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                S[dt][x][e] = src[(long)(16 * dt + 4 * q4 + e) * kD + 32 * wave + 16 * x + c16];
+                S[dt][x][e] = src[(long)(16 * dt + 4 * q4 + e) * kD + kCW * wave + 16 * x + c16];
 }
-__device__ __forceinline__ void state_store(const f32x4 (&S)[8][2], float *dst, int wave, int lane)
+__device__ __forceinline__ void state_store(const f32x4 (&S)[8][kChainCT], float *dst, int wave, int lane)
 {
     const int q4 = lane >> 4, c16 = lane & 15;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
+        for (int x = 0; x < kChainCT; ++x)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                dst[(long)(16 * dt + 4 * q4 + e) * kD + 32 * wave + 16 * x + c16] = S[dt][x][e];
+                dst[(long)(16 * dt + 4 * q4 + e) * kD + kCW * wave + 16 * x + c16] = S[dt][x][e];
 }
 
 // Sequential pass.  kRepair = false: one workgroup per (segment, V head);
@@ -1160,12 +1191,12 @@ __device__ __forceinline__ void state_store(const f32x4 (&S)[8][2], float *dst, 
 // over, those whose warm-up bound was not met; for in-place calls it also
 // hands each sequence of several segments its final state.
 template <bool kRepair>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kChainThreads) __attribute__((amdgpu_waves_per_eu(kChainWaves / 4, kChainWaves / 4)))
 void chain_kernel(PrefillArgs p, Workspace ws)
 {
     __shared__ __attribute__((aligned(16))) uint8_t buf0[ChainBuf::kBytes];
     __shared__ __attribute__((aligned(16))) uint8_t buf1[ChainBuf::kBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t stage_all[4 * kChainStage];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_all[kChainWaves * kChainStage];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     uint8_t *stage = stage_all + wave * kChainStage;
@@ -1179,12 +1210,13 @@ void chain_kernel(PrefillArgs p, Workspace ws)
     const int unit = gu / Hqk, g = gu % Hqk;
     const int h = g * G + j;
     const long C_tot = 2L * Hqk * kD + (long)Hv * kD, cv = 2L * Hqk * kD + (long)h * kD;
-    // conv taps of the wave's two channel tiles
-    const bf16x8 wb[2][2] = {{conv_tap_frag(p.conv_w, cv + 32 * wave + (lane & 15), 0, lane),
-                              conv_tap_frag(p.conv_w, cv + 32 * wave + (lane & 15), 1, lane)},
-                             {conv_tap_frag(p.conv_w, cv + 32 * wave + 16 + (lane & 15), 0, lane),
-                              conv_tap_frag(p.conv_w, cv + 32 * wave + 16 + (lane & 15), 1, lane)}};
-    f32x4 S[8][2];
+    // conv taps of the wave's channel tiles
+    bf16x8 wb[kChainCT][2];
+#pragma unroll
+    for (int x = 0; x < kChainCT; ++x)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) wb[x][m] = conv_tap_frag(p.conv_w, cv + kCW * wave + 16 * x + (lane & 15), m, lane);
+    f32x4 S[8][kChainCT];
 
     if (!kRepair) {
         const int k = unit;
@@ -1357,12 +1389,12 @@ hipError_t launch_prefill(const PrefillArgs &p, void *workspace, hipStream_t str
     const int G = p.Hv / p.Hqk;
     const long seg_groups = (long)p.max_segs * p.Hqk;
     const long seg_blocks = ((seg_groups + 7) / 8) * 8L * G;
-    hipLaunchKernelGGL(chain_kernel<false>, dim3((unsigned)seg_blocks), dim3(256), 0, stream, p, ws);
+    hipLaunchKernelGGL(chain_kernel<false>, dim3((unsigned)seg_blocks), dim3(kChainThreads), 0, stream, p, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(3)) != hipSuccess) return e;
     const long groups = (long)p.N * p.Hqk;
     const long blocks = ((groups + 7) / 8) * 8L * G;
-    hipLaunchKernelGGL(chain_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, p, ws);
+    hipLaunchKernelGGL(chain_kernel<true>, dim3((unsigned)blocks), dim3(kChainThreads), 0, stream, p, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return mark(4);
 }
