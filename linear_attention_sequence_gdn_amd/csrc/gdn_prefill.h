@@ -37,10 +37,10 @@ inline int max_chunks_varlen(int N, int T_tot)
 
 // Per-chunk hand-over from the parallel prep pass to the sequential pass, in
 // bytes.  The fp16 operands are stored in the register order of the
-// matrix-core instruction that consumes them, k^ as plain rows.
+// matrix-core instruction that consumes them.
 constexpr size_t kFragBytes = 64 * 16;               // one 16x32 fp16 operand
 constexpr size_t kQFragBytes = 16 * kFragBytes;      // q^ of a chunk     [64 x 128]
-constexpr size_t kKRowBytes = 64 * 128 * 2;         // k^ of a chunk     [64 x 128], row-major
+constexpr size_t kKFragBytes = 16 * kFragBytes;      // k^ of a chunk     [64 x 128]
 // Per (chunk, V head) record: P, T', gates.  The two lower-triangular 64 x 64
 // matrices keep the six 16x32 fragments that are not structurally zero: (row
 // tile, key block) (0,0) (1,0) (2,0) (2,1) (3,0) (3,1), in that order.  Gate
@@ -58,7 +58,7 @@ struct Workspace {
     int4 *seq_info;     // [N] {chunk0, nchunks, t0, L}
     int *order;         // [N] sequences, longest first
     uint8_t *qfrag;     // [max_chunks][Hqk]
-    uint8_t *krow;      // [max_chunks][Hqk]  k^, token rows of 128 fp16
+    uint8_t *kfrag;     // [max_chunks][Hqk]  k^ (token rows, d contraction)
     uint8_t *hrec;      // [max_chunks][Hv] P, T', gates
     int4 *seg_info;     // [max_segs] {seq, first chunk, end chunk, 1: first of seq | 2: last of seq}; seq -1 = unused
     int4 *seq_seg;      // [N] {first segment, segments, -, -}

@@ -469,22 +469,18 @@ void prep_kernel(PrefillArgs p, Workspace ws)
     }
     __syncthreads();
     // ---- operands of the sequential pass (q^ fragments of row tile `wave`,
-    //      k^ rows), then the lower 16 x 16 tiles of K K^T and K Q^T, five per
+    //      k^ fragments), then the lower 16 x 16 tiles of K K^T and K Q^T, five per
     //      wave: K K^T tile (rt, ct) with ct <= rt, and K Q^T tile (query rt,
     //      key jt) with jt <= rt, kept in registers for every head
     f32x4 kk[3], kq[3];
     const int nkk = wave < 2 ? 3 : 2, nkq = wave < 2 ? 2 : 3;
     {
         half8 *qf = reinterpret_cast<half8 *>(ws.qfrag + gc * kQFragBytes);
+        half8 *kf = reinterpret_cast<half8 *>(ws.kfrag + gc * kKFragBytes);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) qf[(wave * 4 + kb) * 64 + lane] = lds_frag(Qs, kQ_LD, 16 * wave, 32 * kb, lane);
-        // k^ rows: 64 rows of 256 bytes, 16 bytes per thread and pass
-        uint8_t *kr = ws.krow + gc * kKRowBytes;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int piece = t + kPrepThreads * i, row = piece >> 4, col = piece & 15;
-            *reinterpret_cast<i32x4 *>(kr + row * 256 + col * 16) =
-                *reinterpret_cast<const i32x4 *>(Ks + row * kQ_LD + col * 8);
+        for (int kb = 0; kb < 4; ++kb) {
+            qf[(wave * 4 + kb) * 64 + lane] = lds_frag(Qs, kQ_LD, 16 * wave, 32 * kb, lane);
+            kf[(wave * 4 + kb) * 64 + lane] = lds_frag(Ks, kQ_LD, 16 * wave, 32 * kb, lane);
         }
 #pragma unroll
         for (int i = 0; i < 3; ++i) {
@@ -687,7 +683,7 @@ void prep_kernel(PrefillArgs p, Workspace ws)
 constexpr int kChainBlocksPerHead = 1;
 constexpr int kVTileRows = 68;  // raw v rows of a chunk: 1 unused, 3 before the chunk, 64
 struct ChainBuf {
-    // k^ rows, q^ (operand order), the head record (P, T', gates), raw v
+    // k^, q^ (operand order), the head record (P, T', gates), raw v
     static constexpr int kK = 0, kQ = 16384, kRec = 32768;
     static constexpr int kP = kRec + (int)kRecP, kT = kRec + (int)kRecT, kG = kRec + (int)kRecG;
     static constexpr int kV = kRec + (int)kRecBytes;
@@ -702,20 +698,14 @@ constexpr int kCW = 16 * kChainCT;                      // state columns (and v 
 constexpr int kChainStageRows = 16;                    // token rows per output staging round
 constexpr int kChainStage = kChainStageRows * kCW * 2;  // output staging of one wave (bf16)
 
-// k^ tile: 64 token rows of 256 bytes whose 16-byte pieces are stored
-// permuted by a bit shuffle of the row index, ksw(R) = (r3, r1, r0, r2).  It
-// is a bijection on R mod 16, so the sixteen consecutive rows of a token-major
-// operand hit sixteen bank groups; and for four consecutive rows (r0, r1 free)
-// and two adjacent pieces (bit 0 free) it is one-to-one as well, which is
-// what the transposed reads of the d-major operand touch at once.
-__device__ __forceinline__ int ksw(int R)
-{
-    return (R & 8) | ((R & 2) << 1) | ((R & 1) << 1) | ((R >> 2) & 1);
-}
-__device__ __forceinline__ int ktile_offset(int R, int byte_in_row)
-{
-    return R * (kD * 2) + ((((byte_in_row >> 4) ^ ksw(R)) & 15) << 4) + (byte_in_row & 15);
-}
+// k^ in LDS: the sixteen operand fragments (token tile rt, d block kb) in
+// order, the 64 16-byte lane slots of each stored permuted: lane (q, r)
+// (row r of the tile, d = 32kb + 4q .. +3 and +16) sits in slot
+// 16q + (r ^ 4q).  A fragment read touches all 64 slots, so any permutation
+// is conflict-free; the permutation makes the transposed reads of the
+// d-major operand conflict-free too (their sixteen lanes touch four rows r
+// and the four slots q of each).
+__device__ __forceinline__ int kslot(int q4, int r) { return 16 * q4 + (r ^ (4 * q4)); }
 
 // Raw v tile: tile row R holds chunk row R - 4 (rows 1..3: the three rows
 // before the chunk); its 16-byte pieces are stored XOR-swizzled by R mod 16,
@@ -764,7 +754,7 @@ __device__ __forceinline__ ChainDma chain_dma_plan(const PrefillArgs &p, const W
         first ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(run.hist), 0, run.hist ? 3 * ldc : 0,
                                                   0x00020000)
               : __builtin_amdgcn_make_buffer_rsrc(vc - 3 * (ldb / 2), 0, 3 * ldb, 0x00020000);
-    return ChainDma{region_rsrc(ws.krow + gc * kKRowBytes), region_rsrc(ws.qfrag + gc * kQFragBytes),
+    return ChainDma{region_rsrc(ws.kfrag + gc * kKFragBytes), region_rsrc(ws.qfrag + gc * kQFragBytes),
                     region_rsrc(ws.hrec + hc * kRecBytes), rv, rvh, ldb, first ? ldc : ldb};
 }
 
@@ -780,12 +770,13 @@ __device__ __forceinline__ void chain_dma_v(const ChainDma &d, uint8_t *buf, int
         __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rv, (lds_void_t *)dst, 16, (R - 4) * d.ldb + piece * 16, 0, 0, 0);
 }
 
-// k^ rows 4f .. 4f+3: lane L fills slot L % 16 of row R = 4f + L / 16
+// k^ fragment f: LDS slot L receives lane (L / 16, (L % 16) ^ 4 (L / 16)) of
+// the fragment, the lane that kslot places there
 __device__ __forceinline__ void chain_dma_k(const ChainDma &d, uint8_t *buf, int f, int lane)
 {
-    const int R = 4 * f + (lane >> 4), piece = ((lane & 15) ^ ksw(R)) & 15;
+    const int q4 = lane >> 4, r = (lane & 15) ^ (4 * q4);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rk, (lds_void_t *)(buf + ChainBuf::kK + f * 1024), 16,
-                                             R * 256 + piece * 16, 0, 0, 0);
+                                             f * 1024 + (16 * q4 + r) * 16, 0, 0, 0);
 }
 
 template <int I>
@@ -862,29 +853,27 @@ __device__ __forceinline__ bf16x8 conv_row_frag(const uint8_t *vt, int rt, int x
     return __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], hi[0], hi[1]});
 }
 
-// k^ as the A operand of K S (token tile rt, d block kb): lane (q, r) takes
-// token 16rt + r, d = 32kb + 4q .. +3 and 32kb + 16 + 4q .. +3
+// k^ as the A operand of K S (token tile rt, d block kb): one 16-byte read
 __device__ __forceinline__ half8 ktile_frag(const uint8_t *kt, int rt, int kb, int lane)
 {
-    const int q4 = lane >> 4, r = lane & 15, R = 16 * rt + r;
-    const half4 lo = *reinterpret_cast<const half4 *>(kt + ktile_offset(R, (32 * kb + 4 * q4) * 2));
-    const half4 hi = *reinterpret_cast<const half4 *>(kt + ktile_offset(R, (32 * kb + 16 + 4 * q4) * 2));
-    return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return *reinterpret_cast<const half8 *>(kt + (rt * 4 + kb) * 1024 + kslot(lane >> 4, lane & 15) * 16);
 }
 
 // k^T as the A operand of the state update (d tile dt, token block tb):
 // lane (q, r) needs d = 16dt + r at tokens 32tb + 4q .. +3 and 32tb + 16 + 4q
 // .. +3.  A transposed read hands lane i of each 16-lane group element i % 4
 // of the 8 bytes that lane 4j + i / 4 of the group addressed, as its element
-// j; so lane s of group q addresses token row 32tb + 4q + s / 4, d columns
-// 16dt + 4 (s % 4) .. +3.
+// j; so lane s of group q addresses token row R = 32tb + 4q + s / 4, d
+// columns 16dt + 4 (s % 4) .. +3: the half dt % 2 of slot (s % 4, R % 16) of
+// fragment (R / 16, dt / 2).
 __device__ __forceinline__ half8 ktile_frag_t(const uint8_t *kt, int dt, int tb, int lane)
 {
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     const int q4 = lane >> 4, s = lane & 15;
-    const int R = 32 * tb + 4 * q4 + (s >> 2), byte = (16 * dt + 4 * (s & 3)) * 2;
-    const uint8_t *p0 = kt + ktile_offset(R, byte), *p1 = kt + ktile_offset(R + 16, byte);
+    const int R = 32 * tb + 4 * q4 + (s >> 2);
+    const uint8_t *p0 = kt + ((R >> 4) * 4 + (dt >> 1)) * 1024 + kslot(s & 3, R & 15) * 16 + 8 * (dt & 1);
+    const uint8_t *p1 = p0 + 4 * 1024;  // token rows + 16: the next token tile
     const half4 lo = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                                    (lds_s16x4 *)(__attribute__((address_space(3))) uint8_t *)(p0)));
     const half4 hi = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -1335,7 +1324,7 @@ size_t prefill_workspace_bytes(int max_chunks, int N, int Hqk, int Hv)
     total += align256((size_t)N * sizeof(int4));
     total += align256((size_t)N * sizeof(int));
     total += align256(C * Hqk * kQFragBytes);
-    total += align256(C * Hqk * kKRowBytes);
+    total += align256(C * Hqk * kKFragBytes);
     total += align256(C * Hv * kRecBytes);
     total += align256(M * sizeof(int4));
     total += align256((size_t)N * sizeof(int4));
@@ -1359,7 +1348,7 @@ Workspace carve_workspace(void *base, int max_chunks, int N, int Hqk, int Hv)
     ws.seq_info = reinterpret_cast<int4 *>(take((size_t)N * sizeof(int4)));
     ws.order = reinterpret_cast<int *>(take((size_t)N * sizeof(int)));
     ws.qfrag = take(C * Hqk * kQFragBytes);
-    ws.krow = take(C * Hqk * kKRowBytes);
+    ws.kfrag = take(C * Hqk * kKFragBytes);
     ws.hrec = take(C * Hv * kRecBytes);
     ws.seg_info = reinterpret_cast<int4 *>(take(M * sizeof(int4)));
     ws.seq_seg = reinterpret_cast<int4 *>(take((size_t)N * sizeof(int4)));
