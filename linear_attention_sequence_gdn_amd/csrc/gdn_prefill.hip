@@ -69,29 +69,6 @@ __device__ __forceinline__ half8 lds_frag(const _Float16 *M, int ld, int r0, int
 
 __device__ __forceinline__ uint32_t ld_pair(const uint16_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
 
-// Raw rows r0-3 .. r0+15 of channels (2*pp, 2*pp+1) of one 128-channel plane
-// for the causal width-4 conv.  x points at the chunk's first token (row
-// stride ld); rows < 0 come from the previous chunk of the same sequence
-// (first == false), from the carried conv rows `hist` (row stride C_tot), or
-// are zero.  Rows >= n are padding and read as zero.
-__device__ __forceinline__ void conv_window(const uint16_t *__restrict__ x, long ld, int n, bool first,
-                                            const uint16_t *hist, long C_tot, int pp, int r0, uint32_t (&win)[19])
-{
-#pragma unroll
-    for (int i = 0; i < 19; ++i) {
-        const int r = r0 - 3 + i;
-        uint32_t val = 0;
-        if (r >= 0) {
-            if (r < n) val = ld_pair(x + (long)r * ld + 2 * pp);
-        } else if (!first) {
-            val = ld_pair(x + (long)r * ld + 2 * pp);
-        } else if (hist) {
-            val = ld_pair(hist + (long)(3 + r) * C_tot + 2 * pp);
-        }
-        win[i] = val;
-    }
-}
-
 // Conv taps of channels (2*pp, 2*pp+1), tap 3 = current token
 struct ConvW {
     float a[4], b[4];
@@ -120,14 +97,32 @@ __device__ __forceinline__ void conv_silu(const uint32_t (&win)[19], const ConvW
     }
 }
 
-__device__ __forceinline__ void conv_plane(const uint16_t *__restrict__ x, long ld, int n, bool first,
-                                           const uint16_t *hist, long C_tot,
-                                           const uint16_t *__restrict__ w, int pp, int r0,
-                                           float (&z0)[16], float (&z1)[16])
+// Raw rows r0-3 .. r0+15 of channels (2*pp, 2*pp+1) of one 128-channel plane
+// for the causal width-4 conv (one bf16 pair per row), through range-checked
+// buffer loads without branches.  x points at the chunk's first token; one
+// range covers the rows taken from x (the chunk's n rows, and the three
+// before unless the chunk starts the sequence) and rows outside it read as
+// zero.  The three earlier rows of a sequence's first chunk come from the
+// carried conv rows `hist` (zeros without them), selected per row so that
+// each register receives one load.  ldb / ldh: bytes per row of x / of hist.
+__device__ __forceinline__ void conv_window_rc(const uint16_t *x, int ldb, int n, bool first, const uint16_t *hist,
+                                               int ldh, int pp, int r0, uint32_t (&win)[19])
 {
-    uint32_t win[19];
-    conv_window(x, ld, n, first, hist, C_tot, pp, r0, win);
-    conv_silu(win, conv_weights(w, pp), r0, n, z0, z1);
+    const int lo = first ? 0 : -3;  // first row taken from x
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(x) + (long)lo * (ldb / 2), 0, (n - lo) * ldb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rh =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(hist), 0, hist ? 3 * ldh : 0, 0x00020000);
+    const int voff = (r0 - 3 - lo) * ldb + 4 * pp;  // negative offsets fail the range check too
+    const bool carried = first && r0 == 0;
+#pragma unroll
+    for (int i = 0; i < 19; ++i) {
+        if (i < 3)
+            win[i] = __builtin_amdgcn_raw_buffer_load_b32(carried ? rh : rx,
+                                                          carried ? 4 * pp + i * ldh : voff + i * ldb, 0, 0);
+        else
+            win[i] = __builtin_amdgcn_raw_buffer_load_b32(rx, voff + i * ldb, 0, 0);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -451,8 +446,12 @@ void prep_kernel(PrefillArgs p, Workspace ws)
         for (int plane = 0; plane < 2; ++plane) {
             const long ch0 = plane == 0 ? (long)g * kD : (long)Hqk * kD + (long)g * kD;
             const uint16_t *x = (plane == 0 ? p.q : p.k) + (long)t0 * ldqk + (long)g * kD;
-            conv_plane(x, ldqk, n, first, hist ? hist + ch0 : nullptr, C_tot, p.conv_w + ch0 * 4, lane, r0,
-                       z0, z1);
+            {
+                uint32_t win[19];
+                conv_window_rc(x, (int)ldqk * 2, n, first, hist ? hist + ch0 : nullptr, (int)C_tot * 2, lane, r0,
+                               win);
+                conv_silu(win, conv_weights(p.conv_w + ch0 * 4, lane), r0, n, z0, z1);
+            }
             float ss[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) ss[i] = z0[i] * z0[i] + z1[i] * z1[i];
@@ -461,9 +460,9 @@ void prep_kernel(PrefillArgs p, Workspace ws)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float inv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inv_mine), 4 * i));
-                const _Float16 h0 = (_Float16)(z0[i] * inv), h1 = (_Float16)(z1[i] * inv);
-                dst[(r0 + i) * kQ_LD + 2 * lane] = h0;
-                dst[(r0 + i) * kQ_LD + 2 * lane + 1] = h1;
+                typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+                *reinterpret_cast<half2_t *>(dst + (r0 + i) * kQ_LD + 2 * lane) =
+                    half2_t{(_Float16)(z0[i] * inv), (_Float16)(z1[i] * inv)};
             }
         }
     }
