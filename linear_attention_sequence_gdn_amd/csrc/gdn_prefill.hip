@@ -393,13 +393,16 @@ static_assert(64 * kQ_LD * 2 <= kPrepTile, "a token-major q^ / k^ tile fits in a
 
 
 // Lower 16 x 16 tiles of K K^T (row tile, column tile) and of K Q^T (query
-// tile, key tile) computed by each wave: five per wave.  The K Q^T tiles of a
-// P fragment (query tile rt, key block kb) stay within one wave, except for
-// fragment (3, 1), whose two halves come from waves 2 and 3.
-__device__ constexpr int kPrepKK[4][3][2] = {{{0, 0}, {2, 1}, {3, 2}}, {{1, 0}, {2, 2}, {3, 3}},
-                                             {{1, 1}, {3, 0}, {0, 0}}, {{2, 0}, {3, 1}, {0, 0}}};
-__device__ constexpr int kPrepKQ[4][3][2] = {{{0, 0}, {2, 2}, {0, 0}}, {{1, 0}, {1, 1}, {0, 0}},
-                                             {{2, 0}, {2, 1}, {3, 2}}, {{3, 0}, {3, 1}, {3, 3}}};
+// tile, key tile) computed by each wave: five per wave.  Wave w's first K K^T
+// tile is the diagonal tile (w, w), whose block of the inverse the wave then
+// solves itself.  The K Q^T tiles of a P fragment (query tile rt, key block
+// kb) stay within one wave, except for fragment (3, 1), whose two halves come
+// from waves 1 and 3.
+__device__ constexpr int kPrepKK[4][3][2] = {{{0, 0}, {1, 0}, {3, 2}}, {{1, 1}, {2, 0}, {0, 0}},
+                                             {{2, 2}, {2, 1}, {3, 1}}, {{3, 3}, {3, 0}, {0, 0}}};
+__device__ constexpr int kPrepKQ[4][3][2] = {{{1, 0}, {1, 1}, {0, 0}}, {{0, 0}, {2, 2}, {3, 2}},
+                                             {{2, 0}, {2, 1}, {0, 0}}, {{3, 0}, {3, 1}, {3, 3}}};
+__device__ constexpr int kPrepNKK[4] = {3, 2, 3, 2}, kPrepNKQ[4] = {2, 3, 2, 3};
 
 // Four resident workgroups per CU (at most 128 VGPRs): the per-head phases
 // are short stretches between barriers, and other workgroups fill the waits.
@@ -472,7 +475,7 @@ void prep_kernel(PrefillArgs p, Workspace ws)
     //      wave: K K^T tile (rt, ct) with ct <= rt, and K Q^T tile (query rt,
     //      key jt) with jt <= rt, kept in registers for every head
     f32x4 kk[3], kq[3];
-    const int nkk = wave < 2 ? 3 : 2, nkq = wave < 2 ? 2 : 3;
+    const int nkk = kPrepNKK[wave], nkq = kPrepNKQ[wave];
     {
         half8 *qf = reinterpret_cast<half8 *>(ws.qfrag + gc * kQFragBytes);
         half8 *kf = reinterpret_cast<half8 *>(ws.kfrag + gc * kKFragBytes);
@@ -540,8 +543,8 @@ void prep_kernel(PrefillArgs p, Workspace ws)
             }
             // ---- P = (K Q^T)^T * D, lower incl. the diagonal -> global: each
             //      K Q^T tile gives half of a fragment (key tile jt: elements
-            //      4 (jt % 2) .. +3); wave 0 also writes the zero halves of
-            //      fragments (0, 0) and (2, 1)
+            //      4 (jt % 2) .. +3); a diagonal tile of an even key tile
+            //      (fragments (0, 0) and (2, 1)) also writes the zero half
             {
                 uint8_t *pf = ws.hrec + hc * kRecBytes + kRecP;
 #pragma unroll
@@ -558,12 +561,13 @@ void prep_kernel(PrefillArgs p, Workspace ws)
                     }
                     uint8_t *dst = pf + (tri_frag(rt, jt >> 1) * 64 + lane) * 16 + 8 * (jt & 1);
                     *reinterpret_cast<half4 *>(dst) = hv;
-                    if (wave == 0) *reinterpret_cast<half4 *>(dst + 8) = half4{0, 0, 0, 0};
+                    if (jt == rt && (jt & 1) == 0) *reinterpret_cast<half4 *>(dst + 8) = half4{0, 0, 0, 0};
                 }
             }
-            __syncthreads();
-            // ---- X = (I + A)^-1, blocked by 16.  Diagonal blocks by forward
-            //      substitution (wave b, block b).  Then, with L = I + A in
+            // ---- X = (I + A)^-1, blocked by 16.  Diagonal block b by forward
+            //      substitution, by wave b as soon as it has written the A
+            //      tile (b, b) (its own LDS writes, so a wave-level fence
+            //      suffices).  Then, with L = I + A in
             //      32 x 32 blocks, L^-1 = [[X_a, 0], [-X_b L_ba X_a, X_b]]:
             //      first the two 32 x 32 diagonal blocks (X_10, X_32) and, at
             //      the same time, the products that need only diagonal
@@ -572,6 +576,9 @@ void prep_kernel(PrefillArgs p, Workspace ws)
             //      most two dependent 16 x 16 products, on the fp32 matrix
             //      cores, with M kept in LDS between rounds.
             {  // wave b: diagonal block b, lane c (< 16): its column c
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                 float y[16];
                 const int bo = 16 * wave;
 #pragma unroll
