@@ -73,7 +73,7 @@ def test_ragged_lengths_with_carries(oracle_lib, T):
     compare(x, o, so, cso)
 
 
-@pytest.mark.parametrize("Hqk,Hv", [(1, 1), (4, 4), (2, 8), (3, 6)])
+@pytest.mark.parametrize("Hqk,Hv", [(1, 1), (4, 4), (2, 8), (3, 6), (1, 6), (2, 16)])
 def test_head_groupings(oracle_lib, Hqk, Hv):
     x = inputs.make_prefill(T_list=[150], Hqk=Hqk, Hv=Hv, seed=400 + Hv, state_std=0.05)
     o, so, cso = gpu_prefill(x, uniform_T=150)
