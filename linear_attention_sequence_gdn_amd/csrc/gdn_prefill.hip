@@ -81,19 +81,42 @@ __device__ __forceinline__ ConvW conv_weights(const uint16_t *__restrict__ w, in
                  {bf16_lo(wb.x), bf16_hi(wb.x), bf16_lo(wb.y), bf16_hi(wb.y)}};
 }
 
-// Conv + SiLU over a loaded window; rows >= n give 0.
+// Conv + SiLU over a loaded window; rows >= n give 0.  Each raw row is
+// unpacked once and added into the (up to) four outputs it reaches, in tap
+// order, so every output is the same chain of multiply-adds as the plain
+// four-term sum.  The mask is only applied in a partial chunk (wave-uniform).
 __device__ __forceinline__ void conv_silu(const uint32_t (&win)[19], const ConvW &cw, int r0, int n,
                                           float (&z0)[16], float (&z1)[16])
 {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float ya = cw.a[0] * bf16_lo(win[i]) + cw.a[1] * bf16_lo(win[i + 1]) +
-                         cw.a[2] * bf16_lo(win[i + 2]) + cw.a[3] * bf16_lo(win[i + 3]);
-        const float yb = cw.b[0] * bf16_hi(win[i]) + cw.b[1] * bf16_hi(win[i + 1]) +
-                         cw.b[2] * bf16_hi(win[i + 2]) + cw.b[3] * bf16_hi(win[i + 3]);
-        const bool valid = r0 + i < n;
-        z0[i] = valid ? silu_f(ya) : 0.0f;
-        z1[i] = valid ? silu_f(yb) : 0.0f;
+    for (int i = 0; i < 19; ++i) {
+        const float lo = bf16_lo(win[i]), hi = bf16_hi(win[i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = i - j;
+            if (r < 0 || r >= 16) continue;
+            if (j == 0) {
+                z0[r] = cw.a[0] * lo;
+                z1[r] = cw.b[0] * hi;
+            } else {
+                z0[r] = __builtin_fmaf(cw.a[j], lo, z0[r]);
+                z1[r] = __builtin_fmaf(cw.b[j], hi, z1[r]);
+            }
+        }
+    }
+    if (r0 + 16 <= n) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            z0[i] = silu_f(z0[i]);
+            z1[i] = silu_f(z1[i]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const bool valid = r0 + i < n;
+            z0[i] = valid ? silu_f(z0[i]) : 0.0f;
+            z1[i] = valid ? silu_f(z1[i]) : 0.0f;
+        }
     }
 }
 
@@ -414,7 +437,7 @@ void prep_kernel(PrefillArgs p, Workspace ws)
     __shared__ __attribute__((aligned(16))) uint8_t R0[kPrepTile];
     __shared__ __attribute__((aligned(16))) uint8_t R1[kPrepTile];
     __shared__ __attribute__((aligned(16))) float Msc[4 * 256];
-    __shared__ float s_gam2[4 * 64];
+    __shared__ __attribute__((aligned(16))) float s_gam2[4 * 64];
     __shared__ __attribute__((aligned(16))) float s_beta[4 * 64];
     _Float16 *Qs = reinterpret_cast<_Float16 *>(R0), *Ks = reinterpret_cast<_Float16 *>(R1);
     float *As = reinterpret_cast<float *>(R0), *Xs = reinterpret_cast<float *>(R1);
@@ -528,17 +551,23 @@ void prep_kernel(PrefillArgs p, Workspace ws)
         for (int jj = 0; jj < jn; ++jj) {
             const long hc = (long)c * Hv + g * G + j0 + jj;
             const float *gam2 = s_gam2 + 64 * jj, *beta = s_beta + 64 * jj;
-            // ---- A = strict_lower(diag(beta) K K^T * D) -> LDS
+            // ---- A = strict_lower(diag(beta) K K^T * D) -> LDS, without
+            //      branches (a lane's four rows are adjacent: one 16-byte read
+            //      each of gam and beta per tile); the upper parts of the
+            //      diagonal tiles, never read, get zero
 #pragma unroll
             for (int i = 0; i < 3; ++i) {
                 if (i >= nkk) continue;
                 const int rt = kPrepKK[wave][i][0], ct = kPrepKK[wave][i][1];
                 const int jc = 16 * ct + c16;
+                const f32x4 gr = *reinterpret_cast<const f32x4 *>(gam2 + 16 * rt + 4 * q4);
+                const f32x4 br = *reinterpret_cast<const f32x4 *>(beta + 16 * rt + 4 * q4);
                 const float gj = gam2[jc];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 16 * rt + 4 * q4 + e;
-                    if (r > jc) As[r * kAL + jc] = beta[r] * kk[i][e] * __builtin_amdgcn_exp2f(gam2[r] - gj);
+                    const float a = br[e] * kk[i][e] * __builtin_amdgcn_exp2f(gr[e] - gj);
+                    As[r * kAL + jc] = r > jc ? a : 0.f;
                 }
             }
             // ---- P = (K Q^T)^T * D, lower incl. the diagonal -> global: each
@@ -553,11 +582,13 @@ void prep_kernel(PrefillArgs p, Workspace ws)
                     const int rt = kPrepKQ[wave][i][0], jt = kPrepKQ[wave][i][1];
                     const int qi = 16 * rt + c16;
                     const float gi = gam2[qi];
+                    const f32x4 gk = *reinterpret_cast<const f32x4 *>(gam2 + 16 * jt + 4 * q4);
                     half4 hv;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int jc = 16 * jt + 4 * q4 + e;
-                        hv[e] = (_Float16)(qi >= jc ? p.q_scale * kq[i][e] * __builtin_amdgcn_exp2f(gi - gam2[jc]) : 0.f);
+                        const float pv = p.q_scale * kq[i][e] * __builtin_amdgcn_exp2f(gi - gk[e]);
+                        hv[e] = (_Float16)(qi >= jc ? pv : 0.f);
                     }
                     uint8_t *dst = pf + (tri_frag(rt, jt >> 1) * 64 + lane) * 16 + 8 * (jt & 1);
                     *reinterpret_cast<half4 *>(dst) = hv;
@@ -1207,13 +1238,17 @@ void chain_kernel(PrefillArgs p, Workspace ws)
     const long C_tot = 2L * Hqk * kD + (long)Hv * kD, cv = 2L * Hqk * kD + (long)h * kD;
     // conv taps of the wave's channel tiles
     bf16x8 wb[kChainCT][2];
+    auto load_taps = [&] {
 #pragma unroll
-    for (int x = 0; x < kChainCT; ++x)
+        for (int x = 0; x < kChainCT; ++x)
 #pragma unroll
-        for (int m = 0; m < 2; ++m) wb[x][m] = conv_tap_frag(p.conv_w, cv + kCW * wave + 16 * x + (lane & 15), m, lane);
+            for (int m = 0; m < 2; ++m)
+                wb[x][m] = conv_tap_frag(p.conv_w, cv + kCW * wave + 16 * x + (lane & 15), m, lane);
+    };
     f32x4 S[8][kChainCT];
 
     if (!kRepair) {
+        load_taps();
         const int k = unit;
         const int4 sg = Tables::seg(p, ws, k);  // seq, first chunk, end chunk, flags
         if (sg.x < 0) return;
@@ -1268,8 +1303,16 @@ void chain_kernel(PrefillArgs p, Workspace ws)
         const uint16_t *hist = p.conv_state_in ? p.conv_state_in + (long)s * 3 * C_tot + cv : nullptr;
         const uint16_t *vs = p.v + (long)si.z * Hv * kD + (long)h * kD;
         const int nseg = min(ss.y, p.max_segs - ss.x);
+        // the flags of segments 1 .. nseg-1, 64 at a time (usually one load
+        // per lane): with none set there is nothing to recompute
+        unsigned long long any_bad = 0;
+        for (int i0 = 1; i0 < nseg; i0 += 64) {
+            const int i = i0 + lane;
+            any_bad |= __ballot(i < nseg && ws.seg_bad[(long)(ss.x + i) * Hv + h] != 0);
+        }
+        if (any_bad) load_taps();
         bool carry = false;  // S holds the final state of the previous segment
-        for (int i = 1; i < nseg; ++i) {  // a sequence's first segment is never recomputed
+        for (int i = 1; any_bad && i < nseg; ++i) {  // a sequence's first segment is never recomputed
             const int k = ss.x + i;
             if (!ws.seg_bad[(long)k * Hv + h]) {
                 carry = false;
