@@ -66,11 +66,28 @@ struct Workspace {
     float *bstate;      // [max_segs][Hv][128][128] final state of a segment whose successor is recomputed
 };
 
-// Segments of the sequential pass: each sequence's chunks are cut into runs of
-// seg_chunks that proceed in parallel (chosen from the sizes alone, so that the
-// workspace size is a function of the arguments).
+// Segments of the sequential pass: each sequence's chunks are cut into runs
+// that proceed in parallel, seg_chunks long (chosen from the sizes alone, so
+// that the workspace size is a function of the arguments), except that the
+// first run of a sequence takes kSegLead more chunks: it starts from the
+// sequence's own initial state and needs no warm-up, while every later run
+// first re-runs a few chunks before its start.
 int choose_seg_chunks(int max_chunks, int N, int Hv);
 inline int max_segments(int max_chunks, int N, int seg_chunks) { return max_chunks / seg_chunks + N; }
+constexpr int kSegLead = 4;
+// segments of a sequence of nch chunks, and the chunk range [begin, end) of
+// segment i (relative to the sequence's first chunk)
+__host__ __device__ inline int seg_count(int nch, int seg_chunks)
+{
+    const int r = (nch - kSegLead + seg_chunks - 1) / seg_chunks;
+    return r > 1 ? r : 1;
+}
+__host__ __device__ inline int seg_begin(int i, int seg_chunks) { return i == 0 ? 0 : i * seg_chunks + kSegLead; }
+__host__ __device__ inline int seg_end(int i, int nch, int seg_chunks)
+{
+    const int e = (i + 1) * seg_chunks + kSegLead;
+    return e < nch ? e : nch;
+}
 
 size_t prefill_workspace_bytes(int max_chunks, int N, int Hqk, int Hv);
 Workspace carve_workspace(void *base, int max_chunks, int N, int Hqk, int Hv);

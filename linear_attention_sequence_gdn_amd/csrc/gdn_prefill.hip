@@ -202,7 +202,7 @@ __global__ __launch_bounds__(1024) void setup_kernel(PrefillArgs p, Workspace ws
         const int nch = max(0, min((L + kChunk - 1) / kChunk, p.max_chunks - base));
         ws.seq_info[s] = make_int4(base, nch, t0, min(L, nch * kChunk));
         base += nch;
-        segs_local += max(1, (nch + Lseg - 1) / Lseg);
+        segs_local += seg_count(nch, Lseg);
     }
     // chunk table, one chunk per thread: chunk c lies in the sequence range of
     // the first thread whose inclusive count exceeds c
@@ -229,8 +229,7 @@ __global__ __launch_bounds__(1024) void setup_kernel(PrefillArgs p, Workspace ws
         }
         ws.chunk_info[c] = info;
     }
-    // segments of the sequential pass: max(1, ceil(chunks / Lseg)) per
-    // sequence, in sequence order
+    // segments of the sequential pass, in sequence order
     const int segs_incl = block_scan1024(segs_local, s_wsum);
     if (t == 1023) s_wsum[0] = segs_incl;
     __syncthreads();
@@ -238,10 +237,10 @@ __global__ __launch_bounds__(1024) void setup_kernel(PrefillArgs p, Workspace ws
     int sb = segs_incl - segs_local;
     for (int s = s0; s < s1; ++s) {
         const int4 si = ws.seq_info[s];
-        const int ns = max(1, (si.y + Lseg - 1) / Lseg);
+        const int ns = seg_count(si.y, Lseg);
         ws.seq_seg[s] = make_int4(sb, ns, 0, 0);
         for (int i = 0; i < ns && sb + i < p.max_segs; ++i) {
-            const int cb = si.x + i * Lseg, ce = min(si.x + si.y, cb + Lseg);
+            const int cb = si.x + seg_begin(i, Lseg), ce = si.x + seg_end(i, si.y, Lseg);
             ws.seg_info[sb + i] = make_int4(s, cb, ce, (i == 0 ? 1 : 0) | (i == ns - 1 ? 2 : 0));
         }
         sb += ns;
@@ -266,7 +265,7 @@ struct Tables {
     static __device__ __forceinline__ int chunks_per_seq(const PrefillArgs &p) { return (p.T_uniform + kChunk - 1) / kChunk; }
     static __device__ __forceinline__ int segs_per_seq(const PrefillArgs &p)
     {
-        return max(1, (chunks_per_seq(p) + p.seg_chunks - 1) / p.seg_chunks);
+        return seg_count(chunks_per_seq(p), p.seg_chunks);
     }
     // {sequence, first token, length, is-first}
     static __device__ __forceinline__ int4 chunk(const PrefillArgs &p, const Workspace &ws, int c)
@@ -289,7 +288,7 @@ struct Tables {
         const int per = chunks_per_seq(p), ns = segs_per_seq(p);
         const int s = k / ns, i = k % ns;
         if (s >= p.N) return make_int4(-1, 0, 0, 0);
-        const int cb = s * per + i * p.seg_chunks, ce = min(s * per + per, cb + p.seg_chunks);
+        const int cb = s * per + seg_begin(i, p.seg_chunks), ce = s * per + seg_end(i, per, p.seg_chunks);
         return make_int4(s, cb, ce, (i == 0 ? 1 : 0) | (i == ns - 1 ? 2 : 0));
     }
     // {first segment, segments}
@@ -1340,10 +1339,10 @@ int choose_seg_chunks(int max_chunks, int N, int Hv)
     // Makespan model of the segmented sequential pass, for sequences of the
     // mean length: blocks = segments x Hv, run in rounds of kSlots resident
     // blocks (256 CUs, one block each), each round as long as a segment plus
-    // a few warm-up chunks.  The cheapest cut wins; ties go to
-    // longer segments.
+    // its warm-up chunks (the first segment, kSegLead chunks longer, has
+    // none).  The cheapest cut wins; ties go to longer segments.
     constexpr long kSlots = 256;
-    constexpr int kWarmGuess = 4, kMinSeg = 8;
+    constexpr int kWarmGuess = kSegLead, kMinSeg = 8;
     if (N <= 0 || max_chunks <= 0) return kMinSeg;
     const int nch = (max_chunks + N - 1) / N;
     if (nch <= kMinSeg) return kMinSeg;
@@ -1352,7 +1351,7 @@ int choose_seg_chunks(int max_chunks, int N, int Hv)
     int best = nch;
     // for a given number of segments the shortest even cut is the best one
     for (int nseg = 1;; ++nseg) {
-        const int Ls = (nch + nseg - 1) / nseg;
+        const int Ls = nseg == 1 ? nch : (nch - kSegLead + nseg - 1) / nseg;
         if (nseg > 1 && Ls < kMinSeg) break;
         const long rounds = (units * nseg + kSlots - 1) / kSlots;
         const long cost = rounds * (Ls + (nseg > 1 ? kWarmGuess : 0));
