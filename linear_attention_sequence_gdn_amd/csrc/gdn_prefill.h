@@ -71,10 +71,11 @@ struct Workspace {
 // that the workspace size is a function of the arguments), except that the
 // first run of a sequence takes kSegLead more chunks: it starts from the
 // sequence's own initial state and needs no warm-up, while every later run
-// first re-runs a few chunks before its start.
+// first re-runs a few chunks before its start (typically four, each about
+// 0.7 of a full chunk step since it forms no output: about three steps).
 int choose_seg_chunks(int max_chunks, int N, int Hv);
 inline int max_segments(int max_chunks, int N, int seg_chunks) { return max_chunks / seg_chunks + N; }
-constexpr int kSegLead = 4;
+constexpr int kSegLead = 3;
 // segments of a sequence of nch chunks, and the chunk range [begin, end) of
 // segment i (relative to the sequence's first chunk)
 __host__ __device__ inline int seg_count(int nch, int seg_chunks)

@@ -928,13 +928,17 @@ constexpr int kChainVmemAfterDma = 4;
 // lgkmcnt at their no-wait maxima
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
 
-// One chunk from operand buffer `cur`; loads the next chunk's operands into `nxt`.
+// One chunk from operand buffer `cur`; loads the next chunk's operands into
+// `nxt`.  kOut = false: a warm-up chunk, which only advances the state (no
+// Q S, no output); it waits for its own DMA at its end, since it issues no
+// output stores after it.
 //   Z, X, Vn [rt][x]  tokens 16rt.. x columns 16x..  (accumulator rows = tokens)
 //   QST      [x][rt]  (Q S)^T, columns 16x.. x tokens 16rt.. (accumulator rows = columns)
 // The output is formed transposed, O^T = S^T Q^T diag(q_scale Gam) + Vnew^T P^T,
 // so that a lane holds four adjacent columns of one token (8-byte LDS writes
 // into the row staging).  The fragment layout is the same for A and B
 // operands, so the packed state and Vnew serve as A operands unchanged.
+template <bool kOut>
 __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace &ws, uint8_t *cur, uint8_t *nxt,
                                            uint8_t *stage, f32x4 (&S)[8][kChainCT], const bf16x8 (&wb)[kChainCT][2],
                                            const ChainRun &run, int cc, int h, int g, int wave, int lane)
@@ -986,7 +990,7 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             ak[rt] = ktile_frag(kt, rt, kb, lane);
-            aq[rt] = Qf[(rt * 4 + kb) * 64];
+            if (kOut) aq[rt] = Qf[(rt * 4 + kb) * 64];
         }
         if (kb == 0) chain_dma_group<0>(dn, nxt, wave, lane);
         if (kb == 1) chain_dma_group<1>(dn, nxt, wave, lane);
@@ -1002,7 +1006,7 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
         for (int sl = 0; sl < 8 * kChainCT; ++sl) {
             const int rt = sl / (2 * kChainCT), r = sl % (2 * kChainCT);
             if (r < kChainCT) X[rt][r] = mfma16(ak[rt], sb[r], X[rt][r]);
-            else QST[r - kChainCT][rt] = mfma16(sb[r - kChainCT], aq[rt], QST[r - kChainCT][rt]);
+            else if (kOut) QST[r - kChainCT][rt] = mfma16(sb[r - kChainCT], aq[rt], QST[r - kChainCT][rt]);
             if (sl < 4 * kChainCT) Z[kb][sl >> 2][sl & 3] = silu_f(Z[kb][sl >> 2][sl & 3]);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -1039,14 +1043,16 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) kf[0][i][tb] = ktile_frag_t(kt, i, tb, lane);
     half8 pf[6];
+    if (kOut) {
 #pragma unroll
-    for (int i = 0; i < 6; ++i) pf[i] = Pf[i * 64];
+        for (int i = 0; i < 6; ++i) pf[i] = Pf[i * 64];
+    }
     f32x4 rg[4];
     float gm[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
         rg[rt] = *reinterpret_cast<const f32x4 *>(gt + 64 + 16 * rt + 4 * q4);
-        gm[rt] = gt[16 * rt + c16];
+        if (kOut) gm[rt] = gt[16 * rt + c16];
     }
     const float gn = gt[128];
     __builtin_amdgcn_sched_barrier(0);
@@ -1056,7 +1062,7 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int x = 0; x < kChainCT; ++x) {
-            vb[tb][x] = pack_h8(Vn[2 * tb][x], Vn[2 * tb + 1][x]);
+            if (kOut) vb[tb][x] = pack_h8(Vn[2 * tb][x], Vn[2 * tb + 1][x]);
             vr[tb][x] = pack_h8(Vn[2 * tb][x] * rg[2 * tb], Vn[2 * tb + 1][x] * rg[2 * tb + 1]);
         }
     // S <- Gam_n S + k^T (r Vnew), two state tiles at a time, the next pair's
@@ -1081,14 +1087,18 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
             }
         }
     }
+    if (!kOut) {
+        // the operands of the next chunk have landed (no output stores follow)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        return;
+    }
     // O = diag(q_scale Gam) Q S + P Vnew (P lower triangular), through the
     // wave's staging 16 token rows at a time: (Q S)^T tile (x, rt) lane (q, c)
     // holds columns 16x + 4q .. +3 of token 16rt + c.  The buffer range of the
     // stores ends at the chunk's last valid token, so the rows of a partial
-    // chunk and every row of a warm-up chunk (n = 0) are dropped without a
-    // branch.
+    // chunk are dropped without a branch.
     const int rel = (cc - run.c0) * kChunk;
-    const int n = cc >= run.c_out ? min(kChunk, run.L - rel) : 0;
+    const int n = min(kChunk, run.L - rel);
     const int rowb = Hv * kD * 2;  // bytes per token row of o
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
         p.o + ((long)(run.t0 + rel) * Hv + h) * kD + kCW * wave, 0, n * rowb, 0x00020000);
@@ -1133,11 +1143,25 @@ __device__ __forceinline__ void chain_run(const PrefillArgs &p, const Workspace 
     chain_dma(p, ws, run, buf0, run.c_from, h, g, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     int cc = run.c_from;
-    for (; cc + 2 <= run.c_to; cc += 2) {
-        chain_step(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
-        chain_step(p, ws, buf1, buf0, stage, S, wb, run, cc + 1, h, g, wave, lane);
+    // warm-up chunks [c_from, c_out): the state only
+    const int cw = min(run.c_out, run.c_to);
+    for (; cc + 2 <= cw; cc += 2) {
+        chain_step<false>(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
+        chain_step<false>(p, ws, buf1, buf0, stage, S, wb, run, cc + 1, h, g, wave, lane);
     }
-    if (cc < run.c_to) chain_step(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
+    if (cc < cw) {  // an odd warm-up: the next chunk sits in buf1
+        chain_step<false>(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
+        ++cc;
+        if (cc < run.c_to) {
+            chain_step<true>(p, ws, buf1, buf0, stage, S, wb, run, cc, h, g, wave, lane);
+            ++cc;
+        }
+    }
+    for (; cc + 2 <= run.c_to; cc += 2) {
+        chain_step<true>(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
+        chain_step<true>(p, ws, buf1, buf0, stage, S, wb, run, cc + 1, h, g, wave, lane);
+    }
+    if (cc < run.c_to) chain_step<true>(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
     // the last step's DMA into the other buffer is still in flight
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();

@@ -49,7 +49,9 @@ def test_status_strings(L):
 
 def test_workspace_sizes(L):
     assert gdn.gdn_prefill_workspace_size(1, 8192, 16, 48) > 0
-    assert gdn.gdn_prefill_workspace_size(1, 8192, 16, 48) < gdn.gdn_prefill_workspace_size(1, 8193, 16, 48)
+    # (one more chunk can shrink it a little: the segment cut, and with it the
+    # parked-state area, is chosen per size)
+    assert gdn.gdn_prefill_workspace_size(1, 8192, 16, 48) < gdn.gdn_prefill_workspace_size(1, 16384, 16, 48)
     assert gdn.gdn_prefill_workspace_size(1, 64, 16, 48, 64, 128) == 0  # unsupported dims
     assert gdn.gdn_prefill_workspace_size(1, 64, 16, 47) == 0
     # varlen bound covers any split of T_tot into N sequences
