@@ -731,7 +731,7 @@ constexpr int kChainCT = 1;
 constexpr int kChainWaves = 8 / kChainCT;
 constexpr int kChainThreads = 64 * kChainWaves;
 constexpr int kCW = 16 * kChainCT;                      // state columns (and v channels) per wave
-constexpr int kChainStageRows = 16;                    // token rows per output staging round
+constexpr int kChainStageRows = 64;                    // token rows of the output staging (the chunk)
 constexpr int kChainStage = kChainStageRows * kCW * 2;  // output staging of one wave (bf16)
 
 // k^ in LDS: the sixteen operand fragments (token tile rt, d block kb) in
@@ -1103,34 +1103,39 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
         p.o + ((long)(run.t0 + rel) * Hv + h) * kD + kCW * wave, 0, n * rowb, 0x00020000);
     uint16_t *os = reinterpret_cast<uint16_t *>(stage);
-    static_assert(kChainStageRows == 16, "one token tile per staging round");
+    static_assert(kChainStageRows == kChunk, "the whole chunk is staged at once");
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 ov[4][kChainCT];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
         for (int x = 0; x < kChainCT; ++x) {
             f32x4 acc = mfma16(vb[0][x], pf[tri_frag(rt, 0)], QST[x][rt] * gm[rt]);
             if (rt >= 2) acc = mfma16(vb[1][x], pf[tri_frag(rt, 1)], acc);
-            typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-            const u32x2 v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-            *reinterpret_cast<u32x2 *>(os + c16 * kCW + 16 * x + 4 * q4) = v;
+            ov[rt][x] = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // 16 rows of 2 kCW bytes: lane -> (row lane/4, piece lane%4 of kCW/2 bytes)
-        const int row = lane >> 2, piece = lane & 3;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int x = 0; x < kChainCT; ++x)
+            *reinterpret_cast<u32x2 *>(os + (16 * rt + c16) * kCW + 16 * x + 4 * q4) = ov[rt][x];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // 16 rows of 2 kCW bytes per store: lane -> (row lane/4, piece lane%4 of kCW/2 bytes)
+    const int row = lane >> 2, piece = lane & 3;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
         if constexpr (kChainCT == 2) {
-            const i32x4 v = *reinterpret_cast<const i32x4 *>(stage + row * 64 + piece * 16);
+            const i32x4 v = *reinterpret_cast<const i32x4 *>(stage + (16 * rt + row) * 64 + piece * 16);
             __builtin_amdgcn_raw_buffer_store_b128(v, ro, (16 * rt + row) * rowb + piece * 16, 0, 0);
         } else {
             typedef int i32x2 __attribute__((ext_vector_type(2)));
-            const i32x2 v = *reinterpret_cast<const i32x2 *>(stage + row * 32 + piece * 8);
+            const i32x2 v = *reinterpret_cast<const i32x2 *>(stage + (16 * rt + row) * 32 + piece * 8);
             __builtin_amdgcn_raw_buffer_store_b64(v, ro, (16 * rt + row) * rowb + piece * 8, 0, 0);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
+    // the staging is rewritten by the next step only after its block barrier
 }
 
 // The chunks of one run, the state carried in registers.
