@@ -463,20 +463,24 @@ void prep_kernel(PrefillArgs p, Workspace ws)
         av = p.a[ti];
         bv = p.b[ti];
     }
-    // ---- q^, k^ of the chunk: conv + SiLU, L2 norm per token
+    // ---- q^, k^ of the chunk: conv + SiLU, L2 norm per token.  The raw
+    //      rows of both planes are requested before either is used, so that
+    //      the k loads are in flight while q is formed.
     {
         float z0[16], z1[16];
         const long ldqk = (long)Hqk * kD;
+        uint32_t win[2][19];
 #pragma unroll
         for (int plane = 0; plane < 2; ++plane) {
             const long ch0 = plane == 0 ? (long)g * kD : (long)Hqk * kD + (long)g * kD;
             const uint16_t *x = (plane == 0 ? p.q : p.k) + (long)t0 * ldqk + (long)g * kD;
-            {
-                uint32_t win[19];
-                conv_window_rc(x, (int)ldqk * 2, n, first, hist ? hist + ch0 : nullptr, (int)C_tot * 2, lane, r0,
-                               win);
-                conv_silu(win, conv_weights(p.conv_w + ch0 * 4, lane), r0, n, z0, z1);
-            }
+            conv_window_rc(x, (int)ldqk * 2, n, first, hist ? hist + ch0 : nullptr, (int)C_tot * 2, lane, r0,
+                           win[plane]);
+        }
+#pragma unroll
+        for (int plane = 0; plane < 2; ++plane) {
+            const long ch0 = plane == 0 ? (long)g * kD : (long)Hqk * kD + (long)g * kD;
+            conv_silu(win[plane], conv_weights(p.conv_w + ch0 * 4, lane), r0, n, z0, z1);
             float ss[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) ss[i] = z0[i] * z0[i] + z1[i] * z1[i];
@@ -1065,6 +1069,24 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
             if (kOut) vb[tb][x] = pack_h8(Vn[2 * tb][x], Vn[2 * tb + 1][x]);
             vr[tb][x] = pack_h8(Vn[2 * tb][x] * rg[2 * tb], Vn[2 * tb + 1][x] * rg[2 * tb + 1]);
         }
+    // O = diag(q_scale Gam) Q S + P Vnew (P lower triangular), formed
+    // transposed: (Q S)^T tile (x, rt) lane (q, c) holds columns 16x + 4q ..
+    // +3 of token 16rt + c.  Its products go out before the state update, and
+    // its packing and LDS staging run between the update's products, so that
+    // the two overlap; the staged rows are stored after the update.
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    f32x4 oacc[4][kChainCT];
+    if (kOut) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int x = 0; x < kChainCT; ++x) {
+                oacc[rt][x] = mfma16(vb[0][x], pf[tri_frag(rt, 0)], QST[x][rt] * gm[rt]);
+                if (rt >= 2) oacc[rt][x] = mfma16(vb[1][x], pf[tri_frag(rt, 1)], oacc[rt][x]);
+            }
+    }
+    uint16_t *os = reinterpret_cast<uint16_t *>(stage);
+    static_assert(kChainStageRows == kChunk, "the whole chunk is staged at once");
     // S <- Gam_n S + k^T (r Vnew), two state tiles at a time, the next pair's
     // fragments read while this pair multiplies
 #pragma unroll
@@ -1086,39 +1108,28 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
                 S[dt][x] = mfma16(kf[cb][i][1], vr[1][x], S[dt][x]);
             }
         }
+        if (kOut && pr >= 1) {  // output token tiles 2 (pr - 1) .. +1 into the staging
+#pragma unroll
+            for (int rt = 2 * (pr - 1); rt < 2 * pr && rt < 4; ++rt)
+#pragma unroll
+                for (int x = 0; x < kChainCT; ++x)
+                    *reinterpret_cast<u32x2 *>(os + (16 * rt + c16) * kCW + 16 * x + 4 * q4) =
+                        u32x2{pack_bf16x2(oacc[rt][x][0], oacc[rt][x][1]), pack_bf16x2(oacc[rt][x][2], oacc[rt][x][3])};
+        }
     }
     if (!kOut) {
         // the operands of the next chunk have landed (no output stores follow)
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         return;
     }
-    // O = diag(q_scale Gam) Q S + P Vnew (P lower triangular), through the
-    // wave's staging 16 token rows at a time: (Q S)^T tile (x, rt) lane (q, c)
-    // holds columns 16x + 4q .. +3 of token 16rt + c.  The buffer range of the
-    // stores ends at the chunk's last valid token, so the rows of a partial
-    // chunk are dropped without a branch.
+    // the staged rows to o: the buffer range of the stores ends at the
+    // chunk's last valid token, so the rows of a partial chunk are dropped
+    // without a branch
     const int rel = (cc - run.c0) * kChunk;
     const int n = min(kChunk, run.L - rel);
     const int rowb = Hv * kD * 2;  // bytes per token row of o
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
         p.o + ((long)(run.t0 + rel) * Hv + h) * kD + kCW * wave, 0, n * rowb, 0x00020000);
-    uint16_t *os = reinterpret_cast<uint16_t *>(stage);
-    static_assert(kChainStageRows == kChunk, "the whole chunk is staged at once");
-    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-    u32x2 ov[4][kChainCT];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int x = 0; x < kChainCT; ++x) {
-            f32x4 acc = mfma16(vb[0][x], pf[tri_frag(rt, 0)], QST[x][rt] * gm[rt]);
-            if (rt >= 2) acc = mfma16(vb[1][x], pf[tri_frag(rt, 1)], acc);
-            ov[rt][x] = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-        }
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int x = 0; x < kChainCT; ++x)
-            *reinterpret_cast<u32x2 *>(os + (16 * rt + c16) * kCW + 16 * x + 4 * q4) = ov[rt][x];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
