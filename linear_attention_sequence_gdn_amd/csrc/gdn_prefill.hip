@@ -426,6 +426,26 @@ __device__ constexpr int kPrepKQ[4][3][2] = {{{1, 0}, {1, 1}, {0, 0}}, {{0, 0}, 
                                              {{2, 0}, {2, 1}, {0, 0}}, {{3, 0}, {3, 1}, {3, 3}}};
 __device__ constexpr int kPrepNKK[4] = {3, 2, 3, 2}, kPrepNKQ[4] = {2, 3, 2, 3};
 
+// 16 x 16 tile slots of the two fp32 work matrices (A in the first, X in the
+// second; tile (i, j) of a matrix at row 16i, column 16j, row stride kAL):
+// byte offsets from the start of the first.  The diagonal blocks of
+// (I + A)^-1 of up to four heads (head jj, block w) are solved together and
+// parked, for the whole per-head loop, in tiles that loop never writes (A's
+// diagonal and upper tiles, X's upper tiles); the diagonal tiles of A that
+// they are solved from live only until then, in the lower tiles of both
+// matrices and X's diagonal tiles.
+__host__ __device__ constexpr int prep_slot(int m, int i, int j) { return (m * 64 * kAL + 16 * i * kAL + 16 * j) * 4; }
+__device__ constexpr int kPrepXd[4][4] = {
+    {prep_slot(0, 0, 0), prep_slot(0, 1, 1), prep_slot(0, 2, 2), prep_slot(0, 3, 3)},
+    {prep_slot(0, 0, 1), prep_slot(0, 0, 2), prep_slot(0, 0, 3), prep_slot(0, 1, 2)},
+    {prep_slot(0, 1, 3), prep_slot(0, 2, 3), prep_slot(1, 0, 1), prep_slot(1, 0, 2)},
+    {prep_slot(1, 0, 3), prep_slot(1, 1, 2), prep_slot(1, 1, 3), prep_slot(1, 2, 3)}};
+__device__ constexpr int kPrepAd[4][4] = {
+    {prep_slot(0, 1, 0), prep_slot(0, 2, 1), prep_slot(1, 2, 2), prep_slot(1, 3, 3)},
+    {prep_slot(0, 2, 0), prep_slot(0, 3, 1), prep_slot(1, 1, 0), prep_slot(1, 3, 2)},
+    {prep_slot(0, 3, 0), prep_slot(0, 3, 2), prep_slot(1, 2, 1), prep_slot(1, 0, 0)},
+    {prep_slot(1, 2, 0), prep_slot(1, 3, 0), prep_slot(1, 3, 1), prep_slot(1, 1, 1)}};
+
 // Four resident workgroups per CU (at most 128 VGPRs): the per-head phases
 // are short stretches between barriers, and other workgroups fill the waits.
 __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
@@ -433,8 +453,8 @@ void prep_kernel(PrefillArgs p, Workspace ws)
 {
     // LDS plan: [R0] q^ (fp16) -> A (fp32); [R1] k^ (fp16) -> X = (I+A)^-1
     // (fp32); product slots of the inverse; the gates of four heads
-    __shared__ __attribute__((aligned(16))) uint8_t R0[kPrepTile];
-    __shared__ __attribute__((aligned(16))) uint8_t R1[kPrepTile];
+    __shared__ __attribute__((aligned(16))) uint8_t R[2 * kPrepTile];
+    uint8_t *R0 = R, *R1 = R + kPrepTile;
     __shared__ __attribute__((aligned(16))) float Msc[4 * 256];
     __shared__ __attribute__((aligned(16))) float s_gam2[4 * 64];
     __shared__ __attribute__((aligned(16))) float s_beta[4 * 64];
@@ -551,15 +571,58 @@ void prep_kernel(PrefillArgs p, Workspace ws)
         }
         __syncthreads();
         const int jn = min(4, G - j0);
+        // ---- diagonal blocks of X = (I + A)^-1 of these heads: wave w builds
+        //      A's diagonal tile (w, w) of every head (K K^T tile (w, w) is its
+        //      first tile, kk[0]), then solves them all at once by forward
+        //      substitution, lane (q, c) taking column c of head q's block
+        {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                if (jj >= jn) continue;
+                const float *gam2 = s_gam2 + 64 * jj, *beta = s_beta + 64 * jj;
+                const f32x4 gr = *reinterpret_cast<const f32x4 *>(gam2 + 16 * wave + 4 * q4);
+                const f32x4 br = *reinterpret_cast<const f32x4 *>(beta + 16 * wave + 4 * q4);
+                const float gj = gam2[16 * wave + c16];
+                float *ad = reinterpret_cast<float *>(R + kPrepAd[jj][wave]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float a = br[e] * kk[0][e] * __builtin_amdgcn_exp2f(gr[e] - gj);
+                    ad[(4 * q4 + e) * kAL + c16] = 4 * q4 + e > c16 ? a : 0.f;
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int qh = min(q4, jn - 1);  // lanes of absent heads repeat the last one
+            const int ad_off = qh == 0 ? kPrepAd[0][wave] : qh == 1 ? kPrepAd[1][wave]
+                             : qh == 2 ? kPrepAd[2][wave] : kPrepAd[3][wave];
+            const int xd_off = qh == 0 ? kPrepXd[0][wave] : qh == 1 ? kPrepXd[1][wave]
+                             : qh == 2 ? kPrepXd[2][wave] : kPrepXd[3][wave];
+            float y[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) y[i] = i == c16 ? 1.f : 0.f;
+            SolveCol16<0>::run(y, reinterpret_cast<const float *>(R + ad_off));
+            if (q4 < jn) {
+                float *xd = reinterpret_cast<float *>(R + xd_off);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) xd[i * kAL + c16] = y[i];
+            }
+        }
+        __syncthreads();
         for (int jj = 0; jj < jn; ++jj) {
             const long hc = (long)c * Hv + g * G + j0 + jj;
+            // this head's diagonal blocks of X
+            const int xd0 = kPrepXd[jj][0], xd1 = kPrepXd[jj][1], xd2 = kPrepXd[jj][2], xd3 = kPrepXd[jj][3];
+            auto XDt = [&](int i) {
+                return reinterpret_cast<float *>(R + (i == 0 ? xd0 : i == 1 ? xd1 : i == 2 ? xd2 : xd3));
+            };
             const float *gam2 = s_gam2 + 64 * jj, *beta = s_beta + 64 * jj;
-            // ---- A = strict_lower(diag(beta) K K^T * D) -> LDS, without
-            //      branches (a lane's four rows are adjacent: one 16-byte read
-            //      each of gam and beta per tile); the upper parts of the
-            //      diagonal tiles, never read, get zero
+            // ---- A = strict_lower(diag(beta) K K^T * D) -> LDS, its tiles
+            //      below the diagonal (the diagonal ones were solved above),
+            //      without branches (a lane's four rows are adjacent: one
+            //      16-byte read each of gam and beta per tile)
 #pragma unroll
-            for (int i = 0; i < 3; ++i) {
+            for (int i = 1; i < 3; ++i) {
                 if (i >= nkk) continue;
                 const int rt = kPrepKK[wave][i][0], ct = kPrepKK[wave][i][1];
                 const int jc = 16 * ct + c16;
@@ -569,8 +632,7 @@ void prep_kernel(PrefillArgs p, Workspace ws)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 16 * rt + 4 * q4 + e;
-                    const float a = br[e] * kk[i][e] * __builtin_amdgcn_exp2f(gr[e] - gj);
-                    As[r * kAL + jc] = r > jc ? a : 0.f;
+                    As[r * kAL + jc] = br[e] * kk[i][e] * __builtin_amdgcn_exp2f(gr[e] - gj);
                 }
             }
             // ---- P = (K Q^T)^T * D, lower incl. the diagonal -> global: each
@@ -598,10 +660,8 @@ void prep_kernel(PrefillArgs p, Workspace ws)
                     if (jt == rt && (jt & 1) == 0) *reinterpret_cast<half4 *>(dst + 8) = half4{0, 0, 0, 0};
                 }
             }
-            // ---- X = (I + A)^-1, blocked by 16.  Diagonal block b by forward
-            //      substitution, by wave b as soon as it has written the A
-            //      tile (b, b) (its own LDS writes, so a wave-level fence
-            //      suffices).  Then, with L = I + A in
+            // ---- X = (I + A)^-1, blocked by 16, from its diagonal blocks
+            //      (solved above).  With L = I + A in
             //      32 x 32 blocks, L^-1 = [[X_a, 0], [-X_b L_ba X_a, X_b]]:
             //      first the two 32 x 32 diagonal blocks (X_10, X_32) and, at
             //      the same time, the products that need only diagonal
@@ -609,20 +669,6 @@ void prep_kernel(PrefillArgs p, Workspace ws)
             //      M_30 and X_21, X_31; then X_20, X_30 -- three rounds of at
             //      most two dependent 16 x 16 products, on the fp32 matrix
             //      cores, with M kept in LDS between rounds.
-            {  // wave b: diagonal block b, lane c (< 16): its column c
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                float y[16];
-                const int bo = 16 * wave;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) y[i] = i == c16 ? 1.f : 0.f;
-                SolveCol16<0>::run(y, As + bo * kAL + bo);
-                if (lane < 16) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) Xs[(bo + i) * kAL + bo + c16] = y[i];
-                }
-            }
             __syncthreads();
             {
                 const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -638,42 +684,42 @@ void prep_kernel(PrefillArgs p, Workspace ws)
                 //          M_21 = A_21 X_11 (slot 2), M_31 = A_31 X_11 (slot 3)
                 if (wave < 2) {
                     const int i = 2 * wave;  // (1, 0) or (3, 2)
-                    st16_f32(Ms, 16, mm16_f32(At(i + 1, i), kAL, Xt(i, i), kAL, z, lane), lane);
+                    st16_f32(Ms, 16, mm16_f32(At(i + 1, i), kAL, XDt(i), kAL, z, lane), lane);
                     wave_sync();
-                    st16_f32(Xt(i + 1, i), kAL, -mm16_f32(Xt(i + 1, i + 1), kAL, Ms, 16, z, lane), lane);
+                    st16_f32(Xt(i + 1, i), kAL, -mm16_f32(XDt(i + 1), kAL, Ms, 16, z, lane), lane);
                 } else {
-                    st16_f32(Ms, 16, mm16_f32(At(wave, 1), kAL, Xt(1, 1), kAL, z, lane), lane);
+                    st16_f32(Ms, 16, mm16_f32(At(wave, 1), kAL, XDt(1), kAL, z, lane), lane);
                 }
                 __syncthreads();
                 // round 2: M_20 (slot 0), M_30 (slot 1); X_21 = -X_22 M_21,
                 //          X_31 = -(X_32 M_21 + X_33 M_31)
                 if (wave < 2) {
                     const int i = 2 + wave;
-                    f32x4 m = mm16_f32(At(i, 0), kAL, Xt(0, 0), kAL, z, lane);
+                    f32x4 m = mm16_f32(At(i, 0), kAL, XDt(0), kAL, z, lane);
                     m = mm16_f32(At(i, 1), kAL, Xt(1, 0), kAL, m, lane);
                     st16_f32(Ms, 16, m, lane);
                 } else if (wave == 2) {
-                    st16_f32(Xt(2, 1), kAL, -mm16_f32(Xt(2, 2), kAL, Msc + 512, 16, z, lane), lane);
+                    st16_f32(Xt(2, 1), kAL, -mm16_f32(XDt(2), kAL, Msc + 512, 16, z, lane), lane);
                 } else {
                     f32x4 x = mm16_f32(Xt(3, 2), kAL, Msc + 512, 16, z, lane);
-                    x = mm16_f32(Xt(3, 3), kAL, Msc + 768, 16, x, lane);
+                    x = mm16_f32(XDt(3), kAL, Msc + 768, 16, x, lane);
                     st16_f32(Xt(3, 1), kAL, -x, lane);
                 }
                 __syncthreads();
                 // round 3: X_20 = -X_22 M_20, X_30 = -(X_32 M_20 + X_33 M_30)
                 if (wave == 0) {
-                    st16_f32(Xt(2, 0), kAL, -mm16_f32(Xt(2, 2), kAL, Msc, 16, z, lane), lane);
+                    st16_f32(Xt(2, 0), kAL, -mm16_f32(XDt(2), kAL, Msc, 16, z, lane), lane);
                 } else if (wave == 1) {
                     f32x4 x = mm16_f32(Xt(3, 2), kAL, Msc, 16, z, lane);
-                    x = mm16_f32(Xt(3, 3), kAL, Msc + 256, 16, x, lane);
+                    x = mm16_f32(XDt(3), kAL, Msc + 256, 16, x, lane);
                     st16_f32(Xt(3, 0), kAL, -x, lane);
                 }
                 __syncthreads();
             }
             // ---- T' = X diag(beta), lower triangle, as A operands (rows =
             //      tokens i, contraction = tokens j): wave w writes fragments
-            //      w and w + 4.  Entries above the diagonal blocks of X were
-            //      never written and are selected away.
+            //      w and w + 4.  The diagonal blocks come from their parking
+            //      slots; entries above the diagonal are selected away.
             {
                 half8 *tf = reinterpret_cast<half8 *>(ws.hrec + hc * kRecBytes + kRecT);
 #pragma unroll
@@ -686,7 +732,8 @@ void prep_kernel(PrefillArgs p, Workspace ws)
 #pragma unroll
                     for (int hb = 0; hb < 2; ++hb) {
                         const int j0c = 32 * kb + 16 * hb + 4 * q4;
-                        const f32x4 xv = *reinterpret_cast<const f32x4 *>(Xs + i * kAL + j0c);
+                        const float *xp = 2 * kb + hb == rt ? XDt(rt) + c16 * kAL + 4 * q4 : Xs + i * kAL + j0c;
+                        const f32x4 xv = *reinterpret_cast<const f32x4 *>(xp);
                         const f32x4 bb = *reinterpret_cast<const f32x4 *>(beta + j0c);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) fr[4 * hb + e] = (_Float16)(j0c + e <= i ? xv[e] * bb[e] : 0.f);
