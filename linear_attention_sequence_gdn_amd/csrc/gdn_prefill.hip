@@ -741,8 +741,11 @@ void prep_kernel(PrefillArgs p, Workspace ws)
                     tf[f * 64 + lane] = fr;
                 }
             }
-            __syncthreads();  // A and X are rebuilt for the next head
+            // no barrier here: the next head's A build writes only A's lower
+            // tiles, which nothing after the last round reads, and its rounds
+            // start after its own barrier, behind every wave's T' reads
         }
+        __syncthreads();  // the next round of heads rewrites the gates and both matrices
     }
 }
 
