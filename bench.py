@@ -49,7 +49,7 @@ CHUNK = 64
 # ---------------------------------------------------------------------------
 # gdn_prefill_with_events records an event before the first kernel and after
 # each of these, in launch order
-PREFILL_KERNELS = ("setup_kernel", "prep_kernel", "chain_kernel", "chain_repair_kernel")
+PREFILL_KERNELS = ("setup_kernel", "prep_kernel", "chain_kernel")
 N_EVENTS = len(PREFILL_KERNELS) + 1
 
 
@@ -117,8 +117,7 @@ def source_digest():
 
 
 COPY_BYTES = 256 << 20
-TRAFFIC_KERNELS = {"prefill_chain": "chain_kernel<false>", "prefill_chain_repair": "chain_kernel<true>",
-                   "prefill_prep": "prep_kernel",
+TRAFFIC_KERNELS = {"prefill_chain": "chain_kernel(", "prefill_prep": "prep_kernel",
                    "prefill_setup": "setup_kernel", "decode": "decode_step_kernel",
                    "decode_conv_shift": "conv_shift_qk_kernel<1>",
                    "decode_multi": "decode_head_kernel<4>", "decode_multi_conv_shift": "conv_shift_qk_kernel<4>"}

@@ -92,12 +92,13 @@ int gdn_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 
 /*
  * Measurement variant of gdn_prefill: the same work on the same stream, and
- * additionally records five caller-created HIP events (events[i] is a
- * hipEvent_t), so that the caller can time each of the four kernels with
+ * additionally records four caller-created HIP events (events[i] is a
+ * hipEvent_t), so that the caller can time each of the three kernels with
  * hipEventElapsedTime: events[0] before the first kernel, then one after each
  * of the chunk-table setup (nothing is launched for uniform batches), the
- * parallel per-chunk pass, the segmented sequential pass and its in-order
- * repair pass.  events must not be NULL and must hold five events.
+ * parallel per-chunk pass and the segmented sequential pass (which includes
+ * its in-order repair of segments).  events must not be NULL and must hold
+ * four events.
  */
 int gdn_prefill_with_events(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                             const float *a, const float *b, const uint16_t *conv_w,

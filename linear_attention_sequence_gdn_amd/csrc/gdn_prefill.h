@@ -25,7 +25,7 @@ struct PrefillArgs {
     int max_chunks;
     int seg_chunks;  // chunks per segment of the sequential pass
     int max_segs;    // bound of the number of segments
-    int defer_final; // state_out is state_in: final states go through the repair pass
+    int defer_final; // state_out is state_in: final states go through the in-order pass
 };
 
 // Upper bound of the number of 64-token chunks.
@@ -56,14 +56,13 @@ constexpr size_t kStateFloats = 128 * 128;          // one fp32 state
 struct Workspace {
     int4 *chunk_info;   // [max_chunks] {seq, t0, n, first}
     int4 *seq_info;     // [N] {chunk0, nchunks, t0, L}
-    int *order;         // [N] sequences, longest first
     uint8_t *qfrag;     // [max_chunks][Hqk]
     uint8_t *kfrag;     // [max_chunks][Hqk]  k^ (token rows, d contraction)
     uint8_t *hrec;      // [max_chunks][Hv] P, T', gates
     int4 *seg_info;     // [max_segs] {seq, first chunk, end chunk, 1: first of seq | 2: last of seq}; seq -1 = unused
     int4 *seq_seg;      // [N] {first segment, segments, -, -}
-    int *seg_bad;       // [max_segs][Hv] warm-up bound not met: the segment is recomputed in order
-    float *bstate;      // [max_segs][Hv][128][128] final state of a segment whose successor is recomputed
+    float *bstate;      // [max_segs][Hv][128][128] final state of a segment (read when its successor is recomputed)
+    int *seg_done;      // [N][Hv] segments of the pair finished, + 2^16 per missed warm-up bound (zeroed by the parallel pass)
 };
 
 // Segments of the sequential pass: each sequence's chunks are cut into runs
@@ -93,8 +92,8 @@ __host__ __device__ inline int seg_end(int i, int nch, int seg_chunks)
 size_t prefill_workspace_bytes(int max_chunks, int N, int Hqk, int Hv);
 Workspace carve_workspace(void *base, int max_chunks, int N, int Hqk, int Hv);
 // events: NULL, or kPrefillEvents events recorded before the first kernel and
-// after each of the four (setup, prep, chain, chain repair).
-constexpr int kPrefillEvents = 5;
+// after each of the three (setup, prep, chain).
+constexpr int kPrefillEvents = 4;
 hipError_t launch_prefill(const PrefillArgs &p, void *workspace, hipStream_t stream,
                           hipEvent_t const *events = nullptr);
 

@@ -27,8 +27,9 @@
 //                blocked unit-lower-triangular inverse, T';
 //   chain     -- the sequential pass over (segment, V head): conv + SiLU of v
 //                and every product that involves the state; each wave
-//                carries 32 columns of S in registers;
-//   repair    -- segments whose warm-up bound failed, recomputed in order.
+//                carries 16 columns of S in registers.  The last workgroup of
+//                a (sequence, V head) to finish recomputes, in order, the
+//                segments whose warm-up bound failed.
 #include "gdn_prefill.h"
 
 namespace gdn {
@@ -246,16 +247,6 @@ __global__ __launch_bounds__(1024) void setup_kernel(PrefillArgs p, Workspace ws
         sb += ns;
     }
     for (int k = min(segs_total, p.max_segs) + t; k < p.max_segs; k += 1024) ws.seg_info[k] = make_int4(-1, 0, 0, 0);
-    // longest first (ties by index): rank of each sequence
-    for (int s = t; s < p.N; s += 1024) {
-        const int Ls = seq_len(p, s);
-        int rank = 0;
-        for (int j2 = 0; j2 < p.N; ++j2) {
-            const int Lj = seq_len(p, j2);
-            rank += (Lj > Ls) || (Lj == Ls && j2 < s);
-        }
-        ws.order[rank] = s;
-    }
 }
 
 // Table lookups.  Packed (varlen) calls read the tables setup_kernel built;
@@ -299,10 +290,6 @@ struct Tables {
         return make_int2(s * ns, ns);
     }
     // sequences, longest first
-    static __device__ __forceinline__ int order(const PrefillArgs &p, const Workspace &ws, int rank)
-    {
-        return p.cu_seqlens ? ws.order[rank] : rank;
-    }
 };
 
 // ---------------------------------------------------------------------------
@@ -466,6 +453,9 @@ void prep_kernel(PrefillArgs p, Workspace ws)
     const int q4 = lane >> 4, c16 = lane & 15;
     const int Hqk = p.Hqk, Hv = p.Hv, G = Hv / Hqk;
     const int c = blockIdx.x / Hqk, g = blockIdx.x % Hqk;
+    // the sequential pass's per-(sequence, V head) segment counters
+    if (blockIdx.x == 0)
+        for (int i = t; i < p.N * Hv; i += kPrepThreads) ws.seg_done[i] = 0;
     const int4 ci = Tables::chunk(p, ws, c);
     const int n = ci.z;
     if (n == 0) return;  // empty chunk slot (whole workgroup)
@@ -1299,126 +1289,128 @@ __device__ __forceinline__ void state_store(const f32x4 (&S)[8][kChainCT], float
                 dst[(long)(16 * dt + 4 * q4 + e) * kD + kCW * wave + 16 * x + c16] = S[dt][x][e];
 }
 
-// Sequential pass.  kRepair = false: one workgroup per (segment, V head);
-// segments run in parallel, each from its warm-up start.  kRepair = true: one
-// workgroup per (sequence, V head), which walks the sequence's segments in
-// order and recomputes, exactly from the state the previous segment handed
-// over, those whose warm-up bound was not met; for in-place calls it also
-// hands each sequence of several segments its final state.
-template <bool kRepair>
+// Sequential pass: one workgroup per (segment, V head); segments run in
+// parallel, each from its warm-up start.  The last workgroup of a (sequence,
+// V head) to finish -- a device-scope counter per pair, zeroed by the
+// parallel pass, which also counts the segments that missed their warm-up
+// bound -- then walks the sequence's segments in order and recomputes,
+// exactly from the state the previous segment handed over, those whose bound
+// was not met; for in-place calls it also hands a sequence of several
+// segments its final state.  Only a workgroup whose parked state that walk
+// will read publishes it with a device-scope fence, so the common case (no
+// failed bound, out of place) costs one atomic per workgroup.
+constexpr int kSegBadUnit = 1 << 16;  // counter increment of a segment that missed its bound
 __global__ __launch_bounds__(kChainThreads) __attribute__((amdgpu_waves_per_eu(kChainWaves / 4, kChainWaves / 4)))
 void chain_kernel(PrefillArgs p, Workspace ws)
 {
     __shared__ __attribute__((aligned(16))) uint8_t buf0[ChainBuf::kBytes];
     __shared__ __attribute__((aligned(16))) uint8_t buf1[ChainBuf::kBytes];
     __shared__ __attribute__((aligned(16))) uint8_t stage_all[kChainWaves * kChainStage];
+    __shared__ int s_total;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     uint8_t *stage = stage_all + wave * kChainStage;
     const int Hqk = p.Hqk, Hv = p.Hv, G = Hv / Hqk;
-    // block -> (segment or rank, group, head in group); the G heads of one
-    // (segment, QK group) land on the same XCD (same L2)
+    // block -> (segment, group, head in group); the G heads of one (segment,
+    // QK group) land on the same XCD (same L2)
     const int bid = blockIdx.x;
     const int gu = (bid / (8 * G)) * 8 + (bid & 7);
     const int j = (bid >> 3) % G;
-    if (gu >= (kRepair ? p.N : p.max_segs) * Hqk) return;
-    const int unit = gu / Hqk, g = gu % Hqk;
+    if (gu >= p.max_segs * Hqk) return;
+    const int k = gu / Hqk, g = gu % Hqk;
     const int h = g * G + j;
     const long C_tot = 2L * Hqk * kD + (long)Hv * kD, cv = 2L * Hqk * kD + (long)h * kD;
+    const int4 sg = Tables::seg(p, ws, k);  // seq, first chunk, end chunk, flags
+    if (sg.x < 0) return;                   // no segment in this slot
+    const int s = sg.x;
+    const int4 si = Tables::seq(p, ws, s);  // chunk0, nchunks, t0, L
+    const bool first = sg.w & 1, last = sg.w & 2;
+    const long sbase = ((long)s * Hv + h) * kD * kD;
+    const uint16_t *hist = p.conv_state_in ? p.conv_state_in + (long)s * 3 * C_tot + cv : nullptr;
+    const uint16_t *vs = p.v + (long)si.z * Hv * kD + (long)h * kD;
     // conv taps of the wave's channel tiles
     bf16x8 wb[kChainCT][2];
-    auto load_taps = [&] {
 #pragma unroll
-        for (int x = 0; x < kChainCT; ++x)
+    for (int x = 0; x < kChainCT; ++x)
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
-                wb[x][m] = conv_tap_frag(p.conv_w, cv + kCW * wave + 16 * x + (lane & 15), m, lane);
-    };
+        for (int m = 0; m < 2; ++m) wb[x][m] = conv_tap_frag(p.conv_w, cv + kCW * wave + 16 * x + (lane & 15), m, lane);
     f32x4 S[8][kChainCT];
 
-    if (!kRepair) {
-        load_taps();
-        const int k = unit;
-        const int4 sg = Tables::seg(p, ws, k);  // seq, first chunk, end chunk, flags
-        if (sg.x < 0) return;
-        const int s = sg.x;
-        const int4 si = Tables::seq(p, ws, s);  // chunk0, nchunks, t0, L
-        const bool first = sg.w & 1, last = sg.w & 2;
-        const int w = first ? sg.y : warm_start(ws, h, Hv, sg.y, si.x, lane);
-        if (!first && t == 0) ws.seg_bad[(long)k * Hv + h] = w < 0;
-        if (w < 0) return;  // recomputed in order by the repair pass
-        const long sbase = ((long)s * Hv + h) * kD * kD;
+    const int w = first ? sg.y : warm_start(ws, h, Hv, sg.y, si.x, lane);
+    if (w >= 0) {  // else recomputed in order below
         state_load(S, w == si.x && p.state_in ? p.state_in + sbase : nullptr, wave, lane);
-        const uint16_t *hist = p.conv_state_in ? p.conv_state_in + (long)s * 3 * C_tot + cv : nullptr;
-        const uint16_t *vs = p.v + (long)si.z * Hv * kD + (long)h * kD;
         chain_run(p, ws, buf0, buf1, stage, S, wb, ChainRun{si.x, si.z, si.w, w, sg.z, sg.y, vs, hist}, h, g, wave,
                   lane);
         // Final states.  Every segment but the last parks its final state for
-        // the repair pass, which runs after this one and hands it to the next
-        // segment if that one is recomputed.  The last segment writes
-        // state_out, unless state_out is state_in and other blocks of the
-        // sequence may still be reading it: then it parks its state as well
-        // and the repair pass moves it.
+        // the in-order pass, which hands it to the next segment if that one
+        // is recomputed.  The last segment writes state_out, unless state_out
+        // is state_in and other blocks of the sequence may still be reading
+        // it: then it parks its state as well and the in-order pass moves it.
         const bool direct = last && (first || !p.defer_final);
         state_store(S, direct ? p.state_out + sbase : ws.bstate + ((long)k * Hv + h) * kStateFloats, wave, lane);
-        // carried conv rows: the last three raw rows of the sequence (v
-        // channels of head h; the first head of the group also writes the q
-        // and k channels)
-        if (first && p.conv_state_out && wave == 0) {
-            const int Ls = si.w, t0 = si.z;
-            for (int plane = (j == 0 ? 0 : 2); plane < 3; ++plane) {
-                const long ch0 = plane == 0 ? (long)g * kD : plane == 1 ? (long)Hqk * kD + (long)g * kD
-                                                                      : 2L * Hqk * kD + (long)h * kD;
-                const uint16_t *src = plane == 0 ? p.q + (long)g * kD : plane == 1 ? p.k + (long)g * kD
-                                                                                  : p.v + (long)h * kD;
-                const long ld = plane == 2 ? (long)Hv * kD : (long)Hqk * kD;
+    }
+    // carried conv rows: the last three raw rows of the sequence (v channels
+    // of head h; the first head of the group also writes the q and k
+    // channels)
+    if (first && p.conv_state_out && wave == 0) {
+        const int Ls = si.w, t0 = si.z;
+        for (int plane = (j == 0 ? 0 : 2); plane < 3; ++plane) {
+            const long ch0 = plane == 0 ? (long)g * kD : plane == 1 ? (long)Hqk * kD + (long)g * kD
+                                                                  : 2L * Hqk * kD + (long)h * kD;
+            const uint16_t *src = plane == 0 ? p.q + (long)g * kD : plane == 1 ? p.k + (long)g * kD
+                                                                              : p.v + (long)h * kD;
+            const long ld = plane == 2 ? (long)Hv * kD : (long)Hqk * kD;
 #pragma unroll
-                for (int r = 0; r < 3; ++r) {
-                    const int tau = Ls - 3 + r;
-                    uint32_t val = 0;
-                    if (tau >= 0)
-                        val = ld_pair(src + (long)(t0 + tau) * ld + 2 * lane);
-                    else if (p.conv_state_in)
-                        val = ld_pair(p.conv_state_in + ((long)s * 3 + 3 + tau) * C_tot + ch0 + 2 * lane);
-                    *reinterpret_cast<uint32_t *>(p.conv_state_out + ((long)s * 3 + r) * C_tot + ch0 + 2 * lane) = val;
-                }
+            for (int r = 0; r < 3; ++r) {
+                const int tau = Ls - 3 + r;
+                uint32_t val = 0;
+                if (tau >= 0)
+                    val = ld_pair(src + (long)(t0 + tau) * ld + 2 * lane);
+                else if (p.conv_state_in)
+                    val = ld_pair(p.conv_state_in + ((long)s * 3 + 3 + tau) * C_tot + ch0 + 2 * lane);
+                *reinterpret_cast<uint32_t *>(p.conv_state_out + ((long)s * 3 + r) * C_tot + ch0 + 2 * lane) = val;
             }
         }
-    } else {
-        const int s = Tables::order(p, ws, unit);
-        const int4 si = Tables::seq(p, ws, s);
-        const int2 ss = Tables::seq_segs(p, ws, s);  // first segment, segments
-        const long sbase = ((long)s * Hv + h) * kD * kD;
-        const uint16_t *hist = p.conv_state_in ? p.conv_state_in + (long)s * 3 * C_tot + cv : nullptr;
-        const uint16_t *vs = p.v + (long)si.z * Hv * kD + (long)h * kD;
-        const int nseg = min(ss.y, p.max_segs - ss.x);
-        // the flags of segments 1 .. nseg-1, 64 at a time (usually one load
-        // per lane): with none set there is nothing to recompute
-        unsigned long long any_bad = 0;
-        for (int i0 = 1; i0 < nseg; i0 += 64) {
-            const int i = i0 + lane;
-            any_bad |= __ballot(i < nseg && ws.seg_bad[(long)(ss.x + i) * Hv + h] != 0);
+    }
+
+    // this segment is done
+    const int2 ss = Tables::seq_segs(p, ws, s);  // first segment, segments
+    const int nseg = min(ss.y, p.max_segs - ss.x), i_seg = k - ss.x;
+    if (nseg <= 1) return;
+    // publish the parked state if the in-order walk will read it: when the
+    // next segment misses its bound (the same test it makes itself), or for
+    // the final state of an in-place call
+    const bool publish = (i_seg + 1 < nseg && warm_start(ws, h, Hv, Tables::seg(p, ws, k + 1).y, si.x, lane) < 0) ||
+                         (i_seg == nseg - 1 && p.defer_final);
+    if (publish) __threadfence();
+    __syncthreads();
+    if (t == 0) {
+        const int add = 1 + (w < 0 ? kSegBadUnit : 0);
+        s_total = atomicAdd(ws.seg_done + (long)s * Hv + h, add) + add;
+    }
+    __syncthreads();
+    const int total = s_total;
+    if (total % kSegBadUnit != nseg) return;  // not the last to finish
+    const bool any_bad = total >= kSegBadUnit;
+    if (!any_bad && !p.defer_final) return;
+    __threadfence();
+    bool carry = false;  // S holds the final state of the previous segment
+    for (int i = 1; any_bad && i < nseg; ++i) {  // a sequence's first segment is never recomputed
+        const int kk = ss.x + i;
+        const int4 sk = Tables::seg(p, ws, kk);
+        if (warm_start(ws, h, Hv, sk.y, si.x, lane) >= 0) {
+            carry = false;
+            continue;
         }
-        if (any_bad) load_taps();
-        bool carry = false;  // S holds the final state of the previous segment
-        for (int i = 1; any_bad && i < nseg; ++i) {  // a sequence's first segment is never recomputed
-            const int k = ss.x + i;
-            if (!ws.seg_bad[(long)k * Hv + h]) {
-                carry = false;
-                continue;
-            }
-            if (!carry) state_load(S, ws.bstate + ((long)(k - 1) * Hv + h) * kStateFloats, wave, lane);
-            const int4 sg = Tables::seg(p, ws, k);
-            chain_run(p, ws, buf0, buf1, stage, S, wb, ChainRun{si.x, si.z, si.w, sg.y, sg.z, sg.y, vs, hist}, h, g,
-                      wave, lane);
-            carry = true;
-        }
-        // the final state of a sequence of several segments, when its last
-        // segment was recomputed here or parked its state
-        if (nseg > 1 && (carry || p.defer_final)) {
-            if (!carry) state_load(S, ws.bstate + ((long)(ss.x + nseg - 1) * Hv + h) * kStateFloats, wave, lane);
-            state_store(S, p.state_out + sbase, wave, lane);
-        }
+        if (!carry) state_load(S, ws.bstate + ((long)(kk - 1) * Hv + h) * kStateFloats, wave, lane);
+        chain_run(p, ws, buf0, buf1, stage, S, wb, ChainRun{si.x, si.z, si.w, sk.y, sk.z, sk.y, vs, hist}, h, g, wave,
+                  lane);
+        carry = true;
+    }
+    // the final state, when the last segment was recomputed here or parked it
+    if (carry || p.defer_final) {
+        if (!carry) state_load(S, ws.bstate + ((long)(ss.x + nseg - 1) * Hv + h) * kStateFloats, wave, lane);
+        state_store(S, p.state_out + sbase, wave, lane);
     }
 }
 
@@ -1460,14 +1452,13 @@ size_t prefill_workspace_bytes(int max_chunks, int N, int Hqk, int Hv)
     size_t total = 0;
     total += align256(C * sizeof(int4));
     total += align256((size_t)N * sizeof(int4));
-    total += align256((size_t)N * sizeof(int));
     total += align256(C * Hqk * kQFragBytes);
     total += align256(C * Hqk * kKFragBytes);
     total += align256(C * Hv * kRecBytes);
     total += align256(M * sizeof(int4));
     total += align256((size_t)N * sizeof(int4));
-    total += align256(M * Hv * sizeof(int));
     total += align256(M * Hv * kStateFloats * sizeof(float));
+    total += align256((size_t)N * Hv * sizeof(int));
     return total;
 }
 
@@ -1484,14 +1475,13 @@ Workspace carve_workspace(void *base, int max_chunks, int N, int Hqk, int Hv)
     };
     ws.chunk_info = reinterpret_cast<int4 *>(take(C * sizeof(int4)));
     ws.seq_info = reinterpret_cast<int4 *>(take((size_t)N * sizeof(int4)));
-    ws.order = reinterpret_cast<int *>(take((size_t)N * sizeof(int)));
     ws.qfrag = take(C * Hqk * kQFragBytes);
     ws.kfrag = take(C * Hqk * kKFragBytes);
     ws.hrec = take(C * Hv * kRecBytes);
     ws.seg_info = reinterpret_cast<int4 *>(take(M * sizeof(int4)));
     ws.seq_seg = reinterpret_cast<int4 *>(take((size_t)N * sizeof(int4)));
-    ws.seg_bad = reinterpret_cast<int *>(take(M * Hv * sizeof(int)));
     ws.bstate = reinterpret_cast<float *>(take(M * Hv * kStateFloats * sizeof(float)));
+    ws.seg_done = reinterpret_cast<int *>(take((size_t)N * Hv * sizeof(int)));
     return ws;
 }
 
@@ -1516,14 +1506,9 @@ hipError_t launch_prefill(const PrefillArgs &p, void *workspace, hipStream_t str
     const int G = p.Hv / p.Hqk;
     const long seg_groups = (long)p.max_segs * p.Hqk;
     const long seg_blocks = ((seg_groups + 7) / 8) * 8L * G;
-    hipLaunchKernelGGL(chain_kernel<false>, dim3((unsigned)seg_blocks), dim3(kChainThreads), 0, stream, p, ws);
+    hipLaunchKernelGGL(chain_kernel, dim3((unsigned)seg_blocks), dim3(kChainThreads), 0, stream, p, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = mark(3)) != hipSuccess) return e;
-    const long groups = (long)p.N * p.Hqk;
-    const long blocks = ((groups + 7) / 8) * 8L * G;
-    hipLaunchKernelGGL(chain_kernel<true>, dim3((unsigned)blocks), dim3(kChainThreads), 0, stream, p, ws);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    return mark(4);
+    return mark(3);
 }
 
 }  // namespace gdn
