@@ -20,10 +20,13 @@ sources they were taken on.
 
 Timing: HIP events on the stream the library launches on.  The step time is
 K plain gdn_prefill calls between two events; the same K steps are then run
-through gdn_prefill_with_events, which records an event after each of the
-five kernels, for the per-kernel times the roofline uses.  A decode step (two
-kernels) is timed per call.  The CPU baseline is the fp64
-oracle, as it stands, on a bounded sample of the same prefill workload.
+through gdn_prefill_with_events, which records an event after each of its
+kernels (chunk-table setup, parallel pass, sequential pass), for the
+per-kernel times the roofline uses.  The default 200 warm-up steps (about
+70 ms of GPU work) let the clocks settle: after 30 the prefill still runs
+about 10 % slower.  A decode step (two kernels) is timed per call.  The CPU
+baseline is the fp64 oracle, as it stands, on a bounded sample of the same
+prefill workload.
 """
 import argparse
 import ctypes
@@ -117,7 +120,7 @@ def source_digest():
 
 
 COPY_BYTES = 256 << 20
-TRAFFIC_KERNELS = {"prefill_chain": "chain_kernel(", "prefill_prep": "prep_kernel",
+TRAFFIC_KERNELS = {"prefill_chain": "chain_kernel", "prefill_prep": "prep_kernel",
                    "prefill_setup": "setup_kernel", "decode": "decode_step_kernel",
                    "decode_conv_shift": "conv_shift_qk_kernel<1>",
                    "decode_multi": "decode_head_kernel<4>", "decode_multi_conv_shift": "conv_shift_qk_kernel<4>"}
@@ -374,7 +377,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--traffic-report", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
