@@ -62,7 +62,7 @@ struct Workspace {
     int4 *seg_info;     // [max_segs] {seq, first chunk, end chunk, 1: first of seq | 2: last of seq}; seq -1 = unused
     int4 *seq_seg;      // [N] {first segment, segments, -, -}
     float *bstate;      // [max_segs][Hv][128][128] final state of a segment (read when its successor is recomputed)
-    int *seg_done;      // [N][Hv] segments of the pair finished, + 2^16 per missed warm-up bound (zeroed by the parallel pass)
+    int *seg_done;      // [N][Hv] segments of the pair finished, when the in-order walk is needed (zeroed by the parallel pass)
 };
 
 // Segments of the sequential pass: each sequence's chunks are cut into runs

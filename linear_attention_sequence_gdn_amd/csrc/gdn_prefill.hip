@@ -1238,12 +1238,17 @@ constexpr int kMaxWarm = 64;  // chunks a segment looks back at most (one per la
 // chunk 0 = c0): c0 (exact start from the initial state), a chunk in
 // (c0, cb) (start from zero), or -1 when the bound is not met within
 // kMaxWarm chunks.  Wave-uniform, and identical in every block that asks.
-__device__ __forceinline__ int warm_start(const Workspace &ws, int h, int Hv, int cb, int c0, int lane)
+// In two steps, so that several segments' gate loads can be in flight together:
+// warm_gate loads log2 of chunk cb-1-lane's decay, warm_pick decides.
+__device__ __forceinline__ float warm_gate(const Workspace &ws, int h, int Hv, int cb, int c0, int lane)
+{
+    const int c = cb - 1 - lane;
+    return c >= c0 ? reinterpret_cast<const float *>(ws.hrec + ((long)c * Hv + h) * kRecBytes + kRecG)[129] : 0.f;
+}
+__device__ __forceinline__ int warm_pick(float gsum, int cb, int c0, int lane)
 {
     if (cb <= c0) return c0;
-    const int c = cb - 1 - lane;
-    const bool in = c >= c0;
-    float gsum = in ? reinterpret_cast<const float *>(ws.hrec + ((long)c * Hv + h) * kRecBytes + kRecG)[129] : 0.f;
+    const bool in = cb - 1 - lane >= c0;
     // inclusive prefix over lanes: log2 of the decay of chunks cb-1-lane .. cb-1
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -1255,6 +1260,10 @@ __device__ __forceinline__ int warm_start(const Workspace &ws, int h, int Hv, in
     if (hit) w = cb - 1 - __builtin_ctzll(hit);
     else w = (cb - c0 <= kMaxWarm) ? c0 : -1;
     return __builtin_amdgcn_readfirstlane(w);
+}
+__device__ __forceinline__ int warm_start(const Workspace &ws, int h, int Hv, int cb, int c0, int lane)
+{
+    return warm_pick(cb > c0 ? warm_gate(ws, h, Hv, cb, c0, lane) : 0.f, cb, c0, lane);
 }
 
 // state columns 32w .. 32w+31 of one (sequence, head): tile (dt, x) element e
@@ -1290,16 +1299,15 @@ __device__ __forceinline__ void state_store(const f32x4 (&S)[8][kChainCT], float
 }
 
 // Sequential pass: one workgroup per (segment, V head); segments run in
-// parallel, each from its warm-up start.  The last workgroup of a (sequence,
-// V head) to finish -- a device-scope counter per pair, zeroed by the
-// parallel pass, which also counts the segments that missed their warm-up
-// bound -- then walks the sequence's segments in order and recomputes,
-// exactly from the state the previous segment handed over, those whose bound
-// was not met; for in-place calls it also hands a sequence of several
-// segments its final state.  Only a workgroup whose parked state that walk
-// will read publishes it with a device-scope fence, so the common case (no
-// failed bound, out of place) costs one atomic per workgroup.
-constexpr int kSegBadUnit = 1 << 16;  // counter increment of a segment that missed its bound
+// parallel, each from its warm-up start.  Every workgroup makes the warm-up
+// test of all segments of its sequence.  If one misses its bound, or the
+// call is in place, the last workgroup of the (sequence, V head) to finish --
+// a device-scope counter per pair, zeroed by the parallel pass -- walks the
+// sequence's segments in order and recomputes, exactly from the state the
+// previous segment handed over, those whose bound was not met, and hands a
+// sequence of several segments its final state.  Only a workgroup whose
+// parked state that walk will read publishes it with a device-scope fence;
+// the common case (no failed bound, out of place) needs no counter at all.
 __global__ __launch_bounds__(kChainThreads) __attribute__((amdgpu_waves_per_eu(kChainWaves / 4, kChainWaves / 4)))
 void chain_kernel(PrefillArgs p, Workspace ws)
 {
@@ -1336,7 +1344,33 @@ void chain_kernel(PrefillArgs p, Workspace ws)
         for (int m = 0; m < 2; ++m) wb[x][m] = conv_tap_frag(p.conv_w, cv + kCW * wave + 16 * x + (lane & 15), m, lane);
     f32x4 S[8][kChainCT];
 
-    const int w = first ? sg.y : warm_start(ws, h, Hv, sg.y, si.x, lane);
+    // The warm-up test of every segment of the sequence, the same in every
+    // workgroup of it (gate loads of four segments in flight together): this
+    // segment's start, whether the next one misses its bound, and whether
+    // any does.
+    const int2 ss = Tables::seq_segs(p, ws, s);  // first segment, segments
+    const int nseg = min(ss.y, p.max_segs - ss.x), i_seg = k - ss.x;
+    int w = sg.y;
+    bool any_bad = false, next_bad = false;
+    for (int i0 = 1; i0 < nseg; i0 += 4) {
+        int cb[4];
+        float gv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u;
+            cb[u] = i < nseg ? Tables::seg(p, ws, ss.x + i).y : si.x;
+            gv[u] = i < nseg ? warm_gate(ws, h, Hv, cb[u], si.x, lane) : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u;
+            if (i >= nseg) continue;
+            const int wi = warm_pick(gv[u], cb[u], si.x, lane);
+            any_bad |= wi < 0;
+            if (i == i_seg) w = wi;
+            if (i == i_seg + 1) next_bad = wi < 0;
+        }
+    }
     if (w >= 0) {  // else recomputed in order below
         state_load(S, w == si.x && p.state_in ? p.state_in + sbase : nullptr, wave, lane);
         chain_run(p, ws, buf0, buf1, stage, S, wb, ChainRun{si.x, si.z, si.w, w, sg.z, sg.y, vs, hist}, h, g, wave,
@@ -1373,26 +1407,16 @@ void chain_kernel(PrefillArgs p, Workspace ws)
         }
     }
 
-    // this segment is done
-    const int2 ss = Tables::seq_segs(p, ws, s);  // first segment, segments
-    const int nseg = min(ss.y, p.max_segs - ss.x), i_seg = k - ss.x;
-    if (nseg <= 1) return;
-    // publish the parked state if the in-order walk will read it: when the
-    // next segment misses its bound (the same test it makes itself), or for
-    // the final state of an in-place call
-    const bool publish = (i_seg + 1 < nseg && warm_start(ws, h, Hv, Tables::seg(p, ws, k + 1).y, si.x, lane) < 0) ||
-                         (i_seg == nseg - 1 && p.defer_final);
-    if (publish) __threadfence();
+    // The in-order walk, if any segment missed its bound or the call is in
+    // place: the last workgroup of the sequence to finish does it.  A
+    // workgroup publishes its parked state first if the walk will read it
+    // (the next segment is recomputed, or the final state of an in-place call).
+    if (nseg <= 1 || (!any_bad && !p.defer_final)) return;
+    if (next_bad || (i_seg == nseg - 1 && p.defer_final)) __threadfence();
     __syncthreads();
-    if (t == 0) {
-        const int add = 1 + (w < 0 ? kSegBadUnit : 0);
-        s_total = atomicAdd(ws.seg_done + (long)s * Hv + h, add) + add;
-    }
+    if (t == 0) s_total = atomicAdd(ws.seg_done + (long)s * Hv + h, 1) + 1;
     __syncthreads();
-    const int total = s_total;
-    if (total % kSegBadUnit != nseg) return;  // not the last to finish
-    const bool any_bad = total >= kSegBadUnit;
-    if (!any_bad && !p.defer_final) return;
+    if (s_total != nseg) return;  // not the last to finish
     __threadfence();
     bool carry = false;  // S holds the final state of the previous segment
     for (int i = 1; any_bad && i < nseg; ++i) {  // a sequence's first segment is never recomputed
