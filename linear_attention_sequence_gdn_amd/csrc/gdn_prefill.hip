@@ -742,12 +742,13 @@ void prep_kernel(PrefillArgs p, Workspace ws)
 // ---------------------------------------------------------------------------
 // chain: the sequential state carry
 // ---------------------------------------------------------------------------
-// Workgroup = one (segment, V head), 4 waves; wave w owns the state columns
-// 32w .. 32w+31 (two 16-column tiles) in every product of a chunk:
-//   v^ = SiLU(conv v)                  64 tokens x 32 channels, over 4 taps
-//   X = K S,  Q S                      64 tokens x 32 columns, over d_k
-//   Vnew = T' (v^ - diag(Gam) X)       64 tokens x 32 columns, over the chunk
-//   S <- Gam_n S + k^T (r Vnew)        d_k x 32 columns, over the chunk
+// Workgroup = one (segment, V head), 8 waves (kChainCT = 1); wave w owns the
+// state columns kCW w .. kCW w + kCW - 1 (kChainCT 16-column tiles) in every
+// product of a chunk:
+//   v^ = SiLU(conv v)                  64 tokens x kCW channels, over 4 taps
+//   X = K S,  Q S                      64 tokens x kCW columns, over d_k
+//   Vnew = T' (v^ - diag(Gam) X)       64 tokens x kCW columns, over the chunk
+//   S <- Gam_n S + k^T (r Vnew)        d_k x kCW columns, over the chunk
 //   O = diag(q_scale Gam) Q S + P Vnew
 // The B operands of these products are the wave's own accumulators: with the
 // kappa k-mapping, a lane's accumulator rows 4q..4q+3 of two vertically
@@ -759,7 +760,8 @@ void prep_kernel(PrefillArgs p, Workspace ws)
 // v rows), which the workgroup stages in LDS with direct-to-LDS loads into
 // two buffers, one barrier per chunk.  Waiting for a chunk's operands never
 // waits for the output stores: they are the only memory operations issued
-// after the operand loads.
+// after the operand loads (a warm-up step, which stores nothing, waits for
+// its operand loads at its end).
 constexpr int kChainBlocksPerHead = 1;
 constexpr int kVTileRows = 68;  // raw v rows of a chunk: 1 unused, 3 before the chunk, 64
 struct ChainBuf {
@@ -1266,8 +1268,8 @@ __device__ __forceinline__ int warm_start(const Workspace &ws, int h, int Hv, in
     return warm_pick(cb > c0 ? warm_gate(ws, h, Hv, cb, c0, lane) : 0.f, cb, c0, lane);
 }
 
-// state columns 32w .. 32w+31 of one (sequence, head): tile (dt, x) element e
-// is row 16dt + 4q + e, column 32w + 16x + c16
+// state columns kCW w .. kCW w + kCW - 1 of one (sequence, head): tile (dt, x)
+// element e is row 16dt + 4q + e, column kCW w + 16x + c16
 __device__ __forceinline__ void state_load(f32x4 (&S)[8][kChainCT], const float *src, int wave, int lane)
 {
     const int q4 = lane >> 4, c16 = lane & 15;
