@@ -780,6 +780,17 @@ constexpr int kCW = 16 * kChainCT;                      // state columns (and v 
 constexpr int kChainStageRows = 64;                    // token rows of the output staging (the chunk)
 constexpr int kChainStage = kChainStageRows * kCW * 2;  // output staging of one wave (bf16)
 
+// Byte offset in a wave's output staging of token row R, 16-byte piece p of
+// the row, 8-byte half e.  The pieces of rows 8..15 of each 16-row tile are
+// swapped in pairs (p ^ 1 with 32-byte rows, p ^ 2 with 64-byte ones), so
+// that the staging writes (a lane per (row, 8 bytes), sixteen rows at a time)
+// hit distinct banks in each half of the wave; a read of whole rows is a
+// permutation within them.
+__device__ __forceinline__ int stage_offset(int R, int p, int e)
+{
+    return R * (2 * kCW) + ((p ^ (((R >> 3) & 1) * kChainCT)) << 4) + (e << 3);
+}
+
 // k^ in LDS: the sixteen operand fragments (token tile rt, d block kb) in
 // order, the 64 16-byte lane slots of each stored permuted: lane (q, r)
 // (row r of the tile, d = 32kb + 4q .. +3 and +16) sits in slot
@@ -1155,7 +1166,7 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
             for (int rt = 2 * (pr - 1); rt < 2 * pr && rt < 4; ++rt)
 #pragma unroll
                 for (int x = 0; x < kChainCT; ++x)
-                    *reinterpret_cast<u32x2 *>(os + (16 * rt + c16) * kCW + 16 * x + 4 * q4) =
+                    *reinterpret_cast<u32x2 *>(os + stage_offset(16 * rt + c16, 2 * x + (q4 >> 1), q4 & 1) / 2) =
                         u32x2{pack_bf16x2(oacc[rt][x][0], oacc[rt][x][1]), pack_bf16x2(oacc[rt][x][2], oacc[rt][x][3])};
         }
     }
@@ -1180,11 +1191,11 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
         if constexpr (kChainCT == 2) {
-            const i32x4 v = *reinterpret_cast<const i32x4 *>(stage + (16 * rt + row) * 64 + piece * 16);
+            const i32x4 v = *reinterpret_cast<const i32x4 *>(stage + stage_offset(16 * rt + row, piece, 0));
             __builtin_amdgcn_raw_buffer_store_b128(v, ro, (16 * rt + row) * rowb + piece * 16, 0, 0);
         } else {
             typedef int i32x2 __attribute__((ext_vector_type(2)));
-            const i32x2 v = *reinterpret_cast<const i32x2 *>(stage + (16 * rt + row) * 32 + piece * 8);
+            const i32x2 v = *reinterpret_cast<const i32x2 *>(stage + stage_offset(16 * rt + row, piece >> 1, piece & 1));
             __builtin_amdgcn_raw_buffer_store_b64(v, ro, (16 * rt + row) * rowb + piece * 8, 0, 0);
         }
     }
