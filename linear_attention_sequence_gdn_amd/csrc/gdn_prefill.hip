@@ -1017,22 +1017,13 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
     const float *gt = reinterpret_cast<const float *>(cur + ChainBuf::kG);
     const uint8_t *vt = cur + ChainBuf::kV;
 
-    // conv of v at the wave's channels (pre-activation), on the matrix cores
-    f32x4 Z[4][kChainCT];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int x = 0; x < kChainCT; ++x) {
-            Z[rt][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(conv_row_frag(vt, rt, x, 0, wave, lane), wb[x][0],
-                                                               f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            Z[rt][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(conv_row_frag(vt, rt, x, 1, wave, lane), wb[x][1],
-                                                               Z[rt][x], 0, 0, 0);
-        }
-
     // K S and (Q S)^T over the four 32-row blocks of the state; the LDS
     // fragments of block kb+1 are read while block kb multiplies, the next
-    // chunk's DMA goes out one group per block, and SiLU of a quarter of the
-    // conv runs on the vector ALUs meanwhile
+    // chunk's DMA goes out one group per block.  The conv of v at the wave's
+    // channels (pre-activation, on the matrix cores) goes out after the first
+    // block's products, its operands read with that block's; SiLU of conv
+    // tile kb-1 runs on the vector ALUs during block kb, of tile 3 after.
+    f32x4 Z[4][kChainCT];
     f32x4 X[4][kChainCT], QST[kChainCT][4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
@@ -1049,6 +1040,15 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
             ak[rt] = ktile_frag(kt, rt, kb, lane);
             if (kOut) aq[rt] = Qf[(rt * 4 + kb) * 64];
         }
+        bf16x8 cv[4][kChainCT][2];
+        if (kb == 0) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int x = 0; x < kChainCT; ++x)
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) cv[rt][x][m] = conv_row_frag(vt, rt, x, m, wave, lane);
+        }
         if (kb == 0) chain_dma_group<0>(dn, nxt, wave, lane);
         if (kb == 1) chain_dma_group<1>(dn, nxt, wave, lane);
         if (kb == 2) chain_dma_group<2>(dn, nxt, wave, lane);
@@ -1064,10 +1064,23 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
             const int rt = sl / (2 * kChainCT), r = sl % (2 * kChainCT);
             if (r < kChainCT) X[rt][r] = mfma16(ak[rt], sb[r], X[rt][r]);
             else if (kOut) QST[r - kChainCT][rt] = mfma16(sb[r - kChainCT], aq[rt], QST[r - kChainCT][rt]);
-            if (sl < 4 * kChainCT) Z[kb][sl >> 2][sl & 3] = silu_f(Z[kb][sl >> 2][sl & 3]);
+            if (kb > 0 && sl < 4 * kChainCT) Z[kb - 1][sl >> 2][sl & 3] = silu_f(Z[kb - 1][sl >> 2][sl & 3]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (kb == 0) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int x = 0; x < kChainCT; ++x) {
+                    Z[rt][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cv[rt][x][0], wb[x][0], f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                       0, 0, 0);
+                    Z[rt][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cv[rt][x][1], wb[x][1], Z[rt][x], 0, 0, 0);
+                }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+#pragma unroll
+    for (int sl = 0; sl < 4 * kChainCT; ++sl) Z[3][sl >> 2][sl & 3] = silu_f(Z[3][sl >> 2][sl & 3]);
     // Vnew = T' (v^ - diag(Gam) X): the bracket as B operands over the chunk's
     // two 32-token blocks, T' lower triangular
     half8 tf[6];
