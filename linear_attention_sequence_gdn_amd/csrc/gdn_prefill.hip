@@ -70,6 +70,22 @@ __device__ __forceinline__ half8 lds_frag(const _Float16 *M, int ld, int r0, int
 
 __device__ __forceinline__ uint32_t ld_pair(const uint16_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
 
+// The q^ and k^ operand fragments the sequential pass reads hold their two
+// 8-byte halves in swapped order in the lanes of odd lane groups (lane / 16
+// odd): element i of such a lane is contraction index kappa(q, i ^ 4).  The
+// state operand they meet is packed the same way, so the products are
+// unchanged; what it buys is that the transposed reads of k^ (which read one
+// half of each 16-byte lane slot, and whose half-wave touches two slots of
+// every bank group) fetch the two slots of a bank group from opposite halves:
+// no bank conflicts.
+__device__ __forceinline__ half8 swap_halves_if(half8 f, bool odd)
+{
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 u = __builtin_bit_cast(u32x4, f);
+    const u32x4 w = odd ? u32x4{u[2], u[3], u[0], u[1]} : u;
+    return __builtin_bit_cast(half8, w);
+}
+
 // Conv taps of channels (2*pp, 2*pp+1), tap 3 = current token
 struct ConvW {
     float a[4], b[4];
@@ -517,8 +533,8 @@ void prep_kernel(PrefillArgs p, Workspace ws)
         half8 *kf = reinterpret_cast<half8 *>(ws.kfrag + gc * kKFragBytes);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            qf[(wave * 4 + kb) * 64 + lane] = lds_frag(Qs, kQ_LD, 16 * wave, 32 * kb, lane);
-            kf[(wave * 4 + kb) * 64 + lane] = lds_frag(Ks, kQ_LD, 16 * wave, 32 * kb, lane);
+            qf[(wave * 4 + kb) * 64 + lane] = swap_halves_if(lds_frag(Qs, kQ_LD, 16 * wave, 32 * kb, lane), q4 & 1);
+            kf[(wave * 4 + kb) * 64 + lane] = swap_halves_if(lds_frag(Ks, kQ_LD, 16 * wave, 32 * kb, lane), q4 & 1);
         }
 #pragma unroll
         for (int i = 0; i < 3; ++i) {
@@ -957,15 +973,16 @@ __device__ __forceinline__ half8 ktile_frag(const uint8_t *kt, int rt, int kb, i
 // .. +3.  A transposed read hands lane i of each 16-lane group element i % 4
 // of the 8 bytes that lane 4j + i / 4 of the group addressed, as its element
 // j; so lane s of group q addresses token row R = 32tb + 4q + s / 4, d
-// columns 16dt + 4 (s % 4) .. +3: the half dt % 2 of slot (s % 4, R % 16) of
-// fragment (R / 16, dt / 2).
+// columns 16dt + 4 (s % 4) .. +3: half dt % 2 of slot (s % 4, R % 16) of
+// fragment (R / 16, dt / 2), stored as half (dt + s) % 2 (the halves of odd
+// lane groups are swapped, see swap_halves_if).
 __device__ __forceinline__ half8 ktile_frag_t(const uint8_t *kt, int dt, int tb, int lane)
 {
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     const int q4 = lane >> 4, s = lane & 15;
     const int R = 32 * tb + 4 * q4 + (s >> 2);
-    const uint8_t *p0 = kt + ((R >> 4) * 4 + (dt >> 1)) * 1024 + kslot(s & 3, R & 15) * 16 + 8 * (dt & 1);
+    const uint8_t *p0 = kt + ((R >> 4) * 4 + (dt >> 1)) * 1024 + kslot(s & 3, R & 15) * 16 + 8 * ((dt ^ s) & 1);
     const uint8_t *p1 = p0 + 4 * 1024;  // token rows + 16: the next token tile
     const half4 lo = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                                    (lds_s16x4 *)(__attribute__((address_space(3))) uint8_t *)(p0)));
@@ -1056,7 +1073,7 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
         __builtin_amdgcn_sched_barrier(0);
         half8 sb[kChainCT];
 #pragma unroll
-        for (int x = 0; x < kChainCT; ++x) sb[x] = pack_h8(S[2 * kb][x], S[2 * kb + 1][x]);
+        for (int x = 0; x < kChainCT; ++x) sb[x] = swap_halves_if(pack_h8(S[2 * kb][x], S[2 * kb + 1][x]), q4 & 1);
         // per token tile: the X products of the wave's column tiles, then the
         // (Q S)^T ones; SiLU of conv tile kb, one value per slot
 #pragma unroll
