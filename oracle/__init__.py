@@ -62,6 +62,12 @@ def _load():
         lib.gdn_ref_prefill.restype = i
         lib.gdn_ref_prefill.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, i, i, i, i, i,
                                         d, d, _P, i, _P, _P, _P]
+        lib.gdn_ref_prefill_f64.restype = i
+        lib.gdn_ref_prefill_f64.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, i, i, i, i, i,
+                                            d, d, _P, _P]
+        lib.gdn_ref_prefill_backward.restype = i
+        lib.gdn_ref_prefill_backward.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, i, i, i, i, i,
+                                                 d, d, i, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
         lib.gdn_ref_decode_step.restype = i
         lib.gdn_ref_decode_step.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, i, i, i, i, i,
                                             d, d, _P]
@@ -183,6 +189,86 @@ def prefill(q, k, v, a, b, conv_w, cu_seqlens, *, Hqk, Hv, gate_scale,
     if rc != 0:
         raise ValueError("oracle prefill: bad arguments")
     return o, so, cso
+
+
+def prefill_f64(q, k, v, a, b, conv_w, cu_seqlens, *, Hqk, Hv, gate_scale,
+                q_scale=1.0, state_in=None, conv_state_in=None):
+    """The mixer with every input given in float64 (q, k, v [T_tot][H][d], a,
+    b [T_tot][Hv], conv_w [C_tot][4], conv_state_in [N][3][C_tot]): the
+    forward that finite differences perturb.  Returns (o, state_out)."""
+    q, pq = _c(q, np.float64)
+    k, pk = _c(k, np.float64)
+    v, pv = _c(v, np.float64)
+    a, pa = _c(a, np.float64)
+    b, pb = _c(b, np.float64)
+    w, pw = _c(conv_w, np.float64)
+    cu, pcu = _c(cu_seqlens, np.int32)
+    T_tot, _, dk = q.shape
+    dv = v.shape[2]
+    N = cu.shape[0] - 1
+    pcs = None
+    if conv_state_in is not None:
+        cs, pcs = _c(conv_state_in, np.float64)
+    pst = None
+    if state_in is not None:
+        st, pst = _c(state_in, np.float64)
+    o = np.zeros((T_tot, Hv, dv), np.float64)
+    so = np.zeros((N, Hv, dk, dv), np.float64)
+    rc = _load().gdn_ref_prefill_f64(pq, pk, pv, pa, pb, pw, pcs, pst, pcu, N, Hqk, Hv, dk, dv,
+                                     float(gate_scale), float(q_scale), o.ctypes.data_as(_P),
+                                     so.ctypes.data_as(_P))
+    if rc != 0:
+        raise ValueError("oracle prefill_f64: bad arguments")
+    return o, so
+
+
+def prefill_backward(q, k, v, a, b, conv_w, cu_seqlens, d_o, *, Hqk, Hv, gate_scale,
+                     q_scale=1.0, state_in=None, conv_state_in=None, d_state_out=None,
+                     f64=None):
+    """Gradient of sum <d_o, o> + <d_state_out, state_out> with respect to
+    every input of the mixer.  Inputs as ``prefill`` (bf16 as uint16, a/b
+    fp32) or all float64 (``f64``; inferred from q's dtype when None).
+
+    Returns a dict of float64 arrays: q, k [T_tot][Hqk][dk]; v
+    [T_tot][Hv][dv]; a, b [T_tot][Hv]; conv_w [C_tot][4]; conv_state
+    [N][3][C_tot]; state [N][Hv][dk][dv]."""
+    if f64 is None:
+        f64 = np.asarray(q).dtype == np.float64
+    xt = np.float64 if f64 else np.uint16
+    gt = np.float64 if f64 else np.float32
+    q, pq = _c(q, xt)
+    k, pk = _c(k, xt)
+    v, pv = _c(v, xt)
+    a, pa = _c(a, gt)
+    b, pb = _c(b, gt)
+    w, pw = _c(conv_w, xt)
+    cu, pcu = _c(cu_seqlens, np.int32)
+    T_tot, _, dk = q.shape
+    dv = v.shape[2]
+    N = cu.shape[0] - 1
+    C_tot = 2 * Hqk * dk + Hv * dv
+    pcs = None
+    if conv_state_in is not None:
+        cs, pcs = _c(conv_state_in, xt)
+    pst = None
+    if state_in is not None:
+        st, pst = _c(state_in, np.float64)
+    do_, pdo = _c(d_o, np.float64)
+    pds = None
+    if d_state_out is not None:
+        ds, pds = _c(d_state_out, np.float64)
+    out = {"q": np.zeros((T_tot, Hqk, dk)), "k": np.zeros((T_tot, Hqk, dk)),
+           "v": np.zeros((T_tot, Hv, dv)), "a": np.zeros((T_tot, Hv)), "b": np.zeros((T_tot, Hv)),
+           "conv_w": np.zeros((C_tot, 4)), "conv_state": np.zeros((N, 3, C_tot)),
+           "state": np.zeros((N, Hv, dk, dv))}
+    P = {n: x.ctypes.data_as(_P) for n, x in out.items()}
+    rc = _load().gdn_ref_prefill_backward(pq, pk, pv, pa, pb, pw, pcs, pst, pcu, N, Hqk, Hv, dk, dv,
+                                          float(gate_scale), float(q_scale), int(bool(f64)), pdo, pds,
+                                          P["q"], P["k"], P["v"], P["a"], P["b"], P["conv_w"],
+                                          P["conv_state"], P["state"])
+    if rc != 0:
+        raise ValueError("oracle prefill_backward: bad arguments")
+    return out
 
 
 def decode_step(q, k, v, a, b, conv_w, conv_state, state, *, Hqk, Hv, gate_scale,
