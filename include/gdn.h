@@ -189,6 +189,50 @@ int gdn_decode_multi(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                      int B, int T, int Hqk, int Hv, int dk, int dv,
                      float gate_scale, float q_scale, void *stream);
 
+/* Bytes of device workspace gdn_prefill_backward needs for these sizes (0 when
+ * B * T = 0; about 0.36 MB per token at Hqk = 16, Hv = 48). */
+size_t gdn_prefill_backward_workspace_size(int B, int T, int Hqk, int Hv, int dk, int dv);
+
+/*
+ * Training backward of gdn_prefill: the gradients of
+ *     L = sum_t <grad_o_t, o_t> + <grad_state_out, state_out>
+ * with respect to every input, for B sequences of equal length T.  The
+ * chunked form of the update (the WY / chunk-parallel evaluation of the
+ * walkthrough's section 2.1; the FlashQLA announcement on the Qwen blog
+ * describes forward and backward kernels of this chunked training form) is
+ * differentiated line by line; all arithmetic is fp32.
+ *
+ *   q, k, v, a, b, conv_w, conv_state_in, state_in, gate_scale, q_scale:
+ *                    the forward call's inputs (conv_state_in, state_in may
+ *                    be NULL: zero history / zero state)
+ *   grad_o           [B][T][Hv][dv] bf16 gradient of o
+ *   grad_state_out   [B][Hv][dk][dv] fp32 gradient of state_out, or NULL (zero)
+ *   grad_q, grad_k   [B][T][Hqk][dk] fp32  (of the raw, pre-conv q, k)
+ *   grad_v           [B][T][Hv][dv] fp32
+ *   grad_a, grad_b   [B][T][Hv] fp32
+ *   grad_conv_w      [C_tot][4] fp32, summed over the batch
+ *   grad_conv_state_in [B][3][C_tot] fp32, or NULL (not computed): the
+ *                    gradient of the history rows (of zero rows when
+ *                    conv_state_in is NULL)
+ *   grad_state_in    [B][Hv][dk][dv] fp32, or NULL (not computed)
+ *   workspace        device, >= gdn_prefill_backward_workspace_size bytes,
+ *                    16-byte aligned; its contents are scratch
+ * Every gradient is overwritten (not accumulated).  Outputs must not overlap
+ * each other, the inputs or the workspace.  Pointers 4-byte aligned.  With
+ * T = 0, grad_state_in = grad_state_out (or zeros) and the conv gradients
+ * are zero.
+ */
+int gdn_prefill_backward(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                         const float *a, const float *b, const uint16_t *conv_w,
+                         const uint16_t *conv_state_in, const float *state_in,
+                         const uint16_t *grad_o, const float *grad_state_out,
+                         float *grad_q, float *grad_k, float *grad_v,
+                         float *grad_a, float *grad_b, float *grad_conv_w,
+                         float *grad_conv_state_in, float *grad_state_in,
+                         int B, int T, int Hqk, int Hv, int dk, int dv,
+                         float gate_scale, float q_scale,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -70,6 +70,10 @@ def lib():
         L.gdn_prefill_varlen.argtypes = [_P] * 12 + [_I] * 6 + [_F, _F, _P, _SZ, _P]
         L.gdn_decode_step.restype = _I
         L.gdn_decode_step.argtypes = [_P] * 10 + [_I] * 5 + [_F, _F, _P]
+        L.gdn_prefill_backward_workspace_size.restype = _SZ
+        L.gdn_prefill_backward_workspace_size.argtypes = [_I] * 6
+        L.gdn_prefill_backward.restype = _I
+        L.gdn_prefill_backward.argtypes = [_P] * 18 + [_I] * 6 + [_F, _F, _P, _SZ, _P]
         L.gdn_decode_multi.restype = _I
         L.gdn_decode_multi.argtypes = [_P] * 11 + [_I] * 7 + [_F, _F, _P]
         _lib = L
@@ -165,6 +169,58 @@ def gdn_prefill(q, k, v, a, b, conv_w, *, gate_scale, q_scale=1.0, state_in=None
     if rc != GDN_OK:
         raise GDNError("gdn_prefill", rc)
     return o, state_out, conv_state_out
+
+
+def gdn_prefill_backward_workspace_size(B, T, Hqk, Hv, dk=128, dv=128) -> int:
+    return int(lib().gdn_prefill_backward_workspace_size(B, T, Hqk, Hv, dk, dv))
+
+
+def gdn_prefill_backward(q, k, v, a, b, conv_w, grad_o, *, gate_scale, q_scale=1.0,
+                         state_in=None, conv_state_in=None, grad_state_out=None,
+                         want_conv_state=False, want_state=True, workspace=None, stream=None):
+    """Gradients of sum <grad_o, o> + <grad_state_out, state_out> of
+    ``gdn_prefill`` with respect to its inputs (fp32 tensors).
+
+    grad_o: [B][T][Hv][128] bf16; grad_state_out: [B][Hv][128][128] fp32 or
+    None.  Returns a dict with q, k, v, a, b, conv_w and, when asked for,
+    conv_state [B][3][C_tot] and state [B][Hv][128][128].
+    """
+    torch = _torch()
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    C_tot = 2 * Hqk * dk + Hv * dv
+    bf, f32 = torch.bfloat16, torch.float32
+    _check(q, "q", bf, (B, T, Hqk, dk))
+    _check(k, "k", bf, (B, T, Hqk, dk))
+    _check(v, "v", bf, (B, T, Hv, dv))
+    _check(a, "a", f32, (B, T, Hv))
+    _check(b, "b", f32, (B, T, Hv))
+    _check(conv_w, "conv_w", bf, (C_tot, 4))
+    _check(state_in, "state_in", f32, (B, Hv, dk, dv))
+    _check(conv_state_in, "conv_state_in", bf, (B, 3, C_tot))
+    _check(grad_o, "grad_o", bf, (B, T, Hv, dv))
+    _check(grad_state_out, "grad_state_out", f32, (B, Hv, dk, dv))
+    dev = q.device
+    g = {"q": torch.empty((B, T, Hqk, dk), dtype=f32, device=dev),
+         "k": torch.empty((B, T, Hqk, dk), dtype=f32, device=dev),
+         "v": torch.empty((B, T, Hv, dv), dtype=f32, device=dev),
+         "a": torch.empty((B, T, Hv), dtype=f32, device=dev),
+         "b": torch.empty((B, T, Hv), dtype=f32, device=dev),
+         "conv_w": torch.empty((C_tot, 4), dtype=f32, device=dev),
+         "conv_state": torch.empty((B, 3, C_tot), dtype=f32, device=dev) if want_conv_state else None,
+         "state": torch.empty((B, Hv, dk, dv), dtype=f32, device=dev) if want_state else None}
+    need = gdn_prefill_backward_workspace_size(B, T, Hqk, Hv, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rc = lib().gdn_prefill_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(conv_w), _ptr(conv_state_in),
+        _ptr(state_in), _ptr(grad_o), _ptr(grad_state_out), _ptr(g["q"]), _ptr(g["k"]),
+        _ptr(g["v"]), _ptr(g["a"]), _ptr(g["b"]), _ptr(g["conv_w"]), _ptr(g["conv_state"]),
+        _ptr(g["state"]), B, T, Hqk, Hv, dk, dv, float(gate_scale), float(q_scale),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != GDN_OK:
+        raise GDNError("gdn_prefill_backward", rc)
+    return {n: t for n, t in g.items() if t is not None}
 
 
 def gdn_prefill_varlen(q, k, v, a, b, conv_w, cu_seqlens, *, gate_scale, q_scale=1.0,

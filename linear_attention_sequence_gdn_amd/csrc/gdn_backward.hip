@@ -1,0 +1,945 @@
+// gdn_backward.hip -- gradients of the chunked GDN prefill (training
+// backward), for B sequences of equal length T, on gfx950.
+//
+// The forward, per chunk of n <= 64 tokens of one (sequence, V head), with S
+// the state entering the chunk, gamma the in-chunk cumulative log decay (Gam =
+// e^gamma, gamma_n = gamma of the last token), beta the write strengths:
+//   A   = strict_lower(diag(beta) K K^T * D),   D_ij = e^(gamma_i - gamma_j)
+//   X   = (I + A)^-1,   T' = X diag(beta)
+//   Vt  = V - diag(Gam) K S                      (what the state mispredicts)
+//   Vn  = T' Vt
+//   O   = q_scale (diag(Gam) Q S + P Vn),        P = Q K^T * D, lower incl. diagonal
+//   S'  = Gam_n S + Ks^T Vn,                      Ks = diag(e^(gamma_n - gamma)) K
+// (the WY / chunk-parallel form of the update of the local-inference
+// walkthrough, section 2.1; the Qwen FlashQLA announcement describes forward
+// and backward kernels of this chunked form).  The backward applies the chain
+// rule to each of these lines in reverse; the derivative of the inverse is
+// dL = -X^T dX X^T.  Everything here is fp32 on the vector ALUs.
+//
+// Passes (one launch each):
+//   bwd_prep_kernel    conv + SiLU (+ L2 norm) of q, k, v; gates and gamma
+//   bwd_local_kernel   per (chunk, V head): P and X = (I + A)^-1
+//   bwd_fwd_kernel     per (sequence, V head, 16 state columns), in order:
+//                      the state entering every chunk, Vt and Vn
+//   bwd_chain_kernel   per (sequence, V head, 16 columns), in reverse: the
+//                      state gradient at every chunk end, dVn and dVt (= dv^)
+//   bwd_grad_kernel    per (chunk, V head): dq^, dk^ (per V head), dgamma,
+//                      dbeta -> grad_a, grad_b
+//   bwd_dy_kernel      per (chunk, channel plane): back through the L2 norm
+//                      and SiLU to the conv output
+//   bwd_conv_kernel    per (chunk, channel plane): back through the conv to
+//                      q, k, v, the carried conv rows and per-chunk partial
+//                      conv weight gradients
+//   bwd_dw_kernel      the conv weight gradient, summed over chunks in order
+// The state columns are independent in the update, so the two sequential
+// passes split them over eight workgroups per (sequence, V head).
+#include "../../include/gdn.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_common.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kBT = 256;  // threads of every backward workgroup
+constexpr int kCB = 16;   // state columns per workgroup of the sequential passes
+constexpr int kLK = 129;  // LDS row stride of 64 x 128 fp32 tiles
+constexpr int kLN = 65;   // LDS row stride of 64 x 64 fp32 tiles
+constexpr int kLC = 17;   // LDS row stride of 64 x 16 fp32 column slices
+constexpr int kNCB = kD / kCB;
+
+struct BwdArgs {
+    const uint16_t *q, *k, *v;
+    const float *a, *b;
+    const uint16_t *conv_w, *conv_state_in;
+    const float *state_in;
+    const uint16_t *grad_o;
+    const float *grad_state_out;
+    float *grad_q, *grad_k, *grad_v, *grad_a, *grad_b, *grad_conv_w, *grad_conv_state_in, *grad_state_in;
+    int B, T, Hqk, Hv, nc;
+    float gate_scale, q_scale;
+};
+
+// Workspace (fp32).  tok = s*T + t; rows of a chunk beyond its length are
+// never written or read.
+struct BwdWs {
+    float *qh, *kh;     // [tok][Hqk][128]  q^, k^
+    float *vh;          // [tok][Hv][128]   v^
+    float *gam, *beta;  // [tok][Hv]        gamma (natural log), beta
+    float *X, *P;       // [chunk][Hv][64][64]
+    float *Sc, *dSc;    // [chunk][Hv][128][128]  state entering / gradient leaving
+    float *vt, *vn;     // [tok][Hv][128]   Vt, Vn
+    float *dvn, *dvh;   // [tok][Hv][128]   dVn, dVt = dv^
+    float *dqp, *dkp;   // [tok][Hv][128]   dq^, dk^ of each V head
+    float *dy;          // [tok][C_tot]     gradient of the conv outputs
+    float *dwp;         // [chunk][C_tot][4] conv weight gradient of each chunk
+};
+
+__device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + expf(-x)); }
+__device__ __forceinline__ float silu_grad(float y)
+{
+    const float s = sigm(y);
+    return s * (1.0f + y * (1.0f - s));
+}
+
+// channel plane -> tensor, head and conv channel base
+struct Plane {
+    int kind, head;  // kind 0 q, 1 k, 2 v
+    long ch0;        // first conv channel
+    long ld;         // elements per token row of the tensor
+};
+__device__ __forceinline__ Plane plane_of(const BwdArgs &p, int pl)
+{
+    if (pl < p.Hqk) return Plane{0, pl, (long)pl * kD, (long)p.Hqk * kD};
+    if (pl < 2 * p.Hqk) return Plane{1, pl - p.Hqk, (long)p.Hqk * kD + (long)(pl - p.Hqk) * kD, (long)p.Hqk * kD};
+    const int h = pl - 2 * p.Hqk;
+    return Plane{2, h, 2L * p.Hqk * kD + (long)h * kD, (long)p.Hv * kD};
+}
+__device__ __forceinline__ const uint16_t *plane_src(const BwdArgs &p, const Plane &P)
+{
+    return (P.kind == 0 ? p.q : P.kind == 1 ? p.k : p.v) + (long)P.head * kD;
+}
+
+// Conv output y of token t (in-sequence index) of sequence s, channel c of
+// the plane: taps in order, history rows for t - 3 + j < 0.
+__device__ __forceinline__ float conv_y(const BwdArgs &p, const Plane &P, const uint16_t *x, const float (&w)[4],
+                                        int s, int t, int c, long C_tot)
+{
+    float y = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int tau = t - 3 + j;
+        float xv = 0.f;
+        if (tau >= 0)
+            xv = bf16_to_f32(x[((long)s * p.T + tau) * P.ld + c]);
+        else if (p.conv_state_in)
+            xv = bf16_to_f32(p.conv_state_in[((long)s * 3 + 3 + tau) * C_tot + P.ch0 + c]);
+        y = fmaf(w[j], xv, y);
+    }
+    return y;
+}
+
+// ---------------------------------------------------------------------------
+// 1. q^, k^, v^, gamma, beta
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs p, BwdWs ws)
+{
+    __shared__ float zs[64 * kLK];
+    __shared__ float nrm[64];
+    const int cidx = blockIdx.x, s = cidx / p.nc, j = cidx % p.nc;
+    const int n = min(kChunk, p.T - j * kChunk);
+    const long t0 = (long)s * p.T + (long)j * kChunk;
+    const long C_tot = 2L * p.Hqk * kD + (long)p.Hv * kD;
+    const Plane P = plane_of(p, blockIdx.y);
+    const uint16_t *x = plane_src(p, P);
+    const int t = threadIdx.x, c = t & 127, rh = t >> 7;
+    float w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = bf16_to_f32(p.conv_w[(P.ch0 + c) * 4 + i]);
+    for (int r = rh; r < n; r += 2) {
+        const float y = conv_y(p, P, x, w, s, j * kChunk + r, c, C_tot);
+        const float z = y * sigm(y);
+        if (P.kind == 2)
+            ws.vh[((t0 + r) * p.Hv + P.head) * kD + c] = z;
+        else
+            zs[r * kLK + c] = z;
+    }
+    if (P.kind == 2) {
+        // gates of this V head, lane = token: g = -c softplus(a), gamma = in-chunk prefix sum
+        if (t < 64) {
+            float g = 0.f, be = 0.f;
+            if (t < n) {
+                const long ti = (t0 + t) * p.Hv + P.head;
+                const float av = p.a[ti];
+                g = -p.gate_scale * (fmaxf(av, 0.f) + log1pf(expf(-fabsf(av))));
+                be = sigm(p.b[ti]);
+            }
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float u = __shfl_up(g, off, 64);
+                if (t >= off) g += u;
+            }
+            if (t < n) {
+                ws.gam[(t0 + t) * p.Hv + P.head] = g;
+                ws.beta[(t0 + t) * p.Hv + P.head] = be;
+            }
+        }
+        return;
+    }
+    __syncthreads();
+    {
+        const int r = t >> 2, part = t & 3;
+        float ss = 0.f;
+        if (r < n)
+            for (int i = 0; i < 32; ++i) {
+                const float z = zs[r * kLK + part * 32 + i];
+                ss = fmaf(z, z, ss);
+            }
+        ss += __shfl_xor(ss, 1, 64);
+        ss += __shfl_xor(ss, 2, 64);
+        if (part == 0) nrm[r] = sqrtf(ss + 1e-6f);
+    }
+    __syncthreads();
+    float *dst = P.kind == 0 ? ws.qh : ws.kh;
+    for (int r = rh; r < n; r += 2) dst[((t0 + r) * p.Hqk + P.head) * kD + c] = zs[r * kLK + c] / nrm[r];
+}
+
+// ---------------------------------------------------------------------------
+// 2. P and X = (I + A)^-1 per (chunk, V head)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBT) void bwd_local_kernel(BwdArgs p, BwdWs ws)
+{
+    __shared__ float Ks[64 * kLK], Qs[64 * kLK], As[64 * kLN], Xs[64 * kLN];
+    __shared__ float gam[64], bet[64];
+    const int Hv = p.Hv, G = Hv / p.Hqk;
+    const int cidx = blockIdx.x / Hv, h = blockIdx.x % Hv, g = h / G;
+    const int s = cidx / p.nc, j = cidx % p.nc;
+    const int n = min(kChunk, p.T - j * kChunk);
+    const long t0 = (long)s * p.T + (long)j * kChunk;
+    const int t = threadIdx.x;
+    for (int e = 0; e < 32; ++e) {
+        const int idx = t + kBT * e, r = idx >> 7, d = idx & 127;
+        const long src = ((t0 + r) * p.Hqk + g) * kD + d;
+        Ks[r * kLK + d] = r < n ? ws.kh[src] : 0.f;
+        Qs[r * kLK + d] = r < n ? ws.qh[src] : 0.f;
+    }
+    if (t < 64) {
+        gam[t] = t < n ? ws.gam[(t0 + t) * Hv + h] : 0.f;
+        bet[t] = t < n ? ws.beta[(t0 + t) * Hv + h] : 0.f;
+    }
+    __syncthreads();
+    const long mo = ((long)cidx * Hv + h) * 64 * 64;
+    {
+        const int i = t >> 2;
+        for (int m = 0; m < 16; ++m) {
+            const int jj = (t & 3) + 4 * m;
+            float kk = 0.f, qk = 0.f;
+            for (int d = 0; d < kD; ++d) {
+                kk = fmaf(Ks[i * kLK + d], Ks[jj * kLK + d], kk);
+                qk = fmaf(Qs[i * kLK + d], Ks[jj * kLK + d], qk);
+            }
+            const float D = expf(gam[i] - gam[jj]);
+            As[i * kLN + jj] = (jj < i && i < n) ? bet[i] * kk * D : 0.f;
+            ws.P[mo + i * 64 + jj] = (jj <= i && i < n) ? qk * D : 0.f;
+        }
+    }
+    __syncthreads();
+    // unit lower-triangular inverse, thread c takes column c: x_i = [i == c] - sum_{m<i} A_im x_m
+    if (t < 64) {
+        const int c = t;
+        for (int i = 0; i < 64; ++i) {
+            float xv = i == c ? 1.f : 0.f;
+            for (int m = c; m < i; ++m) xv = fmaf(-As[i * kLN + m], Xs[m * kLN + c], xv);
+            Xs[i * kLN + c] = i >= c ? xv : 0.f;
+        }
+    }
+    __syncthreads();
+    for (int e = 0; e < 16; ++e) {
+        const int idx = t + kBT * e, r = idx >> 6, c = idx & 63;
+        ws.X[mo + idx] = Xs[r * kLN + c];
+    }
+}
+
+// Per-chunk operands of the sequential passes in LDS
+struct SeqTile {
+    float K[64 * kLK];
+    float X[64 * kLN];
+    float gam[64], bet[64], eg[64], en[64];
+};
+
+__device__ __forceinline__ void load_seq_tile(const BwdArgs &p, const BwdWs &ws, SeqTile &L, long t0, int n,
+                                              int cidx, int h, int g, float *Qopt, float *Popt)
+{
+    const int t = threadIdx.x, Hv = p.Hv;
+    for (int e = 0; e < 32; ++e) {
+        const int idx = t + kBT * e, r = idx >> 7, d = idx & 127;
+        const long src = ((t0 + r) * p.Hqk + g) * kD + d;
+        L.K[r * kLK + d] = r < n ? ws.kh[src] : 0.f;
+        if (Qopt) Qopt[r * kLK + d] = r < n ? ws.qh[src] : 0.f;
+    }
+    const long mo = ((long)cidx * Hv + h) * 64 * 64;
+    for (int e = 0; e < 16; ++e) {
+        const int idx = t + kBT * e, r = idx >> 6, c = idx & 63;
+        L.X[r * kLN + c] = ws.X[mo + idx];
+        if (Popt) Popt[r * kLN + c] = ws.P[mo + idx];
+    }
+    if (t < 64) {
+        const float gl = ws.gam[(t0 + n - 1) * Hv + h];
+        const float gr = t < n ? ws.gam[(t0 + t) * Hv + h] : 0.f;
+        L.gam[t] = gr;
+        L.bet[t] = t < n ? ws.beta[(t0 + t) * Hv + h] : 0.f;
+        L.eg[t] = t < n ? expf(gr) : 0.f;
+        L.en[t] = t < n ? expf(gl - gr) : 0.f;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. forward again, keeping the state entering every chunk, Vt and Vn
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBT) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
+{
+    __shared__ SeqTile L;
+    __shared__ float Ss[kD * kLC], Vs[64 * kLC], Vts[64 * kLC], Vns[64 * kLC];
+    const int Hv = p.Hv, G = Hv / p.Hqk;
+    const int cb = blockIdx.x % kNCB, sh = blockIdx.x / kNCB, h = sh % Hv, s = sh / Hv, g = h / G;
+    const int col0 = cb * kCB;
+    const int t = threadIdx.x, i = t >> 1, c0 = (t & 1) * 8;
+    float S[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        S[e] = p.state_in ? p.state_in[(((long)s * Hv + h) * kD + i) * kD + col0 + c0 + e] : 0.f;
+    for (int j = 0; j < p.nc; ++j) {
+        const int cidx = s * p.nc + j, n = min(kChunk, p.T - j * kChunk);
+        const long t0 = (long)s * p.T + (long)j * kChunk;
+        float *sc = ws.Sc + ((((long)cidx * Hv + h) * kD + i) * kD + col0 + c0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            sc[e] = S[e];
+            Ss[i * kLC + c0 + e] = S[e];
+        }
+        load_seq_tile(p, ws, L, t0, n, cidx, h, g, nullptr, nullptr);
+        for (int e = 0; e < 4; ++e) {
+            const int idx = t + kBT * e, r = idx >> 4, c = idx & 15;
+            Vs[r * kLC + c] = r < n ? ws.vh[((t0 + r) * Hv + h) * kD + col0 + c] : 0.f;
+        }
+        __syncthreads();
+        const int r = t >> 2, c4 = (t & 3) * 4;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int d = 0; d < kD; ++d) {
+            const float kv = L.K[r * kLK + d];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = fmaf(kv, Ss[d * kLC + c4 + e], acc[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float vt = r < n ? Vs[r * kLC + c4 + e] - L.eg[r] * acc[e] : 0.f;
+            Vts[r * kLC + c4 + e] = vt;
+            if (r < n) ws.vt[((t0 + r) * Hv + h) * kD + col0 + c4 + e] = vt;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = 0.f;
+        for (int m = 0; m <= r; ++m) {
+            const float bx = L.X[r * kLN + m] * L.bet[m];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = fmaf(bx, Vts[m * kLC + c4 + e], acc[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float vn = r < n ? acc[e] : 0.f;
+            Vns[r * kLC + c4 + e] = vn;
+            if (r < n) ws.vn[((t0 + r) * Hv + h) * kD + col0 + c4 + e] = vn;
+        }
+        __syncthreads();
+        const float egn = L.eg[n - 1];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) S[e] *= egn;
+        for (int rr = 0; rr < n; ++rr) {
+            const float kr = L.K[rr * kLK + i] * L.en[rr];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) S[e] = fmaf(kr, Vns[rr * kLC + c0 + e], S[e]);
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 4. the state gradient, chunk by chunk from the last
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBT) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
+{
+    __shared__ SeqTile L;
+    __shared__ float Qs[64 * kLK], Ps[64 * kLN];
+    __shared__ float dSs[kD * kLC], dOs[64 * kLC], dVns[64 * kLC], dVts[64 * kLC];
+    const int Hv = p.Hv, G = Hv / p.Hqk;
+    const int cb = blockIdx.x % kNCB, sh = blockIdx.x / kNCB, h = sh % Hv, s = sh / Hv, g = h / G;
+    const int col0 = cb * kCB;
+    const int t = threadIdx.x, i = t >> 1, c0 = (t & 1) * 8;
+    const long so = (((long)s * Hv + h) * kD + i) * kD + col0 + c0;
+    float dS[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dS[e] = p.grad_state_out ? p.grad_state_out[so + e] : 0.f;
+    for (int j = p.nc - 1; j >= 0; --j) {
+        const int cidx = s * p.nc + j, n = min(kChunk, p.T - j * kChunk);
+        const long t0 = (long)s * p.T + (long)j * kChunk;
+        float *dsc = ws.dSc + ((((long)cidx * Hv + h) * kD + i) * kD + col0 + c0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            dsc[e] = dS[e];
+            dSs[i * kLC + c0 + e] = dS[e];
+        }
+        load_seq_tile(p, ws, L, t0, n, cidx, h, g, Qs, Ps);
+        for (int e = 0; e < 4; ++e) {
+            const int idx = t + kBT * e, r = idx >> 4, c = idx & 15;
+            dOs[r * kLC + c] = r < n ? p.q_scale * bf16_to_f32(p.grad_o[((t0 + r) * Hv + h) * kD + col0 + c]) : 0.f;
+        }
+        __syncthreads();
+        const int r = t >> 2, c4 = (t & 3) * 4;
+        // dVn = Ks dS' + P^T dO'
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int d = 0; d < kD; ++d) {
+            const float kv = L.K[r * kLK + d];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = fmaf(kv, dSs[d * kLC + c4 + e], acc[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] *= L.en[r];
+        for (int m = r; m < n; ++m) {
+            const float pv = Ps[m * kLN + r];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = fmaf(pv, dOs[m * kLC + c4 + e], acc[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float v = r < n ? acc[e] : 0.f;
+            dVns[r * kLC + c4 + e] = v;
+            if (r < n) ws.dvn[((t0 + r) * Hv + h) * kD + col0 + c4 + e] = v;
+        }
+        __syncthreads();
+        // dVt = T'^T dVn = diag(beta) X^T dVn
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = 0.f;
+        for (int m = r; m < n; ++m) {
+            const float xv = L.X[m * kLN + r];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = fmaf(xv, dVns[m * kLC + c4 + e], acc[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float v = r < n ? L.bet[r] * acc[e] : 0.f;
+            dVts[r * kLC + c4 + e] = v;
+            if (r < n) ws.dvh[((t0 + r) * Hv + h) * kD + col0 + c4 + e] = v;
+        }
+        __syncthreads();
+        // dS <- Gam_n dS' + (Gam Q)^T dO' - (Gam K)^T dVt
+        const float egn = L.eg[n - 1];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dS[e] *= egn;
+        for (int rr = 0; rr < n; ++rr) {
+            const float qv = Qs[rr * kLK + i] * L.eg[rr], kv = L.K[rr * kLK + i] * L.eg[rr];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                dS[e] = fmaf(qv, dOs[rr * kLC + c0 + e], fmaf(-kv, dVts[rr * kLC + c0 + e], dS[e]));
+        }
+        __syncthreads();
+    }
+    if (p.grad_state_in) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p.grad_state_in[so + e] = dS[e];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 5. per-chunk gradients
+// ---------------------------------------------------------------------------
+// acc[ri][m] += sum_k fa(r0 + ri, k) fb(k, cc + 16 m) for k < K (a multiple
+// of 32), r0 = 4 (t / 16), cc = t % 16, m < NC: a 64 x (16 NC) product,
+// staged through LDS 32 deep.
+template <int NC, class FA, class FB>
+__device__ __forceinline__ void gemm64(float (&acc)[4][8], int K, FA fa, FB fb, float *sA, float *sB)
+{
+    const int t = threadIdx.x, r0 = 4 * (t >> 4), cc = t & 15;
+    constexpr int NCOL = 16 * NC, LB = NCOL + 1;
+    for (int k0 = 0; k0 < K; k0 += 32) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int idx = t + kBT * e, r = idx >> 5, kk = idx & 31;
+            sA[r * 33 + kk] = fa(r, k0 + kk);
+        }
+#pragma unroll
+        for (int e = 0; e < 2 * NC; ++e) {
+            const int idx = t + kBT * e, kk = idx / NCOL, c = idx % NCOL;
+            sB[kk * LB + c] = fb(k0 + kk, c);
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int kk = 0; kk < 32; ++kk) {
+            float av[4], bv[NC];
+#pragma unroll
+            for (int ri = 0; ri < 4; ++ri) av[ri] = sA[(r0 + ri) * 33 + kk];
+#pragma unroll
+            for (int m = 0; m < NC; ++m) bv[m] = sB[kk * LB + cc + 16 * m];
+#pragma unroll
+            for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+                for (int m = 0; m < NC; ++m) acc[ri][m] = fmaf(av[ri], bv[m], acc[ri][m]);
+        }
+        __syncthreads();
+    }
+}
+
+__device__ __forceinline__ void zero(float (&acc)[4][8])
+{
+#pragma unroll
+    for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) acc[ri][m] = 0.f;
+}
+
+// sum over the 16 lanes of a row group
+__device__ __forceinline__ float sum16(float v)
+{
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    v += __shfl_xor(v, 8, 64);
+    return v;
+}
+
+__global__ __launch_bounds__(kBT) void bwd_grad_kernel(BwdArgs p, BwdWs ws)
+{
+    __shared__ float sA[64 * 33], sB[32 * 129];
+    __shared__ float Em[64 * kLN], Wm[64 * kLN], Ym[64 * kLN];
+    __shared__ float gam[64], bet[64], eg[64], en[64], dgam[64], dbet[64], rowv[64], red[4];
+    const int Hv = p.Hv, Hqk = p.Hqk, G = Hv / Hqk;
+    const int cidx = blockIdx.x / Hv, h = blockIdx.x % Hv, g = h / G;
+    const int s = cidx / p.nc, j = cidx % p.nc;
+    const int n = min(kChunk, p.T - j * kChunk);
+    const long t0 = (long)s * p.T + (long)j * kChunk;
+    const int t = threadIdx.x, r0 = 4 * (t >> 4), cc = t & 15;
+    const long mo = ((long)cidx * Hv + h) * 64 * 64;
+    const float *Sc = ws.Sc + ((long)cidx * Hv + h) * kD * kD;
+    const float *dSc = ws.dSc + ((long)cidx * Hv + h) * kD * kD;
+    if (t < 64) {
+        const float gl = ws.gam[(t0 + n - 1) * Hv + h];
+        const float gr = t < n ? ws.gam[(t0 + t) * Hv + h] : 0.f;
+        gam[t] = gr;
+        bet[t] = t < n ? ws.beta[(t0 + t) * Hv + h] : 0.f;
+        eg[t] = t < n ? expf(gr) : 0.f;
+        en[t] = t < n ? expf(gl - gr) : 0.f;
+        dgam[t] = 0.f;
+        dbet[t] = 0.f;
+    }
+    __syncthreads();
+    auto KH = [&](int r, int d) { return r < n ? ws.kh[((t0 + r) * Hqk + g) * kD + d] : 0.f; };
+    auto QH = [&](int r, int d) { return r < n ? ws.qh[((t0 + r) * Hqk + g) * kD + d] : 0.f; };
+    auto VROW = [&](const float *base, int r, int c) { return r < n ? base[((t0 + r) * Hv + h) * kD + c] : 0.f; };
+    auto DO = [&](int r, int c) {
+        return r < n ? p.q_scale * bf16_to_f32(p.grad_o[((t0 + r) * Hv + h) * kD + c]) : 0.f;
+    };
+    // rows of this thread's group: apply coef[r] * rowsum to dgam (one writer per row)
+    auto row_apply = [&](float (&part)[4], float *dst, const float *coef, float sign) {
+#pragma unroll
+        for (int ri = 0; ri < 4; ++ri) {
+            const float v = sum16(part[ri]);
+            const int r = r0 + ri;
+            if (cc == 0 && r < n) dst[r] += sign * (coef ? coef[r] : 1.f) * v;
+        }
+    };
+    float dQ[4][8], dK[4][8], acc[4][8];
+    zero(dQ);
+    zero(dK);
+
+    // (a) Ks = diag(en) K enters S' = ... + Ks^T Vn: dKs = Vn dS'^T
+    zero(acc);
+    gemm64<8>(acc, kD, [&](int r, int c) { return VROW(ws.vn, r, c); },
+              [&](int c, int i) { return dSc[i * kD + c]; }, sA, sB);
+    {
+        float part[4];
+#pragma unroll
+        for (int ri = 0; ri < 4; ++ri) {
+            const int r = r0 + ri;
+            part[ri] = 0.f;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                dK[ri][m] += en[r] * acc[ri][m];
+                part[ri] = fmaf(acc[ri][m], KH(r, cc + 16 * m), part[ri]);
+            }
+        }
+#pragma unroll
+        for (int ri = 0; ri < 4; ++ri) {
+            const float v = sum16(part[ri]);
+            if (cc == 0) rowv[r0 + ri] = r0 + ri < n ? en[r0 + ri] * v : 0.f;
+        }
+    }
+    // <dS', S> for the Gam_n S term
+    {
+        float fr = 0.f;
+        for (int e = 0; e < 64; ++e) {
+            const int idx = t + kBT * e;
+            fr = fmaf(dSc[idx], Sc[idx], fr);
+        }
+        for (int off = 32; off >= 1; off >>= 1) fr += __shfl_xor(fr, off, 64);
+        if ((t & 63) == 0) red[t >> 6] = fr;
+    }
+    __syncthreads();
+    if (t == 0) {
+        float tot = 0.f;
+        for (int r = 0; r < n; ++r) tot += rowv[r];
+        dgam[n - 1] += tot + eg[n - 1] * (red[0] + red[1] + red[2] + red[3]);
+    }
+    __syncthreads();
+    if (t < n) dgam[t] -= rowv[t];
+    __syncthreads();
+
+    // (c) O = q_scale (diag(Gam) Q S + ...): E1 = dO' S^T
+    zero(acc);
+    gemm64<8>(acc, kD, DO, [&](int c, int i) { return Sc[i * kD + c]; }, sA, sB);
+    {
+        float part[4];
+#pragma unroll
+        for (int ri = 0; ri < 4; ++ri) {
+            const int r = r0 + ri;
+            part[ri] = 0.f;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                dQ[ri][m] += eg[r] * acc[ri][m];
+                part[ri] = fmaf(acc[ri][m], QH(r, cc + 16 * m), part[ri]);
+            }
+        }
+        row_apply(part, dgam, eg, 1.f);
+    }
+    __syncthreads();
+    // (e) Vt = V - diag(Gam) K S: E2 = dVt S^T
+    zero(acc);
+    gemm64<8>(acc, kD, [&](int r, int c) { return VROW(ws.dvh, r, c); },
+              [&](int c, int i) { return Sc[i * kD + c]; }, sA, sB);
+    {
+        float part[4];
+#pragma unroll
+        for (int ri = 0; ri < 4; ++ri) {
+            const int r = r0 + ri;
+            part[ri] = 0.f;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                dK[ri][m] -= eg[r] * acc[ri][m];
+                part[ri] = fmaf(acc[ri][m], KH(r, cc + 16 * m), part[ri]);
+            }
+        }
+        row_apply(part, dgam, eg, -1.f);
+    }
+    __syncthreads();
+    // (d) P = Q K^T * D * M: dP = dO' Vn^T (lower); Em = dP * P; Wm = dP * D
+    zero(acc);
+    gemm64<4>(acc, kD, DO, [&](int c, int jj) { return VROW(ws.vn, jj, c); }, sA, sB);
+#pragma unroll
+    for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = r0 + ri, jj = cc + 16 * m;
+            const bool in = jj <= r && r < n;
+            Em[r * kLN + jj] = in ? acc[ri][m] * ws.P[mo + r * 64 + jj] : 0.f;
+            Wm[r * kLN + jj] = in ? acc[ri][m] * expf(gam[r] - gam[jj]) : 0.f;
+        }
+    __syncthreads();
+    gemm64<8>(dQ, 64, [&](int r, int jj) { return Wm[r * kLN + jj]; }, KH, sA, sB);
+    gemm64<8>(dK, 64, [&](int r, int jj) { return Wm[jj * kLN + r]; }, QH, sA, sB);
+    // (f) Vn = T' Vt: dT' = dVn Vt^T (lower incl. diagonal); dbeta_j += sum_i dT'_ij X_ij; dX = dT' diag(beta)
+    zero(acc);
+    gemm64<4>(acc, kD, [&](int r, int c) { return VROW(ws.dvn, r, c); },
+              [&](int c, int jj) { return VROW(ws.vt, jj, c); }, sA, sB);
+#pragma unroll
+    for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = r0 + ri, jj = cc + 16 * m;
+            const bool in = jj <= r && r < n;
+            Ym[r * kLN + jj] = in ? acc[ri][m] * ws.X[mo + r * 64 + jj] : 0.f;
+            Wm[r * kLN + jj] = in ? acc[ri][m] * bet[jj] : 0.f;
+        }
+    __syncthreads();
+    if (t < n) {
+        float cs = 0.f;
+        for (int r = t; r < n; ++r) cs += Ym[r * kLN + t];
+        dbet[t] += cs;
+    }
+    __syncthreads();
+    // (g) X = (I + A)^-1: dA = strict_lower(-X^T dX X^T)
+    zero(acc);
+    gemm64<4>(acc, 64, [&](int r, int m) { return ws.X[mo + m * 64 + r]; },
+              [&](int m, int jj) { return Wm[m * kLN + jj]; }, sA, sB);
+#pragma unroll
+    for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) Ym[(r0 + ri) * kLN + cc + 16 * m] = acc[ri][m];
+    __syncthreads();
+    zero(acc);
+    gemm64<4>(acc, 64, [&](int r, int m) { return Ym[r * kLN + m]; },
+              [&](int m, int jj) { return ws.X[mo + jj * 64 + m]; }, sA, sB);
+#pragma unroll
+    for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = r0 + ri, jj = cc + 16 * m;
+            Wm[r * kLN + jj] = (jj < r && r < n) ? -acc[ri][m] : 0.f;
+        }
+    __syncthreads();
+    // (h) A = diag(beta) K K^T * D (strict lower): dbeta_i, Em += dA * A, dKK -> Ym
+    zero(acc);
+    gemm64<4>(acc, kD, KH, [&](int d, int jj) { return KH(jj, d); }, sA, sB);
+    {
+        float part[4];
+#pragma unroll
+        for (int ri = 0; ri < 4; ++ri) {
+            part[ri] = 0.f;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int r = r0 + ri, jj = cc + 16 * m;
+                const bool in = jj < r && r < n;
+                const float D = expf(gam[r] - gam[jj]);
+                const float dA = Wm[r * kLN + jj];
+                if (in) {
+                    Em[r * kLN + jj] += dA * bet[r] * acc[ri][m] * D;
+                    part[ri] = fmaf(dA, acc[ri][m] * D, part[ri]);
+                }
+                Ym[r * kLN + jj] = in ? dA * bet[r] * D : 0.f;
+            }
+        }
+        row_apply(part, dbet, nullptr, 1.f);
+    }
+    __syncthreads();
+    gemm64<8>(dK, 64, [&](int r, int jj) { return Ym[r * kLN + jj] + Ym[jj * kLN + r]; }, KH, sA, sB);
+    // gamma: rows of Em count +, columns -; then dg = reverse prefix sum
+    if (t < n) {
+        float v = 0.f;
+        for (int jj = 0; jj < 64; ++jj) v += Em[t * kLN + jj] - Em[jj * kLN + t];
+        dgam[t] += v;
+    }
+    __syncthreads();
+    if (t < n) {
+        float dg = 0.f;
+        for (int r = n - 1; r >= t; --r) dg += dgam[r];
+        const long ti = (t0 + t) * Hv + h;
+        p.grad_a[ti] = dg * (-p.gate_scale * sigm(p.a[ti]));
+        p.grad_b[ti] = dbet[t] * bet[t] * (1.f - bet[t]);
+    }
+#pragma unroll
+    for (int ri = 0; ri < 4; ++ri) {
+        const int r = r0 + ri;
+        if (r >= n) continue;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const long o = ((t0 + r) * Hv + h) * kD + cc + 16 * m;
+            ws.dqp[o] = dQ[ri][m];
+            ws.dkp[o] = dK[ri][m];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 6. back through the L2 norm and SiLU to the conv outputs
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBT) void bwd_dy_kernel(BwdArgs p, BwdWs ws)
+{
+    __shared__ float zs[64 * kLK], ds[64 * kLK];
+    __shared__ float nrm[64], zd[64];
+    const int cidx = blockIdx.x, s = cidx / p.nc, j = cidx % p.nc;
+    const int n = min(kChunk, p.T - j * kChunk);
+    const long t0 = (long)s * p.T + (long)j * kChunk;
+    const long C_tot = 2L * p.Hqk * kD + (long)p.Hv * kD;
+    const int G = p.Hv / p.Hqk;
+    const Plane P = plane_of(p, blockIdx.y);
+    const uint16_t *x = plane_src(p, P);
+    const int t = threadIdx.x, c = t & 127, rh = t >> 7;
+    float w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = bf16_to_f32(p.conv_w[(P.ch0 + c) * 4 + i]);
+    if (P.kind == 2) {
+        for (int r = rh; r < n; r += 2) {
+            const float y = conv_y(p, P, x, w, s, j * kChunk + r, c, C_tot);
+            ws.dy[(t0 + r) * C_tot + P.ch0 + c] = ws.dvh[((t0 + r) * p.Hv + P.head) * kD + c] * silu_grad(y);
+        }
+        return;
+    }
+    const float *part = P.kind == 0 ? ws.dqp : ws.dkp;
+    for (int r = rh; r < n; r += 2) {
+        const float y = conv_y(p, P, x, w, s, j * kChunk + r, c, C_tot);
+        zs[r * kLK + c] = y * sigm(y);
+        float d = 0.f;
+        for (int jh = 0; jh < G; ++jh) d += part[((t0 + r) * p.Hv + P.head * G + jh) * kD + c];
+        ds[r * kLK + c] = d;
+    }
+    __syncthreads();
+    {
+        const int r = t >> 2, pt = t & 3;
+        float ss = 0.f, sd = 0.f;
+        if (r < n)
+            for (int i = 0; i < 32; ++i) {
+                const float z = zs[r * kLK + pt * 32 + i];
+                ss = fmaf(z, z, ss);
+                sd = fmaf(z, ds[r * kLK + pt * 32 + i], sd);
+            }
+        ss += __shfl_xor(ss, 1, 64);
+        ss += __shfl_xor(ss, 2, 64);
+        sd += __shfl_xor(sd, 1, 64);
+        sd += __shfl_xor(sd, 2, 64);
+        if (pt == 0) {
+            nrm[r] = sqrtf(ss + 1e-6f);
+            zd[r] = sd;
+        }
+    }
+    __syncthreads();
+    for (int r = rh; r < n; r += 2) {
+        const float y = conv_y(p, P, x, w, s, j * kChunk + r, c, C_tot);
+        const float rn = nrm[r];
+        const float dz = ds[r * kLK + c] / rn - zs[r * kLK + c] * zd[r] / (rn * rn * rn);
+        ws.dy[(t0 + r) * C_tot + P.ch0 + c] = dz * silu_grad(y);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 7. back through the conv
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBT) void bwd_conv_kernel(BwdArgs p, BwdWs ws)
+{
+    __shared__ float wpart[2][kD][4];
+    const int cidx = blockIdx.x, s = cidx / p.nc, j = cidx % p.nc;
+    const int n = min(kChunk, p.T - j * kChunk);
+    const long t0 = (long)s * p.T + (long)j * kChunk;
+    const long C_tot = 2L * p.Hqk * kD + (long)p.Hv * kD;
+    const Plane P = plane_of(p, blockIdx.y);
+    const uint16_t *x = plane_src(p, P);
+    float *gx = (P.kind == 0 ? p.grad_q : P.kind == 1 ? p.grad_k : p.grad_v) + (long)P.head * kD;
+    const int t = threadIdx.x, c = t & 127, rh = t >> 7;
+    const long ch = P.ch0 + c;
+    float w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = bf16_to_f32(p.conv_w[ch * 4 + i]);
+    const float *dy = ws.dy + (long)s * p.T * C_tot + ch;  // dy of token tau of this sequence: dy[tau * C_tot]
+    float gw[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int r = rh; r < n; r += 2) {
+        const int tau = j * kChunk + r;
+        // x[tau] feeds y[tau + 3 - jj] through tap jj
+        float gxv = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int ty = tau + 3 - jj;
+            if (ty < p.T) gxv = fmaf(w[jj], dy[(long)ty * C_tot], gxv);
+        }
+        gx[(t0 + r) * P.ld + c] = gxv;
+        // y[tau] reads x[tau - 3 + jj] through tap jj
+        const float d = dy[(long)tau * C_tot];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int tx = tau - 3 + jj;
+            float xv = 0.f;
+            if (tx >= 0)
+                xv = bf16_to_f32(x[((long)s * p.T + tx) * P.ld + c]);
+            else if (p.conv_state_in)
+                xv = bf16_to_f32(p.conv_state_in[((long)s * 3 + 3 + tx) * C_tot + ch]);
+            gw[jj] = fmaf(d, xv, gw[jj]);
+        }
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) wpart[rh][c][jj] = gw[jj];
+    __syncthreads();
+    if (rh == 0) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            ws.dwp[((long)cidx * C_tot + ch) * 4 + jj] = wpart[0][c][jj] + wpart[1][c][jj];
+        // the carried rows x[-3..-1] feed the sequence's first tokens
+        if (j == 0 && p.grad_conv_state_in) {
+            for (int rr = 0; rr < 3; ++rr) {
+                float gv = 0.f;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int ty = rr - jj;  // token whose tap jj reads row rr (= x[rr - 3])
+                    if (ty >= 0 && ty < p.T) gv = fmaf(w[jj], dy[(long)ty * C_tot], gv);
+                }
+                p.grad_conv_state_in[((long)s * 3 + rr) * C_tot + ch] = gv;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 8. conv weight gradient: per-chunk parts summed in chunk order
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBT) void bwd_dw_kernel(BwdArgs p, BwdWs ws, long n_elems, int n_chunks)
+{
+    const long e = (long)blockIdx.x * kBT + threadIdx.x;
+    if (e >= n_elems) return;
+    float acc = 0.f;
+    for (int c = 0; c < n_chunks; ++c) acc += ws.dwp[(long)c * n_elems + e];
+    p.grad_conv_w[e] = acc;
+}
+
+__global__ __launch_bounds__(kBT) void bwd_fill_kernel(float *dst, long n)
+{
+    const long e = (long)blockIdx.x * kBT + threadIdx.x;
+    if (e < n) dst[e] = 0.f;
+}
+
+// Workspace carve-up: sizes in floats, each region 64-byte aligned
+struct BwdLayout {
+    long off[18];
+    long total;
+};
+BwdLayout bwd_layout(int B, int T, int Hqk, int Hv)
+{
+    const long tok = (long)B * T, nc = (T + kChunk - 1) / kChunk, chunks = (long)B * nc;
+    const long C_tot = 2L * Hqk * kD + (long)Hv * kD;
+    const long sizes[18] = {tok * Hqk * kD, tok * Hqk * kD, tok * Hv * kD, tok * Hv, tok * Hv,
+                            chunks * Hv * 4096, chunks * Hv * 4096, chunks * Hv * kD * kD, chunks * Hv * kD * kD,
+                            tok * Hv * kD, tok * Hv * kD, tok * Hv * kD, tok * Hv * kD, tok * Hv * kD,
+                            tok * Hv * kD, tok * C_tot, chunks * C_tot * 4, 0};
+    BwdLayout L{};
+    long o = 0;
+    for (int i = 0; i < 18; ++i) {
+        L.off[i] = o;
+        o += (sizes[i] + 15) / 16 * 16;
+    }
+    L.total = o;
+    return L;
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(int B, int T, int Hqk, int Hv)
+{
+    if (B == 0 || T == 0) return 0;
+    return (size_t)bwd_layout(B, T, Hqk, Hv).total * sizeof(float);
+}
+
+hipError_t launch_backward(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
+                           const float *b, const uint16_t *conv_w, const uint16_t *conv_state_in,
+                           const float *state_in, const uint16_t *grad_o, const float *grad_state_out,
+                           float *grad_q, float *grad_k, float *grad_v, float *grad_a, float *grad_b,
+                           float *grad_conv_w, float *grad_conv_state_in, float *grad_state_in, int B, int T,
+                           int Hqk, int Hv, float gate_scale, float q_scale, void *workspace, hipStream_t stream)
+{
+    BwdArgs p{};
+    p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.conv_w = conv_w; p.conv_state_in = conv_state_in;
+    p.state_in = state_in; p.grad_o = grad_o; p.grad_state_out = grad_state_out;
+    p.grad_q = grad_q; p.grad_k = grad_k; p.grad_v = grad_v; p.grad_a = grad_a; p.grad_b = grad_b;
+    p.grad_conv_w = grad_conv_w; p.grad_conv_state_in = grad_conv_state_in; p.grad_state_in = grad_state_in;
+    p.B = B; p.T = T; p.Hqk = Hqk; p.Hv = Hv; p.nc = (T + kChunk - 1) / kChunk;
+    p.gate_scale = gate_scale; p.q_scale = q_scale;
+    const long C_tot = 2L * Hqk * kD + (long)Hv * kD;
+    BwdWs ws{};
+    if (T > 0) {
+        const BwdLayout L = bwd_layout(B, T, Hqk, Hv);
+        float *base = static_cast<float *>(workspace);
+        float **slots[17] = {&ws.qh, &ws.kh, &ws.vh, &ws.gam, &ws.beta, &ws.X, &ws.P, &ws.Sc, &ws.dSc,
+                             &ws.vt, &ws.vn, &ws.dvn, &ws.dvh, &ws.dqp, &ws.dkp, &ws.dy, &ws.dwp};
+        for (int i = 0; i < 17; ++i) *slots[i] = base + L.off[i];
+    }
+    const int chunks = B * p.nc, planes = 2 * Hqk + Hv;
+    if (chunks > 0) {
+        hipLaunchKernelGGL(bwd_prep_kernel, dim3(chunks, planes), dim3(kBT), 0, stream, p, ws);
+        hipLaunchKernelGGL(bwd_local_kernel, dim3(chunks * Hv), dim3(kBT), 0, stream, p, ws);
+        hipLaunchKernelGGL(bwd_fwd_kernel, dim3(B * Hv * kNCB), dim3(kBT), 0, stream, p, ws);
+    }
+    // also with T = 0: the state gradient passes straight through
+    hipLaunchKernelGGL(bwd_chain_kernel, dim3(B * Hv * kNCB), dim3(kBT), 0, stream, p, ws);
+    if (chunks > 0) {
+        hipLaunchKernelGGL(bwd_grad_kernel, dim3(chunks * Hv), dim3(kBT), 0, stream, p, ws);
+        hipLaunchKernelGGL(bwd_dy_kernel, dim3(chunks, planes), dim3(kBT), 0, stream, p, ws);
+        hipLaunchKernelGGL(bwd_conv_kernel, dim3(chunks, planes), dim3(kBT), 0, stream, p, ws);
+        const long nw = C_tot * 4;
+        hipLaunchKernelGGL(bwd_dw_kernel, dim3((nw + kBT - 1) / kBT), dim3(kBT), 0, stream, p, ws, nw, chunks);
+    } else {
+        const long nw = C_tot * 4;
+        hipLaunchKernelGGL(bwd_fill_kernel, dim3((nw + kBT - 1) / kBT), dim3(kBT), 0, stream, grad_conv_w, nw);
+        if (grad_conv_state_in) {
+            const long nh = (long)B * 3 * C_tot;
+            hipLaunchKernelGGL(bwd_fill_kernel, dim3((nh + kBT - 1) / kBT), dim3(kBT), 0, stream,
+                               grad_conv_state_in, nh);
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace gdn

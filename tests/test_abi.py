@@ -141,3 +141,30 @@ def test_decode_multi_validation(L):
     assert call_decode_multi(L, q=0) == gdn.GDN_ERR_INVALID_ARGUMENT
     assert call_decode_multi(L, B=0) == gdn.GDN_OK
 
+
+
+def call_backward(L, B=1, T=64, Hqk=2, Hv=6, dk=128, dv=128, q=FAKE, g_o=FAKE, gw=FAKE, ws=FAKE,
+                  ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = gdn.gdn_prefill_backward_workspace_size(B, T, Hqk, Hv, dk, dv)
+    return L.gdn_prefill_backward(_p(q), _p(), _p(), _p(), _p(), _p(), None, None, _p(g_o), None,
+                                  _p(), _p(), _p(), _p(), _p(), _p(gw), None, None,
+                                  B, T, Hqk, Hv, dk, dv, 0.1, 1.0, _p(ws), ws_bytes, None)
+
+
+def test_backward_validation(L):
+    need = gdn.gdn_prefill_backward_workspace_size(1, 64, 2, 6)
+    assert need > gdn.gdn_prefill_backward_workspace_size(1, 63, 2, 6) > 0
+    assert gdn.gdn_prefill_backward_workspace_size(1, 0, 2, 6) == 0
+    assert gdn.gdn_prefill_backward_workspace_size(1, 64, 2, 6, 64, 128) == 0
+    assert call_backward(L, q=0) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call_backward(L, g_o=0) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call_backward(L, gw=0) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call_backward(L, T=-1) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call_backward(L, dv=64) == gdn.GDN_ERR_UNSUPPORTED
+    assert call_backward(L, Hv=7) == gdn.GDN_ERR_UNSUPPORTED
+    assert call_backward(L, q=FAKE + 2) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call_backward(L, ws=FAKE + 4) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call_backward(L, ws_bytes=need - 1) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL
+    assert call_backward(L, ws=0) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL
+    assert call_backward(L, B=0, ws=0, ws_bytes=0) == gdn.GDN_OK
