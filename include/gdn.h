@@ -218,7 +218,8 @@ size_t gdn_prefill_backward_workspace_size(int B, int T, int Hqk, int Hv, int dk
  *   workspace        device, >= gdn_prefill_backward_workspace_size bytes,
  *                    16-byte aligned; its contents are scratch
  * Every gradient is overwritten (not accumulated).  Outputs must not overlap
- * each other, the inputs or the workspace.  Pointers 4-byte aligned.  With
+ * each other, the inputs or the workspace.  Pointers 4-byte aligned, grad_o
+ * 8-byte aligned.  With
  * T = 0, grad_state_in = grad_state_out (or zeros) and the conv gradients
  * are zero.
  */

@@ -212,7 +212,7 @@ int gdn_prefill_backward(const uint16_t *q, const uint16_t *k, const uint16_t *v
                          grad_state_in};
     for (const void *ptr : al4)
         if (ptr && !aligned(ptr, 4)) return GDN_ERR_INVALID_ARGUMENT;
-    if (workspace && !aligned(workspace, 16)) return GDN_ERR_INVALID_ARGUMENT;
+    if ((workspace && !aligned(workspace, 16)) || (grad_o && !aligned(grad_o, 8))) return GDN_ERR_INVALID_ARGUMENT;
     const size_t need = gdn::backward_workspace_bytes(B, T, Hqk, Hv);
     if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE_TOO_SMALL;
     if (B == 0) return GDN_OK;

@@ -19,9 +19,9 @@
 // Passes (one launch each):
 //   bwd_prep_kernel    conv + SiLU (+ L2 norm) of q, k, v; gates and gamma
 //   bwd_local_kernel   per (chunk, V head): P and X = (I + A)^-1
-//   bwd_fwd_kernel     per (sequence, V head, 16 state columns), in order:
+//   bwd_fwd_kernel     per (sequence, V head, 32 state columns), in order:
 //                      the state entering every chunk, Vt and Vn
-//   bwd_chain_kernel   per (sequence, V head, 16 columns), in reverse: the
+//   bwd_chain_kernel   per (sequence, V head, 32 columns), in reverse: the
 //                      state gradient at every chunk end, dVn and dVt (= dv^)
 //   bwd_grad_kernel    per (chunk, V head): dq^, dk^ (per V head), dgamma,
 //                      dbeta -> grad_a, grad_b
@@ -32,7 +32,7 @@
 //                      conv weight gradients
 //   bwd_dw_kernel      the conv weight gradient, summed over chunks in order
 // The state columns are independent in the update, so the two sequential
-// passes split them over eight workgroups per (sequence, V head).
+// passes split them over four workgroups per (sequence, V head).
 #include "../../include/gdn.h"
 
 #include <hip/hip_runtime.h>
@@ -44,11 +44,15 @@ namespace gdn {
 namespace {
 
 constexpr int kBT = 256;  // threads of every backward workgroup
-constexpr int kCB = 16;   // state columns per workgroup of the sequential passes
-constexpr int kLK = 129;  // LDS row stride of 64 x 128 fp32 tiles
-constexpr int kLN = 65;   // LDS row stride of 64 x 64 fp32 tiles
-constexpr int kLC = 17;   // LDS row stride of 64 x 16 fp32 column slices
+constexpr int kCB = 32;   // state columns per workgroup of the sequential passes
+constexpr int kLK = 132;  // LDS row stride of 64 x 128 fp32 tiles (16-byte rows, 4-bank skew)
+constexpr int kLN = 68;   // LDS row stride of 64 x 64 fp32 tiles
+constexpr int kLC = kCB;  // LDS row stride of kCB-column slices (read as broadcasts)
 constexpr int kNCB = kD / kCB;
+constexpr int kST = 512;             // threads of a sequential-pass workgroup (two waves per SIMD)
+constexpr int kSE = kD * kCB / kST;  // state elements per thread (row t / kSP, kSE columns)
+constexpr int kVE = 64 * kCB / kST;  // slice elements per thread (row t / kVP, kVE columns)
+constexpr int kSP = kCB / kSE, kVP = kCB / kVE;
 
 struct BwdArgs {
     const uint16_t *q, *k, *v;
@@ -189,9 +193,24 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs p, BwdWs ws)
 // ---------------------------------------------------------------------------
 // 2. P and X = (I + A)^-1 per (chunk, V head)
 // ---------------------------------------------------------------------------
+// Column of (I + A)^-1 for a strictly lower A (row stride kLN), y = e_c on
+// entry: right-looking substitution, expanded at compile time so that y
+// stays in registers.
+template <int M>
+struct SolveCol64 {
+    static __device__ __forceinline__ void run(float (&y)[64], const float *A)
+    {
+        if constexpr (M < 63) {
+#pragma unroll
+            for (int ii = M + 1; ii < 64; ++ii) y[ii] = fmaf(-A[ii * kLN + M], y[M], y[ii]);
+            SolveCol64<M + 1>::run(y, A);
+        }
+    }
+};
+
 __global__ __launch_bounds__(kBT) void bwd_local_kernel(BwdArgs p, BwdWs ws)
 {
-    __shared__ float Ks[64 * kLK], Qs[64 * kLK], As[64 * kLN], Xs[64 * kLN];
+    __shared__ float Ks[64 * kLK], Qs[64 * kLK], As[64 * kLN];
     __shared__ float gam[64], bet[64];
     const int Hv = p.Hv, G = Hv / p.Hqk;
     const int cidx = blockIdx.x / Hv, h = blockIdx.x % Hv, g = h / G;
@@ -212,33 +231,38 @@ __global__ __launch_bounds__(kBT) void bwd_local_kernel(BwdArgs p, BwdWs ws)
     __syncthreads();
     const long mo = ((long)cidx * Hv + h) * 64 * 64;
     {
+        // row i, columns (t & 3) + 4m
         const int i = t >> 2;
+        float kk[16], qk[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) kk[m] = qk[m] = 0.f;
+        for (int d = 0; d < kD; ++d) {
+            const float ki = Ks[i * kLK + d], qi = Qs[i * kLK + d];
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const float kj = Ks[((t & 3) + 4 * m) * kLK + d];
+                kk[m] = fmaf(ki, kj, kk[m]);
+                qk[m] = fmaf(qi, kj, qk[m]);
+            }
+        }
+#pragma unroll
         for (int m = 0; m < 16; ++m) {
             const int jj = (t & 3) + 4 * m;
-            float kk = 0.f, qk = 0.f;
-            for (int d = 0; d < kD; ++d) {
-                kk = fmaf(Ks[i * kLK + d], Ks[jj * kLK + d], kk);
-                qk = fmaf(Qs[i * kLK + d], Ks[jj * kLK + d], qk);
-            }
             const float D = expf(gam[i] - gam[jj]);
-            As[i * kLN + jj] = (jj < i && i < n) ? bet[i] * kk * D : 0.f;
-            ws.P[mo + i * 64 + jj] = (jj <= i && i < n) ? qk * D : 0.f;
+            As[i * kLN + jj] = (jj < i && i < n) ? bet[i] * kk[m] * D : 0.f;
+            ws.P[mo + i * 64 + jj] = (jj <= i && i < n) ? qk[m] * D : 0.f;
         }
     }
     __syncthreads();
-    // unit lower-triangular inverse, thread c takes column c: x_i = [i == c] - sum_{m<i} A_im x_m
+    // unit lower-triangular inverse, lane c takes column c in registers:
+    // once x_m is final it is removed from every later row
     if (t < 64) {
-        const int c = t;
-        for (int i = 0; i < 64; ++i) {
-            float xv = i == c ? 1.f : 0.f;
-            for (int m = c; m < i; ++m) xv = fmaf(-As[i * kLN + m], Xs[m * kLN + c], xv);
-            Xs[i * kLN + c] = i >= c ? xv : 0.f;
-        }
-    }
-    __syncthreads();
-    for (int e = 0; e < 16; ++e) {
-        const int idx = t + kBT * e, r = idx >> 6, c = idx & 63;
-        ws.X[mo + idx] = Xs[r * kLN + c];
+        float y[64];
+#pragma unroll
+        for (int ii = 0; ii < 64; ++ii) y[ii] = ii == t ? 1.f : 0.f;
+        SolveCol64<0>::run(y, As);
+#pragma unroll
+        for (int ii = 0; ii < 64; ++ii) ws.X[mo + ii * 64 + t] = y[ii];
     }
 }
 
@@ -249,22 +273,40 @@ struct SeqTile {
     float gam[64], bet[64], eg[64], en[64];
 };
 
+__device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ void st4(float *p, float4 v) { *reinterpret_cast<float4 *>(p) = v; }
+
+// K^ (and Q^) rows of a chunk, 16 bytes per load; rows >= n are zero
+template <int NT>
+__device__ __forceinline__ void load_rows128(const float *src, long t0, int n, int ld_tok, float *dst)
+{
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int e = 0; e < 2048 / NT; ++e) {
+        const int idx = t + NT * e, r = idx >> 5, q = idx & 31;
+        st4(dst + r * kLK + 4 * q, r < n ? ld4(src + (t0 + r) * ld_tok + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f));
+    }
+}
+template <int NT>
+__device__ __forceinline__ void load_tile64(const float *src, float *dst)
+{
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int e = 0; e < 1024 / NT; ++e) {
+        const int idx = t + NT * e, r = idx >> 4, q = idx & 15;
+        st4(dst + r * kLN + 4 * q, ld4(src + r * 64 + 4 * q));
+    }
+}
+
 __device__ __forceinline__ void load_seq_tile(const BwdArgs &p, const BwdWs &ws, SeqTile &L, long t0, int n,
                                               int cidx, int h, int g, float *Qopt, float *Popt)
 {
     const int t = threadIdx.x, Hv = p.Hv;
-    for (int e = 0; e < 32; ++e) {
-        const int idx = t + kBT * e, r = idx >> 7, d = idx & 127;
-        const long src = ((t0 + r) * p.Hqk + g) * kD + d;
-        L.K[r * kLK + d] = r < n ? ws.kh[src] : 0.f;
-        if (Qopt) Qopt[r * kLK + d] = r < n ? ws.qh[src] : 0.f;
-    }
+    load_rows128<kST>(ws.kh + (long)g * kD, t0, n, p.Hqk * kD, L.K);
+    if (Qopt) load_rows128<kST>(ws.qh + (long)g * kD, t0, n, p.Hqk * kD, Qopt);
     const long mo = ((long)cidx * Hv + h) * 64 * 64;
-    for (int e = 0; e < 16; ++e) {
-        const int idx = t + kBT * e, r = idx >> 6, c = idx & 63;
-        L.X[r * kLN + c] = ws.X[mo + idx];
-        if (Popt) Popt[r * kLN + c] = ws.P[mo + idx];
-    }
+    load_tile64<kST>(ws.X + mo, L.X);
+    if (Popt) load_tile64<kST>(ws.P + mo, Popt);
     if (t < 64) {
         const float gl = ws.gam[(t0 + n - 1) * Hv + h];
         const float gr = t < n ? ws.gam[(t0 + t) * Hv + h] : 0.f;
@@ -275,71 +317,87 @@ __device__ __forceinline__ void load_seq_tile(const BwdArgs &p, const BwdWs &ws,
     }
 }
 
+// kCB columns of a chunk's rows of a [tok][Hv][128] tensor, 16 bytes per load
+__device__ __forceinline__ void load_slice(const float *src, long t0, int n, int Hv, int h, int col0, float *dst)
+{
+    const int t = threadIdx.x;
+    constexpr int Q = kCB / 4;
+#pragma unroll
+    for (int e = 0; e < 64 * Q / kST; ++e) {
+        const int idx = t + kST * e, r = idx / Q, q = idx % Q;
+        st4(dst + r * kLC + 4 * q,
+            r < n ? ld4(src + ((t0 + r) * Hv + h) * kD + col0 + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f));
+    }
+}
+
 // ---------------------------------------------------------------------------
 // 3. forward again, keeping the state entering every chunk, Vt and Vn
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kBT) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
+__global__ __launch_bounds__(kST) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
 {
     __shared__ SeqTile L;
-    __shared__ float Ss[kD * kLC], Vs[64 * kLC], Vts[64 * kLC], Vns[64 * kLC];
+    __shared__ __attribute__((aligned(16))) float Ss[kD * kLC], Vs[64 * kLC], Vts[64 * kLC], Vns[64 * kLC];
     const int Hv = p.Hv, G = Hv / p.Hqk;
     const int cb = blockIdx.x % kNCB, sh = blockIdx.x / kNCB, h = sh % Hv, s = sh / Hv, g = h / G;
     const int col0 = cb * kCB;
-    const int t = threadIdx.x, i = t >> 1, c0 = (t & 1) * 8;
-    float S[8];
+    const int t = threadIdx.x, i = t / kSP, c0 = (t % kSP) * kSE;  // state: row i, columns c0..c0+kSE-1
+    const int r = t / kVP, cq = (t % kVP) * kVE;                     // slices: row r, columns cq..cq+kVE-1
+    float S[kSE];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+    for (int e = 0; e < kSE; ++e)
         S[e] = p.state_in ? p.state_in[(((long)s * Hv + h) * kD + i) * kD + col0 + c0 + e] : 0.f;
     for (int j = 0; j < p.nc; ++j) {
         const int cidx = s * p.nc + j, n = min(kChunk, p.T - j * kChunk);
         const long t0 = (long)s * p.T + (long)j * kChunk;
         float *sc = ws.Sc + ((((long)cidx * Hv + h) * kD + i) * kD + col0 + c0);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            sc[e] = S[e];
-            Ss[i * kLC + c0 + e] = S[e];
+        for (int e = 0; e < kSE; e += 4) {
+            const float4 v = make_float4(S[e], S[e + 1], S[e + 2], S[e + 3]);
+            st4(sc + e, v);
+            st4(Ss + i * kLC + c0 + e, v);
         }
         load_seq_tile(p, ws, L, t0, n, cidx, h, g, nullptr, nullptr);
-        for (int e = 0; e < 4; ++e) {
-            const int idx = t + kBT * e, r = idx >> 4, c = idx & 15;
-            Vs[r * kLC + c] = r < n ? ws.vh[((t0 + r) * Hv + h) * kD + col0 + c] : 0.f;
-        }
+        load_slice(ws.vh, t0, n, Hv, h, col0, Vs);
         __syncthreads();
-        const int r = t >> 2, c4 = (t & 3) * 4;
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        // Vt = V - diag(Gam) K S
+        float acc[kVE];
+#pragma unroll
+        for (int e = 0; e < kVE; ++e) acc[e] = 0.f;
         for (int d = 0; d < kD; ++d) {
             const float kv = L.K[r * kLK + d];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = fmaf(kv, Ss[d * kLC + c4 + e], acc[e]);
+            for (int e = 0; e < kVE; ++e) acc[e] = fmaf(kv, Ss[d * kLC + cq + e], acc[e]);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float vt = r < n ? Vs[r * kLC + c4 + e] - L.eg[r] * acc[e] : 0.f;
-            Vts[r * kLC + c4 + e] = vt;
-            if (r < n) ws.vt[((t0 + r) * Hv + h) * kD + col0 + c4 + e] = vt;
+        for (int e = 0; e < kVE; ++e) {
+            const float vt = r < n ? Vs[r * kLC + cq + e] - L.eg[r] * acc[e] : 0.f;
+            Vts[r * kLC + cq + e] = vt;
+            if (r < n) ws.vt[((t0 + r) * Hv + h) * kD + col0 + cq + e] = vt;
         }
         __syncthreads();
+        // Vn = X diag(beta) Vt
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = 0.f;
+        for (int e = 0; e < kVE; ++e) acc[e] = 0.f;
         for (int m = 0; m <= r; ++m) {
             const float bx = L.X[r * kLN + m] * L.bet[m];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = fmaf(bx, Vts[m * kLC + c4 + e], acc[e]);
+            for (int e = 0; e < kVE; ++e) acc[e] = fmaf(bx, Vts[m * kLC + cq + e], acc[e]);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < kVE; ++e) {
             const float vn = r < n ? acc[e] : 0.f;
-            Vns[r * kLC + c4 + e] = vn;
-            if (r < n) ws.vn[((t0 + r) * Hv + h) * kD + col0 + c4 + e] = vn;
+            Vns[r * kLC + cq + e] = vn;
+            if (r < n) ws.vn[((t0 + r) * Hv + h) * kD + col0 + cq + e] = vn;
         }
         __syncthreads();
+        // S <- Gam_n S + Ks^T Vn
         const float egn = L.eg[n - 1];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) S[e] *= egn;
+        for (int e = 0; e < kSE; ++e) S[e] *= egn;
         for (int rr = 0; rr < n; ++rr) {
             const float kr = L.K[rr * kLK + i] * L.en[rr];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) S[e] = fmaf(kr, Vns[rr * kLC + c0 + e], S[e]);
+            for (int e = 0; e < kSE; ++e) S[e] = fmaf(kr, Vns[rr * kLC + c0 + e], S[e]);
         }
         __syncthreads();
     }
@@ -348,86 +406,99 @@ __global__ __launch_bounds__(kBT) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
 // ---------------------------------------------------------------------------
 // 4. the state gradient, chunk by chunk from the last
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kBT) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
+__global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
 {
     __shared__ SeqTile L;
-    __shared__ float Qs[64 * kLK], Ps[64 * kLN];
-    __shared__ float dSs[kD * kLC], dOs[64 * kLC], dVns[64 * kLC], dVts[64 * kLC];
+    __shared__ __attribute__((aligned(16))) float Qs[64 * kLK], Ps[64 * kLN];
+    __shared__ __attribute__((aligned(16))) float dSs[kD * kLC], dOs[64 * kLC], dVns[64 * kLC], dVts[64 * kLC];
     const int Hv = p.Hv, G = Hv / p.Hqk;
     const int cb = blockIdx.x % kNCB, sh = blockIdx.x / kNCB, h = sh % Hv, s = sh / Hv, g = h / G;
     const int col0 = cb * kCB;
-    const int t = threadIdx.x, i = t >> 1, c0 = (t & 1) * 8;
+    const int t = threadIdx.x, i = t / kSP, c0 = (t % kSP) * kSE;
+    const int r = t / kVP, cq = (t % kVP) * kVE;
     const long so = (((long)s * Hv + h) * kD + i) * kD + col0 + c0;
-    float dS[8];
+    float dS[kSE];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dS[e] = p.grad_state_out ? p.grad_state_out[so + e] : 0.f;
+    for (int e = 0; e < kSE; ++e) dS[e] = p.grad_state_out ? p.grad_state_out[so + e] : 0.f;
     for (int j = p.nc - 1; j >= 0; --j) {
         const int cidx = s * p.nc + j, n = min(kChunk, p.T - j * kChunk);
         const long t0 = (long)s * p.T + (long)j * kChunk;
         float *dsc = ws.dSc + ((((long)cidx * Hv + h) * kD + i) * kD + col0 + c0);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            dsc[e] = dS[e];
-            dSs[i * kLC + c0 + e] = dS[e];
+        for (int e = 0; e < kSE; e += 4) {
+            const float4 v = make_float4(dS[e], dS[e + 1], dS[e + 2], dS[e + 3]);
+            st4(dsc + e, v);
+            st4(dSs + i * kLC + c0 + e, v);
         }
         load_seq_tile(p, ws, L, t0, n, cidx, h, g, Qs, Ps);
-        for (int e = 0; e < 4; ++e) {
-            const int idx = t + kBT * e, r = idx >> 4, c = idx & 15;
-            dOs[r * kLC + c] = r < n ? p.q_scale * bf16_to_f32(p.grad_o[((t0 + r) * Hv + h) * kD + col0 + c]) : 0.f;
+        {
+            constexpr int Q = kCB / 4;
+#pragma unroll
+            for (int e = 0; e < 64 * Q / kST; ++e) {
+                const int idx = t + kST * e, rr = idx / Q, q = idx % Q;
+                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (rr < n) {
+                    const uint2 u = *reinterpret_cast<const uint2 *>(p.grad_o + ((t0 + rr) * Hv + h) * kD + col0 + 4 * q);
+                    v = make_float4(p.q_scale * bf16_lo(u.x), p.q_scale * bf16_hi(u.x), p.q_scale * bf16_lo(u.y),
+                                    p.q_scale * bf16_hi(u.y));
+                }
+                st4(dOs + rr * kLC + 4 * q, v);
+            }
         }
         __syncthreads();
-        const int r = t >> 2, c4 = (t & 3) * 4;
         // dVn = Ks dS' + P^T dO'
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        float acc[kVE];
+#pragma unroll
+        for (int e = 0; e < kVE; ++e) acc[e] = 0.f;
         for (int d = 0; d < kD; ++d) {
             const float kv = L.K[r * kLK + d];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = fmaf(kv, dSs[d * kLC + c4 + e], acc[e]);
+            for (int e = 0; e < kVE; ++e) acc[e] = fmaf(kv, dSs[d * kLC + cq + e], acc[e]);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] *= L.en[r];
+        for (int e = 0; e < kVE; ++e) acc[e] *= L.en[r];
         for (int m = r; m < n; ++m) {
             const float pv = Ps[m * kLN + r];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = fmaf(pv, dOs[m * kLC + c4 + e], acc[e]);
+            for (int e = 0; e < kVE; ++e) acc[e] = fmaf(pv, dOs[m * kLC + cq + e], acc[e]);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < kVE; ++e) {
             const float v = r < n ? acc[e] : 0.f;
-            dVns[r * kLC + c4 + e] = v;
-            if (r < n) ws.dvn[((t0 + r) * Hv + h) * kD + col0 + c4 + e] = v;
+            dVns[r * kLC + cq + e] = v;
+            if (r < n) ws.dvn[((t0 + r) * Hv + h) * kD + col0 + cq + e] = v;
         }
         __syncthreads();
         // dVt = T'^T dVn = diag(beta) X^T dVn
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = 0.f;
+        for (int e = 0; e < kVE; ++e) acc[e] = 0.f;
         for (int m = r; m < n; ++m) {
             const float xv = L.X[m * kLN + r];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = fmaf(xv, dVns[m * kLC + c4 + e], acc[e]);
+            for (int e = 0; e < kVE; ++e) acc[e] = fmaf(xv, dVns[m * kLC + cq + e], acc[e]);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < kVE; ++e) {
             const float v = r < n ? L.bet[r] * acc[e] : 0.f;
-            dVts[r * kLC + c4 + e] = v;
-            if (r < n) ws.dvh[((t0 + r) * Hv + h) * kD + col0 + c4 + e] = v;
+            dVts[r * kLC + cq + e] = v;
+            if (r < n) ws.dvh[((t0 + r) * Hv + h) * kD + col0 + cq + e] = v;
         }
         __syncthreads();
         // dS <- Gam_n dS' + (Gam Q)^T dO' - (Gam K)^T dVt
         const float egn = L.eg[n - 1];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dS[e] *= egn;
+        for (int e = 0; e < kSE; ++e) dS[e] *= egn;
         for (int rr = 0; rr < n; ++rr) {
             const float qv = Qs[rr * kLK + i] * L.eg[rr], kv = L.K[rr * kLK + i] * L.eg[rr];
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
+            for (int e = 0; e < kSE; ++e)
                 dS[e] = fmaf(qv, dOs[rr * kLC + c0 + e], fmaf(-kv, dVts[rr * kLC + c0 + e], dS[e]));
         }
         __syncthreads();
     }
     if (p.grad_state_in) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) p.grad_state_in[so + e] = dS[e];
+        for (int e = 0; e < kSE; ++e) p.grad_state_in[so + e] = dS[e];
     }
 }
 
@@ -436,25 +507,30 @@ __global__ __launch_bounds__(kBT) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
 // ---------------------------------------------------------------------------
 // acc[ri][m] += sum_k fa(r0 + ri, k) fb(k, cc + 16 m) for k < K (a multiple
 // of 32), r0 = 4 (t / 16), cc = t % 16, m < NC: a 64 x (16 NC) product,
-// staged through LDS 32 deep.
-template <int NC, class FA, class FB>
+// staged through LDS 32 deep.  AK: fa's source is contiguous along k (else
+// along rows); BK: fb's source is contiguous along k (else along columns).
+// Consecutive threads stage consecutive source elements; the staging loops
+// are unrolled only twice, which keeps the kernel within 256 registers.
+template <int NC, bool AK = true, bool BK = false, class FA, class FB>
 __device__ __forceinline__ void gemm64(float (&acc)[4][8], int K, FA fa, FB fb, float *sA, float *sB)
 {
     const int t = threadIdx.x, r0 = 4 * (t >> 4), cc = t & 15;
     constexpr int NCOL = 16 * NC, LB = NCOL + 1;
     for (int k0 = 0; k0 < K; k0 += 32) {
-#pragma unroll
+#pragma unroll 2
         for (int e = 0; e < 8; ++e) {
-            const int idx = t + kBT * e, r = idx >> 5, kk = idx & 31;
+            const int idx = t + kBT * e;
+            const int r = AK ? idx >> 5 : idx & 63, kk = AK ? idx & 31 : idx >> 6;
             sA[r * 33 + kk] = fa(r, k0 + kk);
         }
-#pragma unroll
+#pragma unroll 2
         for (int e = 0; e < 2 * NC; ++e) {
-            const int idx = t + kBT * e, kk = idx / NCOL, c = idx % NCOL;
+            const int idx = t + kBT * e;
+            const int kk = BK ? idx & 31 : idx / NCOL, c = BK ? idx >> 5 : idx % NCOL;
             sB[kk * LB + c] = fb(k0 + kk, c);
         }
         __syncthreads();
-#pragma unroll 4
+#pragma unroll 2
         for (int kk = 0; kk < 32; ++kk) {
             float av[4], bv[NC];
 #pragma unroll
@@ -488,7 +564,7 @@ __device__ __forceinline__ float sum16(float v)
     return v;
 }
 
-__global__ __launch_bounds__(kBT) void bwd_grad_kernel(BwdArgs p, BwdWs ws)
+__global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_grad_kernel(BwdArgs p, BwdWs ws)
 {
     __shared__ float sA[64 * 33], sB[32 * 129];
     __shared__ float Em[64 * kLN], Wm[64 * kLN], Ym[64 * kLN];
@@ -528,14 +604,57 @@ __global__ __launch_bounds__(kBT) void bwd_grad_kernel(BwdArgs p, BwdWs ws)
             if (cc == 0 && r < n) dst[r] += sign * (coef ? coef[r] : 1.f) * v;
         }
     };
-    float dQ[4][8], dK[4][8], acc[4][8];
-    zero(dQ);
+    float acc[4][8];
+    {
+        // ---- dq^ first, so that its registers are free before dk^ is formed
+        float dQ[4][8];
+        zero(dQ);
+        // (c) O = q_scale (diag(Gam) Q S + ...): E1 = dO' S^T
+        zero(acc);
+        gemm64<8, true, true>(acc, kD, DO, [&](int c, int i) { return Sc[i * kD + c]; }, sA, sB);
+        float part[4];
+#pragma unroll
+        for (int ri = 0; ri < 4; ++ri) {
+            const int r = r0 + ri;
+            part[ri] = 0.f;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                dQ[ri][m] += eg[r] * acc[ri][m];
+                part[ri] = fmaf(acc[ri][m], QH(r, cc + 16 * m), part[ri]);
+            }
+        }
+        row_apply(part, dgam, eg, 1.f);
+        // (d) P = Q K^T * D * M: dP = dO' Vn^T (lower); Em = dP * P; Wm = dP * D
+        zero(acc);
+        gemm64<4, true, true>(acc, kD, DO, [&](int c, int jj) { return VROW(ws.vn, jj, c); }, sA, sB);
+#pragma unroll
+        for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int r = r0 + ri, jj = cc + 16 * m;
+                const bool in = jj <= r && r < n;
+                Em[r * kLN + jj] = in ? acc[ri][m] * ws.P[mo + r * 64 + jj] : 0.f;
+                Wm[r * kLN + jj] = in ? acc[ri][m] * expf(gam[r] - gam[jj]) : 0.f;
+            }
+        __syncthreads();
+        gemm64<8>(dQ, 64, [&](int r, int jj) { return Wm[r * kLN + jj]; }, KH, sA, sB);
+#pragma unroll
+        for (int ri = 0; ri < 4; ++ri) {
+            const int r = r0 + ri;
+            if (r >= n) continue;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) ws.dqp[((t0 + r) * Hv + h) * kD + cc + 16 * m] = dQ[ri][m];
+        }
+    }
+    float dK[4][8];
     zero(dK);
+    // (d) continued: dk^ += dQK^T q^
+    gemm64<8, false>(dK, 64, [&](int r, int jj) { return Wm[jj * kLN + r]; }, QH, sA, sB);
 
     // (a) Ks = diag(en) K enters S' = ... + Ks^T Vn: dKs = Vn dS'^T
     zero(acc);
-    gemm64<8>(acc, kD, [&](int r, int c) { return VROW(ws.vn, r, c); },
-              [&](int c, int i) { return dSc[i * kD + c]; }, sA, sB);
+    gemm64<8, true, true>(acc, kD, [&](int r, int c) { return VROW(ws.vn, r, c); },
+                          [&](int c, int i) { return dSc[i * kD + c]; }, sA, sB);
     {
         float part[4];
 #pragma unroll
@@ -573,29 +692,10 @@ __global__ __launch_bounds__(kBT) void bwd_grad_kernel(BwdArgs p, BwdWs ws)
     __syncthreads();
     if (t < n) dgam[t] -= rowv[t];
     __syncthreads();
-
-    // (c) O = q_scale (diag(Gam) Q S + ...): E1 = dO' S^T
-    zero(acc);
-    gemm64<8>(acc, kD, DO, [&](int c, int i) { return Sc[i * kD + c]; }, sA, sB);
-    {
-        float part[4];
-#pragma unroll
-        for (int ri = 0; ri < 4; ++ri) {
-            const int r = r0 + ri;
-            part[ri] = 0.f;
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                dQ[ri][m] += eg[r] * acc[ri][m];
-                part[ri] = fmaf(acc[ri][m], QH(r, cc + 16 * m), part[ri]);
-            }
-        }
-        row_apply(part, dgam, eg, 1.f);
-    }
-    __syncthreads();
     // (e) Vt = V - diag(Gam) K S: E2 = dVt S^T
     zero(acc);
-    gemm64<8>(acc, kD, [&](int r, int c) { return VROW(ws.dvh, r, c); },
-              [&](int c, int i) { return Sc[i * kD + c]; }, sA, sB);
+    gemm64<8, true, true>(acc, kD, [&](int r, int c) { return VROW(ws.dvh, r, c); },
+                          [&](int c, int i) { return Sc[i * kD + c]; }, sA, sB);
     {
         float part[4];
 #pragma unroll
@@ -611,25 +711,10 @@ __global__ __launch_bounds__(kBT) void bwd_grad_kernel(BwdArgs p, BwdWs ws)
         row_apply(part, dgam, eg, -1.f);
     }
     __syncthreads();
-    // (d) P = Q K^T * D * M: dP = dO' Vn^T (lower); Em = dP * P; Wm = dP * D
-    zero(acc);
-    gemm64<4>(acc, kD, DO, [&](int c, int jj) { return VROW(ws.vn, jj, c); }, sA, sB);
-#pragma unroll
-    for (int ri = 0; ri < 4; ++ri)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int r = r0 + ri, jj = cc + 16 * m;
-            const bool in = jj <= r && r < n;
-            Em[r * kLN + jj] = in ? acc[ri][m] * ws.P[mo + r * 64 + jj] : 0.f;
-            Wm[r * kLN + jj] = in ? acc[ri][m] * expf(gam[r] - gam[jj]) : 0.f;
-        }
-    __syncthreads();
-    gemm64<8>(dQ, 64, [&](int r, int jj) { return Wm[r * kLN + jj]; }, KH, sA, sB);
-    gemm64<8>(dK, 64, [&](int r, int jj) { return Wm[jj * kLN + r]; }, QH, sA, sB);
     // (f) Vn = T' Vt: dT' = dVn Vt^T (lower incl. diagonal); dbeta_j += sum_i dT'_ij X_ij; dX = dT' diag(beta)
     zero(acc);
-    gemm64<4>(acc, kD, [&](int r, int c) { return VROW(ws.dvn, r, c); },
-              [&](int c, int jj) { return VROW(ws.vt, jj, c); }, sA, sB);
+    gemm64<4, true, true>(acc, kD, [&](int r, int c) { return VROW(ws.dvn, r, c); },
+                          [&](int c, int jj) { return VROW(ws.vt, jj, c); }, sA, sB);
 #pragma unroll
     for (int ri = 0; ri < 4; ++ri)
 #pragma unroll
@@ -648,16 +733,16 @@ __global__ __launch_bounds__(kBT) void bwd_grad_kernel(BwdArgs p, BwdWs ws)
     __syncthreads();
     // (g) X = (I + A)^-1: dA = strict_lower(-X^T dX X^T)
     zero(acc);
-    gemm64<4>(acc, 64, [&](int r, int m) { return ws.X[mo + m * 64 + r]; },
-              [&](int m, int jj) { return Wm[m * kLN + jj]; }, sA, sB);
+    gemm64<4, false>(acc, 64, [&](int r, int m) { return ws.X[mo + m * 64 + r]; },
+                     [&](int m, int jj) { return Wm[m * kLN + jj]; }, sA, sB);
 #pragma unroll
     for (int ri = 0; ri < 4; ++ri)
 #pragma unroll
         for (int m = 0; m < 4; ++m) Ym[(r0 + ri) * kLN + cc + 16 * m] = acc[ri][m];
     __syncthreads();
     zero(acc);
-    gemm64<4>(acc, 64, [&](int r, int m) { return Ym[r * kLN + m]; },
-              [&](int m, int jj) { return ws.X[mo + jj * 64 + m]; }, sA, sB);
+    gemm64<4, true, true>(acc, 64, [&](int r, int m) { return Ym[r * kLN + m]; },
+                          [&](int m, int jj) { return ws.X[mo + jj * 64 + m]; }, sA, sB);
 #pragma unroll
     for (int ri = 0; ri < 4; ++ri)
 #pragma unroll
@@ -668,7 +753,7 @@ __global__ __launch_bounds__(kBT) void bwd_grad_kernel(BwdArgs p, BwdWs ws)
     __syncthreads();
     // (h) A = diag(beta) K K^T * D (strict lower): dbeta_i, Em += dA * A, dKK -> Ym
     zero(acc);
-    gemm64<4>(acc, kD, KH, [&](int d, int jj) { return KH(jj, d); }, sA, sB);
+    gemm64<4, true, true>(acc, kD, KH, [&](int d, int jj) { return KH(jj, d); }, sA, sB);
     {
         float part[4];
 #pragma unroll
@@ -710,11 +795,7 @@ __global__ __launch_bounds__(kBT) void bwd_grad_kernel(BwdArgs p, BwdWs ws)
         const int r = r0 + ri;
         if (r >= n) continue;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const long o = ((t0 + r) * Hv + h) * kD + cc + 16 * m;
-            ws.dqp[o] = dQ[ri][m];
-            ws.dkp[o] = dK[ri][m];
-        }
+        for (int m = 0; m < 8; ++m) ws.dkp[((t0 + r) * Hv + h) * kD + cc + 16 * m] = dK[ri][m];
     }
 }
 
@@ -744,8 +825,14 @@ __global__ __launch_bounds__(kBT) void bwd_dy_kernel(BwdArgs p, BwdWs ws)
         return;
     }
     const float *part = P.kind == 0 ? ws.dqp : ws.dkp;
-    for (int r = rh; r < n; r += 2) {
+    float yv[32];  // conv outputs of rows rh, rh + 2, ...
+#pragma unroll
+    for (int ii = 0; ii < 32; ++ii) {
+        const int r = rh + 2 * ii;
+        yv[ii] = 0.f;
+        if (r >= n) continue;
         const float y = conv_y(p, P, x, w, s, j * kChunk + r, c, C_tot);
+        yv[ii] = y;
         zs[r * kLK + c] = y * sigm(y);
         float d = 0.f;
         for (int jh = 0; jh < G; ++jh) d += part[((t0 + r) * p.Hv + P.head * G + jh) * kD + c];
@@ -771,11 +858,13 @@ __global__ __launch_bounds__(kBT) void bwd_dy_kernel(BwdArgs p, BwdWs ws)
         }
     }
     __syncthreads();
-    for (int r = rh; r < n; r += 2) {
-        const float y = conv_y(p, P, x, w, s, j * kChunk + r, c, C_tot);
+#pragma unroll
+    for (int ii = 0; ii < 32; ++ii) {
+        const int r = rh + 2 * ii;
+        if (r >= n) continue;
         const float rn = nrm[r];
         const float dz = ds[r * kLK + c] / rn - zs[r * kLK + c] * zd[r] / (rn * rn * rn);
-        ws.dy[(t0 + r) * C_tot + P.ch0 + c] = dz * silu_grad(y);
+        ws.dy[(t0 + r) * C_tot + P.ch0 + c] = dz * silu_grad(yv[ii]);
     }
 }
 
@@ -920,10 +1009,10 @@ hipError_t launch_backward(const uint16_t *q, const uint16_t *k, const uint16_t 
     if (chunks > 0) {
         hipLaunchKernelGGL(bwd_prep_kernel, dim3(chunks, planes), dim3(kBT), 0, stream, p, ws);
         hipLaunchKernelGGL(bwd_local_kernel, dim3(chunks * Hv), dim3(kBT), 0, stream, p, ws);
-        hipLaunchKernelGGL(bwd_fwd_kernel, dim3(B * Hv * kNCB), dim3(kBT), 0, stream, p, ws);
+        hipLaunchKernelGGL(bwd_fwd_kernel, dim3(B * Hv * kNCB), dim3(kST), 0, stream, p, ws);
     }
     // also with T = 0: the state gradient passes straight through
-    hipLaunchKernelGGL(bwd_chain_kernel, dim3(B * Hv * kNCB), dim3(kBT), 0, stream, p, ws);
+    hipLaunchKernelGGL(bwd_chain_kernel, dim3(B * Hv * kNCB), dim3(kST), 0, stream, p, ws);
     if (chunks > 0) {
         hipLaunchKernelGGL(bwd_grad_kernel, dim3(chunks * Hv), dim3(kBT), 0, stream, p, ws);
         hipLaunchKernelGGL(bwd_dy_kernel, dim3(chunks, planes), dim3(kBT), 0, stream, p, ws);

@@ -165,6 +165,7 @@ def test_backward_validation(L):
     assert call_backward(L, Hv=7) == gdn.GDN_ERR_UNSUPPORTED
     assert call_backward(L, q=FAKE + 2) == gdn.GDN_ERR_INVALID_ARGUMENT
     assert call_backward(L, ws=FAKE + 4) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call_backward(L, g_o=FAKE + 4) == gdn.GDN_ERR_INVALID_ARGUMENT
     assert call_backward(L, ws_bytes=need - 1) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL
     assert call_backward(L, ws=0) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL
     assert call_backward(L, B=0, ws=0, ws_bytes=0) == gdn.GDN_OK
