@@ -276,57 +276,91 @@ struct SeqTile {
 __device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 __device__ __forceinline__ void st4(float *p, float4 v) { *reinterpret_cast<float4 *>(p) = v; }
 
-// K^ (and Q^) rows of a chunk, 16 bytes per load; rows >= n are zero
-template <int NT>
-__device__ __forceinline__ void load_rows128(const float *src, long t0, int n, int ld_tok, float *dst)
+// A chunk's operands for the sequential passes, held in registers: they are
+// requested before the current chunk's products and written to LDS after
+// them, so that their load latency overlaps the arithmetic.  kChain: the
+// backward pass (q^, P and dO as well; else V).
+constexpr int kPrK = 2048 / kST, kPrX = 1024 / kST, kPrS = 64 * kCB / 4 / kST;
+template <bool kChain>
+struct SeqPref {
+    float4 k[kPrK], q[kChain ? kPrK : 1], x[kPrX], pm[kChain ? kPrX : 1], v[kChain ? 1 : kPrS];
+    uint2 o[kChain ? kPrS : 1];
+    float gam, gl, bet;
+    int n;
+    long t0;
+};
+template <bool kChain>
+__device__ __forceinline__ void seq_fetch(const BwdArgs &p, const BwdWs &ws, SeqPref<kChain> &f, int s, int j, int h,
+                                          int g, int col0)
 {
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, Hv = p.Hv, n = min(kChunk, p.T - j * kChunk);
+    const long t0 = (long)s * p.T + (long)j * kChunk, mo = ((long)(s * p.nc + j) * Hv + h) * 64 * 64;
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    f.n = n;
+    f.t0 = t0;
 #pragma unroll
-    for (int e = 0; e < 2048 / NT; ++e) {
-        const int idx = t + NT * e, r = idx >> 5, q = idx & 31;
-        st4(dst + r * kLK + 4 * q, r < n ? ld4(src + (t0 + r) * ld_tok + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f));
+    for (int e = 0; e < kPrK; ++e) {
+        const int idx = t + kST * e, r = idx >> 5, q = idx & 31;
+        const long src = (t0 + r) * p.Hqk * kD + (long)g * kD + 4 * q;
+        f.k[e] = r < n ? ld4(ws.kh + src) : z4;
+        if constexpr (kChain) f.q[e] = r < n ? ld4(ws.qh + src) : z4;
     }
-}
-template <int NT>
-__device__ __forceinline__ void load_tile64(const float *src, float *dst)
-{
-    const int t = threadIdx.x;
 #pragma unroll
-    for (int e = 0; e < 1024 / NT; ++e) {
-        const int idx = t + NT * e, r = idx >> 4, q = idx & 15;
-        st4(dst + r * kLN + 4 * q, ld4(src + r * 64 + 4 * q));
+    for (int e = 0; e < kPrX; ++e) {
+        const int idx = t + kST * e;
+        f.x[e] = ld4(ws.X + mo + 4 * idx);
+        if constexpr (kChain) f.pm[e] = ld4(ws.P + mo + 4 * idx);
     }
-}
-
-__device__ __forceinline__ void load_seq_tile(const BwdArgs &p, const BwdWs &ws, SeqTile &L, long t0, int n,
-                                              int cidx, int h, int g, float *Qopt, float *Popt)
-{
-    const int t = threadIdx.x, Hv = p.Hv;
-    load_rows128<kST>(ws.kh + (long)g * kD, t0, n, p.Hqk * kD, L.K);
-    if (Qopt) load_rows128<kST>(ws.qh + (long)g * kD, t0, n, p.Hqk * kD, Qopt);
-    const long mo = ((long)cidx * Hv + h) * 64 * 64;
-    load_tile64<kST>(ws.X + mo, L.X);
-    if (Popt) load_tile64<kST>(ws.P + mo, Popt);
-    if (t < 64) {
-        const float gl = ws.gam[(t0 + n - 1) * Hv + h];
-        const float gr = t < n ? ws.gam[(t0 + t) * Hv + h] : 0.f;
-        L.gam[t] = gr;
-        L.bet[t] = t < n ? ws.beta[(t0 + t) * Hv + h] : 0.f;
-        L.eg[t] = t < n ? expf(gr) : 0.f;
-        L.en[t] = t < n ? expf(gl - gr) : 0.f;
-    }
-}
-
-// kCB columns of a chunk's rows of a [tok][Hv][128] tensor, 16 bytes per load
-__device__ __forceinline__ void load_slice(const float *src, long t0, int n, int Hv, int h, int col0, float *dst)
-{
-    const int t = threadIdx.x;
     constexpr int Q = kCB / 4;
 #pragma unroll
-    for (int e = 0; e < 64 * Q / kST; ++e) {
+    for (int e = 0; e < kPrS; ++e) {
         const int idx = t + kST * e, r = idx / Q, q = idx % Q;
-        st4(dst + r * kLC + 4 * q,
-            r < n ? ld4(src + ((t0 + r) * Hv + h) * kD + col0 + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f));
+        const long src = ((t0 + r) * Hv + h) * kD + col0 + 4 * q;
+        if constexpr (kChain)
+            f.o[e] = r < n ? *reinterpret_cast<const uint2 *>(p.grad_o + src) : make_uint2(0u, 0u);
+        else
+            f.v[e] = r < n ? ld4(ws.vh + src) : z4;
+    }
+    if (t < 64) {
+        f.gl = ws.gam[(t0 + n - 1) * Hv + h];
+        f.gam = t < n ? ws.gam[(t0 + t) * Hv + h] : 0.f;
+        f.bet = t < n ? ws.beta[(t0 + t) * Hv + h] : 0.f;
+    }
+}
+template <bool kChain>
+__device__ __forceinline__ void seq_commit(const BwdArgs &p, const SeqPref<kChain> &f, SeqTile &L, float *Qs,
+                                           float *Ps, float *slice)
+{
+    const int t = threadIdx.x, n = f.n;
+#pragma unroll
+    for (int e = 0; e < kPrK; ++e) {
+        const int idx = t + kST * e, r = idx >> 5, q = idx & 31;
+        st4(L.K + r * kLK + 4 * q, f.k[e]);
+        if constexpr (kChain) st4(Qs + r * kLK + 4 * q, f.q[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < kPrX; ++e) {
+        const int idx = t + kST * e, r = idx >> 4, q = idx & 15;
+        st4(L.X + r * kLN + 4 * q, f.x[e]);
+        if constexpr (kChain) st4(Ps + r * kLN + 4 * q, f.pm[e]);
+    }
+    constexpr int Q = kCB / 4;
+#pragma unroll
+    for (int e = 0; e < kPrS; ++e) {
+        const int idx = t + kST * e, r = idx / Q, q = idx % Q;
+        if constexpr (kChain) {
+            const uint2 u = f.o[e];
+            st4(slice + r * kLC + 4 * q, make_float4(p.q_scale * bf16_lo(u.x), p.q_scale * bf16_hi(u.x),
+                                                     p.q_scale * bf16_lo(u.y), p.q_scale * bf16_hi(u.y)));
+        } else {
+            st4(slice + r * kLC + 4 * q, f.v[e]);
+        }
+    }
+    if (t < 64) {
+        L.gam[t] = f.gam;
+        L.bet[t] = f.bet;
+        L.eg[t] = t < n ? expf(f.gam) : 0.f;
+        L.en[t] = t < n ? expf(f.gl - f.gam) : 0.f;
     }
 }
 
@@ -346,6 +380,9 @@ __global__ __launch_bounds__(kST) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
 #pragma unroll
     for (int e = 0; e < kSE; ++e)
         S[e] = p.state_in ? p.state_in[(((long)s * Hv + h) * kD + i) * kD + col0 + c0 + e] : 0.f;
+    SeqPref<false> f;
+    seq_fetch<false>(p, ws, f, s, 0, h, g, col0);
+    seq_commit<false>(p, f, L, nullptr, nullptr, Vs);
     for (int j = 0; j < p.nc; ++j) {
         const int cidx = s * p.nc + j, n = min(kChunk, p.T - j * kChunk);
         const long t0 = (long)s * p.T + (long)j * kChunk;
@@ -356,8 +393,7 @@ __global__ __launch_bounds__(kST) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
             st4(sc + e, v);
             st4(Ss + i * kLC + c0 + e, v);
         }
-        load_seq_tile(p, ws, L, t0, n, cidx, h, g, nullptr, nullptr);
-        load_slice(ws.vh, t0, n, Hv, h, col0, Vs);
+        if (j + 1 < p.nc) seq_fetch<false>(p, ws, f, s, j + 1, h, g, col0);
         __syncthreads();
         // Vt = V - diag(Gam) K S
         float acc[kVE];
@@ -400,6 +436,7 @@ __global__ __launch_bounds__(kST) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
             for (int e = 0; e < kSE; ++e) S[e] = fmaf(kr, Vns[rr * kLC + c0 + e], S[e]);
         }
         __syncthreads();
+        if (j + 1 < p.nc) seq_commit<false>(p, f, L, nullptr, nullptr, Vs);
     }
 }
 
@@ -420,6 +457,11 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
     float dS[kSE];
 #pragma unroll
     for (int e = 0; e < kSE; ++e) dS[e] = p.grad_state_out ? p.grad_state_out[so + e] : 0.f;
+    SeqPref<true> f;
+    if (p.nc > 0) {
+        seq_fetch<true>(p, ws, f, s, p.nc - 1, h, g, col0);
+        seq_commit<true>(p, f, L, Qs, Ps, dOs);
+    }
     for (int j = p.nc - 1; j >= 0; --j) {
         const int cidx = s * p.nc + j, n = min(kChunk, p.T - j * kChunk);
         const long t0 = (long)s * p.T + (long)j * kChunk;
@@ -430,21 +472,7 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
             st4(dsc + e, v);
             st4(dSs + i * kLC + c0 + e, v);
         }
-        load_seq_tile(p, ws, L, t0, n, cidx, h, g, Qs, Ps);
-        {
-            constexpr int Q = kCB / 4;
-#pragma unroll
-            for (int e = 0; e < 64 * Q / kST; ++e) {
-                const int idx = t + kST * e, rr = idx / Q, q = idx % Q;
-                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (rr < n) {
-                    const uint2 u = *reinterpret_cast<const uint2 *>(p.grad_o + ((t0 + rr) * Hv + h) * kD + col0 + 4 * q);
-                    v = make_float4(p.q_scale * bf16_lo(u.x), p.q_scale * bf16_hi(u.x), p.q_scale * bf16_lo(u.y),
-                                    p.q_scale * bf16_hi(u.y));
-                }
-                st4(dOs + rr * kLC + 4 * q, v);
-            }
-        }
+        if (j > 0) seq_fetch<true>(p, ws, f, s, j - 1, h, g, col0);
         __syncthreads();
         // dVn = Ks dS' + P^T dO'
         float acc[kVE];
@@ -495,6 +523,7 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
                 dS[e] = fmaf(qv, dOs[rr * kLC + c0 + e], fmaf(-kv, dVts[rr * kLC + c0 + e], dS[e]));
         }
         __syncthreads();
+        if (j > 0) seq_commit<true>(p, f, L, Qs, Ps, dOs);
     }
     if (p.grad_state_in) {
 #pragma unroll
