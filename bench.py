@@ -4,7 +4,8 @@
 A step is one chunked prefill of the model-layer workload (B = 1, T = 8192,
 16 QK / 48 V heads, d = 128, seeded synthetic bf16 inputs already resident in
 HBM).  The decode workload (B = 256 sequences, 64 consecutive in-place steps)
-is timed in the same run and reported under "decode".  Prints ONE JSON line.
+is timed in the same run and reported under "decode", and the training
+backward of the prefill workload under "backward".  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                   [--calibrate-copy]
@@ -46,6 +47,7 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN prefill tokens/s (T=8192, 16QK/48V heads, d=128); decode μs/step at B=256"
 PEAK_MFMA_F16 = 2.5e15      # dense fp16/bf16 matrix-core FLOP/s
 PEAK_HBM = 8.0e12           # bytes/s
+PEAK_VALU_F32 = 157.3e12    # fp32 vector FLOP/s (the published figure counts packed fp32)
 D = 128
 CHUNK = 64
 
@@ -75,6 +77,23 @@ def prefill_bytes(T, Hqk, Hv, d=D):
     """Compulsory HBM bytes of one prefill (zero initial state, no conv carry)."""
     per_tok = 2 * (2 * Hqk * d + Hv * d) + 2 * 4 * Hv + 2 * Hv * d
     return T * per_tok + Hv * d * d * 4 + (2 * Hqk * d + Hv * d) * 4 * 2
+
+
+def backward_flops(T, Hqk, Hv, n=CHUNK, d=D):
+    """Algorithmic FLOP of the training backward per sequence of T tokens,
+    counted per full chunk and V head (2 per multiply-add; triangular n x n
+    factors at half):
+
+      recomputed forward   K S, Ks^T Vn: 4 n d^2;          T' Vt: n^2 d
+      state-gradient pass  Ks dS', (Gam Q)^T dO', (Gam K)^T dVt: 6 n d^2;
+                           P^T dO', T'^T dVn: 2 n^2 d
+      chunk-local          K K^T, Q K^T: 2 n^2 d;   (I + A)^-1: n^3 / 3
+      per-chunk gradients  Vn dS'^T, dO' S^T, dVt S^T: 6 n d^2;
+                           dO' Vn^T, dVn Vt^T: 2 n^2 d (full); dQK K, dQK^T Q,
+                           K K^T, (dKK + dKK^T) K: 5 n^2 d; X^T dX X^T: 2 n^3 / 3
+    """
+    per = 16 * n * d * d + 12 * n * n * d + n ** 3
+    return per * (T // n) * Hv
 
 
 def decode_bytes(B, Hqk, Hv, d=D):
@@ -115,10 +134,15 @@ class Hip:
         return float(out.value)
 
 
-def source_digest():
+# kernel sources behind each group of measured kernels
+FWD_SOURCES = ("gdn_common.h", "gdn_prefill.h", "gdn_prefill.hip", "gdn_decode.hip")
+BWD_SOURCES = ("gdn_common.h", "gdn_backward.hip")
+
+
+def source_digest(files=FWD_SOURCES):
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "linear_attention_sequence_gdn_amd", "csrc", "*"))):
-        h.update(open(f, "rb").read())
+    for f in sorted(files):
+        h.update(open(os.path.join(ROOT, "linear_attention_sequence_gdn_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -127,6 +151,9 @@ TRAFFIC_KERNELS = {"prefill_chain": "chain_kernel", "prefill_prep": "prep_kernel
                    "prefill_setup": "setup_kernel", "decode": "decode_step_kernel",
                    "decode_conv_shift": "conv_shift_qk_kernel<1>",
                    "decode_multi": "decode_head_kernel<4>", "decode_multi_conv_shift": "conv_shift_qk_kernel<4>"}
+BWD_KERNELS = ("bwd_prep_kernel", "bwd_local_kernel", "bwd_fwd_kernel", "bwd_chain_kernel", "bwd_grad_kernel",
+               "bwd_dy_kernel", "bwd_conv_kernel", "bwd_dw_kernel")
+TRAFFIC_KERNELS.update({"backward_" + k_[4:-7]: k_ for k_ in BWD_KERNELS})
 
 
 def _counter_rows(path, counter):
@@ -146,8 +173,11 @@ def traffic_report(fetch_csv, write_csv):
     fetch = _counter_rows(fetch_csv, "FETCH_SIZE")
     write = _counter_rows(write_csv, "WRITE_SIZE")
 
+    def named(k_, sub):  # the kernel itself, not one whose name contains it
+        return ("::" + sub + "(") in k_ or k_.startswith(sub + "(")
+
     def rows(table, sub):
-        hits = [v_ for k_, v_ in table.items() if sub in k_]
+        hits = [v_ for k_, v_ in table.items() if named(k_, sub)]
         if len(hits) != 1:
             raise SystemExit(f"traffic report: {len(hits)} kernels match {sub!r}")
         return hits[0]
@@ -156,21 +186,27 @@ def traffic_report(fetch_csv, write_csv):
         r = rows(table, sub)
         return sum(v_ for _, v_ in r) / len(r)
 
-    f_copy = max(rows(fetch, "copyBuffer"))[1] * 1024
-    w_copy = max(rows(write, "copyBuffer"))[1] * 1024
+    def copy_rows(table):
+        hits = [v_ for k_, v_ in table.items() if "copyBuffer" in k_]
+        if len(hits) != 1:
+            raise SystemExit(f"traffic report: {len(hits)} copy kernels")
+        return hits[0]
+
+    f_copy = max(copy_rows(fetch))[1] * 1024
+    w_copy = max(copy_rows(write))[1] * 1024
     f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
-    digest = source_digest()
+    digest, bwd_digest = source_digest(), source_digest(BWD_SOURCES)
     out = {"_calibration": {"copy_bytes": COPY_BYTES, "fetch_counter_bytes": f_copy,
                             "write_counter_bytes": w_copy, "fetch_scale": f_scale,
                             "write_scale": w_scale}}
     for name, sub in TRAFFIC_KERNELS.items():
-        if not any(sub in k_ for k_ in fetch):
+        if not any(named(k_, sub) for k_ in fetch):
             print(f"{sub:22s} not launched in this run")
             continue
         rd = mean(fetch, sub) * 1024 * f_scale
         wr = mean(write, sub) * 1024 * w_scale
         out[name] = {"kernel": sub, "read_bytes": rd, "write_bytes": wr, "bytes_per_launch": rd + wr,
-                     "source_digest": digest}
+                     "source_digest": bwd_digest if name.startswith("backward") else digest}
         print(f"{sub:22s} read {rd / 2**20:10.2f} MiB  write {wr / 2**20:10.2f} MiB per launch")
     print(f"copy calibration: FETCH_SIZE x{f_scale:.3f}, WRITE_SIZE x{w_scale:.3f}")
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -356,6 +392,47 @@ def bench_decode_multi(hip, T=4, steps=32):
             "us_per_call": us, "us_per_token_step": us / T, "tokens_per_s": B * T / (us * 1e-6)}
 
 
+def bench_backward(hip, steps=10, warmup=3):
+    """gdn_prefill_backward on the prefill workload (same seeded inputs, a
+    seeded bf16 output gradient and final-state gradient), K calls between
+    two events."""
+    import numpy as np
+    import torch
+    import linear_attention_sequence_gdn_amd as gdn
+    from linear_attention_sequence_gdn_amd import inputs
+
+    c = inputs.CONFIGS[1]
+    B, T, Hqk, Hv = c["B"], c["T"], c["Hqk"], c["Hv"]
+    x = inputs.make_prefill(T_list=[T], Hqk=Hqk, Hv=Hv, seed=1001, gate_scale=c["gate_scale"])
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    rng = np.random.default_rng(2001)
+    g_o = bf(inputs.bf16_bits(rng.standard_normal((B, T, Hv, D), dtype=np.float32)))
+    g_S = f32(rng.standard_normal((B, Hv, D, D), dtype=np.float32))
+    args = (bf(x["q"].reshape(B, T, Hqk, D)), bf(x["k"].reshape(B, T, Hqk, D)), bf(x["v"].reshape(B, T, Hv, D)),
+            f32(x["a"].reshape(B, T, Hv)), f32(x["b"].reshape(B, T, Hv)), bf(x["conv_w"]), g_o)
+    ws = torch.empty(gdn.gdn_prefill_backward_workspace_size(B, T, Hqk, Hv), dtype=torch.uint8, device="cuda")
+    run = lambda: gdn.gdn_prefill_backward(*args, gate_scale=c["gate_scale"], grad_state_out=g_S, workspace=ws)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    t0, t1 = hip.event(), hip.event()
+    hip.record(t0, sp)
+    for _ in range(steps):
+        run()
+    hip.record(t1, sp)
+    torch.cuda.synchronize()
+    ms = hip.ms(t0, t1) / steps
+    flop = backward_flops(T, Hqk, Hv)
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"metric": "training backward tokens/s (B=1, T=8192, 16QK/48V; all gradients, fp32)",
+            "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms, "steps": steps,
+            "roofline": {"bound": "alu", "kernel": "whole backward (eight launches)", "achieved": tf,
+                         "peak": PEAK_VALU_F32 / 1e12, "unit": "TFLOP/s", "frac": tf * 1e12 / PEAK_VALU_F32,
+                         "traffic": None, "algorithmic_flop_per_call": flop}}
+
+
 def cpu_baseline(min_seconds=12.0, max_reps=60):
     import oracle
     from linear_attention_sequence_gdn_amd import inputs
@@ -403,6 +480,9 @@ def main():
     pf = bench_prefill(hip, args.steps, args.warmup)
     dc = bench_decode(hip)
     dm = bench_decode_multi(hip)
+    bw = bench_backward(hip)
+    bw["roofline"]["traffic"] = _sum_or_none(*(load_traffic("backward_" + k_[4:-7], source_digest(BWD_SOURCES))
+                                               for k_ in BWD_KERNELS))
     T, Hqk, Hv = pf["T"], pf["Hqk"], pf["Hv"]
     flop_prep, flop_chain = prefill_flops(T, Hqk, Hv)
     tok_s = T / (pf["ms_per_step"] * 1e-3)
@@ -460,6 +540,7 @@ def main():
                                                         load_traffic("decode_conv_shift", digest)),
                                 "algorithmic_bytes_per_launch": dec_bytes}},
         "decode_multi": dm,
+        "backward": bw,
         "source_digest": digest,
     }
     if args.calibrate_copy:
