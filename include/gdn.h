@@ -234,6 +234,32 @@ int gdn_prefill_backward(const uint16_t *q, const uint16_t *k, const uint16_t *v
                          float gate_scale, float q_scale,
                          void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of device workspace gdn_prefill_backward_varlen needs (an upper bound
+ * over every split of T_tot tokens into N sequences; 0 when T_tot = 0). */
+size_t gdn_prefill_backward_varlen_workspace_size(int N, int T_tot, int Hqk, int Hv, int dk, int dv);
+
+/*
+ * Training backward of gdn_prefill_varlen: the same gradients as
+ * gdn_prefill_backward for N packed sequences of any lengths (chunking
+ * restarts at every sequence start; empty sequences pass their state
+ * gradient through).  cu_seqlens is the forward call's DEVICE int32 [N+1];
+ * q, k, v, grad_q, grad_k, grad_v are [T_tot][H][d]; a, b, grad_a, grad_b
+ * [T_tot][Hv]; grad_o [T_tot][Hv][dv]; states and their gradients
+ * [N][Hv][dk][dv]; conv rows and their gradient [N][3][C_tot].  Bounds
+ * outside [0, T_tot] are clamped.  Other rules as gdn_prefill_backward.
+ */
+int gdn_prefill_backward_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                const float *a, const float *b, const uint16_t *conv_w,
+                                const uint16_t *conv_state_in, const float *state_in,
+                                const uint16_t *grad_o, const float *grad_state_out,
+                                float *grad_q, float *grad_k, float *grad_v,
+                                float *grad_a, float *grad_b, float *grad_conv_w,
+                                float *grad_conv_state_in, float *grad_state_in,
+                                const int32_t *cu_seqlens, int N, int T_tot,
+                                int Hqk, int Hv, int dk, int dv,
+                                float gate_scale, float q_scale,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

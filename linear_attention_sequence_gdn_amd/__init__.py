@@ -74,6 +74,10 @@ def lib():
         L.gdn_prefill_backward_workspace_size.argtypes = [_I] * 6
         L.gdn_prefill_backward.restype = _I
         L.gdn_prefill_backward.argtypes = [_P] * 18 + [_I] * 6 + [_F, _F, _P, _SZ, _P]
+        L.gdn_prefill_backward_varlen_workspace_size.restype = _SZ
+        L.gdn_prefill_backward_varlen_workspace_size.argtypes = [_I] * 6
+        L.gdn_prefill_backward_varlen.restype = _I
+        L.gdn_prefill_backward_varlen.argtypes = [_P] * 19 + [_I] * 6 + [_F, _F, _P, _SZ, _P]
         L.gdn_decode_multi.restype = _I
         L.gdn_decode_multi.argtypes = [_P] * 11 + [_I] * 7 + [_F, _F, _P]
         _lib = L
@@ -220,6 +224,57 @@ def gdn_prefill_backward(q, k, v, a, b, conv_w, grad_o, *, gate_scale, q_scale=1
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     if rc != GDN_OK:
         raise GDNError("gdn_prefill_backward", rc)
+    return {n: t for n, t in g.items() if t is not None}
+
+
+def gdn_prefill_backward_varlen_workspace_size(N, T_tot, Hqk, Hv, dk=128, dv=128) -> int:
+    return int(lib().gdn_prefill_backward_varlen_workspace_size(N, T_tot, Hqk, Hv, dk, dv))
+
+
+def gdn_prefill_backward_varlen(q, k, v, a, b, conv_w, cu_seqlens, grad_o, *, gate_scale, q_scale=1.0,
+                                state_in=None, conv_state_in=None, grad_state_out=None,
+                                want_conv_state=False, want_state=True, workspace=None, stream=None):
+    """Gradients of ``gdn_prefill_varlen`` (packed sequences): q, k:
+    [T_tot][Hqk][128] bf16; v, grad_o: [T_tot][Hv][128] bf16; a, b:
+    [T_tot][Hv] fp32; cu_seqlens: int32 [N+1] on the GPU.  Returns a dict of
+    fp32 gradients as ``gdn_prefill_backward``."""
+    torch = _torch()
+    T_tot, Hqk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    N = cu_seqlens.shape[0] - 1
+    C_tot = 2 * Hqk * dk + Hv * dv
+    bf, f32 = torch.bfloat16, torch.float32
+    _check(q, "q", bf, (T_tot, Hqk, dk))
+    _check(k, "k", bf, (T_tot, Hqk, dk))
+    _check(v, "v", bf, (T_tot, Hv, dv))
+    _check(a, "a", f32, (T_tot, Hv))
+    _check(b, "b", f32, (T_tot, Hv))
+    _check(conv_w, "conv_w", bf, (C_tot, 4))
+    _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
+    _check(state_in, "state_in", f32, (N, Hv, dk, dv))
+    _check(conv_state_in, "conv_state_in", bf, (N, 3, C_tot))
+    _check(grad_o, "grad_o", bf, (T_tot, Hv, dv))
+    _check(grad_state_out, "grad_state_out", f32, (N, Hv, dk, dv))
+    dev = q.device
+    g = {"q": torch.empty((T_tot, Hqk, dk), dtype=f32, device=dev),
+         "k": torch.empty((T_tot, Hqk, dk), dtype=f32, device=dev),
+         "v": torch.empty((T_tot, Hv, dv), dtype=f32, device=dev),
+         "a": torch.empty((T_tot, Hv), dtype=f32, device=dev),
+         "b": torch.empty((T_tot, Hv), dtype=f32, device=dev),
+         "conv_w": torch.empty((C_tot, 4), dtype=f32, device=dev),
+         "conv_state": torch.empty((N, 3, C_tot), dtype=f32, device=dev) if want_conv_state else None,
+         "state": torch.empty((N, Hv, dk, dv), dtype=f32, device=dev) if want_state else None}
+    need = gdn_prefill_backward_varlen_workspace_size(N, T_tot, Hqk, Hv, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rc = lib().gdn_prefill_backward_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(conv_w), _ptr(conv_state_in),
+        _ptr(state_in), _ptr(grad_o), _ptr(grad_state_out), _ptr(g["q"]), _ptr(g["k"]),
+        _ptr(g["v"]), _ptr(g["a"]), _ptr(g["b"]), _ptr(g["conv_w"]), _ptr(g["conv_state"]),
+        _ptr(g["state"]), _ptr(cu_seqlens), N, T_tot, Hqk, Hv, dk, dv, float(gate_scale), float(q_scale),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != GDN_OK:
+        raise GDNError("gdn_prefill_backward_varlen", rc)
     return {n: t for n, t in g.items() if t is not None}
 
 

@@ -15,13 +15,14 @@ hipError_t launch_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v
                          const float *state_in, float *state_out, uint16_t *o, const int32_t *slots,
                          int n_rows, int B, int T, int Hqk, int Hv, float gate_scale, float q_scale,
                          hipStream_t stream);
-size_t backward_workspace_bytes(int B, int T, int Hqk, int Hv);
+size_t backward_workspace_bytes(int N, int T_tot, bool packed, int Hqk, int Hv);
 hipError_t launch_backward(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
                            const float *b, const uint16_t *conv_w, const uint16_t *conv_state_in,
                            const float *state_in, const uint16_t *grad_o, const float *grad_state_out,
                            float *grad_q, float *grad_k, float *grad_v, float *grad_a, float *grad_b,
-                           float *grad_conv_w, float *grad_conv_state_in, float *grad_state_in, int B, int T,
-                           int Hqk, int Hv, float gate_scale, float q_scale, void *workspace, hipStream_t stream);
+                           float *grad_conv_w, float *grad_conv_state_in, float *grad_state_in,
+                           const int32_t *cu_seqlens, int N, int T, int T_tot, int Hqk, int Hv, float gate_scale,
+                           float q_scale, void *workspace, hipStream_t stream);
 }  // namespace gdn
 
 namespace {
@@ -188,7 +189,43 @@ int gdn_prefill_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, 
 size_t gdn_prefill_backward_workspace_size(int B, int T, int Hqk, int Hv, int dk, int dv)
 {
     if (B < 0 || T < 0 || check_dims(Hqk, Hv, dk, dv) != GDN_OK) return 0;
-    return gdn::backward_workspace_bytes(B, T, Hqk, Hv);
+    if ((long)B * T > 0x7fffffffL) return 0;
+    return gdn::backward_workspace_bytes(B, B * T, false, Hqk, Hv);
+}
+
+size_t gdn_prefill_backward_varlen_workspace_size(int N, int T_tot, int Hqk, int Hv, int dk, int dv)
+{
+    if (N < 0 || T_tot < 0 || check_dims(Hqk, Hv, dk, dv) != GDN_OK) return 0;
+    return gdn::backward_workspace_bytes(N, T_tot, true, Hqk, Hv);
+}
+
+static int backward_common(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
+                           const float *b, const uint16_t *conv_w, const uint16_t *conv_state_in,
+                           const float *state_in, const uint16_t *grad_o, const float *grad_state_out,
+                           float *grad_q, float *grad_k, float *grad_v, float *grad_a, float *grad_b,
+                           float *grad_conv_w, float *grad_conv_state_in, float *grad_state_in,
+                           const int32_t *cu_seqlens, int N, int T, int T_tot, int Hqk, int Hv,
+                           float gate_scale, float q_scale, void *workspace, size_t workspace_bytes,
+                           void *stream)
+{
+    if (!conv_w || !grad_conv_w) return GDN_ERR_INVALID_ARGUMENT;
+    if (T_tot > 0 && (!q || !k || !v || !a || !b || !grad_o || !grad_q || !grad_k || !grad_v ||
+                      !grad_a || !grad_b))
+        return GDN_ERR_INVALID_ARGUMENT;
+    const void *al4[] = {q, k, v, a, b, conv_w, conv_state_in, state_in, grad_o, grad_state_out,
+                         grad_q, grad_k, grad_v, grad_a, grad_b, grad_conv_w, grad_conv_state_in,
+                         grad_state_in, cu_seqlens};
+    for (const void *ptr : al4)
+        if (ptr && !aligned(ptr, 4)) return GDN_ERR_INVALID_ARGUMENT;
+    if ((workspace && !aligned(workspace, 16)) || (grad_o && !aligned(grad_o, 8))) return GDN_ERR_INVALID_ARGUMENT;
+    const size_t need = gdn::backward_workspace_bytes(N, T_tot, cu_seqlens != nullptr, Hqk, Hv);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE_TOO_SMALL;
+    if (N == 0) return GDN_OK;
+    hipError_t e = gdn::launch_backward(q, k, v, a, b, conv_w, conv_state_in, state_in, grad_o, grad_state_out,
+                                        grad_q, grad_k, grad_v, grad_a, grad_b, grad_conv_w, grad_conv_state_in,
+                                        grad_state_in, cu_seqlens, N, T, T_tot, Hqk, Hv, gate_scale, q_scale,
+                                        workspace, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
 int gdn_prefill_backward(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
@@ -203,24 +240,28 @@ int gdn_prefill_backward(const uint16_t *q, const uint16_t *k, const uint16_t *v
     int rc = check_dims(Hqk, Hv, dk, dv);
     if (rc != GDN_OK) return rc;
     if ((long)B * T > 0x7fffffffL) return GDN_ERR_UNSUPPORTED;
-    if (!conv_w || !grad_conv_w) return GDN_ERR_INVALID_ARGUMENT;
-    if ((long)B * T > 0 && (!q || !k || !v || !a || !b || !grad_o || !grad_q || !grad_k || !grad_v ||
-                            !grad_a || !grad_b))
-        return GDN_ERR_INVALID_ARGUMENT;
-    const void *al4[] = {q, k, v, a, b, conv_w, conv_state_in, state_in, grad_o, grad_state_out,
-                         grad_q, grad_k, grad_v, grad_a, grad_b, grad_conv_w, grad_conv_state_in,
-                         grad_state_in};
-    for (const void *ptr : al4)
-        if (ptr && !aligned(ptr, 4)) return GDN_ERR_INVALID_ARGUMENT;
-    if ((workspace && !aligned(workspace, 16)) || (grad_o && !aligned(grad_o, 8))) return GDN_ERR_INVALID_ARGUMENT;
-    const size_t need = gdn::backward_workspace_bytes(B, T, Hqk, Hv);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE_TOO_SMALL;
-    if (B == 0) return GDN_OK;
-    hipError_t e = gdn::launch_backward(q, k, v, a, b, conv_w, conv_state_in, state_in, grad_o, grad_state_out,
-                                        grad_q, grad_k, grad_v, grad_a, grad_b, grad_conv_w, grad_conv_state_in,
-                                        grad_state_in, B, T, Hqk, Hv, gate_scale, q_scale, workspace,
-                                        reinterpret_cast<hipStream_t>(stream));
-    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    return backward_common(q, k, v, a, b, conv_w, conv_state_in, state_in, grad_o, grad_state_out, grad_q,
+                           grad_k, grad_v, grad_a, grad_b, grad_conv_w, grad_conv_state_in, grad_state_in,
+                           nullptr, B, T, B * T, Hqk, Hv, gate_scale, q_scale, workspace, workspace_bytes, stream);
+}
+
+int gdn_prefill_backward_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
+                                const float *b, const uint16_t *conv_w, const uint16_t *conv_state_in,
+                                const float *state_in, const uint16_t *grad_o, const float *grad_state_out,
+                                float *grad_q, float *grad_k, float *grad_v, float *grad_a, float *grad_b,
+                                float *grad_conv_w, float *grad_conv_state_in, float *grad_state_in,
+                                const int32_t *cu_seqlens, int N, int T_tot, int Hqk, int Hv, int dk, int dv,
+                                float gate_scale, float q_scale, void *workspace, size_t workspace_bytes,
+                                void *stream)
+{
+    if (N < 0 || T_tot < 0) return GDN_ERR_INVALID_ARGUMENT;
+    int rc = check_dims(Hqk, Hv, dk, dv);
+    if (rc != GDN_OK) return rc;
+    if (!cu_seqlens) return GDN_ERR_INVALID_ARGUMENT;
+    return backward_common(q, k, v, a, b, conv_w, conv_state_in, state_in, grad_o, grad_state_out, grad_q,
+                           grad_k, grad_v, grad_a, grad_b, grad_conv_w, grad_conv_state_in, grad_state_in,
+                           cu_seqlens, N, 0, T_tot, Hqk, Hv, gate_scale, q_scale, workspace, workspace_bytes,
+                           stream);
 }
 
 }  // extern "C"

@@ -1,5 +1,6 @@
 // gdn_backward.hip -- gradients of the chunked GDN prefill (training
-// backward), for B sequences of equal length T, on gfx950.
+// backward), for B sequences of equal length T or packed sequences of any
+// lengths, on gfx950.
 //
 // The forward, per chunk of n <= 64 tokens of one (sequence, V head), with S
 // the state entering the chunk, gamma the in-chunk cumulative log decay (Gam =
@@ -17,6 +18,7 @@
 // dL = -X^T dX X^T.  Everything here is fp32 on the vector ALUs.
 //
 // Passes (one launch each):
+//   bwd_setup_kernel   (packed calls) chunk and sequence tables from cu_seqlens
 //   bwd_prep_kernel    conv + SiLU (+ L2 norm) of q, k, v; gates and gamma
 //   bwd_local_kernel   per (chunk, V head): P and X = (I + A)^-1
 //   bwd_fwd_kernel     per (sequence, V head, 32 state columns), in order:
@@ -62,13 +64,19 @@ struct BwdArgs {
     const uint16_t *grad_o;
     const float *grad_state_out;
     float *grad_q, *grad_k, *grad_v, *grad_a, *grad_b, *grad_conv_w, *grad_conv_state_in, *grad_state_in;
-    int B, T, Hqk, Hv, nc;
+    const int32_t *cu_seqlens;  // packed calls: sequence bounds (device); else NULL
+    int N;                      // sequences
+    int T, nc;                  // uniform calls: tokens and chunks per sequence
+    int T_tot, max_chunks;      // all tokens; chunk slots
+    int Hqk, Hv;
     float gate_scale, q_scale;
 };
 
 // Workspace (fp32).  tok = s*T + t; rows of a chunk beyond its length are
 // never written or read.
 struct BwdWs {
+    int4 *chunk_info;   // [chunk slot] {sequence, its first token, length, index in it} (packed calls)
+    int4 *seq_info;     // [sequence] {first chunk slot, chunks, first token, length} (packed calls)
     float *qh, *kh;     // [tok][Hqk][128]  q^, k^
     float *vh;          // [tok][Hv][128]   v^
     float *gam, *beta;  // [tok][Hv]        gamma (natural log), beta
@@ -82,6 +90,20 @@ struct BwdWs {
 };
 
 __device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// {sequence, its first token, chunk length (0: empty slot), chunk index in the sequence}
+__device__ __forceinline__ int4 bchunk(const BwdArgs &p, const BwdWs &ws, int cidx)
+{
+    if (p.cu_seqlens) return ws.chunk_info[cidx];
+    const int s = cidx / p.nc, j = cidx % p.nc;
+    return make_int4(s, s * p.T, min(kChunk, p.T - j * kChunk), j);
+}
+// {first chunk slot, chunks, first token, length}
+__device__ __forceinline__ int4 bseq(const BwdArgs &p, const BwdWs &ws, int s)
+{
+    if (p.cu_seqlens) return ws.seq_info[s];
+    return make_int4(s * p.nc, p.nc, s * p.T, p.T);
+}
 __device__ __forceinline__ float silu_grad(float y)
 {
     const float s = sigm(y);
@@ -109,7 +131,7 @@ __device__ __forceinline__ const uint16_t *plane_src(const BwdArgs &p, const Pla
 // Conv output y of token t (in-sequence index) of sequence s, channel c of
 // the plane: taps in order, history rows for t - 3 + j < 0.
 __device__ __forceinline__ float conv_y(const BwdArgs &p, const Plane &P, const uint16_t *x, const float (&w)[4],
-                                        int s, int t, int c, long C_tot)
+                                        int s, long seq0, int t, int c, long C_tot)
 {
     float y = 0.f;
 #pragma unroll
@@ -117,7 +139,7 @@ __device__ __forceinline__ float conv_y(const BwdArgs &p, const Plane &P, const 
         const int tau = t - 3 + j;
         float xv = 0.f;
         if (tau >= 0)
-            xv = bf16_to_f32(x[((long)s * p.T + tau) * P.ld + c]);
+            xv = bf16_to_f32(x[(seq0 + tau) * P.ld + c]);
         else if (p.conv_state_in)
             xv = bf16_to_f32(p.conv_state_in[((long)s * 3 + 3 + tau) * C_tot + P.ch0 + c]);
         y = fmaf(w[j], xv, y);
@@ -132,9 +154,10 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs p, BwdWs ws)
 {
     __shared__ float zs[64 * kLK];
     __shared__ float nrm[64];
-    const int cidx = blockIdx.x, s = cidx / p.nc, j = cidx % p.nc;
-    const int n = min(kChunk, p.T - j * kChunk);
-    const long t0 = (long)s * p.T + (long)j * kChunk;
+    const int4 ci = bchunk(p, ws, blockIdx.x);
+    const int s = ci.x, n = ci.z, j = ci.w;
+    if (n == 0) return;  // empty chunk slot
+    const long seq0 = ci.y, t0 = seq0 + (long)j * kChunk;
     const long C_tot = 2L * p.Hqk * kD + (long)p.Hv * kD;
     const Plane P = plane_of(p, blockIdx.y);
     const uint16_t *x = plane_src(p, P);
@@ -143,7 +166,7 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs p, BwdWs ws)
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = bf16_to_f32(p.conv_w[(P.ch0 + c) * 4 + i]);
     for (int r = rh; r < n; r += 2) {
-        const float y = conv_y(p, P, x, w, s, j * kChunk + r, c, C_tot);
+        const float y = conv_y(p, P, x, w, s, seq0, j * kChunk + r, c, C_tot);
         const float z = y * sigm(y);
         if (P.kind == 2)
             ws.vh[((t0 + r) * p.Hv + P.head) * kD + c] = z;
@@ -214,9 +237,10 @@ __global__ __launch_bounds__(kBT) void bwd_local_kernel(BwdArgs p, BwdWs ws)
     __shared__ float gam[64], bet[64];
     const int Hv = p.Hv, G = Hv / p.Hqk;
     const int cidx = blockIdx.x / Hv, h = blockIdx.x % Hv, g = h / G;
-    const int s = cidx / p.nc, j = cidx % p.nc;
-    const int n = min(kChunk, p.T - j * kChunk);
-    const long t0 = (long)s * p.T + (long)j * kChunk;
+    const int4 ci = bchunk(p, ws, cidx);
+    const int n = ci.z;
+    if (n == 0) return;
+    const long t0 = (long)ci.y + (long)ci.w * kChunk;
     const int t = threadIdx.x;
     for (int e = 0; e < 32; ++e) {
         const int idx = t + kBT * e, r = idx >> 7, d = idx & 127;
@@ -290,11 +314,11 @@ struct SeqPref {
     long t0;
 };
 template <bool kChain>
-__device__ __forceinline__ void seq_fetch(const BwdArgs &p, const BwdWs &ws, SeqPref<kChain> &f, int s, int j, int h,
-                                          int g, int col0)
+__device__ __forceinline__ void seq_fetch(const BwdArgs &p, const BwdWs &ws, SeqPref<kChain> &f, int cidx, long t0,
+                                          int n, int h, int g, int col0)
 {
-    const int t = threadIdx.x, Hv = p.Hv, n = min(kChunk, p.T - j * kChunk);
-    const long t0 = (long)s * p.T + (long)j * kChunk, mo = ((long)(s * p.nc + j) * Hv + h) * 64 * 64;
+    const int t = threadIdx.x, Hv = p.Hv;
+    const long mo = ((long)cidx * Hv + h) * 64 * 64;
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
     f.n = n;
     f.t0 = t0;
@@ -380,12 +404,16 @@ __global__ __launch_bounds__(kST) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
 #pragma unroll
     for (int e = 0; e < kSE; ++e)
         S[e] = p.state_in ? p.state_in[(((long)s * Hv + h) * kD + i) * kD + col0 + c0 + e] : 0.f;
+    const int4 sq = bseq(p, ws, s);  // {first chunk slot, chunks, first token, length}
+    const int nch = sq.y;
     SeqPref<false> f;
-    seq_fetch<false>(p, ws, f, s, 0, h, g, col0);
-    seq_commit<false>(p, f, L, nullptr, nullptr, Vs);
-    for (int j = 0; j < p.nc; ++j) {
-        const int cidx = s * p.nc + j, n = min(kChunk, p.T - j * kChunk);
-        const long t0 = (long)s * p.T + (long)j * kChunk;
+    if (nch > 0) {
+        seq_fetch<false>(p, ws, f, sq.x, sq.z, min(kChunk, sq.w), h, g, col0);
+        seq_commit<false>(p, f, L, nullptr, nullptr, Vs);
+    }
+    for (int j = 0; j < nch; ++j) {
+        const int cidx = sq.x + j, n = min(kChunk, sq.w - j * kChunk);
+        const long t0 = (long)sq.z + (long)j * kChunk;
         float *sc = ws.Sc + ((((long)cidx * Hv + h) * kD + i) * kD + col0 + c0);
 #pragma unroll
         for (int e = 0; e < kSE; e += 4) {
@@ -393,7 +421,7 @@ __global__ __launch_bounds__(kST) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
             st4(sc + e, v);
             st4(Ss + i * kLC + c0 + e, v);
         }
-        if (j + 1 < p.nc) seq_fetch<false>(p, ws, f, s, j + 1, h, g, col0);
+        if (j + 1 < nch) seq_fetch<false>(p, ws, f, cidx + 1, t0 + kChunk, min(kChunk, sq.w - (j + 1) * kChunk), h, g, col0);
         __syncthreads();
         // Vt = V - diag(Gam) K S
         float acc[kVE];
@@ -436,7 +464,7 @@ __global__ __launch_bounds__(kST) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
             for (int e = 0; e < kSE; ++e) S[e] = fmaf(kr, Vns[rr * kLC + c0 + e], S[e]);
         }
         __syncthreads();
-        if (j + 1 < p.nc) seq_commit<false>(p, f, L, nullptr, nullptr, Vs);
+        if (j + 1 < nch) seq_commit<false>(p, f, L, nullptr, nullptr, Vs);
     }
 }
 
@@ -457,14 +485,17 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
     float dS[kSE];
 #pragma unroll
     for (int e = 0; e < kSE; ++e) dS[e] = p.grad_state_out ? p.grad_state_out[so + e] : 0.f;
+    const int4 sq = bseq(p, ws, s);  // {first chunk slot, chunks, first token, length}
+    const int nch = sq.y;
     SeqPref<true> f;
-    if (p.nc > 0) {
-        seq_fetch<true>(p, ws, f, s, p.nc - 1, h, g, col0);
+    if (nch > 0) {
+        seq_fetch<true>(p, ws, f, sq.x + nch - 1, sq.z + (long)(nch - 1) * kChunk, sq.w - (nch - 1) * kChunk, h, g,
+                        col0);
         seq_commit<true>(p, f, L, Qs, Ps, dOs);
     }
-    for (int j = p.nc - 1; j >= 0; --j) {
-        const int cidx = s * p.nc + j, n = min(kChunk, p.T - j * kChunk);
-        const long t0 = (long)s * p.T + (long)j * kChunk;
+    for (int j = nch - 1; j >= 0; --j) {
+        const int cidx = sq.x + j, n = min(kChunk, sq.w - j * kChunk);
+        const long t0 = (long)sq.z + (long)j * kChunk;
         float *dsc = ws.dSc + ((((long)cidx * Hv + h) * kD + i) * kD + col0 + c0);
 #pragma unroll
         for (int e = 0; e < kSE; e += 4) {
@@ -472,7 +503,7 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
             st4(dsc + e, v);
             st4(dSs + i * kLC + c0 + e, v);
         }
-        if (j > 0) seq_fetch<true>(p, ws, f, s, j - 1, h, g, col0);
+        if (j > 0) seq_fetch<true>(p, ws, f, cidx - 1, t0 - kChunk, kChunk, h, g, col0);
         __syncthreads();
         // dVn = Ks dS' + P^T dO'
         float acc[kVE];
@@ -600,9 +631,10 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __shared__ float gam[64], bet[64], eg[64], en[64], dgam[64], dbet[64], rowv[64], red[4];
     const int Hv = p.Hv, Hqk = p.Hqk, G = Hv / Hqk;
     const int cidx = blockIdx.x / Hv, h = blockIdx.x % Hv, g = h / G;
-    const int s = cidx / p.nc, j = cidx % p.nc;
-    const int n = min(kChunk, p.T - j * kChunk);
-    const long t0 = (long)s * p.T + (long)j * kChunk;
+    const int4 ci = bchunk(p, ws, cidx);
+    const int n = ci.z;
+    if (n == 0) return;
+    const long t0 = (long)ci.y + (long)ci.w * kChunk;
     const int t = threadIdx.x, r0 = 4 * (t >> 4), cc = t & 15;
     const long mo = ((long)cidx * Hv + h) * 64 * 64;
     const float *Sc = ws.Sc + ((long)cidx * Hv + h) * kD * kD;
@@ -835,9 +867,10 @@ __global__ __launch_bounds__(kBT) void bwd_dy_kernel(BwdArgs p, BwdWs ws)
 {
     __shared__ float zs[64 * kLK], ds[64 * kLK];
     __shared__ float nrm[64], zd[64];
-    const int cidx = blockIdx.x, s = cidx / p.nc, j = cidx % p.nc;
-    const int n = min(kChunk, p.T - j * kChunk);
-    const long t0 = (long)s * p.T + (long)j * kChunk;
+    const int4 ci = bchunk(p, ws, blockIdx.x);
+    const int s = ci.x, n = ci.z, j = ci.w;
+    if (n == 0) return;
+    const long seq0 = ci.y, t0 = seq0 + (long)j * kChunk;
     const long C_tot = 2L * p.Hqk * kD + (long)p.Hv * kD;
     const int G = p.Hv / p.Hqk;
     const Plane P = plane_of(p, blockIdx.y);
@@ -848,7 +881,7 @@ __global__ __launch_bounds__(kBT) void bwd_dy_kernel(BwdArgs p, BwdWs ws)
     for (int i = 0; i < 4; ++i) w[i] = bf16_to_f32(p.conv_w[(P.ch0 + c) * 4 + i]);
     if (P.kind == 2) {
         for (int r = rh; r < n; r += 2) {
-            const float y = conv_y(p, P, x, w, s, j * kChunk + r, c, C_tot);
+            const float y = conv_y(p, P, x, w, s, seq0, j * kChunk + r, c, C_tot);
             ws.dy[(t0 + r) * C_tot + P.ch0 + c] = ws.dvh[((t0 + r) * p.Hv + P.head) * kD + c] * silu_grad(y);
         }
         return;
@@ -860,7 +893,7 @@ __global__ __launch_bounds__(kBT) void bwd_dy_kernel(BwdArgs p, BwdWs ws)
         const int r = rh + 2 * ii;
         yv[ii] = 0.f;
         if (r >= n) continue;
-        const float y = conv_y(p, P, x, w, s, j * kChunk + r, c, C_tot);
+        const float y = conv_y(p, P, x, w, s, seq0, j * kChunk + r, c, C_tot);
         yv[ii] = y;
         zs[r * kLK + c] = y * sigm(y);
         float d = 0.f;
@@ -903,11 +936,18 @@ __global__ __launch_bounds__(kBT) void bwd_dy_kernel(BwdArgs p, BwdWs ws)
 __global__ __launch_bounds__(kBT) void bwd_conv_kernel(BwdArgs p, BwdWs ws)
 {
     __shared__ float wpart[2][kD][4];
-    const int cidx = blockIdx.x, s = cidx / p.nc, j = cidx % p.nc;
-    const int n = min(kChunk, p.T - j * kChunk);
-    const long t0 = (long)s * p.T + (long)j * kChunk;
+    const int cidx = blockIdx.x;
+    const int4 ci = bchunk(p, ws, cidx);
+    const int s = ci.x, n = ci.z, j = ci.w;
     const long C_tot = 2L * p.Hqk * kD + (long)p.Hv * kD;
     const Plane P = plane_of(p, blockIdx.y);
+    if (n == 0) {  // an empty chunk slot contributes nothing to the weight gradient
+        if (threadIdx.x < kD)
+            for (int jj = 0; jj < 4; ++jj) ws.dwp[((long)cidx * C_tot + P.ch0 + threadIdx.x) * 4 + jj] = 0.f;
+        return;
+    }
+    const long seq0 = ci.y, t0 = seq0 + (long)j * kChunk;
+    const int L = bseq(p, ws, s).w;  // sequence length
     const uint16_t *x = plane_src(p, P);
     float *gx = (P.kind == 0 ? p.grad_q : P.kind == 1 ? p.grad_k : p.grad_v) + (long)P.head * kD;
     const int t = threadIdx.x, c = t & 127, rh = t >> 7;
@@ -915,7 +955,7 @@ __global__ __launch_bounds__(kBT) void bwd_conv_kernel(BwdArgs p, BwdWs ws)
     float w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = bf16_to_f32(p.conv_w[ch * 4 + i]);
-    const float *dy = ws.dy + (long)s * p.T * C_tot + ch;  // dy of token tau of this sequence: dy[tau * C_tot]
+    const float *dy = ws.dy + seq0 * C_tot + ch;  // dy of token tau of this sequence: dy[tau * C_tot]
     float gw[4] = {0.f, 0.f, 0.f, 0.f};
     for (int r = rh; r < n; r += 2) {
         const int tau = j * kChunk + r;
@@ -924,7 +964,7 @@ __global__ __launch_bounds__(kBT) void bwd_conv_kernel(BwdArgs p, BwdWs ws)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             const int ty = tau + 3 - jj;
-            if (ty < p.T) gxv = fmaf(w[jj], dy[(long)ty * C_tot], gxv);
+            if (ty < L) gxv = fmaf(w[jj], dy[(long)ty * C_tot], gxv);
         }
         gx[(t0 + r) * P.ld + c] = gxv;
         // y[tau] reads x[tau - 3 + jj] through tap jj
@@ -934,7 +974,7 @@ __global__ __launch_bounds__(kBT) void bwd_conv_kernel(BwdArgs p, BwdWs ws)
             const int tx = tau - 3 + jj;
             float xv = 0.f;
             if (tx >= 0)
-                xv = bf16_to_f32(x[((long)s * p.T + tx) * P.ld + c]);
+                xv = bf16_to_f32(x[(seq0 + tx) * P.ld + c]);
             else if (p.conv_state_in)
                 xv = bf16_to_f32(p.conv_state_in[((long)s * 3 + 3 + tx) * C_tot + ch]);
             gw[jj] = fmaf(d, xv, gw[jj]);
@@ -954,7 +994,7 @@ __global__ __launch_bounds__(kBT) void bwd_conv_kernel(BwdArgs p, BwdWs ws)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int ty = rr - jj;  // token whose tap jj reads row rr (= x[rr - 3])
-                    if (ty >= 0 && ty < p.T) gv = fmaf(w[jj], dy[(long)ty * C_tot], gv);
+                    if (ty >= 0 && ty < L) gv = fmaf(w[jj], dy[(long)ty * C_tot], gv);
                 }
                 p.grad_conv_state_in[((long)s * 3 + rr) * C_tot + ch] = gv;
             }
@@ -980,22 +1020,62 @@ __global__ __launch_bounds__(kBT) void bwd_fill_kernel(float *dst, long n)
     if (e < n) dst[e] = 0.f;
 }
 
+// Packed calls: chunk and sequence tables from cu_seqlens, one workgroup.
+// Sequence bounds are clamped into [0, T_tot] and chunk slots to max_chunks,
+// so that a malformed cu_seqlens cannot send any kernel outside the buffers.
+__global__ __launch_bounds__(1024) void bwd_setup_kernel(BwdArgs p, BwdWs ws)
+{
+    __shared__ int scan[1024];
+    __shared__ int base_chunk;
+    const int t = threadIdx.x;
+    if (t == 0) base_chunk = 0;
+    __syncthreads();
+    for (int s0 = 0; s0 < p.N; s0 += 1024) {
+        const int s = s0 + t;
+        int start = 0, len = 0;
+        if (s < p.N) {
+            start = min(max(p.cu_seqlens[s], 0), p.T_tot);
+            len = max(min(max(p.cu_seqlens[s + 1], 0), p.T_tot) - start, 0);
+        }
+        const int nch = (len + kChunk - 1) / kChunk;
+        scan[t] = nch;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {
+            const int v = t >= off ? scan[t - off] : 0;
+            __syncthreads();
+            scan[t] += v;
+            __syncthreads();
+        }
+        if (s < p.N) {
+            const int first = min(base_chunk + scan[t] - nch, p.max_chunks);
+            const int cnt = min(nch, p.max_chunks - first);
+            ws.seq_info[s] = make_int4(first, cnt, start, min(len, cnt * kChunk));
+            for (int j = 0; j < cnt; ++j) ws.chunk_info[first + j] = make_int4(s, start, min(kChunk, len - j * kChunk), j);
+        }
+        __syncthreads();
+        if (t == 0) base_chunk += scan[1023];
+        __syncthreads();
+    }
+    for (int c = min(base_chunk, p.max_chunks) + t; c < p.max_chunks; c += 1024) ws.chunk_info[c] = make_int4(0, 0, 0, 0);
+}
+
 // Workspace carve-up: sizes in floats, each region 64-byte aligned
 struct BwdLayout {
-    long off[18];
+    long off[20];
     long total;
 };
-BwdLayout bwd_layout(int B, int T, int Hqk, int Hv)
+BwdLayout bwd_layout(int N, int T_tot, int max_chunks, int Hqk, int Hv)
 {
-    const long tok = (long)B * T, nc = (T + kChunk - 1) / kChunk, chunks = (long)B * nc;
+    const long tok = T_tot, chunks = max_chunks;
     const long C_tot = 2L * Hqk * kD + (long)Hv * kD;
-    const long sizes[18] = {tok * Hqk * kD, tok * Hqk * kD, tok * Hv * kD, tok * Hv, tok * Hv,
+    const long sizes[20] = {chunks * 4, (long)N * 4,  // int4 tables
+                            tok * Hqk * kD, tok * Hqk * kD, tok * Hv * kD, tok * Hv, tok * Hv,
                             chunks * Hv * 4096, chunks * Hv * 4096, chunks * Hv * kD * kD, chunks * Hv * kD * kD,
                             tok * Hv * kD, tok * Hv * kD, tok * Hv * kD, tok * Hv * kD, tok * Hv * kD,
                             tok * Hv * kD, tok * C_tot, chunks * C_tot * 4, 0};
     BwdLayout L{};
     long o = 0;
-    for (int i = 0; i < 18; ++i) {
+    for (int i = 0; i < 20; ++i) {
         L.off[i] = o;
         o += (sizes[i] + 15) / 16 * 16;
     }
@@ -1003,59 +1083,77 @@ BwdLayout bwd_layout(int B, int T, int Hqk, int Hv)
     return L;
 }
 
-}  // namespace
-
-size_t backward_workspace_bytes(int B, int T, int Hqk, int Hv)
+int bwd_max_chunks(const int32_t *cu_seqlens, int N, int T_tot)
 {
-    if (B == 0 || T == 0) return 0;
-    return (size_t)bwd_layout(B, T, Hqk, Hv).total * sizeof(float);
+    // uniform: N sequences of T_tot / N tokens; packed: sum of ceil(L_i / 64) <= T_tot / 64 + N
+    if (cu_seqlens) return T_tot / kChunk + N;
+    return N == 0 ? 0 : N * ((T_tot / N + kChunk - 1) / kChunk);
 }
 
+}  // namespace
+
+size_t backward_workspace_bytes(int N, int T_tot, bool packed, int Hqk, int Hv)
+{
+    if (N == 0 || T_tot == 0) return 0;
+    const int mc = packed ? T_tot / kChunk + N : bwd_max_chunks(nullptr, N, T_tot);
+    return (size_t)bwd_layout(N, T_tot, mc, Hqk, Hv).total * sizeof(float);
+}
+
+// Uniform calls: cu_seqlens NULL, N sequences of T tokens (T_tot = N T).
+// Packed calls: cu_seqlens (device) with N + 1 bounds over T_tot tokens.
 hipError_t launch_backward(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
                            const float *b, const uint16_t *conv_w, const uint16_t *conv_state_in,
                            const float *state_in, const uint16_t *grad_o, const float *grad_state_out,
                            float *grad_q, float *grad_k, float *grad_v, float *grad_a, float *grad_b,
-                           float *grad_conv_w, float *grad_conv_state_in, float *grad_state_in, int B, int T,
-                           int Hqk, int Hv, float gate_scale, float q_scale, void *workspace, hipStream_t stream)
+                           float *grad_conv_w, float *grad_conv_state_in, float *grad_state_in,
+                           const int32_t *cu_seqlens, int N, int T, int T_tot, int Hqk, int Hv, float gate_scale,
+                           float q_scale, void *workspace, hipStream_t stream)
 {
     BwdArgs p{};
     p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.conv_w = conv_w; p.conv_state_in = conv_state_in;
     p.state_in = state_in; p.grad_o = grad_o; p.grad_state_out = grad_state_out;
     p.grad_q = grad_q; p.grad_k = grad_k; p.grad_v = grad_v; p.grad_a = grad_a; p.grad_b = grad_b;
     p.grad_conv_w = grad_conv_w; p.grad_conv_state_in = grad_conv_state_in; p.grad_state_in = grad_state_in;
-    p.B = B; p.T = T; p.Hqk = Hqk; p.Hv = Hv; p.nc = (T + kChunk - 1) / kChunk;
-    p.gate_scale = gate_scale; p.q_scale = q_scale;
+    p.cu_seqlens = cu_seqlens; p.N = N; p.T = T; p.nc = (T + kChunk - 1) / kChunk;
+    p.T_tot = T_tot; p.max_chunks = T_tot > 0 ? bwd_max_chunks(cu_seqlens, N, T_tot) : 0;
+    p.Hqk = Hqk; p.Hv = Hv; p.gate_scale = gate_scale; p.q_scale = q_scale;
     const long C_tot = 2L * Hqk * kD + (long)Hv * kD;
     BwdWs ws{};
-    if (T > 0) {
-        const BwdLayout L = bwd_layout(B, T, Hqk, Hv);
+    if (T_tot > 0) {
+        const BwdLayout L = bwd_layout(N, T_tot, p.max_chunks, Hqk, Hv);
         float *base = static_cast<float *>(workspace);
-        float **slots[17] = {&ws.qh, &ws.kh, &ws.vh, &ws.gam, &ws.beta, &ws.X, &ws.P, &ws.Sc, &ws.dSc,
-                             &ws.vt, &ws.vn, &ws.dvn, &ws.dvh, &ws.dqp, &ws.dkp, &ws.dy, &ws.dwp};
-        for (int i = 0; i < 17; ++i) *slots[i] = base + L.off[i];
+        ws.chunk_info = reinterpret_cast<int4 *>(base + L.off[0]);
+        ws.seq_info = reinterpret_cast<int4 *>(base + L.off[1]);
+        float **slots[18] = {&ws.qh, &ws.kh, &ws.vh, &ws.gam, &ws.beta, &ws.X, &ws.P, &ws.Sc, &ws.dSc,
+                             &ws.vt, &ws.vn, &ws.dvn, &ws.dvh, &ws.dqp, &ws.dkp, &ws.dy, &ws.dwp, nullptr};
+        for (int i = 0; i < 17; ++i) *slots[i] = base + L.off[i + 2];
+    } else {
+        p.cu_seqlens = nullptr;  // nothing to tabulate: every sequence is empty
+        p.T = 0;
+        p.nc = 0;
     }
-    const int chunks = B * p.nc, planes = 2 * Hqk + Hv;
+    const int chunks = p.max_chunks, planes = 2 * Hqk + Hv;
     if (chunks > 0) {
+        if (p.cu_seqlens) hipLaunchKernelGGL(bwd_setup_kernel, dim3(1), dim3(1024), 0, stream, p, ws);
         hipLaunchKernelGGL(bwd_prep_kernel, dim3(chunks, planes), dim3(kBT), 0, stream, p, ws);
         hipLaunchKernelGGL(bwd_local_kernel, dim3(chunks * Hv), dim3(kBT), 0, stream, p, ws);
-        hipLaunchKernelGGL(bwd_fwd_kernel, dim3(B * Hv * kNCB), dim3(kST), 0, stream, p, ws);
+        hipLaunchKernelGGL(bwd_fwd_kernel, dim3(N * Hv * kNCB), dim3(kST), 0, stream, p, ws);
     }
-    // also with T = 0: the state gradient passes straight through
-    hipLaunchKernelGGL(bwd_chain_kernel, dim3(B * Hv * kNCB), dim3(kST), 0, stream, p, ws);
+    // also with no tokens: the state gradient passes straight through
+    hipLaunchKernelGGL(bwd_chain_kernel, dim3(N * Hv * kNCB), dim3(kST), 0, stream, p, ws);
+    if (grad_conv_state_in && (chunks == 0 || p.cu_seqlens)) {
+        // rows of sequences without a first chunk (empty ones) stay zero
+        const long nh = (long)N * 3 * C_tot;
+        hipLaunchKernelGGL(bwd_fill_kernel, dim3((nh + kBT - 1) / kBT), dim3(kBT), 0, stream, grad_conv_state_in, nh);
+    }
+    const long nw = C_tot * 4;
     if (chunks > 0) {
         hipLaunchKernelGGL(bwd_grad_kernel, dim3(chunks * Hv), dim3(kBT), 0, stream, p, ws);
         hipLaunchKernelGGL(bwd_dy_kernel, dim3(chunks, planes), dim3(kBT), 0, stream, p, ws);
         hipLaunchKernelGGL(bwd_conv_kernel, dim3(chunks, planes), dim3(kBT), 0, stream, p, ws);
-        const long nw = C_tot * 4;
         hipLaunchKernelGGL(bwd_dw_kernel, dim3((nw + kBT - 1) / kBT), dim3(kBT), 0, stream, p, ws, nw, chunks);
     } else {
-        const long nw = C_tot * 4;
         hipLaunchKernelGGL(bwd_fill_kernel, dim3((nw + kBT - 1) / kBT), dim3(kBT), 0, stream, grad_conv_w, nw);
-        if (grad_conv_state_in) {
-            const long nh = (long)B * 3 * C_tot;
-            hipLaunchKernelGGL(bwd_fill_kernel, dim3((nh + kBT - 1) / kBT), dim3(kBT), 0, stream,
-                               grad_conv_state_in, nh);
-        }
     }
     return hipGetLastError();
 }

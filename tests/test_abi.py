@@ -169,3 +169,19 @@ def test_backward_validation(L):
     assert call_backward(L, ws_bytes=need - 1) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL
     assert call_backward(L, ws=0) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL
     assert call_backward(L, B=0, ws=0, ws_bytes=0) == gdn.GDN_OK
+
+
+def test_backward_varlen_validation(L):
+    def call(cu=FAKE, N=3, T_tot=200, Hv=6, ws_bytes=None):
+        if ws_bytes is None:
+            ws_bytes = gdn.gdn_prefill_backward_varlen_workspace_size(N, T_tot, 2, Hv)
+        return L.gdn_prefill_backward_varlen(_p(), _p(), _p(), _p(), _p(), _p(), None, None, _p(), None,
+                                             _p(), _p(), _p(), _p(), _p(), _p(), None, None, _p(cu),
+                                             N, T_tot, 2, Hv, 128, 128, 0.1, 1.0, _p(), ws_bytes, None)
+    # the packed bound covers any split: at least the uniform size
+    assert gdn.gdn_prefill_backward_varlen_workspace_size(4, 256, 2, 6) >= gdn.gdn_prefill_backward_workspace_size(4, 64, 2, 6)
+    assert call(cu=0) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(N=-1) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(Hv=9) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(ws_bytes=10) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL
+    assert call(cu=FAKE + 2) == gdn.GDN_ERR_INVALID_ARGUMENT

@@ -147,3 +147,56 @@ def test_backward_full_size_sampled_groups(oracle_lib):
               "a": got["a"][:, :, hv], "b": got["b"][:, :, hv], "conv_w": got["conv_w"][chans],
               "conv_state": got["conv_state"][:, :, chans], "state": got["state"][:, hv]}
         _compare(gs, ref, B, T, f"full size, group {grp}")
+
+
+def _gpu_varlen(inp, g_o, g_S, q_scale):
+    import linear_attention_sequence_gdn_amd as gdn
+    import torch
+    from gdn_testutil import dev_i32
+    g = gdn.gdn_prefill_backward_varlen(
+        dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"]), dev_f32(inp["a"]), dev_f32(inp["b"]),
+        dev_bf16(inp["conv_w"]), dev_i32(inp["cu_seqlens"]), dev_bf16(g_o), gate_scale=inp["gate_scale"],
+        q_scale=q_scale, state_in=None if inp["state_in"] is None else dev_f32(inp["state_in"]),
+        conv_state_in=None if inp["conv_state_in"] is None else dev_bf16(inp["conv_state_in"]),
+        grad_state_out=None if g_S is None else dev_f32(g_S), want_conv_state=True)
+    torch.cuda.synchronize()
+    return {n: t.cpu().numpy().astype(np.float64) for n, t in g.items()}
+
+
+def _varlen_case(lens, Hqk, Hv, seed, q_scale=1.0):
+    inp = inputs.make_prefill(T_list=lens, Hqk=Hqk, Hv=Hv, seed=seed, state_std=0.05, conv_state_std=1.0)
+    rng = np.random.default_rng(seed + 77)
+    g_o = inputs.bf16_bits(rng.standard_normal((inp["T_tot"], Hv, inp["d"]), dtype=np.float32))
+    g_S = rng.standard_normal((len(lens), Hv, inp["d"], inp["d"])).astype(np.float32)
+    return inp, g_o, g_S, q_scale
+
+
+def test_backward_varlen_against_oracle(oracle_lib):
+    # packed sequences with empty, one-token, ragged and whole-chunk lengths
+    lens = [5, 0, 130, 64, 1, 200, 65, 0]
+    inp, g_o, g_S, qs = _varlen_case(lens, 2, 6, seed=61, q_scale=0.9)
+    got = _gpu_varlen(inp, g_o, g_S, qs)
+    ref = _oracle(oracle_lib, inp, g_o, g_S, qs)
+    _compare(got, ref, 1, inp["T_tot"], "varlen")
+    # empty sequences: the state gradient passes through, the conv rows get none
+    for s in (1, 7):
+        assert np.array_equal(got["state"][s], g_S[s].astype(np.float64))
+        assert not np.any(got["conv_state"][s])
+
+
+def test_backward_varlen_equals_uniform():
+    # equal lengths through the packed tables give the uniform call's gradients bit for bit
+    B, T = 3, 100
+    inp, g_o, g_S, qs = _case(B, T, 2, 4, seed=71)
+    uni = _gpu(inp, g_o, g_S, qs, B, T)
+    var = _gpu_varlen(inp, g_o, g_S, qs)
+    for n in uni:
+        assert np.array_equal(uni[n].reshape(var[n].shape), var[n]), n
+
+
+def test_backward_varlen_long_mixed(oracle_lib):
+    # log-uniform lengths, a few thousand tokens in all
+    lens = [int(x) for x in inputs.varlen_lengths(81, 6, 20, 1500)]
+    inp, g_o, g_S, qs = _varlen_case(lens, 1, 3, seed=81)
+    _compare(_gpu_varlen(inp, g_o, g_S, qs), _oracle(oracle_lib, inp, g_o, g_S, qs), 1, inp["T_tot"],
+             f"varlen {lens}")
