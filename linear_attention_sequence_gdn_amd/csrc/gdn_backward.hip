@@ -51,10 +51,7 @@ constexpr int kLK = 132;  // LDS row stride of 64 x 128 fp32 tiles (16-byte rows
 constexpr int kLN = 68;   // LDS row stride of 64 x 64 fp32 tiles
 constexpr int kLC = kCB;  // LDS row stride of kCB-column slices (read as broadcasts)
 constexpr int kNCB = kD / kCB;
-constexpr int kST = 512;             // threads of a sequential-pass workgroup (two waves per SIMD)
-constexpr int kSE = kD * kCB / kST;  // state elements per thread (row t / kSP, kSE columns)
-constexpr int kVE = 64 * kCB / kST;  // slice elements per thread (row t / kVP, kVE columns)
-constexpr int kSP = kCB / kSE, kVP = kCB / kVE;
+constexpr int kST = 512;  // threads of a sequential-pass workgroup: eight waves, two per SIMD
 
 struct BwdArgs {
     const uint16_t *q, *k, *v;
@@ -391,6 +388,16 @@ __device__ __forceinline__ void seq_commit(const BwdArgs &p, const SeqPref<kChai
 // ---------------------------------------------------------------------------
 // 3. forward again, keeping the state entering every chunk, Vt and Vn
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// The sequential passes multiply on the fp32 matrix cores in 16 x 16 tiles:
+// lane l supplies A[16 tile + l%16][k] and B[k][16 tile + l%16] for
+// k = 4 kb + l/16, and holds rows 4 (l/16) .. +3 of column l%16 of its tile.
+// The state (or its gradient), 128 x 32: wave w holds row tile w in both
+// column tiles.  A 64 x 32 slice: wave w holds tile (w / 2, w % 2).
 __global__ __launch_bounds__(kST) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
 {
     __shared__ SeqTile L;
@@ -398,12 +405,16 @@ __global__ __launch_bounds__(kST) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
     const int Hv = p.Hv, G = Hv / p.Hqk;
     const int cb = blockIdx.x % kNCB, sh = blockIdx.x / kNCB, h = sh % Hv, s = sh / Hv, g = h / G;
     const int col0 = cb * kCB;
-    const int t = threadIdx.x, i = t / kSP, c0 = (t % kSP) * kSE;  // state: row i, columns c0..c0+kSE-1
-    const int r = t / kVP, cq = (t % kVP) * kVE;                     // slices: row r, columns cq..cq+kVE-1
-    float S[kSE];
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63, lr = lane & 15, lq = lane >> 4;
+    const int srow = 16 * w + 4 * lq;                      // state rows srow .. srow + 3
+    const int vrt = w >> 1, vrow = 16 * vrt + 4 * lq, vcol = 16 * (w & 1) + lr;  // slice tile
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 S[2];
 #pragma unroll
-    for (int e = 0; e < kSE; ++e)
-        S[e] = p.state_in ? p.state_in[(((long)s * Hv + h) * kD + i) * kD + col0 + c0 + e] : 0.f;
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            S[ct][e] = p.state_in ? p.state_in[(((long)s * Hv + h) * kD + srow + e) * kD + col0 + 16 * ct + lr] : 0.f;
     const int4 sq = bseq(p, ws, s);  // {first chunk slot, chunks, first token, length}
     const int nch = sq.y;
     SeqPref<false> f;
@@ -414,54 +425,55 @@ __global__ __launch_bounds__(kST) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
     for (int j = 0; j < nch; ++j) {
         const int cidx = sq.x + j, n = min(kChunk, sq.w - j * kChunk);
         const long t0 = (long)sq.z + (long)j * kChunk;
-        float *sc = ws.Sc + ((((long)cidx * Hv + h) * kD + i) * kD + col0 + c0);
+        float *sc = ws.Sc + ((long)cidx * Hv + h) * kD * kD + col0;
 #pragma unroll
-        for (int e = 0; e < kSE; e += 4) {
-            const float4 v = make_float4(S[e], S[e + 1], S[e + 2], S[e + 3]);
-            st4(sc + e, v);
-            st4(Ss + i * kLC + c0 + e, v);
-        }
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sc[(long)(srow + e) * kD + 16 * ct + lr] = S[ct][e];
+                Ss[(srow + e) * kLC + 16 * ct + lr] = S[ct][e];
+            }
         if (j + 1 < nch) seq_fetch<false>(p, ws, f, cidx + 1, t0 + kChunk, min(kChunk, sq.w - (j + 1) * kChunk), h, g, col0);
         __syncthreads();
         // Vt = V - diag(Gam) K S
-        float acc[kVE];
+        f32x4 acc = z4;
+#pragma unroll 8
+        for (int kb = 0; kb < kD / 4; ++kb)
+            acc = mfma4(L.K[(16 * vrt + lr) * kLK + 4 * kb + lq], Ss[(4 * kb + lq) * kLC + vcol], acc);
 #pragma unroll
-        for (int e = 0; e < kVE; ++e) acc[e] = 0.f;
-        for (int d = 0; d < kD; ++d) {
-            const float kv = L.K[r * kLK + d];
-#pragma unroll
-            for (int e = 0; e < kVE; ++e) acc[e] = fmaf(kv, Ss[d * kLC + cq + e], acc[e]);
-        }
-#pragma unroll
-        for (int e = 0; e < kVE; ++e) {
-            const float vt = r < n ? Vs[r * kLC + cq + e] - L.eg[r] * acc[e] : 0.f;
-            Vts[r * kLC + cq + e] = vt;
-            if (r < n) ws.vt[((t0 + r) * Hv + h) * kD + col0 + cq + e] = vt;
+        for (int e = 0; e < 4; ++e) {
+            const int r = vrow + e;
+            const float vt = r < n ? Vs[r * kLC + vcol] - L.eg[r] * acc[e] : 0.f;
+            Vts[r * kLC + vcol] = vt;
+            if (r < n) ws.vt[((t0 + r) * Hv + h) * kD + col0 + vcol] = vt;
         }
         __syncthreads();
-        // Vn = X diag(beta) Vt
-#pragma unroll
-        for (int e = 0; e < kVE; ++e) acc[e] = 0.f;
-        for (int m = 0; m <= r; ++m) {
-            const float bx = L.X[r * kLN + m] * L.bet[m];
-#pragma unroll
-            for (int e = 0; e < kVE; ++e) acc[e] = fmaf(bx, Vts[m * kLC + cq + e], acc[e]);
+        // Vn = X diag(beta) Vt (X lower: k < 16 (vrt + 1))
+        acc = z4;
+        for (int kb = 0; kb < 4 * vrt + 4; ++kb) {
+            const int k = 4 * kb + lq;
+            acc = mfma4(L.X[(16 * vrt + lr) * kLN + k] * L.bet[k], Vts[k * kLC + vcol], acc);
         }
 #pragma unroll
-        for (int e = 0; e < kVE; ++e) {
+        for (int e = 0; e < 4; ++e) {
+            const int r = vrow + e;
             const float vn = r < n ? acc[e] : 0.f;
-            Vns[r * kLC + cq + e] = vn;
-            if (r < n) ws.vn[((t0 + r) * Hv + h) * kD + col0 + cq + e] = vn;
+            Vns[r * kLC + vcol] = vn;
+            if (r < n) ws.vn[((t0 + r) * Hv + h) * kD + col0 + vcol] = vn;
         }
         __syncthreads();
         // S <- Gam_n S + Ks^T Vn
         const float egn = L.eg[n - 1];
 #pragma unroll
-        for (int e = 0; e < kSE; ++e) S[e] *= egn;
-        for (int rr = 0; rr < n; ++rr) {
-            const float kr = L.K[rr * kLK + i] * L.en[rr];
+        for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-            for (int e = 0; e < kSE; ++e) S[e] = fmaf(kr, Vns[rr * kLC + c0 + e], S[e]);
+            for (int e = 0; e < 4; ++e) S[ct][e] *= egn;
+#pragma unroll 4
+        for (int kb = 0; kb < 16; ++kb) {
+            const int k = 4 * kb + lq;
+            const float a = L.en[k] * L.K[k * kLK + 16 * w + lr];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) S[ct] = mfma4(a, Vns[k * kLC + 16 * ct + lr], S[ct]);
         }
         __syncthreads();
         if (j + 1 < nch) seq_commit<false>(p, f, L, nullptr, nullptr, Vs);
@@ -479,12 +491,17 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
     const int Hv = p.Hv, G = Hv / p.Hqk;
     const int cb = blockIdx.x % kNCB, sh = blockIdx.x / kNCB, h = sh % Hv, s = sh / Hv, g = h / G;
     const int col0 = cb * kCB;
-    const int t = threadIdx.x, i = t / kSP, c0 = (t % kSP) * kSE;
-    const int r = t / kVP, cq = (t % kVP) * kVE;
-    const long so = (((long)s * Hv + h) * kD + i) * kD + col0 + c0;
-    float dS[kSE];
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63, lr = lane & 15, lq = lane >> 4;
+    const int srow = 16 * w + 4 * lq;
+    const int vrt = w >> 1, vrow = 16 * vrt + 4 * lq, vcol = 16 * (w & 1) + lr;
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    const long so = ((long)s * Hv + h) * kD * kD + col0;
+    f32x4 dS[2];
 #pragma unroll
-    for (int e = 0; e < kSE; ++e) dS[e] = p.grad_state_out ? p.grad_state_out[so + e] : 0.f;
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            dS[ct][e] = p.grad_state_out ? p.grad_state_out[so + (long)(srow + e) * kD + 16 * ct + lr] : 0.f;
     const int4 sq = bseq(p, ws, s);  // {first chunk slot, chunks, first token, length}
     const int nch = sq.y;
     SeqPref<true> f;
@@ -496,69 +513,73 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
     for (int j = nch - 1; j >= 0; --j) {
         const int cidx = sq.x + j, n = min(kChunk, sq.w - j * kChunk);
         const long t0 = (long)sq.z + (long)j * kChunk;
-        float *dsc = ws.dSc + ((((long)cidx * Hv + h) * kD + i) * kD + col0 + c0);
+        float *dsc = ws.dSc + ((long)cidx * Hv + h) * kD * kD + col0;
 #pragma unroll
-        for (int e = 0; e < kSE; e += 4) {
-            const float4 v = make_float4(dS[e], dS[e + 1], dS[e + 2], dS[e + 3]);
-            st4(dsc + e, v);
-            st4(dSs + i * kLC + c0 + e, v);
-        }
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dsc[(long)(srow + e) * kD + 16 * ct + lr] = dS[ct][e];
+                dSs[(srow + e) * kLC + 16 * ct + lr] = dS[ct][e];
+            }
         if (j > 0) seq_fetch<true>(p, ws, f, cidx - 1, t0 - kChunk, kChunk, h, g, col0);
         __syncthreads();
-        // dVn = Ks dS' + P^T dO'
-        float acc[kVE];
+        // dVn = diag(en) K dS' + P^T dO'  (P^T upper: k >= 16 vrt)
+        f32x4 acc = z4;
+#pragma unroll 8
+        for (int kb = 0; kb < kD / 4; ++kb)
+            acc = mfma4(L.K[(16 * vrt + lr) * kLK + 4 * kb + lq], dSs[(4 * kb + lq) * kLC + vcol], acc);
 #pragma unroll
-        for (int e = 0; e < kVE; ++e) acc[e] = 0.f;
-        for (int d = 0; d < kD; ++d) {
-            const float kv = L.K[r * kLK + d];
-#pragma unroll
-            for (int e = 0; e < kVE; ++e) acc[e] = fmaf(kv, dSs[d * kLC + cq + e], acc[e]);
+        for (int e = 0; e < 4; ++e) acc[e] *= L.en[vrow + e];
+        for (int kb = 4 * vrt; kb < 16; ++kb) {
+            const int k = 4 * kb + lq;
+            acc = mfma4(Ps[k * kLN + 16 * vrt + lr], dOs[k * kLC + vcol], acc);
         }
 #pragma unroll
-        for (int e = 0; e < kVE; ++e) acc[e] *= L.en[r];
-        for (int m = r; m < n; ++m) {
-            const float pv = Ps[m * kLN + r];
-#pragma unroll
-            for (int e = 0; e < kVE; ++e) acc[e] = fmaf(pv, dOs[m * kLC + cq + e], acc[e]);
-        }
-#pragma unroll
-        for (int e = 0; e < kVE; ++e) {
+        for (int e = 0; e < 4; ++e) {
+            const int r = vrow + e;
             const float v = r < n ? acc[e] : 0.f;
-            dVns[r * kLC + cq + e] = v;
-            if (r < n) ws.dvn[((t0 + r) * Hv + h) * kD + col0 + cq + e] = v;
+            dVns[r * kLC + vcol] = v;
+            if (r < n) ws.dvn[((t0 + r) * Hv + h) * kD + col0 + vcol] = v;
         }
         __syncthreads();
         // dVt = T'^T dVn = diag(beta) X^T dVn
-#pragma unroll
-        for (int e = 0; e < kVE; ++e) acc[e] = 0.f;
-        for (int m = r; m < n; ++m) {
-            const float xv = L.X[m * kLN + r];
-#pragma unroll
-            for (int e = 0; e < kVE; ++e) acc[e] = fmaf(xv, dVns[m * kLC + cq + e], acc[e]);
+        acc = z4;
+        for (int kb = 4 * vrt; kb < 16; ++kb) {
+            const int k = 4 * kb + lq;
+            acc = mfma4(L.X[k * kLN + 16 * vrt + lr], dVns[k * kLC + vcol], acc);
         }
 #pragma unroll
-        for (int e = 0; e < kVE; ++e) {
+        for (int e = 0; e < 4; ++e) {
+            const int r = vrow + e;
             const float v = r < n ? L.bet[r] * acc[e] : 0.f;
-            dVts[r * kLC + cq + e] = v;
-            if (r < n) ws.dvh[((t0 + r) * Hv + h) * kD + col0 + cq + e] = v;
+            dVts[r * kLC + vcol] = v;
+            if (r < n) ws.dvh[((t0 + r) * Hv + h) * kD + col0 + vcol] = v;
         }
         __syncthreads();
         // dS <- Gam_n dS' + (Gam Q)^T dO' - (Gam K)^T dVt
         const float egn = L.eg[n - 1];
 #pragma unroll
-        for (int e = 0; e < kSE; ++e) dS[e] *= egn;
-        for (int rr = 0; rr < n; ++rr) {
-            const float qv = Qs[rr * kLK + i] * L.eg[rr], kv = L.K[rr * kLK + i] * L.eg[rr];
+        for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-            for (int e = 0; e < kSE; ++e)
-                dS[e] = fmaf(qv, dOs[rr * kLC + c0 + e], fmaf(-kv, dVts[rr * kLC + c0 + e], dS[e]));
+            for (int e = 0; e < 4; ++e) dS[ct][e] *= egn;
+#pragma unroll 4
+        for (int kb = 0; kb < 16; ++kb) {
+            const int k = 4 * kb + lq;
+            const float aq = L.eg[k] * Qs[k * kLK + 16 * w + lr], ak = -L.eg[k] * L.K[k * kLK + 16 * w + lr];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                dS[ct] = mfma4(aq, dOs[k * kLC + 16 * ct + lr], dS[ct]);
+                dS[ct] = mfma4(ak, dVts[k * kLC + 16 * ct + lr], dS[ct]);
+            }
         }
         __syncthreads();
         if (j > 0) seq_commit<true>(p, f, L, Qs, Ps, dOs);
     }
     if (p.grad_state_in) {
 #pragma unroll
-        for (int e = 0; e < kSE; ++e) p.grad_state_in[so + e] = dS[e];
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p.grad_state_in[so + (long)(srow + e) * kD + 16 * ct + lr] = dS[ct][e];
     }
 }
 
