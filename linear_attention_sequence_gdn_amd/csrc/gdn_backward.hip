@@ -586,29 +586,51 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
 // ---------------------------------------------------------------------------
 // 5. per-chunk gradients
 // ---------------------------------------------------------------------------
-// acc[ri][m] += sum_k fa(r0 + ri, k) fb(k, cc + 16 m) for k < K (a multiple
+// acc[ri][m] += sum_k A(r0 + ri, k) B(k, cc + 16 m) for k < K (a multiple
 // of 32), r0 = 4 (t / 16), cc = t % 16, m < NC: a 64 x (16 NC) product,
-// staged through LDS 32 deep.  AK: fa's source is contiguous along k (else
-// along rows); BK: fb's source is contiguous along k (else along columns).
-// Consecutive threads stage consecutive source elements; the staging loops
-// are unrolled only twice, which keeps the kernel within 256 registers.
-template <int NC, bool AK = true, bool BK = false, class FA, class FB>
-__device__ __forceinline__ void gemm64(float (&acc)[4][8], int K, FA fa, FB fb, float *sA, float *sB)
+// staged through LDS 32 deep.  The sources are read 16 bytes at a time along
+// their contiguous dimension: fa4(r, k) is A(r, k..k+3) when AK, else
+// A(r..r+3, k); fb4(k, c) is B(k..k+3, c) when BK, else B(k, c..c+3).
+template <int NC, bool AK, bool BK, class FA4, class FB4>
+__device__ __forceinline__ void gemm64(float (&acc)[4][8], int K, FA4 fa4, FB4 fb4, float *sA, float *sB)
 {
     const int t = threadIdx.x, r0 = 4 * (t >> 4), cc = t & 15;
     constexpr int NCOL = 16 * NC, LB = NCOL + 1;
     for (int k0 = 0; k0 < K; k0 += 32) {
-#pragma unroll 2
-        for (int e = 0; e < 8; ++e) {
+        float4 va[2], vb[NC / 2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
             const int idx = t + kBT * e;
-            const int r = AK ? idx >> 5 : idx & 63, kk = AK ? idx & 31 : idx >> 6;
-            sA[r * 33 + kk] = fa(r, k0 + kk);
+            va[e] = AK ? fa4(idx >> 3, k0 + 4 * (idx & 7)) : fa4(4 * (idx & 15), k0 + (idx >> 4));
         }
-#pragma unroll 2
-        for (int e = 0; e < 2 * NC; ++e) {
+#pragma unroll
+        for (int e = 0; e < NC / 2; ++e) {
             const int idx = t + kBT * e;
-            const int kk = BK ? idx & 31 : idx / NCOL, c = BK ? idx >> 5 : idx % NCOL;
-            sB[kk * LB + c] = fb(k0 + kk, c);
+            vb[e] = BK ? fb4(k0 + 4 * (idx & 7), idx >> 3) : fb4(k0 + idx / (NCOL / 4), 4 * (idx % (NCOL / 4)));
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int idx = t + kBT * e;
+            const float v[4] = {va[e].x, va[e].y, va[e].z, va[e].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (AK)
+                    sA[(idx >> 3) * 33 + 4 * (idx & 7) + i] = v[i];
+                else
+                    sA[(4 * (idx & 15) + i) * 33 + (idx >> 4)] = v[i];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < NC / 2; ++e) {
+            const int idx = t + kBT * e;
+            const float v[4] = {vb[e].x, vb[e].y, vb[e].z, vb[e].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (BK)
+                    sB[(4 * (idx & 7) + i) * LB + (idx >> 3)] = v[i];
+                else
+                    sB[(idx / (NCOL / 4)) * LB + 4 * (idx % (NCOL / 4)) + i] = v[i];
+            }
         }
         __syncthreads();
 #pragma unroll 2
@@ -673,10 +695,17 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
     auto KH = [&](int r, int d) { return r < n ? ws.kh[((t0 + r) * Hqk + g) * kD + d] : 0.f; };
     auto QH = [&](int r, int d) { return r < n ? ws.qh[((t0 + r) * Hqk + g) * kD + d] : 0.f; };
-    auto VROW = [&](const float *base, int r, int c) { return r < n ? base[((t0 + r) * Hv + h) * kD + c] : 0.f; };
-    auto DO = [&](int r, int c) {
-        return r < n ? p.q_scale * bf16_to_f32(p.grad_o[((t0 + r) * Hv + h) * kD + c]) : 0.f;
+    // 16-byte sources: four consecutive elements of a row (rows >= n read as zero)
+    auto KH4 = [&](int r, int d) { return r < n ? ld4(ws.kh + ((t0 + r) * Hqk + g) * kD + d) : make_float4(0.f, 0.f, 0.f, 0.f); };
+    auto QH4 = [&](int r, int d) { return r < n ? ld4(ws.qh + ((t0 + r) * Hqk + g) * kD + d) : make_float4(0.f, 0.f, 0.f, 0.f); };
+    auto V4 = [&](const float *base, int r, int c) { return r < n ? ld4(base + ((t0 + r) * Hv + h) * kD + c) : make_float4(0.f, 0.f, 0.f, 0.f); };
+    auto DO4 = [&](int r, int c) {
+        if (r >= n) return make_float4(0.f, 0.f, 0.f, 0.f);
+        const uint2 u = *reinterpret_cast<const uint2 *>(p.grad_o + ((t0 + r) * Hv + h) * kD + c);
+        return make_float4(p.q_scale * bf16_lo(u.x), p.q_scale * bf16_hi(u.x), p.q_scale * bf16_lo(u.y),
+                           p.q_scale * bf16_hi(u.y));
     };
+    auto L4 = [](const float *q) { return *reinterpret_cast<const float4 *>(q); };
     // rows of this thread's group: apply coef[r] * rowsum to dgam (one writer per row)
     auto row_apply = [&](float (&part)[4], float *dst, const float *coef, float sign) {
 #pragma unroll
@@ -693,7 +722,7 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         zero(dQ);
         // (c) O = q_scale (diag(Gam) Q S + ...): E1 = dO' S^T
         zero(acc);
-        gemm64<8, true, true>(acc, kD, DO, [&](int c, int i) { return Sc[i * kD + c]; }, sA, sB);
+        gemm64<8, true, true>(acc, kD, DO4, [&](int c, int i) { return ld4(Sc + i * kD + c); }, sA, sB);
         float part[4];
 #pragma unroll
         for (int ri = 0; ri < 4; ++ri) {
@@ -708,7 +737,7 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         row_apply(part, dgam, eg, 1.f);
         // (d) P = Q K^T * D * M: dP = dO' Vn^T (lower); Em = dP * P; Wm = dP * D
         zero(acc);
-        gemm64<4, true, true>(acc, kD, DO, [&](int c, int jj) { return VROW(ws.vn, jj, c); }, sA, sB);
+        gemm64<4, true, true>(acc, kD, DO4, [&](int c, int jj) { return V4(ws.vn, jj, c); }, sA, sB);
 #pragma unroll
         for (int ri = 0; ri < 4; ++ri)
 #pragma unroll
@@ -719,7 +748,7 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 Wm[r * kLN + jj] = in ? acc[ri][m] * expf(gam[r] - gam[jj]) : 0.f;
             }
         __syncthreads();
-        gemm64<8>(dQ, 64, [&](int r, int jj) { return Wm[r * kLN + jj]; }, KH, sA, sB);
+        gemm64<8, true, false>(dQ, 64, [&](int r, int jj) { return L4(Wm + r * kLN + jj); }, KH4, sA, sB);
 #pragma unroll
         for (int ri = 0; ri < 4; ++ri) {
             const int r = r0 + ri;
@@ -731,12 +760,12 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     float dK[4][8];
     zero(dK);
     // (d) continued: dk^ += dQK^T q^
-    gemm64<8, false>(dK, 64, [&](int r, int jj) { return Wm[jj * kLN + r]; }, QH, sA, sB);
+    gemm64<8, false, false>(dK, 64, [&](int r, int jj) { return L4(Wm + jj * kLN + r); }, QH4, sA, sB);
 
     // (a) Ks = diag(en) K enters S' = ... + Ks^T Vn: dKs = Vn dS'^T
     zero(acc);
-    gemm64<8, true, true>(acc, kD, [&](int r, int c) { return VROW(ws.vn, r, c); },
-                          [&](int c, int i) { return dSc[i * kD + c]; }, sA, sB);
+    gemm64<8, true, true>(acc, kD, [&](int r, int c) { return V4(ws.vn, r, c); },
+                          [&](int c, int i) { return ld4(dSc + i * kD + c); }, sA, sB);
     {
         float part[4];
 #pragma unroll
@@ -776,8 +805,8 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
     // (e) Vt = V - diag(Gam) K S: E2 = dVt S^T
     zero(acc);
-    gemm64<8, true, true>(acc, kD, [&](int r, int c) { return VROW(ws.dvh, r, c); },
-                          [&](int c, int i) { return Sc[i * kD + c]; }, sA, sB);
+    gemm64<8, true, true>(acc, kD, [&](int r, int c) { return V4(ws.dvh, r, c); },
+                          [&](int c, int i) { return ld4(Sc + i * kD + c); }, sA, sB);
     {
         float part[4];
 #pragma unroll
@@ -795,8 +824,8 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
     // (f) Vn = T' Vt: dT' = dVn Vt^T (lower incl. diagonal); dbeta_j += sum_i dT'_ij X_ij; dX = dT' diag(beta)
     zero(acc);
-    gemm64<4, true, true>(acc, kD, [&](int r, int c) { return VROW(ws.dvn, r, c); },
-                          [&](int c, int jj) { return VROW(ws.vt, jj, c); }, sA, sB);
+    gemm64<4, true, true>(acc, kD, [&](int r, int c) { return V4(ws.dvn, r, c); },
+                          [&](int c, int jj) { return V4(ws.vt, jj, c); }, sA, sB);
 #pragma unroll
     for (int ri = 0; ri < 4; ++ri)
 #pragma unroll
@@ -815,16 +844,16 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
     // (g) X = (I + A)^-1: dA = strict_lower(-X^T dX X^T)
     zero(acc);
-    gemm64<4, false>(acc, 64, [&](int r, int m) { return ws.X[mo + m * 64 + r]; },
-                     [&](int m, int jj) { return Wm[m * kLN + jj]; }, sA, sB);
+    gemm64<4, false, false>(acc, 64, [&](int r, int m) { return ld4(ws.X + mo + m * 64 + r); },
+                            [&](int m, int jj) { return L4(Wm + m * kLN + jj); }, sA, sB);
 #pragma unroll
     for (int ri = 0; ri < 4; ++ri)
 #pragma unroll
         for (int m = 0; m < 4; ++m) Ym[(r0 + ri) * kLN + cc + 16 * m] = acc[ri][m];
     __syncthreads();
     zero(acc);
-    gemm64<4, true, true>(acc, 64, [&](int r, int m) { return Ym[r * kLN + m]; },
-                          [&](int m, int jj) { return ws.X[mo + jj * 64 + m]; }, sA, sB);
+    gemm64<4, true, true>(acc, 64, [&](int r, int m) { return L4(Ym + r * kLN + m); },
+                          [&](int m, int jj) { return ld4(ws.X + mo + jj * 64 + m); }, sA, sB);
 #pragma unroll
     for (int ri = 0; ri < 4; ++ri)
 #pragma unroll
@@ -835,7 +864,7 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
     // (h) A = diag(beta) K K^T * D (strict lower): dbeta_i, Em += dA * A, dKK -> Ym
     zero(acc);
-    gemm64<4, true, true>(acc, kD, KH, [&](int d, int jj) { return KH(jj, d); }, sA, sB);
+    gemm64<4, true, true>(acc, kD, KH4, [&](int d, int jj) { return KH4(jj, d); }, sA, sB);
     {
         float part[4];
 #pragma unroll
@@ -857,7 +886,11 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         row_apply(part, dbet, nullptr, 1.f);
     }
     __syncthreads();
-    gemm64<8>(dK, 64, [&](int r, int jj) { return Ym[r * kLN + jj] + Ym[jj * kLN + r]; }, KH, sA, sB);
+    gemm64<8, true, false>(dK, 64, [&](int r, int jj) {
+        const float4 u = L4(Ym + r * kLN + jj);
+        return make_float4(u.x + Ym[jj * kLN + r], u.y + Ym[(jj + 1) * kLN + r], u.z + Ym[(jj + 2) * kLN + r],
+                           u.w + Ym[(jj + 3) * kLN + r]);
+    }, KH4, sA, sB);
     // gamma: rows of Em count +, columns -; then dg = reverse prefix sum
     if (t < n) {
         float v = 0.f;
