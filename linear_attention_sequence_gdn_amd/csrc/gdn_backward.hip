@@ -20,7 +20,7 @@
 // Passes (one launch each):
 //   bwd_setup_kernel   (packed calls) chunk and sequence tables from cu_seqlens
 //   bwd_prep_kernel    conv + SiLU (+ L2 norm) of q, k, v; gates and gamma
-//   bwd_local_kernel   per (chunk, V head): P and X = (I + A)^-1
+//   bwd_local_kernel   per (chunk, QK group): P and X = (I + A)^-1 of its V heads
 //   bwd_fwd_kernel     per (sequence, V head, 32 state columns), in order:
 //                      the state entering every chunk, Vt and Vn
 //   bwd_chain_kernel   per (sequence, V head, 32 columns), in reverse: the
@@ -87,6 +87,8 @@ struct BwdWs {
 };
 
 __device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + expf(-x)); }
+__device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ void st4(float *p, float4 v) { *reinterpret_cast<float4 *>(p) = v; }
 
 // {sequence, its first token, chunk length (0: empty slot), chunk index in the sequence}
 __device__ __forceinline__ int4 bchunk(const BwdArgs &p, const BwdWs &ws, int cidx)
@@ -228,29 +230,34 @@ struct SolveCol64 {
     }
 };
 
+// One workgroup per (chunk, QK group): K^K^T and Q^K^T once, then the
+// group's V heads four at a time (their A matrices reuse the LDS of the k^ /
+// q^ rows), wave w solving head w.
+constexpr int kLocalR = 4 * 64 * kLN;  // >= 2 * 64 * kLK: the k^ and q^ rows, or four A matrices
+static_assert(kLocalR >= 2 * 64 * kLK, "the A matrices overlay the k^ and q^ rows");
+
 __global__ __launch_bounds__(kBT) void bwd_local_kernel(BwdArgs p, BwdWs ws)
 {
-    __shared__ float Ks[64 * kLK], Qs[64 * kLK], As[64 * kLN];
-    __shared__ float gam[64], bet[64];
-    const int Hv = p.Hv, G = Hv / p.Hqk;
-    const int cidx = blockIdx.x / Hv, h = blockIdx.x % Hv, g = h / G;
+    __shared__ __attribute__((aligned(16))) float R[kLocalR];
+    __shared__ float KK[64 * kLN], QK[64 * kLN];
+    __shared__ float gam[4][64], bet[4][64];
+    const int Hv = p.Hv, Hqk = p.Hqk, G = Hv / Hqk;
+    const int cidx = blockIdx.x / Hqk, g = blockIdx.x % Hqk;
     const int4 ci = bchunk(p, ws, cidx);
     const int n = ci.z;
     if (n == 0) return;
     const long t0 = (long)ci.y + (long)ci.w * kChunk;
-    const int t = threadIdx.x;
-    for (int e = 0; e < 32; ++e) {
-        const int idx = t + kBT * e, r = idx >> 7, d = idx & 127;
-        const long src = ((t0 + r) * p.Hqk + g) * kD + d;
-        Ks[r * kLK + d] = r < n ? ws.kh[src] : 0.f;
-        Qs[r * kLK + d] = r < n ? ws.qh[src] : 0.f;
-    }
-    if (t < 64) {
-        gam[t] = t < n ? ws.gam[(t0 + t) * Hv + h] : 0.f;
-        bet[t] = t < n ? ws.beta[(t0 + t) * Hv + h] : 0.f;
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+    float *Ks = R, *Qs = R + 64 * kLK;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int idx = t + kBT * e, r = idx >> 5, q = idx & 31;
+        const long src = ((t0 + r) * Hqk + g) * kD + 4 * q;
+        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+        st4(Ks + r * kLK + 4 * q, r < n ? ld4(ws.kh + src) : z);
+        st4(Qs + r * kLK + 4 * q, r < n ? ld4(ws.qh + src) : z);
     }
     __syncthreads();
-    const long mo = ((long)cidx * Hv + h) * 64 * 64;
     {
         // row i, columns (t & 3) + 4m
         const int i = t >> 2;
@@ -268,22 +275,40 @@ __global__ __launch_bounds__(kBT) void bwd_local_kernel(BwdArgs p, BwdWs ws)
         }
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
-            const int jj = (t & 3) + 4 * m;
-            const float D = expf(gam[i] - gam[jj]);
-            As[i * kLN + jj] = (jj < i && i < n) ? bet[i] * kk[m] * D : 0.f;
-            ws.P[mo + i * 64 + jj] = (jj <= i && i < n) ? qk[m] * D : 0.f;
+            KK[i * kLN + (t & 3) + 4 * m] = kk[m];
+            QK[i * kLN + (t & 3) + 4 * m] = qk[m];
         }
     }
-    __syncthreads();
-    // unit lower-triangular inverse, lane c takes column c in registers:
-    // once x_m is final it is removed from every later row
-    if (t < 64) {
-        float y[64];
+    __syncthreads();  // the k^ / q^ rows are dead from here on
+    for (int j0 = 0; j0 < G; j0 += 4) {
+        const int jn = min(4, G - j0);
+        if (w < jn) {
+            const int h = g * G + j0 + w;
+            gam[w][lane] = lane < n ? ws.gam[(t0 + lane) * Hv + h] : 0.f;
+            bet[w][lane] = lane < n ? ws.beta[(t0 + lane) * Hv + h] : 0.f;
+        }
+        __syncthreads();
+        // A (strict lower) into LDS and P (lower incl. the diagonal) to the workspace, for each head
+        for (int idx = t; idx < jn * 4096; idx += kBT) {
+            const int jh = idx >> 12, i = (idx >> 6) & 63, jj = idx & 63;
+            const float D = expf(gam[jh][i] - gam[jh][jj]);
+            R[jh * 64 * kLN + i * kLN + jj] = (jj < i && i < n) ? bet[jh][i] * KK[i * kLN + jj] * D : 0.f;
+            const long mo = ((long)cidx * Hv + g * G + j0 + jh) * 4096;
+            ws.P[mo + i * 64 + jj] = (jj <= i && i < n) ? QK[i * kLN + jj] * D : 0.f;
+        }
+        __syncthreads();
+        // unit lower-triangular inverse of head w's I + A, lane c takes column c in
+        // registers: once x_m is final it is removed from every later row
+        if (w < jn) {
+            float y[64];
 #pragma unroll
-        for (int ii = 0; ii < 64; ++ii) y[ii] = ii == t ? 1.f : 0.f;
-        SolveCol64<0>::run(y, As);
+            for (int ii = 0; ii < 64; ++ii) y[ii] = ii == lane ? 1.f : 0.f;
+            SolveCol64<0>::run(y, R + w * 64 * kLN);
+            const long mo = ((long)cidx * Hv + g * G + j0 + w) * 4096;
 #pragma unroll
-        for (int ii = 0; ii < 64; ++ii) ws.X[mo + ii * 64 + t] = y[ii];
+            for (int ii = 0; ii < 64; ++ii) ws.X[mo + ii * 64 + lane] = y[ii];
+        }
+        __syncthreads();  // the next round rewrites the gates and the A matrices
     }
 }
 
@@ -294,8 +319,6 @@ struct SeqTile {
     float gam[64], bet[64], eg[64], en[64];
 };
 
-__device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
-__device__ __forceinline__ void st4(float *p, float4 v) { *reinterpret_cast<float4 *>(p) = v; }
 
 // A chunk's operands for the sequential passes, held in registers: they are
 // requested before the current chunk's products and written to LDS after
@@ -1190,7 +1213,7 @@ hipError_t launch_backward(const uint16_t *q, const uint16_t *k, const uint16_t 
     if (chunks > 0) {
         if (p.cu_seqlens) hipLaunchKernelGGL(bwd_setup_kernel, dim3(1), dim3(1024), 0, stream, p, ws);
         hipLaunchKernelGGL(bwd_prep_kernel, dim3(chunks, planes), dim3(kBT), 0, stream, p, ws);
-        hipLaunchKernelGGL(bwd_local_kernel, dim3(chunks * Hv), dim3(kBT), 0, stream, p, ws);
+        hipLaunchKernelGGL(bwd_local_kernel, dim3(chunks * Hqk), dim3(kBT), 0, stream, p, ws);
         hipLaunchKernelGGL(bwd_fwd_kernel, dim3(N * Hv * kNCB), dim3(kST), 0, stream, p, ws);
     }
     // also with no tokens: the state gradient passes straight through
