@@ -127,22 +127,31 @@ __device__ __forceinline__ const uint16_t *plane_src(const BwdArgs &p, const Pla
     return (P.kind == 0 ? p.q : P.kind == 1 ? p.k : p.v) + (long)P.head * kD;
 }
 
-// Conv output y of token t (in-sequence index) of sequence s, channel c of
-// the plane: taps in order, history rows for t - 3 + j < 0.
-__device__ __forceinline__ float conv_y(const BwdArgs &p, const Plane &P, const uint16_t *x, const float (&w)[4],
-                                        int s, long seq0, int t, int c, long C_tot)
+// The conv rows a thread needs, held in registers: thread (channel c, half
+// rh) of a chunk takes its rows 32 rh .. 32 rh + 31 (sequence positions
+// tb .. tb + 31), and the window holds the raw rows tb - 3 .. tb + 31 of
+// channel c (carried rows, or zeros, before the sequence; zeros past it).
+constexpr int kWin = 35;
+__device__ __forceinline__ void x_window(const BwdArgs &p, const Plane &P, const uint16_t *x, int s, long seq0,
+                                         int tb, int L, int c, long C_tot, float (&xw)[kWin])
+{
+#pragma unroll
+    for (int i = 0; i < kWin; ++i) {
+        const int tau = tb - 3 + i;
+        float v = 0.f;
+        if (tau >= 0 && tau < L)
+            v = bf16_to_f32(x[(seq0 + tau) * P.ld + c]);
+        else if (tau < 0 && p.conv_state_in)
+            v = bf16_to_f32(p.conv_state_in[((long)s * 3 + 3 + tau) * C_tot + P.ch0 + c]);
+        xw[i] = v;
+    }
+}
+// conv output of the window's row r (sequence position tb + r): taps in order
+__device__ __forceinline__ float conv_at(const float (&w)[4], const float (&xw)[kWin], int r)
 {
     float y = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int tau = t - 3 + j;
-        float xv = 0.f;
-        if (tau >= 0)
-            xv = bf16_to_f32(x[(seq0 + tau) * P.ld + c]);
-        else if (p.conv_state_in)
-            xv = bf16_to_f32(p.conv_state_in[((long)s * 3 + 3 + tau) * C_tot + P.ch0 + c]);
-        y = fmaf(w[j], xv, y);
-    }
+    for (int j = 0; j < 4; ++j) y = fmaf(w[j], xw[r + j], y);
     return y;
 }
 
@@ -157,20 +166,26 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs p, BwdWs ws)
     const int s = ci.x, n = ci.z, j = ci.w;
     if (n == 0) return;  // empty chunk slot
     const long seq0 = ci.y, t0 = seq0 + (long)j * kChunk;
+    const int L = bseq(p, ws, s).w;
     const long C_tot = 2L * p.Hqk * kD + (long)p.Hv * kD;
     const Plane P = plane_of(p, blockIdx.y);
     const uint16_t *x = plane_src(p, P);
-    const int t = threadIdx.x, c = t & 127, rh = t >> 7;
+    const int t = threadIdx.x, c = t & 127, rh = t >> 7, rb = 32 * rh;
     float w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = bf16_to_f32(p.conv_w[(P.ch0 + c) * 4 + i]);
-    for (int r = rh; r < n; r += 2) {
-        const float y = conv_y(p, P, x, w, s, seq0, j * kChunk + r, c, C_tot);
-        const float z = y * sigm(y);
-        if (P.kind == 2)
-            ws.vh[((t0 + r) * p.Hv + P.head) * kD + c] = z;
-        else
-            zs[r * kLK + c] = z;
+    float xw[kWin];
+    x_window(p, P, x, s, seq0, j * kChunk + rb, L, c, C_tot, xw);
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+        if (rb + r < n) {
+            const float y = conv_at(w, xw, r);
+            const float z = y * sigm(y);
+            if (P.kind == 2)
+                ws.vh[((t0 + rb + r) * p.Hv + P.head) * kD + c] = z;
+            else
+                zs[(rb + r) * kLK + c] = z;
+        }
     }
     if (P.kind == 2) {
         // gates of this V head, lane = token: g = -c softplus(a), gamma = in-chunk prefix sum
@@ -209,7 +224,12 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs p, BwdWs ws)
     }
     __syncthreads();
     float *dst = P.kind == 0 ? ws.qh : ws.kh;
-    for (int r = rh; r < n; r += 2) dst[((t0 + r) * p.Hqk + P.head) * kD + c] = zs[r * kLK + c] / nrm[r];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+        if (rb + r < n) {
+            dst[((t0 + rb + r) * p.Hqk + P.head) * kD + c] = zs[(rb + r) * kLK + c] / nrm[rb + r];
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -948,34 +968,37 @@ __global__ __launch_bounds__(kBT) void bwd_dy_kernel(BwdArgs p, BwdWs ws)
     const int s = ci.x, n = ci.z, j = ci.w;
     if (n == 0) return;
     const long seq0 = ci.y, t0 = seq0 + (long)j * kChunk;
+    const int L = bseq(p, ws, s).w;
     const long C_tot = 2L * p.Hqk * kD + (long)p.Hv * kD;
     const int G = p.Hv / p.Hqk;
     const Plane P = plane_of(p, blockIdx.y);
     const uint16_t *x = plane_src(p, P);
-    const int t = threadIdx.x, c = t & 127, rh = t >> 7;
+    const int t = threadIdx.x, c = t & 127, rh = t >> 7, rb = 32 * rh;
     float w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = bf16_to_f32(p.conv_w[(P.ch0 + c) * 4 + i]);
+    float xw[kWin];
+    x_window(p, P, x, s, seq0, j * kChunk + rb, L, c, C_tot, xw);
     if (P.kind == 2) {
-        for (int r = rh; r < n; r += 2) {
-            const float y = conv_y(p, P, x, w, s, seq0, j * kChunk + r, c, C_tot);
-            ws.dy[(t0 + r) * C_tot + P.ch0 + c] = ws.dvh[((t0 + r) * p.Hv + P.head) * kD + c] * silu_grad(y);
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+            if (rb + r < n) {
+                const long tok = t0 + rb + r;
+                ws.dy[tok * C_tot + P.ch0 + c] = ws.dvh[(tok * p.Hv + P.head) * kD + c] * silu_grad(conv_at(w, xw, r));
+            }
         }
         return;
     }
     const float *part = P.kind == 0 ? ws.dqp : ws.dkp;
-    float yv[32];  // conv outputs of rows rh, rh + 2, ...
 #pragma unroll
-    for (int ii = 0; ii < 32; ++ii) {
-        const int r = rh + 2 * ii;
-        yv[ii] = 0.f;
-        if (r >= n) continue;
-        const float y = conv_y(p, P, x, w, s, seq0, j * kChunk + r, c, C_tot);
-        yv[ii] = y;
-        zs[r * kLK + c] = y * sigm(y);
-        float d = 0.f;
-        for (int jh = 0; jh < G; ++jh) d += part[((t0 + r) * p.Hv + P.head * G + jh) * kD + c];
-        ds[r * kLK + c] = d;
+    for (int r = 0; r < 32; ++r) {
+        if (rb + r < n) {
+            const float y = conv_at(w, xw, r);
+            zs[(rb + r) * kLK + c] = y * sigm(y);
+            float d = 0.f;
+            for (int jh = 0; jh < G; ++jh) d += part[((t0 + rb + r) * p.Hv + P.head * G + jh) * kD + c];
+            ds[(rb + r) * kLK + c] = d;
+        }
     }
     __syncthreads();
     {
@@ -998,12 +1021,13 @@ __global__ __launch_bounds__(kBT) void bwd_dy_kernel(BwdArgs p, BwdWs ws)
     }
     __syncthreads();
 #pragma unroll
-    for (int ii = 0; ii < 32; ++ii) {
-        const int r = rh + 2 * ii;
-        if (r >= n) continue;
-        const float rn = nrm[r];
-        const float dz = ds[r * kLK + c] / rn - zs[r * kLK + c] * zd[r] / (rn * rn * rn);
-        ws.dy[(t0 + r) * C_tot + P.ch0 + c] = dz * silu_grad(yv[ii]);
+    for (int r = 0; r < 32; ++r) {
+        const int rr = rb + r;
+        if (rr < n) {
+            const float rn = nrm[rr];
+            const float dz = ds[rr * kLK + c] / rn - zs[rr * kLK + c] * zd[rr] / (rn * rn * rn);
+            ws.dy[(t0 + rr) * C_tot + P.ch0 + c] = dz * silu_grad(conv_at(w, xw, r));
+        }
     }
 }
 
@@ -1027,34 +1051,28 @@ __global__ __launch_bounds__(kBT) void bwd_conv_kernel(BwdArgs p, BwdWs ws)
     const int L = bseq(p, ws, s).w;  // sequence length
     const uint16_t *x = plane_src(p, P);
     float *gx = (P.kind == 0 ? p.grad_q : P.kind == 1 ? p.grad_k : p.grad_v) + (long)P.head * kD;
-    const int t = threadIdx.x, c = t & 127, rh = t >> 7;
+    const int t = threadIdx.x, c = t & 127, rh = t >> 7, rb = 32 * rh, tb = j * kChunk + rb;
     const long ch = P.ch0 + c;
     float w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = bf16_to_f32(p.conv_w[ch * 4 + i]);
-    const float *dy = ws.dy + seq0 * C_tot + ch;  // dy of token tau of this sequence: dy[tau * C_tot]
+    // dy of sequence positions tb .. tb + 34 (zero past the sequence), and the raw rows tb - 3 .. tb + 31
+    const float *dy = ws.dy + seq0 * C_tot + ch;
+    float dw[kWin], xw[kWin];
+#pragma unroll
+    for (int i = 0; i < kWin; ++i) dw[i] = tb + i < L ? dy[(long)(tb + i) * C_tot] : 0.f;
+    x_window(p, P, x, s, seq0, tb, L, c, C_tot, xw);
     float gw[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int r = rh; r < n; r += 2) {
-        const int tau = j * kChunk + r;
-        // x[tau] feeds y[tau + 3 - jj] through tap jj
-        float gxv = 0.f;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int ty = tau + 3 - jj;
-            if (ty < L) gxv = fmaf(w[jj], dy[(long)ty * C_tot], gxv);
-        }
-        gx[(t0 + r) * P.ld + c] = gxv;
-        // y[tau] reads x[tau - 3 + jj] through tap jj
-        const float d = dy[(long)tau * C_tot];
+    for (int r = 0; r < 32; ++r) {
+        if (rb + r < n) {
+            // x[tau] feeds y[tau + 3 - jj] through tap jj; y[tau] reads x[tau - 3 + jj]
+            float gxv = 0.f;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int tx = tau - 3 + jj;
-            float xv = 0.f;
-            if (tx >= 0)
-                xv = bf16_to_f32(x[(seq0 + tx) * P.ld + c]);
-            else if (p.conv_state_in)
-                xv = bf16_to_f32(p.conv_state_in[((long)s * 3 + 3 + tx) * C_tot + ch]);
-            gw[jj] = fmaf(d, xv, gw[jj]);
+            for (int jj = 0; jj < 4; ++jj) gxv = fmaf(w[jj], dw[r + 3 - jj], gxv);
+            gx[(t0 + rb + r) * P.ld + c] = gxv;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) gw[jj] = fmaf(dw[r], xw[r + jj], gw[jj]);
         }
     }
 #pragma unroll
@@ -1066,13 +1084,12 @@ __global__ __launch_bounds__(kBT) void bwd_conv_kernel(BwdArgs p, BwdWs ws)
             ws.dwp[((long)cidx * C_tot + ch) * 4 + jj] = wpart[0][c][jj] + wpart[1][c][jj];
         // the carried rows x[-3..-1] feed the sequence's first tokens
         if (j == 0 && p.grad_conv_state_in) {
+#pragma unroll
             for (int rr = 0; rr < 3; ++rr) {
                 float gv = 0.f;
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int ty = rr - jj;  // token whose tap jj reads row rr (= x[rr - 3])
-                    if (ty >= 0 && ty < L) gv = fmaf(w[jj], dy[(long)ty * C_tot], gv);
-                }
+                for (int jj = 0; jj < 4; ++jj)
+                    if (rr - jj >= 0) gv = fmaf(w[jj], dw[rr - jj], gv);  // token rr - jj reads row rr through tap jj
                 p.grad_conv_state_in[((long)s * 3 + rr) * C_tot + ch] = gv;
             }
         }
