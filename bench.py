@@ -452,6 +452,33 @@ def cpu_baseline(min_seconds=12.0, max_reps=60):
                       f"{reps} run(s) in {dt:.1f} s wall"}
 
 
+def cpu_baseline_backward(T_sample=1024, min_seconds=4.0, max_reps=20):
+    """The oracle's backward (fp64, token by token) on the first T_sample
+    tokens of the backward workload, all heads; its cost per token does not
+    depend on T, so tokens/s carries over to the whole sequence."""
+    import numpy as np
+    import oracle
+    from linear_attention_sequence_gdn_amd import inputs
+    c = inputs.CONFIGS[1]
+    Hqk, Hv = c["Hqk"], c["Hv"]
+    x = inputs.make_prefill(T_list=[T_sample], Hqk=Hqk, Hv=Hv, seed=1001, gate_scale=c["gate_scale"])
+    rng = np.random.default_rng(2001)
+    g_o = rng.standard_normal((T_sample, Hv, D))
+    oracle.build(force=False)
+    reps, t0 = 0, time.perf_counter()
+    while reps < max_reps:
+        oracle.prefill_backward(x["q"], x["k"], x["v"], x["a"], x["b"], x["conv_w"], x["cu_seqlens"], g_o,
+                                Hqk=Hqk, Hv=Hv, gate_scale=c["gate_scale"])
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": T_sample * reps / dt, "unit": "tokens/s", "cores": min(oracle.num_threads(), Hqk),
+            "kind": "oracle",
+            "sample": f"fp64 token-by-token oracle backward on the first {T_sample} tokens of the workload, "
+                      f"16QK/48V, parallel over the 16 QK groups; {reps} run(s) in {dt:.1f} s wall"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -550,6 +577,7 @@ def main():
         torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
+        line["backward"]["cpu_baseline"] = cpu_baseline_backward()
     print(json.dumps(line), flush=True)
 
 
