@@ -200,3 +200,17 @@ def test_backward_varlen_long_mixed(oracle_lib):
     inp, g_o, g_S, qs = _varlen_case(lens, 1, 3, seed=81)
     _compare(_gpu_varlen(inp, g_o, g_S, qs), _oracle(oracle_lib, inp, g_o, g_S, qs), 1, inp["T_tot"],
              f"varlen {lens}")
+
+
+def test_backward_strong_decay(oracle_lib):
+    # gate_scale 2: the in-chunk cumulative log decay reaches about -100, so
+    # e^gamma underflows fp32 within a chunk; the chunk form only ever takes
+    # e^(gamma_i - gamma_j) with i >= j and e^gamma itself, so nothing overflows
+    inp, g_o, g_S, qs = _case(1, 200, 2, 4, seed=91, gate_scale=2.0)
+    _compare(_gpu(inp, g_o, g_S, qs, 1, 200), _oracle(oracle_lib, inp, g_o, g_S, qs), 1, 200, "strong decay")
+
+
+def test_backward_no_decay(oracle_lib):
+    # gate_scale 0: alpha = 1 for every token, the state only accumulates writes
+    inp, g_o, g_S, qs = _case(1, 300, 1, 2, seed=92, gate_scale=0.0)
+    _compare(_gpu(inp, g_o, g_S, qs, 1, 300), _oracle(oracle_lib, inp, g_o, g_S, qs), 1, 300, "no decay")
