@@ -96,12 +96,14 @@ def backward_flops(T, Hqk, Hv, n=CHUNK, d=D):
     return per * (T // n) * Hv
 
 
-def decode_bytes(B, Hqk, Hv, d=D):
-    """Compulsory HBM bytes of one decode step (state read + write dominate)."""
+def decode_bytes(B, Hqk, Hv, d=D, T=1):
+    """Compulsory HBM bytes of one decode call of T tokens per sequence: the
+    fp32 state read and written once, per token the q/k/v rows, o and the
+    gates, and the conv rows read and written once."""
     C_tot = 2 * Hqk * d + Hv * d
     state = 2 * B * Hv * d * d * 4
-    per_seq = 2 * (2 * Hqk * d + Hv * d) + 2 * Hv * d + 2 * 4 * Hv + 2 * 3 * C_tot * 2
-    return state + B * per_seq
+    per_tok = 2 * (2 * Hqk * d + Hv * d) + 2 * Hv * d + 2 * 4 * Hv
+    return state + B * (T * per_tok + 2 * 3 * C_tot * 2)
 
 
 # ---------------------------------------------------------------------------
@@ -388,8 +390,15 @@ def bench_decode_multi(hip, T=4, steps=32):
     hip.record(t1, sp)
     torch.cuda.synchronize()
     us = hip.ms(t0, t1) * 1e3 / steps
+    nbytes = decode_bytes(B, Hqk, Hv, T=T)
+    gbs = nbytes / (us * 1e-6) / 1e9
     return {"metric": f"multi-token decode (B=256, T={T} tokens per sequence per call, 16QK/48V)",
-            "us_per_call": us, "us_per_token_step": us / T, "tokens_per_s": B * T / (us * 1e-6)}
+            "us_per_call": us, "us_per_token_step": us / T, "tokens_per_s": B * T / (us * 1e-6),
+            "roofline": {"bound": "hbm", "kernel": "decode_head_kernel<4> + conv_shift_qk_kernel<4>",
+                         "achieved": gbs, "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": gbs * 1e9 / PEAK_HBM,
+                         "traffic": _sum_or_none(load_traffic("decode_multi", source_digest()),
+                                                 load_traffic("decode_multi_conv_shift", source_digest())),
+                         "algorithmic_bytes_per_launch": nbytes}}
 
 
 def bench_backward(hip, steps=10, warmup=3):
