@@ -198,8 +198,9 @@ size_t gdn_prefill_backward_workspace_size(int B, int T, int Hqk, int Hv, int dk
  *     L = sum_t <grad_o_t, o_t> + <grad_state_out, state_out>
  * with respect to every input, for B sequences of equal length T.  The
  * chunked form of the update (the WY / chunk-parallel evaluation of the
- * walkthrough's section 2.1; the FlashQLA announcement on the Qwen blog
- * describes forward and backward kernels of this chunked training form) is
+ * walkthrough's section 2.1; section 9 of the architecture deep dive on
+ * alwayszhang.cn describes FlashQLA's forward and backward kernels of this
+ * chunked training form) is
  * differentiated line by line; all arithmetic is fp32.
  *
  *   q, k, v, a, b, conv_w, conv_state_in, state_in, gate_scale, q_scale:

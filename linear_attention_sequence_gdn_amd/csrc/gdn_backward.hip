@@ -12,8 +12,9 @@
 //   O   = q_scale (diag(Gam) Q S + P Vn),        P = Q K^T * D, lower incl. diagonal
 //   S'  = Gam_n S + Ks^T Vn,                      Ks = diag(e^(gamma_n - gamma)) K
 // (the WY / chunk-parallel form of the update of the local-inference
-// walkthrough, section 2.1; the Qwen FlashQLA announcement describes forward
-// and backward kernels of this chunked form).  The backward applies the chain
+// walkthrough, section 2.1; section 9 of the architecture deep dive on
+// alwayszhang.cn describes FlashQLA's forward and backward kernels of this
+// chunked form).  The backward applies the chain
 // rule to each of these lines in reverse; the derivative of the inverse is
 // dL = -X^T dX X^T.  Everything here is fp32 on the vector ALUs.
 //

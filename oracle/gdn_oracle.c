@@ -43,10 +43,10 @@
  * conv rows, the initial state), by reverse-mode differentiation of the same
  * token-by-token definition, written out by hand: the state update is undone
  * step by step from the last token, and each step's local derivatives are the
- * chain rule applied to the five operations above.  The fast-weight update and
- * its chunked training form are the subject of the FlashQLA announcement
- * (Qwen blog, forward and backward kernels of the chunked form); no chunking
- * is used here.  All forward states of a (sequence, V head) are kept, so the
+ * chain rule applied to the five operations above.  Section 9 of the
+ * architecture deep dive (alwayszhang.cn) names forward and backward kernels
+ * of the chunked form (FlashQLA) as what training needs; no chunking is used
+ * here.  All forward states of a (sequence, V head) are kept, so the
  * backward is meant for test sizes.
  */
 #include <math.h>
