@@ -88,6 +88,28 @@ struct BwdWs {
 };
 
 __device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// Sequential-pass block id -> (sequence, V head, column block), so that the
+// G * kNCB blocks of one (sequence, QK group), which read the same k^ and q^
+// rows chunk after chunk, get ids of one residue mod 8: they run on the same
+// XCD (blocks are dealt to the eight XCDs round-robin) and share its L2.  A
+// tail of fewer than eight groups maps plainly.
+__device__ __forceinline__ void seq_block(const BwdArgs &p, int b, int &s, int &h, int &cb)
+{
+    const int G = p.Hv / p.Hqk, P = G * kNCB, N = gridDim.x;
+    const int full = N / (8 * P) * (8 * P);
+    int unit, member;
+    if (b < full) {
+        unit = 8 * ((b >> 3) / P) + (b & 7);
+        member = (b >> 3) % P;
+    } else {
+        unit = b / P;
+        member = b % P;
+    }
+    s = unit / p.Hqk;
+    h = (unit % p.Hqk) * G + member / kNCB;
+    cb = member % kNCB;
+}
 __device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 __device__ __forceinline__ void st4(float *p, float4 v) { *reinterpret_cast<float4 *>(p) = v; }
 
@@ -447,8 +469,9 @@ __global__ __launch_bounds__(kST) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
     __shared__ SeqTile L;
     __shared__ __attribute__((aligned(16))) float Ss[kD * kLC], Vs[64 * kLC], Vts[64 * kLC], Vns[64 * kLC];
     const int Hv = p.Hv, G = Hv / p.Hqk;
-    const int cb = blockIdx.x % kNCB, sh = blockIdx.x / kNCB, h = sh % Hv, s = sh / Hv, g = h / G;
-    const int col0 = cb * kCB;
+    int s, h, cb;
+    seq_block(p, blockIdx.x, s, h, cb);
+    const int g = h / G, col0 = cb * kCB;
     const int t = threadIdx.x, w = t >> 6, lane = t & 63, lr = lane & 15, lq = lane >> 4;
     const int srow = 16 * w + 4 * lq;                      // state rows srow .. srow + 3
     const int vrt = w >> 1, vrow = 16 * vrt + 4 * lq, vcol = 16 * (w & 1) + lr;  // slice tile
@@ -533,8 +556,9 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
     __shared__ __attribute__((aligned(16))) float Qs[64 * kLK], Ps[64 * kLN];
     __shared__ __attribute__((aligned(16))) float dSs[kD * kLC], dOs[64 * kLC], dVns[64 * kLC], dVts[64 * kLC];
     const int Hv = p.Hv, G = Hv / p.Hqk;
-    const int cb = blockIdx.x % kNCB, sh = blockIdx.x / kNCB, h = sh % Hv, s = sh / Hv, g = h / G;
-    const int col0 = cb * kCB;
+    int s, h, cb;
+    seq_block(p, blockIdx.x, s, h, cb);
+    const int g = h / G, col0 = cb * kCB;
     const int t = threadIdx.x, w = t >> 6, lane = t & 63, lr = lane & 15, lq = lane >> 4;
     const int srow = 16 * w + 4 * lq;
     const int vrt = w >> 1, vrow = 16 * vrt + 4 * lq, vcol = 16 * (w & 1) + lr;
