@@ -14,9 +14,10 @@
 // (the WY / chunk-parallel form of the update of the local-inference
 // walkthrough, section 2.1; section 9 of the architecture deep dive on
 // alwayszhang.cn describes FlashQLA's forward and backward kernels of this
-// chunked form).  The backward applies the chain
-// rule to each of these lines in reverse; the derivative of the inverse is
-// dL = -X^T dX X^T.  Everything here is fp32 on the vector ALUs.
+// chunked form).  The backward applies the chain rule to each of these
+// lines in reverse; the derivative of the inverse is dL = -X^T dX X^T.  All
+// arithmetic is fp32: the two sequential passes multiply on the fp32 matrix
+// cores, everything else on the vector ALUs.
 //
 // Passes (one launch each):
 //   bwd_setup_kernel   (packed calls) chunk and sequence tables from cu_seqlens
@@ -35,7 +36,8 @@
 //                      conv weight gradients
 //   bwd_dw_kernel      the conv weight gradient, summed over chunks in order
 // The state columns are independent in the update, so the two sequential
-// passes split them over four workgroups per (sequence, V head).
+// passes split them over four workgroups per (sequence, V head); the twelve
+// workgroups of one (sequence, QK group) run on one XCD and share its L2.
 #include "../../include/gdn.h"
 
 #include <hip/hip_runtime.h>
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs p, BwdWs ws)
 }
 
 // ---------------------------------------------------------------------------
-// 2. P and X = (I + A)^-1 per (chunk, V head)
+// 2. P and X = (I + A)^-1 per (chunk, QK group)
 // ---------------------------------------------------------------------------
 // Column of (I + A)^-1 for a strictly lower A (row stride kLN), y = e_c on
 // entry: right-looking substitution, expanded at compile time so that y
