@@ -743,7 +743,17 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __shared__ float Em[64 * kLN], Wm[64 * kLN], Ym[64 * kLN];
     __shared__ float gam[64], bet[64], eg[64], en[64], dgam[64], dbet[64], rowv[64], red[4];
     const int Hv = p.Hv, Hqk = p.Hqk, G = Hv / Hqk;
-    const int cidx = blockIdx.x / Hv, h = blockIdx.x % Hv, g = h / G;
+    // the G blocks of one (chunk, QK group), which read the same k^ and q^
+    // rows, get ids of one residue mod 8: the same XCD, one L2
+    int cidx, h;
+    {
+        const int b = blockIdx.x, full = (int)gridDim.x / (8 * G) * (8 * G);
+        const int unit = b < full ? 8 * ((b >> 3) / G) + (b & 7) : b / G;
+        const int member = b < full ? (b >> 3) % G : b % G;
+        cidx = unit / Hqk;
+        h = (unit % Hqk) * G + member;
+    }
+    const int g = h / G;
     const int4 ci = bchunk(p, ws, cidx);
     const int n = ci.z;
     if (n == 0) return;
