@@ -214,3 +214,27 @@ def test_backward_no_decay(oracle_lib):
     # gate_scale 0: alpha = 1 for every token, the state only accumulates writes
     inp, g_o, g_S, qs = _case(1, 300, 1, 2, seed=92, gate_scale=0.0)
     _compare(_gpu(inp, g_o, g_S, qs, 1, 300), _oracle(oracle_lib, inp, g_o, g_S, qs), 1, 300, "no decay")
+
+
+def test_backward_ignores_stale_workspace():
+    # a workspace full of NaN bit patterns (as a previous call or another user
+    # may leave it) gives the same gradients bit for bit: every region is
+    # written before it is read
+    import linear_attention_sequence_gdn_amd as gdn
+    import torch
+    B, T, Hqk, Hv = 1, 130, 2, 4
+    inp, g_o, g_S, qs = _case(B, T, Hqk, Hv, seed=95)
+    d = inp["d"]
+    args = (dev_bf16(inp["q"].reshape(B, T, Hqk, d)), dev_bf16(inp["k"].reshape(B, T, Hqk, d)),
+            dev_bf16(inp["v"].reshape(B, T, Hv, d)), dev_f32(inp["a"].reshape(B, T, Hv)),
+            dev_f32(inp["b"].reshape(B, T, Hv)), dev_bf16(inp["conv_w"]), dev_bf16(g_o.reshape(B, T, Hv, d)))
+    kw = dict(gate_scale=inp["gate_scale"], q_scale=qs, state_in=dev_f32(inp["state_in"]),
+              conv_state_in=dev_bf16(inp["conv_state_in"]), grad_state_out=dev_f32(g_S), want_conv_state=True)
+    need = gdn.gdn_prefill_backward_workspace_size(B, T, Hqk, Hv)
+    clean = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    dirty = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    a = gdn.gdn_prefill_backward(*args, workspace=clean, **kw)
+    b = gdn.gdn_prefill_backward(*args, workspace=dirty, **kw)
+    torch.cuda.synchronize()
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
