@@ -265,3 +265,29 @@ def test_config2_native_context_three_heads(oracle_lib):
     o_ref, s_ref, _ = oracle_prefill(x, heads=heads)
     check_output(og, o_ref[:, heads])
     check_state(sg, s_ref[:, heads])
+
+
+def test_stale_workspace_segmented():
+    """A workspace full of 0xFF bytes (as a previous call may leave it) gives
+    the same results bit for bit, in the case that uses the workspace most: a
+    sequence cut into segments, two of whose V heads do not decay, so that
+    the segment counters elect a workgroup for the in-order walk."""
+    import torch
+    import linear_attention_sequence_gdn_amd as gdn
+    T = 8192 + 37
+    x = inputs.make_prefill(T_list=[T], Hqk=2, Hv=6, seed=513, state_std=0.05, conv_state_std=1.0)
+    x["a"][:, :2] = -9.0
+    d = x["d"]
+    args = (dev_bf16(x["q"].reshape(1, T, 2, d)), dev_bf16(x["k"].reshape(1, T, 2, d)),
+            dev_bf16(x["v"].reshape(1, T, 6, d)), dev_f32(x["a"].reshape(1, T, 6)),
+            dev_f32(x["b"].reshape(1, T, 6)), dev_bf16(x["conv_w"]))
+    need = gdn.gdn_prefill_workspace_size(1, T, 2, 6)
+    outs = []
+    for fill in (0x00, 0xFF):
+        ws = torch.full((need,), fill, dtype=torch.uint8, device="cuda")
+        o, so, _ = gdn.gdn_prefill(*args, gate_scale=x["gate_scale"], state_in=dev_f32(x["state_in"]),
+                                   conv_state_in=dev_bf16(x["conv_state_in"]), workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((host_u16(o), so.cpu().numpy()))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])
