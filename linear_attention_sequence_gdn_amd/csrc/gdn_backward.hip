@@ -55,6 +55,7 @@ constexpr int kLN = 68;   // LDS row stride of 64 x 64 fp32 tiles
 constexpr int kLC = kCB;  // LDS row stride of kCB-column slices (read as broadcasts)
 constexpr int kNCB = kD / kCB;
 constexpr int kST = 512;  // threads of a sequential-pass workgroup: eight waves, two per SIMD
+constexpr int kSD = kNCB * (kST / 64);  // <dS', S> partials per (chunk, V head): one per wave
 
 struct BwdArgs {
     const uint16_t *q, *k, *v;
@@ -86,6 +87,8 @@ struct BwdWs {
     float *dvn, *dvh;   // [tok][Hv][128]   dVn, dVt = dv^
     float *dqp, *dkp;   // [tok][Hv][128]   dq^, dk^ of each V head
     float *dy;          // [tok][C_tot]     gradient of the conv outputs
+    float *sdot;        // [chunk][Hv][kSD] <dS', S> of each (column block, wave): state
+                        //                   gradient leaving the chunk, state entering it
     float *dwp;         // [chunk][C_tot][4] conv weight gradient of each chunk
 };
 
@@ -575,7 +578,18 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
     const int4 sq = bseq(p, ws, s);  // {first chunk slot, chunks, first token, length}
     const int nch = sq.y;
     SeqPref<true> f;
+    // this block's columns of the state entering a chunk, loaded one chunk
+    // ahead, for <dS', S> (the gate gradient's Gam_n S term)
+    float sv[8];
+    auto load_sv = [&](int c) {
+        const float *sc = ws.Sc + ((long)c * Hv + h) * kD * kD + col0;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sv[4 * ct + e] = sc[(long)(srow + e) * kD + 16 * ct + lr];
+    };
     if (nch > 0) {
+        load_sv(sq.x + nch - 1);
         seq_fetch<true>(p, ws, f, sq.x + nch - 1, sq.z + (long)(nch - 1) * kChunk, sq.w - (nch - 1) * kChunk, h, g,
                         col0);
         seq_commit<true>(p, f, L, Qs, Ps, dOs);
@@ -584,13 +598,18 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
         const int cidx = sq.x + j, n = min(kChunk, sq.w - j * kChunk);
         const long t0 = (long)sq.z + (long)j * kChunk;
         float *dsc = ws.dSc + ((long)cidx * Hv + h) * kD * kD + col0;
+        float part = 0.f;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 dsc[(long)(srow + e) * kD + 16 * ct + lr] = dS[ct][e];
                 dSs[(srow + e) * kLC + 16 * ct + lr] = dS[ct][e];
+                part = fmaf(dS[ct][e], sv[4 * ct + e], part);
             }
+        part = wave_sum(part);
+        if (lane == 0) ws.sdot[((long)cidx * Hv + h) * kSD + (kST / 64) * cb + w] = part;
+        if (j > 0) load_sv(cidx - 1);
         if (j > 0) seq_fetch<true>(p, ws, f, cidx - 1, t0 - kChunk, kChunk, h, g, col0);
         __syncthreads();
         // dVn = diag(en) K dS' + P^T dO'  (P^T upper: k >= 16 vrt)
@@ -741,7 +760,7 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 {
     __shared__ float sA[64 * 33], sB[32 * 129];
     __shared__ float Em[64 * kLN], Wm[64 * kLN], Ym[64 * kLN];
-    __shared__ float gam[64], bet[64], eg[64], en[64], dgam[64], dbet[64], rowv[64], red[4];
+    __shared__ float gam[64], bet[64], eg[64], en[64], dgam[64], dbet[64], rowv[64];
     const int Hv = p.Hv, Hqk = p.Hqk, G = Hv / Hqk;
     // the G blocks of one (chunk, QK group), which read the same k^ and q^
     // rows, get ids of one residue mod 8: the same XCD, one L2
@@ -864,21 +883,13 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (cc == 0) rowv[r0 + ri] = r0 + ri < n ? en[r0 + ri] * v : 0.f;
         }
     }
-    // <dS', S> for the Gam_n S term
-    {
-        float fr = 0.f;
-        for (int e = 0; e < 64; ++e) {
-            const int idx = t + kBT * e;
-            fr = fmaf(dSc[idx], Sc[idx], fr);
-        }
-        for (int off = 32; off >= 1; off >>= 1) fr += __shfl_xor(fr, off, 64);
-        if ((t & 63) == 0) red[t >> 6] = fr;
-    }
+    // <dS', S> for the Gam_n S term: the state-gradient pass left it per column block
     __syncthreads();
     if (t == 0) {
-        float tot = 0.f;
+        float tot = 0.f, sd = 0.f;
         for (int r = 0; r < n; ++r) tot += rowv[r];
-        dgam[n - 1] += tot + eg[n - 1] * (red[0] + red[1] + red[2] + red[3]);
+        for (int i = 0; i < kSD; ++i) sd += ws.sdot[((long)cidx * Hv + h) * kSD + i];
+        dgam[n - 1] += tot + eg[n - 1] * sd;
     }
     __syncthreads();
     if (t < n) dgam[t] -= rowv[t];
@@ -1203,7 +1214,7 @@ BwdLayout bwd_layout(int N, int T_tot, int max_chunks, int Hqk, int Hv)
                             tok * Hqk * kD, tok * Hqk * kD, tok * Hv * kD, tok * Hv, tok * Hv,
                             chunks * Hv * 4096, chunks * Hv * 4096, chunks * Hv * kD * kD, chunks * Hv * kD * kD,
                             tok * Hv * kD, tok * Hv * kD, tok * Hv * kD, tok * Hv * kD, tok * Hv * kD,
-                            tok * Hv * kD, tok * C_tot, chunks * C_tot * 4, 0};
+                            tok * Hv * kD, tok * C_tot, chunks * C_tot * 4, chunks * Hv * kSD};
     BwdLayout L{};
     long o = 0;
     for (int i = 0; i < 20; ++i) {
@@ -1256,8 +1267,8 @@ hipError_t launch_backward(const uint16_t *q, const uint16_t *k, const uint16_t 
         ws.chunk_info = reinterpret_cast<int4 *>(base + L.off[0]);
         ws.seq_info = reinterpret_cast<int4 *>(base + L.off[1]);
         float **slots[18] = {&ws.qh, &ws.kh, &ws.vh, &ws.gam, &ws.beta, &ws.X, &ws.P, &ws.Sc, &ws.dSc,
-                             &ws.vt, &ws.vn, &ws.dvn, &ws.dvh, &ws.dqp, &ws.dkp, &ws.dy, &ws.dwp, nullptr};
-        for (int i = 0; i < 17; ++i) *slots[i] = base + L.off[i + 2];
+                             &ws.vt, &ws.vn, &ws.dvn, &ws.dvh, &ws.dqp, &ws.dkp, &ws.dy, &ws.dwp, &ws.sdot};
+        for (int i = 0; i < 18; ++i) *slots[i] = base + L.off[i + 2];
     } else {
         p.cu_seqlens = nullptr;  // nothing to tabulate: every sequence is empty
         p.T = 0;
