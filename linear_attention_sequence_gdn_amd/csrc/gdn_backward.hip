@@ -1027,25 +1027,33 @@ __global__ __launch_bounds__(kBT) void bwd_dy_kernel(BwdArgs p, BwdWs ws)
     for (int i = 0; i < 4; ++i) w[i] = bf16_to_f32(p.conv_w[(P.ch0 + c) * 4 + i]);
     float xw[kWin];
     x_window(p, P, x, s, seq0, j * kChunk + rb, L, c, C_tot, xw);
+    // the 32 rows' gradient loads are issued together: rows past the chunk's
+    // end read its last row (in bounds) and are not used
+    const long hs = (long)p.Hv * kD;
     if (P.kind == 2) {
+        const float *gv = ws.dvh + t0 * hs + (long)P.head * kD + c;
+        float gr[32];
 #pragma unroll
-        for (int r = 0; r < 32; ++r) {
-            if (rb + r < n) {
-                const long tok = t0 + rb + r;
-                ws.dy[tok * C_tot + P.ch0 + c] = ws.dvh[(tok * p.Hv + P.head) * kD + c] * silu_grad(conv_at(w, xw, r));
-            }
-        }
+        for (int r = 0; r < 32; ++r) gr[r] = gv[min(rb + r, n - 1) * hs];
+#pragma unroll
+        for (int r = 0; r < 32; ++r)
+            if (rb + r < n) ws.dy[(t0 + rb + r) * C_tot + P.ch0 + c] = gr[r] * silu_grad(conv_at(w, xw, r));
         return;
     }
-    const float *part = P.kind == 0 ? ws.dqp : ws.dkp;
+    float dsum[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) dsum[r] = 0.f;
+    for (int jh = 0; jh < G; ++jh) {
+        const float *pj = (P.kind == 0 ? ws.dqp : ws.dkp) + t0 * hs + (long)(P.head * G + jh) * kD + c;
+#pragma unroll
+        for (int r = 0; r < 32; ++r) dsum[r] += pj[min(rb + r, n - 1) * hs];
+    }
 #pragma unroll
     for (int r = 0; r < 32; ++r) {
         if (rb + r < n) {
             const float y = conv_at(w, xw, r);
             zs[(rb + r) * kLK + c] = y * sigm(y);
-            float d = 0.f;
-            for (int jh = 0; jh < G; ++jh) d += part[((t0 + rb + r) * p.Hv + P.head * G + jh) * kD + c];
-            ds[(rb + r) * kLK + c] = d;
+            ds[(rb + r) * kLK + c] = dsum[r];
         }
     }
     __syncthreads();
