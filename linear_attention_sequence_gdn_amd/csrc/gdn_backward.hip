@@ -163,12 +163,17 @@ constexpr int kWin = 35;
 __device__ __forceinline__ void x_window(const BwdArgs &p, const Plane &P, const uint16_t *x, int s, long seq0,
                                          int tb, int L, int c, long C_tot, float (&xw)[kWin])
 {
+    // all rows are loaded first, clamped into the sequence, so that the loads
+    // are in flight together; rows outside it are then replaced
+    uint16_t raw[kWin];
+#pragma unroll
+    for (int i = 0; i < kWin; ++i) raw[i] = x[(seq0 + min(max(tb - 3 + i, 0), L - 1)) * P.ld + c];
 #pragma unroll
     for (int i = 0; i < kWin; ++i) {
         const int tau = tb - 3 + i;
         float v = 0.f;
         if (tau >= 0 && tau < L)
-            v = bf16_to_f32(x[(seq0 + tau) * P.ld + c]);
+            v = bf16_to_f32(raw[i]);
         else if (tau < 0 && p.conv_state_in)
             v = bf16_to_f32(p.conv_state_in[((long)s * 3 + 3 + tau) * C_tot + P.ch0 + c]);
         xw[i] = v;
@@ -1116,7 +1121,9 @@ __global__ __launch_bounds__(kBT) void bwd_conv_kernel(BwdArgs p, BwdWs ws)
     const float *dy = ws.dy + seq0 * C_tot + ch;
     float dw[kWin], xw[kWin];
 #pragma unroll
-    for (int i = 0; i < kWin; ++i) dw[i] = tb + i < L ? dy[(long)(tb + i) * C_tot] : 0.f;
+    for (int i = 0; i < kWin; ++i) dw[i] = dy[(long)min(tb + i, L - 1) * C_tot];
+#pragma unroll
+    for (int i = 0; i < kWin; ++i) dw[i] = tb + i < L ? dw[i] : 0.f;
     x_window(p, P, x, s, seq0, tb, L, c, C_tot, xw);
     float gw[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
