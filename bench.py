@@ -4,13 +4,17 @@
 A step is one chunked prefill of the model-layer workload (B = 1, T = 8192,
 16 QK / 48 V heads, d = 128, seeded synthetic bf16 inputs already resident in
 HBM).  The decode workload (B = 256 sequences, 64 consecutive in-place steps)
-is timed in the same run and reported under "decode", and the training
-backward of the prefill workload under "backward".  Prints ONE JSON line.
+is timed in the same run and reported under "decode", the training backward
+of the prefill workload under "backward", and the other prefill workloads
+(the tiny 2 QK / 6 V one, the 262,144-token one, the 64-sequence packed one)
+under "configs".  Prints ONE JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                  [--calibrate-copy]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS]
+                  [--no-cpu-baseline] [--only LEG ...] [--calibrate-copy]
   python bench.py --traffic-report FETCH_CSV WRITE_CSV
 
+--only restricts the run to some legs (prefill, decode, decode_multi,
+backward, configs), for profiling; the JSON line then holds those legs.
 --calibrate-copy ends the run with a plain 256 MiB device-to-device copy, so
 that a rocprofv3 --pmc pass over this command also reads its counters for a
 transfer of known size.  --traffic-report turns two such passes (FETCH_SIZE,
@@ -19,18 +23,21 @@ launch of each kernel, scaled by what the counters read for the copy, and
 writes them to profiles/traffic.json tagged with the digest of the kernel
 sources they were taken on.
 
-Timing: HIP events on the stream the library launches on.  The step time is
-K plain gdn_prefill calls between two events; the same K steps are then run
-through gdn_prefill_with_events, which records an event after each of its
-kernels (chunk-table setup, parallel pass, sequential pass), for the
-per-kernel times the roofline uses.  Each recorded event costs the stream a
-few microseconds; the interval before the first kernel, empty for a uniform
-batch, measures that cost, and it is subtracted from the kernels' intervals
-(the raw intervals are reported too).  The default 200 warm-up steps (about
-70 ms of GPU work) let the clocks settle: after 30 the prefill still runs
-about 10 % slower.  The 64 decode steps run back to back between two
-events.  The CPU baseline is the fp64 oracle, as it stands, on a bounded
-sample of the same prefill workload.
+Timing: HIP events on the stream the library launches on.  Before anything is
+timed, each leg runs its own work back to back until at least --settle-ms of
+GPU time (default 400 ms) has passed, whatever --warmup says: the GPU's
+clocks ramp up under load, and a prefill timed after 30 steps (5 ms) ran
+about 10 % slower than one timed after 200.  The step time is K plain
+gdn_prefill calls between two events; the same K steps are then run through
+gdn_prefill_with_events, which records an event after each of its kernels
+(chunk-table setup, parallel pass, sequential pass), for the per-kernel times
+the roofline uses.  Each recorded event costs the stream a few microseconds;
+the interval before the first kernel, empty for a uniform batch, measures
+that cost, and it is subtracted from the kernels' intervals (the raw
+intervals are reported too).  The 64 decode steps run back to back between
+two events.  The GPU's shader clock is sampled from the driver while the legs
+run.  The CPU baselines are the fp64 oracle, as it stands, on bounded samples
+of the same workloads.
 """
 import argparse
 import ctypes
@@ -71,6 +78,21 @@ def prefill_flops(T, Hqk, Hv, n=CHUNK, d=D):
     prep = chunks * (Hqk * 4 * n * n * d + Hv * n ** 3 / 3)
     chain = chunks * Hv * (6 * n * d * d + 4 * n * n * d)
     return prep, chain
+
+
+def method_flops(lengths, Hqk, Hv, n=CHUNK, d=D):
+    """Algorithmic FLOP of the chunked method over sequences of the given
+    lengths, C fixed at 64 and a partial last chunk counted with its own n:
+    per chunk and V head 6 n d^2 (W S, K^T Vnew, Q S) + 6 n^2 d (W, U', P
+    Vnew) + n^3 / 3 (the triangular inverse); per chunk and QK head 4 n^2 d
+    (K K^T, Q K^T).  7,667,712 FLOP per token at 16 QK / 48 V heads."""
+    total = 0.0
+    for L in lengths:
+        L = int(L)
+        full, rem = divmod(L, n)
+        for m, cnt in ((n, full), (rem, 1 if rem else 0)):
+            total += cnt * (Hv * (6 * m * d * d + 6 * m * m * d + m ** 3 / 3) + Hqk * 4 * m * m * d)
+    return total
 
 
 def prefill_bytes(T, Hqk, Hv, d=D):
@@ -134,6 +156,94 @@ class Hip:
         out = ctypes.c_float()
         assert self.L.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
         return float(out.value)
+
+
+def settle(hip, stream, work, settle_ms, batch=20):
+    """Run `work` back to back, `batch` calls between two events, until at
+    least settle_ms of GPU time has passed (the clocks ramp up under load).
+    Returns (GPU ms spent, calls made)."""
+    spent, calls = 0.0, 0
+    t0, t1 = hip.event(), hip.event()
+    while spent < settle_ms:
+        hip.record(t0, stream)
+        for _ in range(batch):
+            work()
+        hip.record(t1, stream)
+        spent += hip.ms(t0, t1)
+        calls += batch
+    return spent, calls
+
+
+class ClockSampler:
+    """Samples the GPU's shader clock (MHz) from the driver in a background
+    thread while legs run: the amdgpu sysfs DPM table where it is readable,
+    else rocm-smi.  Reports None where neither answers."""
+
+    def __init__(self, period_s=0.05):
+        import threading
+        self.samples = []
+        self.source = None
+        self._stop = threading.Event()
+        self._sysfs = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self._thread = threading.Thread(target=self._run, args=(period_s,), daemon=True)
+
+    def _read(self):
+        import re
+        import subprocess
+        for path in self._sysfs:
+            try:
+                for line in open(path):
+                    if line.rstrip().endswith("*"):
+                        m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                        if m:
+                            self.source = "sysfs pp_dpm_sclk"
+                            return float(m.group(1))
+            except OSError:
+                pass
+        try:
+            out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
+                                 timeout=10).stdout
+            m = re.search(r"sclk.*?\((\d+)\s*[Mm][Hh]z\)", out)
+            if m:
+                self.source = "rocm-smi --showclocks"
+                return float(m.group(1))
+        except (OSError, subprocess.SubprocessError):
+            pass
+        return None
+
+    def _run(self, period_s):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is None:
+                return
+            self.samples.append(v)
+            self._stop.wait(period_s if self.source and self.source.startswith("sysfs") else 1.0)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=15)
+
+    def summary(self):
+        if not self.samples:
+            return None
+        xs = sorted(self.samples)
+        return {"sclk_mhz_median": xs[len(xs) // 2], "sclk_mhz_max": xs[-1], "samples": len(xs),
+                "source": self.source}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or None
 
 
 # kernel sources behind each group of measured kernels
@@ -238,7 +348,7 @@ def load_traffic(name, digest):
 
 
 # ---------------------------------------------------------------------------
-def bench_prefill(hip, steps, warmup):
+def bench_prefill(hip, steps, warmup, settle_ms):
     import torch
     import linear_attention_sequence_gdn_amd as gdn
     from linear_attention_sequence_gdn_amd import inputs
@@ -287,6 +397,7 @@ def bench_prefill(hip, steps, warmup):
     for _ in range(warmup):
         run()
         run(warm)
+    settle_gpu_ms, settle_calls = settle(hip, sp, run, settle_ms)
     torch.cuda.synchronize()
     # the step time: plain calls, nothing recorded between the kernels
     t0, t1 = hip.event(), hip.event()
@@ -307,10 +418,11 @@ def bench_prefill(hip, steps, warmup):
         for i, name in enumerate(PREFILL_KERNELS):
             stage[name] += hip.ms(ev[i], ev[i + 1])
     stage = {k_: v_ / steps for k_, v_ in stage.items()}
-    return dict(ms_per_step=total_ms / steps, stage_ms=stage, T=T, Hqk=Hqk, Hv=Hv)
+    return dict(ms_per_step=total_ms / steps, stage_ms=stage, T=T, Hqk=Hqk, Hv=Hv,
+                settle_gpu_ms=settle_gpu_ms, settle_calls=settle_calls + warmup)
 
 
-def bench_decode(hip, steps=64):
+def bench_decode(hip, settle_ms, steps=64):
     import numpy as np
     import torch
     import linear_attention_sequence_gdn_amd as gdn
@@ -342,6 +454,8 @@ def bench_decode(hip, steps=64):
 
     for i in range(16):  # warm-up, then restore the initial state
         step(i)
+    it = iter(range(1 << 30))
+    settle(hip, sp, lambda: step(next(it) % steps), settle_ms, batch=64)
     torch.cuda.synchronize()
     conv.copy_(conv0)
     st.copy_(st0)
@@ -357,7 +471,7 @@ def bench_decode(hip, steps=64):
     return dict(us_per_step=hip.ms(t0, t1) * 1e3 / steps, B=B, Hqk=Hqk, Hv=Hv, steps=steps)
 
 
-def bench_decode_multi(hip, T=4, steps=32):
+def bench_decode_multi(hip, settle_ms, T=4, steps=32):
     """B = 256 sequences, T tokens each per call (multi-token decode): the
     state is read and written once per call, so the per-token cost falls."""
     import numpy as np
@@ -379,10 +493,10 @@ def bench_decode_multi(hip, T=4, steps=32):
     conv = torch.from_numpy(x["conv_state"].view(np.int16)).view(torch.bfloat16).cuda()
     st = torch.from_numpy(x["state"]).cuda()
     o = torch.empty((B, T, Hv, D), dtype=torch.bfloat16, device="cuda")
-    for _ in range(4):
-        gdn.gdn_decode_multi(q, k, v, a, b, w, conv, st, o=o, gate_scale=c["gate_scale"])
-    torch.cuda.synchronize()
     sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    settle(hip, sp, lambda: gdn.gdn_decode_multi(q, k, v, a, b, w, conv, st, o=o, gate_scale=c["gate_scale"]),
+           settle_ms, batch=16)
+    torch.cuda.synchronize()
     t0, t1 = hip.event(), hip.event()
     hip.record(t0, sp)
     for _ in range(steps):
@@ -401,7 +515,7 @@ def bench_decode_multi(hip, T=4, steps=32):
                          "algorithmic_bytes_per_launch": nbytes}}
 
 
-def bench_backward(hip, steps=10, warmup=3):
+def bench_backward(hip, settle_ms, steps=10, warmup=3):
     """gdn_prefill_backward on the prefill workload (same seeded inputs, a
     seeded bf16 output gradient and final-state gradient), K calls between
     two events."""
@@ -422,10 +536,11 @@ def bench_backward(hip, steps=10, warmup=3):
             f32(x["a"].reshape(B, T, Hv)), f32(x["b"].reshape(B, T, Hv)), bf(x["conv_w"]), g_o)
     ws = torch.empty(gdn.gdn_prefill_backward_workspace_size(B, T, Hqk, Hv), dtype=torch.uint8, device="cuda")
     run = lambda: gdn.gdn_prefill_backward(*args, gate_scale=c["gate_scale"], grad_state_out=g_S, workspace=ws)
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     for _ in range(warmup):
         run()
+    settle(hip, sp, run, settle_ms, batch=4)
     torch.cuda.synchronize()
-    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     t0, t1 = hip.event(), hip.event()
     hip.record(t0, sp)
     for _ in range(steps):
@@ -440,6 +555,102 @@ def bench_backward(hip, steps=10, warmup=3):
             "roofline": {"bound": "alu", "kernel": "whole backward (eight launches)", "achieved": tf,
                          "peak": PEAK_VALU_F32 / 1e12, "unit": "TFLOP/s", "frac": tf * 1e12 / PEAK_VALU_F32,
                          "traffic": None, "algorithmic_flop_per_call": flop}}
+
+
+def bench_config(hip, idx, settle_ms, steps):
+    """One of the other prefill workloads, timed as the step is: the tiny
+    2 QK / 6 V prefill (T = 512), the native-context prefill (T = 262,144,
+    long memory) and the packed batch of 64 sequences (log-uniform lengths
+    128..32768, nonzero initial states).  Whole calls between two events."""
+    import numpy as np
+    import torch
+    import linear_attention_sequence_gdn_amd as gdn
+    from linear_attention_sequence_gdn_amd import inputs
+
+    x = inputs.make_config(idx)
+    Hqk, Hv, N, T_tot = x["Hqk"], x["Hv"], x["N"], x["T_tot"]
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    lengths = np.diff(x["cu_seqlens"])
+    uniform = idx != 4
+    st = None if x["state_in"] is None else f32(x["state_in"])
+    w = bf(x["conv_w"])
+    if uniform:
+        T = int(lengths[0])
+        args = (bf(x["q"].reshape(N, T, Hqk, D)), bf(x["k"].reshape(N, T, Hqk, D)), bf(x["v"].reshape(N, T, Hv, D)),
+                f32(x["a"].reshape(N, T, Hv)), f32(x["b"].reshape(N, T, Hv)), w)
+        need = gdn.gdn_prefill_workspace_size(N, T, Hqk, Hv)
+    else:
+        args = (bf(x["q"]), bf(x["k"]), bf(x["v"]), f32(x["a"]), f32(x["b"]), w,
+                torch.from_numpy(x["cu_seqlens"]).cuda())
+        need = gdn.gdn_prefill_varlen_workspace_size(N, T_tot, Hqk, Hv)
+    del x
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    so = torch.empty((N, Hv, D, D), dtype=torch.float32, device="cuda")
+    o = torch.empty((T_tot * Hv * D,), dtype=torch.bfloat16, device="cuda")
+    o = o.view(N, -1, Hv, D) if uniform else o.view(T_tot, Hv, D)
+    fn = gdn.gdn_prefill if uniform else gdn.gdn_prefill_varlen
+    gs = inputs.CONFIGS[idx]["gate_scale"]
+    run = lambda: fn(*args, gate_scale=gs, state_in=st, state_out=so, o=o, workspace=ws)
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    run()
+    settle(hip, sp, run, settle_ms, batch=max(1, min(20, int(20 * 8192 / max(T_tot, 1)))))
+    k = max(3, min(steps, int(steps * 8192 * 4 / max(T_tot, 1))))
+    t0, t1 = hip.event(), hip.event()
+    hip.record(t0, sp)
+    for _ in range(k):
+        run()
+    hip.record(t1, sp)
+    torch.cuda.synchronize()
+    ms = hip.ms(t0, t1) / k
+    flop = method_flops(lengths, Hqk, Hv)
+    names = {0: "tiny_prefill_T512_2qk_6v", 2: "native_context_prefill_T262144_16qk_48v",
+             4: "varlen_prefill_64seq_16qk_48v"}
+    return {"workload": names[idx], "tokens": int(T_tot), "sequences": int(N), "ms_per_call": ms, "calls": k,
+            "tokens_per_s": T_tot / (ms * 1e-3), "algorithmic_flop": flop,
+            "mfma_frac": flop / (ms * 1e-3) / PEAK_MFMA_F16}
+
+
+def cpu_baseline_config(idx, min_seconds=4.0, max_reps=20):
+    """The oracle on a bounded sample of config idx's workload."""
+    import numpy as np
+    import oracle
+    from linear_attention_sequence_gdn_amd import inputs
+    oracle.build(force=False)
+    c = inputs.CONFIGS[idx]
+    heads = None
+    if idx == 2:  # the first 16384 tokens, V heads 0, 23, 47 (the parity test's heads)
+        x = inputs.make_config(2, heads=[0, 23, 47], qk_heads=[0, 7, 15], T_override=16384)
+        heads = [0, 23, 47]
+        what = "first 16384 tokens of the T=262144 workload, V heads 0, 23, 47 (3 of 48)"
+    elif idx == 4:  # four of the 64 packed sequences
+        full = inputs.make_config(4)
+        cu = full["cu_seqlens"]
+        pick = [3, 17, 40, 63]
+        idxs = np.concatenate([np.arange(cu[s_], cu[s_ + 1]) for s_ in pick])
+        x = dict(full)
+        for key in ("q", "k", "v", "a", "b"):
+            x[key] = np.ascontiguousarray(full[key][idxs])
+        L = np.diff(cu)[pick]
+        x["cu_seqlens"] = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+        x["state_in"] = np.ascontiguousarray(full["state_in"][pick])
+        del full
+        what = f"sequences 3, 17, 40, 63 of the 64-sequence packed workload ({int(L.sum())} tokens), all heads"
+    else:
+        x = inputs.make_config(idx)
+        what = "the whole workload"
+    T = int(x["cu_seqlens"][-1])
+    reps, t0 = 0, time.perf_counter()
+    while reps < max_reps:
+        oracle.prefill(x["q"], x["k"], x["v"], x["a"], x["b"], x["conv_w"], x["cu_seqlens"], Hqk=c["Hqk"],
+                       Hv=c["Hv"], gate_scale=c["gate_scale"], state_in=x["state_in"], heads=heads)
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    threads = oracle.num_threads() if heads is None else min(oracle.num_threads(), len(heads))
+    return {"value": T * reps / dt, "unit": "tokens/s" + (" (3 of 48 V heads)" if heads else ""),
+            "cores": threads, "kind": "oracle", "sample": f"fp64 oracle on {what}; {reps} run(s) in {dt:.1f} s wall"}
 
 
 def cpu_baseline(min_seconds=12.0, max_reps=60):
@@ -488,12 +699,17 @@ def cpu_baseline_backward(T_sample=1024, min_seconds=4.0, max_reps=20):
                       f"16QK/48V, parallel over the 16 QK groups; {reps} run(s) in {dt:.1f} s wall"}
 
 
+LEGS = ("prefill", "decode", "decode_multi", "backward", "configs")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--settle-ms", type=float, default=400.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", nargs="+", choices=LEGS)
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--traffic-report", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
@@ -512,81 +728,91 @@ def main():
     gdn.lib()
     hip = Hip()
     digest = source_digest()
+    legs = set(args.only or LEGS)
+    settle_ms = args.settle_ms
 
-    pf = bench_prefill(hip, args.steps, args.warmup)
-    dc = bench_decode(hip)
-    dm = bench_decode_multi(hip)
-    bw = bench_backward(hip)
-    bw["roofline"]["traffic"] = _sum_or_none(*(load_traffic("backward_" + k_[4:-7], source_digest(BWD_SOURCES))
-                                               for k_ in BWD_KERNELS))
-    T, Hqk, Hv = pf["T"], pf["Hqk"], pf["Hv"]
-    flop_prep, flop_chain = prefill_flops(T, Hqk, Hv)
-    tok_s = T / (pf["ms_per_step"] * 1e-3)
-
-    # dominant prefill kernel (the longer of the two that carry the matrix
-    # products), priced against the fp16 dense matrix-core peak
-    # Each recorded event costs the stream about as much as the interval
-    # before the first kernel, which is empty here (a uniform batch launches
-    # no setup kernel); it is subtracted from the kernels' intervals.
-    raw = pf["stage_ms"]
-    event_ms = raw["setup_kernel"]
-    km = {k_: max(v_ - event_ms, 0.0) for k_, v_ in raw.items() if k_ != "setup_kernel"}
-    dom = "chain_kernel" if km["chain_kernel"] >= km["prep_kernel"] else "prep_kernel"
-    dom_flop = flop_chain if dom == "chain_kernel" else flop_prep
-    dom_ms = km[dom]
-    achieved = dom_flop / (dom_ms * 1e-3) / 1e12
-    roof = {"bound": "mfma", "kernel": dom, "achieved": achieved,
-            "peak": PEAK_MFMA_F16 / 1e12, "unit": "TFLOP/s", "frac": achieved * 1e12 / PEAK_MFMA_F16,
-            "traffic": load_traffic("prefill_chain" if dom == "chain_kernel" else "prefill_prep", digest),
-            "algorithmic_flop_per_launch": dom_flop, "avg_launch_ms": dom_ms}
-    path_flop = flop_prep + flop_chain
-    dec_bytes = decode_bytes(dc["B"], dc["Hqk"], dc["Hv"])
-    dec_gbs = dec_bytes / (dc["us_per_step"] * 1e-6) / 1e9
-    line = {
-        "metric": METRIC,
-        "value": tok_s,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": pf["ms_per_step"],
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f16 MFMA operands, f32 accumulate/state, bf16 I/O",
-        "data": "synthetic (seeded, inputs resident in HBM)",
-        "config": {"workload": "layer_prefill_T8192_16qk_48v", "B": 1, "T": T, "Hqk": Hqk, "Hv": Hv,
-                   "d": D, "chunk": CHUNK, "seed": 1001},
-        "roofline": roof,
-        "path": {"algorithmic_flop": path_flop,
-                 "mfma_frac": path_flop / (pf["ms_per_step"] * 1e-3) / PEAK_MFMA_F16,
-                 "compulsory_bytes": prefill_bytes(T, Hqk, Hv),
-                 "hbm_frac": prefill_bytes(T, Hqk, Hv) / (pf["ms_per_step"] * 1e-3) / PEAK_HBM,
-                 "kernel_ms": km,
-                 "event_intervals_ms": raw,
-                 "other_kernel": {"kernel": "prep_kernel" if dom == "chain_kernel" else "chain_kernel",
-                                  "tflops": (flop_prep if dom == "chain_kernel" else flop_chain) /
-                                  (km["prep_kernel" if dom == "chain_kernel" else "chain_kernel"] * 1e-3) / 1e12}},
-        "decode": {"metric": "decode us/step (B=256, 16QK/48V, 64 in-place steps)",
-                   "value": dc["us_per_step"], "unit": "us/step", "higher_is_better": False,
-                   "roofline": {"bound": "hbm", "kernel": "decode step (decode_step_kernel + conv_shift_qk_kernel<1>)",
-                                "achieved": dec_gbs, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                                "frac": dec_gbs * 1e9 / PEAK_HBM,
-                                "traffic": _sum_or_none(load_traffic("decode", digest),
-                                                        load_traffic("decode_conv_shift", digest)),
-                                "algorithmic_bytes_per_launch": dec_bytes}},
-        "decode_multi": dm,
-        "backward": bw,
-        "source_digest": digest,
-    }
+    line = {"metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f16 MFMA operands, f32 accumulate/state, bf16 I/O",
+            "data": "synthetic (seeded, inputs resident in HBM)",
+            "config": {"workload": "layer_prefill_T8192_16qk_48v", "B": 1, "T": 8192, "Hqk": 16, "Hv": 48,
+                       "d": D, "chunk": CHUNK, "seed": 1001}}
+    with ClockSampler() as clock:
+        if "prefill" in legs:
+            pf = bench_prefill(hip, args.steps, args.warmup, settle_ms)
+            T, Hqk, Hv = pf["T"], pf["Hqk"], pf["Hv"]
+            flop_prep, flop_chain = prefill_flops(T, Hqk, Hv)
+            # dominant prefill kernel (the longer of the two that carry the
+            # matrix products), priced against the fp16 dense matrix-core
+            # peak.  Each recorded event costs the stream about as much as
+            # the interval before the first kernel, which is empty here (a
+            # uniform batch launches no setup kernel); it is subtracted from
+            # the kernels' intervals.
+            raw = pf["stage_ms"]
+            event_ms = raw["setup_kernel"]
+            km = {k_: max(v_ - event_ms, 0.0) for k_, v_ in raw.items() if k_ != "setup_kernel"}
+            dom = "chain_kernel" if km["chain_kernel"] >= km["prep_kernel"] else "prep_kernel"
+            other = "prep_kernel" if dom == "chain_kernel" else "chain_kernel"
+            kflop = {"chain_kernel": flop_chain, "prep_kernel": flop_prep}
+            achieved = kflop[dom] / (km[dom] * 1e-3) / 1e12
+            path_flop = method_flops([T], Hqk, Hv)
+            line.update({
+                "value": T / (pf["ms_per_step"] * 1e-3),
+                "ms_per_step": pf["ms_per_step"],
+                "warmup_gpu_ms": pf["settle_gpu_ms"],
+                "warmup_steps_run": pf["settle_calls"],
+                "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved,
+                             "peak": PEAK_MFMA_F16 / 1e12, "unit": "TFLOP/s",
+                             "frac": achieved * 1e12 / PEAK_MFMA_F16,
+                             "traffic": load_traffic("prefill_chain" if dom == "chain_kernel" else "prefill_prep",
+                                                     digest),
+                             "algorithmic_flop_per_launch": kflop[dom], "avg_launch_ms": km[dom]},
+                "path": {"algorithmic_flop": path_flop,
+                         "mfma_frac": path_flop / (pf["ms_per_step"] * 1e-3) / PEAK_MFMA_F16,
+                         "compulsory_bytes": prefill_bytes(T, Hqk, Hv),
+                         "hbm_frac": prefill_bytes(T, Hqk, Hv) / (pf["ms_per_step"] * 1e-3) / PEAK_HBM,
+                         "kernel_ms": km, "event_intervals_ms": raw,
+                         "other_kernel": {"kernel": other,
+                                          "tflops": kflop[other] / (km[other] * 1e-3) / 1e12}}})
+        if "decode" in legs:
+            dc = bench_decode(hip, settle_ms)
+            dec_bytes = decode_bytes(dc["B"], dc["Hqk"], dc["Hv"])
+            dec_gbs = dec_bytes / (dc["us_per_step"] * 1e-6) / 1e9
+            line["decode"] = {
+                "metric": "decode us/step (B=256, 16QK/48V, 64 in-place steps)",
+                "value": dc["us_per_step"], "unit": "us/step", "higher_is_better": False,
+                "roofline": {"bound": "hbm", "kernel": "decode step (decode_step_kernel + conv_shift_qk_kernel<1>)",
+                             "achieved": dec_gbs, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                             "frac": dec_gbs * 1e9 / PEAK_HBM,
+                             "traffic": _sum_or_none(load_traffic("decode", digest),
+                                                     load_traffic("decode_conv_shift", digest)),
+                             "algorithmic_bytes_per_launch": dec_bytes}}
+        if "decode_multi" in legs:
+            line["decode_multi"] = bench_decode_multi(hip, settle_ms)
+        if "backward" in legs:
+            bw = bench_backward(hip, settle_ms)
+            bw["roofline"]["traffic"] = _sum_or_none(
+                *(load_traffic("backward_" + k_[4:-7], source_digest(BWD_SOURCES)) for k_ in BWD_KERNELS))
+            line["backward"] = bw
+        if "configs" in legs:
+            line["configs"] = {str(i): bench_config(hip, i, settle_ms, args.steps) for i in (0, 2, 4)}
+    line["gpu_clock"] = clock.summary()
+    line["source_digest"] = digest
     if args.calibrate_copy:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline()
-        line["backward"]["cpu_baseline"] = cpu_baseline_backward()
+        if "prefill" in legs:
+            line["cpu_baseline"] = cpu_baseline()
+            line["cpu_baseline"]["cpu_model"] = cpu_model()
+        if "backward" in legs:
+            line["backward"]["cpu_baseline"] = cpu_baseline_backward()
+        if "configs" in legs:
+            for i in (0, 2, 4):
+                line["configs"][str(i)]["cpu_baseline"] = cpu_baseline_config(i)
+    line["cpu_model"] = cpu_model()
     print(json.dumps(line), flush=True)
 
 

@@ -79,7 +79,9 @@ size_t gdn_prefill_workspace_size(int B, int T, int Hqk, int Hv, int dk, int dv)
  *                  (in place), any other overlap is undefined
  *   o              [B][T][Hv][dv] bf16 output (round to nearest even)
  *   workspace      device scratch of >= gdn_prefill_workspace_size(...) bytes,
- *                  256-byte aligned; its contents on entry are irrelevant
+ *                  16-byte aligned (a misaligned one is rejected with
+ *                  GDN_ERR_INVALID_ARGUMENT); its contents on entry are
+ *                  irrelevant
  * T = 0 copies state_in to state_out (zeros if state_in is NULL).
  */
 int gdn_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -114,9 +116,13 @@ int gdn_prefill_with_events(const uint16_t *q, const uint16_t *k, const uint16_t
 size_t gdn_prefill_varlen_workspace_size(int N, int T_tot, int Hqk, int Hv, int dk, int dv);
 
 /*
- * Packed variable-length prefill with state carry-in (continuation of a
- * prefix: chunked prefill and prefix caching in serving engines hand over the
- * state and the conv rows).  Same as gdn_prefill, except:
+ * Packed variable-length prefill with state carry-in: the continuation of a
+ * prefix.  The local-inference walkthrough (bjdmk.com.cn) serves the model
+ * with chunked prefill and prefix caching switched on (section 3, the engine
+ * configuration; section 5, chunked prefill against out-of-memory errors;
+ * section 6, prefix caching for repeated long prompts).  Both resume a
+ * sequence from the state and the conv rows a previous call left, which is
+ * what state_in and conv_state_in carry.  Same as gdn_prefill, except:
  *
  *   q, k           [T_tot][Hqk][dk], v [T_tot][Hv][dv], a, b [T_tot][Hv],
  *                  o [T_tot][Hv][dv]: tokens of all sequences packed
@@ -160,10 +166,14 @@ int gdn_decode_step(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 /*
  * Multi-token decode with an optional slot table: T = 1..4 new tokens for
  * each of B sequences, processed in order, the state read once and written
- * once (multi-token decoding and the verification of tokens proposed by a
- * multi-token-prediction head; the pages name MTP speculative decoding as part
- * of the model's serving path).  Same computation as T successive calls of
- * gdn_decode_step.
+ * once.  This is the verification step of speculative decoding with the
+ * model's multi-token-prediction head: the walkthrough (bjdmk.com.cn) serves
+ * with num_speculative_tokens = 3 (section 3) and measures its gain (section
+ * 4); the architecture deep dive (alwayszhang.cn, section 7) describes the MTP
+ * head and its use for speculative decoding.  The slot table addresses the
+ * state and conv caches of a serving engine (walkthrough, sections 3 and 6:
+ * prefix caching keeps those caches across requests).  Same computation as T
+ * successive calls of gdn_decode_step.
  *
  *   q, k        [B][T][Hqk][dk] bf16 raw;  v [B][T][Hv][dv] bf16 raw
  *   a, b        [B][T][Hv] fp32

@@ -57,6 +57,13 @@ def lib():
             raise RuntimeError(
                 f"HIP library {LIB_PATH} is not built; run "
                 "`python -m linear_attention_sequence_gdn_amd.build` (there is no CPU fallback)")
+        # The library and torch must share one HIP runtime.  torch ships its
+        # own libamdhip64 (soname libamdhip64.so.7, loaded from torch's
+        # directory); the library names libamdhip64.so.7.  Importing torch
+        # first puts that runtime in the process, and the library then binds
+        # to it by soname.  Loaded the other way round, the process would hold
+        # two HIP runtimes, and the one the library calls into sees no device.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_status_string.argtypes = [_I]

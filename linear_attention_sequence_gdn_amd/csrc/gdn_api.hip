@@ -98,6 +98,24 @@ size_t gdn_prefill_varlen_workspace_size(int N, int T_tot, int Hqk, int Hv, int 
     return gdn::prefill_workspace_bytes(gdn::max_chunks_varlen(N, T_tot), N, Hqk, Hv);
 }
 
+// Checks of the arguments every prefill entry point shares, apart from the
+// workspace (no HIP call).
+static int prefill_check(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
+                         const float *b, const uint16_t *conv_w, const uint16_t *conv_state_in,
+                         uint16_t *conv_state_out, const float *state_in, float *state_out, uint16_t *o,
+                         const int32_t *cu_seqlens, int T_tot)
+{
+    if (!state_out || !conv_w) return GDN_ERR_INVALID_ARGUMENT;
+    if (T_tot > 0 && (!q || !k || !v || !a || !b || !o)) return GDN_ERR_INVALID_ARGUMENT;
+    const void *al16[] = {q, k, v, conv_w, conv_state_in, conv_state_out, state_in, state_out, o};
+    for (const void *ptr : al16)
+        if (ptr && !aligned(ptr, 16)) return GDN_ERR_INVALID_ARGUMENT;
+    if ((a && !aligned(a, 4)) || (b && !aligned(b, 4)) || (cu_seqlens && !aligned(cu_seqlens, 4)))
+        return GDN_ERR_INVALID_ARGUMENT;
+    if (conv_state_in && conv_state_out == conv_state_in) return GDN_ERR_INVALID_ARGUMENT;
+    return GDN_OK;
+}
+
 static int prefill_common(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
                           const float *b, const uint16_t *conv_w, const uint16_t *conv_state_in,
                           uint16_t *conv_state_out, const float *state_in, float *state_out,
@@ -106,15 +124,10 @@ static int prefill_common(const uint16_t *q, const uint16_t *k, const uint16_t *
                           void *workspace, size_t workspace_bytes, void *stream,
                           void *const *events = nullptr)
 {
-    if (!state_out || !conv_w) return GDN_ERR_INVALID_ARGUMENT;
-    if (T_tot > 0 && (!q || !k || !v || !a || !b || !o)) return GDN_ERR_INVALID_ARGUMENT;
-    const void *al16[] = {q, k, v, conv_w, conv_state_in, conv_state_out, state_in, state_out, o,
-                          workspace};
-    for (const void *ptr : al16)
-        if (ptr && !aligned(ptr, 16)) return GDN_ERR_INVALID_ARGUMENT;
-    if ((a && !aligned(a, 4)) || (b && !aligned(b, 4)) || (cu_seqlens && !aligned(cu_seqlens, 4)))
-        return GDN_ERR_INVALID_ARGUMENT;
-    if (conv_state_in && conv_state_out == conv_state_in) return GDN_ERR_INVALID_ARGUMENT;
+    const int rc = prefill_check(q, k, v, a, b, conv_w, conv_state_in, conv_state_out, state_in, state_out, o,
+                                 cu_seqlens, T_tot);
+    if (rc != GDN_OK) return rc;
+    if (workspace && !aligned(workspace, 16)) return GDN_ERR_INVALID_ARGUMENT;
     const int max_chunks = cu_seqlens ? gdn::max_chunks_varlen(N, T_tot)
                                       : gdn::max_chunks_uniform(N, T_uniform);
     const size_t need = gdn::prefill_workspace_bytes(max_chunks, N, Hqk, Hv);

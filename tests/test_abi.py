@@ -100,6 +100,8 @@ def test_prefill_validation(L):
     assert call_prefill(L, ws_bytes=need - 1) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL
     assert call_prefill(L, ws=0) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL
     assert call_prefill(L, cs_in=FAKE, cs_out=FAKE) == gdn.GDN_ERR_INVALID_ARGUMENT  # aliasing conv rows
+    # the workspace must be 16-byte aligned, as the header states
+    assert call_prefill(L, ws=FAKE + 8) == gdn.GDN_ERR_INVALID_ARGUMENT
     assert call_prefill(L, B=0, T=0, ws=0, ws_bytes=0) == gdn.GDN_OK  # empty batch: nothing to do
 
 
@@ -185,3 +187,4 @@ def test_backward_varlen_validation(L):
     assert call(Hv=9) == gdn.GDN_ERR_UNSUPPORTED
     assert call(ws_bytes=10) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL
     assert call(cu=FAKE + 2) == gdn.GDN_ERR_INVALID_ARGUMENT
+

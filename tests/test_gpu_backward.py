@@ -5,7 +5,18 @@ Tolerance: the backward computes in fp32 throughout (no matrix-core operand
 rounding), so its error is fp32 rounding through the chunk chain: relative L2
 error of every gradient <= 1e-5, about a hundred times fp32's unit roundoff
 (6e-8) for dot products of length 128 and the chunk-to-chunk carry; the
-measured errors are 1e-7 to 8e-7.
+measured errors are 1e-7 to 8e-7.  Element by element the bound is the
+worst case rather than the typical one: a length-n fp32 dot product is off by
+at most gamma_n = n u / (1 - n u) of the sum of its terms' magnitudes, and a
+gradient element passes through about four such stages with n <= 256 (the
+recomputed forward, the state-gradient step, the per-chunk products, the
+norm / SiLU / conv chain), 4 * 256 * 6e-8 = 6e-5 of the magnitudes involved.
+Taking those as the element's own size plus the tensor's RMS (elements that
+cancel to near zero are sums of terms of about that size):
+    |g - g_ref| <= 1e-4 * (|g_ref| + RMS(g_ref)),
+so that an error confined to a few elements (one chunk's gate gradient, one
+conv channel) cannot hide inside a large tensor's norm.  Measured: at most
+2e-5, in the strong-decay case.
 """
 import numpy as np
 import pytest
@@ -16,6 +27,7 @@ from gdn_testutil import dev_bf16, dev_f32, rel_l2
 pytestmark = pytest.mark.gpu
 
 GRAD_REL_L2 = 1e-5
+GRAD_ELEM = 1e-4
 
 
 def _case(B, T, Hqk, Hv, seed, carries=True, gate_scale=0.1, q_scale=1.0):
@@ -64,9 +76,14 @@ def _compare(got, ref, B, T, what=""):
         g = got[n].reshape(shapes[n]) if n in shapes else got[n]
         assert np.all(np.isfinite(g)), f"{what} {n}: non-finite"
         r = rel_l2(g, ref[n])
-        worst[n] = r
+        rf = np.asarray(ref[n], np.float64).reshape(np.shape(g))
+        rms = np.sqrt(np.mean(rf ** 2)) if rf.size else 0.0
+        elem = np.abs(g - rf) / (np.abs(rf) + rms) if rms > 0 else np.abs(g - rf)
+        e = float(elem.max()) if elem.size else 0.0
+        worst[n] = (r, e)
         assert r <= GRAD_REL_L2, f"{what} grad {n}: relL2 {r:.3e} > {GRAD_REL_L2}"
-    print(what, " ".join(f"{n}={v:.1e}" for n, v in worst.items()), flush=True)
+        assert e <= GRAD_ELEM, f"{what} grad {n}: element error {e:.3e} (|ref| + RMS) > {GRAD_ELEM}"
+    print(what, " ".join(f"{n}={v[0]:.1e}/{v[1]:.1e}" for n, v in worst.items()), flush=True)
     return worst
 
 

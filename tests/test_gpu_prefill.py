@@ -47,22 +47,25 @@ def oracle_prefill(x, heads=None):
                           state_in=x["state_in"], conv_state_in=x["conv_state_in"], heads=heads)
 
 
-def compare(x, o, so, cso, heads=None, seqs=None):
+def compare(x, o, so, cso, heads=None, label=None):
     o_ref, s_ref, cs_ref = oracle_prefill(x, heads)
     hs = list(range(x["Hv"])) if heads is None else list(heads)
     og = host_bf16(o)
-    check_output(og[:, hs], o_ref[:, hs])
+    r_o, ex = check_output(og[:, hs], o_ref[:, hs])
     sg = so.cpu().numpy()
-    check_state(sg[:, hs], s_ref[:, hs])
+    r_s = check_state(sg[:, hs], s_ref[:, hs])
     if cso is not None:
         np.testing.assert_array_equal(host_u16(cso), cs_ref)
+    if label:
+        print(f"{label} margins: o relL2 {r_o:.2e}, max-abs excess {ex:.2e} RMS, state relL2 {r_s:.2e}",
+              flush=True)
     return og, sg
 
 
 def test_config0_tiny(oracle_lib):
     x = inputs.make_config(0)
     o, so, cso = gpu_prefill(x, uniform_T=512)
-    compare(x, o, so, cso)
+    compare(x, o, so, cso, label="config 0")
 
 
 @pytest.mark.parametrize("T", [1, 2, 3, 5, 63, 64, 65, 100, 129, 200])
@@ -215,7 +218,7 @@ def test_decode_steps_match_prefill(oracle_lib):
 def test_config1_layer_prefill(oracle_lib):
     x = inputs.make_config(1)
     o, so, cso = gpu_prefill(x, uniform_T=8192)
-    compare(x, o, so, cso)
+    compare(x, o, so, cso, label="config 1")
 
 
 def test_config4_varlen_sampled(oracle_lib):
@@ -230,6 +233,7 @@ def test_config4_varlen_sampled(oracle_lib):
     cu = x["cu_seqlens"]
     L = np.diff(cu)
     pick = sorted(set([int(np.argmin(L)), int(np.argmax(L)), 3, 17, 40, 63]))
+    worst = [0.0, 0.0, 0.0]
     for s in pick:
         sub = dict(x)
         t0, t1 = cu[s], cu[s + 1]
@@ -238,8 +242,9 @@ def test_config4_varlen_sampled(oracle_lib):
         sub["cu_seqlens"] = np.array([0, t1 - t0], np.int32)
         sub["state_in"] = x["state_in"][s:s + 1]
         o_ref, s_ref, cs_ref = oracle_prefill(sub)
-        check_output(og[t0:t1], o_ref, what=f"o seq {s}")
-        check_state(sg[s:s + 1], s_ref, what=f"state seq {s}")
+        r_o, ex = check_output(og[t0:t1], o_ref, what=f"o seq {s}")
+        r_s = check_state(sg[s:s + 1], s_ref, what=f"state seq {s}")
+        worst = [max(worst[0], r_o), max(worst[1], ex), max(worst[2], r_s)]
         np.testing.assert_array_equal(csg[s], cs_ref[0])
     # first 64 tokens of every sequence
     head = dict(x)
@@ -248,7 +253,10 @@ def test_config4_varlen_sampled(oracle_lib):
         head[key] = x[key][idx]
     head["cu_seqlens"] = np.arange(0, 64 * len(L) + 1, 64, dtype=np.int32)
     o_ref, _, _ = oracle_prefill(head)
-    check_output(og[idx], o_ref, what="first 64 tokens of every sequence")
+    r_h, ex_h = check_output(og[idx], o_ref, what="first 64 tokens of every sequence")
+    print(f"config 4 margins (worst of the sampled sequences): o relL2 {worst[0]:.2e}, max-abs excess "
+          f"{worst[1]:.2e} RMS, state relL2 {worst[2]:.2e}; first 64 tokens of all: o relL2 {r_h:.2e}, "
+          f"max-abs excess {ex_h:.2e} RMS", flush=True)
 
 
 def test_config2_native_context_three_heads(oracle_lib):
@@ -263,8 +271,11 @@ def test_config2_native_context_three_heads(oracle_lib):
     del o
     torch.cuda.empty_cache()
     o_ref, s_ref, _ = oracle_prefill(x, heads=heads)
-    check_output(og, o_ref[:, heads])
-    check_state(sg, s_ref[:, heads])
+    r_o, ex = check_output(og, o_ref[:, heads])
+    r_s = check_state(sg, s_ref[:, heads])
+    worst_head = max(check_state(sg[:, i], s_ref[:, h], what=f"state head {h}") for i, h in enumerate(heads))
+    print(f"config 2 margins (V heads 0, 23, 47): o relL2 {r_o:.2e}, max-abs excess {ex:.2e} RMS, "
+          f"state relL2 {r_s:.2e} (worst head {worst_head:.2e})", flush=True)
 
 
 def test_stale_workspace_segmented():
