@@ -111,6 +111,39 @@ int gdn_prefill_with_events(const uint16_t *q, const uint16_t *k, const uint16_t
                             void *workspace, size_t workspace_bytes, void *stream,
                             void *const *events);
 
+/*
+ * gdn_prefill for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and kernels as gdn_prefill, with the workspace taken from
+ * a file-scope device array of the library instead of a caller's buffer.  It
+ * calls no hipMalloc, hipFree or other allocating routine.
+ *
+ *   - Every other argument is as for gdn_prefill; there is no workspace.
+ *   - The array holds gdn_prefill_noalloc_max_workspace() bytes (192 MiB)
+ *     on each GPU the library runs on, until the process ends.  A call whose
+ *     gdn_prefill_workspace_size(B, T, Hqk, Hv, dk, dv) exceeds it returns
+ *     GDN_ERR_WORKSPACE_TOO_SMALL with nothing launched (at 16 QK / 48 V
+ *     heads: T up to 8192 for B = 1).
+ *   - The array of the CURRENT device is used (hipGetDevice), which must be
+ *     the device of `stream`.  Its address is looked up with
+ *     hipGetSymbolAddress on the first call on each device and kept: this
+ *     entry point, unlike the others, keeps that per-device address.
+ *   - All calls on one GPU share its array, and the array keeps the last
+ *     call's contents (the kernels clear what must start at zero): two calls
+ *     that overlap in time on one GPU (on different streams, or on one
+ *     stream from several host threads without ordering) race and give
+ *     undefined results.  Calls ordered on one stream are safe.
+ */
+int gdn_prefill_noalloc(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                        const float *a, const float *b, const uint16_t *conv_w,
+                        const uint16_t *conv_state_in, uint16_t *conv_state_out,
+                        const float *state_in, float *state_out, uint16_t *o,
+                        int B, int T, int Hqk, int Hv, int dk, int dv,
+                        float gate_scale, float q_scale, void *stream);
+
+/* Bytes of the device array gdn_prefill_noalloc uses as its workspace. */
+size_t gdn_prefill_noalloc_max_workspace(void);
+
 /* Bytes of device workspace gdn_prefill_varlen needs (any lengths summing to
  * T_tot over N sequences). */
 size_t gdn_prefill_varlen_workspace_size(int N, int T_tot, int Hqk, int Hv, int dk, int dv);

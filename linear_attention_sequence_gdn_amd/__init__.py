@@ -87,6 +87,10 @@ def lib():
         L.gdn_prefill_backward_varlen.argtypes = [_P] * 19 + [_I] * 6 + [_F, _F, _P, _SZ, _P]
         L.gdn_decode_multi.restype = _I
         L.gdn_decode_multi.argtypes = [_P] * 11 + [_I] * 7 + [_F, _F, _P]
+        L.gdn_prefill_noalloc.restype = _I
+        L.gdn_prefill_noalloc.argtypes = [_P] * 11 + [_I] * 6 + [_F, _F, _P]
+        L.gdn_prefill_noalloc_max_workspace.restype = _SZ
+        L.gdn_prefill_noalloc_max_workspace.argtypes = []
         _lib = L
     return _lib
 
@@ -179,6 +183,46 @@ def gdn_prefill(q, k, v, a, b, conv_w, *, gate_scale, q_scale=1.0, state_in=None
                            workspace.numel() * workspace.element_size(), _stream(stream))
     if rc != GDN_OK:
         raise GDNError("gdn_prefill", rc)
+    return o, state_out, conv_state_out
+
+
+def gdn_prefill_noalloc_max_workspace() -> int:
+    return int(lib().gdn_prefill_noalloc_max_workspace())
+
+
+def gdn_prefill_noalloc(q, k, v, a, b, conv_w, *, gate_scale, q_scale=1.0, state_in=None,
+                        conv_state_in=None, state_out=None, o=None, conv_state_out=None, stream=None):
+    """``gdn_prefill`` with the library's own device workspace (no workspace
+    argument, nothing allocated by the library).  Outputs default to new
+    tensors, as in ``gdn_prefill``; pass ``o`` and ``state_out`` to allocate
+    nothing at all.  Returns (o, state_out, conv_state_out)."""
+    torch = _torch()
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    C_tot = 2 * Hqk * dk + Hv * dv
+    bf, f32 = torch.bfloat16, torch.float32
+    _check(q, "q", bf, (B, T, Hqk, dk))
+    _check(k, "k", bf, (B, T, Hqk, dk))
+    _check(v, "v", bf, (B, T, Hv, dv))
+    _check(a, "a", f32, (B, T, Hv))
+    _check(b, "b", f32, (B, T, Hv))
+    _check(conv_w, "conv_w", bf, (C_tot, 4))
+    _check(state_in, "state_in", f32, (B, Hv, dk, dv))
+    _check(conv_state_in, "conv_state_in", bf, (B, 3, C_tot))
+    dev = q.device
+    if o is None:
+        o = torch.empty((B, T, Hv, dv), dtype=bf, device=dev)
+    if state_out is None:
+        state_out = torch.empty((B, Hv, dk, dv), dtype=f32, device=dev)
+    _check(o, "o", bf, (B, T, Hv, dv))
+    _check(state_out, "state_out", f32, (B, Hv, dk, dv))
+    _check(conv_state_out, "conv_state_out", bf, (B, 3, C_tot))
+    rc = lib().gdn_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(conv_w),
+                                   _ptr(conv_state_in), _ptr(conv_state_out), _ptr(state_in),
+                                   _ptr(state_out), _ptr(o), B, T, Hqk, Hv, dk, dv,
+                                   float(gate_scale), float(q_scale), _stream(stream))
+    if rc != GDN_OK:
+        raise GDNError("gdn_prefill_noalloc", rc)
     return o, state_out, conv_state_out
 
 

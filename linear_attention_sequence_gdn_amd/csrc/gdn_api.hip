@@ -7,6 +7,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "gdn_prefill.h"
 
 namespace gdn {
@@ -162,6 +164,72 @@ int gdn_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v, const f
     return prefill_common(q, k, v, a, b, conv_w, conv_state_in, conv_state_out, state_in,
                           state_out, o, nullptr, B, T, B * T, Hqk, Hv, gate_scale, q_scale,
                           workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// gdn_prefill_noalloc: gdn_prefill with its workspace in a file-scope device
+// array instead of a caller's buffer, for callers that cannot allocate.  The
+// array lives in the library's code object: each GPU the library runs on
+// holds its own copy, at its own address, until the process ends.  Host code
+// must not pass the array's name to a kernel (on the host it names a host-side
+// stand-in); the device address is looked up once per device with
+// hipGetSymbolAddress and kept in kScratchDevAddr.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)192 << 20;  // the T = 8192, 16 / 48-head prefill needs 160 MiB
+constexpr int kScratchMaxDevices = 64;
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex kScratchMutex;
+void *kScratchDevAddr[kScratchMaxDevices];
+
+// Device address of the current device's scratch array, looked up on the
+// first call on that device.
+int scratch_address(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return GDN_ERR_HIP;
+    if (dev < 0 || dev >= kScratchMaxDevices) return GDN_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(kScratchMutex);
+    if (!kScratchDevAddr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return GDN_ERR_HIP;
+        kScratchDevAddr[dev] = ptr;
+    }
+    *out = kScratchDevAddr[dev];
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_prefill_noalloc_max_workspace(void) { return kScratchBytes; }
+
+int gdn_prefill_noalloc(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
+                        const float *b, const uint16_t *conv_w, const uint16_t *conv_state_in,
+                        uint16_t *conv_state_out, const float *state_in, float *state_out, uint16_t *o,
+                        int B, int T, int Hqk, int Hv, int dk, int dv, float gate_scale, float q_scale,
+                        void *stream)
+{
+    if (B < 0 || T < 0) return GDN_ERR_INVALID_ARGUMENT;
+    int rc = check_dims(Hqk, Hv, dk, dv);
+    if (rc != GDN_OK) return rc;
+    if ((long)B * T > 0x7fffffffL) return GDN_ERR_UNSUPPORTED;
+    rc = prefill_check(q, k, v, a, b, conv_w, conv_state_in, conv_state_out, state_in, state_out, o, nullptr,
+                       B * T);
+    if (rc != GDN_OK) return rc;
+    const size_t need = gdn::prefill_workspace_bytes(gdn::max_chunks_uniform(B, T), B, Hqk, Hv);
+    if (need > kScratchBytes) return GDN_ERR_WORKSPACE_TOO_SMALL;
+    void *ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc != GDN_OK) return rc;
+    return prefill_common(q, k, v, a, b, conv_w, conv_state_in, conv_state_out, state_in, state_out, o, nullptr,
+                          B, T, B * T, Hqk, Hv, gate_scale, q_scale, ws, kScratchBytes, stream);
 }
 
 int gdn_prefill_with_events(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,

@@ -188,3 +188,17 @@ def test_backward_varlen_validation(L):
     assert call(ws_bytes=10) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL
     assert call(cu=FAKE + 2) == gdn.GDN_ERR_INVALID_ARGUMENT
 
+
+def test_noalloc_validation(L):
+    # every failing call returns before any HIP call (no GPU needed)
+    def call(q=FAKE, B=1, T=64, Hqk=2, Hv=6, dk=128, cs=0):
+        return L.gdn_prefill_noalloc(_p(q), _p(), _p(), _p(), _p(), _p(), _p(cs), _p(cs), None, _p(), _p(),
+                                     B, T, Hqk, Hv, dk, 128, 0.1, 1.0, None)
+    assert gdn.gdn_prefill_noalloc_max_workspace() >= gdn.gdn_prefill_workspace_size(1, 8192, 16, 48)
+    assert call(q=0) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(T=-1) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(dk=64) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(Hv=5) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(q=FAKE + 2) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(cs=FAKE) == gdn.GDN_ERR_INVALID_ARGUMENT  # conv rows in and out alias
+    assert call(T=16384, Hqk=16, Hv=48) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL  # beyond the array
