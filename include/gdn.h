@@ -73,7 +73,8 @@ size_t gdn_prefill_workspace_size(int B, int T, int Hqk, int Hv, int dk, int dv)
  *   conv_state_in  [B][3][C_tot] bf16 history rows, or NULL (zero history)
  *   conv_state_out [B][3][C_tot] bf16, or NULL (not written): the last three
  *                  raw rows of each sequence (reaching into conv_state_in when
- *                  T < 3); must not overlap conv_state_in
+ *                  T < 3); may equal conv_state_in (in place), any other
+ *                  overlap is undefined
  *   state_in       [B][Hv][dk][dv] fp32 initial state, or NULL (zeros)
  *   state_out      [B][Hv][dk][dv] fp32 final state; may equal state_in
  *                  (in place), any other overlap is undefined
@@ -175,6 +176,32 @@ int gdn_prefill_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                        int Hqk, int Hv, int dk, int dv,
                        float gate_scale, float q_scale,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_prefill_varlen with a slot table into state and conv-row pools: the
+ * prefill side of a serving engine's state cache (prefix caching and chunked
+ * prefill resume a sequence from the cache row its previous call left;
+ * walkthrough, bjdmk.com.cn, sections 3 and 6).  Same as gdn_prefill_varlen,
+ * except:
+ *
+ *   slots          DEVICE int32 [N] (required): sequence s reads row slots[s]
+ *                  of state_in and conv_state_in and writes row slots[s] of
+ *                  state_out and conv_state_out
+ *   n_rows         rows of each pool: state_* [n_rows][Hv][dk][dv],
+ *                  conv_state_* [n_rows][3][C_tot]
+ * A sequence whose slot lies outside [0, n_rows) is skipped: none of its
+ * outputs (o rows, state, conv rows) is written.  Two sequences must not
+ * share a slot.  The pools may be updated in place (state_out == state_in,
+ * conv_state_out == conv_state_in); rows no sequence names are untouched.
+ */
+int gdn_prefill_varlen_slots(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                             const float *a, const float *b, const uint16_t *conv_w,
+                             const uint16_t *conv_state_in, uint16_t *conv_state_out,
+                             const float *state_in, float *state_out, uint16_t *o,
+                             const int32_t *cu_seqlens, const int32_t *slots, int n_rows,
+                             int N, int T_tot, int Hqk, int Hv, int dk, int dv,
+                             float gate_scale, float q_scale,
+                             void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * One decode step: one new token for each of B independent sequences (the

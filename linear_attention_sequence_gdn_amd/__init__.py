@@ -87,6 +87,8 @@ def lib():
         L.gdn_prefill_backward_varlen.argtypes = [_P] * 19 + [_I] * 6 + [_F, _F, _P, _SZ, _P]
         L.gdn_decode_multi.restype = _I
         L.gdn_decode_multi.argtypes = [_P] * 11 + [_I] * 7 + [_F, _F, _P]
+        L.gdn_prefill_varlen_slots.restype = _I
+        L.gdn_prefill_varlen_slots.argtypes = [_P] * 13 + [_I] * 7 + [_F, _F, _P, _SZ, _P]
         L.gdn_prefill_noalloc.restype = _I
         L.gdn_prefill_noalloc.argtypes = [_P] * 11 + [_I] * 6 + [_F, _F, _P]
         L.gdn_prefill_noalloc_max_workspace.restype = _SZ
@@ -331,10 +333,13 @@ def gdn_prefill_backward_varlen(q, k, v, a, b, conv_w, cu_seqlens, grad_o, *, ga
 
 def gdn_prefill_varlen(q, k, v, a, b, conv_w, cu_seqlens, *, gate_scale, q_scale=1.0,
                        state_in=None, conv_state_in=None, state_out=None, o=None,
-                       conv_state_out=None, workspace=None, stream=None):
+                       conv_state_out=None, slots=None, workspace=None, stream=None):
     """Packed variable-length prefill.  q, k: [T_tot][Hqk][128]; v: [T_tot][Hv][128];
     a, b: [T_tot][Hv]; cu_seqlens: int32 [N+1] on the GPU; states [N][...].
-    Returns (o, state_out, conv_state_out)."""
+    With ``slots`` (int32 [N] on the GPU) the states and conv rows are pools
+    of any number of rows and sequence s uses row slots[s]
+    (``gdn_prefill_varlen_slots``); state_out then defaults to state_in (the
+    pool updated in place).  Returns (o, state_out, conv_state_out)."""
     torch = _torch()
     T_tot, Hqk, dk = q.shape
     Hv, dv = v.shape[1], v.shape[2]
@@ -348,26 +353,44 @@ def gdn_prefill_varlen(q, k, v, a, b, conv_w, cu_seqlens, *, gate_scale, q_scale
     _check(b, "b", f32, (T_tot, Hv))
     _check(conv_w, "conv_w", bf, (C_tot, 4))
     _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
-    _check(state_in, "state_in", f32, (N, Hv, dk, dv))
-    _check(conv_state_in, "conv_state_in", bf, (N, 3, C_tot))
+    rows = N
+    if slots is not None:
+        _check(slots, "slots", torch.int32, (N,))
+        if state_out is None:
+            state_out = state_in
+        if state_out is None:
+            raise ValueError("a slot table needs a state pool (state_in or state_out)")
+        rows = state_out.shape[0]
+    _check(state_in, "state_in", f32, (rows, Hv, dk, dv))
+    _check(conv_state_in, "conv_state_in", bf, (rows, 3, C_tot))
     dev = q.device
     if o is None:
         o = torch.empty((T_tot, Hv, dv), dtype=bf, device=dev)
     if state_out is None:
         state_out = torch.empty((N, Hv, dk, dv), dtype=f32, device=dev)
     _check(o, "o", bf, (T_tot, Hv, dv))
-    _check(state_out, "state_out", f32, (N, Hv, dk, dv))
-    _check(conv_state_out, "conv_state_out", bf, (N, 3, C_tot))
+    _check(state_out, "state_out", f32, (rows, Hv, dk, dv))
+    _check(conv_state_out, "conv_state_out", bf, (rows, 3, C_tot))
     need = gdn_prefill_varlen_workspace_size(N, T_tot, Hqk, Hv, dk, dv)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    rc = lib().gdn_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(conv_w),
-                                  _ptr(conv_state_in), _ptr(conv_state_out), _ptr(state_in),
-                                  _ptr(state_out), _ptr(o), _ptr(cu_seqlens), N, T_tot, Hqk, Hv,
-                                  dk, dv, float(gate_scale), float(q_scale), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), _stream(stream))
+    if slots is None:
+        rc = lib().gdn_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(conv_w),
+                                      _ptr(conv_state_in), _ptr(conv_state_out), _ptr(state_in),
+                                      _ptr(state_out), _ptr(o), _ptr(cu_seqlens), N, T_tot, Hqk, Hv,
+                                      dk, dv, float(gate_scale), float(q_scale), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(stream))
+        name = "gdn_prefill_varlen"
+    else:
+        rc = lib().gdn_prefill_varlen_slots(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(conv_w),
+                                            _ptr(conv_state_in), _ptr(conv_state_out), _ptr(state_in),
+                                            _ptr(state_out), _ptr(o), _ptr(cu_seqlens), _ptr(slots), rows,
+                                            N, T_tot, Hqk, Hv, dk, dv, float(gate_scale), float(q_scale),
+                                            _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                            _stream(stream))
+        name = "gdn_prefill_varlen_slots"
     if rc != GDN_OK:
-        raise GDNError("gdn_prefill_varlen", rc)
+        raise GDNError(name, rc)
     return o, state_out, conv_state_out
 
 

@@ -114,7 +114,6 @@ static int prefill_check(const uint16_t *q, const uint16_t *k, const uint16_t *v
         if (ptr && !aligned(ptr, 16)) return GDN_ERR_INVALID_ARGUMENT;
     if ((a && !aligned(a, 4)) || (b && !aligned(b, 4)) || (cu_seqlens && !aligned(cu_seqlens, 4)))
         return GDN_ERR_INVALID_ARGUMENT;
-    if (conv_state_in && conv_state_out == conv_state_in) return GDN_ERR_INVALID_ARGUMENT;
     return GDN_OK;
 }
 
@@ -124,7 +123,7 @@ static int prefill_common(const uint16_t *q, const uint16_t *k, const uint16_t *
                           uint16_t *o, const int32_t *cu_seqlens, int N, int T_uniform,
                           int T_tot, int Hqk, int Hv, float gate_scale, float q_scale,
                           void *workspace, size_t workspace_bytes, void *stream,
-                          void *const *events = nullptr)
+                          void *const *events = nullptr, const int32_t *slots = nullptr, int n_rows = 0)
 {
     const int rc = prefill_check(q, k, v, a, b, conv_w, conv_state_in, conv_state_out, state_in, state_out, o,
                                  cu_seqlens, T_tot);
@@ -146,6 +145,9 @@ static int prefill_common(const uint16_t *q, const uint16_t *k, const uint16_t *
     p.seg_chunks = gdn::choose_seg_chunks(max_chunks, N, Hv);
     p.max_segs = gdn::max_segments(max_chunks, N, p.seg_chunks);
     p.defer_final = state_in != nullptr && state_in == state_out;
+    p.defer_conv = conv_state_in != nullptr && conv_state_in == conv_state_out;
+    p.slots = slots;
+    p.n_rows = n_rows;
     hipError_t e = gdn::launch_prefill(p, workspace, reinterpret_cast<hipStream_t>(stream),
                                        reinterpret_cast<hipEvent_t const *>(events));
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
@@ -265,6 +267,22 @@ int gdn_prefill_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, 
     return prefill_common(q, k, v, a, b, conv_w, conv_state_in, conv_state_out, state_in,
                           state_out, o, cu_seqlens, N, 0, T_tot, Hqk, Hv, gate_scale, q_scale,
                           workspace, workspace_bytes, stream);
+}
+
+int gdn_prefill_varlen_slots(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
+                             const float *b, const uint16_t *conv_w, const uint16_t *conv_state_in,
+                             uint16_t *conv_state_out, const float *state_in, float *state_out, uint16_t *o,
+                             const int32_t *cu_seqlens, const int32_t *slots, int n_rows, int N, int T_tot,
+                             int Hqk, int Hv, int dk, int dv, float gate_scale, float q_scale, void *workspace,
+                             size_t workspace_bytes, void *stream)
+{
+    if (N < 0 || T_tot < 0) return GDN_ERR_INVALID_ARGUMENT;
+    int rc = check_dims(Hqk, Hv, dk, dv);
+    if (rc != GDN_OK) return rc;
+    if (!cu_seqlens || !slots || n_rows < 0 || !aligned(slots, 4)) return GDN_ERR_INVALID_ARGUMENT;
+    return prefill_common(q, k, v, a, b, conv_w, conv_state_in, conv_state_out, state_in, state_out, o,
+                          cu_seqlens, N, 0, T_tot, Hqk, Hv, gate_scale, q_scale, workspace, workspace_bytes,
+                          stream, nullptr, slots, n_rows);
 }
 
 size_t gdn_prefill_backward_workspace_size(int B, int T, int Hqk, int Hv, int dk, int dv)

@@ -26,7 +26,19 @@ struct PrefillArgs {
     int seg_chunks;  // chunks per segment of the sequential pass
     int max_segs;    // bound of the number of segments
     int defer_final; // state_out is state_in: final states go through the in-order pass
+    int defer_conv;  // conv_state_out is conv_state_in: the v rows are written by the in-order pass
+    const int32_t *slots;  // NULL, or DEVICE [N]: sequence s reads and writes row slots[s] of the
+    int n_rows;            // state and conv-row pools of n_rows rows (out of range: skipped)
 };
+
+// Pool row of sequence s (s itself without a slot table), or -1 when its slot
+// lies outside the pool.
+__device__ __forceinline__ int seq_row(const PrefillArgs &p, int s)
+{
+    if (!p.slots) return s;
+    const int r = p.slots[s];
+    return (r >= 0 && r < p.n_rows) ? r : -1;
+}
 
 // Upper bound of the number of 64-token chunks.
 inline int max_chunks_uniform(int B, int T) { return B * ((T + kChunk - 1) / kChunk); }

@@ -478,7 +478,8 @@ void prep_kernel(PrefillArgs p, Workspace ws)
     const int s = ci.x, t0 = ci.y;
     const bool first = ci.w != 0;
     const long C_tot = 2L * Hqk * kD + (long)Hv * kD;
-    const uint16_t *hist = (first && p.conv_state_in) ? p.conv_state_in + (long)s * 3 * C_tot : nullptr;
+    const int row = seq_row(p, s);
+    const uint16_t *hist = (first && p.conv_state_in && row >= 0) ? p.conv_state_in + (long)row * 3 * C_tot : nullptr;
     const int r0 = 16 * wave;
     const long gc = (long)c * Hqk + g;
 
@@ -1341,6 +1342,35 @@ __device__ __forceinline__ void state_store(const f32x4 (&S)[8][kChainCT], float
                 dst[(long)(16 * dt + 4 * q4 + e) * kD + kCW * wave + 16 * x + c16] = S[dt][x][e];
 }
 
+// The carried conv rows of one sequence (pool row `row`), planes [pl0, pl1)
+// of q | k | v for QK head g / V head h, one wave: the last three raw rows,
+// reaching back into the incoming rows when the sequence is shorter than
+// three tokens.  In place, a lane reads each incoming row before it writes
+// it: row r is written from row r + L (L < 3), which is read first.
+__device__ __forceinline__ void write_conv_rows(const PrefillArgs &p, const int4 &si, int row, int g, int h,
+                                                int pl0, int pl1, int lane)
+{
+    const int Hqk = p.Hqk, Hv = p.Hv;
+    const long C_tot = 2L * Hqk * kD + (long)Hv * kD;
+    const int Ls = si.w, t0 = si.z;
+    for (int plane = pl0; plane < pl1; ++plane) {
+        const long ch0 = plane == 0 ? (long)g * kD : plane == 1 ? (long)Hqk * kD + (long)g * kD
+                                                              : 2L * Hqk * kD + (long)h * kD;
+        const uint16_t *src = plane == 0 ? p.q + (long)g * kD : plane == 1 ? p.k + (long)g * kD : p.v + (long)h * kD;
+        const long ld = plane == 2 ? (long)Hv * kD : (long)Hqk * kD;
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            const int tau = Ls - 3 + r;
+            uint32_t val = 0;
+            if (tau >= 0)
+                val = ld_pair(src + (long)(t0 + tau) * ld + 2 * lane);
+            else if (p.conv_state_in)
+                val = ld_pair(p.conv_state_in + ((long)row * 3 + 3 + tau) * C_tot + ch0 + 2 * lane);
+            *reinterpret_cast<uint32_t *>(p.conv_state_out + ((long)row * 3 + r) * C_tot + ch0 + 2 * lane) = val;
+        }
+    }
+}
+
 // Sequential pass: one workgroup per (segment, V head); segments run in
 // parallel, each from its warm-up start.  Every workgroup makes the warm-up
 // test of all segments of its sequence.  If one misses its bound, or the
@@ -1374,10 +1404,12 @@ void chain_kernel(PrefillArgs p, Workspace ws)
     const int4 sg = Tables::seg(p, ws, k);  // seq, first chunk, end chunk, flags
     if (sg.x < 0) return;                   // no segment in this slot
     const int s = sg.x;
+    const int row = seq_row(p, s);          // pool row of the sequence's state and conv rows
+    if (row < 0) return;                    // its slot lies outside the pool: skipped
     const int4 si = Tables::seq(p, ws, s);  // chunk0, nchunks, t0, L
     const bool first = sg.w & 1, last = sg.w & 2;
-    const long sbase = ((long)s * Hv + h) * kD * kD;
-    const uint16_t *hist = p.conv_state_in ? p.conv_state_in + (long)s * 3 * C_tot + cv : nullptr;
+    const long sbase = ((long)row * Hv + h) * kD * kD;
+    const uint16_t *hist = p.conv_state_in ? p.conv_state_in + (long)row * 3 * C_tot + cv : nullptr;
     const uint16_t *vs = p.v + (long)si.z * Hv * kD + (long)h * kD;
     // conv taps of the wave's channel tiles
     bf16x8 wb[kChainCT][2];
@@ -1428,33 +1460,18 @@ void chain_kernel(PrefillArgs p, Workspace ws)
     }
     // carried conv rows: the last three raw rows of the sequence (v channels
     // of head h; the first head of the group also writes the q and k
-    // channels)
-    if (first && p.conv_state_out && wave == 0) {
-        const int Ls = si.w, t0 = si.z;
-        for (int plane = (j == 0 ? 0 : 2); plane < 3; ++plane) {
-            const long ch0 = plane == 0 ? (long)g * kD : plane == 1 ? (long)Hqk * kD + (long)g * kD
-                                                                  : 2L * Hqk * kD + (long)h * kD;
-            const uint16_t *src = plane == 0 ? p.q + (long)g * kD : plane == 1 ? p.k + (long)g * kD
-                                                                              : p.v + (long)h * kD;
-            const long ld = plane == 2 ? (long)Hv * kD : (long)Hqk * kD;
-#pragma unroll
-            for (int r = 0; r < 3; ++r) {
-                const int tau = Ls - 3 + r;
-                uint32_t val = 0;
-                if (tau >= 0)
-                    val = ld_pair(src + (long)(t0 + tau) * ld + 2 * lane);
-                else if (p.conv_state_in)
-                    val = ld_pair(p.conv_state_in + ((long)s * 3 + 3 + tau) * C_tot + ch0 + 2 * lane);
-                *reinterpret_cast<uint32_t *>(p.conv_state_out + ((long)s * 3 + r) * C_tot + ch0 + 2 * lane) = val;
-            }
-        }
-    }
+    // channels).  In place, the v rows wait for every workgroup of the
+    // (sequence, head) that may read them (a later segment whose warm-up
+    // reaches back to the sequence start does), so the in-order walk below
+    // writes them; the q and k rows were read by the parallel pass only.
+    if (first && p.conv_state_out && wave == 0)
+        write_conv_rows(p, si, row, g, h, j == 0 ? 0 : 2, (p.defer_conv && nseg > 1) ? 2 : 3, lane);
 
     // The in-order walk, if any segment missed its bound or the call is in
     // place: the last workgroup of the sequence to finish does it.  A
     // workgroup publishes its parked state first if the walk will read it
     // (the next segment is recomputed, or the final state of an in-place call).
-    if (nseg <= 1 || (!any_bad && !p.defer_final)) return;
+    if (nseg <= 1 || (!any_bad && !p.defer_final && !p.defer_conv)) return;
     if (next_bad || (i_seg == nseg - 1 && p.defer_final)) __threadfence();
     __syncthreads();
     if (t == 0) s_total = atomicAdd(ws.seg_done + (long)s * Hv + h, 1) + 1;
@@ -1479,6 +1496,8 @@ void chain_kernel(PrefillArgs p, Workspace ws)
         if (!carry) state_load(S, ws.bstate + ((long)(ss.x + nseg - 1) * Hv + h) * kStateFloats, wave, lane);
         state_store(S, p.state_out + sbase, wave, lane);
     }
+    // the v rows of an in-place conv carry, now that no workgroup reads them
+    if (p.defer_conv && p.conv_state_out && wave == 0) write_conv_rows(p, si, row, g, h, 2, 3, lane);
 }
 
 }  // namespace

@@ -87,8 +87,12 @@ int main()
                               0.1f, 1.f, F, 1 << 30, nullptr), GDN_ERR_INVALID_ARGUMENT);
     EXPECT(gdn_prefill_noalloc(u, u, u, f, f, u, nullptr, nullptr, nullptr, fo, uo, 1, 16384, 16, 48, 128, 128,
                                0.1f, 1.f, nullptr), GDN_ERR_WORKSPACE_TOO_SMALL);
-    EXPECT(gdn_prefill_noalloc(u, u, u, f, f, u, u, uo, nullptr, fo, uo, 1, 64, 2, 6, 128, 128, 0.1f, 1.f,
-                               nullptr), GDN_ERR_INVALID_ARGUMENT);
+    EXPECT(gdn_prefill_noalloc(nullptr, u, u, f, f, u, nullptr, nullptr, nullptr, fo, uo, 1, 64, 2, 6, 128, 128,
+                               0.1f, 1.f, nullptr), GDN_ERR_INVALID_ARGUMENT);
+    EXPECT(gdn_prefill_varlen_slots(u, u, u, f, f, u, nullptr, nullptr, nullptr, fo, uo, cu, nullptr, 4, 2, 100, 2,
+                                    6, 128, 128, 0.1f, 1.f, F, 1 << 30, nullptr), GDN_ERR_INVALID_ARGUMENT);
+    EXPECT(gdn_prefill_varlen_slots(u, u, u, f, f, u, nullptr, nullptr, nullptr, fo, uo, cu, cu, -1, 2, 100, 2, 6,
+                                    128, 128, 0.1f, 1.f, F, 1 << 30, nullptr), GDN_ERR_INVALID_ARGUMENT);
     EXPECT(gdn_decode_step(nullptr, u, u, f, f, u, uo, f, fo, uo, 2, 2, 6, 128, 128, 0.1f, 1.f, nullptr),
            GDN_ERR_INVALID_ARGUMENT);
     EXPECT(gdn_decode_multi(u, u, u, f, f, u, uo, f, fo, uo, nullptr, 0, 2, 5, 2, 6, 128, 128, 0.1f, 1.f,

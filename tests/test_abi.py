@@ -99,7 +99,6 @@ def test_prefill_validation(L):
     need = gdn.gdn_prefill_workspace_size(1, 64, 2, 6)
     assert call_prefill(L, ws_bytes=need - 1) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL
     assert call_prefill(L, ws=0) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL
-    assert call_prefill(L, cs_in=FAKE, cs_out=FAKE) == gdn.GDN_ERR_INVALID_ARGUMENT  # aliasing conv rows
     # the workspace must be 16-byte aligned, as the header states
     assert call_prefill(L, ws=FAKE + 8) == gdn.GDN_ERR_INVALID_ARGUMENT
     assert call_prefill(L, B=0, T=0, ws=0, ws_bytes=0) == gdn.GDN_OK  # empty batch: nothing to do
@@ -116,6 +115,20 @@ def test_varlen_validation(L):
     assert call(Hv=9) == gdn.GDN_ERR_UNSUPPORTED
     assert call(ws_bytes=10) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL
     assert call(cu=FAKE + 1) == gdn.GDN_ERR_INVALID_ARGUMENT
+
+
+def test_varlen_slots_validation(L):
+    def call(cu=FAKE, slots=FAKE, n_rows=4, N=2, T_tot=100, Hv=6):
+        ws_bytes = gdn.gdn_prefill_varlen_workspace_size(N, T_tot, 2, 6)
+        return L.gdn_prefill_varlen_slots(_p(), _p(), _p(), _p(), _p(), _p(), None, None, None, _p(), _p(),
+                                          _p(cu), _p(slots), n_rows, N, T_tot, 2, Hv, 128, 128, 0.1, 1.0, _p(),
+                                          ws_bytes, None)
+    assert call(slots=0) == gdn.GDN_ERR_INVALID_ARGUMENT  # the table is required
+    assert call(cu=0) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(n_rows=-1) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(slots=FAKE + 2) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert call(Hv=9) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(N=-1) == gdn.GDN_ERR_INVALID_ARGUMENT
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
@@ -200,5 +213,4 @@ def test_noalloc_validation(L):
     assert call(dk=64) == gdn.GDN_ERR_UNSUPPORTED
     assert call(Hv=5) == gdn.GDN_ERR_UNSUPPORTED
     assert call(q=FAKE + 2) == gdn.GDN_ERR_INVALID_ARGUMENT
-    assert call(cs=FAKE) == gdn.GDN_ERR_INVALID_ARGUMENT  # conv rows in and out alias
     assert call(T=16384, Hqk=16, Hv=48) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL  # beyond the array

@@ -302,3 +302,127 @@ def test_stale_workspace_segmented():
         outs.append((host_u16(o), so.cpu().numpy()))
     np.testing.assert_array_equal(outs[0][0], outs[1][0])
     np.testing.assert_array_equal(outs[0][1], outs[1][1])
+
+
+# ---------------------------------------------------------------------------
+# slot tables into state / conv-row pools, conv rows in place
+# ---------------------------------------------------------------------------
+def _pool_case(lens, rows, seed, Hqk=2, Hv=6, bad=None):
+    """Packed sequences whose states and conv rows live in pools of `rows`
+    rows; sequence s uses row slots[s] (slots[bad] lies outside the pool)."""
+    x = inputs.make_prefill(T_list=lens, Hqk=Hqk, Hv=Hv, seed=seed, state_std=0.05, conv_state_std=1.0)
+    rng = np.random.default_rng(seed + 1)
+    N, d = len(lens), x["d"]
+    C_tot = 2 * Hqk * d + Hv * d
+    slots = rng.permutation(rows)[:N].astype(np.int32)
+    if bad is not None:
+        slots[bad] = rows + 5
+    ok = [i for i in range(N) if 0 <= slots[i] < rows]
+    pool_st = (rng.standard_normal((rows, Hv, d, d)) * 0.05).astype(np.float32)
+    pool_cs = inputs.bf16_bits(rng.standard_normal((rows, 3, C_tot)).astype(np.float32))
+    pool_st[slots[ok]] = x["state_in"][ok]
+    pool_cs[slots[ok]] = x["conv_state_in"][ok]
+    return x, slots, ok, pool_st, pool_cs
+
+
+def test_varlen_slots_in_place_against_oracle(oracle_lib):
+    """A slot table into pools updated in place (state and conv rows): the
+    named rows get the oracle's results with carry-in from those rows, other
+    rows stay untouched, and a sequence whose slot lies outside the pool
+    writes nothing (its output rows keep their previous contents)."""
+    import torch
+    import linear_attention_sequence_gdn_amd as gdn
+    lens = [70, 0, 200, 5, 64, 129, 2]
+    rows = 11
+    x, slots, ok, pool_st, pool_cs = _pool_case(lens, rows, seed=560, bad=3)
+    d, Hv = x["d"], x["Hv"]
+    st, cs = dev_f32(pool_st), dev_bf16(pool_cs)
+    o = torch.full((x["T_tot"], Hv, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    gdn.gdn_prefill_varlen(dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"]), dev_f32(x["a"]), dev_f32(x["b"]),
+                           dev_bf16(x["conv_w"]), dev_i32(x["cu_seqlens"]), gate_scale=x["gate_scale"],
+                           state_in=st, state_out=st, conv_state_in=cs, conv_state_out=cs, o=o,
+                           slots=dev_i32(slots))
+    torch.cuda.synchronize()
+    og, sg, cg = host_bf16(o), st.cpu().numpy(), host_u16(cs)
+    cu = x["cu_seqlens"]
+    # the oracle on the sequences that have a slot, carried in from their rows
+    sub = dict(x)
+    idx = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in ok])
+    for key in ("q", "k", "v", "a", "b"):
+        sub[key] = x[key][idx]
+    sub["cu_seqlens"] = np.concatenate([[0], np.cumsum([lens[s] for s in ok])]).astype(np.int32)
+    sub["state_in"] = pool_st[slots[ok]]
+    sub["conv_state_in"] = pool_cs[slots[ok]]
+    o_ref, s_ref, cs_ref = oracle_prefill(sub)
+    check_output(og[idx], o_ref)
+    check_state(sg[slots[ok]], s_ref)
+    np.testing.assert_array_equal(cg[slots[ok]], cs_ref)
+    untouched = sorted(set(range(rows)) - set(slots[ok].tolist()))
+    np.testing.assert_array_equal(sg[untouched], pool_st[untouched])
+    np.testing.assert_array_equal(cg[untouched], pool_cs[untouched])
+    assert np.all(og[cu[3]:cu[4]] == 7.0)  # the skipped sequence
+    # the empty sequence's row holds its carried state unchanged
+    np.testing.assert_array_equal(sg[slots[1]], pool_st[slots[1]])
+
+
+def test_varlen_slots_equal_plain_call_bitwise():
+    """Through a slot table (out of place, rows permuted) the results are bit
+    for bit those of the plain packed call on gathered rows."""
+    import torch
+    import linear_attention_sequence_gdn_amd as gdn
+    lens = [90, 64, 7, 200]
+    rows = 6
+    x, slots, ok, pool_st, pool_cs = _pool_case(lens, rows, seed=561)
+    o1, s1, c1 = gpu_prefill(x)
+    w = dev_bf16(x["conv_w"])
+    st_out = dev_f32(np.zeros_like(pool_st))
+    cs_out = torch.zeros((rows,) + pool_cs.shape[1:], dtype=torch.bfloat16, device="cuda")
+    o2, _, _ = gdn.gdn_prefill_varlen(dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"]), dev_f32(x["a"]),
+                                      dev_f32(x["b"]), w, dev_i32(x["cu_seqlens"]), gate_scale=x["gate_scale"],
+                                      state_in=dev_f32(pool_st), state_out=st_out,
+                                      conv_state_in=dev_bf16(pool_cs), conv_state_out=cs_out, slots=dev_i32(slots))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_u16(o2), host_u16(o1))
+    np.testing.assert_array_equal(st_out.cpu().numpy()[slots], s1.cpu().numpy())
+    np.testing.assert_array_equal(host_u16(cs_out)[slots], host_u16(c1))
+
+
+def test_conv_rows_in_place_segmented(oracle_lib):
+    """conv_state_out == conv_state_in on a sequence cut into segments, where
+    later segments restart from the sequence start (and so read the incoming
+    conv rows) and others are recomputed in order: bit for bit the
+    out-of-place result, which the oracle checks."""
+    import torch
+    import linear_attention_sequence_gdn_amd as gdn
+    T = 8192 + 37
+    x = inputs.make_prefill(T_list=[T], Hqk=2, Hv=6, seed=562, state_std=0.05, conv_state_std=1.0)
+    x["a"][:, :3] = -9.0
+    x["a"][4000:4400, :3] = 5.0
+    o1, s1, c1 = gpu_prefill(x, uniform_T=T)
+    compare(x, o1, s1, c1)
+    d = x["d"]
+    cs = dev_bf16(x["conv_state_in"])
+    o2, s2, _ = gdn.gdn_prefill(dev_bf16(x["q"].reshape(1, T, 2, d)), dev_bf16(x["k"].reshape(1, T, 2, d)),
+                                dev_bf16(x["v"].reshape(1, T, 6, d)), dev_f32(x["a"].reshape(1, T, 6)),
+                                dev_f32(x["b"].reshape(1, T, 6)), dev_bf16(x["conv_w"]), gate_scale=x["gate_scale"],
+                                state_in=dev_f32(x["state_in"]), conv_state_in=cs, conv_state_out=cs)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_u16(o2.reshape(T, 6, d)), host_u16(o1))
+    np.testing.assert_array_equal(s2.cpu().numpy(), s1.cpu().numpy())
+    np.testing.assert_array_equal(host_u16(cs), host_u16(c1))
+
+
+def test_conv_rows_in_place_short_sequences(oracle_lib):
+    """In place with sequences shorter than the conv window: the new rows
+    reach back into the incoming ones, which are read before they are
+    overwritten."""
+    import torch
+    import linear_attention_sequence_gdn_amd as gdn
+    x = inputs.make_prefill(T_list=[1, 2, 0, 3, 40], Hqk=2, Hv=6, seed=563, state_std=0.05, conv_state_std=1.0)
+    _, _, cs_ref = oracle_prefill(x)
+    cs = dev_bf16(x["conv_state_in"])
+    gdn.gdn_prefill_varlen(dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"]), dev_f32(x["a"]), dev_f32(x["b"]),
+                           dev_bf16(x["conv_w"]), dev_i32(x["cu_seqlens"]), gate_scale=x["gate_scale"],
+                           state_in=dev_f32(x["state_in"]), conv_state_in=cs, conv_state_out=cs)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_u16(cs), cs_ref)
