@@ -12,6 +12,8 @@ under "configs".  Prints ONE JSON line.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS]
                   [--no-cpu-baseline] [--only LEG ...] [--calibrate-copy]
   python bench.py --traffic-report FETCH_CSV WRITE_CSV
+  python bench.py --counter-report OUT_MD DB [DB ...] [--counter-command CMD]
+  python bench.py --trace-report OUT_MD DB [--counter-command CMD]
 
 --only restricts the run to some legs (prefill, decode, decode_multi,
 backward, configs), for profiling; the JSON line then holds those legs.
@@ -21,7 +23,9 @@ transfer of known size.  --traffic-report turns two such passes (FETCH_SIZE,
 then WRITE_SIZE; rocprofv3's counter_collection.csv files) into HBM bytes per
 launch of each kernel, scaled by what the counters read for the copy, and
 writes them to profiles/traffic.json tagged with the digest of the kernel
-sources they were taken on.
+sources they were taken on.  --counter-report summarises rocprofv3 --pmc
+databases (one per pass) per kernel: matrix-core busy fraction and FLOP, LDS
+instructions, bank conflicts and issue waits.
 
 Timing: HIP events on the stream the library launches on.  Before anything is
 timed, each leg runs its own work back to back until at least --settle-ms of
@@ -260,7 +264,7 @@ def source_digest(files=FWD_SOURCES):
 
 COPY_BYTES = 256 << 20
 TRAFFIC_KERNELS = {"prefill_chain": "chain_kernel", "prefill_prep": "prep_kernel",
-                   "prefill_setup": "setup_kernel", "decode": "decode_step_kernel",
+                   "prefill_setup": "setup_kernel", "decode": "decode_persist_kernel",
                    "decode_conv_shift": "conv_shift_qk_kernel<1>",
                    "decode_multi": "decode_head_kernel<4>", "decode_multi_conv_shift": "conv_shift_qk_kernel<4>"}
 BWD_KERNELS = ("bwd_prep_kernel", "bwd_local_kernel", "bwd_fwd_kernel", "bwd_chain_kernel", "bwd_grad_kernel",
@@ -326,6 +330,92 @@ def traffic_report(fetch_csv, write_csv):
         json.dump(out, fh, indent=1)
         fh.write("\n")
     print("wrote", path)
+
+
+XCDS, CUS, SIMDS_PER_CU = 8, 256, 4
+
+
+def counter_report(out_md, dbs, command=""):
+    """Per-kernel averages (per dispatch) of the counters in rocprofv3
+    databases (one --pmc pass each), and what follows from them:
+
+    * MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GUI cycles x 256 CUs x 4 SIMDs),
+      the fraction of the kernel's time the matrix cores are busy.
+      GRBM_GUI_ACTIVE reads the sum over the 8 XCDs, so one XCD's active
+      cycles are a eighth of it.
+    * matrix-core FLOP = 512 per MOP (SQ_INSTS_VALU_MFMA_MOPS_*).
+    * LDS: instructions, bank-conflict cycles per CU as a fraction of the
+      active cycles, and the share of wave cycles spent waiting to issue an
+      LDS instruction (SQ_WAIT_INST_LDS) or any instruction (SQ_WAIT_INST_ANY).
+    Writes a markdown table to out_md."""
+    import collections
+    import re
+    import sqlite3
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for db in dbs:
+        con = sqlite3.connect(db)
+        for kname, ctr, val in con.execute(
+                "select kernel_name, counter_name, value from counters_collection"):
+            m = re.search(r"(\w+(?:<[^>]*>)?)\(", kname)
+            acc[m.group(1) if m else kname][ctr].append(float(val))
+    lines = ["# Counter summary", "", "Command(s):", ""] + [f"    {c_}" for c_ in command.split(" ;; ") if c_] + [""]
+    for k_, ctrs in sorted(acc.items()):
+        avg = {c_: sum(v_) / len(v_) for c_, v_ in ctrs.items()}
+        n = max(len(v_) for v_ in ctrs.values())
+        lines += [f"## {k_} ({n} dispatches per pass)", "", "| counter | mean per dispatch |", "|---|---|"]
+        lines += [f"| {c_} | {v_:,.0f} |" for c_, v_ in sorted(avg.items())]
+        gui = avg.get("GRBM_GUI_ACTIVE")
+        der = []
+        if gui:
+            cyc = gui / XCDS
+            der.append(("active cycles per XCD", f"{cyc:,.0f}"))
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+                der.append(("MFMA busy (of all SIMDs' cycles)",
+                            f"{avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * CUS * SIMDS_PER_CU):.3f}"))
+            f16 = 512 * (avg.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0) + avg.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0))
+            if f16:
+                der.append(("fp16/bf16 matrix-core FLOP per dispatch", f"{f16 / 1e9:.2f} G"))
+                der.append(("fp16/bf16 FLOP per cycle / dense peak (4096 per CU-cycle)",
+                            f"{f16 / (cyc * CUS * 4096):.3f}"))
+            if "SQ_LDS_BANK_CONFLICT" in avg:
+                der.append(("LDS bank-conflict cycles per CU / active cycles",
+                            f"{avg['SQ_LDS_BANK_CONFLICT'] / CUS / cyc:.3f}"))
+        if "SQ_WAVE_CYCLES" in avg:
+            wc = avg["SQ_WAVE_CYCLES"]
+            for c_, name in (("SQ_WAIT_INST_LDS", "wave cycles waiting to issue LDS"),
+                             ("SQ_WAIT_INST_ANY", "wave cycles waiting to issue any instruction"),
+                             ("SQ_ACTIVE_INST_VALU", "wave cycles issuing VALU (incl. MFMA)")):
+                if c_ in avg:
+                    der.append((name, f"{avg[c_] / wc:.3f}"))
+        if der:
+            lines += ["", "| derived | value |", "|---|---|"] + [f"| {a_} | {b_} |" for a_, b_ in der]
+        lines.append("")
+    open(out_md, "w").write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def trace_report(out_md, db, command="", tail=40):
+    """Per-kernel dispatch count and mean / min / max duration from a
+    rocprofv3 --kernel-trace database, as a markdown table in out_md, with the
+    mean over each kernel's last `tail` dispatches: the bench's timed steps
+    (K plain calls, then K with events) come last, after the settle phase."""
+    import re
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, count(*), avg(duration), min(duration), max(duration), sum(duration) "
+                       "from kernels group by name order by sum(duration) desc").fetchall()
+    total = sum(r[5] for r in rows) or 1.0
+    lines = ["# Kernel trace summary", "", "Command:", "", f"    {command}", "",
+             f"| kernel | dispatches | mean us | mean of the last {tail} us | min us | max us | share of kernel time |",
+             "|---|---|---|---|---|---|---|"]
+    for name, n, avg, mn, mx, tot in rows:
+        m = re.search(r"(\w+(?:<[^>]*>)?)\(", name)
+        last = [r[0] for r in con.execute("select duration from kernels where name = ? order by start desc limit ?",
+                                          (name, tail))]
+        lines.append(f"| {m.group(1) if m else name} | {n} | {avg / 1e3:.2f} | {sum(last) / len(last) / 1e3:.2f} | "
+                     f"{mn / 1e3:.2f} | {mx / 1e3:.2f} | {tot / total:.3f} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def _sum_or_none(*xs):
@@ -712,9 +802,18 @@ def main():
     ap.add_argument("--only", nargs="+", choices=LEGS)
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--traffic-report", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--counter-report", nargs="+", metavar=("OUT_MD", "DB"))
+    ap.add_argument("--counter-command", default="")
+    ap.add_argument("--trace-report", nargs=2, metavar=("OUT_MD", "DB"))
     args = ap.parse_args()
     if args.traffic_report:
         traffic_report(*args.traffic_report)
+        return
+    if args.trace_report:
+        trace_report(*args.trace_report, command=args.counter_command)
+        return
+    if args.counter_report:
+        counter_report(args.counter_report[0], args.counter_report[1:], args.counter_command)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -781,7 +880,7 @@ def main():
             line["decode"] = {
                 "metric": "decode us/step (B=256, 16QK/48V, 64 in-place steps)",
                 "value": dc["us_per_step"], "unit": "us/step", "higher_is_better": False,
-                "roofline": {"bound": "hbm", "kernel": "decode step (decode_step_kernel + conv_shift_qk_kernel<1>)",
+                "roofline": {"bound": "hbm", "kernel": "decode step (decode_persist_kernel + conv_shift_qk_kernel<1>)",
                              "achieved": dec_gbs, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                              "frac": dec_gbs * 1e9 / PEAK_HBM,
                              "traffic": _sum_or_none(load_traffic("decode", digest),

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void decode_head_kernel(DecodeArgs p)
     __shared__ float s_red[TM][4];
     __shared__ float s_ab[TM][2];
     __shared__ float s_kq[TM];
-    __shared__ f32x4 s_part[2][8][32][2];  // [buffer][row group][col group][k^/q^ partial]
+    __shared__ f32x4 s_part[2][2][8][32];  // [buffer][k^/q^ partial][row group][col group]
 
     const int t = threadIdx.x;
     const int h = blockIdx.x % p.Hv;
@@ -168,14 +168,14 @@ __global__ __launch_bounds__(kThreads) void decode_head_kernel(DecodeArgs p)
             pq += st[r] * qr;
         }
         // (the same summation order as the single-token build)
-        s_part[i & 1][rg][cg][0] = pk;
-        s_part[i & 1][rg][cg][1] = pq;
+        s_part[i & 1][0][rg][cg] = pk;
+        s_part[i & 1][1][rg][cg] = pq;
         __syncthreads();
         f32x4 PK = {0.f, 0.f, 0.f, 0.f}, PQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            PK += s_part[i & 1][r][cg][0];
-            PQ += s_part[i & 1][r][cg][1];
+            PK += s_part[i & 1][0][r][cg];
+            PQ += s_part[i & 1][1][r][cg];
         }
         const float al = s_ab[i][0], be = s_ab[i][1], kq = s_kq[i];
         f32x4 u, ov;
@@ -197,76 +197,77 @@ __global__ __launch_bounds__(kThreads) void decode_head_kernel(DecodeArgs p)
     for (int r = 0; r < 16; ++r) __builtin_nontemporal_store(st[r], dst + r * 256);
 }
 
-// ---- one token, no slot table: the lean build the single-step entry point
-//      uses (fewest registers, so the most resident waves for the stream)
-
-// conv (width 4) + SiLU of one channel, and the in-place shift of its rows
-__device__ __forceinline__ float conv_channel(const DecodeArgs &p, int b, long C_tot, long c,
-                                              uint16_t x)
+// One token per sequence: a persistent workgroup walks the (sequence, V head)
+// items blockIdx.x, blockIdx.x + gridDim.x, ..., and requests the next item's
+// state into a second set of registers while it works on the current one, so
+// that state loads stay in flight through the prologue and the update (a
+// one-item workgroup leaves HBM idle while it computes).  Two workgroups per
+// CU.  The arithmetic is decode_head_kernel's for one token, operation for
+// operation, so a T-token call of that kernel equals T calls of this one bit
+// for bit.
+__device__ __forceinline__ void decode_one(const DecodeArgs &p, int item, int row, f32x4 (&st)[16],
+                                           f32x4 (&sn)[16], int next_item, int next_row, float *s_q, float *s_k,
+                                           float *s_v, float *s_red, float *s_ab, float *s_kq,
+                                           f32x4 (*s_part)[8][32])
 {
-    uint16_t *cs = p.conv_state + (long)b * 3 * C_tot + c;
-    uint16_t h0 = cs[0], h1 = cs[C_tot], h2 = cs[2 * C_tot];
-    uint2 w = *reinterpret_cast<const uint2 *>(p.conv_w + c * 4);
-    float y = bf16_lo(w.x) * bf16_to_f32(h0) + bf16_hi(w.x) * bf16_to_f32(h1) +
-              bf16_lo(w.y) * bf16_to_f32(h2) + bf16_hi(w.y) * bf16_to_f32(x);
-    cs[0] = h1;
-    cs[C_tot] = h2;
-    cs[2 * C_tot] = x;
-    return silu_f(y);
-}
-
-__device__ __forceinline__ float conv_channel_ro(const DecodeArgs &p, int b, long C_tot, long c, uint16_t x)
-{
-    const uint16_t *cs = p.conv_state + (long)b * 3 * C_tot + c;
-    const uint2 w = *reinterpret_cast<const uint2 *>(p.conv_w + c * 4);
-    const float y = bf16_lo(w.x) * bf16_to_f32(cs[0]) + bf16_hi(w.x) * bf16_to_f32(cs[C_tot]) +
-                    bf16_lo(w.y) * bf16_to_f32(cs[2 * C_tot]) + bf16_hi(w.y) * bf16_to_f32(x);
-    return silu_f(y);
-}
-
-__global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeArgs p)
-{
-    __shared__ float s_q[kD], s_k[kD], s_v[kD];
-    __shared__ float s_red[4];
-    __shared__ float s_ab[2];
-    __shared__ float s_kq;
-    __shared__ f32x4 s_part[8][32][2];  // [row group][col group][k^/q^ partial]
-
     const int t = threadIdx.x;
-    const int h = blockIdx.x % p.Hv;
-    const int b = blockIdx.x / p.Hv;
+    const int h = item % p.Hv;
+    const int b = item / p.Hv;
     const int g = h / (p.Hv / p.Hqk);
     const long C_tot = 2L * p.Hqk * kD + (long)p.Hv * kD;
     const int lane = t & 63, wave = t >> 6;
-
-    // the state is requested first, so that its latency covers the prologue:
-    // thread owns columns 4cg..4cg+3, rows rg + 8i
     const int cg = t & 31, rg = t >> 5;
-    const long head0 = ((long)b * p.Hv + h) * kD * kD;
-    const f32x4 *src = reinterpret_cast<const f32x4 *>(p.state_in + head0) + rg * 32 + cg;
-    f32x4 *dst = reinterpret_cast<f32x4 *>(p.state_out + head0) + rg * 32 + cg;
-    f32x4 st[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) st[i] = __builtin_nontemporal_load(src + i * 256);
+    f32x4 *dst = reinterpret_cast<f32x4 *>(p.state_out + ((long)row * p.Hv + h) * kD * kD) + rg * 32 + cg;
 
-    // ---- prologue: q_g (threads 0..127) and k_g (128..255), read-only conv
-    //      rows; v_h (threads 0..127) with its in-place shift; the gates
+    // ---- prologue loads: q_g (threads 0..127) and k_g (128..255) from the
+    //      read-only conv rows; v_h (threads 0..127); the gates
+    const bool isq = t < kD;
+    const int ch = t & (kD - 1);
+    const long c = isq ? (long)g * kD + ch : (long)p.Hqk * kD + (long)g * kD + ch;
+    const uint16_t *cs = p.conv_state + (long)row * 3 * C_tot + c;
+    uint16_t win[4];
+    win[0] = cs[0];
+    win[1] = cs[C_tot];
+    win[2] = cs[2 * C_tot];
+    win[3] = (isq ? p.q : p.k)[((long)b * p.Hqk + g) * kD + ch];
+    const long cv = 2L * p.Hqk * kD + (long)h * kD + ch;
+    uint16_t *csv = p.conv_state + (long)row * 3 * C_tot + cv;
+    uint16_t wv[4];
+    float av = 0.f, bv = 0.f;
+    if (isq) {
+        wv[0] = csv[0];
+        wv[1] = csv[C_tot];
+        wv[2] = csv[2 * C_tot];
+        wv[3] = p.v[((long)b * p.Hv + h) * kD + ch];
+    } else if (ch == 0) {
+        av = p.a[(long)b * p.Hv + h];
+        bv = p.b[(long)b * p.Hv + h];
+    }
+    // ---- the next item's state, after the prologue loads (loads complete in
+    //      order, so waiting for the prologue does not wait for these)
+    if (next_row >= 0) {
+        const f32x4 *srcn = reinterpret_cast<const f32x4 *>(p.state_in + ((long)next_row * p.Hv + next_item % p.Hv) *
+                                                                            kD * kD) + rg * 32 + cg;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sn[i] = __builtin_nontemporal_load(srcn + i * 256);
+    }
     {
-        const bool isq = t < kD;
-        const int ch = t & (kD - 1);
-        const long c = isq ? (long)g * kD + ch : (long)p.Hqk * kD + (long)g * kD + ch;
-        const uint16_t x = isq ? p.q[((long)b * p.Hqk + g) * kD + ch] : p.k[((long)b * p.Hqk + g) * kD + ch];
-        const float z = conv_channel_ro(p, b, C_tot, c, x);
-        const float ss = wave_sum(z * z);
+        float z[1];
+        conv_tokens<1>(win, p.conv_w + c * 4, 1, z);
+        const float ss = wave_sum(z[0] * z[0]);
         if (lane == 0) s_red[wave] = ss;
-        if (isq) s_q[ch] = z; else s_k[ch] = z;
+        if (isq) s_q[ch] = z[0]; else s_k[ch] = z[0];
         if (isq) {
-            const long cv = 2L * p.Hqk * kD + (long)h * kD + ch;
-            s_v[ch] = conv_channel(p, b, C_tot, cv, p.v[((long)b * p.Hv + h) * kD + ch]);
-        }
-        if (t == kD) {
-            s_ab[0] = __expf(-p.gate_scale * softplus_f(p.a[(long)b * p.Hv + h]));
-            s_ab[1] = sigmoid_f(p.b[(long)b * p.Hv + h]);
+            float zv[1];
+            conv_tokens<1>(wv, p.conv_w + cv * 4, 1, zv);
+            s_v[ch] = zv[0];
+            // the last three raw rows become the carried rows
+            csv[0] = wv[1];
+            csv[C_tot] = wv[2];
+            csv[2 * C_tot] = wv[3];
+        } else if (ch == 0) {
+            s_ab[0] = __expf(-p.gate_scale * softplus_f(av));
+            s_ab[1] = sigmoid_f(bv);
         }
     }
     __syncthreads();
@@ -278,26 +279,26 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeArgs p)
     if (wave == 0) {
         float kq = s_k[lane] * s_q[lane] + s_k[lane + 64] * s_q[lane + 64];
         kq = wave_sum(kq);
-        if (lane == 0) s_kq = kq;
+        if (lane == 0) s_kq[0] = kq;
     }
-    // ---- S^T k^ and S^T q^
+    // ---- S^T k^ and S^T q^, the output and the new state
     f32x4 pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float kr = s_k[rg + 8 * i], qr = s_q[rg + 8 * i];
-        pk += st[i] * kr;
-        pq += st[i] * qr;
+    for (int r = 0; r < 16; ++r) {
+        const float kr = s_k[rg + 8 * r], qr = s_q[rg + 8 * r];
+        pk += st[r] * kr;
+        pq += st[r] * qr;
     }
-    s_part[rg][cg][0] = pk;
-    s_part[rg][cg][1] = pq;
+    s_part[0][rg][cg] = pk;
+    s_part[1][rg][cg] = pq;
     __syncthreads();
     f32x4 PK = {0.f, 0.f, 0.f, 0.f}, PQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-        PK += s_part[r][cg][0];
-        PQ += s_part[r][cg][1];
+        PK += s_part[0][r][cg];
+        PQ += s_part[1][r][cg];
     }
-    const float al = s_ab[0], be = s_ab[1], kq = s_kq;
+    const float al = s_ab[0], be = s_ab[1], kq = s_kq[0];
     f32x4 u, ov;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -305,15 +306,51 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeArgs p)
         ov[e] = (al * PQ[e] + u[e] * kq) * p.q_scale;
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float kr = s_k[rg + 8 * i];
-        __builtin_nontemporal_store(st[i] * al + u * kr, dst + i * 256);
-    }
+    for (int r = 0; r < 16; ++r) __builtin_nontemporal_store(st[r] * al + u * s_k[rg + 8 * r], dst + r * 256);
     if (rg == 0) {
         uint2 packed;
         packed.x = pack_bf16x2(ov[0], ov[1]);
         packed.y = pack_bf16x2(ov[2], ov[3]);
         *reinterpret_cast<uint2 *>(p.o + ((long)b * p.Hv + h) * kD + 4 * cg) = packed;
+    }
+    __syncthreads();  // the next item rewrites the LDS arrays
+}
+
+__global__ __launch_bounds__(kThreads, 2) void decode_persist_kernel(DecodeArgs p)
+{
+    __shared__ float s_q[kD], s_k[kD], s_v[kD];
+    __shared__ float s_red[4];
+    __shared__ float s_ab[2];
+    __shared__ float s_kq[1];
+    __shared__ f32x4 s_part[2][8][32];  // [k^/q^ partial][row group][col group]: a wave's 16-byte
+                                        // accesses are consecutive (no bank conflicts)
+
+    const int items = p.B * p.Hv;
+    const int t = threadIdx.x, cg = t & 31, rg = t >> 5;
+    int item = blockIdx.x;
+    if (item >= items) return;
+    int row = pool_row(p, item / p.Hv);
+    f32x4 st[16], sn[16];
+    if (row >= 0) {
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(p.state_in + ((long)row * p.Hv + item % p.Hv) * kD * kD) +
+                           rg * 32 + cg;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st[i] = __builtin_nontemporal_load(src + i * 256);
+    }
+    for (; item < items; item += gridDim.x) {
+        const int next = item + gridDim.x;
+        const int next_row = next < items ? pool_row(p, next / p.Hv) : -1;
+        if (row >= 0)  // else the slot lies outside the pool: the sequence is skipped
+            decode_one(p, item, row, st, sn, next, next_row, s_q, s_k, s_v, s_red, s_ab, s_kq, s_part);
+        else if (next_row >= 0) {
+            const f32x4 *srcn = reinterpret_cast<const f32x4 *>(p.state_in + ((long)next_row * p.Hv + next % p.Hv) *
+                                                                                kD * kD) + rg * 32 + cg;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sn[i] = __builtin_nontemporal_load(srcn + i * 256);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st[i] = sn[i];
+        row = next_row;
     }
 }
 
@@ -361,13 +398,17 @@ hipError_t launch_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v
     const long grid = (long)B * Hv;
     const long pairs = (long)B * Hqk * kD;  // 2 * Hqk * kD channels, two per thread
     const dim3 shift_grid((unsigned)((pairs + kThreads - 1) / kThreads));
-    // a single token takes a lean build (fewer registers, more resident waves)
-    if (T == 1 && !slots)
-        hipLaunchKernelGGL(decode_step_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
-    else if (T == 1)
-        hipLaunchKernelGGL(decode_head_kernel<1>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
-    else
+    if (T == 1) {
+        // persistent: two workgroups per CU, each walking items gridDim apart
+        int dev = 0, cus = 0;
+        hipError_t e0 = hipGetDevice(&dev);
+        if (e0 == hipSuccess) e0 = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e0 != hipSuccess) return e0;
+        const unsigned pg = (unsigned)(grid < 2L * cus ? grid : 2L * cus);
+        hipLaunchKernelGGL(decode_persist_kernel, dim3(pg), dim3(kThreads), 0, stream, p);
+    } else {
         hipLaunchKernelGGL(decode_head_kernel<kMaxDecodeTokens>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (T == 1)
