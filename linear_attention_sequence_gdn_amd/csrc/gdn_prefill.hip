@@ -342,18 +342,18 @@ __device__ __forceinline__ float reduce_scatter16(const float (&v)[16], int lane
 }
 
 // Column c of the inverse of a 16 x 16 unit lower-triangular block I + A (A
-// strictly lower, row stride kAL), by right-looking substitution: once y_m is
+// strictly lower, row stride LD), by right-looking substitution: once y_m is
 // final it is removed from every later row, y_i -= A[i][m] y_m, so the chain
 // of dependent operations is one multiply-add per row.  Expanded at compile
 // time so that y stays in registers.
-template <int M>
+template <int M, int LD>
 struct SolveCol16 {
     static __device__ __forceinline__ void run(float (&y)[16], const float *A)
     {
         if constexpr (M < 15) {
 #pragma unroll
-            for (int i = M + 1; i < 16; ++i) y[i] -= A[i * kAL + M] * y[M];
-            SolveCol16<M + 1>::run(y, A);
+            for (int i = M + 1; i < 16; ++i) y[i] -= A[i * LD + M] * y[M];
+            SolveCol16<M + 1, LD>::run(y, A);
         }
     }
 };
@@ -429,40 +429,31 @@ __device__ constexpr int kPrepKQ[4][3][2] = {{{1, 0}, {1, 1}, {0, 0}}, {{0, 0}, 
                                              {{2, 0}, {2, 1}, {0, 0}}, {{3, 0}, {3, 1}, {3, 3}}};
 __device__ constexpr int kPrepNKK[4] = {3, 2, 3, 2}, kPrepNKQ[4] = {2, 3, 2, 3};
 
-// 16 x 16 tile slots of the two fp32 work matrices (A in the first, X in the
-// second; tile (i, j) of a matrix at row 16i, column 16j, row stride kAL):
-// byte offsets from the start of the first.  The diagonal blocks of
-// (I + A)^-1 of up to four heads (head jj, block w) are solved together and
-// parked, for the whole per-head loop, in tiles that loop never writes (A's
-// diagonal and upper tiles, X's upper tiles); the diagonal tiles of A that
-// they are solved from live only until then, in the lower tiles of both
-// matrices and X's diagonal tiles.
-__host__ __device__ constexpr int prep_slot(int m, int i, int j) { return (m * 64 * kAL + 16 * i * kAL + 16 * j) * 4; }
-__device__ constexpr int kPrepXd[4][4] = {
-    {prep_slot(0, 0, 0), prep_slot(0, 1, 1), prep_slot(0, 2, 2), prep_slot(0, 3, 3)},
-    {prep_slot(0, 0, 1), prep_slot(0, 0, 2), prep_slot(0, 0, 3), prep_slot(0, 1, 2)},
-    {prep_slot(0, 1, 3), prep_slot(0, 2, 3), prep_slot(1, 0, 1), prep_slot(1, 0, 2)},
-    {prep_slot(1, 0, 3), prep_slot(1, 1, 2), prep_slot(1, 1, 3), prep_slot(1, 2, 3)}};
-__device__ constexpr int kPrepAd[4][4] = {
-    {prep_slot(0, 1, 0), prep_slot(0, 2, 1), prep_slot(1, 2, 2), prep_slot(1, 3, 3)},
-    {prep_slot(0, 2, 0), prep_slot(0, 3, 1), prep_slot(1, 1, 0), prep_slot(1, 3, 2)},
-    {prep_slot(0, 3, 0), prep_slot(0, 3, 2), prep_slot(1, 2, 1), prep_slot(1, 0, 0)},
-    {prep_slot(1, 2, 0), prep_slot(1, 3, 0), prep_slot(1, 3, 1), prep_slot(1, 1, 1)}};
+// The per-head phase works on up to kPrepHeads V heads at a time, each in a
+// region of its own: the ten 16 x 16 tiles (i, j), i >= j, of its lower
+// triangle (first A, then, in place, X = (I + A)^-1) and one temporary tile,
+// fp32 with row stride kHLD (17: the column reads of the fp32 products fall in
+// distinct banks).  The regions reuse the LDS of the q^ / k^ tiles.
+constexpr int kPrepHeads = 3;
+constexpr int kHLD = 17;
+constexpr int kHTile = 16 * kHLD;                    // floats per tile slot
+constexpr int kHSlots = 11;                          // ten lower tiles and a temporary
+__host__ __device__ constexpr int htri(int i, int j) { return i * (i + 1) / 2 + j; }
+constexpr int kPrepR = 2 * kPrepTile > kPrepHeads * kHSlots * kHTile * 4 ? 2 * kPrepTile
+                                                                        : kPrepHeads * kHSlots * kHTile * 4;
 
 // Four resident workgroups per CU (at most 128 VGPRs): the per-head phases
 // are short stretches between barriers, and other workgroups fill the waits.
 __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void prep_kernel(PrefillArgs p, Workspace ws)
 {
-    // LDS plan: [R0] q^ (fp16) -> A (fp32); [R1] k^ (fp16) -> X = (I+A)^-1
-    // (fp32); product slots of the inverse; the gates of four heads
-    __shared__ __attribute__((aligned(16))) uint8_t R[2 * kPrepTile];
-    uint8_t *R0 = R, *R1 = R + kPrepTile;
-    __shared__ __attribute__((aligned(16))) float Msc[4 * 256];
-    __shared__ __attribute__((aligned(16))) float s_gam2[4 * 64];
-    __shared__ __attribute__((aligned(16))) float s_beta[4 * 64];
-    _Float16 *Qs = reinterpret_cast<_Float16 *>(R0), *Ks = reinterpret_cast<_Float16 *>(R1);
-    float *As = reinterpret_cast<float *>(R0), *Xs = reinterpret_cast<float *>(R1);
+    // LDS plan: q^ and k^ (fp16 token-major tiles), then, reusing them, the
+    // head regions of the per-head phase; the gates of kPrepHeads heads
+    __shared__ __attribute__((aligned(16))) uint8_t R[kPrepR];
+    __shared__ __attribute__((aligned(16))) float s_gam2[kPrepHeads * 64];
+    __shared__ __attribute__((aligned(16))) float s_beta[kPrepHeads * 64];
+    _Float16 *Qs = reinterpret_cast<_Float16 *>(R), *Ks = reinterpret_cast<_Float16 *>(R + kPrepTile);
+    float *Hs = reinterpret_cast<float *>(R);
 
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -561,9 +552,10 @@ void prep_kernel(PrefillArgs p, Workspace ws)
     }
     __syncthreads();  // the q^ / k^ tiles are dead from here on
 
-    for (int j0 = 0; j0 < G; j0 += 4) {
-        // gates of heads j0 .. j0+3 of the group (wave w: head j0 + w)
-        if (j0 + wave < G) {
+    for (int j0 = 0; j0 < G; j0 += kPrepHeads) {
+        const int jn = min(kPrepHeads, G - j0);
+        // gates of heads j0 .. j0 + jn - 1 of the group (wave w: head j0 + w)
+        if (wave < jn) {
             if (j0 > 0) {
                 av = bv = 0.f;
                 if (lane < n) {
@@ -577,182 +569,149 @@ void prep_kernel(PrefillArgs p, Workspace ws)
                        s_beta + 64 * wave, lane);
         }
         __syncthreads();
-        const int jn = min(4, G - j0);
-        // ---- diagonal blocks of X = (I + A)^-1 of these heads: wave w builds
-        //      A's diagonal tile (w, w) of every head (K K^T tile (w, w) is its
-        //      first tile, kk[0]), then solves them all at once by forward
-        //      substitution, lane (q, c) taking column c of head q's block
-        {
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                if (jj >= jn) continue;
-                const float *gam2 = s_gam2 + 64 * jj, *beta = s_beta + 64 * jj;
-                const f32x4 gr = *reinterpret_cast<const f32x4 *>(gam2 + 16 * wave + 4 * q4);
-                const f32x4 br = *reinterpret_cast<const f32x4 *>(beta + 16 * wave + 4 * q4);
-                const float gj = gam2[16 * wave + c16];
-                float *ad = reinterpret_cast<float *>(R + kPrepAd[jj][wave]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float a = br[e] * kk[0][e] * __builtin_amdgcn_exp2f(gr[e] - gj);
-                    ad[(4 * q4 + e) * kAL + c16] = 4 * q4 + e > c16 ? a : 0.f;
-                }
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const int qh = min(q4, jn - 1);  // lanes of absent heads repeat the last one
-            const int ad_off = qh == 0 ? kPrepAd[0][wave] : qh == 1 ? kPrepAd[1][wave]
-                             : qh == 2 ? kPrepAd[2][wave] : kPrepAd[3][wave];
-            const int xd_off = qh == 0 ? kPrepXd[0][wave] : qh == 1 ? kPrepXd[1][wave]
-                             : qh == 2 ? kPrepXd[2][wave] : kPrepXd[3][wave];
-            float y[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) y[i] = i == c16 ? 1.f : 0.f;
-            SolveCol16<0>::run(y, reinterpret_cast<const float *>(R + ad_off));
-            if (q4 < jn) {
-                float *xd = reinterpret_cast<float *>(R + xd_off);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) xd[i * kAL + c16] = y[i];
-            }
-        }
-        __syncthreads();
+        // ---- A = strict_lower(diag(beta) K K^T * D) of every head of the
+        //      round, from the K K^T tiles this wave holds (a lane's four rows
+        //      are adjacent: one 16-byte read each of gam and beta per tile);
+        //      the diagonal tiles' entries on and above the diagonal are never
+        //      read.  P = (K Q^T)^T * D, lower incl. the diagonal, to the
+        //      records, from the K Q^T tiles: each gives half of a fragment
+        //      (key tile jt: elements 4 (jt % 2) .. +3); a diagonal tile of an
+        //      even key tile (fragments (0, 0) and (2, 1)) also writes the
+        //      zero half
         for (int jj = 0; jj < jn; ++jj) {
-            const long hc = (long)c * Hv + g * G + j0 + jj;
-            // this head's diagonal blocks of X
-            const int xd0 = kPrepXd[jj][0], xd1 = kPrepXd[jj][1], xd2 = kPrepXd[jj][2], xd3 = kPrepXd[jj][3];
-            auto XDt = [&](int i) {
-                return reinterpret_cast<float *>(R + (i == 0 ? xd0 : i == 1 ? xd1 : i == 2 ? xd2 : xd3));
-            };
             const float *gam2 = s_gam2 + 64 * jj, *beta = s_beta + 64 * jj;
-            // ---- A = strict_lower(diag(beta) K K^T * D) -> LDS, its tiles
-            //      below the diagonal (the diagonal ones were solved above),
-            //      without branches (a lane's four rows are adjacent: one
-            //      16-byte read each of gam and beta per tile)
+            float *Hh = Hs + jj * kHSlots * kHTile;
 #pragma unroll
-            for (int i = 1; i < 3; ++i) {
+            for (int i = 0; i < 3; ++i) {
                 if (i >= nkk) continue;
                 const int rt = kPrepKK[wave][i][0], ct = kPrepKK[wave][i][1];
                 const int jc = 16 * ct + c16;
                 const f32x4 gr = *reinterpret_cast<const f32x4 *>(gam2 + 16 * rt + 4 * q4);
                 const f32x4 br = *reinterpret_cast<const f32x4 *>(beta + 16 * rt + 4 * q4);
                 const float gj = gam2[jc];
+                float *tile = Hh + htri(rt, ct) * kHTile;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * rt + 4 * q4 + e;
-                    As[r * kAL + jc] = br[e] * kk[i][e] * __builtin_amdgcn_exp2f(gr[e] - gj);
+                    const float a = br[e] * kk[i][e] * __builtin_amdgcn_exp2f(gr[e] - gj);
+                    tile[(4 * q4 + e) * kHLD + c16] = (rt > ct || 4 * q4 + e > c16) ? a : 0.f;
                 }
             }
-            // ---- P = (K Q^T)^T * D, lower incl. the diagonal -> global: each
-            //      K Q^T tile gives half of a fragment (key tile jt: elements
-            //      4 (jt % 2) .. +3); a diagonal tile of an even key tile
-            //      (fragments (0, 0) and (2, 1)) also writes the zero half
-            {
-                uint8_t *pf = ws.hrec + hc * kRecBytes + kRecP;
+            const long hc = (long)c * Hv + g * G + j0 + jj;
+            uint8_t *pf = ws.hrec + hc * kRecBytes + kRecP;
 #pragma unroll
-                for (int i = 0; i < 3; ++i) {
-                    if (i >= nkq) continue;
-                    const int rt = kPrepKQ[wave][i][0], jt = kPrepKQ[wave][i][1];
-                    const int qi = 16 * rt + c16;
-                    const float gi = gam2[qi];
-                    const f32x4 gk = *reinterpret_cast<const f32x4 *>(gam2 + 16 * jt + 4 * q4);
-                    half4 hv;
+            for (int i = 0; i < 3; ++i) {
+                if (i >= nkq) continue;
+                const int rt = kPrepKQ[wave][i][0], jt = kPrepKQ[wave][i][1];
+                const int qi = 16 * rt + c16;
+                const float gi = gam2[qi];
+                const f32x4 gk = *reinterpret_cast<const f32x4 *>(gam2 + 16 * jt + 4 * q4);
+                half4 hv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int jc = 16 * jt + 4 * q4 + e;
+                    const float pv = p.q_scale * kq[i][e] * __builtin_amdgcn_exp2f(gi - gk[e]);
+                    hv[e] = (_Float16)(qi >= jc ? pv : 0.f);
+                }
+                uint8_t *dst = pf + (tri_frag(rt, jt >> 1) * 64 + lane) * 16 + 8 * (jt & 1);
+                *reinterpret_cast<half4 *>(dst) = hv;
+                if (jt == rt && (jt & 1) == 0) *reinterpret_cast<half4 *>(dst + 8) = half4{0, 0, 0, 0};
+            }
+        }
+        __syncthreads();
+        // ---- X = (I + A)^-1 of head j0 + w by wave w alone, in place in its
+        //      region, with wave-level synchronisation only: the four diagonal
+        //      blocks by forward substitution (lane (q, c) takes column c of
+        //      block q), then the blocks below them by the 2 x 2 block
+        //      recursion L^-1 = [[X_a, 0], [-X_b L_ba X_a, X_b]] within and
+        //      across the 32 x 32 halves, on the fp32 matrix cores; then T' =
+        //      X diag(beta) as A operands (rows = tokens i, contraction =
+        //      tokens j) to the record
+        if (wave < jn) {
+            float *Hh = Hs + wave * kHSlots * kHTile;
+            auto T = [&](int i, int j) { return Hh + htri(i, j) * kHTile; };
+            float *tmp = Hh + 10 * kHTile;
+            auto wave_sync = [] {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            };
+            {
+                float y[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) y[i] = i == c16 ? 1.f : 0.f;
+                const float *Ad = q4 == 0 ? T(0, 0) : q4 == 1 ? T(1, 1) : q4 == 2 ? T(2, 2) : T(3, 3);
+                SolveCol16<0, kHLD>::run(y, Ad);
+                wave_sync();
+                float *Xd = const_cast<float *>(Ad);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) Xd[i * kHLD + c16] = y[i];
+                wave_sync();
+            }
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            // X_10 = -X_11 (A_10 X_00), X_32 = -X_33 (A_32 X_22)
+            st16_f32(tmp, kHLD, mm16_f32(T(1, 0), kHLD, T(0, 0), kHLD, z, lane), lane);
+            wave_sync();
+            st16_f32(T(1, 0), kHLD, -mm16_f32(T(1, 1), kHLD, tmp, kHLD, z, lane), lane);
+            wave_sync();
+            st16_f32(tmp, kHLD, mm16_f32(T(3, 2), kHLD, T(2, 2), kHLD, z, lane), lane);
+            wave_sync();
+            st16_f32(T(3, 2), kHLD, -mm16_f32(T(3, 3), kHLD, tmp, kHLD, z, lane), lane);
+            wave_sync();
+            // M_20 = A_20 X_00 + A_21 X_10, M_21 = A_21 X_11, M_30, M_31 likewise, each over its A tile
+#pragma unroll
+            for (int i = 2; i < 4; ++i) {
+                f32x4 m = mm16_f32(T(i, 0), kHLD, T(0, 0), kHLD, z, lane);
+                m = mm16_f32(T(i, 1), kHLD, T(1, 0), kHLD, m, lane);
+                const f32x4 m1 = mm16_f32(T(i, 1), kHLD, T(1, 1), kHLD, z, lane);
+                wave_sync();
+                st16_f32(T(i, 0), kHLD, m, lane);
+                st16_f32(T(i, 1), kHLD, m1, lane);
+                wave_sync();
+            }
+            // X_31 = -(X_32 M_21 + X_33 M_31) (via tmp), X_21 = -X_22 M_21
+            {
+                f32x4 x = mm16_f32(T(3, 2), kHLD, T(2, 1), kHLD, z, lane);
+                x = mm16_f32(T(3, 3), kHLD, T(3, 1), kHLD, x, lane);
+                const f32x4 x21 = mm16_f32(T(2, 2), kHLD, T(2, 1), kHLD, z, lane);
+                wave_sync();
+                st16_f32(T(3, 1), kHLD, -x, lane);
+                st16_f32(T(2, 1), kHLD, -x21, lane);
+                wave_sync();
+            }
+            // X_30 = -(X_32 M_20 + X_33 M_30), X_20 = -X_22 M_20
+            {
+                f32x4 x = mm16_f32(T(3, 2), kHLD, T(2, 0), kHLD, z, lane);
+                x = mm16_f32(T(3, 3), kHLD, T(3, 0), kHLD, x, lane);
+                const f32x4 x20 = mm16_f32(T(2, 2), kHLD, T(2, 0), kHLD, z, lane);
+                wave_sync();
+                st16_f32(T(3, 0), kHLD, -x, lane);
+                st16_f32(T(2, 0), kHLD, -x20, lane);
+                wave_sync();
+            }
+            // T' = X diag(beta), the six fragments (row tile rt, key block kb);
+            // entries above the diagonal are selected away
+            const float *beta = s_beta + 64 * wave;
+            const long hc = (long)c * Hv + g * G + j0 + wave;
+            half8 *tf = reinterpret_cast<half8 *>(ws.hrec + hc * kRecBytes + kRecT);
+#pragma unroll
+            for (int f = 0; f < 6; ++f) {
+                const int rt = f < 2 ? f : (f + 2) >> 1, kb = f < 2 ? 0 : f & 1;
+                const int i = 16 * rt + c16;
+                half8 fr;
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb) {
+                    const int cb = 2 * kb + hb, j0c = 16 * cb + 4 * q4;
+                    const f32x4 bb = *reinterpret_cast<const f32x4 *>(beta + j0c);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int jc = 16 * jt + 4 * q4 + e;
-                        const float pv = p.q_scale * kq[i][e] * __builtin_amdgcn_exp2f(gi - gk[e]);
-                        hv[e] = (_Float16)(qi >= jc ? pv : 0.f);
+                        const float xv = cb <= rt ? T(rt, cb <= rt ? cb : 0)[c16 * kHLD + 4 * q4 + e] : 0.f;
+                        fr[4 * hb + e] = (_Float16)(j0c + e <= i ? xv * bb[e] : 0.f);
                     }
-                    uint8_t *dst = pf + (tri_frag(rt, jt >> 1) * 64 + lane) * 16 + 8 * (jt & 1);
-                    *reinterpret_cast<half4 *>(dst) = hv;
-                    if (jt == rt && (jt & 1) == 0) *reinterpret_cast<half4 *>(dst + 8) = half4{0, 0, 0, 0};
                 }
+                tf[f * 64 + lane] = fr;
             }
-            // ---- X = (I + A)^-1, blocked by 16, from its diagonal blocks
-            //      (solved above).  With L = I + A in
-            //      32 x 32 blocks, L^-1 = [[X_a, 0], [-X_b L_ba X_a, X_b]]:
-            //      first the two 32 x 32 diagonal blocks (X_10, X_32) and, at
-            //      the same time, the products that need only diagonal
-            //      blocks (M_21 = A_21 X_11, M_31 = A_31 X_11); then M_20,
-            //      M_30 and X_21, X_31; then X_20, X_30 -- three rounds of at
-            //      most two dependent 16 x 16 products, on the fp32 matrix
-            //      cores, with M kept in LDS between rounds.
-            __syncthreads();
-            {
-                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                auto At = [&](int i, int j) { return As + 16 * i * kAL + 16 * j; };
-                auto Xt = [&](int i, int j) { return Xs + 16 * i * kAL + 16 * j; };
-                float *Ms = Msc + 256 * wave;  // this wave's product slot
-                auto wave_sync = [] {
-                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                    __builtin_amdgcn_wave_barrier();
-                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                };
-                // round 1: X_10 = -X_11 (A_10 X_00), X_32 = -X_33 (A_32 X_22);
-                //          M_21 = A_21 X_11 (slot 2), M_31 = A_31 X_11 (slot 3)
-                if (wave < 2) {
-                    const int i = 2 * wave;  // (1, 0) or (3, 2)
-                    st16_f32(Ms, 16, mm16_f32(At(i + 1, i), kAL, XDt(i), kAL, z, lane), lane);
-                    wave_sync();
-                    st16_f32(Xt(i + 1, i), kAL, -mm16_f32(XDt(i + 1), kAL, Ms, 16, z, lane), lane);
-                } else {
-                    st16_f32(Ms, 16, mm16_f32(At(wave, 1), kAL, XDt(1), kAL, z, lane), lane);
-                }
-                __syncthreads();
-                // round 2: M_20 (slot 0), M_30 (slot 1); X_21 = -X_22 M_21,
-                //          X_31 = -(X_32 M_21 + X_33 M_31)
-                if (wave < 2) {
-                    const int i = 2 + wave;
-                    f32x4 m = mm16_f32(At(i, 0), kAL, XDt(0), kAL, z, lane);
-                    m = mm16_f32(At(i, 1), kAL, Xt(1, 0), kAL, m, lane);
-                    st16_f32(Ms, 16, m, lane);
-                } else if (wave == 2) {
-                    st16_f32(Xt(2, 1), kAL, -mm16_f32(XDt(2), kAL, Msc + 512, 16, z, lane), lane);
-                } else {
-                    f32x4 x = mm16_f32(Xt(3, 2), kAL, Msc + 512, 16, z, lane);
-                    x = mm16_f32(XDt(3), kAL, Msc + 768, 16, x, lane);
-                    st16_f32(Xt(3, 1), kAL, -x, lane);
-                }
-                __syncthreads();
-                // round 3: X_20 = -X_22 M_20, X_30 = -(X_32 M_20 + X_33 M_30)
-                if (wave == 0) {
-                    st16_f32(Xt(2, 0), kAL, -mm16_f32(XDt(2), kAL, Msc, 16, z, lane), lane);
-                } else if (wave == 1) {
-                    f32x4 x = mm16_f32(Xt(3, 2), kAL, Msc, 16, z, lane);
-                    x = mm16_f32(XDt(3), kAL, Msc + 256, 16, x, lane);
-                    st16_f32(Xt(3, 0), kAL, -x, lane);
-                }
-                __syncthreads();
-            }
-            // ---- T' = X diag(beta), lower triangle, as A operands (rows =
-            //      tokens i, contraction = tokens j): wave w writes fragments
-            //      w and w + 4.  The diagonal blocks come from their parking
-            //      slots; entries above the diagonal are selected away.
-            {
-                half8 *tf = reinterpret_cast<half8 *>(ws.hrec + hc * kRecBytes + kRecT);
-#pragma unroll
-                for (int f2 = 0; f2 < 2; ++f2) {
-                    const int f = wave + 4 * f2;
-                    if (f >= 6) continue;
-                    const int rt = f < 2 ? f : (f + 2) >> 1, kb = f < 2 ? 0 : f & 1;
-                    const int i = 16 * rt + c16;
-                    half8 fr;
-#pragma unroll
-                    for (int hb = 0; hb < 2; ++hb) {
-                        const int j0c = 32 * kb + 16 * hb + 4 * q4;
-                        const float *xp = 2 * kb + hb == rt ? XDt(rt) + c16 * kAL + 4 * q4 : Xs + i * kAL + j0c;
-                        const f32x4 xv = *reinterpret_cast<const f32x4 *>(xp);
-                        const f32x4 bb = *reinterpret_cast<const f32x4 *>(beta + j0c);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) fr[4 * hb + e] = (_Float16)(j0c + e <= i ? xv[e] * bb[e] : 0.f);
-                    }
-                    tf[f * 64 + lane] = fr;
-                }
-            }
-            // no barrier here: the next head's A build writes only A's lower
-            // tiles, which nothing after the last round reads, and its rounds
-            // start after its own barrier, behind every wave's T' reads
         }
-        __syncthreads();  // the next round of heads rewrites the gates and both matrices
+        if (j0 + kPrepHeads < G) __syncthreads();  // the next round rewrites the gates and the regions
     }
 }
 
