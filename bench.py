@@ -16,7 +16,10 @@ under "configs".  Prints ONE JSON line.
   python bench.py --trace-report OUT_MD DB [--counter-command CMD]
 
 --only restricts the run to some legs (prefill, decode, decode_multi,
-backward, configs), for profiling; the JSON line then holds those legs.
+backward, configs, segments), for profiling; the JSON line then holds those
+legs.  "segments" times a tensor-parallel shard's head shape (2 QK / 6 V)
+at T = 8192 and 262,144 with and without the sequential pass's sequence
+split.
 --calibrate-copy ends the run with a plain 256 MiB device-to-device copy, so
 that a rocprofv3 --pmc pass over this command also reads its counters for a
 transfer of known size.  --traffic-report turns two such passes (FETCH_SIZE,
@@ -701,6 +704,52 @@ def bench_config(hip, idx, settle_ms, steps):
             "mfma_frac": flop / (ms * 1e-3) / PEAK_MFMA_F16}
 
 
+def bench_segments(hip, settle_ms, steps):
+    """What intra-card sequence parallelism buys at a tensor-parallel shard's
+    head shape (2 QK / 6 V heads: 48 V heads over 8 GPUs), T = 8192 and
+    T = 262,144: the prefill with the library's segment split against the
+    same call with every sequence run as one segment (gdn_prefill_with_options)."""
+    import numpy as np
+    import torch
+    import linear_attention_sequence_gdn_amd as gdn
+    from linear_attention_sequence_gdn_amd import inputs
+
+    L = gdn.lib()
+    Hqk, Hv = 2, 6
+    out = {}
+    for T in (8192, 262144):
+        x = inputs.make_prefill(T_list=[T], Hqk=Hqk, Hv=Hv, seed=1100, gate_scale=0.1)
+        bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+        q, k, v = bf(x["q"]), bf(x["k"]), bf(x["v"])
+        a, b, w = f32(x["a"]), f32(x["b"]), bf(x["conv_w"])
+        del x
+        o = torch.empty((T, Hv, D), dtype=torch.bfloat16, device="cuda")
+        so = torch.empty((1, Hv, D, D), dtype=torch.float32, device="cuda")
+        need = gdn.gdn_prefill_workspace_size(1, T, Hqk, Hv)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        P = lambda t_: ctypes.c_void_p(t_.data_ptr())
+        res = {}
+        for name, segc in (("auto", 0), ("one_segment", (T + CHUNK - 1) // CHUNK)):
+            run = lambda: L.gdn_prefill_with_options(P(q), P(k), P(v), P(a), P(b), P(w), None, None, None, P(so),
+                                                     P(o), 1, T, Hqk, Hv, D, D, 0.1, 1.0, P(ws), need, sp, segc, None)
+            assert run() == 0
+            settle(hip, sp, run, settle_ms / 2, batch=max(1, 20 * 8192 // T))
+            kk = max(3, min(steps, steps * 8192 // T * 4))
+            t0, t1 = hip.event(), hip.event()
+            hip.record(t0, sp)
+            for _ in range(kk):
+                run()
+            hip.record(t1, sp)
+            ms = hip.ms(t0, t1) / kk
+            res[name] = {"ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3)}
+        res["speedup_of_segments"] = res["one_segment"]["ms_per_call"] / res["auto"]["ms_per_call"]
+        out[f"T{T}_2qk_6v"] = res
+        del q, k, v, o, ws
+    return out
+
+
 def cpu_baseline_config(idx, min_seconds=4.0, max_reps=20):
     """The oracle on a bounded sample of config idx's workload."""
     import numpy as np
@@ -789,7 +838,7 @@ def cpu_baseline_backward(T_sample=1024, min_seconds=4.0, max_reps=20):
                       f"16QK/48V, parallel over the 16 QK groups; {reps} run(s) in {dt:.1f} s wall"}
 
 
-LEGS = ("prefill", "decode", "decode_multi", "backward", "configs")
+LEGS = ("prefill", "decode", "decode_multi", "backward", "configs", "segments")
 
 
 def main():
@@ -895,6 +944,8 @@ def main():
             line["backward"] = bw
         if "configs" in legs:
             line["configs"] = {str(i): bench_config(hip, i, settle_ms, args.steps) for i in (0, 2, 4)}
+        if "segments" in legs:
+            line["segments"] = bench_segments(hip, settle_ms, args.steps)
     line["gpu_clock"] = clock.summary()
     line["source_digest"] = digest
     if args.calibrate_copy:

@@ -145,6 +145,28 @@ int gdn_prefill_noalloc(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 /* Bytes of the device array gdn_prefill_noalloc uses as its workspace. */
 size_t gdn_prefill_noalloc_max_workspace(void);
 
+/*
+ * Measurement variant of gdn_prefill with a choice of how the sequential
+ * pass splits each sequence (the intra-card sequence parallelism that the
+ * architecture deep dive, alwayszhang.cn, section 9, names among FlashQLA's
+ * features for TP, long-sequence and few-head settings): seg_chunks = 0 lets
+ * the library choose, as gdn_prefill does; a positive value makes every
+ * segment at least that many 64-token chunks long (never more segments than
+ * the library's choice, so the workspace of gdn_prefill_workspace_size
+ * suffices); a value at least the sequence's chunk count runs each sequence
+ * as one segment.  The results are those of gdn_prefill up to rounding order
+ * (bit for bit when the split is the same).  events: NULL, or four events as
+ * for gdn_prefill_with_events.
+ */
+int gdn_prefill_with_options(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                             const float *a, const float *b, const uint16_t *conv_w,
+                             const uint16_t *conv_state_in, uint16_t *conv_state_out,
+                             const float *state_in, float *state_out, uint16_t *o,
+                             int B, int T, int Hqk, int Hv, int dk, int dv,
+                             float gate_scale, float q_scale,
+                             void *workspace, size_t workspace_bytes, void *stream,
+                             int seg_chunks, void *const *events);
+
 /* Bytes of device workspace gdn_prefill_varlen needs (any lengths summing to
  * T_tot over N sequences). */
 size_t gdn_prefill_varlen_workspace_size(int N, int T_tot, int Hqk, int Hv, int dk, int dv);

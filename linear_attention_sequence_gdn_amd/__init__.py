@@ -87,6 +87,8 @@ def lib():
         L.gdn_prefill_backward_varlen.argtypes = [_P] * 19 + [_I] * 6 + [_F, _F, _P, _SZ, _P]
         L.gdn_decode_multi.restype = _I
         L.gdn_decode_multi.argtypes = [_P] * 11 + [_I] * 7 + [_F, _F, _P]
+        L.gdn_prefill_with_options.restype = _I
+        L.gdn_prefill_with_options.argtypes = [_P] * 11 + [_I] * 6 + [_F, _F, _P, _SZ, _P, _I, _P]
         L.gdn_prefill_varlen_slots.restype = _I
         L.gdn_prefill_varlen_slots.argtypes = [_P] * 13 + [_I] * 7 + [_F, _F, _P, _SZ, _P]
         L.gdn_prefill_noalloc.restype = _I

@@ -123,7 +123,8 @@ static int prefill_common(const uint16_t *q, const uint16_t *k, const uint16_t *
                           uint16_t *o, const int32_t *cu_seqlens, int N, int T_uniform,
                           int T_tot, int Hqk, int Hv, float gate_scale, float q_scale,
                           void *workspace, size_t workspace_bytes, void *stream,
-                          void *const *events = nullptr, const int32_t *slots = nullptr, int n_rows = 0)
+                          void *const *events = nullptr, const int32_t *slots = nullptr, int n_rows = 0,
+                          int seg_chunks_min = 0)
 {
     const int rc = prefill_check(q, k, v, a, b, conv_w, conv_state_in, conv_state_out, state_in, state_out, o,
                                  cu_seqlens, T_tot);
@@ -143,6 +144,8 @@ static int prefill_common(const uint16_t *q, const uint16_t *k, const uint16_t *
     p.Hqk = Hqk; p.Hv = Hv; p.gate_scale = gate_scale; p.q_scale = q_scale;
     p.max_chunks = max_chunks;
     p.seg_chunks = gdn::choose_seg_chunks(max_chunks, N, Hv);
+    // a caller's longer segments (fewer of them: the workspace still fits)
+    if (seg_chunks_min > p.seg_chunks) p.seg_chunks = seg_chunks_min;
     p.max_segs = gdn::max_segments(max_chunks, N, p.seg_chunks);
     p.defer_final = state_in != nullptr && state_in == state_out;
     p.defer_conv = conv_state_in != nullptr && conv_state_in == conv_state_out;
@@ -234,6 +237,25 @@ int gdn_prefill_noalloc(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                           B, T, B * T, Hqk, Hv, gate_scale, q_scale, ws, kScratchBytes, stream);
 }
 
+int gdn_prefill_with_options(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
+                             const float *b, const uint16_t *conv_w, const uint16_t *conv_state_in,
+                             uint16_t *conv_state_out, const float *state_in, float *state_out,
+                             uint16_t *o, int B, int T, int Hqk, int Hv, int dk, int dv,
+                             float gate_scale, float q_scale, void *workspace,
+                             size_t workspace_bytes, void *stream, int seg_chunks, void *const *events)
+{
+    if (events)
+        for (int i = 0; i < gdn::kPrefillEvents; ++i)
+            if (!events[i]) return GDN_ERR_INVALID_ARGUMENT;
+    if (B < 0 || T < 0 || seg_chunks < 0) return GDN_ERR_INVALID_ARGUMENT;
+    int rc = check_dims(Hqk, Hv, dk, dv);
+    if (rc != GDN_OK) return rc;
+    if ((long)B * T > 0x7fffffffL) return GDN_ERR_UNSUPPORTED;
+    return prefill_common(q, k, v, a, b, conv_w, conv_state_in, conv_state_out, state_in,
+                          state_out, o, nullptr, B, T, B * T, Hqk, Hv, gate_scale, q_scale,
+                          workspace, workspace_bytes, stream, events, nullptr, 0, seg_chunks);
+}
+
 int gdn_prefill_with_events(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
                             const float *b, const uint16_t *conv_w, const uint16_t *conv_state_in,
                             uint16_t *conv_state_out, const float *state_in, float *state_out,
@@ -242,15 +264,9 @@ int gdn_prefill_with_events(const uint16_t *q, const uint16_t *k, const uint16_t
                             size_t workspace_bytes, void *stream, void *const *events)
 {
     if (!events) return GDN_ERR_INVALID_ARGUMENT;
-    for (int i = 0; i < gdn::kPrefillEvents; ++i)
-        if (!events[i]) return GDN_ERR_INVALID_ARGUMENT;
-    if (B < 0 || T < 0) return GDN_ERR_INVALID_ARGUMENT;
-    int rc = check_dims(Hqk, Hv, dk, dv);
-    if (rc != GDN_OK) return rc;
-    if ((long)B * T > 0x7fffffffL) return GDN_ERR_UNSUPPORTED;
-    return prefill_common(q, k, v, a, b, conv_w, conv_state_in, conv_state_out, state_in,
-                          state_out, o, nullptr, B, T, B * T, Hqk, Hv, gate_scale, q_scale,
-                          workspace, workspace_bytes, stream, events);
+    return gdn_prefill_with_options(q, k, v, a, b, conv_w, conv_state_in, conv_state_out, state_in, state_out, o,
+                                    B, T, Hqk, Hv, dk, dv, gate_scale, q_scale, workspace, workspace_bytes, stream,
+                                    0, events);
 }
 
 int gdn_prefill_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,

@@ -72,6 +72,7 @@ struct Workspace {
     uint8_t *kfrag;     // [max_chunks][Hqk]  k^ (token rows, d contraction)
     uint8_t *hrec;      // [max_chunks][Hv] P, T', gates
     int4 *seg_info;     // [max_segs] {seq, first chunk, end chunk, 1: first of seq | 2: last of seq}; seq -1 = unused
+    int *seg_order;     // [max_segs] segments longest first: the sequential pass's order (packed calls only)
     int4 *seq_seg;      // [N] {first segment, segments, -, -}
     float *bstate;      // [max_segs][Hv][128][128] final state of a segment (read when its successor is recomputed)
     int *seg_done;      // [N][Hv] segments of the pair finished, when the in-order walk is needed (zeroed by the parallel pass)

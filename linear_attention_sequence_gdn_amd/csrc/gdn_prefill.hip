@@ -263,6 +263,29 @@ __global__ __launch_bounds__(1024) void setup_kernel(PrefillArgs p, Workspace ws
         sb += ns;
     }
     for (int k = min(segs_total, p.max_segs) + t; k < p.max_segs; k += 1024) ws.seg_info[k] = make_int4(-1, 0, 0, 0);
+    // The order in which the sequential pass takes the segments: longest
+    // first (a counting sort by chunk count, descending; ties in any order),
+    // so that the short segments of short sequences fill the tail of the
+    // launch instead of long ones starting last.  Slots past the segments
+    // keep their own index (unused segments).
+    __syncthreads();  // the segment table is complete
+    const int nsegs = min(segs_total, p.max_segs);
+    s_scan[t] = 0;
+    __syncthreads();
+    for (int k = t; k < nsegs; k += 1024) {
+        const int4 sk = ws.seg_info[k];
+        atomicAdd(&s_scan[1023 - min(sk.z - sk.y, 1023)], 1);
+    }
+    __syncthreads();
+    const int cnt = s_scan[t];
+    const int before = block_scan1024(cnt, s_wsum) - cnt;  // segments in longer bins
+    s_scan[t] = before;
+    __syncthreads();
+    for (int k = t; k < nsegs; k += 1024) {
+        const int4 sk = ws.seg_info[k];
+        ws.seg_order[atomicAdd(&s_scan[1023 - min(sk.z - sk.y, 1023)], 1)] = k;
+    }
+    for (int k = nsegs + t; k < p.max_segs; k += 1024) ws.seg_order[k] = k;
 }
 
 // Table lookups.  Packed (varlen) calls read the tables setup_kernel built;
@@ -305,7 +328,6 @@ struct Tables {
         const int ns = segs_per_seq(p);
         return make_int2(s * ns, ns);
     }
-    // sequences, longest first
 };
 
 // ---------------------------------------------------------------------------
@@ -1357,7 +1379,8 @@ void chain_kernel(PrefillArgs p, Workspace ws)
     const int gu = (bid / (8 * G)) * 8 + (bid & 7);
     const int j = (bid >> 3) % G;
     if (gu >= p.max_segs * Hqk) return;
-    const int k = gu / Hqk, g = gu % Hqk;
+    // packed calls take the segments longest first (setup_kernel's order)
+    const int k = p.cu_seqlens ? ws.seg_order[gu / Hqk] : gu / Hqk, g = gu % Hqk;
     const int h = g * G + j;
     const long C_tot = 2L * Hqk * kD + (long)Hv * kD, cv = 2L * Hqk * kD + (long)h * kD;
     const int4 sg = Tables::seg(p, ws, k);  // seq, first chunk, end chunk, flags
@@ -1501,6 +1524,7 @@ size_t prefill_workspace_bytes(int max_chunks, int N, int Hqk, int Hv)
     total += align256(C * Hqk * kKFragBytes);
     total += align256(C * Hv * kRecBytes);
     total += align256(M * sizeof(int4));
+    total += align256(M * sizeof(int));
     total += align256((size_t)N * sizeof(int4));
     total += align256(M * Hv * kStateFloats * sizeof(float));
     total += align256((size_t)N * Hv * sizeof(int));
@@ -1524,6 +1548,7 @@ Workspace carve_workspace(void *base, int max_chunks, int N, int Hqk, int Hv)
     ws.kfrag = take(C * Hqk * kKFragBytes);
     ws.hrec = take(C * Hv * kRecBytes);
     ws.seg_info = reinterpret_cast<int4 *>(take(M * sizeof(int4)));
+    ws.seg_order = reinterpret_cast<int *>(take(M * sizeof(int)));
     ws.seq_seg = reinterpret_cast<int4 *>(take((size_t)N * sizeof(int4)));
     ws.bstate = reinterpret_cast<float *>(take(M * Hv * kStateFloats * sizeof(float)));
     ws.seg_done = reinterpret_cast<int *>(take((size_t)N * Hv * sizeof(int)));

@@ -64,6 +64,7 @@ int main()
         memset(ws.kfrag, 4, gdn::kKFragBytes * max_chunks * Hqk);
         memset(ws.hrec, 5, gdn::kRecBytes * max_chunks * Hv);
         memset(ws.seg_info, 6, sizeof(int4) * segs);
+        memset(ws.seg_order, 6, sizeof(int) * segs);
         memset(ws.seq_seg, 7, sizeof(int4) * N);
         memset(ws.bstate, 8, sizeof(float) * gdn::kStateFloats * segs * Hv);
         memset(ws.seg_done, 9, sizeof(int) * N * Hv);
