@@ -685,11 +685,20 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
 // staged through LDS 32 deep.  The sources are read 16 bytes at a time along
 // their contiguous dimension: fa4(r, k) is A(r, k..k+3) when AK, else
 // A(r..r+3, k); fb4(k, c) is B(k..k+3, c) when BK, else B(k, c..c+3).
+// The staged slices are k-major, laid out so that a thread's operands of one
+// k are contiguous: its four A rows (r0 .. r0+3), read as one 16-byte
+// broadcast, and its NC B columns, column cc + 16 m at position
+// 64 (m / 4) + 4 cc + m % 4, read 16 bytes at a time (the sixteen lanes of a
+// quarter wave cover 256 consecutive bytes: no bank conflicts).
+constexpr int kGA = 64 + 4;   // row stride of the A slice (k-major)
+constexpr int kGB = 128 + 4;  // row stride of the B slice (k-major)
+__device__ __forceinline__ int gemm_bpos(int c) { return 64 * ((c >> 4) >> 2) + 4 * (c & 15) + ((c >> 4) & 3); }
+
 template <int NC, bool AK, bool BK, class FA4, class FB4>
 __device__ __forceinline__ void gemm64(float (&acc)[4][8], int K, FA4 fa4, FB4 fb4, float *sA, float *sB)
 {
     const int t = threadIdx.x, r0 = 4 * (t >> 4), cc = t & 15;
-    constexpr int NCOL = 16 * NC, LB = NCOL + 1;
+    constexpr int NCOL = 16 * NC;
     for (int k0 = 0; k0 < K; k0 += 32) {
         float4 va[2], vb[NC / 2];
 #pragma unroll
@@ -705,13 +714,12 @@ __device__ __forceinline__ void gemm64(float (&acc)[4][8], int K, FA4 fa4, FB4 f
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int idx = t + kBT * e;
-            const float v[4] = {va[e].x, va[e].y, va[e].z, va[e].w};
+            if (AK) {
+                const float v[4] = {va[e].x, va[e].y, va[e].z, va[e].w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (AK)
-                    sA[(idx >> 3) * 33 + 4 * (idx & 7) + i] = v[i];
-                else
-                    sA[(4 * (idx & 15) + i) * 33 + (idx >> 4)] = v[i];
+                for (int i = 0; i < 4; ++i) sA[(4 * (idx & 7) + i) * kGA + (idx >> 3)] = v[i];
+            } else {
+                *reinterpret_cast<float4 *>(sA + (idx >> 4) * kGA + 4 * (idx & 15)) = va[e];
             }
         }
 #pragma unroll
@@ -721,19 +729,25 @@ __device__ __forceinline__ void gemm64(float (&acc)[4][8], int K, FA4 fa4, FB4 f
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if (BK)
-                    sB[(4 * (idx & 7) + i) * LB + (idx >> 3)] = v[i];
+                    sB[(4 * (idx & 7) + i) * kGB + gemm_bpos(idx >> 3)] = v[i];
                 else
-                    sB[(idx / (NCOL / 4)) * LB + 4 * (idx % (NCOL / 4)) + i] = v[i];
+                    sB[(idx / (NCOL / 4)) * kGB + gemm_bpos(4 * (idx % (NCOL / 4)) + i)] = v[i];
             }
         }
         __syncthreads();
 #pragma unroll 2
         for (int kk = 0; kk < 32; ++kk) {
-            float av[4], bv[NC];
+            const float4 a4 = *reinterpret_cast<const float4 *>(sA + kk * kGA + r0);
+            const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+            float bv[NC];
 #pragma unroll
-            for (int ri = 0; ri < 4; ++ri) av[ri] = sA[(r0 + ri) * 33 + kk];
-#pragma unroll
-            for (int m = 0; m < NC; ++m) bv[m] = sB[kk * LB + cc + 16 * m];
+            for (int h = 0; h < NC / 4; ++h) {
+                const float4 b4 = *reinterpret_cast<const float4 *>(sB + kk * kGB + 64 * h + 4 * cc);
+                bv[4 * h] = b4.x;
+                bv[4 * h + 1] = b4.y;
+                bv[4 * h + 2] = b4.z;
+                bv[4 * h + 3] = b4.w;
+            }
 #pragma unroll
             for (int ri = 0; ri < 4; ++ri)
 #pragma unroll
@@ -763,7 +777,7 @@ __device__ __forceinline__ float sum16(float v)
 
 __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_grad_kernel(BwdArgs p, BwdWs ws)
 {
-    __shared__ float sA[64 * 33], sB[32 * 129];
+    __shared__ __attribute__((aligned(16))) float sA[32 * kGA], sB[32 * kGB];
     __shared__ float Em[64 * kLN], Wm[64 * kLN], Ym[64 * kLN];
     __shared__ float gam[64], bet[64], eg[64], en[64], dgam[64], dbet[64], rowv[64];
     const int Hv = p.Hv, Hqk = p.Hqk, G = Hv / Hqk;
