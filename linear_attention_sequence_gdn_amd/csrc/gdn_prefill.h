@@ -55,14 +55,23 @@ constexpr size_t kQFragBytes = 16 * kFragBytes;      // q^ of a chunk     [64 x 
 constexpr size_t kKFragBytes = 16 * kFragBytes;      // k^ of a chunk     [64 x 128]
 // Per (chunk, V head) record: P, T', gates.  The two lower-triangular 64 x 64
 // matrices keep the six 16x32 fragments that are not structurally zero: (row
-// tile, key block) (0,0) (1,0) (2,0) (2,1) (3,0) (3,1), in that order.  Gate
-// floats: [0,64) q_scale Gamma, [64,128) Gamma_n / Gamma, 128 Gamma_n,
-// 129 log2 Gamma_n, [192,256) Gamma.
-constexpr size_t kPFragBytes = 6 * kFragBytes;       // P of a chunk      [64 x 64]
-constexpr size_t kTFragBytes = 6 * kFragBytes;       // T' of a chunk     [64 x 64]
+// tile, key block) (0,0) (1,0) (2,0) (2,1) (3,0) (3,1), f = 0..5 in that
+// order.  Fragments 0 and 3 are zero in their upper halves (elements 4..7 of
+// every lane), so each matrix is stored compactly in 5 KiB: fragments 1, 2, 4,
+// 5 whole (16 bytes per lane), then the lower halves of fragments 0 and 3 (8
+// bytes per lane each); tri_off gives the place of a lane's half.  Gate
+// floats: [0,64) q_scale Gamma, [64,128) Gamma_n / Gamma, 128 Gamma_n, 129
+// log2 Gamma_n, [192,256) Gamma.
+constexpr size_t kTriBytes = 5 * kFragBytes;         // a compact lower-triangular operand [64 x 64]
 constexpr size_t kGateFloats = 256;
-constexpr size_t kRecP = 0, kRecT = kPFragBytes, kRecG = kPFragBytes + kTFragBytes;
-constexpr size_t kRecBytes = kRecG + kGateFloats * 4;  // 13 KiB
+constexpr size_t kRecT = 0, kRecP = kTriBytes, kRecG = 2 * kTriBytes;
+constexpr size_t kRecBytes = kRecG + kGateFloats * 4;  // 11 KiB
+__host__ __device__ constexpr bool tri_half_only(int f) { return f == 0 || f == 3; }
+// byte offset of 8-byte half hb (0 for fragments 0 and 3) of lane `lane` of fragment f
+__host__ __device__ constexpr int tri_off(int f, int hb, int lane)
+{
+    return tri_half_only(f) ? 4096 + 512 * (f == 3) + 8 * lane : 1024 * (f - 1 - (f > 3)) + 16 * lane + 8 * hb;
+}
 constexpr size_t kStateFloats = 128 * 128;          // one fp32 state
 
 struct Workspace {

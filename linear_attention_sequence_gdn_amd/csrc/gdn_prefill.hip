@@ -634,9 +634,7 @@ void prep_kernel(PrefillArgs p, Workspace ws)
                     const float pv = p.q_scale * kq[i][e] * __builtin_amdgcn_exp2f(gi - gk[e]);
                     hv[e] = (_Float16)(qi >= jc ? pv : 0.f);
                 }
-                uint8_t *dst = pf + (tri_frag(rt, jt >> 1) * 64 + lane) * 16 + 8 * (jt & 1);
-                *reinterpret_cast<half4 *>(dst) = hv;
-                if (jt == rt && (jt & 1) == 0) *reinterpret_cast<half4 *>(dst + 8) = half4{0, 0, 0, 0};
+                *reinterpret_cast<half4 *>(pf + tri_off(tri_frag(rt, jt >> 1), jt & 1, lane)) = hv;
             }
         }
         __syncthreads();
@@ -714,7 +712,7 @@ void prep_kernel(PrefillArgs p, Workspace ws)
             // entries above the diagonal are selected away
             const float *beta = s_beta + 64 * wave;
             const long hc = (long)c * Hv + g * G + j0 + wave;
-            half8 *tf = reinterpret_cast<half8 *>(ws.hrec + hc * kRecBytes + kRecT);
+            uint8_t *tf = ws.hrec + hc * kRecBytes + kRecT;
 #pragma unroll
             for (int f = 0; f < 6; ++f) {
                 const int rt = f < 2 ? f : (f + 2) >> 1, kb = f < 2 ? 0 : f & 1;
@@ -730,7 +728,10 @@ void prep_kernel(PrefillArgs p, Workspace ws)
                         fr[4 * hb + e] = (_Float16)(j0c + e <= i ? xv * bb[e] : 0.f);
                     }
                 }
-                tf[f * 64 + lane] = fr;
+                if (tri_half_only(f))
+                    *reinterpret_cast<half4 *>(tf + tri_off(f, 0, lane)) = half4{fr[0], fr[1], fr[2], fr[3]};
+                else
+                    *reinterpret_cast<half8 *>(tf + tri_off(f, 0, lane)) = fr;
             }
         }
         if (j0 + kPrepHeads < G) __syncthreads();  // the next round rewrites the gates and the regions
@@ -769,6 +770,8 @@ struct ChainBuf {
     static constexpr int kV = kRec + (int)kRecBytes;
     static constexpr int kBytes = kV + kVTileRows * kD * 2;
 };
+constexpr int kRecPieces = (int)(kRecBytes / 1024);  // 1 KiB pieces of the head record
+static_assert(kRecBytes % 1024 == 0, "the head record moves in 1 KiB pieces");
 // 16-column tiles of the state per wave: 1 gives eight waves of 16 columns
 // (two per SIMD, which hide each other's latencies), 2 gives four waves of 32.
 constexpr int kChainCT = 1;
@@ -807,9 +810,10 @@ __device__ __forceinline__ int vtile_offset(int R, int byte_in_row)
     return R * (kD * 2) + ((((byte_in_row >> 4) ^ R) & 15) << 4) + (byte_in_row & 15);
 }
 
-// Chunk c's operands into one LDS buffer: 62 pieces of 1 KiB; wave w moves
-// pieces 4i + w of k^, q^ and of the raw v tile (i < 4) and of the head
-// record (4i + w < 13), and wave 3 the last piece of the v tile.
+// Chunk c's operands into one LDS buffer: 60 pieces of 1 KiB; with four
+// waves, wave w moves pieces 4i + w of k^, q^ and of the raw v tile (i < 4)
+// and of the head record (4i + w < 11), and wave 3 the last piece of the v
+// tile.
 // Issued in four groups (i = 0..3), spread through a chunk step so that the
 // memory unit takes them while the matrix cores work.
 struct ChainDma {
@@ -879,8 +883,8 @@ __device__ __forceinline__ void chain_dma_group(const ChainDma &d, uint8_t *buf,
         chain_dma_k(d, buf, f, lane);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rq, (lds_void_t *)(buf + ChainBuf::kQ + f * 1024), 16, v16, f * 1024, 0, 0);
         chain_dma_v(d, buf, f, lane);
-        // head record: 13 pieces (P 0-5, T' 6-11, gates 12)
-        if (I < 3 || wave == 0)
+        // head record: T' 0-4, P 5-9, gates 10
+        if (f < kRecPieces)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rh, (lds_void_t *)(buf + ChainBuf::kRec + f * 1024), 16, v16, f * 1024, 0, 0);
         if (I == 1 && wave == 3) chain_dma_v(d, buf, 16, lane);
     } else {
@@ -893,7 +897,7 @@ __device__ __forceinline__ void chain_dma_group(const ChainDma &d, uint8_t *buf,
             if (I == 1)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rq, (lds_void_t *)(buf + ChainBuf::kQ + f * 1024), 16, v16, f * 1024, 0, 0);
             if (I == 2) chain_dma_v(d, buf, f, lane);
-            if (I == 3 && f < 13)
+            if (I == 3 && f < kRecPieces)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rh, (lds_void_t *)(buf + ChainBuf::kRec + f * 1024), 16, v16, f * 1024, 0, 0);
         }
         if (I == 2 && wave == 0) chain_dma_v(d, buf, 16, lane);
@@ -984,6 +988,16 @@ constexpr int kChainVmemAfterDma = 4;
 // lgkmcnt at their no-wait maxima
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
 
+// Fragment f of a compact lower-triangular operand in LDS (T' or P)
+__device__ __forceinline__ half8 tri_frag_ld(const uint8_t *base, int f, int lane)
+{
+    if (tri_half_only(f)) {
+        const half4 lo = *reinterpret_cast<const half4 *>(base + tri_off(f, 0, lane));
+        return half8{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+    }
+    return *reinterpret_cast<const half8 *>(base + tri_off(f, 0, lane));
+}
+
 // One chunk from operand buffer `cur`; loads the next chunk's operands into
 // `nxt`.  kOut = false: a warm-up chunk, which only advances the state (no
 // Q S, no output); it waits for its own DMA at its end, since it issues no
@@ -1011,8 +1025,7 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
 
     const uint8_t *kt = cur + ChainBuf::kK;
     const half8 *Qf = reinterpret_cast<const half8 *>(cur + ChainBuf::kQ) + lane;
-    const half8 *Pf = reinterpret_cast<const half8 *>(cur + ChainBuf::kP) + lane;
-    const half8 *Tf = reinterpret_cast<const half8 *>(cur + ChainBuf::kT) + lane;
+    const uint8_t *Pf = cur + ChainBuf::kP, *Tf = cur + ChainBuf::kT;
     const float *gt = reinterpret_cast<const float *>(cur + ChainBuf::kG);
     const uint8_t *vt = cur + ChainBuf::kV;
 
@@ -1084,7 +1097,7 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
     // two 32-token blocks, T' lower triangular
     half8 tf[6];
 #pragma unroll
-    for (int i = 0; i < 6; ++i) tf[i] = Tf[i * 64];
+    for (int i = 0; i < 6; ++i) tf[i] = tri_frag_ld(Tf, i, lane);
     f32x4 Vn[4][kChainCT];
     {
         f32x4 gg[4];
@@ -1114,7 +1127,7 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
     half8 pf[6];
     if (kOut) {
 #pragma unroll
-        for (int i = 0; i < 6; ++i) pf[i] = Pf[i * 64];
+        for (int i = 0; i < 6; ++i) pf[i] = tri_frag_ld(Pf, i, lane);
     }
     f32x4 rg[4];
     float gm[4];
