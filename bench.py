@@ -102,6 +102,23 @@ def method_flops(lengths, Hqk, Hv, n=CHUNK, d=D):
     return total
 
 
+# bytes per (chunk, QK group) of the q^ and k^ operands, and per (chunk, V
+# head) of the T' / P / gates record, that the parallel pass hands over
+QK_FRAG_BYTES = 2 * 16 * 1024
+REC_BYTES = 11 * 1024
+
+
+def prep_bytes(T, Hqk, Hv, d=D):
+    """Bytes the parallel pass moves by its design: q and k read (bf16), a and
+    b read (fp32), the conv taps of q and k, and its hand-over written.  Its
+    arithmetic (about 20 FLOP per byte) is far below the fp16 matrix-core
+    ridge (2.5 PFLOP/s / 8 TB/s = 312 FLOP per byte), so HBM bounds it."""
+    chunks = -(-T // CHUNK)
+    read = 2 * T * Hqk * d * 2 + 2 * T * Hv * 4 + 2 * Hqk * d * 4 * 2
+    write = chunks * (Hqk * QK_FRAG_BYTES + Hv * REC_BYTES)
+    return read + write
+
+
 def prefill_bytes(T, Hqk, Hv, d=D):
     """Compulsory HBM bytes of one prefill (zero initial state, no conv carry)."""
     per_tok = 2 * (2 * Hqk * d + Hv * d) + 2 * 4 * Hv + 2 * Hv * d
@@ -921,7 +938,14 @@ def main():
                          "hbm_frac": prefill_bytes(T, Hqk, Hv) / (pf["ms_per_step"] * 1e-3) / PEAK_HBM,
                          "kernel_ms": km, "event_intervals_ms": raw,
                          "other_kernel": {"kernel": other,
-                                          "tflops": kflop[other] / (km[other] * 1e-3) / 1e12}}})
+                                          "tflops": kflop[other] / (km[other] * 1e-3) / 1e12},
+                         "prep_hbm_roofline": {
+                             "bound": "hbm", "kernel": "prep_kernel",
+                             "achieved": prep_bytes(T, Hqk, Hv) / (km["prep_kernel"] * 1e-3) / 1e9,
+                             "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                             "frac": prep_bytes(T, Hqk, Hv) / (km["prep_kernel"] * 1e-3) / PEAK_HBM,
+                             "design_bytes_per_launch": prep_bytes(T, Hqk, Hv),
+                             "traffic": load_traffic("prefill_prep", digest)}}})
         if "decode" in legs:
             dc = bench_decode(hip, settle_ms)
             dec_bytes = decode_bytes(dc["B"], dc["Hqk"], dc["Hv"])
