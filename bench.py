@@ -725,7 +725,11 @@ def bench_segments(hip, settle_ms, steps):
     """What intra-card sequence parallelism buys at a tensor-parallel shard's
     head shape (2 QK / 6 V heads: 48 V heads over 8 GPUs), T = 8192 and
     T = 262,144: the prefill with the library's segment split against the
-    same call with every sequence run as one segment (gdn_prefill_with_options)."""
+    same call with every sequence run as one segment (gdn_prefill_with_options).
+    A third case, T = 8192 with no decay on any head (a = -30: alpha = 1 to
+    fp32 precision), makes every later segment miss its warm-up bound, so
+    that the in-order walk recomputes them all: it shows what the split costs
+    when it cannot help."""
     import numpy as np
     import torch
     import linear_attention_sequence_gdn_amd as gdn
@@ -734,8 +738,10 @@ def bench_segments(hip, settle_ms, steps):
     L = gdn.lib()
     Hqk, Hv = 2, 6
     out = {}
-    for T in (8192, 262144):
+    for T, decay in ((8192, True), (262144, True), (8192, False)):
         x = inputs.make_prefill(T_list=[T], Hqk=Hqk, Hv=Hv, seed=1100, gate_scale=0.1)
+        if not decay:
+            x["a"][:] = -30.0
         bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
         f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
         q, k, v = bf(x["q"]), bf(x["k"]), bf(x["v"])
@@ -762,7 +768,7 @@ def bench_segments(hip, settle_ms, steps):
             ms = hip.ms(t0, t1) / kk
             res[name] = {"ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3)}
         res["speedup_of_segments"] = res["one_segment"]["ms_per_call"] / res["auto"]["ms_per_call"]
-        out[f"T{T}_2qk_6v"] = res
+        out[f"T{T}_2qk_6v" + ("" if decay else "_no_decay")] = res
         del q, k, v, o, ws
     return out
 
