@@ -726,10 +726,9 @@ def bench_segments(hip, settle_ms, steps):
     head shape (2 QK / 6 V heads: 48 V heads over 8 GPUs), T = 8192 and
     T = 262,144: the prefill with the library's segment split against the
     same call with every sequence run as one segment (gdn_prefill_with_options).
-    A third case, T = 8192 with no decay on any head (a = -30: alpha = 1 to
-    fp32 precision), makes every later segment miss its warm-up bound, so
-    that the in-order walk recomputes them all: it shows what the split costs
-    when it cannot help."""
+    Both again with no decay on any head (a = -30: alpha = 1 to fp32
+    precision): every later segment then misses its warm-up bound and goes
+    through its transition matrix and the in-order combine."""
     import numpy as np
     import torch
     import linear_attention_sequence_gdn_amd as gdn
@@ -738,7 +737,7 @@ def bench_segments(hip, settle_ms, steps):
     L = gdn.lib()
     Hqk, Hv = 2, 6
     out = {}
-    for T, decay in ((8192, True), (262144, True), (8192, False)):
+    for T, decay in ((8192, True), (262144, True), (8192, False), (262144, False)):
         x = inputs.make_prefill(T_list=[T], Hqk=Hqk, Hv=Hv, seed=1100, gate_scale=0.1)
         if not decay:
             x["a"][:] = -30.0

@@ -184,7 +184,7 @@ int gdn_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v, const f
 // ---------------------------------------------------------------------------
 namespace {
 
-constexpr size_t kScratchBytes = (size_t)192 << 20;  // the T = 8192, 16 / 48-head prefill needs 160 MiB
+constexpr size_t kScratchBytes = (size_t)192 << 20;  // the T = 8192, 16 / 48-head prefill needs 166 MiB
 constexpr int kScratchMaxDevices = 64;
 
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];

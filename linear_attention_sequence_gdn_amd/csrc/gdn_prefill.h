@@ -83,8 +83,12 @@ struct Workspace {
     int4 *seg_info;     // [max_segs] {seq, first chunk, end chunk, 1: first of seq | 2: last of seq}; seq -1 = unused
     int *seg_order;     // [max_segs] segments longest first: the sequential pass's order (packed calls only)
     int4 *seq_seg;      // [N] {first segment, segments, -, -}
-    float *bstate;      // [max_segs][Hv][128][128] final state of a segment (read when its successor is recomputed)
+    float *bstate;      // [max_segs][Hv][128][128] final state of a segment (read by the in-order combine and by the
+                        // extra workgroup of its successor); a segment that misses its warm-up bound parks here its
+                        // final state from a zero start, which the combine replaces by the true one
+    float *mstate;      // [max_segs][Hv][128][128] transition matrix of a segment that misses its warm-up bound
     int *seg_done;      // [N][Hv] segments of the pair finished, when the in-order walk is needed (zeroed by the parallel pass)
+    int *seg_ready;     // [N][Hv] the pair's in-order combine is done (zeroed by the parallel pass)
 };
 
 // Segments of the sequential pass: each sequence's chunks are cut into runs

@@ -482,9 +482,9 @@ void prep_kernel(PrefillArgs p, Workspace ws)
     const int q4 = lane >> 4, c16 = lane & 15;
     const int Hqk = p.Hqk, Hv = p.Hv, G = Hv / Hqk;
     const int c = blockIdx.x / Hqk, g = blockIdx.x % Hqk;
-    // the sequential pass's per-(sequence, V head) segment counters
+    // the sequential pass's per-(sequence, V head) segment counters and flags
     if (blockIdx.x == 0)
-        for (int i = t; i < p.N * Hv; i += kPrepThreads) ws.seg_done[i] = 0;
+        for (int i = t; i < p.N * Hv; i += kPrepThreads) ws.seg_done[i] = ws.seg_ready[i] = 0;
     const int4 ci = Tables::chunk(p, ws, c);
     const int n = ci.z;
     if (n == 0) return;  // empty chunk slot (whole workgroup)
@@ -1001,14 +1001,15 @@ __device__ __forceinline__ half8 tri_frag_ld(const uint8_t *base, int f, int lan
 // One chunk from operand buffer `cur`; loads the next chunk's operands into
 // `nxt`.  kOut = false: a warm-up chunk, which only advances the state (no
 // Q S, no output); it waits for its own DMA at its end, since it issues no
-// output stores after it.
+// output stores after it.  kZeroV: the chunk's v^ taken as zero (the run
+// that carries a segment's transition matrix instead of a state).
 //   Z, X, Vn [rt][x]  tokens 16rt.. x columns 16x..  (accumulator rows = tokens)
 //   QST      [x][rt]  (Q S)^T, columns 16x.. x tokens 16rt.. (accumulator rows = columns)
 // The output is formed transposed, O^T = S^T Q^T diag(q_scale Gam) + Vnew^T P^T,
 // so that a lane holds four adjacent columns of one token (8-byte LDS writes
 // into the row staging).  The fragment layout is the same for A and B
 // operands, so the packed state and Vnew serve as A operands unchanged.
-template <bool kOut>
+template <bool kOut, bool kZeroV = false>
 __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace &ws, uint8_t *cur, uint8_t *nxt,
                                            uint8_t *stage, f32x4 (&S)[8][kChainCT], const bf16x8 (&wb)[kChainCT][2],
                                            const ChainRun &run, int cc, int h, int g, int wave, int lane)
@@ -1053,7 +1054,7 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
             if (kOut) aq[rt] = Qf[(rt * 4 + kb) * 64];
         }
         bf16x8 cv[4][kChainCT][2];
-        if (kb == 0) {
+        if (kb == 0 && !kZeroV) {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -1076,7 +1077,7 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
             const int rt = sl / (2 * kChainCT), r = sl % (2 * kChainCT);
             if (r < kChainCT) X[rt][r] = mfma16(ak[rt], sb[r], X[rt][r]);
             else if (kOut) QST[r - kChainCT][rt] = mfma16(sb[r - kChainCT], aq[rt], QST[r - kChainCT][rt]);
-            if (kb > 0 && sl < 4 * kChainCT) Z[kb - 1][sl >> 2][sl & 3] = silu_f(Z[kb - 1][sl >> 2][sl & 3]);
+            if (!kZeroV && kb > 0 && sl < 4 * kChainCT) Z[kb - 1][sl >> 2][sl & 3] = silu_f(Z[kb - 1][sl >> 2][sl & 3]);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (kb == 0) {
@@ -1084,6 +1085,10 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                 for (int x = 0; x < kChainCT; ++x) {
+                    if (kZeroV) {
+                        Z[rt][x] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        continue;
+                    }
                     Z[rt][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cv[rt][x][0], wb[x][0], f32x4{0.f, 0.f, 0.f, 0.f},
                                                                        0, 0, 0);
                     Z[rt][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cv[rt][x][1], wb[x][1], Z[rt][x], 0, 0, 0);
@@ -1091,8 +1096,10 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    if (!kZeroV) {
 #pragma unroll
-    for (int sl = 0; sl < 4 * kChainCT; ++sl) Z[3][sl >> 2][sl & 3] = silu_f(Z[3][sl >> 2][sl & 3]);
+        for (int sl = 0; sl < 4 * kChainCT; ++sl) Z[3][sl >> 2][sl & 3] = silu_f(Z[3][sl >> 2][sl & 3]);
+    }
     // Vnew = T' (v^ - diag(Gam) X): the bracket as B operands over the chunk's
     // two 32-token blocks, T' lower triangular
     half8 tf[6];
@@ -1227,7 +1234,10 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
     // the staging is rewritten by the next step only after its block barrier
 }
 
-// The chunks of one run, the state carried in registers.
+// The chunks of one run, the state carried in registers.  kZeroV: v^ taken
+// as zero, for a segment's transition matrix; such a run has no output
+// chunks (c_out >= c_to).
+template <bool kZeroV = false>
 __device__ __forceinline__ void chain_run(const PrefillArgs &p, const Workspace &ws, uint8_t *buf0, uint8_t *buf1,
                                           uint8_t *stage, f32x4 (&S)[8][kChainCT],
                                           const bf16x8 (&wb)[kChainCT][2], const ChainRun &run, int h, int g, int wave,
@@ -1240,22 +1250,26 @@ __device__ __forceinline__ void chain_run(const PrefillArgs &p, const Workspace 
     // warm-up chunks [c_from, c_out): the state only
     const int cw = min(run.c_out, run.c_to);
     for (; cc + 2 <= cw; cc += 2) {
-        chain_step<false>(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
-        chain_step<false>(p, ws, buf1, buf0, stage, S, wb, run, cc + 1, h, g, wave, lane);
+        chain_step<false, kZeroV>(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
+        chain_step<false, kZeroV>(p, ws, buf1, buf0, stage, S, wb, run, cc + 1, h, g, wave, lane);
     }
     if (cc < cw) {  // an odd warm-up: the next chunk sits in buf1
-        chain_step<false>(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
+        chain_step<false, kZeroV>(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
         ++cc;
-        if (cc < run.c_to) {
-            chain_step<true>(p, ws, buf1, buf0, stage, S, wb, run, cc, h, g, wave, lane);
-            ++cc;
+        if constexpr (!kZeroV) {
+            if (cc < run.c_to) {
+                chain_step<true>(p, ws, buf1, buf0, stage, S, wb, run, cc, h, g, wave, lane);
+                ++cc;
+            }
         }
     }
-    for (; cc + 2 <= run.c_to; cc += 2) {
-        chain_step<true>(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
-        chain_step<true>(p, ws, buf1, buf0, stage, S, wb, run, cc + 1, h, g, wave, lane);
+    if constexpr (!kZeroV) {
+        for (; cc + 2 <= run.c_to; cc += 2) {
+            chain_step<true>(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
+            chain_step<true>(p, ws, buf1, buf0, stage, S, wb, run, cc + 1, h, g, wave, lane);
+        }
+        if (cc < run.c_to) chain_step<true>(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
     }
-    if (cc < run.c_to) chain_step<true>(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
     // the last step's DMA into the other buffer is still in flight
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -1336,6 +1350,91 @@ __device__ __forceinline__ void state_store(const f32x4 (&S)[8][kChainCT], float
                 dst[(long)(16 * dt + 4 * q4 + e) * kD + kCW * wave + 16 * x + c16] = S[dt][x][e];
 }
 
+// The identity in the state layout: where a segment's transition-matrix run
+// starts (the map from the state entering the segment to the state leaving
+// it is S -> M S + S0, M the product of the chunks' linear parts; carrying
+// the identity through the chunks with v^ = 0 gives M)
+__device__ __forceinline__ void state_identity(f32x4 (&S)[8][kChainCT], int wave, int lane)
+{
+    const int q4 = lane >> 4, c16 = lane & 15;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int x = 0; x < kChainCT; ++x)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[dt][x][e] = 16 * dt + 4 * q4 + e == kCW * wave + 16 * x + c16 ? 1.f : 0.f;
+}
+
+// S <- M S + S0 for the wave's state columns, M (d_k x d_k) and S0 (a state)
+// row-major fp32, on the fp32 matrix cores.  M arrives in registers (mreg:
+// thread t holds rows (t + 512 i) / 32, float4 column block (t + 512 i) % 32,
+// as m_fetch requests them) and the workgroup stages it in LDS (rows 0..63 in
+// lo, 64..127 in hi, kMLD floats apart: the sixteen rows a quarter wave reads
+// fall in distinct banks); mreg is then free, and `next` (if not NULL) is
+// requested into it while the products run.  Output tile (rt, x) sums 32
+// four-deep steps (dt, e), whose A operand is M[16 rt + r][16 dt + 4q + e]
+// (lane (q, r)) and whose B operand is S[16 dt + 4q + e][column]: the lane's
+// own element S[dt][x][e].  Called by the whole workgroup.
+constexpr int kMLD = 132;
+constexpr int kMRegs = 128 * 32 / kChainThreads;  // float4 blocks of M per thread
+static_assert(64 * kMLD * 4 <= ChainBuf::kBytes, "half of M fits in an operand buffer");
+__device__ __forceinline__ void m_fetch(f32x4 (&mreg)[kMRegs], const float *M)
+{
+#pragma unroll
+    for (int i = 0; i < kMRegs; ++i) {
+        const int idx = (int)threadIdx.x + kChainThreads * i;
+        mreg[i] = *reinterpret_cast<const f32x4 *>(M + (long)(idx >> 5) * kD + 4 * (idx & 31));
+    }
+}
+__device__ __forceinline__ void state_affine(f32x4 (&S)[8][kChainCT], f32x4 (&mreg)[kMRegs], const float *next,
+                                             const float *S0, uint8_t *lo, uint8_t *hi, int wave, int lane)
+{
+    const int q4 = lane >> 4, c16 = lane & 15;
+    float s0[8][kChainCT][4];
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int x = 0; x < kChainCT; ++x)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s0[rt][x][e] = S0[(long)(16 * rt + 4 * q4 + e) * kD + kCW * wave + 16 * x + c16];
+    __syncthreads();  // the buffers may hold the previous product's M
+#pragma unroll
+    for (int i = 0; i < kMRegs; ++i) {
+        const int idx = (int)threadIdx.x + kChainThreads * i, r = idx >> 5, c4 = idx & 31;
+        *reinterpret_cast<f32x4 *>((r < 64 ? lo : hi) + ((r & 63) * kMLD + 4 * c4) * 4) = mreg[i];
+    }
+    __syncthreads();
+    if (next) m_fetch(mreg, next);
+    f32x4 acc[8][kChainCT];
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt) {
+        const uint8_t *mrow = (rt < 4 ? lo : hi) + ((16 * rt + c16) & 63) * kMLD * 4 + 16 * q4;
+#pragma unroll
+        for (int x = 0; x < kChainCT; ++x) acc[rt][x] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const f32x4 a4 = *reinterpret_cast<const f32x4 *>(mrow + 64 * dt);
+#pragma unroll
+            for (int x = 0; x < kChainCT; ++x)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[rt][x] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[e], S[dt][x][e], acc[rt][x], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int x = 0; x < kChainCT; ++x)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[rt][x][e] = acc[rt][x][e] + s0[rt][x][e];
+}
+
+// Polls of the flag that tells an extra workgroup its segment's incoming
+// state is ready (a load and a short sleep each, about 1-2 us: a bound of
+// one to two seconds).  The flag is set by a workgroup of lower id, which
+// the dispatcher has started before this one, so the wait ends long before.
+constexpr int kReadyPolls = 1 << 20;
+
 // The carried conv rows of one sequence (pool row `row`), planes [pl0, pl1)
 // of q | k | v for QK head g / V head h, one wave: the last three raw rows,
 // reaching back into the incoming rows when the sequence is shorter than
@@ -1387,8 +1486,13 @@ void chain_kernel(PrefillArgs p, Workspace ws)
     uint8_t *stage = stage_all + wave * kChainStage;
     const int Hqk = p.Hqk, Hv = p.Hv, G = Hv / Hqk;
     // block -> (segment, group, head in group); the G heads of one (segment,
-    // QK group) land on the same XCD (same L2)
-    const int bid = blockIdx.x;
+    // QK group) land on the same XCD (same L2).  The second half of the grid
+    // are the extra workgroups, one per (segment, V head) again (same XCD as
+    // the main one): they form the output of a segment that misses its
+    // warm-up bound, once the in-order combine has its incoming state.
+    const int n_main = ((p.max_segs * Hqk + 7) / 8) * 8 * G;
+    const bool extra = (int)blockIdx.x >= n_main;
+    const int bid = extra ? (int)blockIdx.x - n_main : (int)blockIdx.x;
     const int gu = (bid / (8 * G)) * 8 + (bid & 7);
     const int j = (bid >> 3) % G;
     if (gu >= p.max_segs * Hqk) return;
@@ -1413,6 +1517,26 @@ void chain_kernel(PrefillArgs p, Workspace ws)
 #pragma unroll
         for (int m = 0; m < 2; ++m) wb[x][m] = conv_tap_frag(p.conv_w, cv + kCW * wave + 16 * x + (lane & 15), m, lane);
     f32x4 S[8][kChainCT];
+
+    if (extra) {
+        if (first) return;  // a sequence's first segment always starts from the true state
+        if (warm_start(ws, h, Hv, sg.y, si.x, lane) >= 0) return;  // its main workgroup wrote its output
+        if (t == 0) {
+            int ok = 0;
+            for (int n = 0; n < kReadyPolls && !ok; ++n) {
+                ok = __hip_atomic_load(ws.seg_ready + (long)s * Hv + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (!ok) __builtin_amdgcn_s_sleep(8);
+            }
+            s_total = ok;
+        }
+        __syncthreads();
+        if (!s_total) return;  // not reached: the combine's workgroup has a lower id
+        __threadfence();
+        state_load(S, ws.bstate + ((long)(k - 1) * Hv + h) * kStateFloats, wave, lane);
+        chain_run(p, ws, buf0, buf1, stage, S, wb, ChainRun{si.x, si.z, si.w, sg.y, sg.z, sg.y, vs, hist}, h, g, wave,
+                  lane);
+        return;
+    }
 
     // The warm-up test of every segment of the sequence, the same in every
     // workgroup of it (gate loads of four segments in flight together): this
@@ -1441,17 +1565,31 @@ void chain_kernel(PrefillArgs p, Workspace ws)
             if (i == i_seg + 1) next_bad = wi < 0;
         }
     }
-    if (w >= 0) {  // else recomputed in order below
+    if (w >= 0) {
         state_load(S, w == si.x && p.state_in ? p.state_in + sbase : nullptr, wave, lane);
         chain_run(p, ws, buf0, buf1, stage, S, wb, ChainRun{si.x, si.z, si.w, w, sg.z, sg.y, vs, hist}, h, g, wave,
                   lane);
         // Final states.  Every segment but the last parks its final state for
         // the in-order pass, which hands it to the next segment if that one
-        // is recomputed.  The last segment writes state_out, unless state_out
-        // is state_in and other blocks of the sequence may still be reading
-        // it: then it parks its state as well and the in-order pass moves it.
+        // misses its bound.  The last segment writes state_out, unless
+        // state_out is state_in and other blocks of the sequence may still be
+        // reading it: then it parks its state as well and the in-order pass
+        // moves it.
         const bool direct = last && (first || !p.defer_final);
         state_store(S, direct ? p.state_out + sbase : ws.bstate + ((long)k * Hv + h) * kStateFloats, wave, lane);
+    } else {
+        // The segment misses its warm-up bound: the map from the state that
+        // enters it to the one that leaves it, S -> M S + S0, is formed here
+        // (two runs without output) and parked; the in-order pass applies it
+        // and the segment's extra workgroup forms the output.
+        state_load(S, nullptr, wave, lane);
+        chain_run(p, ws, buf0, buf1, stage, S, wb, ChainRun{si.x, si.z, si.w, sg.y, sg.z, sg.z, vs, hist}, h, g, wave,
+                  lane);
+        state_store(S, ws.bstate + ((long)k * Hv + h) * kStateFloats, wave, lane);
+        state_identity(S, wave, lane);
+        chain_run<true>(p, ws, buf0, buf1, stage, S, wb, ChainRun{si.x, si.z, si.w, sg.y, sg.z, sg.z, vs, hist}, h, g,
+                        wave, lane);
+        state_store(S, ws.mstate + ((long)k * Hv + h) * kStateFloats, wave, lane);
     }
     // carried conv rows: the last three raw rows of the sequence (v channels
     // of head h; the first head of the group also writes the q and k
@@ -1467,24 +1605,39 @@ void chain_kernel(PrefillArgs p, Workspace ws)
     // workgroup publishes its parked state first if the walk will read it
     // (the next segment is recomputed, or the final state of an in-place call).
     if (nseg <= 1 || (!any_bad && !p.defer_final && !p.defer_conv)) return;
-    if (next_bad || (i_seg == nseg - 1 && p.defer_final)) __threadfence();
+    if (w < 0 || next_bad || (i_seg == nseg - 1 && p.defer_final)) __threadfence();
     __syncthreads();
     if (t == 0) s_total = atomicAdd(ws.seg_done + (long)s * Hv + h, 1) + 1;
     __syncthreads();
     if (s_total != nseg) return;  // not the last to finish
     __threadfence();
-    bool carry = false;  // S holds the final state of the previous segment
-    for (int i = 1; any_bad && i < nseg; ++i) {  // a sequence's first segment is never recomputed
+    bool carry = false;   // S holds the final state of the previous segment
+    bool m_next = false;  // mreg holds (or is receiving) the M of segment ss.x + i
+    f32x4 mreg[kMRegs];
+    for (int i = 1; any_bad && i < nseg; ++i) {  // a sequence's first segment always meets its bound
         const int kk = ss.x + i;
         const int4 sk = Tables::seg(p, ws, kk);
         if (warm_start(ws, h, Hv, sk.y, si.x, lane) >= 0) {
-            carry = false;
+            carry = m_next = false;
             continue;
         }
+        // S <- M S + S0: the state leaving segment kk from the one entering
+        // it, which its extra workgroup reads from the previous slot; the
+        // next segment's M is requested meanwhile, in case it is needed
+        float *park = ws.bstate + ((long)kk * Hv + h) * kStateFloats;
         if (!carry) state_load(S, ws.bstate + ((long)(kk - 1) * Hv + h) * kStateFloats, wave, lane);
-        chain_run(p, ws, buf0, buf1, stage, S, wb, ChainRun{si.x, si.z, si.w, sk.y, sk.z, sk.y, vs, hist}, h, g, wave,
-                  lane);
+        if (!m_next) m_fetch(mreg, ws.mstate + ((long)kk * Hv + h) * kStateFloats);
+        m_next = i < nseg - 1;
+        state_affine(S, mreg, m_next ? ws.mstate + ((long)(kk + 1) * Hv + h) * kStateFloats : nullptr, park, buf0,
+                     buf1, wave, lane);
+        if (i < nseg - 1) state_store(S, park, wave, lane);
         carry = true;
+    }
+    // the extra workgroups of the segments that missed their bounds may start
+    if (any_bad) {
+        __threadfence();
+        __syncthreads();
+        if (t == 0) __hip_atomic_store(ws.seg_ready + (long)s * Hv + h, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     // the final state, when the last segment was recomputed here or parked it
     if (carry || p.defer_final) {
@@ -1540,6 +1693,8 @@ size_t prefill_workspace_bytes(int max_chunks, int N, int Hqk, int Hv)
     total += align256(M * sizeof(int));
     total += align256((size_t)N * sizeof(int4));
     total += align256(M * Hv * kStateFloats * sizeof(float));
+    total += align256(M * Hv * kStateFloats * sizeof(float));
+    total += align256((size_t)N * Hv * sizeof(int));
     total += align256((size_t)N * Hv * sizeof(int));
     return total;
 }
@@ -1564,7 +1719,9 @@ Workspace carve_workspace(void *base, int max_chunks, int N, int Hqk, int Hv)
     ws.seg_order = reinterpret_cast<int *>(take(M * sizeof(int)));
     ws.seq_seg = reinterpret_cast<int4 *>(take((size_t)N * sizeof(int4)));
     ws.bstate = reinterpret_cast<float *>(take(M * Hv * kStateFloats * sizeof(float)));
+    ws.mstate = reinterpret_cast<float *>(take(M * Hv * kStateFloats * sizeof(float)));
     ws.seg_done = reinterpret_cast<int *>(take((size_t)N * Hv * sizeof(int)));
+    ws.seg_ready = reinterpret_cast<int *>(take((size_t)N * Hv * sizeof(int)));
     return ws;
 }
 
@@ -1589,7 +1746,8 @@ hipError_t launch_prefill(const PrefillArgs &p, void *workspace, hipStream_t str
     const int G = p.Hv / p.Hqk;
     const long seg_groups = (long)p.max_segs * p.Hqk;
     const long seg_blocks = ((seg_groups + 7) / 8) * 8L * G;
-    hipLaunchKernelGGL(chain_kernel, dim3((unsigned)seg_blocks), dim3(kChainThreads), 0, stream, p, ws);
+    // main workgroups, then as many extra ones (started after every main one)
+    hipLaunchKernelGGL(chain_kernel, dim3((unsigned)(2 * seg_blocks)), dim3(kChainThreads), 0, stream, p, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return mark(3);
 }
