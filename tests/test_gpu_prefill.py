@@ -97,8 +97,9 @@ def test_segmented_pass_weak_and_strong_decay(oracle_lib):
     V heads 0-2 barely decay (alpha ~ 1), except over tokens 4000-4399 where
     they decay hard: their segments within 64 chunks of the start restart
     from the initial state, those just after the strong stretch start from a
-    truncated warm-up, and the rest miss the warm-up bound and are recomputed
-    in order from the state handed over.  Heads 3-5 decay as usual."""
+    truncated warm-up, and the rest miss the warm-up bound and go through
+    their transition matrices and the in-order combine.  Heads 3-5 decay as
+    usual."""
     T = 8192 + 37
     x = inputs.make_prefill(T_list=[T], Hqk=2, Hv=6, seed=510, state_std=0.05, conv_state_std=1.0)
     x["a"][:, :3] = -9.0
@@ -107,9 +108,23 @@ def test_segmented_pass_weak_and_strong_decay(oracle_lib):
     compare(x, o, so, cso)
 
 
+def test_long_chain_of_segment_maps(oracle_lib):
+    """No V head decays over a 32,787-token sequence, so every segment after
+    the first misses its warm-up bound: some forty segment maps S -> M S + S0
+    are chained in order (each product while the next M is in flight) before
+    the extra workgroups form the segments' outputs.  All heads against the
+    oracle, with a carried-in state and conv rows."""
+    T = 32768 + 19
+    x = inputs.make_prefill(T_list=[T], Hqk=2, Hv=6, seed=514, state_std=0.05, conv_state_std=1.0)
+    x["a"][:] = -9.0
+    o, so, cso = gpu_prefill(x, uniform_T=T)
+    compare(x, o, so, cso, label="long chain of segment maps")
+
+
 def test_segmented_varlen_mixed_decay(oracle_lib):
     """Packed sequences of several lengths cut into segments, two V heads
-    without decay (recomputed in order) beside normally decaying ones."""
+    without decay (their later segments through transition matrices and the
+    in-order combine) beside normally decaying ones."""
     x = inputs.make_prefill(T_list=[5000, 300, 9001, 0, 4500], Hqk=2, Hv=6, seed=511, state_std=0.05)
     x["a"][:, 1] = -9.0
     x["a"][:, 4] = -9.0
@@ -119,12 +134,12 @@ def test_segmented_varlen_mixed_decay(oracle_lib):
 
 def test_in_place_state_with_segments():
     """state_out == state_in on a sequence cut into many segments (some of
-    them recomputed in order) gives exactly the out-of-place result."""
+    them missing their warm-up bounds) gives exactly the out-of-place result."""
     import torch
     import linear_attention_sequence_gdn_amd as gdn
     T = 8192 + 37
     x = inputs.make_prefill(T_list=[T], Hqk=2, Hv=6, seed=512, state_std=0.05)
-    x["a"][:, :2] = -9.0  # two heads without decay: their later segments are recomputed
+    x["a"][:, :2] = -9.0  # two heads without decay: their later segments miss the bound
     o1, s1, _ = gpu_prefill(x, uniform_T=T, conv_out=False)
     d = x["d"]
     st = dev_f32(x["state_in"])
@@ -390,7 +405,7 @@ def test_varlen_slots_equal_plain_call_bitwise():
 def test_conv_rows_in_place_segmented(oracle_lib):
     """conv_state_out == conv_state_in on a sequence cut into segments, where
     later segments restart from the sequence start (and so read the incoming
-    conv rows) and others are recomputed in order: bit for bit the
+    conv rows) and others miss the warm-up bound: bit for bit the
     out-of-place result, which the oracle checks."""
     import torch
     import linear_attention_sequence_gdn_amd as gdn

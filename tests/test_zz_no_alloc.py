@@ -49,8 +49,8 @@ def _run(x, T, noalloc):
 def test_noalloc_equals_workspace_call_twice():
     import linear_attention_sequence_gdn_amd as gdn
     # first call: a sequence cut into segments, two of its V heads without
-    # decay (their later segments are recomputed in order through the
-    # per-(sequence, head) counters that live in the workspace)
+    # decay (their later segments go through the segment maps, the
+    # per-(sequence, head) counters and flags that live in the workspace)
     T1 = 8192 + 37
     x1 = inputs.make_prefill(T_list=[T1], Hqk=2, Hv=6, seed=901, state_std=0.05, conv_state_std=1.0)
     x1["a"][:, :2] = -9.0
