@@ -100,7 +100,7 @@ int gdn_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v,
  * hipEventElapsedTime: events[0] before the first kernel, then one after each
  * of the chunk-table setup (nothing is launched for uniform batches), the
  * parallel per-chunk pass and the segmented sequential pass (which includes
- * its in-order repair of segments).  events must not be NULL and must hold
+ * the in-order combine of the segments that miss their warm-up bound).  events must not be NULL and must hold
  * four events.
  */
 int gdn_prefill_with_events(const uint16_t *q, const uint16_t *k, const uint16_t *v,

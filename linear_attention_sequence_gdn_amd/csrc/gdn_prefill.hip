@@ -27,9 +27,11 @@
 //                blocked unit-lower-triangular inverse, T';
 //   chain     -- the sequential pass over (segment, V head): conv + SiLU of v
 //                and every product that involves the state; each wave
-//                carries 16 columns of S in registers.  The last workgroup of
-//                a (sequence, V head) to finish recomputes, in order, the
-//                segments whose warm-up bound failed.
+//                carries 16 columns of S in registers.  A segment whose
+//                warm-up bound fails carries its transition matrix as well;
+//                the last workgroup of a (sequence, V head) to finish chains
+//                the segments' affine maps in order, and extra workgroups
+//                form those segments' outputs from the states it hands them.
 #include "gdn_prefill.h"
 
 namespace gdn {
@@ -1466,14 +1468,18 @@ __device__ __forceinline__ void write_conv_rows(const PrefillArgs &p, const int4
 
 // Sequential pass: one workgroup per (segment, V head); segments run in
 // parallel, each from its warm-up start.  Every workgroup makes the warm-up
-// test of all segments of its sequence.  If one misses its bound, or the
-// call is in place, the last workgroup of the (sequence, V head) to finish --
-// a device-scope counter per pair, zeroed by the parallel pass -- walks the
-// sequence's segments in order and recomputes, exactly from the state the
-// previous segment handed over, those whose bound was not met, and hands a
-// sequence of several segments its final state.  Only a workgroup whose
-// parked state that walk will read publishes it with a device-scope fence;
-// the common case (no failed bound, out of place) needs no counter at all.
+// test of all segments of its sequence.  A segment that misses its bound
+// forms instead the affine map S -> M S + S0 from the state entering it to
+// the one leaving it (two runs without output).  If a segment misses its
+// bound, or the call is in place, the last workgroup of the (sequence, V
+// head) to finish -- a device-scope counter per pair, zeroed by the parallel
+// pass -- walks the sequence's segments in order, applies the maps to the
+// states the previous segments hand over, hands a sequence of several
+// segments its final state, and sets the pair's flag, on which the extra
+// workgroups of the missed segments (the second half of the grid) wait
+// before they form those segments' outputs.  Only a workgroup whose parked
+// state the walk will read publishes it with a device-scope fence; the
+// common case (no failed bound, out of place) needs no counter at all.
 __global__ __launch_bounds__(kChainThreads) __attribute__((amdgpu_waves_per_eu(kChainWaves / 4, kChainWaves / 4)))
 void chain_kernel(PrefillArgs p, Workspace ws)
 {
@@ -1602,8 +1608,9 @@ void chain_kernel(PrefillArgs p, Workspace ws)
 
     // The in-order walk, if any segment missed its bound or the call is in
     // place: the last workgroup of the sequence to finish does it.  A
-    // workgroup publishes its parked state first if the walk will read it
-    // (the next segment is recomputed, or the final state of an in-place call).
+    // workgroup publishes what it parked first if the walk will read it (its
+    // own segment or the next one missed the bound, or the final state of an
+    // in-place call).
     if (nseg <= 1 || (!any_bad && !p.defer_final && !p.defer_conv)) return;
     if (w < 0 || next_bad || (i_seg == nseg - 1 && p.defer_final)) __threadfence();
     __syncthreads();
@@ -1639,7 +1646,7 @@ void chain_kernel(PrefillArgs p, Workspace ws)
         __syncthreads();
         if (t == 0) __hip_atomic_store(ws.seg_ready + (long)s * Hv + h, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    // the final state, when the last segment was recomputed here or parked it
+    // the final state, when the walk formed the last segment's or it was parked
     if (carry || p.defer_final) {
         if (!carry) state_load(S, ws.bstate + ((long)(ss.x + nseg - 1) * Hv + h) * kStateFloats, wave, lane);
         state_store(S, p.state_out + sbase, wave, lane);
