@@ -1003,15 +1003,14 @@ __device__ __forceinline__ half8 tri_frag_ld(const uint8_t *base, int f, int lan
 // One chunk from operand buffer `cur`; loads the next chunk's operands into
 // `nxt`.  kOut = false: a warm-up chunk, which only advances the state (no
 // Q S, no output); it waits for its own DMA at its end, since it issues no
-// output stores after it.  kZeroV: the chunk's v^ taken as zero (the run
-// that carries a segment's transition matrix instead of a state).
+// output stores after it.
 //   Z, X, Vn [rt][x]  tokens 16rt.. x columns 16x..  (accumulator rows = tokens)
 //   QST      [x][rt]  (Q S)^T, columns 16x.. x tokens 16rt.. (accumulator rows = columns)
 // The output is formed transposed, O^T = S^T Q^T diag(q_scale Gam) + Vnew^T P^T,
 // so that a lane holds four adjacent columns of one token (8-byte LDS writes
 // into the row staging).  The fragment layout is the same for A and B
 // operands, so the packed state and Vnew serve as A operands unchanged.
-template <bool kOut, bool kZeroV = false>
+template <bool kOut>
 __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace &ws, uint8_t *cur, uint8_t *nxt,
                                            uint8_t *stage, f32x4 (&S)[8][kChainCT], const bf16x8 (&wb)[kChainCT][2],
                                            const ChainRun &run, int cc, int h, int g, int wave, int lane)
@@ -1056,7 +1055,7 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
             if (kOut) aq[rt] = Qf[(rt * 4 + kb) * 64];
         }
         bf16x8 cv[4][kChainCT][2];
-        if (kb == 0 && !kZeroV) {
+        if (kb == 0) {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -1079,7 +1078,7 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
             const int rt = sl / (2 * kChainCT), r = sl % (2 * kChainCT);
             if (r < kChainCT) X[rt][r] = mfma16(ak[rt], sb[r], X[rt][r]);
             else if (kOut) QST[r - kChainCT][rt] = mfma16(sb[r - kChainCT], aq[rt], QST[r - kChainCT][rt]);
-            if (!kZeroV && kb > 0 && sl < 4 * kChainCT) Z[kb - 1][sl >> 2][sl & 3] = silu_f(Z[kb - 1][sl >> 2][sl & 3]);
+            if (kb > 0 && sl < 4 * kChainCT) Z[kb - 1][sl >> 2][sl & 3] = silu_f(Z[kb - 1][sl >> 2][sl & 3]);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (kb == 0) {
@@ -1087,10 +1086,6 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                 for (int x = 0; x < kChainCT; ++x) {
-                    if (kZeroV) {
-                        Z[rt][x] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        continue;
-                    }
                     Z[rt][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cv[rt][x][0], wb[x][0], f32x4{0.f, 0.f, 0.f, 0.f},
                                                                        0, 0, 0);
                     Z[rt][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cv[rt][x][1], wb[x][1], Z[rt][x], 0, 0, 0);
@@ -1098,10 +1093,8 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    if (!kZeroV) {
 #pragma unroll
-        for (int sl = 0; sl < 4 * kChainCT; ++sl) Z[3][sl >> 2][sl & 3] = silu_f(Z[3][sl >> 2][sl & 3]);
-    }
+    for (int sl = 0; sl < 4 * kChainCT; ++sl) Z[3][sl >> 2][sl & 3] = silu_f(Z[3][sl >> 2][sl & 3]);
     // Vnew = T' (v^ - diag(Gam) X): the bracket as B operands over the chunk's
     // two 32-token blocks, T' lower triangular
     half8 tf[6];
@@ -1236,10 +1229,7 @@ __device__ __forceinline__ void chain_step(const PrefillArgs &p, const Workspace
     // the staging is rewritten by the next step only after its block barrier
 }
 
-// The chunks of one run, the state carried in registers.  kZeroV: v^ taken
-// as zero, for a segment's transition matrix; such a run has no output
-// chunks (c_out >= c_to).
-template <bool kZeroV = false>
+// The chunks of one run, the state carried in registers.
 __device__ __forceinline__ void chain_run(const PrefillArgs &p, const Workspace &ws, uint8_t *buf0, uint8_t *buf1,
                                           uint8_t *stage, f32x4 (&S)[8][kChainCT],
                                           const bf16x8 (&wb)[kChainCT][2], const ChainRun &run, int h, int g, int wave,
@@ -1252,26 +1242,22 @@ __device__ __forceinline__ void chain_run(const PrefillArgs &p, const Workspace 
     // warm-up chunks [c_from, c_out): the state only
     const int cw = min(run.c_out, run.c_to);
     for (; cc + 2 <= cw; cc += 2) {
-        chain_step<false, kZeroV>(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
-        chain_step<false, kZeroV>(p, ws, buf1, buf0, stage, S, wb, run, cc + 1, h, g, wave, lane);
+        chain_step<false>(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
+        chain_step<false>(p, ws, buf1, buf0, stage, S, wb, run, cc + 1, h, g, wave, lane);
     }
     if (cc < cw) {  // an odd warm-up: the next chunk sits in buf1
-        chain_step<false, kZeroV>(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
+        chain_step<false>(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
         ++cc;
-        if constexpr (!kZeroV) {
-            if (cc < run.c_to) {
-                chain_step<true>(p, ws, buf1, buf0, stage, S, wb, run, cc, h, g, wave, lane);
-                ++cc;
-            }
+        if (cc < run.c_to) {
+            chain_step<true>(p, ws, buf1, buf0, stage, S, wb, run, cc, h, g, wave, lane);
+            ++cc;
         }
     }
-    if constexpr (!kZeroV) {
-        for (; cc + 2 <= run.c_to; cc += 2) {
-            chain_step<true>(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
-            chain_step<true>(p, ws, buf1, buf0, stage, S, wb, run, cc + 1, h, g, wave, lane);
-        }
-        if (cc < run.c_to) chain_step<true>(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
+    for (; cc + 2 <= run.c_to; cc += 2) {
+        chain_step<true>(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
+        chain_step<true>(p, ws, buf1, buf0, stage, S, wb, run, cc + 1, h, g, wave, lane);
     }
+    if (cc < run.c_to) chain_step<true>(p, ws, buf0, buf1, stage, S, wb, run, cc, h, g, wave, lane);
     // the last step's DMA into the other buffer is still in flight
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -1516,14 +1502,12 @@ void chain_kernel(PrefillArgs p, Workspace ws)
     const long sbase = ((long)row * Hv + h) * kD * kD;
     const uint16_t *hist = p.conv_state_in ? p.conv_state_in + (long)row * 3 * C_tot + cv : nullptr;
     const uint16_t *vs = p.v + (long)si.z * Hv * kD + (long)h * kD;
-    // conv taps of the wave's channel tiles
-    bf16x8 wb[kChainCT][2];
-#pragma unroll
-    for (int x = 0; x < kChainCT; ++x)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) wb[x][m] = conv_tap_frag(p.conv_w, cv + kCW * wave + 16 * x + (lane & 15), m, lane);
     f32x4 S[8][kChainCT];
 
+    const int2 ss = Tables::seq_segs(p, ws, s);  // first segment, segments
+    const int nseg = min(ss.y, p.max_segs - ss.x), i_seg = k - ss.x;
+    int w = sg.y;
+    bool any_bad = false, next_bad = false;
     if (extra) {
         if (first) return;  // a sequence's first segment always starts from the true state
         if (warm_start(ws, h, Hv, sg.y, si.x, lane) >= 0) return;  // its main workgroup wrote its output
@@ -1536,67 +1520,91 @@ void chain_kernel(PrefillArgs p, Workspace ws)
             s_total = ok;
         }
         __syncthreads();
-        if (!s_total) return;  // not reached: the combine's workgroup has a lower id
+        if (!s_total) {
+            // not reached (the combine's workgroup has a lower id and waits
+            // on nothing); should the bound ever expire, the segment's output
+            // rows are NaN instead of left unwritten
+            const int rel0 = (sg.y - si.x) * kChunk, rel1 = min((sg.z - si.x) * kChunk, si.w);
+            const uint16_t nan16 = 0x7fc0;
+            for (long i = t; i < (long)(rel1 - rel0) * kD; i += kChainThreads)
+                p.o[((long)(si.z + rel0 + i / kD) * Hv + h) * kD + i % kD] = nan16;
+            return;
+        }
         __threadfence();
-        state_load(S, ws.bstate + ((long)(k - 1) * Hv + h) * kStateFloats, wave, lane);
-        chain_run(p, ws, buf0, buf1, stage, S, wb, ChainRun{si.x, si.z, si.w, sg.y, sg.z, sg.y, vs, hist}, h, g, wave,
-                  lane);
-        return;
-    }
-
-    // The warm-up test of every segment of the sequence, the same in every
-    // workgroup of it (gate loads of four segments in flight together): this
-    // segment's start, whether the next one misses its bound, and whether
-    // any does.
-    const int2 ss = Tables::seq_segs(p, ws, s);  // first segment, segments
-    const int nseg = min(ss.y, p.max_segs - ss.x), i_seg = k - ss.x;
-    int w = sg.y;
-    bool any_bad = false, next_bad = false;
-    for (int i0 = 1; i0 < nseg; i0 += 4) {
-        int cb[4];
-        float gv[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = i0 + u;
-            cb[u] = i < nseg ? Tables::seg(p, ws, ss.x + i).y : si.x;
-            gv[u] = i < nseg ? warm_gate(ws, h, Hv, cb[u], si.x, lane) : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = i0 + u;
-            if (i >= nseg) continue;
-            const int wi = warm_pick(gv[u], cb[u], si.x, lane);
-            any_bad |= wi < 0;
-            if (i == i_seg) w = wi;
-            if (i == i_seg + 1) next_bad = wi < 0;
-        }
-    }
-    if (w >= 0) {
-        state_load(S, w == si.x && p.state_in ? p.state_in + sbase : nullptr, wave, lane);
-        chain_run(p, ws, buf0, buf1, stage, S, wb, ChainRun{si.x, si.z, si.w, w, sg.z, sg.y, vs, hist}, h, g, wave,
-                  lane);
-        // Final states.  Every segment but the last parks its final state for
-        // the in-order pass, which hands it to the next segment if that one
-        // misses its bound.  The last segment writes state_out, unless
-        // state_out is state_in and other blocks of the sequence may still be
-        // reading it: then it parks its state as well and the in-order pass
-        // moves it.
-        const bool direct = last && (first || !p.defer_final);
-        state_store(S, direct ? p.state_out + sbase : ws.bstate + ((long)k * Hv + h) * kStateFloats, wave, lane);
     } else {
-        // The segment misses its warm-up bound: the map from the state that
-        // enters it to the one that leaves it, S -> M S + S0, is formed here
-        // (two runs without output) and parked; the in-order pass applies it
-        // and the segment's extra workgroup forms the output.
-        state_load(S, nullptr, wave, lane);
-        chain_run(p, ws, buf0, buf1, stage, S, wb, ChainRun{si.x, si.z, si.w, sg.y, sg.z, sg.z, vs, hist}, h, g, wave,
-                  lane);
-        state_store(S, ws.bstate + ((long)k * Hv + h) * kStateFloats, wave, lane);
+        // The warm-up test of every segment of the sequence, the same in
+        // every workgroup of it (gate loads of four segments in flight
+        // together): this segment's start, whether the next one misses its
+        // bound, and whether any does.
+        for (int i0 = 1; i0 < nseg; i0 += 4) {
+            int cb[4];
+            float gv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + u;
+                cb[u] = i < nseg ? Tables::seg(p, ws, ss.x + i).y : si.x;
+                gv[u] = i < nseg ? warm_gate(ws, h, Hv, cb[u], si.x, lane) : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + u;
+                if (i >= nseg) continue;
+                const int wi = warm_pick(gv[u], cb[u], si.x, lane);
+                any_bad |= wi < 0;
+                if (i == i_seg) w = wi;
+                if (i == i_seg + 1) next_bad = wi < 0;
+            }
+        }
+    }
+    // The workgroup's runs:
+    //  - main, bound met: from the initial state at the sequence start, or
+    //    from zero at its warm-up start, with output from the segment start.
+    //    Every segment but the last parks its final state for the in-order
+    //    pass, which hands it to the next segment if that one misses its
+    //    bound.  The last segment writes state_out, unless state_out is
+    //    state_in and other blocks of the sequence may still be reading it:
+    //    then it parks its state as well and the in-order pass moves it.
+    //  - main, bound missed: the map from the state that enters the segment
+    //    to the one that leaves it, S -> M S + S0: S0 from zero, then M from
+    //    the identity with v^ = 0 (zero conv taps: SiLU(0) = 0), both without
+    //    output and parked; the in-order pass applies the map.
+    //  - extra: from the state the in-order pass parked for the segment, with
+    //    output.
+    const bool missed = !extra && w < 0;
+    {
+        const float *src = nullptr;
+        float *dst = nullptr;
+        int c_from = sg.y, c_out = sg.y;
+        if (extra) {
+            src = ws.bstate + ((long)(k - 1) * Hv + h) * kStateFloats;
+        } else if (!missed) {
+            const bool direct = last && (first || !p.defer_final);
+            src = w == si.x && p.state_in ? p.state_in + sbase : nullptr;
+            dst = direct ? p.state_out + sbase : ws.bstate + ((long)k * Hv + h) * kStateFloats;
+            c_from = w;
+        } else {
+            dst = ws.bstate + ((long)k * Hv + h) * kStateFloats;
+            c_out = sg.z;
+        }
+        // conv taps of the wave's channel tiles
+        bf16x8 taps[kChainCT][2];
+#pragma unroll
+        for (int x = 0; x < kChainCT; ++x)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) taps[x][m] = conv_tap_frag(p.conv_w, cv + kCW * wave + 16 * x + (lane & 15), m, lane);
+        state_load(S, src, wave, lane);
+        chain_run(p, ws, buf0, buf1, stage, S, taps, ChainRun{si.x, si.z, si.w, c_from, sg.z, c_out, vs, hist}, h, g,
+                  wave, lane);
+        if (dst) state_store(S, dst, wave, lane);
+    }
+    if (missed) {
+        const bf16x8 zero_taps[kChainCT][2] = {};
         state_identity(S, wave, lane);
-        chain_run<true>(p, ws, buf0, buf1, stage, S, wb, ChainRun{si.x, si.z, si.w, sg.y, sg.z, sg.z, vs, hist}, h, g,
-                        wave, lane);
+        chain_run(p, ws, buf0, buf1, stage, S, zero_taps, ChainRun{si.x, si.z, si.w, sg.y, sg.z, sg.z, vs, hist}, h,
+                  g, wave, lane);
         state_store(S, ws.mstate + ((long)k * Hv + h) * kStateFloats, wave, lane);
     }
+    if (extra) return;
     // carried conv rows: the last three raw rows of the sequence (v channels
     // of head h; the first head of the group also writes the q and k
     // channels).  In place, the v rows wait for every workgroup of the
