@@ -380,6 +380,45 @@ def test_varlen_slots_in_place_against_oracle(oracle_lib):
     np.testing.assert_array_equal(sg[slots[1]], pool_st[slots[1]])
 
 
+def test_varlen_slots_in_place_segmented_no_decay(oracle_lib):
+    """Long packed sequences through a slot table into pools updated in place,
+    cut into segments, with two V heads that do not decay: their later
+    segments go through the segment maps, whose in-order pass also moves the
+    final states into the pool rows and writes the v conv rows last."""
+    import torch
+    import linear_attention_sequence_gdn_amd as gdn
+    lens = [9000, 0, 5000, 300]
+    rows = 7
+    x, slots, ok, pool_st, pool_cs = _pool_case(lens, rows, seed=570, bad=3)
+    x["a"][:, 1] = -9.0
+    x["a"][:, 4] = -9.0
+    d, Hv = x["d"], x["Hv"]
+    st, cs = dev_f32(pool_st), dev_bf16(pool_cs)
+    o = torch.full((x["T_tot"], Hv, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    gdn.gdn_prefill_varlen(dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"]), dev_f32(x["a"]), dev_f32(x["b"]),
+                           dev_bf16(x["conv_w"]), dev_i32(x["cu_seqlens"]), gate_scale=x["gate_scale"],
+                           state_in=st, state_out=st, conv_state_in=cs, conv_state_out=cs, o=o,
+                           slots=dev_i32(slots))
+    torch.cuda.synchronize()
+    og, sg, cg = host_bf16(o), st.cpu().numpy(), host_u16(cs)
+    cu = x["cu_seqlens"]
+    sub = dict(x)
+    idx = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in ok])
+    for key in ("q", "k", "v", "a", "b"):
+        sub[key] = x[key][idx]
+    sub["cu_seqlens"] = np.concatenate([[0], np.cumsum([lens[s] for s in ok])]).astype(np.int32)
+    sub["state_in"] = pool_st[slots[ok]]
+    sub["conv_state_in"] = pool_cs[slots[ok]]
+    o_ref, s_ref, cs_ref = oracle_prefill(sub)
+    check_output(og[idx], o_ref)
+    check_state(sg[slots[ok]], s_ref)
+    np.testing.assert_array_equal(cg[slots[ok]], cs_ref)
+    untouched = sorted(set(range(rows)) - set(slots[ok].tolist()))
+    np.testing.assert_array_equal(sg[untouched], pool_st[untouched])
+    np.testing.assert_array_equal(cg[untouched], pool_cs[untouched])
+    assert np.all(og[cu[3]:cu[4]] == 7.0)  # the skipped sequence
+
+
 def test_varlen_slots_equal_plain_call_bitwise():
     """Through a slot table (out of place, rows permuted) the results are bit
     for bit those of the plain packed call on gathered rows."""
