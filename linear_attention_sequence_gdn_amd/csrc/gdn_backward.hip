@@ -90,6 +90,7 @@ struct BwdWs {
     float *sdot;        // [chunk][Hv][kSD] <dS', S> of each (column block, wave): state
                         //                   gradient leaving the chunk, state entering it
     float *dwp;         // [chunk][C_tot][4] conv weight gradient of each chunk
+    float *KK;          // [chunk][Hqk][64][64] k^ k^T of each (chunk, QK group)
 };
 
 __device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + expf(-x)); }
@@ -326,10 +327,12 @@ __global__ __launch_bounds__(kBT) void bwd_local_kernel(BwdArgs p, BwdWs ws)
                 qk[m] = fmaf(qi, kj, qk[m]);
             }
         }
+        float *kkg = ws.KK + ((long)cidx * Hqk + g) * 4096 + i * 64;
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
             KK[i * kLN + (t & 3) + 4 * m] = kk[m];
             QK[i * kLN + (t & 3) + 4 * m] = qk[m];
+            kkg[(t & 3) + 4 * m] = kk[m];  // for the per-head gradient kernel
         }
     }
     __syncthreads();  // the k^ / q^ rows are dead from here on
@@ -972,9 +975,16 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             Wm[r * kLN + jj] = (jj < r && r < n) ? -acc[ri][m] : 0.f;
         }
     __syncthreads();
-    // (h) A = diag(beta) K K^T * D (strict lower): dbeta_i, Em += dA * A, dKK -> Ym
-    zero(acc);
-    gemm64<4, true, true>(acc, kD, KH4, [&](int d, int jj) { return KH4(jj, d); }, sA, sB);
+    // (h) A = diag(beta) K K^T * D (strict lower): dbeta_i, Em += dA * A, dKK -> Ym;
+    //     K K^T of the QK group as the chunk-local pass formed it (the same
+    //     multiply-adds in the same order)
+    {
+        const float *kkg = ws.KK + ((long)cidx * Hqk + g) * 4096;
+#pragma unroll
+        for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) acc[ri][m] = kkg[(r0 + ri) * 64 + cc + 16 * m];
+    }
     {
         float part[4];
 #pragma unroll
@@ -1231,22 +1241,23 @@ __global__ __launch_bounds__(1024) void bwd_setup_kernel(BwdArgs p, BwdWs ws)
 }
 
 // Workspace carve-up: sizes in floats, each region 64-byte aligned
+constexpr int kBwdRegions = 21;  // two int4 tables and the nineteen float regions of BwdWs
 struct BwdLayout {
-    long off[20];
+    long off[kBwdRegions];
     long total;
 };
 BwdLayout bwd_layout(int N, int T_tot, int max_chunks, int Hqk, int Hv)
 {
     const long tok = T_tot, chunks = max_chunks;
     const long C_tot = 2L * Hqk * kD + (long)Hv * kD;
-    const long sizes[20] = {chunks * 4, (long)N * 4,  // int4 tables
+    const long sizes[kBwdRegions] = {chunks * 4, (long)N * 4,  // int4 tables
                             tok * Hqk * kD, tok * Hqk * kD, tok * Hv * kD, tok * Hv, tok * Hv,
                             chunks * Hv * 4096, chunks * Hv * 4096, chunks * Hv * kD * kD, chunks * Hv * kD * kD,
                             tok * Hv * kD, tok * Hv * kD, tok * Hv * kD, tok * Hv * kD, tok * Hv * kD,
-                            tok * Hv * kD, tok * C_tot, chunks * C_tot * 4, chunks * Hv * kSD};
+                            tok * Hv * kD, tok * C_tot, chunks * C_tot * 4, chunks * Hv * kSD, chunks * Hqk * 4096};
     BwdLayout L{};
     long o = 0;
-    for (int i = 0; i < 20; ++i) {
+    for (int i = 0; i < kBwdRegions; ++i) {
         L.off[i] = o;
         o += (sizes[i] + 15) / 16 * 16;
     }
@@ -1295,9 +1306,9 @@ hipError_t launch_backward(const uint16_t *q, const uint16_t *k, const uint16_t 
         float *base = static_cast<float *>(workspace);
         ws.chunk_info = reinterpret_cast<int4 *>(base + L.off[0]);
         ws.seq_info = reinterpret_cast<int4 *>(base + L.off[1]);
-        float **slots[18] = {&ws.qh, &ws.kh, &ws.vh, &ws.gam, &ws.beta, &ws.X, &ws.P, &ws.Sc, &ws.dSc,
-                             &ws.vt, &ws.vn, &ws.dvn, &ws.dvh, &ws.dqp, &ws.dkp, &ws.dy, &ws.dwp, &ws.sdot};
-        for (int i = 0; i < 18; ++i) *slots[i] = base + L.off[i + 2];
+        float **slots[kBwdRegions - 2] = {&ws.qh, &ws.kh, &ws.vh, &ws.gam, &ws.beta, &ws.X, &ws.P, &ws.Sc, &ws.dSc,
+                             &ws.vt, &ws.vn, &ws.dvn, &ws.dvh, &ws.dqp, &ws.dkp, &ws.dy, &ws.dwp, &ws.sdot, &ws.KK};
+        for (int i = 0; i < kBwdRegions - 2; ++i) *slots[i] = base + L.off[i + 2];
     } else {
         p.cu_seqlens = nullptr;  // nothing to tabulate: every sequence is empty
         p.T = 0;
