@@ -266,6 +266,32 @@ def test_linearity_in_values_and_state(oracle_lib):
     np.testing.assert_allclose(S4, S1 + S3, atol=1e-12)
 
 
+@pytest.mark.parametrize("decay", [True, False])
+def test_segment_map_from_identity_run(oracle_lib, decay):
+    """The state a stretch of tokens leaves behind is M S + S0 in the state S
+    it starts from, where M is the stretch run with zero values from the
+    identity and S0 the stretch run from a zero state: what lets a segment
+    whose warm-up cannot reach back be chained exactly.  Checked with and
+    without decay (alpha = 1)."""
+    rng = np.random.default_rng(19)
+    T, d = 40, 24
+    Q, K, V = rng.standard_normal((3, T, d))
+    K /= np.linalg.norm(K, axis=1, keepdims=True)
+    al = rng.uniform(0.6, 1.0, T) if decay else np.ones(T)
+    be = rng.uniform(0.0, 1.0, T)
+    _, M = oracle_lib.recurrence(Q, K, np.zeros_like(V), al, be, S0=np.eye(d))
+    _, S0 = oracle_lib.recurrence(Q, K, V, al, be, S0=np.zeros((d, d)))
+    for trial in range(3):
+        S = rng.standard_normal((d, d))
+        _, S_out = oracle_lib.recurrence(Q, K, V, al, be, S0=S)
+        np.testing.assert_allclose(S_out, M @ S + S0, rtol=1e-12, atol=1e-12)
+    # M is the product of the per-token transitions alpha_t (I - beta_t k_t k_t^T), latest on the left
+    P = np.eye(d)
+    for t in range(T):
+        P = al[t] * (np.eye(d) - be[t] * np.outer(K[t], K[t])) @ P
+    np.testing.assert_allclose(M, P, rtol=1e-12, atol=1e-12)
+
+
 def test_columns_of_state_evolve_independently(oracle_lib):
     rng = np.random.default_rng(17)
     T, d = 15, 16
