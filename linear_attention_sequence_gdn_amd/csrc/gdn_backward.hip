@@ -760,6 +760,73 @@ __device__ __forceinline__ void gemm64(float (&acc)[4][8], int K, FA4 fa4, FB4 f
     }
 }
 
+// Two 64-row products over the same B: acc1 += A1 B and acc2 += A2 B, with
+// the B slice staged once per 32-deep step (A row-major sources, B k-major,
+// as gemm64<8, true, true>).  Each accumulator sees the multiply-adds of
+// gemm64 in the same order.
+template <class FA4, class FA4b, class FB4>
+__device__ __forceinline__ void gemm64x2(float (&acc1)[4][8], float (&acc2)[4][8], int K, FA4 fa1, FA4b fa2, FB4 fb4,
+                                         float *sA1, float *sA2, float *sB)
+{
+    const int t = threadIdx.x, r0 = 4 * (t >> 4), cc = t & 15;
+    for (int k0 = 0; k0 < K; k0 += 32) {
+        float4 va1[2], va2[2], vb[4];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int idx = t + kBT * e;
+            va1[e] = fa1(idx >> 3, k0 + 4 * (idx & 7));
+            va2[e] = fa2(idx >> 3, k0 + 4 * (idx & 7));
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int idx = t + kBT * e;
+            vb[e] = fb4(k0 + 4 * (idx & 7), idx >> 3);
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int idx = t + kBT * e;
+            const float v1[4] = {va1[e].x, va1[e].y, va1[e].z, va1[e].w};
+            const float v2[4] = {va2[e].x, va2[e].y, va2[e].z, va2[e].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sA1[(4 * (idx & 7) + i) * kGA + (idx >> 3)] = v1[i];
+                sA2[(4 * (idx & 7) + i) * kGA + (idx >> 3)] = v2[i];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int idx = t + kBT * e;
+            const float v[4] = {vb[e].x, vb[e].y, vb[e].z, vb[e].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sB[(4 * (idx & 7) + i) * kGB + gemm_bpos(idx >> 3)] = v[i];
+        }
+        __syncthreads();
+#pragma unroll 2
+        for (int kk = 0; kk < 32; ++kk) {
+            const float4 a1 = *reinterpret_cast<const float4 *>(sA1 + kk * kGA + r0);
+            const float4 a2 = *reinterpret_cast<const float4 *>(sA2 + kk * kGA + r0);
+            const float av1[4] = {a1.x, a1.y, a1.z, a1.w}, av2[4] = {a2.x, a2.y, a2.z, a2.w};
+            float bv[8];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const float4 b4 = *reinterpret_cast<const float4 *>(sB + kk * kGB + 64 * h + 4 * cc);
+                bv[4 * h] = b4.x;
+                bv[4 * h + 1] = b4.y;
+                bv[4 * h + 2] = b4.z;
+                bv[4 * h + 3] = b4.w;
+            }
+#pragma unroll
+            for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    acc1[ri][m] = fmaf(av1[ri], bv[m], acc1[ri][m]);
+                    acc2[ri][m] = fmaf(av2[ri], bv[m], acc2[ri][m]);
+                }
+        }
+        __syncthreads();
+    }
+}
+
 __device__ __forceinline__ void zero(float (&acc)[4][8])
 {
 #pragma unroll
@@ -836,14 +903,32 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (cc == 0 && r < n) dst[r] += sign * (coef ? coef[r] : 1.f) * v;
         }
     };
-    float acc[4][8];
+    float acc[4][8], dK[4][8];
     {
-        // ---- dq^ first, so that its registers are free before dk^ is formed
+        // ---- dq^ first, so that its registers are free before the rest of dk^ is formed
         float dQ[4][8];
         zero(dQ);
-        // (c) O = q_scale (diag(Gam) Q S + ...): E1 = dO' S^T
+        // (c) O = q_scale (diag(Gam) Q S + ...): E1 = dO' S^T, and (e) Vt = V -
+        //     diag(Gam) K S: E2 = dVt S^T, in one pass over S (the second A
+        //     slice is staged in Ym, which is free until (f))
         zero(acc);
-        gemm64<8, true, true>(acc, kD, DO4, [&](int c, int i) { return ld4(Sc + i * kD + c); }, sA, sB);
+        zero(dK);
+        gemm64x2(acc, dK, kD, DO4, [&](int r, int c) { return V4(ws.dvh, r, c); },
+                 [&](int c, int i) { return ld4(Sc + i * kD + c); }, sA, Ym, sB);
+        {
+            float part[4];
+#pragma unroll
+            for (int ri = 0; ri < 4; ++ri) {
+                const int r = r0 + ri;
+                part[ri] = 0.f;
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    part[ri] = fmaf(dK[ri][m], KH(r, cc + 16 * m), part[ri]);
+                    dK[ri][m] *= -eg[r];
+                }
+            }
+            row_apply(part, dgam, eg, -1.f);
+        }
         float part[4];
 #pragma unroll
         for (int ri = 0; ri < 4; ++ri) {
@@ -878,8 +963,6 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int m = 0; m < 8; ++m) ws.dqp[((t0 + r) * Hv + h) * kD + cc + 16 * m] = dQ[ri][m];
         }
     }
-    float dK[4][8];
-    zero(dK);
     // (d) continued: dk^ += dQK^T q^
     gemm64<8, false, false>(dK, 64, [&](int r, int jj) { return L4(Wm + jj * kLN + r); }, QH4, sA, sB);
 
@@ -916,24 +999,6 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
     if (t < n) dgam[t] -= rowv[t];
     __syncthreads();
-    // (e) Vt = V - diag(Gam) K S: E2 = dVt S^T
-    zero(acc);
-    gemm64<8, true, true>(acc, kD, [&](int r, int c) { return V4(ws.dvh, r, c); },
-                          [&](int c, int i) { return ld4(Sc + i * kD + c); }, sA, sB);
-    {
-        float part[4];
-#pragma unroll
-        for (int ri = 0; ri < 4; ++ri) {
-            const int r = r0 + ri;
-            part[ri] = 0.f;
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                dK[ri][m] -= eg[r] * acc[ri][m];
-                part[ri] = fmaf(acc[ri][m], KH(r, cc + 16 * m), part[ri]);
-            }
-        }
-        row_apply(part, dgam, eg, -1.f);
-    }
     __syncthreads();
     // (f) Vn = T' Vt: dT' = dVn Vt^T (lower incl. diagonal); dbeta_j += sum_i dT'_ij X_ij; dX = dT' diag(beta)
     zero(acc);
