@@ -702,8 +702,10 @@ __device__ __forceinline__ void gemm64(float (&acc)[4][8], int K, FA4 fa4, FB4 f
 {
     const int t = threadIdx.x, r0 = 4 * (t >> 4), cc = t & 15;
     constexpr int NCOL = 16 * NC;
-    for (int k0 = 0; k0 < K; k0 += 32) {
-        float4 va[2], vb[NC / 2];
+    // the sources of slice k0 + 32 are requested before slice k0's
+    // multiply-adds, so that their latency overlaps them
+    float4 va[2], vb[NC / 2];
+    auto fetch = [&](int k0) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int idx = t + kBT * e;
@@ -714,6 +716,9 @@ __device__ __forceinline__ void gemm64(float (&acc)[4][8], int K, FA4 fa4, FB4 f
             const int idx = t + kBT * e;
             vb[e] = BK ? fb4(k0 + 4 * (idx & 7), idx >> 3) : fb4(k0 + idx / (NCOL / 4), 4 * (idx % (NCOL / 4)));
         }
+    };
+    fetch(0);
+    for (int k0 = 0; k0 < K; k0 += 32) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int idx = t + kBT * e;
@@ -738,6 +743,7 @@ __device__ __forceinline__ void gemm64(float (&acc)[4][8], int K, FA4 fa4, FB4 f
             }
         }
         __syncthreads();
+        if (k0 + 32 < K) fetch(k0 + 32);
 #pragma unroll 2
         for (int kk = 0; kk < 32; ++kk) {
             const float4 a4 = *reinterpret_cast<const float4 *>(sA + kk * kGA + r0);
@@ -769,8 +775,8 @@ __device__ __forceinline__ void gemm64x2(float (&acc1)[4][8], float (&acc2)[4][8
                                          float *sA1, float *sA2, float *sB)
 {
     const int t = threadIdx.x, r0 = 4 * (t >> 4), cc = t & 15;
-    for (int k0 = 0; k0 < K; k0 += 32) {
-        float4 va1[2], va2[2], vb[4];
+    float4 va1[2], va2[2], vb[4];
+    auto fetch = [&](int k0) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int idx = t + kBT * e;
@@ -782,6 +788,9 @@ __device__ __forceinline__ void gemm64x2(float (&acc1)[4][8], float (&acc2)[4][8
             const int idx = t + kBT * e;
             vb[e] = fb4(k0 + 4 * (idx & 7), idx >> 3);
         }
+    };
+    fetch(0);
+    for (int k0 = 0; k0 < K; k0 += 32) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int idx = t + kBT * e;
@@ -801,6 +810,7 @@ __device__ __forceinline__ void gemm64x2(float (&acc1)[4][8], float (&acc2)[4][8
             for (int i = 0; i < 4; ++i) sB[(4 * (idx & 7) + i) * kGB + gemm_bpos(idx >> 3)] = v[i];
         }
         __syncthreads();
+        if (k0 + 32 < K) fetch(k0 + 32);
 #pragma unroll 2
         for (int kk = 0; kk < 32; ++kk) {
             const float4 a1 = *reinterpret_cast<const float4 *>(sA1 + kk * kGA + r0);
