@@ -684,26 +684,102 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
 // 5. per-chunk gradients
 // ---------------------------------------------------------------------------
 // acc[ri][m] += sum_k A(r0 + ri, k) B(k, cc + 16 m) for k < K (a multiple
-// of 32), r0 = 4 (t / 16), cc = t % 16, m < NC: a 64 x (16 NC) product,
-// staged through LDS 32 deep.  The sources are read 16 bytes at a time along
-// their contiguous dimension: fa4(r, k) is A(r, k..k+3) when AK, else
+// of 32), r0 = 4 (t / 16), cc = t % 16, m < NC: a 64 x (16 NC) product on
+// the fp32 matrix cores (16x16x4 steps), staged through LDS 32 deep.  Wave w
+// computes row tile w: its accumulator layout (lane (q, c) holds rows
+// 4q .. 4q+3 of column c) is exactly the thread layout above, so acc is the
+// accumulator of column tile m.  The sources are read 16 bytes at a time
+// along their contiguous dimension: fa4(r, k) is A(r, k..k+3) when AK, else
 // A(r..r+3, k); fb4(k, c) is B(k..k+3, c) when BK, else B(k, c..c+3).
-// The staged slices are k-major, laid out so that a thread's operands of one
-// k are contiguous: its four A rows (r0 .. r0+3), read as one 16-byte
-// broadcast, and its NC B columns, column cc + 16 m at position
-// 64 (m / 4) + 4 cc + m % 4, read 16 bytes at a time (the sixteen lanes of a
-// quarter wave cover 256 consecutive bytes: no bank conflicts).
-constexpr int kGA = 64 + 4;   // row stride of the A slice (k-major)
-constexpr int kGB = 128 + 4;  // row stride of the B slice (k-major)
-__device__ __forceinline__ int gemm_bpos(int c) { return 64 * ((c >> 4) >> 2) + 4 * (c & 15) + ((c >> 4) & 3); }
+// Staged slices hold A by rows and B by columns, 32 k-values (128 bytes) per
+// row, the eight 16-byte pieces of row (or column) x stored at piece
+// p ^ ((x >> 1) & 7): a lane reads the 8 k-values 8q .. 8q+7 of its row as
+// two 16-byte pieces, and the sixteen lanes of a quarter wave then cover all
+// 64 banks.  Step s of a slice contracts k = 8q + s in lane group q (the
+// same permutation of k for A and B).
+__device__ __forceinline__ int gslot(int x, int k) { return x * 32 + ((((k >> 2) ^ (x >> 1)) & 7) << 2) + (k & 3); }
+
+template <int NC, bool AK, bool BK>
+__device__ __forceinline__ void gemm_stage(const float4 (&va)[2], const float4 (&vb)[NC / 2], float *sA, float *sB)
+{
+    const int t = threadIdx.x;
+    constexpr int NCOL = 16 * NC;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int idx = t + kBT * e;
+        if (AK) {
+            *reinterpret_cast<float4 *>(sA + gslot(idx >> 3, 4 * (idx & 7))) = va[e];
+        } else {
+            const int r = 4 * (idx & 15), k = idx >> 4;
+            sA[gslot(r, k)] = va[e].x;
+            sA[gslot(r + 1, k)] = va[e].y;
+            sA[gslot(r + 2, k)] = va[e].z;
+            sA[gslot(r + 3, k)] = va[e].w;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < NC / 2; ++e) {
+        const int idx = t + kBT * e;
+        if (BK) {
+            *reinterpret_cast<float4 *>(sB + gslot(idx >> 3, 4 * (idx & 7))) = vb[e];
+        } else {
+            const int k = idx / (NCOL / 4), c = 4 * (idx % (NCOL / 4));
+            sB[gslot(c, k)] = vb[e].x;
+            sB[gslot(c + 1, k)] = vb[e].y;
+            sB[gslot(c + 2, k)] = vb[e].z;
+            sB[gslot(c + 3, k)] = vb[e].w;
+        }
+    }
+}
+
+// The eight k-values 8q .. 8q+7 of staged row x
+__device__ __forceinline__ void gemm_frag(const float *src, int x, int q, float (&v)[8])
+{
+    const float4 lo = *reinterpret_cast<const float4 *>(src + gslot(x, 8 * q));
+    const float4 hi = *reinterpret_cast<const float4 *>(src + gslot(x, 8 * q + 4));
+    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+}
+
+// One staged slice: acc (column tiles m < NC of the wave's row tile) += A B
+template <int NC>
+__device__ __forceinline__ void gemm_slice(f32x4 (&acc)[NC], const float *sA, const float *sB)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, q = lane >> 4, r16 = lane & 15;
+    float a[8], b[2][8];
+    gemm_frag(sA, 16 * w + r16, q, a);
+    gemm_frag(sB, r16, q, b[0]);
+#pragma unroll
+    for (int m = 0; m < NC; ++m) {
+        if (m + 1 < NC) gemm_frag(sB, 16 * (m + 1) + r16, q, b[(m + 1) & 1]);  // the next tile's column in flight
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+            acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], b[m & 1][st], acc[m], 0, 0, 0);
+    }
+}
+
+template <int NC>
+__device__ __forceinline__ void acc_load(f32x4 (&d)[NC], const float (&acc)[4][8])
+{
+#pragma unroll
+    for (int m = 0; m < NC; ++m) d[m] = f32x4{acc[0][m], acc[1][m], acc[2][m], acc[3][m]};
+}
+template <int NC>
+__device__ __forceinline__ void acc_store(float (&acc)[4][8], const f32x4 (&d)[NC])
+{
+#pragma unroll
+    for (int m = 0; m < NC; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e][m] = d[m][e];
+}
 
 template <int NC, bool AK, bool BK, class FA4, class FB4>
 __device__ __forceinline__ void gemm64(float (&acc)[4][8], int K, FA4 fa4, FB4 fb4, float *sA, float *sB)
 {
-    const int t = threadIdx.x, r0 = 4 * (t >> 4), cc = t & 15;
+    const int t = threadIdx.x;
     constexpr int NCOL = 16 * NC;
-    // the sources of slice k0 + 32 are requested before slice k0's
-    // multiply-adds, so that their latency overlaps them
+    // the sources of slice k0 + 32 are requested before slice k0's products,
+    // so that their latency overlaps them
     float4 va[2], vb[NC / 2];
     auto fetch = [&](int k0) {
 #pragma unroll
@@ -717,64 +793,27 @@ __device__ __forceinline__ void gemm64(float (&acc)[4][8], int K, FA4 fa4, FB4 f
             vb[e] = BK ? fb4(k0 + 4 * (idx & 7), idx >> 3) : fb4(k0 + idx / (NCOL / 4), 4 * (idx % (NCOL / 4)));
         }
     };
+    f32x4 d[NC];
+    acc_load<NC>(d, acc);
     fetch(0);
     for (int k0 = 0; k0 < K; k0 += 32) {
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int idx = t + kBT * e;
-            if (AK) {
-                const float v[4] = {va[e].x, va[e].y, va[e].z, va[e].w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sA[(4 * (idx & 7) + i) * kGA + (idx >> 3)] = v[i];
-            } else {
-                *reinterpret_cast<float4 *>(sA + (idx >> 4) * kGA + 4 * (idx & 15)) = va[e];
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < NC / 2; ++e) {
-            const int idx = t + kBT * e;
-            const float v[4] = {vb[e].x, vb[e].y, vb[e].z, vb[e].w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (BK)
-                    sB[(4 * (idx & 7) + i) * kGB + gemm_bpos(idx >> 3)] = v[i];
-                else
-                    sB[(idx / (NCOL / 4)) * kGB + gemm_bpos(4 * (idx % (NCOL / 4)) + i)] = v[i];
-            }
-        }
+        gemm_stage<NC, AK, BK>(va, vb, sA, sB);
         __syncthreads();
         if (k0 + 32 < K) fetch(k0 + 32);
-#pragma unroll 2
-        for (int kk = 0; kk < 32; ++kk) {
-            const float4 a4 = *reinterpret_cast<const float4 *>(sA + kk * kGA + r0);
-            const float av[4] = {a4.x, a4.y, a4.z, a4.w};
-            float bv[NC];
-#pragma unroll
-            for (int h = 0; h < NC / 4; ++h) {
-                const float4 b4 = *reinterpret_cast<const float4 *>(sB + kk * kGB + 64 * h + 4 * cc);
-                bv[4 * h] = b4.x;
-                bv[4 * h + 1] = b4.y;
-                bv[4 * h + 2] = b4.z;
-                bv[4 * h + 3] = b4.w;
-            }
-#pragma unroll
-            for (int ri = 0; ri < 4; ++ri)
-#pragma unroll
-                for (int m = 0; m < NC; ++m) acc[ri][m] = fmaf(av[ri], bv[m], acc[ri][m]);
-        }
+        gemm_slice<NC>(d, sA, sB);
         __syncthreads();
     }
+    acc_store<NC>(acc, d);
 }
 
 // Two 64-row products over the same B: acc1 += A1 B and acc2 += A2 B, with
 // the B slice staged once per 32-deep step (A row-major sources, B k-major,
-// as gemm64<8, true, true>).  Each accumulator sees the multiply-adds of
-// gemm64 in the same order.
+// as gemm64<8, true, true>).
 template <class FA4, class FA4b, class FB4>
 __device__ __forceinline__ void gemm64x2(float (&acc1)[4][8], float (&acc2)[4][8], int K, FA4 fa1, FA4b fa2, FB4 fb4,
                                          float *sA1, float *sA2, float *sB)
 {
-    const int t = threadIdx.x, r0 = 4 * (t >> 4), cc = t & 15;
+    const int t = threadIdx.x;
     float4 va1[2], va2[2], vb[4];
     auto fetch = [&](int k0) {
 #pragma unroll
@@ -789,52 +828,23 @@ __device__ __forceinline__ void gemm64x2(float (&acc1)[4][8], float (&acc2)[4][8
             vb[e] = fb4(k0 + 4 * (idx & 7), idx >> 3);
         }
     };
+    f32x4 d1[8], d2[8];
+    acc_load<8>(d1, acc1);
+    acc_load<8>(d2, acc2);
     fetch(0);
     for (int k0 = 0; k0 < K; k0 += 32) {
+        gemm_stage<8, true, true>(va1, vb, sA1, sB);
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int idx = t + kBT * e;
-            const float v1[4] = {va1[e].x, va1[e].y, va1[e].z, va1[e].w};
-            const float v2[4] = {va2[e].x, va2[e].y, va2[e].z, va2[e].w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sA1[(4 * (idx & 7) + i) * kGA + (idx >> 3)] = v1[i];
-                sA2[(4 * (idx & 7) + i) * kGA + (idx >> 3)] = v2[i];
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int idx = t + kBT * e;
-            const float v[4] = {vb[e].x, vb[e].y, vb[e].z, vb[e].w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sB[(4 * (idx & 7) + i) * kGB + gemm_bpos(idx >> 3)] = v[i];
-        }
+        for (int e = 0; e < 2; ++e)
+            *reinterpret_cast<float4 *>(sA2 + gslot((t + kBT * e) >> 3, 4 * ((t + kBT * e) & 7))) = va2[e];
         __syncthreads();
         if (k0 + 32 < K) fetch(k0 + 32);
-#pragma unroll 2
-        for (int kk = 0; kk < 32; ++kk) {
-            const float4 a1 = *reinterpret_cast<const float4 *>(sA1 + kk * kGA + r0);
-            const float4 a2 = *reinterpret_cast<const float4 *>(sA2 + kk * kGA + r0);
-            const float av1[4] = {a1.x, a1.y, a1.z, a1.w}, av2[4] = {a2.x, a2.y, a2.z, a2.w};
-            float bv[8];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const float4 b4 = *reinterpret_cast<const float4 *>(sB + kk * kGB + 64 * h + 4 * cc);
-                bv[4 * h] = b4.x;
-                bv[4 * h + 1] = b4.y;
-                bv[4 * h + 2] = b4.z;
-                bv[4 * h + 3] = b4.w;
-            }
-#pragma unroll
-            for (int ri = 0; ri < 4; ++ri)
-#pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    acc1[ri][m] = fmaf(av1[ri], bv[m], acc1[ri][m]);
-                    acc2[ri][m] = fmaf(av2[ri], bv[m], acc2[ri][m]);
-                }
-        }
+        gemm_slice<8>(d1, sA1, sB);
+        gemm_slice<8>(d2, sA2, sB);
         __syncthreads();
     }
+    acc_store<8>(acc1, d1);
+    acc_store<8>(acc2, d2);
 }
 
 __device__ __forceinline__ void zero(float (&acc)[4][8])
@@ -857,8 +867,8 @@ __device__ __forceinline__ float sum16(float v)
 
 __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_grad_kernel(BwdArgs p, BwdWs ws)
 {
-    __shared__ __attribute__((aligned(16))) float sA[32 * kGA], sB[32 * kGB];
-    __shared__ float Em[64 * kLN], Wm[64 * kLN], Ym[64 * kLN];
+    __shared__ __attribute__((aligned(16))) float sA[64 * 32], sB[128 * 32];
+    __shared__ __attribute__((aligned(16))) float Em[64 * kLN], Wm[64 * kLN], Ym[64 * kLN];
     __shared__ float gam[64], bet[64], eg[64], en[64], dgam[64], dbet[64], rowv[64];
     const int Hv = p.Hv, Hqk = p.Hqk, G = Hv / Hqk;
     // the G blocks of one (chunk, QK group), which read the same k^ and q^
