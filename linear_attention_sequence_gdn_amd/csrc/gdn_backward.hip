@@ -269,24 +269,114 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs p, BwdWs ws)
 // ---------------------------------------------------------------------------
 // 2. P and X = (I + A)^-1 per (chunk, QK group)
 // ---------------------------------------------------------------------------
-// Column of (I + A)^-1 for a strictly lower A (row stride kLN), y = e_c on
-// entry: right-looking substitution, expanded at compile time so that y
-// stays in registers.
-template <int M>
-struct SolveCol64 {
-    static __device__ __forceinline__ void run(float (&y)[64], const float *A)
-    {
-        if constexpr (M < 63) {
+// acc += A_blk B_blk for 16 x 16 blocks of row-major LDS matrices (row
+// strides lda, ldb), on the fp32 matrix cores: lane l supplies A[l%16][k] and
+// B[k][l%16] for k = 4 kb + l/16; acc in accumulator layout (lane (q, c):
+// rows 4q .. 4q+3 of column c).
+__device__ __forceinline__ f32x4 blk_mm(const float *Ab, int lda, const float *Bb, int ldb, f32x4 acc, int lane)
+{
+    const int r = lane & 15, k = lane >> 4;
 #pragma unroll
-            for (int ii = M + 1; ii < 64; ++ii) y[ii] = fmaf(-A[ii * kLN + M], y[M], y[ii]);
-            SolveCol64<M + 1>::run(y, A);
+    for (int kb = 0; kb < 4; ++kb)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Ab[r * lda + 4 * kb + k], Bb[(4 * kb + k) * ldb + r], acc, 0, 0, 0);
+    return acc;
+}
+__device__ __forceinline__ void blk_st(float *Db, int ldd, f32x4 v, int lane)
+{
+    const int c = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Db[(4 * q + e) * ldd + c] = v[e];
+}
+
+// Column c of the inverse of the 16 x 16 unit lower-triangular block I + A
+// (A strictly lower, row stride kLN), y = e_c on entry: right-looking
+// substitution, expanded at compile time so that y stays in registers.
+template <int M>
+struct SolveCol16b {
+    static __device__ __forceinline__ void run(float (&y)[16], const float *A)
+    {
+        if constexpr (M < 15) {
+#pragma unroll
+            for (int ii = M + 1; ii < 16; ++ii) y[ii] = fmaf(-A[ii * kLN + M], y[M], y[ii]);
+            SolveCol16b<M + 1>::run(y, A);
         }
     }
 };
 
-// One workgroup per (chunk, QK group): K^K^T and Q^K^T once, then the
-// group's V heads four at a time (their A matrices reuse the LDS of the k^ /
-// q^ rows), wave w solving head w.
+// X = (I + A)^-1 of one 64 x 64 strictly lower A (row stride kLN), in place,
+// by one wave with wave-level synchronisation only: the four diagonal 16 x 16
+// blocks by substitution (lane (q, c) takes column c of block q), then the
+// blocks below them by the 2 x 2 block recursion
+// [[X_a, 0], [L_ba, X_b]]^-1 = [[X_a, 0], [-X_b L_ba X_a, X_b]], within and
+// across the 32 x 32 halves.  Block (0, 1), above the diagonal, holds the
+// intermediate products; the blocks above the diagonal are left to the caller.
+__device__ __forceinline__ void inverse64(float *H, int lane)
+{
+    auto B = [&](int i, int j) { return H + 16 * i * kLN + 16 * j; };
+    auto wave_sync = [] {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    {
+        const int q = lane >> 4, c = lane & 15;
+        float y[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) y[i] = i == c ? 1.f : 0.f;
+        SolveCol16b<0>::run(y, B(q, q));
+        wave_sync();
+#pragma unroll
+        for (int i = 0; i < 16; ++i) B(q, q)[i * kLN + c] = y[i];
+        wave_sync();
+    }
+    float *tmp = B(0, 1);
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    // X_10 = -X_11 (A_10 X_00), X_32 = -X_33 (A_32 X_22)
+    blk_st(tmp, kLN, blk_mm(B(1, 0), kLN, B(0, 0), kLN, z, lane), lane);
+    wave_sync();
+    blk_st(B(1, 0), kLN, -blk_mm(B(1, 1), kLN, tmp, kLN, z, lane), lane);
+    wave_sync();
+    blk_st(tmp, kLN, blk_mm(B(3, 2), kLN, B(2, 2), kLN, z, lane), lane);
+    wave_sync();
+    blk_st(B(3, 2), kLN, -blk_mm(B(3, 3), kLN, tmp, kLN, z, lane), lane);
+    wave_sync();
+    // M_i0 = A_i0 X_00 + A_i1 X_10, M_i1 = A_i1 X_11 (i = 2, 3), over the A blocks
+#pragma unroll
+    for (int i = 2; i < 4; ++i) {
+        f32x4 m = blk_mm(B(i, 0), kLN, B(0, 0), kLN, z, lane);
+        m = blk_mm(B(i, 1), kLN, B(1, 0), kLN, m, lane);
+        const f32x4 m1 = blk_mm(B(i, 1), kLN, B(1, 1), kLN, z, lane);
+        wave_sync();
+        blk_st(B(i, 0), kLN, m, lane);
+        blk_st(B(i, 1), kLN, m1, lane);
+        wave_sync();
+    }
+    // X_31 = -(X_32 M_21 + X_33 M_31), X_21 = -X_22 M_21
+    {
+        f32x4 x = blk_mm(B(3, 2), kLN, B(2, 1), kLN, z, lane);
+        x = blk_mm(B(3, 3), kLN, B(3, 1), kLN, x, lane);
+        const f32x4 x21 = blk_mm(B(2, 2), kLN, B(2, 1), kLN, z, lane);
+        wave_sync();
+        blk_st(B(3, 1), kLN, -x, lane);
+        blk_st(B(2, 1), kLN, -x21, lane);
+        wave_sync();
+    }
+    // X_30 = -(X_32 M_20 + X_33 M_30), X_20 = -X_22 M_20
+    {
+        f32x4 x = blk_mm(B(3, 2), kLN, B(2, 0), kLN, z, lane);
+        x = blk_mm(B(3, 3), kLN, B(3, 0), kLN, x, lane);
+        const f32x4 x20 = blk_mm(B(2, 2), kLN, B(2, 0), kLN, z, lane);
+        wave_sync();
+        blk_st(B(3, 0), kLN, -x, lane);
+        blk_st(B(2, 0), kLN, -x20, lane);
+        wave_sync();
+    }
+}
+
+// One workgroup per (chunk, QK group): K^K^T and Q^K^T once (their lower
+// 16 x 16 tiles on the fp32 matrix cores), then the group's V heads four at
+// a time (their A matrices reuse the LDS of the k^ / q^ rows), wave w
+// inverting head w's I + A.
 constexpr int kLocalR = 4 * 64 * kLN;  // >= 2 * 64 * kLK: the k^ and q^ rows, or four A matrices
 static_assert(kLocalR >= 2 * 64 * kLK, "the A matrices overlay the k^ and q^ rows");
 
@@ -313,26 +403,39 @@ __global__ __launch_bounds__(kBT) void bwd_local_kernel(BwdArgs p, BwdWs ws)
     }
     __syncthreads();
     {
-        // row i, columns (t & 3) + 4m
-        const int i = t >> 2;
-        float kk[16], qk[16];
+        // lower tiles (I, J <= I): K K^T by waves 0 (row blocks 0, 3) and 1
+        // (1, 2), Q K^T by waves 2 and 3 likewise; lane (lq, lr) contracts
+        // k = 32 lq .. 32 lq + 31 (a permutation of the 16x16x4 steps' k)
+        const int lq = lane >> 4, lr = lane & 15;
+        const float *Asrc = w < 2 ? Ks : Qs;
+        float *dst = w < 2 ? KK : QK;
+        float *kkg = ws.KK + ((long)cidx * Hqk + g) * 4096;
 #pragma unroll
-        for (int m = 0; m < 16; ++m) kk[m] = qk[m] = 0.f;
-        for (int d = 0; d < kD; ++d) {
-            const float ki = Ks[i * kLK + d], qi = Qs[i * kLK + d];
+        for (int pass = 0; pass < 2; ++pass) {
+            const int I = (w & 1) ? 1 + pass : 3 * pass;
+            float a[32];
 #pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                const float kj = Ks[((t & 3) + 4 * m) * kLK + d];
-                kk[m] = fmaf(ki, kj, kk[m]);
-                qk[m] = fmaf(qi, kj, qk[m]);
+            for (int v = 0; v < 8; ++v) {
+                const float4 u = ld4(Asrc + (16 * I + lr) * kLK + 32 * lq + 4 * v);
+                a[4 * v] = u.x; a[4 * v + 1] = u.y; a[4 * v + 2] = u.z; a[4 * v + 3] = u.w;
             }
-        }
-        float *kkg = ws.KK + ((long)cidx * Hqk + g) * 4096 + i * 64;
+            for (int J = 0; J <= I; ++J) {
+                float b[32];
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            KK[i * kLN + (t & 3) + 4 * m] = kk[m];
-            QK[i * kLN + (t & 3) + 4 * m] = qk[m];
-            kkg[(t & 3) + 4 * m] = kk[m];  // for the per-head gradient kernel
+                for (int v = 0; v < 8; ++v) {
+                    const float4 u = ld4(Ks + (16 * J + lr) * kLK + 32 * lq + 4 * v);
+                    b[4 * v] = u.x; b[4 * v + 1] = u.y; b[4 * v + 2] = u.z; b[4 * v + 3] = u.w;
+                }
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st = 0; st < 32; ++st) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], b[st], acc, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * I + 4 * lq + e, j = 16 * J + lr;
+                    dst[i * kLN + j] = acc[e];
+                    if (w < 2) kkg[i * 64 + j] = acc[e];  // for the per-head gradient kernel (lower tiles)
+                }
+            }
         }
     }
     __syncthreads();  // the k^ / q^ rows are dead from here on
@@ -344,25 +447,33 @@ __global__ __launch_bounds__(kBT) void bwd_local_kernel(BwdArgs p, BwdWs ws)
             bet[w][lane] = lane < n ? ws.beta[(t0 + lane) * Hv + h] : 0.f;
         }
         __syncthreads();
-        // A (strict lower) into LDS and P (lower incl. the diagonal) to the workspace, for each head
+        // A (strict lower) into LDS and P (lower incl. the diagonal) to the
+        // workspace, for each head; tiles above the diagonal are never read
         for (int idx = t; idx < jn * 4096; idx += kBT) {
             const int jh = idx >> 12, i = (idx >> 6) & 63, jj = idx & 63;
+            if (jj > i) {
+                const long mo = ((long)cidx * Hv + g * G + j0 + jh) * 4096;
+                ws.P[mo + i * 64 + jj] = 0.f;
+                continue;
+            }
             const float D = expf(gam[jh][i] - gam[jh][jj]);
             R[jh * 64 * kLN + i * kLN + jj] = (jj < i && i < n) ? bet[jh][i] * KK[i * kLN + jj] * D : 0.f;
             const long mo = ((long)cidx * Hv + g * G + j0 + jh) * 4096;
-            ws.P[mo + i * 64 + jj] = (jj <= i && i < n) ? QK[i * kLN + jj] * D : 0.f;
+            ws.P[mo + i * 64 + jj] = i < n ? QK[i * kLN + jj] * D : 0.f;
         }
         __syncthreads();
-        // unit lower-triangular inverse of head w's I + A, lane c takes column c in
-        // registers: once x_m is final it is removed from every later row
+        // X = (I + A)^-1 of head w, in place; written out whole, zero above the diagonal
         if (w < jn) {
-            float y[64];
-#pragma unroll
-            for (int ii = 0; ii < 64; ++ii) y[ii] = ii == lane ? 1.f : 0.f;
-            SolveCol64<0>::run(y, R + w * 64 * kLN);
+            float *H = R + w * 64 * kLN;
+            inverse64(H, lane);
             const long mo = ((long)cidx * Hv + g * G + j0 + w) * 4096;
 #pragma unroll
-            for (int ii = 0; ii < 64; ++ii) ws.X[mo + ii * 64 + lane] = y[ii];
+            for (int e = 0; e < 16; ++e) {
+                const int idx = lane + 64 * e, r = idx >> 4, c4 = 4 * (idx & 15);
+                const float4 v = c4 >= 16 * (r / 16 + 1) ? make_float4(0.f, 0.f, 0.f, 0.f)
+                                                         : *reinterpret_cast<const float4 *>(H + r * kLN + c4);
+                st4(ws.X + mo + r * 64 + c4, v);
+            }
         }
         __syncthreads();  // the next round rewrites the gates and the A matrices
     }
