@@ -794,12 +794,12 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
 // ---------------------------------------------------------------------------
 // 5. per-chunk gradients
 // ---------------------------------------------------------------------------
-// acc[ri][m] += sum_k A(r0 + ri, k) B(k, cc + 16 m) for k < K (a multiple
+// acc[m][ri] += sum_k A(r0 + ri, k) B(k, cc + 16 m) for k < K (a multiple
 // of 32), r0 = 4 (t / 16), cc = t % 16, m < NC: a 64 x (16 NC) product on
 // the fp32 matrix cores (16x16x4 steps), staged through LDS 32 deep.  Wave w
 // computes row tile w: its accumulator layout (lane (q, c) holds rows
-// 4q .. 4q+3 of column c) is exactly the thread layout above, so acc is the
-// accumulator of column tile m.  The sources are read 16 bytes at a time
+// 4q .. 4q+3 of column c) is exactly the thread layout above, so acc[m] is
+// the accumulator of column tile m.  The sources are read 16 bytes at a time
 // along their contiguous dimension: fa4(r, k) is A(r, k..k+3) when AK, else
 // A(r..r+3, k); fb4(k, c) is B(k..k+3, c) when BK, else B(k, c..c+3).
 // Staged slices hold A by rows and B by columns, 32 k-values (128 bytes) per
@@ -869,23 +869,8 @@ __device__ __forceinline__ void gemm_slice(f32x4 (&acc)[NC], const float *sA, co
     }
 }
 
-template <int NC>
-__device__ __forceinline__ void acc_load(f32x4 (&d)[NC], const float (&acc)[4][8])
-{
-#pragma unroll
-    for (int m = 0; m < NC; ++m) d[m] = f32x4{acc[0][m], acc[1][m], acc[2][m], acc[3][m]};
-}
-template <int NC>
-__device__ __forceinline__ void acc_store(float (&acc)[4][8], const f32x4 (&d)[NC])
-{
-#pragma unroll
-    for (int m = 0; m < NC; ++m)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e][m] = d[m][e];
-}
-
 template <int NC, bool AK, bool BK, class FA4, class FB4>
-__device__ __forceinline__ void gemm64(float (&acc)[4][8], int K, FA4 fa4, FB4 fb4, float *sA, float *sB)
+__device__ __forceinline__ void gemm64(f32x4 (&acc)[8], int K, FA4 fa4, FB4 fb4, float *sA, float *sB)
 {
     const int t = threadIdx.x;
     constexpr int NCOL = 16 * NC;
@@ -904,8 +889,7 @@ __device__ __forceinline__ void gemm64(float (&acc)[4][8], int K, FA4 fa4, FB4 f
             vb[e] = BK ? fb4(k0 + 4 * (idx & 7), idx >> 3) : fb4(k0 + idx / (NCOL / 4), 4 * (idx % (NCOL / 4)));
         }
     };
-    f32x4 d[NC];
-    acc_load<NC>(d, acc);
+    f32x4 (&d)[NC] = reinterpret_cast<f32x4 (&)[NC]>(acc);
     fetch(0);
     for (int k0 = 0; k0 < K; k0 += 32) {
         gemm_stage<NC, AK, BK>(va, vb, sA, sB);
@@ -914,14 +898,13 @@ __device__ __forceinline__ void gemm64(float (&acc)[4][8], int K, FA4 fa4, FB4 f
         gemm_slice<NC>(d, sA, sB);
         __syncthreads();
     }
-    acc_store<NC>(acc, d);
 }
 
 // Two 64-row products over the same B: acc1 += A1 B and acc2 += A2 B, with
 // the B slice staged once per 32-deep step (A row-major sources, B k-major,
 // as gemm64<8, true, true>).
 template <class FA4, class FA4b, class FB4>
-__device__ __forceinline__ void gemm64x2(float (&acc1)[4][8], float (&acc2)[4][8], int K, FA4 fa1, FA4b fa2, FB4 fb4,
+__device__ __forceinline__ void gemm64x2(f32x4 (&acc1)[8], f32x4 (&acc2)[8], int K, FA4 fa1, FA4b fa2, FB4 fb4,
                                          float *sA1, float *sA2, float *sB)
 {
     const int t = threadIdx.x;
@@ -939,9 +922,7 @@ __device__ __forceinline__ void gemm64x2(float (&acc1)[4][8], float (&acc2)[4][8
             vb[e] = fb4(k0 + 4 * (idx & 7), idx >> 3);
         }
     };
-    f32x4 d1[8], d2[8];
-    acc_load<8>(d1, acc1);
-    acc_load<8>(d2, acc2);
+    f32x4 (&d1)[8] = acc1, (&d2)[8] = acc2;
     fetch(0);
     for (int k0 = 0; k0 < K; k0 += 32) {
         gemm_stage<8, true, true>(va1, vb, sA1, sB);
@@ -954,16 +935,12 @@ __device__ __forceinline__ void gemm64x2(float (&acc1)[4][8], float (&acc2)[4][8
         gemm_slice<8>(d2, sA2, sB);
         __syncthreads();
     }
-    acc_store<8>(acc1, d1);
-    acc_store<8>(acc2, d2);
 }
 
-__device__ __forceinline__ void zero(float (&acc)[4][8])
+__device__ __forceinline__ void zero(f32x4 (&acc)[8])
 {
 #pragma unroll
-    for (int ri = 0; ri < 4; ++ri)
-#pragma unroll
-        for (int m = 0; m < 8; ++m) acc[ri][m] = 0.f;
+    for (int m = 0; m < 8; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // sum over the 16 lanes of a row group
@@ -1034,10 +1011,10 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (cc == 0 && r < n) dst[r] += sign * (coef ? coef[r] : 1.f) * v;
         }
     };
-    float acc[4][8], dK[4][8];
+    f32x4 acc[8], dK[8];  // [column tile m][row ri]: the accumulator layout
     {
         // ---- dq^ first, so that its registers are free before the rest of dk^ is formed
-        float dQ[4][8];
+        f32x4 dQ[8];
         zero(dQ);
         // (c) O = q_scale (diag(Gam) Q S + ...): E1 = dO' S^T, and (e) Vt = V -
         //     diag(Gam) K S: E2 = dVt S^T, in one pass over S (the second A
@@ -1054,8 +1031,8 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 part[ri] = 0.f;
 #pragma unroll
                 for (int m = 0; m < 8; ++m) {
-                    part[ri] = fmaf(dK[ri][m], KH(r, cc + 16 * m), part[ri]);
-                    dK[ri][m] *= -eg[r];
+                    part[ri] = fmaf(dK[m][ri], KH(r, cc + 16 * m), part[ri]);
+                    dK[m][ri] *= -eg[r];
                 }
             }
             row_apply(part, dgam, eg, -1.f);
@@ -1067,8 +1044,8 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             part[ri] = 0.f;
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
-                dQ[ri][m] += eg[r] * acc[ri][m];
-                part[ri] = fmaf(acc[ri][m], QH(r, cc + 16 * m), part[ri]);
+                dQ[m][ri] += eg[r] * acc[m][ri];
+                part[ri] = fmaf(acc[m][ri], QH(r, cc + 16 * m), part[ri]);
             }
         }
         row_apply(part, dgam, eg, 1.f);
@@ -1081,8 +1058,8 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int m = 0; m < 4; ++m) {
                 const int r = r0 + ri, jj = cc + 16 * m;
                 const bool in = jj <= r && r < n;
-                Em[r * kLN + jj] = in ? acc[ri][m] * ws.P[mo + r * 64 + jj] : 0.f;
-                Wm[r * kLN + jj] = in ? acc[ri][m] * expf(gam[r] - gam[jj]) : 0.f;
+                Em[r * kLN + jj] = in ? acc[m][ri] * ws.P[mo + r * 64 + jj] : 0.f;
+                Wm[r * kLN + jj] = in ? acc[m][ri] * expf(gam[r] - gam[jj]) : 0.f;
             }
         __syncthreads();
         gemm64<8, true, false>(dQ, 64, [&](int r, int jj) { return L4(Wm + r * kLN + jj); }, KH4, sA, sB);
@@ -1091,7 +1068,7 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int r = r0 + ri;
             if (r >= n) continue;
 #pragma unroll
-            for (int m = 0; m < 8; ++m) ws.dqp[((t0 + r) * Hv + h) * kD + cc + 16 * m] = dQ[ri][m];
+            for (int m = 0; m < 8; ++m) ws.dqp[((t0 + r) * Hv + h) * kD + cc + 16 * m] = dQ[m][ri];
         }
     }
     // (d) continued: dk^ += dQK^T q^
@@ -1109,8 +1086,8 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             part[ri] = 0.f;
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
-                dK[ri][m] += en[r] * acc[ri][m];
-                part[ri] = fmaf(acc[ri][m], KH(r, cc + 16 * m), part[ri]);
+                dK[m][ri] += en[r] * acc[m][ri];
+                part[ri] = fmaf(acc[m][ri], KH(r, cc + 16 * m), part[ri]);
             }
         }
 #pragma unroll
@@ -1141,8 +1118,8 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int m = 0; m < 4; ++m) {
             const int r = r0 + ri, jj = cc + 16 * m;
             const bool in = jj <= r && r < n;
-            Ym[r * kLN + jj] = in ? acc[ri][m] * ws.X[mo + r * 64 + jj] : 0.f;
-            Wm[r * kLN + jj] = in ? acc[ri][m] * bet[jj] : 0.f;
+            Ym[r * kLN + jj] = in ? acc[m][ri] * ws.X[mo + r * 64 + jj] : 0.f;
+            Wm[r * kLN + jj] = in ? acc[m][ri] * bet[jj] : 0.f;
         }
     __syncthreads();
     if (t < n) {
@@ -1158,7 +1135,7 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int ri = 0; ri < 4; ++ri)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) Ym[(r0 + ri) * kLN + cc + 16 * m] = acc[ri][m];
+        for (int m = 0; m < 4; ++m) Ym[(r0 + ri) * kLN + cc + 16 * m] = acc[m][ri];
     __syncthreads();
     zero(acc);
     gemm64<4, true, true>(acc, 64, [&](int r, int m) { return L4(Ym + r * kLN + m); },
@@ -1168,7 +1145,7 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int r = r0 + ri, jj = cc + 16 * m;
-            Wm[r * kLN + jj] = (jj < r && r < n) ? -acc[ri][m] : 0.f;
+            Wm[r * kLN + jj] = (jj < r && r < n) ? -acc[m][ri] : 0.f;
         }
     __syncthreads();
     // (h) A = diag(beta) K K^T * D (strict lower): dbeta_i, Em += dA * A, dKK -> Ym;
@@ -1179,7 +1156,7 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int ri = 0; ri < 4; ++ri)
 #pragma unroll
-            for (int m = 0; m < 4; ++m) acc[ri][m] = kkg[(r0 + ri) * 64 + cc + 16 * m];
+            for (int m = 0; m < 4; ++m) acc[m][ri] = kkg[(r0 + ri) * 64 + cc + 16 * m];
     }
     {
         float part[4];
@@ -1193,8 +1170,8 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const float D = expf(gam[r] - gam[jj]);
                 const float dA = Wm[r * kLN + jj];
                 if (in) {
-                    Em[r * kLN + jj] += dA * bet[r] * acc[ri][m] * D;
-                    part[ri] = fmaf(dA, acc[ri][m] * D, part[ri]);
+                    Em[r * kLN + jj] += dA * bet[r] * acc[m][ri] * D;
+                    part[ri] = fmaf(dA, acc[m][ri] * D, part[ri]);
                 }
                 Ym[r * kLN + jj] = in ? dA * bet[r] * D : 0.f;
             }
@@ -1226,7 +1203,7 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int r = r0 + ri;
         if (r >= n) continue;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) ws.dkp[((t0 + r) * Hv + h) * kD + cc + 16 * m] = dK[ri][m];
+        for (int m = 0; m < 8; ++m) ws.dkp[((t0 + r) * Hv + h) * kD + cc + 16 * m] = dK[m][ri];
     }
 }
 
