@@ -79,10 +79,21 @@ size_t gdn_prefill_workspace_size(int B, int T, int Hqk, int Hv, int dk, int dv)
  *   state_out      [B][Hv][dk][dv] fp32 final state; may equal state_in
  *                  (in place), any other overlap is undefined
  *   o              [B][T][Hv][dv] bf16 output (round to nearest even)
- *   workspace      device scratch of >= gdn_prefill_workspace_size(...) bytes,
- *                  16-byte aligned (a misaligned one is rejected with
- *                  GDN_ERR_INVALID_ARGUMENT); its contents on entry are
- *                  irrelevant
+ *   workspace      device scratch, 16-byte aligned (a misaligned one is
+ *                  rejected with GDN_ERR_INVALID_ARGUMENT); its contents on
+ *                  entry are irrelevant.  With gdn_prefill_workspace_size(B,
+ *                  T, ...) bytes or more the call runs at once.  With less,
+ *                  but at least gdn_prefill_workspace_size(B, 64, ...), it
+ *                  runs in windows of Tw tokens of every sequence, Tw the
+ *                  largest multiple of 64 whose workspace fits.  Each window
+ *                  continues the sequences from the state (written to
+ *                  state_out, then updated there in place) and the input rows
+ *                  the previous one left, so the chunk grid is the call's own
+ *                  and the result equals the one-window result up to
+ *                  rounding.  The workspace then stays bounded whatever T is:
+ *                  the explainer (section 3) stresses the mixer's fixed-size
+ *                  state.  With less than one 64-token window's worth it
+ *                  returns GDN_ERR_WORKSPACE_TOO_SMALL, nothing launched.
  * T = 0 copies state_in to state_out (zeros if state_in is NULL).
  */
 int gdn_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -121,10 +132,12 @@ int gdn_prefill_with_events(const uint16_t *q, const uint16_t *k, const uint16_t
  *
  *   - Every other argument is as for gdn_prefill; there is no workspace.
  *   - The array holds gdn_prefill_noalloc_max_workspace() bytes (192 MiB)
- *     on each GPU the library runs on, until the process ends.  A call whose
- *     gdn_prefill_workspace_size(B, T, Hqk, Hv, dk, dv) exceeds it returns
- *     GDN_ERR_WORKSPACE_TOO_SMALL with nothing launched (at 16 QK / 48 V
- *     heads: T up to 8192 for B = 1).
+ *     on each GPU the library runs on, until the process ends.  A call
+ *     longer than the array holds runs in windows, as gdn_prefill does with
+ *     a short workspace (at 16 QK / 48 V heads and B = 1: at once up to
+ *     T = 8192, in windows beyond).  A batch whose 64-token window alone
+ *     exceeds the array returns GDN_ERR_WORKSPACE_TOO_SMALL, nothing
+ *     launched.
  *   - The array of the CURRENT device is used (hipGetDevice), which must be
  *     the device of `stream`.  Its address is looked up with
  *     hipGetSymbolAddress on the first call on each device and kept: this

@@ -133,27 +133,59 @@ static int prefill_common(const uint16_t *q, const uint16_t *k, const uint16_t *
     const int max_chunks = cu_seqlens ? gdn::max_chunks_varlen(N, T_tot)
                                       : gdn::max_chunks_uniform(N, T_uniform);
     const size_t need = gdn::prefill_workspace_bytes(max_chunks, N, Hqk, Hv);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE_TOO_SMALL;
+    // A uniform call whose workspace holds less than the whole call runs in
+    // windows of Tw tokens (a multiple of the chunk), the largest that fits:
+    // each window continues the sequences from the state and rows the
+    // previous one left, so the chunk grid and the result (up to rounding)
+    // are those of one call.
+    int Tw = T_uniform;
+    if (need > 0 && (!workspace || workspace_bytes < need)) {
+        if (cu_seqlens || slots || events || seg_chunks_min > 0 || !workspace) return GDN_ERR_WORKSPACE_TOO_SMALL;
+        int lo = 0, hi = (T_uniform + gdn::kChunk - 1) / gdn::kChunk;  // chunks per window: lo fits, hi does not
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) / 2;
+            if (gdn::prefill_workspace_bytes(gdn::max_chunks_uniform(N, mid * gdn::kChunk), N, Hqk, Hv) <=
+                workspace_bytes)
+                lo = mid;
+            else
+                hi = mid;
+        }
+        if (lo == 0) return GDN_ERR_WORKSPACE_TOO_SMALL;
+        Tw = lo * gdn::kChunk;
+    }
     if (N == 0) return GDN_OK;
 
-    gdn::PrefillArgs p{};
-    p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.conv_w = conv_w;
-    p.conv_state_in = conv_state_in; p.conv_state_out = conv_state_out;
-    p.state_in = state_in; p.state_out = state_out; p.o = o;
-    p.cu_seqlens = cu_seqlens; p.N = N; p.T_uniform = T_uniform; p.T_tot = T_tot;
-    p.Hqk = Hqk; p.Hv = Hv; p.gate_scale = gate_scale; p.q_scale = q_scale;
-    p.max_chunks = max_chunks;
-    p.seg_chunks = gdn::choose_seg_chunks(max_chunks, N, Hv);
-    // a caller's longer segments (fewer of them: the workspace still fits)
-    if (seg_chunks_min > p.seg_chunks) p.seg_chunks = seg_chunks_min;
-    p.max_segs = gdn::max_segments(max_chunks, N, p.seg_chunks);
-    p.defer_final = state_in != nullptr && state_in == state_out;
-    p.defer_conv = conv_state_in != nullptr && conv_state_in == conv_state_out;
-    p.slots = slots;
-    p.n_rows = n_rows;
-    hipError_t e = gdn::launch_prefill(p, workspace, reinterpret_cast<hipStream_t>(stream),
-                                       reinterpret_cast<hipEvent_t const *>(events));
-    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    for (int t_off = 0; t_off < T_uniform || (t_off == 0 && T_uniform == 0); t_off += Tw) {
+        const int len = T_uniform - t_off < Tw ? T_uniform - t_off : Tw;
+        const bool first_w = t_off == 0, last_w = t_off + len >= T_uniform;
+        const int wchunks = cu_seqlens ? max_chunks : gdn::max_chunks_uniform(N, len);
+        gdn::PrefillArgs p{};
+        p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.conv_w = conv_w;
+        // later windows start from the state the previous one wrote, and read
+        // their sequences' earlier rows from the input; only the last writes
+        // the carried rows
+        p.conv_state_in = first_w ? conv_state_in : nullptr;
+        p.conv_state_out = last_w ? conv_state_out : nullptr;
+        p.state_in = first_w ? state_in : state_out;
+        p.state_out = state_out; p.o = o;
+        p.cu_seqlens = cu_seqlens; p.N = N; p.T_uniform = len; p.T_tot = T_tot;
+        p.T_stride = T_uniform; p.t_off = t_off; p.cont = !first_w;
+        p.Hqk = Hqk; p.Hv = Hv; p.gate_scale = gate_scale; p.q_scale = q_scale;
+        p.max_chunks = wchunks;
+        p.seg_chunks = gdn::choose_seg_chunks(wchunks, N, Hv);
+        // a caller's longer segments (fewer of them: the workspace still fits)
+        if (seg_chunks_min > p.seg_chunks) p.seg_chunks = seg_chunks_min;
+        p.max_segs = gdn::max_segments(wchunks, N, p.seg_chunks);
+        p.defer_final = p.state_in != nullptr && p.state_in == state_out;
+        p.defer_conv = p.conv_state_in != nullptr && p.conv_state_in == p.conv_state_out;
+        p.slots = slots;
+        p.n_rows = n_rows;
+        hipError_t e = gdn::launch_prefill(p, workspace, reinterpret_cast<hipStream_t>(stream),
+                                           reinterpret_cast<hipEvent_t const *>(events));
+        if (e != hipSuccess) return GDN_ERR_HIP;
+        if (cu_seqlens || T_uniform == 0) break;
+    }
+    return GDN_OK;
 }
 
 int gdn_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
@@ -228,8 +260,11 @@ int gdn_prefill_noalloc(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     rc = prefill_check(q, k, v, a, b, conv_w, conv_state_in, conv_state_out, state_in, state_out, o, nullptr,
                        B * T);
     if (rc != GDN_OK) return rc;
-    const size_t need = gdn::prefill_workspace_bytes(gdn::max_chunks_uniform(B, T), B, Hqk, Hv);
-    if (need > kScratchBytes) return GDN_ERR_WORKSPACE_TOO_SMALL;
+    // one 64-token window of the batch must fit in the array; longer calls run
+    // in windows (prefill_common)
+    if (gdn::prefill_workspace_bytes(gdn::max_chunks_uniform(B, T < gdn::kChunk ? T : gdn::kChunk), B, Hqk, Hv) >
+        kScratchBytes)
+        return GDN_ERR_WORKSPACE_TOO_SMALL;
     void *ws = nullptr;
     rc = scratch_address(&ws);
     if (rc != GDN_OK) return rc;

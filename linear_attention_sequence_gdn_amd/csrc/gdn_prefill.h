@@ -20,6 +20,11 @@ struct PrefillArgs {
     uint16_t *o;
     const int32_t *cu_seqlens;  // NULL: N sequences of T_uniform tokens
     int N, T_uniform, T_tot;
+    // uniform calls: sequence s's tokens start at s * T_stride + t_off (a
+    // window of T_uniform tokens of longer sequences; T_stride = T_uniform,
+    // t_off = 0 for a whole call); cont: the window continues its sequences,
+    // so the rows before its first chunk are the sequences' own earlier rows
+    int T_stride, t_off, cont;
     int Hqk, Hv;
     float gate_scale, q_scale;
     int max_chunks;

@@ -174,7 +174,7 @@ __device__ __forceinline__ void conv_window_rc(const uint16_t *x, int ldb, int n
 // cannot send any kernel outside the caller's buffers.
 __device__ __forceinline__ int seq_start(const PrefillArgs &p, int s)
 {
-    return p.cu_seqlens ? min(max(p.cu_seqlens[s], 0), p.T_tot) : s * p.T_uniform;
+    return p.cu_seqlens ? min(max(p.cu_seqlens[s], 0), p.T_tot) : s * p.T_stride + p.t_off;
 }
 __device__ __forceinline__ int seq_len(const PrefillArgs &p, int s)
 {
@@ -304,14 +304,15 @@ struct Tables {
     {
         if (p.cu_seqlens) return ws.chunk_info[c];
         const int per = chunks_per_seq(p), s = c / per, j = c % per;
-        return make_int4(s, s * p.T_uniform + j * kChunk, min(kChunk, p.T_uniform - j * kChunk), j == 0);
+        return make_int4(s, s * p.T_stride + p.t_off + j * kChunk, min(kChunk, p.T_uniform - j * kChunk),
+                         j == 0 && !p.cont);
     }
     // {first chunk, chunks, first token, length}
     static __device__ __forceinline__ int4 seq(const PrefillArgs &p, const Workspace &ws, int s)
     {
         if (p.cu_seqlens) return ws.seq_info[s];
         const int per = chunks_per_seq(p);
-        return make_int4(s * per, per, s * p.T_uniform, p.T_uniform);
+        return make_int4(s * per, per, s * p.T_stride + p.t_off, p.T_uniform);
     }
     // {sequence or -1, first chunk, end chunk, 1: first of sequence | 2: last}
     static __device__ __forceinline__ int4 seg(const PrefillArgs &p, const Workspace &ws, int k)
@@ -844,7 +845,7 @@ __device__ __forceinline__ ChainDma chain_dma_plan(const PrefillArgs &p, const W
     const int rel = ((int)c - run.c0) * kChunk;
     const int n = min(kChunk, run.L - rel);
     const int ldb = Hv * kD * 2, ldc = (2 * Hqk * kD + Hv * kD) * 2;
-    const bool first = (int)c == run.c0;
+    const bool first = (int)c == run.c0 && !p.cont;  // a continuation reads its own earlier rows
     uint16_t *vc = const_cast<uint16_t *>(run.v) + (long)rel * (ldb / 2);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(vc, 0, n * ldb, 0x00020000);
     const __amdgpu_buffer_rsrc_t rvh =
@@ -1426,7 +1427,8 @@ constexpr int kReadyPolls = 1 << 20;
 // The carried conv rows of one sequence (pool row `row`), planes [pl0, pl1)
 // of q | k | v for QK head g / V head h, one wave: the last three raw rows,
 // reaching back into the incoming rows when the sequence is shorter than
-// three tokens.  In place, a lane reads each incoming row before it writes
+// three tokens (into the input's earlier rows when the call is a window that
+// continues its sequences).  In place, a lane reads each incoming row before it writes
 // it: row r is written from row r + L (L < 3), which is read first.
 __device__ __forceinline__ void write_conv_rows(const PrefillArgs &p, const int4 &si, int row, int g, int h,
                                                 int pl0, int pl1, int lane)
@@ -1443,7 +1445,7 @@ __device__ __forceinline__ void write_conv_rows(const PrefillArgs &p, const int4
         for (int r = 0; r < 3; ++r) {
             const int tau = Ls - 3 + r;
             uint32_t val = 0;
-            if (tau >= 0)
+            if (tau >= 0 || p.cont)  // a window that continues its sequence has its earlier rows in the input
                 val = ld_pair(src + (long)(t0 + tau) * ld + 2 * lane);
             else if (p.conv_state_in)
                 val = ld_pair(p.conv_state_in + ((long)row * 3 + 3 + tau) * C_tot + ch0 + 2 * lane);

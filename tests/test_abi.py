@@ -213,4 +213,6 @@ def test_noalloc_validation(L):
     assert call(dk=64) == gdn.GDN_ERR_UNSUPPORTED
     assert call(Hv=5) == gdn.GDN_ERR_UNSUPPORTED
     assert call(q=FAKE + 2) == gdn.GDN_ERR_INVALID_ARGUMENT
-    assert call(T=16384, Hqk=16, Hv=48) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL  # beyond the array
+    # a longer call runs in windows; only a batch whose 64-token window alone
+    # exceeds the array is refused
+    assert call(B=64, T=16384, Hqk=16, Hv=48) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL

@@ -480,3 +480,81 @@ def test_conv_rows_in_place_short_sequences(oracle_lib):
                            state_in=dev_f32(x["state_in"]), conv_state_in=cs, conv_state_out=cs)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host_u16(cs), cs_ref)
+
+
+def _prefill_small_workspace(x, T, ws_tokens, in_place=False):
+    """gdn_prefill of N sequences of T tokens with a workspace sized for
+    ws_tokens tokens per sequence, less than the call needs: the library runs
+    the call in windows, carrying the state and the conv rows between them."""
+    import torch
+    import linear_attention_sequence_gdn_amd as gdn
+    N, Hqk, Hv, d = x["N"], x["Hqk"], x["Hv"], x["d"]
+    C_tot = 2 * Hqk * d + Hv * d
+    need = gdn.gdn_prefill_workspace_size(N, T, Hqk, Hv)
+    ws = torch.empty(gdn.gdn_prefill_workspace_size(N, ws_tokens, Hqk, Hv), dtype=torch.uint8, device="cuda")
+    assert ws.numel() < need
+    st = dev_f32(x["state_in"])
+    cs = dev_bf16(x["conv_state_in"])
+    so = st if in_place else None
+    cso = cs if in_place else torch.zeros((N, 3, C_tot), dtype=torch.bfloat16, device="cuda")
+    o, so, cso = gdn.gdn_prefill(dev_bf16(x["q"].reshape(N, T, Hqk, d)), dev_bf16(x["k"].reshape(N, T, Hqk, d)),
+                                 dev_bf16(x["v"].reshape(N, T, Hv, d)), dev_f32(x["a"].reshape(N, T, Hv)),
+                                 dev_f32(x["b"].reshape(N, T, Hv)), dev_bf16(x["conv_w"]),
+                                 gate_scale=x["gate_scale"], state_in=st, conv_state_in=cs, state_out=so,
+                                 conv_state_out=cso, workspace=ws)
+    torch.cuda.synchronize()
+    return o.reshape(N * T, Hv, d), so, cso
+
+
+@pytest.mark.parametrize("T,ws_tokens", [(700, 192), (194, 64), (130, 64)])
+def test_windowed_prefill_against_oracle(oracle_lib, T, ws_tokens):
+    """A workspace smaller than the call's: the call runs in windows of whole
+    chunks (the last one 2 tokens long in the second and third cases, whose
+    carried conv rows reach back into the previous window's rows), and
+    matches the oracle and the one-window call."""
+    x = inputs.make_prefill(T_list=[T, T], Hqk=2, Hv=6, seed=811 + T, state_std=0.05, conv_state_std=1.0)
+    o, so, cso = _prefill_small_workspace(x, T, ws_tokens)
+    og, sg = compare(x, o, so, cso, label=f"windowed T={T} (windows of {ws_tokens})")
+    o1, s1, cs1 = gpu_prefill(x, uniform_T=T)
+    assert rel_l2(og, host_bf16(o1)) < 1e-3
+    assert rel_l2(sg, s1.cpu().numpy()) < 1e-4
+    np.testing.assert_array_equal(host_u16(cso), host_u16(cs1))
+
+
+def test_windowed_prefill_in_place(oracle_lib):
+    """Windows with the state and the conv rows updated in place."""
+    T = 450
+    x = inputs.make_prefill(T_list=[T, T, T], Hqk=2, Hv=6, seed=823, state_std=0.05, conv_state_std=1.0)
+    o, so, cso = _prefill_small_workspace(x, T, 128, in_place=True)
+    compare(x, o, so, cso)
+
+
+def test_noalloc_beyond_its_array_runs_in_windows(oracle_lib):
+    """gdn_prefill_noalloc on a layer longer than its array holds (16 QK / 48
+    V heads, T = 16,384): the oracle on V heads 0, 23 and 47, and the plain
+    call with a whole workspace on all heads."""
+    import torch
+    import linear_attention_sequence_gdn_amd as gdn
+    T, Hqk, Hv, d = 16384, 16, 48, 128
+    assert gdn.gdn_prefill_workspace_size(1, T, Hqk, Hv) > gdn.gdn_prefill_noalloc_max_workspace()
+    x = inputs.make_prefill(T_list=[T], Hqk=Hqk, Hv=Hv, seed=829, state_std=0.05, conv_state_std=1.0)
+    args = (dev_bf16(x["q"].reshape(1, T, Hqk, d)), dev_bf16(x["k"].reshape(1, T, Hqk, d)),
+            dev_bf16(x["v"].reshape(1, T, Hv, d)), dev_f32(x["a"].reshape(1, T, Hv)),
+            dev_f32(x["b"].reshape(1, T, Hv)), dev_bf16(x["conv_w"]))
+    kw = dict(gate_scale=x["gate_scale"], state_in=dev_f32(x["state_in"]), conv_state_in=dev_bf16(x["conv_state_in"]))
+    C_tot = 2 * Hqk * d + Hv * d
+    cso = torch.zeros((1, 3, C_tot), dtype=torch.bfloat16, device="cuda")
+    o, so, cso = gdn.gdn_prefill_noalloc(*args, conv_state_out=cso, **kw)
+    torch.cuda.synchronize()
+    o1, s1, cs1 = gdn.gdn_prefill(*args, conv_state_out=torch.zeros_like(cso), **kw)
+    torch.cuda.synchronize()
+    og, sg = host_bf16(o.reshape(T, Hv, d)), so.cpu().numpy()
+    assert rel_l2(og, host_bf16(o1.reshape(T, Hv, d))) < 1e-3
+    assert rel_l2(sg, s1.cpu().numpy()) < 1e-4
+    np.testing.assert_array_equal(host_u16(cso), host_u16(cs1))
+    del o1
+    torch.cuda.empty_cache()
+    # the carried rows are checked against the whole call above (the oracle
+    # fills only the selected heads)
+    compare(x, o.reshape(T, Hv, d), so, None, heads=[0, 23, 47],
+            label="noalloc in windows, T=16384 (V heads 0, 23, 47)")

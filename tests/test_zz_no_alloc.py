@@ -68,11 +68,15 @@ def test_noalloc_equals_workspace_call_twice():
 
 
 def test_noalloc_rejects_oversize_before_launch():
+    """A call longer than the array holds runs in windows; a batch whose
+    first 64-token window alone exceeds the array is refused before anything
+    is launched (the pointers here are not device memory, so a launch would
+    fault)."""
     import linear_attention_sequence_gdn_amd as gdn
     L = gdn.lib()
-    T = 16384  # needs more than the array holds at 16 QK / 48 V heads
-    assert gdn.gdn_prefill_workspace_size(1, T, 16, 48) > gdn.gdn_prefill_noalloc_max_workspace()
+    B, T = 64, 16384
+    assert gdn.gdn_prefill_workspace_size(B, 64, 16, 48) > gdn.gdn_prefill_noalloc_max_workspace()
     fake = ctypes.c_void_p(0x10000)
     rc = L.gdn_prefill_noalloc(fake, fake, fake, fake, fake, fake, None, None, None, fake, fake,
-                               1, T, 16, 48, 128, 128, 0.1, 1.0, None)
+                               B, T, 16, 48, 128, 128, 0.1, 1.0, None)
     assert rc == gdn.GDN_ERR_WORKSPACE_TOO_SMALL
