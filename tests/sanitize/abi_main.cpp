@@ -86,7 +86,9 @@ int main()
                               128, 0.1f, 1.f, F, 1 << 30, nullptr), GDN_ERR_INVALID_ARGUMENT);
     EXPECT(gdn_prefill_varlen(u, u, u, f, f, u, nullptr, nullptr, nullptr, fo, uo, cu, -1, 100, 2, 6, 128, 128,
                               0.1f, 1.f, F, 1 << 30, nullptr), GDN_ERR_INVALID_ARGUMENT);
-    EXPECT(gdn_prefill_noalloc(u, u, u, f, f, u, nullptr, nullptr, nullptr, fo, uo, 1, 16384, 16, 48, 128, 128,
+    // a batch whose first 64-token window alone exceeds the array (longer
+    // calls with smaller batches run in windows)
+    EXPECT(gdn_prefill_noalloc(u, u, u, f, f, u, nullptr, nullptr, nullptr, fo, uo, 64, 16384, 16, 48, 128, 128,
                                0.1f, 1.f, nullptr), GDN_ERR_WORKSPACE_TOO_SMALL);
     EXPECT(gdn_prefill_noalloc(nullptr, u, u, f, f, u, nullptr, nullptr, nullptr, fo, uo, 1, 64, 2, 6, 128, 128,
                                0.1f, 1.f, nullptr), GDN_ERR_INVALID_ARGUMENT);
