@@ -716,9 +716,32 @@ def bench_config(hip, idx, settle_ms, steps):
     flop = method_flops(lengths, Hqk, Hv)
     names = {0: "tiny_prefill_T512_2qk_6v", 2: "native_context_prefill_T262144_16qk_48v",
              4: "varlen_prefill_64seq_16qk_48v"}
-    return {"workload": names[idx], "tokens": int(T_tot), "sequences": int(N), "ms_per_call": ms, "calls": k,
-            "tokens_per_s": T_tot / (ms * 1e-3), "algorithmic_flop": flop,
-            "mfma_frac": flop / (ms * 1e-3) / PEAK_MFMA_F16}
+    out = {"workload": names[idx], "tokens": int(T_tot), "sequences": int(N), "ms_per_call": ms, "calls": k,
+           "tokens_per_s": T_tot / (ms * 1e-3), "algorithmic_flop": flop,
+           "mfma_frac": flop / (ms * 1e-3) / PEAK_MFMA_F16}
+    if uniform and need > gdn.gdn_prefill_noalloc_max_workspace():
+        # the same call with its workspace bounded to the no-alloc array's
+        # size: the library runs it in windows of whole chunks
+        bound = gdn.gdn_prefill_noalloc_max_workspace()
+        ws_b = ws[:bound]
+        # the window the library picks: the largest whole-chunk window whose
+        # workspace fits beside the two state buffers it hands states through
+        sb = (N * Hv * D * D * 4 + 255) // 256 * 256
+        tw = 64
+        while tw + 64 <= T and gdn.gdn_prefill_workspace_size(N, tw + 64, Hqk, Hv) <= (bound - 2 * sb) // 256 * 256:
+            tw += 64
+        run_b = lambda: fn(*args, gate_scale=gs, state_in=st, state_out=so, o=o, workspace=ws_b)
+        run_b()
+        kb = max(3, k // 2)
+        hip.record(t0, sp)
+        for _ in range(kb):
+            run_b()
+        hip.record(t1, sp)
+        torch.cuda.synchronize()
+        msb = hip.ms(t0, t1) / kb
+        out["bounded_workspace"] = {"workspace_bytes": bound, "window_tokens": tw, "windows": -(-T // tw),
+                                    "ms_per_call": msb, "tokens_per_s": T_tot / (msb * 1e-3)}
+    return out
 
 
 def bench_segments(hip, settle_ms, steps):

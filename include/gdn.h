@@ -86,9 +86,10 @@ size_t gdn_prefill_workspace_size(int B, int T, int Hqk, int Hv, int dk, int dv)
  *                  but at least gdn_prefill_workspace_size(B, 64, ...), it
  *                  runs in windows of Tw tokens of every sequence, Tw the
  *                  largest multiple of 64 whose workspace fits.  Each window
- *                  continues the sequences from the state (written to
- *                  state_out, then updated there in place) and the input rows
- *                  the previous one left, so the chunk grid is the call's own
+ *                  continues the sequences from the state (handed over in
+ *                  two state buffers at the workspace's end, or, when they
+ *                  do not fit, in state_out in place) and the input rows the
+ *                  previous one left, so the chunk grid is the call's own
  *                  and the result equals the one-window result up to
  *                  rounding.  The workspace then stays bounded whatever T is:
  *                  the explainer (section 3) stresses the mixer's fixed-size

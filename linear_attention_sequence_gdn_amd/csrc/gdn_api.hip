@@ -139,16 +139,34 @@ static int prefill_common(const uint16_t *q, const uint16_t *k, const uint16_t *
     // previous one left, so the chunk grid and the result (up to rounding)
     // are those of one call.
     int Tw = T_uniform;
+    float *ping[2] = {nullptr, nullptr};  // the states handed from window to window
     if (need > 0 && (!workspace || workspace_bytes < need)) {
         if (cu_seqlens || slots || events || seg_chunks_min > 0 || !workspace) return GDN_ERR_WORKSPACE_TOO_SMALL;
-        int lo = 0, hi = (T_uniform + gdn::kChunk - 1) / gdn::kChunk;  // chunks per window: lo fits, hi does not
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) / 2;
-            if (gdn::prefill_workspace_bytes(gdn::max_chunks_uniform(N, mid * gdn::kChunk), N, Hqk, Hv) <=
-                workspace_bytes)
-                lo = mid;
-            else
-                hi = mid;
+        // chunks per window whose workspace fits in `budget`: lo fits, hi does not
+        auto window_chunks = [&](size_t budget) {
+            int lo = 0, hi = (T_uniform + gdn::kChunk - 1) / gdn::kChunk;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) / 2;
+                if (gdn::prefill_workspace_bytes(gdn::max_chunks_uniform(N, mid * gdn::kChunk), N, Hqk, Hv) <= budget)
+                    lo = mid;
+                else
+                    hi = mid;
+            }
+            return lo;
+        };
+        // preferably with two state buffers at the workspace's end, so that no
+        // window updates a state in place (which routes every final state
+        // through the sequential pass's in-order walk); else in place in state_out
+        const size_t sbytes = (size_t)N * Hv * gdn::kStateFloats * sizeof(float);
+        const size_t tail = 2 * ((sbytes + 255) & ~(size_t)255);
+        int lo = 0;
+        if (workspace_bytes > tail) lo = window_chunks((workspace_bytes - tail) & ~(size_t)255);
+        if (lo > 0) {
+            uint8_t *base = static_cast<uint8_t *>(workspace) + (((workspace_bytes - tail) & ~(size_t)255));
+            ping[0] = reinterpret_cast<float *>(base);
+            ping[1] = reinterpret_cast<float *>(base + tail / 2);
+        } else {
+            lo = window_chunks(workspace_bytes);
         }
         if (lo == 0) return GDN_ERR_WORKSPACE_TOO_SMALL;
         Tw = lo * gdn::kChunk;
@@ -166,8 +184,15 @@ static int prefill_common(const uint16_t *q, const uint16_t *k, const uint16_t *
         // the carried rows
         p.conv_state_in = first_w ? conv_state_in : nullptr;
         p.conv_state_out = last_w ? conv_state_out : nullptr;
-        p.state_in = first_w ? state_in : state_out;
-        p.state_out = state_out; p.o = o;
+        const int w_idx = t_off / (Tw > 0 ? Tw : 1);
+        if (ping[0]) {
+            p.state_in = first_w ? state_in : ping[(w_idx - 1) & 1];
+            p.state_out = last_w ? state_out : ping[w_idx & 1];
+        } else {
+            p.state_in = first_w ? state_in : state_out;
+            p.state_out = state_out;
+        }
+        p.o = o;
         p.cu_seqlens = cu_seqlens; p.N = N; p.T_uniform = len; p.T_tot = T_tot;
         p.T_stride = T_uniform; p.t_off = t_off; p.cont = !first_w;
         p.Hqk = Hqk; p.Hv = Hv; p.gate_scale = gate_scale; p.q_scale = q_scale;
@@ -176,7 +201,7 @@ static int prefill_common(const uint16_t *q, const uint16_t *k, const uint16_t *
         // a caller's longer segments (fewer of them: the workspace still fits)
         if (seg_chunks_min > p.seg_chunks) p.seg_chunks = seg_chunks_min;
         p.max_segs = gdn::max_segments(wchunks, N, p.seg_chunks);
-        p.defer_final = p.state_in != nullptr && p.state_in == state_out;
+        p.defer_final = p.state_in != nullptr && p.state_in == p.state_out;
         p.defer_conv = p.conv_state_in != nullptr && p.conv_state_in == p.conv_state_out;
         p.slots = slots;
         p.n_rows = n_rows;
