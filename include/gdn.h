@@ -58,7 +58,8 @@ enum gdn_status {
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *gdn_status_string(int status);
 
-/* Bytes of device workspace gdn_prefill needs for these sizes. */
+/* Bytes of device workspace gdn_prefill needs to run these sizes at once
+ * (with less, down to the size for T = 64, it runs in windows). */
 size_t gdn_prefill_workspace_size(int B, int T, int Hqk, int Hv, int dk, int dv);
 
 /*
