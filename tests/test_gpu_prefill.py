@@ -482,7 +482,7 @@ def test_conv_rows_in_place_short_sequences(oracle_lib):
     np.testing.assert_array_equal(host_u16(cs), cs_ref)
 
 
-def _prefill_small_workspace(x, T, ws_tokens, in_place=False):
+def _prefill_small_workspace(x, T, ws_tokens, in_place=False, carries=True):
     """gdn_prefill of N sequences of T tokens with a workspace sized for
     ws_tokens tokens per sequence, less than the call needs: the library runs
     the call in windows, carrying the state and the conv rows between them."""
@@ -493,8 +493,8 @@ def _prefill_small_workspace(x, T, ws_tokens, in_place=False):
     need = gdn.gdn_prefill_workspace_size(N, T, Hqk, Hv)
     ws = torch.empty(gdn.gdn_prefill_workspace_size(N, ws_tokens, Hqk, Hv), dtype=torch.uint8, device="cuda")
     assert ws.numel() < need
-    st = dev_f32(x["state_in"])
-    cs = dev_bf16(x["conv_state_in"])
+    st = dev_f32(x["state_in"]) if carries else None
+    cs = dev_bf16(x["conv_state_in"]) if carries else None
     so = st if in_place else None
     cso = cs if in_place else torch.zeros((N, 3, C_tot), dtype=torch.bfloat16, device="cuda")
     o, so, cso = gdn.gdn_prefill(dev_bf16(x["q"].reshape(N, T, Hqk, d)), dev_bf16(x["k"].reshape(N, T, Hqk, d)),
@@ -558,3 +558,14 @@ def test_noalloc_beyond_its_array_runs_in_windows(oracle_lib):
     # fills only the selected heads)
     compare(x, o.reshape(T, Hv, d), so, None, heads=[0, 23, 47],
             label="noalloc in windows, T=16384 (V heads 0, 23, 47)")
+
+
+def test_windowed_prefill_without_carries(oracle_lib):
+    """Windows of a call with no initial state and no carried conv rows (the
+    first window starts from zeros, the later ones from the handed-over
+    state)."""
+    T = 333
+    x = inputs.make_prefill(T_list=[T], Hqk=2, Hv=6, seed=837)
+    assert x["state_in"] is None and x["conv_state_in"] is None
+    o, so, cso = _prefill_small_workspace(x, T, 64, carries=False)
+    compare(x, o, so, cso, label="windowed T=333 (windows of 64), no carries")
