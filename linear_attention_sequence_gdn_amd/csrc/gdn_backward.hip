@@ -38,6 +38,8 @@
 // The state columns are independent in the update, so the two sequential
 // passes split them over four workgroups per (sequence, V head); the twelve
 // workgroups of one (sequence, QK group) run on one XCD and share its L2.
+// Long sequences are further cut into segments, run in parallel, each after
+// a warm-up whose decay bounds what its zero start drops.
 #include "../../include/gdn.h"
 
 #include <hip/hip_runtime.h>
@@ -71,6 +73,7 @@ struct BwdArgs {
     int T_tot, max_chunks;      // all tokens; chunk slots
     int Hqk, Hv;
     float gate_scale, q_scale;
+    int nseg;                   // workgroups (segments) per sequence in the two sequential passes
 };
 
 // Workspace (fp32).  tok = s*T + t; rows of a chunk beyond its length are
@@ -95,14 +98,16 @@ struct BwdWs {
 
 __device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + expf(-x)); }
 
-// Sequential-pass block id -> (sequence, V head, column block), so that the
-// G * kNCB blocks of one (sequence, QK group), which read the same k^ and q^
-// rows chunk after chunk, get ids of one residue mod 8: they run on the same
-// XCD (blocks are dealt to the eight XCDs round-robin) and share its L2.  A
-// tail of fewer than eight groups maps plainly.
-__device__ __forceinline__ void seq_block(const BwdArgs &p, int b, int &s, int &h, int &cb)
+// Sequential-pass block id -> (segment, sequence, V head, column block), so
+// that the G * kNCB blocks of one (segment, sequence, QK group), which read
+// the same k^ and q^ rows chunk after chunk, get ids of one residue mod 8:
+// they run on the same XCD (blocks are dealt to the eight XCDs round-robin)
+// and share its L2.  A tail of fewer than eight groups maps plainly.
+__device__ __forceinline__ void seq_block(const BwdArgs &p, int &seg, int &s, int &h, int &cb)
 {
-    const int G = p.Hv / p.Hqk, P = G * kNCB, N = gridDim.x;
+    const int G = p.Hv / p.Hqk, P = G * kNCB, N = gridDim.x / p.nseg;
+    const int b = blockIdx.x % N;
+    seg = blockIdx.x / N;
     const int full = N / (8 * P) * (8 * P);
     int unit, member;
     if (b < full) {
@@ -132,6 +137,110 @@ __device__ __forceinline__ int4 bseq(const BwdArgs &p, const BwdWs &ws, int s)
     if (p.cu_seqlens) return ws.seq_info[s];
     return make_int4(s * p.nc, p.nc, s * p.T, p.T);
 }
+// Segments of the two sequential passes.  A sequence of nch chunks is cut
+// into ns <= p.nseg segments, each run by its own workgroups, in parallel.
+// Segment 0 (the first chunks in the forward pass, the last ones in the
+// state-gradient pass) starts from the given state or state gradient and is
+// kBwdLead chunks longer; every other segment starts from zero a few chunks
+// before its own (its warm-up, which stores nothing).  Each token's
+// transition alpha (I - beta k k^T), and so its transpose, has spectral norm
+// <= alpha (beta in (0,1), |k| = 1), so what a zero start drops reaches the
+// segment scaled by at most the product of the warm-up chunks' decays.  The
+// warm-up is the shortest one whose product is <= 2^-24, below fp32
+// resolution of what it drops.  When a segment finds none within 64 chunks
+// (weak or no decay), segment 0 runs the whole sequence and the others exit.
+constexpr int kBwdLead = 4, kBwdMinSeg = 8, kBwdMaxSeg = 8;
+constexpr float kBwdWarmLn = -16.6355323f;  // ln 2^-24
+
+__device__ __forceinline__ int seg_count(const BwdArgs &p, int nch)
+{
+    return min(p.nseg, max(1, (nch - kBwdLead) / kBwdMinSeg));
+}
+// first chunk of segment k counted from the pass's start (k = ns: nch)
+__device__ __forceinline__ int seg_bound(int nch, int ns, int k)
+{
+    if (k == 0) return 0;
+    if (k >= ns) return nch;
+    const int L = (nch - kBwdLead + ns - 1) / ns;
+    return min(nch, kBwdLead + k * L);
+}
+// natural log of chunk c's decay: gamma at its last token
+__device__ __forceinline__ float chunk_logdecay(const BwdArgs &p, const BwdWs &ws, int4 sq, int c, int h)
+{
+    const int n = min(kChunk, sq.w - c * kChunk);
+    return ws.gam[((long)sq.z + (long)c * kChunk + n - 1) * p.Hv + h];
+}
+// Warm-up start of a segment.  kRev = false: the segment starts at chunk e,
+// and the pass runs forward from the chunk returned (0: from the sequence
+// start, exactly).  kRev = true: the segment ends before chunk e, and the
+// pass runs backward from the chunk returned (nch - 1: from the sequence
+// end, exactly).  -1: no warm-up within 64 chunks meets the bound.
+// Wave-uniform.
+template <bool kRev>
+__device__ int seg_warm_start(const BwdArgs &p, const BwdWs &ws, int4 sq, int h, int e, int lane)
+{
+    const int nch = sq.y;
+    const int c = kRev ? e + lane : e - 1 - lane;
+    const bool in = kRev ? c < nch : c >= 0;
+    float g = in ? chunk_logdecay(p, ws, sq, c, h) : 0.f;
+    // inclusive prefix over lanes: log of the decay of the lane + 1 chunks next to the segment
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(g, off, 64);
+        if (lane >= off) g += y;
+    }
+    const unsigned long long hit = __ballot(in && g <= kBwdWarmLn);
+    int w;
+    if (kRev) w = hit ? e + (int)__builtin_ctzll(hit) : (nch - e <= 64 ? nch - 1 : -1);
+    else w = hit ? e - 1 - (int)__builtin_ctzll(hit) : (e <= 64 ? 0 : -1);
+    return __builtin_amdgcn_readfirstlane(w);
+}
+// A workgroup's chunks: its own [lo, hi), which it stores, and j0, where its
+// pass starts (kRev: going down), from the given state or state gradient
+// when `exact`, else from zero.  false: nothing to do.
+struct SegPlan {
+    int lo, hi, j0;
+    bool exact;
+};
+template <bool kRev>
+__device__ bool seg_plan(const BwdArgs &p, const BwdWs &ws, int4 sq, int h, int seg, SegPlan &pl)
+{
+    __shared__ int wstart[kBwdMaxSeg];
+    const int nch = sq.y, ns = seg_count(p, nch);
+    if (seg >= ns) return false;
+    if (ns > 1) {
+        // wave k tests segment k; every workgroup of the sequence decides alike
+        const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        if (w >= 1 && w < ns) {
+            const int e = kRev ? nch - seg_bound(nch, ns, w) : seg_bound(nch, ns, w);
+            const int st = seg_warm_start<kRev>(p, ws, sq, h, e, lane);
+            if (lane == 0) wstart[w] = st;
+        }
+        __syncthreads();
+        bool ok = true;
+        for (int k = 1; k < ns; ++k) ok = ok && wstart[k] >= 0;
+        if (!ok) {
+            if (seg > 0) return false;
+            pl.lo = 0;
+            pl.hi = nch;
+            pl.j0 = kRev ? nch - 1 : 0;
+            pl.exact = true;
+            return true;
+        }
+    }
+    const int a = seg_bound(nch, ns, seg), b = seg_bound(nch, ns, seg + 1);
+    pl.lo = kRev ? nch - b : a;
+    pl.hi = kRev ? nch - a : b;
+    if (seg == 0) {
+        pl.j0 = kRev ? nch - 1 : 0;
+        pl.exact = true;
+    } else {
+        pl.j0 = wstart[seg];
+        pl.exact = pl.j0 == (kRev ? nch - 1 : 0);
+    }
+    return true;
+}
+
 __device__ __forceinline__ float silu_grad(float y)
 {
     const float s = sigm(y);
@@ -593,38 +702,44 @@ __global__ __launch_bounds__(kST) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
     __shared__ SeqTile L;
     __shared__ __attribute__((aligned(16))) float Ss[kD * kLC], Vs[64 * kLC], Vts[64 * kLC], Vns[64 * kLC];
     const int Hv = p.Hv, G = Hv / p.Hqk;
-    int s, h, cb;
-    seq_block(p, blockIdx.x, s, h, cb);
+    int seg, s, h, cb;
+    seq_block(p, seg, s, h, cb);
     const int g = h / G, col0 = cb * kCB;
     const int t = threadIdx.x, w = t >> 6, lane = t & 63, lr = lane & 15, lq = lane >> 4;
     const int srow = 16 * w + 4 * lq;                      // state rows srow .. srow + 3
     const int vrt = w >> 1, vrow = 16 * vrt + 4 * lq, vcol = 16 * (w & 1) + lr;  // slice tile
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    const int4 sq = bseq(p, ws, s);  // {first chunk slot, chunks, first token, length}
+    SegPlan pl;
+    if (!seg_plan<false>(p, ws, sq, h, seg, pl)) return;
     f32x4 S[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            S[ct][e] = p.state_in ? p.state_in[(((long)s * Hv + h) * kD + srow + e) * kD + col0 + 16 * ct + lr] : 0.f;
-    const int4 sq = bseq(p, ws, s);  // {first chunk slot, chunks, first token, length}
-    const int nch = sq.y;
+            S[ct][e] = pl.exact && p.state_in
+                           ? p.state_in[(((long)s * Hv + h) * kD + srow + e) * kD + col0 + 16 * ct + lr]
+                           : 0.f;
     SeqPref<false> f;
-    if (nch > 0) {
-        seq_fetch<false>(p, ws, f, sq.x, sq.z, min(kChunk, sq.w), h, g, col0);
+    if (pl.j0 < pl.hi) {
+        seq_fetch<false>(p, ws, f, sq.x + pl.j0, sq.z + (long)pl.j0 * kChunk, min(kChunk, sq.w - pl.j0 * kChunk),
+                         h, g, col0);
         seq_commit<false>(p, f, L, nullptr, nullptr, Vs);
     }
-    for (int j = 0; j < nch; ++j) {
+    for (int j = pl.j0; j < pl.hi; ++j) {
         const int cidx = sq.x + j, n = min(kChunk, sq.w - j * kChunk);
         const long t0 = (long)sq.z + (long)j * kChunk;
+        const bool own = j >= pl.lo;  // else a warm-up chunk: nothing stored
         float *sc = ws.Sc + ((long)cidx * Hv + h) * kD * kD + col0;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                sc[(long)(srow + e) * kD + 16 * ct + lr] = S[ct][e];
+                if (own) sc[(long)(srow + e) * kD + 16 * ct + lr] = S[ct][e];
                 Ss[(srow + e) * kLC + 16 * ct + lr] = S[ct][e];
             }
-        if (j + 1 < nch) seq_fetch<false>(p, ws, f, cidx + 1, t0 + kChunk, min(kChunk, sq.w - (j + 1) * kChunk), h, g, col0);
+        if (j + 1 < pl.hi)
+            seq_fetch<false>(p, ws, f, cidx + 1, t0 + kChunk, min(kChunk, sq.w - (j + 1) * kChunk), h, g, col0);
         __syncthreads();
         // Vt = V - diag(Gam) K S
         f32x4 acc = z4;
@@ -636,7 +751,7 @@ __global__ __launch_bounds__(kST) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
             const int r = vrow + e;
             const float vt = r < n ? Vs[r * kLC + vcol] - L.eg[r] * acc[e] : 0.f;
             Vts[r * kLC + vcol] = vt;
-            if (r < n) ws.vt[((t0 + r) * Hv + h) * kD + col0 + vcol] = vt;
+            if (own && r < n) ws.vt[((t0 + r) * Hv + h) * kD + col0 + vcol] = vt;
         }
         __syncthreads();
         // Vn = X diag(beta) Vt (X lower: k < 16 (vrt + 1))
@@ -650,7 +765,7 @@ __global__ __launch_bounds__(kST) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
             const int r = vrow + e;
             const float vn = r < n ? acc[e] : 0.f;
             Vns[r * kLC + vcol] = vn;
-            if (r < n) ws.vn[((t0 + r) * Hv + h) * kD + col0 + vcol] = vn;
+            if (own && r < n) ws.vn[((t0 + r) * Hv + h) * kD + col0 + vcol] = vn;
         }
         __syncthreads();
         // S <- Gam_n S + Ks^T Vn
@@ -667,7 +782,7 @@ __global__ __launch_bounds__(kST) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
             for (int ct = 0; ct < 2; ++ct) S[ct] = mfma4(a, Vns[k * kLC + 16 * ct + lr], S[ct]);
         }
         __syncthreads();
-        if (j + 1 < nch) seq_commit<false>(p, f, L, nullptr, nullptr, Vs);
+        if (j + 1 < pl.hi) seq_commit<false>(p, f, L, nullptr, nullptr, Vs);
     }
 }
 
@@ -680,22 +795,24 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
     __shared__ __attribute__((aligned(16))) float Qs[64 * kLK], Ps[64 * kLN];
     __shared__ __attribute__((aligned(16))) float dSs[kD * kLC], dOs[64 * kLC], dVns[64 * kLC], dVts[64 * kLC];
     const int Hv = p.Hv, G = Hv / p.Hqk;
-    int s, h, cb;
-    seq_block(p, blockIdx.x, s, h, cb);
+    int seg, s, h, cb;
+    seq_block(p, seg, s, h, cb);
     const int g = h / G, col0 = cb * kCB;
     const int t = threadIdx.x, w = t >> 6, lane = t & 63, lr = lane & 15, lq = lane >> 4;
     const int srow = 16 * w + 4 * lq;
     const int vrt = w >> 1, vrow = 16 * vrt + 4 * lq, vcol = 16 * (w & 1) + lr;
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
     const long so = ((long)s * Hv + h) * kD * kD + col0;
+    const int4 sq = bseq(p, ws, s);  // {first chunk slot, chunks, first token, length}
+    SegPlan pl;
+    if (!seg_plan<true>(p, ws, sq, h, seg, pl)) return;
     f32x4 dS[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            dS[ct][e] = p.grad_state_out ? p.grad_state_out[so + (long)(srow + e) * kD + 16 * ct + lr] : 0.f;
-    const int4 sq = bseq(p, ws, s);  // {first chunk slot, chunks, first token, length}
-    const int nch = sq.y;
+            dS[ct][e] = pl.exact && p.grad_state_out ? p.grad_state_out[so + (long)(srow + e) * kD + 16 * ct + lr]
+                                                     : 0.f;
     SeqPref<true> f;
     // this block's columns of the state entering a chunk, loaded one chunk
     // ahead, for <dS', S> (the gate gradient's Gam_n S term)
@@ -707,29 +824,30 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
 #pragma unroll
             for (int e = 0; e < 4; ++e) sv[4 * ct + e] = sc[(long)(srow + e) * kD + 16 * ct + lr];
     };
-    if (nch > 0) {
-        load_sv(sq.x + nch - 1);
-        seq_fetch<true>(p, ws, f, sq.x + nch - 1, sq.z + (long)(nch - 1) * kChunk, sq.w - (nch - 1) * kChunk, h, g,
-                        col0);
+    if (pl.j0 >= pl.lo) {
+        load_sv(sq.x + pl.j0);
+        seq_fetch<true>(p, ws, f, sq.x + pl.j0, sq.z + (long)pl.j0 * kChunk, min(kChunk, sq.w - pl.j0 * kChunk), h,
+                        g, col0);
         seq_commit<true>(p, f, L, Qs, Ps, dOs);
     }
-    for (int j = nch - 1; j >= 0; --j) {
+    for (int j = pl.j0; j >= pl.lo; --j) {
         const int cidx = sq.x + j, n = min(kChunk, sq.w - j * kChunk);
         const long t0 = (long)sq.z + (long)j * kChunk;
+        const bool own = j < pl.hi;  // else a warm-up chunk: nothing stored
         float *dsc = ws.dSc + ((long)cidx * Hv + h) * kD * kD + col0;
         float part = 0.f;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                dsc[(long)(srow + e) * kD + 16 * ct + lr] = dS[ct][e];
+                if (own) dsc[(long)(srow + e) * kD + 16 * ct + lr] = dS[ct][e];
                 dSs[(srow + e) * kLC + 16 * ct + lr] = dS[ct][e];
                 part = fmaf(dS[ct][e], sv[4 * ct + e], part);
             }
         part = wave_sum(part);
-        if (lane == 0) ws.sdot[((long)cidx * Hv + h) * kSD + (kST / 64) * cb + w] = part;
-        if (j > 0) load_sv(cidx - 1);
-        if (j > 0) seq_fetch<true>(p, ws, f, cidx - 1, t0 - kChunk, kChunk, h, g, col0);
+        if (own && lane == 0) ws.sdot[((long)cidx * Hv + h) * kSD + (kST / 64) * cb + w] = part;
+        if (j > pl.lo) load_sv(cidx - 1);
+        if (j > pl.lo) seq_fetch<true>(p, ws, f, cidx - 1, t0 - kChunk, kChunk, h, g, col0);
         __syncthreads();
         // dVn = diag(en) K dS' + P^T dO'  (P^T upper: k >= 16 vrt)
         f32x4 acc = z4;
@@ -747,7 +865,7 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
             const int r = vrow + e;
             const float v = r < n ? acc[e] : 0.f;
             dVns[r * kLC + vcol] = v;
-            if (r < n) ws.dvn[((t0 + r) * Hv + h) * kD + col0 + vcol] = v;
+            if (own && r < n) ws.dvn[((t0 + r) * Hv + h) * kD + col0 + vcol] = v;
         }
         __syncthreads();
         // dVt = T'^T dVn = diag(beta) X^T dVn
@@ -761,7 +879,7 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
             const int r = vrow + e;
             const float v = r < n ? L.bet[r] * acc[e] : 0.f;
             dVts[r * kLC + vcol] = v;
-            if (r < n) ws.dvh[((t0 + r) * Hv + h) * kD + col0 + vcol] = v;
+            if (own && r < n) ws.dvh[((t0 + r) * Hv + h) * kD + col0 + vcol] = v;
         }
         __syncthreads();
         // dS <- Gam_n dS' + (Gam Q)^T dO' - (Gam K)^T dVt
@@ -781,9 +899,9 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
             }
         }
         __syncthreads();
-        if (j > 0) seq_commit<true>(p, f, L, Qs, Ps, dOs);
+        if (j > pl.lo) seq_commit<true>(p, f, L, Qs, Ps, dOs);
     }
-    if (p.grad_state_in) {
+    if (p.grad_state_in && pl.lo == 0) {
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
@@ -1445,6 +1563,32 @@ int bwd_max_chunks(const int32_t *cu_seqlens, int N, int T_tot)
     return N == 0 ? 0 : N * ((T_tot / N + kChunk - 1) / kChunk);
 }
 
+// Segments per sequence of the two sequential passes, from a makespan model
+// for sequences of the mean length: blocks = units x segments, run in rounds
+// of 256 resident blocks (one per CU), each round as long as a segment plus
+// its warm-up (taken as kBwdLead chunks; segment 0, that much longer, has
+// none).  The cheapest cut wins; ties go to fewer segments.
+int bwd_choose_nseg(int N, int T_tot, int Hv)
+{
+    constexpr long kSlots = 256;
+    if (N <= 0 || T_tot <= 0) return 1;
+    const int nch = (int)(((long)T_tot / N + kChunk - 1) / kChunk);
+    const long units = (long)N * Hv * kNCB;
+    long best_cost = -1;
+    int best = 1;
+    for (int ns = 1; ns <= kBwdMaxSeg; ++ns) {
+        if (ns > 1 && (nch - kBwdLead) / kBwdMinSeg < ns) break;
+        const long L = ns == 1 ? nch : (nch - kBwdLead + ns - 1) / ns;
+        const long rounds = (units * ns + kSlots - 1) / kSlots;
+        const long cost = rounds * (L + (ns > 1 ? kBwdLead : 0));
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best = ns;
+        }
+    }
+    return best;
+}
+
 }  // namespace
 
 size_t backward_workspace_bytes(int N, int T_tot, bool packed, int Hqk, int Hv)
@@ -1472,6 +1616,7 @@ hipError_t launch_backward(const uint16_t *q, const uint16_t *k, const uint16_t 
     p.cu_seqlens = cu_seqlens; p.N = N; p.T = T; p.nc = (T + kChunk - 1) / kChunk;
     p.T_tot = T_tot; p.max_chunks = T_tot > 0 ? bwd_max_chunks(cu_seqlens, N, T_tot) : 0;
     p.Hqk = Hqk; p.Hv = Hv; p.gate_scale = gate_scale; p.q_scale = q_scale;
+    p.nseg = bwd_choose_nseg(N, T_tot, Hv);
     const long C_tot = 2L * Hqk * kD + (long)Hv * kD;
     BwdWs ws{};
     if (T_tot > 0) {
@@ -1492,10 +1637,10 @@ hipError_t launch_backward(const uint16_t *q, const uint16_t *k, const uint16_t 
         if (p.cu_seqlens) hipLaunchKernelGGL(bwd_setup_kernel, dim3(1), dim3(1024), 0, stream, p, ws);
         hipLaunchKernelGGL(bwd_prep_kernel, dim3(chunks, planes), dim3(kBT), 0, stream, p, ws);
         hipLaunchKernelGGL(bwd_local_kernel, dim3(chunks * Hqk), dim3(kBT), 0, stream, p, ws);
-        hipLaunchKernelGGL(bwd_fwd_kernel, dim3(N * Hv * kNCB), dim3(kST), 0, stream, p, ws);
+        hipLaunchKernelGGL(bwd_fwd_kernel, dim3(N * Hv * kNCB * p.nseg), dim3(kST), 0, stream, p, ws);
     }
     // also with no tokens: the state gradient passes straight through
-    hipLaunchKernelGGL(bwd_chain_kernel, dim3(N * Hv * kNCB), dim3(kST), 0, stream, p, ws);
+    hipLaunchKernelGGL(bwd_chain_kernel, dim3(N * Hv * kNCB * p.nseg), dim3(kST), 0, stream, p, ws);
     if (grad_conv_state_in && (chunks == 0 || p.cu_seqlens)) {
         // rows of sequences without a first chunk (empty ones) stay zero
         const long nh = (long)N * 3 * C_tot;

@@ -233,6 +233,41 @@ def test_backward_no_decay(oracle_lib):
     _compare(_gpu(inp, g_o, g_S, qs, 1, 300), _oracle(oracle_lib, inp, g_o, g_S, qs), 1, 300, "no decay")
 
 
+def test_backward_segments(oracle_lib):
+    # 47 chunks at 1 QK / 2 V heads: the two sequential passes cut the
+    # sequence into three segments run in parallel; the later ones start from
+    # zero after a warm-up of a few chunks whose decay bounds what they drop
+    inp, g_o, g_S, qs = _case(1, 3000, 1, 2, seed=101)
+    _compare(_gpu(inp, g_o, g_S, qs, 1, 3000), _oracle(oracle_lib, inp, g_o, g_S, qs), 1, 3000, "segments")
+
+
+def test_backward_segments_exact_starts(oracle_lib):
+    # weak decay: no warm-up meets its bound, but every segment has the
+    # sequence's end within 64 chunks, so each runs from the given state (or
+    # state gradient) itself
+    inp, g_o, g_S, qs = _case(1, 3000, 1, 2, seed=102, gate_scale=0.002)
+    _compare(_gpu(inp, g_o, g_S, qs, 1, 3000), _oracle(oracle_lib, inp, g_o, g_S, qs), 1, 3000,
+             "segments, exact starts")
+
+
+def test_backward_segments_fall_back(oracle_lib):
+    # 141 chunks: V head 0 has no decay, so its later segments find no warm-up
+    # within reach and its first segment runs the whole sequence; V head 1
+    # decays and stays cut
+    inp, g_o, g_S, qs = _case(1, 9000, 1, 2, seed=103)
+    inp["a"][:, 0] = -30.0
+    _compare(_gpu(inp, g_o, g_S, qs, 1, 9000), _oracle(oracle_lib, inp, g_o, g_S, qs), 1, 9000,
+             "segments, one head whole")
+
+
+def test_backward_varlen_segments(oracle_lib):
+    # packed: the two long sequences are cut into segments, the short one is not
+    lens = [3000, 70, 2500]
+    inp, g_o, g_S, qs = _varlen_case(lens, 1, 2, seed=104)
+    _compare(_gpu_varlen(inp, g_o, g_S, qs), _oracle(oracle_lib, inp, g_o, g_S, qs), 1, inp["T_tot"],
+             "varlen segments")
+
+
 def test_backward_ignores_stale_workspace():
     # a workspace full of NaN bit patterns (as a previous call or another user
     # may leave it) gives the same gradients bit for bit: every region is
