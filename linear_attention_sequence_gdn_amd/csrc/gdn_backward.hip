@@ -54,7 +54,12 @@ constexpr int kBT = 256;  // threads of every backward workgroup
 constexpr int kCB = 32;   // state columns per workgroup of the sequential passes
 constexpr int kLK = 132;  // LDS row stride of 64 x 128 fp32 tiles (16-byte rows, 4-bank skew)
 constexpr int kLN = 68;   // LDS row stride of 64 x 64 fp32 tiles
-constexpr int kLC = kCB;  // LDS row stride of kCB-column slices (read as broadcasts)
+constexpr int kLC = kCB;  // LDS row stride of kCB-column slices
+// Element (k, c) of a kCB-column slice in LDS.  The sequential passes read
+// slices at rows k = 4 kb + lq, lane group lq = 0..3, 16 columns per group:
+// rows of one parity share a half of the 64 banks, so the 16-column halves
+// of rows 4 kb + 2, 4 kb + 3 are swapped to keep the four groups apart.
+__device__ __forceinline__ int sl(int k, int c) { return k * kLC + (c ^ (((k >> 1) & 1) << 4)); }
 constexpr int kNCB = kD / kCB;
 constexpr int kST = 512;  // threads of a sequential-pass workgroup: eight waves, two per SIMD
 constexpr int kSD = kNCB * (kST / 64);  // <dS', S> partials per (chunk, V head): one per wave
@@ -670,10 +675,10 @@ __device__ __forceinline__ void seq_commit(const BwdArgs &p, const SeqPref<kChai
         const int idx = t + kST * e, r = idx / Q, q = idx % Q;
         if constexpr (kChain) {
             const uint2 u = f.o[e];
-            st4(slice + r * kLC + 4 * q, make_float4(p.q_scale * bf16_lo(u.x), p.q_scale * bf16_hi(u.x),
+            st4(slice + sl(r, 4 * q), make_float4(p.q_scale * bf16_lo(u.x), p.q_scale * bf16_hi(u.x),
                                                      p.q_scale * bf16_lo(u.y), p.q_scale * bf16_hi(u.y)));
         } else {
-            st4(slice + r * kLC + 4 * q, f.v[e]);
+            st4(slice + sl(r, 4 * q), f.v[e]);
         }
     }
     if (t < 64) {
@@ -736,7 +741,7 @@ __global__ __launch_bounds__(kST) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 if (own) sc[(long)(srow + e) * kD + 16 * ct + lr] = S[ct][e];
-                Ss[(srow + e) * kLC + 16 * ct + lr] = S[ct][e];
+                Ss[sl(srow + e, 16 * ct + lr)] = S[ct][e];
             }
         if (j + 1 < pl.hi)
             seq_fetch<false>(p, ws, f, cidx + 1, t0 + kChunk, min(kChunk, sq.w - (j + 1) * kChunk), h, g, col0);
@@ -745,12 +750,12 @@ __global__ __launch_bounds__(kST) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
         f32x4 acc = z4;
 #pragma unroll 8
         for (int kb = 0; kb < kD / 4; ++kb)
-            acc = mfma4(L.K[(16 * vrt + lr) * kLK + 4 * kb + lq], Ss[(4 * kb + lq) * kLC + vcol], acc);
+            acc = mfma4(L.K[(16 * vrt + lr) * kLK + 4 * kb + lq], Ss[sl(4 * kb + lq, vcol)], acc);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = vrow + e;
-            const float vt = r < n ? Vs[r * kLC + vcol] - L.eg[r] * acc[e] : 0.f;
-            Vts[r * kLC + vcol] = vt;
+            const float vt = r < n ? Vs[sl(r, vcol)] - L.eg[r] * acc[e] : 0.f;
+            Vts[sl(r, vcol)] = vt;
             if (own && r < n) ws.vt[((t0 + r) * Hv + h) * kD + col0 + vcol] = vt;
         }
         __syncthreads();
@@ -758,13 +763,13 @@ __global__ __launch_bounds__(kST) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
         acc = z4;
         for (int kb = 0; kb < 4 * vrt + 4; ++kb) {
             const int k = 4 * kb + lq;
-            acc = mfma4(L.X[(16 * vrt + lr) * kLN + k] * L.bet[k], Vts[k * kLC + vcol], acc);
+            acc = mfma4(L.X[(16 * vrt + lr) * kLN + k] * L.bet[k], Vts[sl(k, vcol)], acc);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = vrow + e;
             const float vn = r < n ? acc[e] : 0.f;
-            Vns[r * kLC + vcol] = vn;
+            Vns[sl(r, vcol)] = vn;
             if (own && r < n) ws.vn[((t0 + r) * Hv + h) * kD + col0 + vcol] = vn;
         }
         __syncthreads();
@@ -779,7 +784,7 @@ __global__ __launch_bounds__(kST) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
             const int k = 4 * kb + lq;
             const float a = L.en[k] * L.K[k * kLK + 16 * w + lr];
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) S[ct] = mfma4(a, Vns[k * kLC + 16 * ct + lr], S[ct]);
+            for (int ct = 0; ct < 2; ++ct) S[ct] = mfma4(a, Vns[sl(k, 16 * ct + lr)], S[ct]);
         }
         __syncthreads();
         if (j + 1 < pl.hi) seq_commit<false>(p, f, L, nullptr, nullptr, Vs);
@@ -841,7 +846,7 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 if (own) dsc[(long)(srow + e) * kD + 16 * ct + lr] = dS[ct][e];
-                dSs[(srow + e) * kLC + 16 * ct + lr] = dS[ct][e];
+                dSs[sl(srow + e, 16 * ct + lr)] = dS[ct][e];
                 part = fmaf(dS[ct][e], sv[4 * ct + e], part);
             }
         part = wave_sum(part);
@@ -853,18 +858,18 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
         f32x4 acc = z4;
 #pragma unroll 8
         for (int kb = 0; kb < kD / 4; ++kb)
-            acc = mfma4(L.K[(16 * vrt + lr) * kLK + 4 * kb + lq], dSs[(4 * kb + lq) * kLC + vcol], acc);
+            acc = mfma4(L.K[(16 * vrt + lr) * kLK + 4 * kb + lq], dSs[sl(4 * kb + lq, vcol)], acc);
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] *= L.en[vrow + e];
         for (int kb = 4 * vrt; kb < 16; ++kb) {
             const int k = 4 * kb + lq;
-            acc = mfma4(Ps[k * kLN + 16 * vrt + lr], dOs[k * kLC + vcol], acc);
+            acc = mfma4(Ps[k * kLN + 16 * vrt + lr], dOs[sl(k, vcol)], acc);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = vrow + e;
             const float v = r < n ? acc[e] : 0.f;
-            dVns[r * kLC + vcol] = v;
+            dVns[sl(r, vcol)] = v;
             if (own && r < n) ws.dvn[((t0 + r) * Hv + h) * kD + col0 + vcol] = v;
         }
         __syncthreads();
@@ -872,13 +877,13 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
         acc = z4;
         for (int kb = 4 * vrt; kb < 16; ++kb) {
             const int k = 4 * kb + lq;
-            acc = mfma4(L.X[k * kLN + 16 * vrt + lr], dVns[k * kLC + vcol], acc);
+            acc = mfma4(L.X[k * kLN + 16 * vrt + lr], dVns[sl(k, vcol)], acc);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = vrow + e;
             const float v = r < n ? L.bet[r] * acc[e] : 0.f;
-            dVts[r * kLC + vcol] = v;
+            dVts[sl(r, vcol)] = v;
             if (own && r < n) ws.dvh[((t0 + r) * Hv + h) * kD + col0 + vcol] = v;
         }
         __syncthreads();
@@ -894,8 +899,8 @@ __global__ __launch_bounds__(kST) void bwd_chain_kernel(BwdArgs p, BwdWs ws)
             const float aq = L.eg[k] * Qs[k * kLK + 16 * w + lr], ak = -L.eg[k] * L.K[k * kLK + 16 * w + lr];
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
-                dS[ct] = mfma4(aq, dOs[k * kLC + 16 * ct + lr], dS[ct]);
-                dS[ct] = mfma4(ak, dVts[k * kLC + 16 * ct + lr], dS[ct]);
+                dS[ct] = mfma4(aq, dOs[sl(k, 16 * ct + lr)], dS[ct]);
+                dS[ct] = mfma4(ak, dVts[sl(k, 16 * ct + lr)], dS[ct]);
             }
         }
         __syncthreads();
