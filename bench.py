@@ -286,7 +286,7 @@ COPY_BYTES = 256 << 20
 TRAFFIC_KERNELS = {"prefill_chain": "chain_kernel", "prefill_prep": "prep_kernel",
                    "prefill_setup": "setup_kernel", "decode": "decode_persist_kernel",
                    "decode_conv_shift": "conv_shift_qk_kernel<1>",
-                   "decode_multi": "decode_head_kernel<4>", "decode_multi_conv_shift": "conv_shift_qk_kernel<4>"}
+                   "decode_multi": "decode_tokens_kernel<4>", "decode_multi_conv_shift": "conv_shift_qk_kernel<4>"}
 BWD_KERNELS = ("bwd_prep_kernel", "bwd_local_kernel", "bwd_fwd_kernel", "bwd_chain_kernel", "bwd_grad_kernel",
                "bwd_dy_kernel", "bwd_conv_kernel", "bwd_dw_kernel")
 TRAFFIC_KERNELS.update({"backward_" + k_[4:-7]: k_ for k_ in BWD_KERNELS})
@@ -618,7 +618,7 @@ def bench_decode_multi(hip, settle_ms, T=4, steps=32):
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"metric": f"multi-token decode (B=256, T={T} tokens per sequence per call, 16QK/48V)",
             "us_per_call": us, "us_per_token_step": us / T, "tokens_per_s": B * T / (us * 1e-6),
-            "roofline": {"bound": "hbm", "kernel": "decode_head_kernel<4> + conv_shift_qk_kernel<4>",
+            "roofline": {"bound": "hbm", "kernel": "decode_tokens_kernel<4> + conv_shift_qk_kernel<4>",
                          "achieved": gbs, "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": gbs * 1e9 / PEAK_HBM,
                          "traffic": _sum_or_none(load_traffic("decode_multi", source_digest()),
                                                  load_traffic("decode_multi_conv_shift", source_digest())),

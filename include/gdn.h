@@ -269,8 +269,11 @@ int gdn_decode_step(const uint16_t *q, const uint16_t *k, const uint16_t *v,
  * 4); the architecture deep dive (alwayszhang.cn, section 7) describes the MTP
  * head and its use for speculative decoding.  The slot table addresses the
  * state and conv caches of a serving engine (walkthrough, sections 3 and 6:
- * prefix caching keeps those caches across requests).  Same computation as T
- * successive calls of gdn_decode_step.
+ * prefix caching keeps those caches across requests).  The same result as T
+ * successive calls of gdn_decode_step up to fp32 rounding: for T >= 2 the
+ * tokens are taken from one pass over the state (the one-token update
+ * unrolled over the T tokens), so its sums run in another order; T = 1 is
+ * gdn_decode_step's own computation.
  *
  *   q, k        [B][T][Hqk][dk] bf16 raw;  v [B][T][Hv][dv] bf16 raw
  *   a, b        [B][T][Hv] fp32

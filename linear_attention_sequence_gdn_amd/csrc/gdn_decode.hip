@@ -1,6 +1,5 @@
 // gdn_decode.hip -- decode steps of the GDN mixer on gfx950: T = 1..4 new
-// tokens for each of B sequences, the state read once, advanced token by
-// token in registers and written once.
+// tokens for each of B sequences, the state read once and written once.
 //
 // The work is streaming every (sequence, V head) state once from HBM and once
 // back (64 KiB each way per head at d = 128), with a few hundred flops per
@@ -11,7 +10,8 @@
 // token, with p = alpha S^T k^ and u = beta (v^ - p):
 //     S' = alpha S + k^ u^T,      o = S'^T q^ = alpha S^T q^ + u (k^ . q^)
 // so both reductions over the d_k rows (S^T k^ and S^T q^) come from one pass
-// over the old state, and the new state follows in the same pass.
+// over the old state, and the new state follows in the same pass.  Several
+// tokens unroll the same way (decode_tokens_kernel).
 //
 // Sequences may address their state and conv rows through a slot table (a
 // serving engine's state cache): sequence b then reads and writes row
@@ -61,21 +61,41 @@ __device__ __forceinline__ void conv_tokens(const uint16_t (&win)[3 + TM], const
     }
 }
 
-// One workgroup per (sequence b, V head h), so that each streams a single
-// 64 KiB state (many short workgroups keep more of HBM busy than a few long
-// ones).  q^ and k^ of the head's QK group are computed by each of the group's
-// workgroups from the conv rows as they were before the step, which stay
-// untouched here; only the workgroup's own v channels are shifted in place,
-// and conv_shift_qk_kernel shifts the q and k rows afterwards (same stream).
-// TM: tokens the kernel is built for (the step has T <= TM)
+// T = 2..4 tokens per sequence in one pass over the state, on the fp32
+// matrix cores.  With S_0 the state before the step, A_i the product of the
+// decays of tokens 0..i and r_ji that of tokens j+1..i, the one-token update
+// unrolls (the chunk form of the local-inference walkthrough, section 2.1,
+// for one chunk of T tokens) to
+//   alpha_i S_{i-1}^T k_i = A_i S_0^T k_i + sum_{j<i}  r_ji (k_j . k_i) u_j
+//   u_i = beta_i (v_i - alpha_i S_{i-1}^T k_i)
+//   o_i = S_i^T q_i       = A_i S_0^T q_i + sum_{j<=i} r_ji (k_j . q_i) u_j
+//   S_{T-1} = A_{T-1} S_0 + sum_j r_j,T-1 k_j u_j^T
+// so one product [k_0..k_3 q_0..q_3]^T S_0 gives all that the tokens need of
+// the old state, the tokens themselves need only a few scalars per state
+// column, and the new state is S_0 scaled plus one rank-T product.  Wave w
+// holds rows 64 (w / 2) + 4 s + lq (s < 16) of columns 64 (w % 2) + 4 lr ..
+// + 3, lane = 16 lq + lr, as one 16-byte piece per s.  Element e of piece s
+// is the B operand of step s of a 16x16x4 product over the wave's rows for
+// the columns 64 (w % 2) + 4 c + e, c < 16; and pieces 4 tt .. 4 tt + 3 hold,
+// element e, the accumulator tile of rows 64 (w / 2) + 16 tt + 4 i + q
+// (tile row 4 q + i) of those columns, which the rank-T product updates in
+// place.  So the state is loaded and stored in 256-byte runs and is never
+// exchanged between lanes.  One workgroup per (sequence, V head): q^ and k^
+// of the head's QK group come from the conv rows as they were before the
+// step, which stay untouched here; only the workgroup's own v channels are
+// shifted in place, and conv_shift_qk_kernel shifts the q and k rows
+// afterwards (same stream).
 template <int TM>
-__global__ __launch_bounds__(kThreads) void decode_head_kernel(DecodeArgs p)
+__global__ __launch_bounds__(kThreads) void decode_tokens_kernel(DecodeArgs p)
 {
-    __shared__ float s_q[TM][kD], s_k[TM][kD], s_v[TM][kD];
+    constexpr int kXS = kD + 4;     // s_x row stride: the A reads of a step hit distinct banks
+    __shared__ float s_x[8][kXS];   // k^_0..k^_3, q^_0..q^_3 (zero beyond T)
+    __shared__ float s_v[TM][kD];
     __shared__ float s_red[TM][4];
     __shared__ float s_ab[TM][2];
-    __shared__ float s_kq[TM];
-    __shared__ f32x4 s_part[2][2][8][32];  // [buffer][k^/q^ partial][row group][col group]
+    __shared__ float s_g[2][4][4];  // k^_j . k^_i and k^_j . q^_i
+    __shared__ float s_P[2][8][kD]; // [row half][x][column]: the halves of x^T S_0
+    __shared__ float s_u[4][kD];    // r_j,T-1 u_j (zero beyond T)
 
     const int t = threadIdx.x;
     const int h = blockIdx.x % p.Hv;
@@ -83,19 +103,17 @@ __global__ __launch_bounds__(kThreads) void decode_head_kernel(DecodeArgs p)
     const int row = pool_row(p, b);
     if (row < 0) return;  // slot out of range: the sequence is skipped
     const int g = h / (p.Hv / p.Hqk);
-    const int T = TM == 1 ? 1 : p.T;
+    const int T = p.T;
     const long C_tot = 2L * p.Hqk * kD + (long)p.Hv * kD;
-    const int lane = t & 63, wave = t >> 6;
+    const int lane = t & 63, wave = t >> 6, lq = lane >> 4, lr = lane & 15;
+    const int r0 = 64 * (wave >> 1), c0 = 64 * (wave & 1);
 
-    // the state is requested first, so that its latency covers the prologue:
-    // thread owns columns 4cg..4cg+3, rows rg + 8i
-    const int cg = t & 31, rg = t >> 5;
-    const long head0 = ((long)row * p.Hv + h) * kD * kD;
-    const f32x4 *src = reinterpret_cast<const f32x4 *>(p.state_in + head0) + rg * 32 + cg;
-    f32x4 *dst = reinterpret_cast<f32x4 *>(p.state_out + head0) + rg * 32 + cg;
+    // the state first, so that its latency covers the prologue
+    const long piece0 = ((long)row * p.Hv + h) * kD * kD + (long)(r0 + lq) * kD + c0 + 4 * lr;
     f32x4 st[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) st[i] = __builtin_nontemporal_load(src + i * 256);
+    for (int s = 0; s < 16; ++s)
+        st[s] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p.state_in + piece0 + 4L * s * kD));
 
     // ---- prologue: q_g (threads 0..127) and k_g (128..255) from read-only
     //      conv rows; v_h (threads 0..127) with its in-place shift; the gates
@@ -117,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void decode_head_kernel(DecodeArgs p)
         for (int i = 0; i < TM; ++i) {
             const float ss = wave_sum(z[i] * z[i]);
             if (lane == 0) s_red[i][wave] = ss;
-            if (isq) s_q[i][ch] = z[i]; else s_k[i][ch] = z[i];
+            s_x[(isq ? 4 : 0) + i][ch] = z[i];
         }
         if (isq) {
             const long cv = 2L * p.Hqk * kD + (long)h * kD + ch;
@@ -147,54 +165,99 @@ __global__ __launch_bounds__(kThreads) void decode_head_kernel(DecodeArgs p)
     if (t < kD) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            s_q[i][t] *= rsqrtf(s_red[i][0] + s_red[i][1] + 1e-6f);
-            s_k[i][t] *= rsqrtf(s_red[i][2] + s_red[i][3] + 1e-6f);
+            s_x[4 + i][t] *= rsqrtf(s_red[i][0] + s_red[i][1] + 1e-6f);
+            s_x[i][t] *= rsqrtf(s_red[i][2] + s_red[i][3] + 1e-6f);
         }
     }
     __syncthreads();
-    if (wave < T) {
-        float kq = s_k[wave][lane] * s_q[wave][lane] + s_k[wave][lane + 64] * s_q[wave][lane + 64];
-        kq = wave_sum(kq);
-        if (lane == 0) s_kq[wave] = kq;
+    // the Gram scalars k^_j . k^_i and k^_j . q^_i, eight lanes each
+    {
+        const int pr = t >> 3, part = t & 7, kind = pr >> 4, j = (pr >> 2) & 3, i = pr & 3;
+        const float *xa = s_x[j], *xb = s_x[4 * kind + i];
+        float acc = 0.f;
+#pragma unroll
+        for (int n = 0; n < 16; ++n) acc += xa[part + 8 * n] * xb[part + 8 * n];
+        acc += __shfl_xor(acc, 1, 64);
+        acc += __shfl_xor(acc, 2, 64);
+        acc += __shfl_xor(acc, 4, 64);
+        if (part == 0) s_g[kind][j][i] = acc;
     }
-
-    // ---- the tokens in order, the state in registers
-    for (int i = 0; i < T; ++i) {
-        f32x4 pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
+    // x^T S_0 over the wave's 64 rows: lane (lq, lr) supplies x_lr (lr < 8)
+    // at row r0 + 4 s + lq and the state at that row, column c0 + 4 lr + e;
+    // it receives x_(4 lq + i) . S_0[rows][c0 + 4 lr + e] as element i of D[e]
+    f32x4 D[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float kr = s_k[i][rg + 8 * r], qr = s_q[i][rg + 8 * r];
-            pk += st[r] * kr;
-            pq += st[r] * qr;
-        }
-        // (the same summation order as the single-token build)
-        s_part[i & 1][0][rg][cg] = pk;
-        s_part[i & 1][1][rg][cg] = pq;
-        __syncthreads();
-        f32x4 PK = {0.f, 0.f, 0.f, 0.f}, PQ = {0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 4; ++e) D[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            PK += s_part[i & 1][0][r][cg];
-            PQ += s_part[i & 1][1][r][cg];
+    for (int s = 0; s < 16; ++s) {
+        const float xa = lr < 8 ? s_x[lr][r0 + 4 * s + lq] : 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) D[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, st[s][e], D[e], 0, 0, 0);
+    }
+    if (lq < 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s_P[wave >> 1][4 * lq + i][c0 + 4 * lr + e] = D[e][i];
+    }
+    __syncthreads();
+    // ---- the tokens in order, one state column per thread
+    float al[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) al[i] = i < T ? s_ab[i][0] : 1.f;
+    if (t < kD) {
+        float u[TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            u[i] = 0.f;
+            if (i >= T) continue;
+            float A = al[0];
+#pragma unroll
+            for (int l = 1; l <= i; ++l) A *= al[l];
+            float c = A * (s_P[0][i][t] + s_P[1][i][t]);
+            float o = A * (s_P[0][4 + i][t] + s_P[1][4 + i][t]);
+#pragma unroll
+            for (int j = 0; j < i; ++j) {
+                float r = 1.f;
+#pragma unroll
+                for (int l = j + 1; l <= i; ++l) r *= al[l];
+                c += r * s_g[0][j][i] * u[j];
+                o += r * s_g[1][j][i] * u[j];
+            }
+            u[i] = s_ab[i][1] * (s_v[i][t] - c);
+            o += s_g[1][i][i] * u[i];
+            p.o[(((long)b * T + i) * p.Hv + h) * kD + t] = (uint16_t)f32_to_bf16(o * p.q_scale);
         }
-        const float al = s_ab[i][0], be = s_ab[i][1], kq = s_kq[i];
-        f32x4 u, ov;
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+            float r = 1.f;
+#pragma unroll
+            for (int l = j + 1; l < TM; ++l) r *= al[l];
+            s_u[j][t] = r * u[j];
+        }
+    }
+    __syncthreads();
+    // ---- S' = A_(T-1) S_0 + sum_j r_j,T-1 k_j u_j^T, tile by tile in place
+    float AT = al[0];
+#pragma unroll
+    for (int l = 1; l < TM; ++l) AT *= al[l];
+    float ub[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ub[e] = s_u[lq][c0 + 4 * lr + e];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        const float ka = s_x[lq][r0 + 16 * tt + 4 * (lr & 3) + (lr >> 2)];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            u[e] = be * (s_v[i][4 * cg + e] - al * PK[e]);
-            ov[e] = (al * PQ[e] + u[e] * kq) * p.q_scale;
-        }
+            f32x4 c = {st[4 * tt][e] * AT, st[4 * tt + 1][e] * AT, st[4 * tt + 2][e] * AT, st[4 * tt + 3][e] * AT};
+            c = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, ub[e], c, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) st[r] = st[r] * al + u * s_k[i][rg + 8 * r];
-        if (rg == 0) {
-            uint2 packed;
-            packed.x = pack_bf16x2(ov[0], ov[1]);
-            packed.y = pack_bf16x2(ov[2], ov[3]);
-            *reinterpret_cast<uint2 *>(p.o + (((long)b * T + i) * p.Hv + h) * kD + 4 * cg) = packed;
+            for (int i = 0; i < 4; ++i) st[4 * tt + i][e] = c[i];
         }
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) __builtin_nontemporal_store(st[r], dst + r * 256);
+    for (int s = 0; s < 16; ++s)
+        __builtin_nontemporal_store(st[s], reinterpret_cast<f32x4 *>(p.state_out + piece0 + 4L * s * kD));
 }
 
 // One token per sequence: a persistent workgroup walks the (sequence, V head)
@@ -202,9 +265,7 @@ __global__ __launch_bounds__(kThreads) void decode_head_kernel(DecodeArgs p)
 // state into a second set of registers while it works on the current one, so
 // that state loads stay in flight through the prologue and the update (a
 // one-item workgroup leaves HBM idle while it computes).  Two workgroups per
-// CU.  The arithmetic is decode_head_kernel's for one token, operation for
-// operation, so a T-token call of that kernel equals T calls of this one bit
-// for bit.
+// CU.
 __device__ __forceinline__ void decode_one(const DecodeArgs &p, int item, int row, f32x4 (&st)[16],
                                            f32x4 (&sn)[16], int next_item, int next_row, float *s_q, float *s_k,
                                            float *s_v, float *s_red, float *s_ab, float *s_kq,
@@ -354,7 +415,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_persist_kernel(DecodeArgs 
     }
 }
 
-// The in-place shift of the q and k conv rows, after decode_head_kernel has
+// The in-place shift of the q and k conv rows, after the decode kernel has
 // read them: the last three of (r0, r1, r2, x_0 .. x_{T-1}) become the rows,
 // two channels per thread.
 template <int TM>
@@ -407,7 +468,7 @@ hipError_t launch_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v
         const unsigned pg = (unsigned)(grid < 2L * cus ? grid : 2L * cus);
         hipLaunchKernelGGL(decode_persist_kernel, dim3(pg), dim3(kThreads), 0, stream, p);
     } else {
-        hipLaunchKernelGGL(decode_head_kernel<kMaxDecodeTokens>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL(decode_tokens_kernel<kMaxDecodeTokens>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -98,8 +98,14 @@ def _multi_inputs(B, T, Hqk, Hv, seed):
 
 
 @pytest.mark.parametrize("T", [1, 2, 3, 4])
-def test_decode_multi_equals_single_steps(T):
-    """T tokens in one call give bit for bit what T single steps give."""
+def test_decode_multi_matches_single_steps(T):
+    """T tokens in one call against T single steps.  One call takes all T
+    tokens from one pass over the state (the sums over the state's rows run
+    once, in another order than T single steps run them), so for T >= 2 the
+    two agree to fp32 rounding: the state within 1e-6 relative L2 and 1e-5 of
+    (|s| + RMS) per element, the bf16 output within one bf16 rounding step
+    (2^-7 relative) of each element.  T = 1 runs the single-step kernel and
+    must agree bit for bit; the conv rows are copies and agree bit for bit."""
     import torch
     import linear_attention_sequence_gdn_amd as gdn
     B, Hqk, Hv = 5, 2, 6
@@ -110,9 +116,18 @@ def test_decode_multi_equals_single_steps(T):
     o, so = gdn.gdn_decode_multi(dev_bf16(m["q"]), dev_bf16(m["k"]), dev_bf16(m["v"]), dev_f32(m["a"]),
                                  dev_f32(m["b"]), dev_bf16(x["conv_w"]), conv, st, gate_scale=x["gate_scale"])
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(host_bf16(o), np.swapaxes(o1, 0, 1))
-    np.testing.assert_array_equal(so.cpu().numpy(), s1)
+    got_o, ref_o = host_bf16(o).astype(np.float64), np.swapaxes(o1, 0, 1).astype(np.float64)
+    got_s, ref_s = so.cpu().numpy().astype(np.float64), s1.astype(np.float64)
     np.testing.assert_array_equal(host_u16(conv), c1)
+    if T == 1:
+        np.testing.assert_array_equal(got_o, ref_o)
+        np.testing.assert_array_equal(got_s, ref_s)
+        return
+    assert np.linalg.norm(got_s - ref_s) <= 1e-6 * np.linalg.norm(ref_s)
+    rms = np.sqrt(np.mean(ref_s ** 2))
+    assert np.max(np.abs(got_s - ref_s) / (np.abs(ref_s) + rms)) <= 1e-5
+    o_rms = np.sqrt(np.mean(ref_o ** 2))
+    assert np.all(np.abs(got_o - ref_o) <= 2.0 ** -7 * np.abs(ref_o) + 1e-6 * o_rms)
 
 
 def test_decode_multi_against_oracle(oracle_lib):
