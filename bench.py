@@ -363,25 +363,33 @@ def counter_report(out_md, dbs, command=""):
       the fraction of the kernel's time the matrix cores are busy.
       GRBM_GUI_ACTIVE reads the sum over the 8 XCDs, so one XCD's active
       cycles are a eighth of it.
-    * matrix-core FLOP = 512 per MOP (SQ_INSTS_VALU_MFMA_MOPS_*).
+    * matrix-core FLOP = 512 per MOP (SQ_INSTS_VALU_MFMA_MOPS_*); dense peaks
+      per CU-cycle: 4096 fp16/bf16, 256 fp32.
     * LDS: instructions, bank-conflict cycles per CU as a fraction of the
       active cycles, and the share of wave cycles spent waiting to issue an
       LDS instruction (SQ_WAIT_INST_LDS) or any instruction (SQ_WAIT_INST_ANY).
+    Inputs are rocprofv3 databases or --output-format csv counter files.
     Writes a markdown table to out_md."""
     import collections
     import re
     import sqlite3
     acc = collections.defaultdict(lambda: collections.defaultdict(list))
     for db in dbs:
-        con = sqlite3.connect(db)
-        for kname, ctr, val in con.execute(
-                "select kernel_name, counter_name, value from counters_collection"):
+        if db.endswith(".csv"):  # --output-format csv: one row per (dispatch, counter)
+            import csv
+            per = collections.defaultdict(float)
+            for r_ in csv.DictReader(open(db)):
+                per[(r_["Kernel_Name"], r_["Dispatch_Id"], r_["Counter_Name"])] += float(r_["Counter_Value"])
+            rows_ = [(k_, c_, v_) for (k_, _, c_), v_ in per.items()]
+        else:
+            rows_ = sqlite3.connect(db).execute("select kernel_name, counter_name, value from counters_collection")
+        for kname, ctr, val in rows_:
             m = re.search(r"(\w+(?:<[^>]*>)?)\(", kname)
             acc[m.group(1) if m else kname][ctr].append(float(val))
     lines = ["# Counter summary", "", "Command(s):", ""] + [f"    {c_}" for c_ in command.split(" ;; ") if c_] + [""]
     for k_, ctrs in sorted(acc.items()):
         avg = {c_: sum(v_) / len(v_) for c_, v_ in ctrs.items()}
-        n = max(len(v_) for v_ in ctrs.values())
+        n = min(len(v_) for v_ in ctrs.values())
         lines += [f"## {k_} ({n} dispatches per pass)", "", "| counter | mean per dispatch |", "|---|---|"]
         lines += [f"| {c_} | {v_:,.0f} |" for c_, v_ in sorted(avg.items())]
         gui = avg.get("GRBM_GUI_ACTIVE")
@@ -397,6 +405,11 @@ def counter_report(out_md, dbs, command=""):
                 der.append(("fp16/bf16 matrix-core FLOP per dispatch", f"{f16 / 1e9:.2f} G"))
                 der.append(("fp16/bf16 FLOP per cycle / dense peak (4096 per CU-cycle)",
                             f"{f16 / (cyc * CUS * 4096):.3f}"))
+            f32 = 512 * avg.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0)
+            if f32:
+                der.append(("fp32 matrix-core FLOP per dispatch", f"{f32 / 1e9:.2f} G"))
+                der.append(("fp32 FLOP per cycle / dense peak (256 per CU-cycle)",
+                            f"{f32 / (cyc * CUS * 256):.3f}"))
             if "SQ_LDS_BANK_CONFLICT" in avg:
                 der.append(("LDS bank-conflict cycles per CU / active cycles",
                             f"{avg['SQ_LDS_BANK_CONFLICT'] / CUS / cyc:.3f}"))
