@@ -86,7 +86,10 @@ __device__ __forceinline__ void conv_tokens(const uint16_t (&win)[3 + TM], const
 // shifted in place, and conv_shift_qk_kernel shifts the q and k rows
 // afterwards (same stream).
 template <int TM>
-__global__ __launch_bounds__(kThreads) void decode_tokens_kernel(DecodeArgs p)
+// Five waves per SIMD (96 registers, five workgroups per CU): the state's
+// loads are issued after the prologue, whose registers are free by then, so
+// that nothing spills; the other workgroups' streams cover their latency.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 5))) void decode_tokens_kernel(DecodeArgs p)
 {
     constexpr int kXS = kD + 4;     // s_x row stride: the A reads of a step hit distinct banks
     __shared__ float s_x[8][kXS];   // k^_0..k^_3, q^_0..q^_3 (zero beyond T)
@@ -108,12 +111,7 @@ __global__ __launch_bounds__(kThreads) void decode_tokens_kernel(DecodeArgs p)
     const int lane = t & 63, wave = t >> 6, lq = lane >> 4, lr = lane & 15;
     const int r0 = 64 * (wave >> 1), c0 = 64 * (wave & 1);
 
-    // the state first, so that its latency covers the prologue
     const long piece0 = ((long)row * p.Hv + h) * kD * kD + (long)(r0 + lq) * kD + c0 + 4 * lr;
-    f32x4 st[16];
-#pragma unroll
-    for (int s = 0; s < 16; ++s)
-        st[s] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p.state_in + piece0 + 4L * s * kD));
 
     // ---- prologue: q_g (threads 0..127) and k_g (128..255) from read-only
     //      conv rows; v_h (threads 0..127) with its in-place shift; the gates
@@ -161,6 +159,11 @@ __global__ __launch_bounds__(kThreads) void decode_tokens_kernel(DecodeArgs p)
             s_ab[ch][1] = sigmoid_f(p.b[ab]);
         }
     }
+    // the state
+    f32x4 st[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+        st[s] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p.state_in + piece0 + 4L * s * kD));
     __syncthreads();
     if (t < kD) {
 #pragma unroll
