@@ -233,12 +233,13 @@ def test_backward_no_decay(oracle_lib):
     _compare(_gpu(inp, g_o, g_S, qs, 1, 300), _oracle(oracle_lib, inp, g_o, g_S, qs), 1, 300, "no decay")
 
 
-def test_backward_segments(oracle_lib):
-    # 47 chunks at 1 QK / 2 V heads: the two sequential passes cut the
-    # sequence into three segments run in parallel; the later ones start from
-    # zero after a warm-up of a few chunks whose decay bounds what they drop
-    inp, g_o, g_S, qs = _case(1, 3000, 1, 2, seed=101)
-    _compare(_gpu(inp, g_o, g_S, qs, 1, 3000), _oracle(oracle_lib, inp, g_o, g_S, qs), 1, 3000, "segments")
+@pytest.mark.parametrize("B", [1, 2])
+def test_backward_segments(oracle_lib, B):
+    # 47 chunks at 1 QK / 2 V heads: the two sequential passes cut each
+    # sequence into segments run in parallel (five here); the later ones start
+    # from zero after a warm-up of a few chunks whose decay bounds what they drop
+    inp, g_o, g_S, qs = _case(B, 3000, 1, 2, seed=101 + B)
+    _compare(_gpu(inp, g_o, g_S, qs, B, 3000), _oracle(oracle_lib, inp, g_o, g_S, qs), B, 3000, f"segments B{B}")
 
 
 def test_backward_segments_exact_starts(oracle_lib):
