@@ -497,7 +497,6 @@ static_assert(kLocalR >= 2 * 64 * kLK, "the A matrices overlay the k^ and q^ row
 __global__ __launch_bounds__(kBT) void bwd_local_kernel(BwdArgs p, BwdWs ws)
 {
     __shared__ __attribute__((aligned(16))) float R[kLocalR];
-    __shared__ float KK[64 * kLN], QK[64 * kLN];
     __shared__ float gam[4][64], bet[4][64];
     const int Hv = p.Hv, Hqk = p.Hqk, G = Hv / Hqk;
     const int cidx = blockIdx.x / Hqk, g = blockIdx.x % Hqk;
@@ -516,39 +515,37 @@ __global__ __launch_bounds__(kBT) void bwd_local_kernel(BwdArgs p, BwdWs ws)
         st4(Qs + r * kLK + 4 * q, r < n ? ld4(ws.qh + src) : z);
     }
     __syncthreads();
+    // lower tiles (I, J <= I): K K^T by waves 0 (row blocks 0, 3) and 1
+    // (1, 2), Q K^T by waves 2 and 3 likewise; lane (lq, lr) contracts
+    // k = 32 lq .. 32 lq + 31 (a permutation of the 16x16x4 steps' k).  A
+    // wave keeps its five tiles in registers (element e: row 16 I + 4 lq + e,
+    // column 16 J + lr) until it has formed the A (or P) tiles of every head.
+    constexpr int kTi[2][5] = {{0, 3, 3, 3, 3}, {1, 1, 2, 2, 2}}, kTj[2][5] = {{0, 0, 1, 2, 3}, {0, 1, 0, 1, 2}};
+    const int lq = lane >> 4, lr = lane & 15, par = w & 1;
+    const bool isk = w < 2;  // K K^T (then A) or Q K^T (then P)
+    f32x4 tl[5];
     {
-        // lower tiles (I, J <= I): K K^T by waves 0 (row blocks 0, 3) and 1
-        // (1, 2), Q K^T by waves 2 and 3 likewise; lane (lq, lr) contracts
-        // k = 32 lq .. 32 lq + 31 (a permutation of the 16x16x4 steps' k)
-        const int lq = lane >> 4, lr = lane & 15;
-        const float *Asrc = w < 2 ? Ks : Qs;
-        float *dst = w < 2 ? KK : QK;
+        const float *Asrc = isk ? Ks : Qs;
         float *kkg = ws.KK + ((long)cidx * Hqk + g) * 4096;
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-            const int I = (w & 1) ? 1 + pass : 3 * pass;
-            float a[32];
+        for (int kt = 0; kt < 5; ++kt) {
+            const int I = kTi[par][kt], J = kTj[par][kt];
+            float a[32], b[32];
 #pragma unroll
             for (int v = 0; v < 8; ++v) {
                 const float4 u = ld4(Asrc + (16 * I + lr) * kLK + 32 * lq + 4 * v);
                 a[4 * v] = u.x; a[4 * v + 1] = u.y; a[4 * v + 2] = u.z; a[4 * v + 3] = u.w;
+                const float4 u2 = ld4(Ks + (16 * J + lr) * kLK + 32 * lq + 4 * v);
+                b[4 * v] = u2.x; b[4 * v + 1] = u2.y; b[4 * v + 2] = u2.z; b[4 * v + 3] = u2.w;
             }
-            for (int J = 0; J <= I; ++J) {
-                float b[32];
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int v = 0; v < 8; ++v) {
-                    const float4 u = ld4(Ks + (16 * J + lr) * kLK + 32 * lq + 4 * v);
-                    b[4 * v] = u.x; b[4 * v + 1] = u.y; b[4 * v + 2] = u.z; b[4 * v + 3] = u.w;
-                }
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int st = 0; st < 32; ++st) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], b[st], acc, 0, 0, 0);
+            tl[kt] = acc;
+            if (isk) {
 #pragma unroll
-                for (int st = 0; st < 32; ++st) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], b[st], acc, 0, 0, 0);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 16 * I + 4 * lq + e, j = 16 * J + lr;
-                    dst[i * kLN + j] = acc[e];
-                    if (w < 2) kkg[i * 64 + j] = acc[e];  // for the per-head gradient kernel (lower tiles)
-                }
+                for (int e = 0; e < 4; ++e)  // for the per-head gradient kernel (lower tiles)
+                    kkg[(16 * I + 4 * lq + e) * 64 + 16 * J + lr] = acc[e];
             }
         }
     }
@@ -561,19 +558,30 @@ __global__ __launch_bounds__(kBT) void bwd_local_kernel(BwdArgs p, BwdWs ws)
             bet[w][lane] = lane < n ? ws.beta[(t0 + lane) * Hv + h] : 0.f;
         }
         __syncthreads();
-        // A (strict lower) into LDS and P (lower incl. the diagonal) to the
-        // workspace, for each head; tiles above the diagonal are never read
-        for (int idx = t; idx < jn * 4096; idx += kBT) {
-            const int jh = idx >> 12, i = (idx >> 6) & 63, jj = idx & 63;
-            if (jj > i) {
-                const long mo = ((long)cidx * Hv + g * G + j0 + jh) * 4096;
-                ws.P[mo + i * 64 + jj] = 0.f;
-                continue;
-            }
-            const float D = expf(gam[jh][i] - gam[jh][jj]);
-            R[jh * 64 * kLN + i * kLN + jj] = (jj < i && i < n) ? bet[jh][i] * KK[i * kLN + jj] * D : 0.f;
+        // A (strict lower) into LDS from the K K^T tiles, P (lower incl. the
+        // diagonal) to the workspace from the Q K^T tiles, for each head;
+        // the A tiles above the diagonal are never read, the P tiles above
+        // it are written as zeros
+        for (int jh = 0; jh < jn; ++jh) {
             const long mo = ((long)cidx * Hv + g * G + j0 + jh) * 4096;
-            ws.P[mo + i * 64 + jj] = i < n ? QK[i * kLN + jj] * D : 0.f;
+#pragma unroll
+            for (int kt = 0; kt < 5; ++kt) {
+                const int I = kTi[par][kt], J = kTj[par][kt], jj = 16 * J + lr;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * I + 4 * lq + e;
+                    const float D = expf(gam[jh][i] - gam[jh][jj]);
+                    if (isk)
+                        R[jh * 64 * kLN + i * kLN + jj] = (jj < i && i < n) ? bet[jh][i] * tl[kt][e] * D : 0.f;
+                    else
+                        ws.P[mo + i * 64 + jj] = (jj <= i && i < n) ? tl[kt][e] * D : 0.f;
+                }
+            }
+        }
+        for (int idx = t; idx < jn * 1024; idx += kBT) {
+            const int jh = idx >> 10, i = (idx >> 4) & 63, c4 = 4 * (idx & 15);
+            if (c4 >= 16 * (i / 16 + 1))
+                st4(ws.P + ((long)cidx * Hv + g * G + j0 + jh) * 4096 + i * 64 + c4, make_float4(0.f, 0.f, 0.f, 0.f));
         }
         __syncthreads();
         // X = (I + A)^-1 of head w, in place; written out whole, zero above the diagonal
