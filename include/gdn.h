@@ -326,8 +326,24 @@ size_t gdn_prefill_backward_workspace_size(int B, int T, int Hqk, int Hv, int dk
  *                    gradient of the history rows (of zero rows when
  *                    conv_state_in is NULL)
  *   grad_state_in    [B][Hv][dk][dv] fp32, or NULL (not computed)
- *   workspace        device, >= gdn_prefill_backward_workspace_size bytes,
- *                    16-byte aligned; its contents are scratch
+ *   workspace        device scratch, 16-byte aligned; its contents on entry
+ *                    are irrelevant.  With gdn_prefill_backward_workspace_size
+ *                    bytes or more the batch runs at once.  With less, it runs
+ *                    sequence by sequence, each in windows of Tw tokens (Tw a
+ *                    multiple of 64, the largest whose plan fits; the chunk
+ *                    grid is the one-pass grid): a forward sweep keeps the
+ *                    state entering every window (Hv x 64 KiB each), then the
+ *                    windows' backwards run from the last, each handing its
+ *                    state gradient and the gradient of its three history
+ *                    rows to the window before it.  The result equals the
+ *                    one-pass result up to rounding (the conv weight gradient
+ *                    is summed in another order).  gdn_prefill_backward_windows
+ *                    reports Tw; when not even 64-token windows fit it
+ *                    returns GDN_ERR_WORKSPACE_TOO_SMALL, nothing launched.
+ *                    The workspace then stays bounded by one window's
+ *                    backward plus the window states, whatever T is (the
+ *                    explainer, section 3, stresses the mixer's fixed-size
+ *                    state).
  * Every gradient is overwritten (not accumulated).  Outputs must not overlap
  * each other, the inputs or the workspace.  Pointers 4-byte aligned, grad_o
  * 8-byte aligned.  With
@@ -345,6 +361,17 @@ int gdn_prefill_backward(const uint16_t *q, const uint16_t *k, const uint16_t *v
                          float gate_scale, float q_scale,
                          void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Window length gdn_prefill_backward takes with workspace_bytes of workspace
+ * for these sizes: *window_tokens = T when the whole batch runs at once (also
+ * when B * T = 0), else the window length Tw of its sequence-by-sequence run.
+ * Returns GDN_OK, or GDN_ERR_WORKSPACE_TOO_SMALL when not even 64-token
+ * windows fit (GDN_ERR_INVALID_ARGUMENT / GDN_ERR_UNSUPPORTED for bad sizes,
+ * as gdn_prefill_backward).  Host only: no HIP call.
+ */
+int gdn_prefill_backward_windows(int B, int T, int Hqk, int Hv, int dk, int dv, size_t workspace_bytes,
+                                 int *window_tokens);
+
 /* Bytes of device workspace gdn_prefill_backward_varlen needs (an upper bound
  * over every split of T_tot tokens into N sequences; 0 when T_tot = 0). */
 size_t gdn_prefill_backward_varlen_workspace_size(int N, int T_tot, int Hqk, int Hv, int dk, int dv);
@@ -357,7 +384,10 @@ size_t gdn_prefill_backward_varlen_workspace_size(int N, int T_tot, int Hqk, int
  * q, k, v, grad_q, grad_k, grad_v are [T_tot][H][d]; a, b, grad_a, grad_b
  * [T_tot][Hv]; grad_o [T_tot][Hv][dv]; states and their gradients
  * [N][Hv][dk][dv]; conv rows and their gradient [N][3][C_tot].  Bounds
- * outside [0, T_tot] are clamped.  Other rules as gdn_prefill_backward.
+ * outside [0, T_tot] are clamped.  The workspace must hold the whole call
+ * (a caller with a memory budget splits the batch into calls, or uses
+ * gdn_prefill_backward sequence by sequence).  Other rules as
+ * gdn_prefill_backward.
  */
 int gdn_prefill_backward_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                 const float *a, const float *b, const uint16_t *conv_w,

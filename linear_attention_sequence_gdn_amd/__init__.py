@@ -79,6 +79,8 @@ def lib():
         L.gdn_decode_step.argtypes = [_P] * 10 + [_I] * 5 + [_F, _F, _P]
         L.gdn_prefill_backward_workspace_size.restype = _SZ
         L.gdn_prefill_backward_workspace_size.argtypes = [_I] * 6
+        L.gdn_prefill_backward_windows.restype = _I
+        L.gdn_prefill_backward_windows.argtypes = [_I] * 6 + [_SZ, ctypes.POINTER(_I)]
         L.gdn_prefill_backward.restype = _I
         L.gdn_prefill_backward.argtypes = [_P] * 18 + [_I] * 6 + [_F, _F, _P, _SZ, _P]
         L.gdn_prefill_backward_varlen_workspace_size.restype = _SZ
@@ -232,6 +234,18 @@ def gdn_prefill_noalloc(q, k, v, a, b, conv_w, *, gate_scale, q_scale=1.0, state
 
 def gdn_prefill_backward_workspace_size(B, T, Hqk, Hv, dk=128, dv=128) -> int:
     return int(lib().gdn_prefill_backward_workspace_size(B, T, Hqk, Hv, dk, dv))
+
+
+def gdn_prefill_backward_windows(B, T, Hqk, Hv, workspace_bytes, dk=128, dv=128) -> int:
+    """Window length ``gdn_prefill_backward`` takes with ``workspace_bytes`` of
+    workspace: T when the batch runs at once, else the window length of its
+    sequence-by-sequence run.  Raises GDNError when not even 64-token windows
+    fit."""
+    out = _I(0)
+    rc = lib().gdn_prefill_backward_windows(B, T, Hqk, Hv, dk, dv, int(workspace_bytes), ctypes.byref(out))
+    if rc != GDN_OK:
+        raise GDNError("gdn_prefill_backward_windows", rc)
+    return int(out.value)
 
 
 def gdn_prefill_backward(q, k, v, a, b, conv_w, grad_o, *, gate_scale, q_scale=1.0,

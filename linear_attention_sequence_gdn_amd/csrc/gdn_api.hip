@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "gdn_prefill.h"
@@ -24,7 +25,13 @@ hipError_t launch_backward(const uint16_t *q, const uint16_t *k, const uint16_t 
                            float *grad_q, float *grad_k, float *grad_v, float *grad_a, float *grad_b,
                            float *grad_conv_w, float *grad_conv_state_in, float *grad_state_in,
                            const int32_t *cu_seqlens, int N, int T, int T_tot, int Hqk, int Hv, float gate_scale,
-                           float q_scale, void *workspace, hipStream_t stream);
+                           float q_scale, float *state_final, bool forward_only, void *workspace,
+                           hipStream_t stream);
+hipError_t launch_bwd_accum(float *dst, const float *src, long n, hipStream_t stream);
+hipError_t launch_bwd_hist(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *rows, long tok0,
+                           int Hqk, int Hv, hipStream_t stream);
+hipError_t launch_bwd_addrows(const float *g, float *gq, float *gk, float *gv, long tok0, int Hqk, int Hv,
+                              hipStream_t stream);
 }  // namespace gdn
 
 namespace {
@@ -374,6 +381,136 @@ size_t gdn_prefill_backward_varlen_workspace_size(int N, int T_tot, int Hqk, int
     return gdn::backward_workspace_bytes(N, T_tot, true, Hqk, Hv);
 }
 
+// ---- the backward of a uniform batch in pieces ---------------------------
+// A call whose workspace is short of the one-pass size runs sequence by
+// sequence, each cut into windows of Tw tokens (a multiple of 64, so the
+// chunk grid is the one-pass grid).  A forward sweep (the backward's own fp32
+// recomputation) leaves the state entering every window; a reverse sweep then
+// runs the whole backward of each window from that state, with the raw rows
+// before the window as its conv history, and the state gradient the window
+// after it handed back as its grad_state_out.  Each window's gradient of its
+// history rows is added into the gradients of those rows once the window
+// before has written them, and the conv weight gradients are summed in a
+// fixed order.
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+static size_t bwd_state_bytes(int Hv) { return (size_t)Hv * gdn::kD * gdn::kD * sizeof(float); }
+static size_t bwd_ctot(int Hqk, int Hv) { return (size_t)(2 * Hqk + Hv) * gdn::kD; }
+
+// Workspace of one sequence of T tokens in windows of Tw: one window's
+// backward, the states entering windows 1 .. nw-1, two state-gradient
+// buffers, a window's history rows, two buffers of their gradient, and one
+// conv weight gradient.
+static size_t bwd_window_bytes(int T, int Tw, int Hqk, int Hv)
+{
+    const size_t nw = (size_t)((T + Tw - 1) / Tw), st = bwd_state_bytes(Hv), C_tot = bwd_ctot(Hqk, Hv);
+    return align256(gdn::backward_workspace_bytes(1, Tw, false, Hqk, Hv)) + (nw + 1) * st +
+           align256(3 * C_tot * sizeof(uint16_t)) + 2 * align256(3 * C_tot * sizeof(float)) +
+           align256(4 * C_tot * sizeof(float));
+}
+
+// Window length a uniform backward takes with W bytes of workspace: T when
+// the whole batch runs at once; else the longest window (fewest windows)
+// whose plan fits; 0 when not even 64-token windows fit.
+static int bwd_window_tokens(int B, int T, int Hqk, int Hv, size_t W)
+{
+    if (B == 0 || T == 0 || W >= gdn::backward_workspace_bytes(B, B * T, false, Hqk, Hv)) return T;
+    const size_t st = bwd_state_bytes(Hv);
+    const int max_nw = (T + gdn::kChunk - 1) / gdn::kChunk;
+    for (int nw = 1; nw <= max_nw; ++nw) {
+        if ((size_t)(nw + 1) * st > W) break;  // the states alone no longer fit
+        const int Tw = nw == 1 ? T : ((T + nw - 1) / nw + gdn::kChunk - 1) / gdn::kChunk * gdn::kChunk;
+        if (bwd_window_bytes(T, Tw, Hqk, Hv) <= W) return Tw;
+    }
+    return 0;
+}
+
+static hipError_t backward_windows(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
+                                   const float *b, const uint16_t *conv_w, const uint16_t *conv_state_in,
+                                   const float *state_in, const uint16_t *grad_o, const float *grad_state_out,
+                                   float *grad_q, float *grad_k, float *grad_v, float *grad_a, float *grad_b,
+                                   float *grad_conv_w, float *grad_conv_state_in, float *grad_state_in, int B,
+                                   int T, int Tw, int Hqk, int Hv, float gate_scale, float q_scale, void *workspace,
+                                   hipStream_t st)
+{
+    const long nq = (long)Hqk * gdn::kD, nv = (long)Hv * gdn::kD, C_tot = (long)bwd_ctot(Hqk, Hv);
+    const long sfl = (long)Hv * gdn::kD * gdn::kD;  // floats of one sequence's states
+    const int nw = (T + Tw - 1) / Tw;
+    uint8_t *base = static_cast<uint8_t *>(workspace);
+    size_t off = 0;
+    auto carve = [&](size_t bytes) {
+        uint8_t *r = base + off;
+        off += align256(bytes);
+        return r;
+    };
+    void *wbwd = carve(gdn::backward_workspace_bytes(1, Tw, false, Hqk, Hv));
+    float *states = reinterpret_cast<float *>(carve((size_t)(nw - 1) * bwd_state_bytes(Hv)));
+    float *ds[2] = {reinterpret_cast<float *>(carve(bwd_state_bytes(Hv))),
+                    reinterpret_cast<float *>(carve(bwd_state_bytes(Hv)))};
+    uint16_t *hist = reinterpret_cast<uint16_t *>(carve(3 * C_tot * sizeof(uint16_t)));
+    float *hg[2] = {reinterpret_cast<float *>(carve(3 * C_tot * sizeof(float))),
+                    reinterpret_cast<float *>(carve(3 * C_tot * sizeof(float)))};
+    float *dw = reinterpret_cast<float *>(carve(4 * C_tot * sizeof(float)));
+    auto slot = [&](int w) { return (nw - 1 - w) & 1; };  // window w's buffer of a ping-pong pair
+    hipError_t e = hipSuccess;
+    auto ok = [&](hipError_t r) { return (e = r) == hipSuccess; };
+    bool first_dw = true;
+    for (int s = 0; s < B; ++s) {
+        const long so = (long)s * T;  // the sequence's first token in the batch
+        const float *s_in = state_in ? state_in + s * sfl : nullptr;
+        const uint16_t *c_in = conv_state_in ? conv_state_in + s * 3 * C_tot : nullptr;
+        const float *gs_out = grad_state_out ? grad_state_out + s * sfl : nullptr;
+        float *gs_in = grad_state_in ? grad_state_in + s * sfl : nullptr;
+        float *gc_in = grad_conv_state_in ? grad_conv_state_in + s * 3 * C_tot : nullptr;
+        // forward sweep: the states entering windows 1 .. nw-1
+        for (int w = 0; w + 1 < nw; ++w) {
+            const long t0 = so + (long)w * Tw;
+            if (w > 0 && !ok(gdn::launch_bwd_hist(q, k, v, hist, t0 - 3, Hqk, Hv, st))) return e;
+            if (!ok(gdn::launch_backward(q + t0 * nq, k + t0 * nq, v + t0 * nv, a + t0 * Hv, b + t0 * Hv, conv_w,
+                                         w == 0 ? c_in : hist, w == 0 ? s_in : states + (w - 1) * sfl,
+                                         grad_o + t0 * nv, nullptr, grad_q + t0 * nq, grad_k + t0 * nq,
+                                         grad_v + t0 * nv, grad_a + t0 * Hv, grad_b + t0 * Hv, grad_conv_w, nullptr,
+                                         nullptr, nullptr, 1, Tw, Tw, Hqk, Hv, gate_scale, q_scale,
+                                         states + w * sfl, true, wbwd, st)))
+                return e;
+        }
+        // reverse sweep
+        for (int w = nw - 1; w >= 0; --w) {
+            const long t0 = so + (long)w * Tw;
+            const int Lw = (int)std::min<long>(Tw, T - (long)w * Tw);
+            if (w > 0 && !ok(gdn::launch_bwd_hist(q, k, v, hist, t0 - 3, Hqk, Hv, st))) return e;
+            float *dwo = first_dw ? grad_conv_w : dw;
+            if (!ok(gdn::launch_backward(q + t0 * nq, k + t0 * nq, v + t0 * nv, a + t0 * Hv, b + t0 * Hv, conv_w,
+                                         w == 0 ? c_in : hist, w == 0 ? s_in : states + (w - 1) * sfl,
+                                         grad_o + t0 * nv, w == nw - 1 ? gs_out : ds[slot(w + 1)],
+                                         grad_q + t0 * nq, grad_k + t0 * nq, grad_v + t0 * nv, grad_a + t0 * Hv,
+                                         grad_b + t0 * Hv, dwo, w == 0 ? gc_in : hg[slot(w)],
+                                         w == 0 ? gs_in : ds[slot(w)], nullptr, 1, Lw, Lw, Hqk, Hv, gate_scale,
+                                         q_scale, nullptr, false, wbwd, st)))
+                return e;
+            if (!first_dw && !ok(gdn::launch_bwd_accum(grad_conv_w, dw, 4 * C_tot, st))) return e;
+            first_dw = false;
+            // the window after this one reached into its last three rows
+            if (w + 1 < nw && !ok(gdn::launch_bwd_addrows(hg[slot(w + 1)], grad_q, grad_k, grad_v,
+                                                          so + (long)(w + 1) * Tw - 3, Hqk, Hv, st)))
+                return e;
+        }
+    }
+    return e;
+}
+
+int gdn_prefill_backward_windows(int B, int T, int Hqk, int Hv, int dk, int dv, size_t workspace_bytes,
+                                 int *window_tokens)
+{
+    if (B < 0 || T < 0 || !window_tokens) return GDN_ERR_INVALID_ARGUMENT;
+    int rc = check_dims(Hqk, Hv, dk, dv);
+    if (rc != GDN_OK) return rc;
+    if ((long)B * T > 0x7fffffffL) return GDN_ERR_UNSUPPORTED;
+    const int Tw = bwd_window_tokens(B, T, Hqk, Hv, workspace_bytes);
+    if (Tw == 0 && (long)B * T > 0) return GDN_ERR_WORKSPACE_TOO_SMALL;
+    *window_tokens = Tw;
+    return GDN_OK;
+}
+
 static int backward_common(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
                            const float *b, const uint16_t *conv_w, const uint16_t *conv_state_in,
                            const float *state_in, const uint16_t *grad_o, const float *grad_state_out,
@@ -394,12 +531,21 @@ static int backward_common(const uint16_t *q, const uint16_t *k, const uint16_t 
         if (ptr && !aligned(ptr, 4)) return GDN_ERR_INVALID_ARGUMENT;
     if ((workspace && !aligned(workspace, 16)) || (grad_o && !aligned(grad_o, 8))) return GDN_ERR_INVALID_ARGUMENT;
     const size_t need = gdn::backward_workspace_bytes(N, T_tot, cu_seqlens != nullptr, Hqk, Hv);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE_TOO_SMALL;
+    if (need > 0 && (!workspace || workspace_bytes < need)) {
+        // a uniform batch runs sequence by sequence, in windows of whole chunks
+        const int Tw = cu_seqlens || !workspace ? 0 : bwd_window_tokens(N, T, Hqk, Hv, workspace_bytes);
+        if (Tw == 0) return GDN_ERR_WORKSPACE_TOO_SMALL;
+        hipError_t e = backward_windows(q, k, v, a, b, conv_w, conv_state_in, state_in, grad_o, grad_state_out,
+                                        grad_q, grad_k, grad_v, grad_a, grad_b, grad_conv_w, grad_conv_state_in,
+                                        grad_state_in, N, T, Tw, Hqk, Hv, gate_scale, q_scale, workspace,
+                                        reinterpret_cast<hipStream_t>(stream));
+        return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    }
     if (N == 0) return GDN_OK;
     hipError_t e = gdn::launch_backward(q, k, v, a, b, conv_w, conv_state_in, state_in, grad_o, grad_state_out,
                                         grad_q, grad_k, grad_v, grad_a, grad_b, grad_conv_w, grad_conv_state_in,
                                         grad_state_in, cu_seqlens, N, T, T_tot, Hqk, Hv, gate_scale, q_scale,
-                                        workspace, reinterpret_cast<hipStream_t>(stream));
+                                        nullptr, false, workspace, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 

@@ -79,6 +79,8 @@ struct BwdArgs {
     int Hqk, Hv;
     float gate_scale, q_scale;
     int nseg;                   // workgroups (segments) per sequence in the two sequential passes
+    float *state_final;         // optional [N][Hv][128][128]: the state after each sequence's last
+                                // chunk, from the recomputed forward (NULL: not written)
 };
 
 // Workspace (fp32).  tok = s*T + t; rows of a chunk beyond its length are
@@ -797,6 +799,14 @@ __global__ __launch_bounds__(kST) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
         __syncthreads();
         if (j + 1 < pl.hi) seq_commit<false>(p, f, L, nullptr, nullptr, Vs);
     }
+    // the workgroup that ends at the sequence's last chunk leaves the final state
+    if (p.state_final && pl.hi == sq.y) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                p.state_final[(((long)s * Hv + h) * kD + srow + e) * kD + col0 + 16 * ct + lr] = S[ct][e];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1505,6 +1515,41 @@ __global__ __launch_bounds__(kBT) void bwd_fill_kernel(float *dst, long n)
     if (e < n) dst[e] = 0.f;
 }
 
+// ---------------------------------------------------------------------------
+// Windows of one sequence (a backward run in pieces of whole chunks)
+// ---------------------------------------------------------------------------
+// dst[e] += src[e]
+__global__ __launch_bounds__(kBT) void bwd_accum_kernel(float *dst, const float *src, long n)
+{
+    const long e = (long)blockIdx.x * kBT + threadIdx.x;
+    if (e < n) dst[e] += src[e];
+}
+
+// The three raw rows before a window, tokens tok0 .. tok0 + 2 of q, k and v,
+// as conv history rows [3][C_tot] (channel order q | k | v)
+__global__ __launch_bounds__(kBT) void bwd_hist_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                                       uint16_t *rows, long tok0, int Hqk, int Hv)
+{
+    const long nq = (long)Hqk * kD, C_tot = 2 * nq + (long)Hv * kD;
+    const long e = (long)blockIdx.x * kBT + threadIdx.x;
+    if (e >= 3 * C_tot) return;
+    const long r = e / C_tot, c = e % C_tot, tok = tok0 + r;
+    rows[e] = c < nq ? q[tok * nq + c] : c < 2 * nq ? k[tok * nq + c - nq] : v[tok * Hv * kD + c - 2 * nq];
+}
+
+// The gradient of a window's history rows [3][C_tot] added into the gradients
+// of the raw rows tok0 .. tok0 + 2, which the window before it has written
+__global__ __launch_bounds__(kBT) void bwd_addrows_kernel(const float *g, float *gq, float *gk, float *gv,
+                                                          long tok0, int Hqk, int Hv)
+{
+    const long nq = (long)Hqk * kD, C_tot = 2 * nq + (long)Hv * kD;
+    const long e = (long)blockIdx.x * kBT + threadIdx.x;
+    if (e >= 3 * C_tot) return;
+    const long r = e / C_tot, c = e % C_tot, tok = tok0 + r;
+    float *dst = c < nq ? gq + tok * nq + c : c < 2 * nq ? gk + tok * nq + c - nq : gv + tok * Hv * kD + c - 2 * nq;
+    *dst += g[e];
+}
+
 // Packed calls: chunk and sequence tables from cu_seqlens, one workgroup.
 // Sequence bounds are clamped into [0, T_tot] and chunk slots to max_chunks,
 // so that a malformed cu_seqlens cannot send any kernel outside the buffers.
@@ -1619,9 +1664,11 @@ hipError_t launch_backward(const uint16_t *q, const uint16_t *k, const uint16_t 
                            float *grad_q, float *grad_k, float *grad_v, float *grad_a, float *grad_b,
                            float *grad_conv_w, float *grad_conv_state_in, float *grad_state_in,
                            const int32_t *cu_seqlens, int N, int T, int T_tot, int Hqk, int Hv, float gate_scale,
-                           float q_scale, void *workspace, hipStream_t stream)
+                           float q_scale, float *state_final, bool forward_only, void *workspace,
+                           hipStream_t stream)
 {
     BwdArgs p{};
+    p.state_final = state_final;
     p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.conv_w = conv_w; p.conv_state_in = conv_state_in;
     p.state_in = state_in; p.grad_o = grad_o; p.grad_state_out = grad_state_out;
     p.grad_q = grad_q; p.grad_k = grad_k; p.grad_v = grad_v; p.grad_a = grad_a; p.grad_b = grad_b;
@@ -1652,6 +1699,7 @@ hipError_t launch_backward(const uint16_t *q, const uint16_t *k, const uint16_t 
         hipLaunchKernelGGL(bwd_local_kernel, dim3(chunks * Hqk), dim3(kBT), 0, stream, p, ws);
         hipLaunchKernelGGL(bwd_fwd_kernel, dim3(N * Hv * kNCB * p.nseg), dim3(kST), 0, stream, p, ws);
     }
+    if (forward_only) return hipGetLastError();  // the recomputed forward alone (state_final)
     // also with no tokens: the state gradient passes straight through
     hipLaunchKernelGGL(bwd_chain_kernel, dim3(N * Hv * kNCB * p.nseg), dim3(kST), 0, stream, p, ws);
     if (grad_conv_state_in && (chunks == 0 || p.cu_seqlens)) {
@@ -1668,6 +1716,31 @@ hipError_t launch_backward(const uint16_t *q, const uint16_t *k, const uint16_t 
     } else {
         hipLaunchKernelGGL(bwd_fill_kernel, dim3((nw + kBT - 1) / kBT), dim3(kBT), 0, stream, grad_conv_w, nw);
     }
+    return hipGetLastError();
+}
+
+// The window kernels of a backward run in pieces (one sequence at a time)
+hipError_t launch_bwd_accum(float *dst, const float *src, long n, hipStream_t stream)
+{
+    hipLaunchKernelGGL(bwd_accum_kernel, dim3((n + kBT - 1) / kBT), dim3(kBT), 0, stream, dst, src, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_hist(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *rows, long tok0,
+                           int Hqk, int Hv, hipStream_t stream)
+{
+    const long n = 3 * (2L * Hqk * kD + (long)Hv * kD);
+    hipLaunchKernelGGL(bwd_hist_kernel, dim3((n + kBT - 1) / kBT), dim3(kBT), 0, stream, q, k, v, rows, tok0, Hqk,
+                       Hv);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_addrows(const float *g, float *gq, float *gk, float *gv, long tok0, int Hqk, int Hv,
+                              hipStream_t stream)
+{
+    const long n = 3 * (2L * Hqk * kD + (long)Hv * kD);
+    hipLaunchKernelGGL(bwd_addrows_kernel, dim3((n + kBT - 1) / kBT), dim3(kBT), 0, stream, g, gq, gk, gv, tok0,
+                       Hqk, Hv);
     return hipGetLastError();
 }
 

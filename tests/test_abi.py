@@ -186,6 +186,40 @@ def test_backward_validation(L):
     assert call_backward(L, B=0, ws=0, ws_bytes=0) == gdn.GDN_OK
 
 
+def test_backward_window_plan(L):
+    # the window a workspace leads to (host-only query)
+    need = gdn.gdn_prefill_backward_workspace_size(1, 8192, 16, 48)
+    assert gdn.gdn_prefill_backward_windows(1, 8192, 16, 48, need) == 8192
+    assert gdn.gdn_prefill_backward_windows(1, 8192, 16, 48, 10 * need) == 8192
+    tw = gdn.gdn_prefill_backward_windows(1, 8192, 16, 48, need - 1)
+    assert 64 <= tw < 8192 and tw % 64 == 0
+    # more workspace never gives shorter windows
+    prev = 0
+    for frac in (0.1, 0.2, 0.4, 0.6, 0.8, 0.99):
+        tw = gdn.gdn_prefill_backward_windows(1, 8192, 16, 48, int(frac * need))
+        assert tw >= prev and tw % 64 == 0
+        prev = tw
+    # the native-context sequence: 262,144 tokens in about 3 GiB instead of the one-pass ~87 GiB
+    one_pass = gdn.gdn_prefill_backward_workspace_size(1, 262144, 16, 48)
+    assert one_pass > 80 * 2**30
+    assert gdn.gdn_prefill_backward_windows(1, 262144, 16, 48, 3 * 2**30) >= 4096
+    # a batch whose sequences fit one at a time runs them whole
+    one = gdn.gdn_prefill_backward_workspace_size(1, 200, 2, 6)
+    assert gdn.gdn_prefill_backward_windows(4, 200, 2, 6, 2 * one) == 200
+    # too small, bad sizes, nothing to do
+    with pytest.raises(gdn.GDNError) as e:
+        gdn.gdn_prefill_backward_windows(1, 8192, 16, 48, 2**20)
+    assert e.value.status == gdn.GDN_ERR_WORKSPACE_TOO_SMALL
+    out = ctypes.c_int(-1)
+    assert L.gdn_prefill_backward_windows(1, 64, 2, 7, 128, 128, 1 << 30, ctypes.byref(out)) == gdn.GDN_ERR_UNSUPPORTED
+    assert L.gdn_prefill_backward_windows(-1, 64, 2, 6, 128, 128, 1 << 30, ctypes.byref(out)) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert L.gdn_prefill_backward_windows(1, 64, 2, 6, 128, 128, 1 << 30, None) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert gdn.gdn_prefill_backward_windows(0, 64, 2, 6, 0) == 64
+    assert gdn.gdn_prefill_backward_windows(1, 0, 2, 6, 0) == 0
+    # a call whose workspace fits no window is refused before anything is launched
+    assert call_backward(L, T=8192, Hqk=16, Hv=48, ws_bytes=2**20) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL
+
+
 def test_backward_varlen_validation(L):
     def call(cu=FAKE, N=3, T_tot=200, Hv=6, ws_bytes=None):
         if ws_bytes is None:

@@ -40,7 +40,7 @@ def _case(B, T, Hqk, Hv, seed, carries=True, gate_scale=0.1, q_scale=1.0):
     return inp, g_o, g_S, q_scale
 
 
-def _gpu(inp, g_o, g_S, q_scale, B, T):
+def _gpu(inp, g_o, g_S, q_scale, B, T, ws_bytes=None):
     import linear_attention_sequence_gdn_amd as gdn
     import torch
     Hqk, Hv, d = inp["Hqk"], inp["Hv"], inp["d"]
@@ -48,6 +48,8 @@ def _gpu(inp, g_o, g_S, q_scale, B, T):
                 state_in=None if inp["state_in"] is None else dev_f32(inp["state_in"]),
                 conv_state_in=None if inp["conv_state_in"] is None else dev_bf16(inp["conv_state_in"]),
                 grad_state_out=None if g_S is None else dev_f32(g_S), want_conv_state=True)
+    if ws_bytes is not None:  # a workspace of exactly this size (stale contents)
+        args["workspace"] = torch.full((ws_bytes,), 0xFF, dtype=torch.uint8, device="cuda")
     g = gdn.gdn_prefill_backward(
         dev_bf16(inp["q"].reshape(B, T, Hqk, d)), dev_bf16(inp["k"].reshape(B, T, Hqk, d)),
         dev_bf16(inp["v"].reshape(B, T, Hv, d)), dev_f32(inp["a"].reshape(B, T, Hv)),
@@ -291,3 +293,50 @@ def test_backward_ignores_stale_workspace():
     torch.cuda.synchronize()
     for n in a:
         assert torch.equal(a[n], b[n]), n
+
+
+def _workspace_for_window(B, T, Hqk, Hv, Tw):
+    """The smallest workspace with which the backward runs in windows of at
+    least Tw tokens (the window query is host-only)."""
+    import linear_attention_sequence_gdn_amd as gdn
+
+    def window(W):
+        try:
+            return gdn.gdn_prefill_backward_windows(B, T, Hqk, Hv, W)
+        except gdn.GDNError:
+            return 0
+    lo, hi = 0, gdn.gdn_prefill_backward_workspace_size(B, T, Hqk, Hv)
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if window(mid) >= Tw:
+            hi = mid
+        else:
+            lo = mid
+    return hi, window(hi)
+
+
+@pytest.mark.parametrize("Tw", [64, 128, 192])
+def test_backward_in_windows_against_oracle(oracle_lib, Tw):
+    # two sequences of 333 tokens run one at a time, in windows of 64, 128 or
+    # 192 tokens (the last ragged), every carry in and out
+    B, T, Hqk, Hv = 2, 333, 2, 6
+    inp, g_o, g_S, qs = _case(B, T, Hqk, Hv, seed=61, q_scale=0.8)
+    W, got_tw = _workspace_for_window(B, T, Hqk, Hv, Tw)
+    assert got_tw == Tw, (Tw, got_tw)
+    win = _gpu(inp, g_o, g_S, qs, B, T, ws_bytes=W)
+    _compare(win, _oracle(oracle_lib, inp, g_o, g_S, qs), B, T, f"windows of {Tw}")
+    # and the one-pass result: the same up to rounding
+    whole = _gpu(inp, g_o, g_S, qs, B, T)
+    for n in whole:
+        assert rel_l2(win[n], whole[n]) <= 1e-6, (n, rel_l2(win[n], whole[n]))
+
+
+def test_backward_in_segmented_windows_against_oracle(oracle_lib):
+    # 8192 tokens in windows of 2048: each window's sequential passes are cut
+    # into segments, and the forward sweep's state comes out of the last one
+    B, T, Hqk, Hv = 1, 8192, 2, 6
+    inp, g_o, g_S, qs = _case(B, T, Hqk, Hv, seed=62)
+    W, got_tw = _workspace_for_window(B, T, Hqk, Hv, 2048)
+    assert got_tw == 2048
+    _compare(_gpu(inp, g_o, g_S, qs, B, T, ws_bytes=W), _oracle(oracle_lib, inp, g_o, g_S, qs), B, T,
+             "T8192 windows of 2048")
