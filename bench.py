@@ -16,10 +16,12 @@ under "configs".  Prints ONE JSON line.
   python bench.py --trace-report OUT_MD DB [--counter-command CMD]
 
 --only restricts the run to some legs (prefill, decode, decode_multi,
-backward, configs, segments), for profiling; the JSON line then holds those
-legs.  "segments" times a tensor-parallel shard's head shape (2 QK / 6 V)
-at T = 8192 and 262,144 with and without the sequential pass's sequence
-split.
+backward, backward_windows, configs, segments), for profiling; the JSON line
+then holds those legs.  "segments" times a tensor-parallel shard's head shape
+(2 QK / 6 V) at T = 8192 and 262,144 with and without the sequential pass's
+sequence split.  "backward_windows" times the backward with a workspace short
+of the one-pass size (T = 8192 in 512 MiB, T = 262,144 in 3 GiB), which runs
+in windows.
 --calibrate-copy ends the run with a plain 256 MiB device-to-device copy, so
 that a rocprofv3 --pmc pass over this command also reads its counters for a
 transfer of known size.  --traffic-report turns two such passes (FETCH_SIZE,
@@ -680,6 +682,60 @@ def bench_backward(hip, settle_ms, steps=10, warmup=3):
                          "traffic": None, "algorithmic_flop_per_call": flop}}
 
 
+def bench_backward_windows(hip):
+    """The backward in a workspace short of the one-pass size: T = 8192 in
+    512 MiB (the cost of the windows at the same length) and the native-context
+    length T = 262,144 (one pass: ~94 GB) in 3 GiB."""
+    import numpy as np
+    import torch
+    from linear_attention_sequence_gdn_amd import inputs
+
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    out = {}
+    for idx, seed, ws_bytes, steps in ((1, 1001, 512 << 20, 3), (2, 1002, 3 << 30, 2)):
+        c = inputs.CONFIGS[idx]
+        B, T, Hqk, Hv = 1, c["T"], c["Hqk"], c["Hv"]
+        x = inputs.make_prefill(T_list=[T], Hqk=Hqk, Hv=Hv, seed=seed, gate_scale=c["gate_scale"])
+        gen = torch.Generator(device="cuda").manual_seed(2000 + idx)
+        g_o = torch.randn((B, T, Hv, D), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        g_S = torch.randn((B, Hv, D, D), generator=gen, device="cuda", dtype=torch.float32)
+        args = (bf(x["q"].reshape(B, T, Hqk, D)), bf(x["k"].reshape(B, T, Hqk, D)), bf(x["v"].reshape(B, T, Hv, D)),
+                f32(x["a"].reshape(B, T, Hv)), f32(x["b"].reshape(B, T, Hv)), bf(x["conv_w"]), g_o)
+        del x
+        out[f"T{T}"] = bench_backward_bounded(hip, args, g_S, T, Hqk, Hv, c["gate_scale"], ws_bytes, steps)
+        del args, g_o
+        torch.cuda.empty_cache()
+    return out
+
+
+def bench_backward_bounded(hip, args, g_S, T, Hqk, Hv, gate_scale, ws_bytes, steps):
+    """gdn_prefill_backward with a workspace of ws_bytes, short of the one-pass
+    size: the sequence runs in windows (forward sweep for the window states,
+    then the windows' backwards from the last).  One warm-up call, then K
+    calls between two events."""
+    import torch
+    import linear_attention_sequence_gdn_amd as gdn
+
+    tw = gdn.gdn_prefill_backward_windows(1, T, Hqk, Hv, ws_bytes)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    run = lambda: gdn.gdn_prefill_backward(*args, gate_scale=gate_scale, grad_state_out=g_S, workspace=ws)
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    run()
+    torch.cuda.synchronize()
+    t0, t1 = hip.event(), hip.event()
+    hip.record(t0, sp)
+    for _ in range(steps):
+        run()
+    hip.record(t1, sp)
+    torch.cuda.synchronize()
+    ms = hip.ms(t0, t1) / steps
+    return {"T": T, "workspace_bytes": ws_bytes,
+            "one_pass_workspace_bytes": gdn.gdn_prefill_backward_workspace_size(1, T, Hqk, Hv),
+            "window_tokens": tw, "windows": -(-T // tw), "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3),
+            "calls": steps}
+
+
 def bench_config(hip, idx, settle_ms, steps):
     """One of the other prefill workloads, timed as the step is: the tiny
     2 QK / 6 V prefill (T = 512), the native-context prefill (T = 262,144,
@@ -896,7 +952,7 @@ def cpu_baseline_backward(T_sample=1024, min_seconds=4.0, max_reps=20):
                       f"16QK/48V, parallel over the 16 QK groups; {reps} run(s) in {dt:.1f} s wall"}
 
 
-LEGS = ("prefill", "decode", "decode_multi", "backward", "configs", "segments")
+LEGS = ("prefill", "decode", "decode_multi", "backward", "backward_windows", "configs", "segments")
 
 
 def main():
@@ -1007,6 +1063,8 @@ def main():
             bw["roofline"]["traffic"] = _sum_or_none(
                 *(load_traffic("backward_" + k_[4:-7], source_digest(BWD_SOURCES)) for k_ in BWD_KERNELS))
             line["backward"] = bw
+        if "backward_windows" in legs:
+            line.setdefault("backward", {})["bounded_workspace"] = bench_backward_windows(hip)
         if "configs" in legs:
             line["configs"] = {str(i): bench_config(hip, i, settle_ms, args.steps) for i in (0, 2, 4)}
         if "segments" in legs:
