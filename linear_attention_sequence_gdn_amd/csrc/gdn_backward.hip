@@ -16,8 +16,9 @@
 // alwayszhang.cn describes FlashQLA's forward and backward kernels of this
 // chunked form).  The backward applies the chain rule to each of these
 // lines in reverse; the derivative of the inverse is dL = -X^T dX X^T.  All
-// arithmetic is fp32: the two sequential passes multiply on the fp32 matrix
-// cores, everything else on the vector ALUs.
+// arithmetic is fp32: the products of the two sequential passes, the
+// chunk-local pass and the per-chunk gradients run on the fp32 matrix cores,
+// the conv, norm and gate steps on the vector ALUs.
 //
 // Passes (one launch each):
 //   bwd_setup_kernel   (packed calls) chunk and sequence tables from cu_seqlens
@@ -29,12 +30,16 @@
 //                      state gradient at every chunk end, dVn and dVt (= dv^)
 //   bwd_grad_kernel    per (chunk, V head): dq^, dk^ (per V head), dgamma,
 //                      dbeta -> grad_a, grad_b
-//   bwd_dy_kernel      per (chunk, channel plane): back through the L2 norm
-//                      and SiLU to the conv output
-//   bwd_conv_kernel    per (chunk, channel plane): back through the conv to
-//                      q, k, v, the carried conv rows and per-chunk partial
-//                      conv weight gradients
+//   bwd_dyconv_kernel  per (chunk, channel plane): back through the L2 norm
+//                      and SiLU to the conv output (in LDS, with the three
+//                      rows after the chunk), then through the conv to q, k,
+//                      v, the carried conv rows and per-chunk partial conv
+//                      weight gradients
 //   bwd_dw_kernel      the conv weight gradient, summed over chunks in order
+// A uniform call short of its one-pass workspace runs sequence by sequence in
+// windows of whole chunks; bwd_hist_kernel, bwd_addrows_kernel and
+// bwd_accum_kernel carry the conv rows, their gradients and the conv weight
+// gradient between windows.
 // The state columns are independent in the update, so the two sequential
 // passes split them over four workgroups per (sequence, V head); the twelve
 // workgroups of one (sequence, QK group) run on one XCD and share its L2.
@@ -96,7 +101,6 @@ struct BwdWs {
     float *vt, *vn;     // [tok][Hv][128]   Vt, Vn
     float *dvn, *dvh;   // [tok][Hv][128]   dVn, dVt = dv^
     float *dqp, *dkp;   // [tok][Hv][128]   dq^, dk^ of each V head
-    float *dy;          // [tok][C_tot]     gradient of the conv outputs
     float *sdot;        // [chunk][Hv][kSD] <dS', S> of each (column block, wave): state
                         //                   gradient leaving the chunk, state entering it
     float *dwp;         // [chunk][C_tot][4] conv weight gradient of each chunk
@@ -1349,119 +1353,144 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ---------------------------------------------------------------------------
-// 6. back through the L2 norm and SiLU to the conv outputs
+// 6. back through the L2 norm and SiLU to the conv outputs, then through the
+//    conv, per (chunk, channel plane)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kBT) void bwd_dy_kernel(BwdArgs p, BwdWs ws)
+// The conv-output gradient dy of the chunk's rows and of the three rows after
+// it (which the conv backward of its last rows reads) is formed into LDS and
+// consumed there: row x of the conv input feeds outputs x .. x + 3.  The three
+// rows after the chunk are formed again by the next chunk's workgroup; the
+// arithmetic is the same, so both see the same values.
+constexpr int kDyRows = kChunk + 3;
+constexpr int kDyHalf = (kDyRows + 1) / 2;  // rows per thread half when forming dy
+constexpr int kDyWin = kDyHalf + 3;         // their conv input window
+
+// Raw rows tb - 3 .. tb - 3 + NW - 1 of channel c of a plane (carried rows,
+// or zeros, before the sequence; zeros past it), loaded together
+template <int NW>
+__device__ __forceinline__ void x_window_n(const BwdArgs &p, const Plane &P, const uint16_t *x, int s, long seq0,
+                                           int tb, int L, int c, long C_tot, float (&xw)[NW])
 {
-    __shared__ float zs[64 * kLK], ds[64 * kLK];
-    __shared__ float nrm[64], zd[64];
-    const int4 ci = bchunk(p, ws, blockIdx.x);
-    const int s = ci.x, n = ci.z, j = ci.w;
-    if (n == 0) return;
-    const long seq0 = ci.y, t0 = seq0 + (long)j * kChunk;
-    const int L = bseq(p, ws, s).w;
-    const long C_tot = 2L * p.Hqk * kD + (long)p.Hv * kD;
-    const int G = p.Hv / p.Hqk;
-    const Plane P = plane_of(p, blockIdx.y);
-    const uint16_t *x = plane_src(p, P);
-    const int t = threadIdx.x, c = t & 127, rh = t >> 7, rb = 32 * rh;
-    float w[4];
+    uint16_t raw[NW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = bf16_to_f32(p.conv_w[(P.ch0 + c) * 4 + i]);
-    float xw[kWin];
-    x_window(p, P, x, s, seq0, j * kChunk + rb, L, c, C_tot, xw);
-    // the 32 rows' gradient loads are issued together: rows past the chunk's
-    // end read its last row (in bounds) and are not used
-    const long hs = (long)p.Hv * kD;
-    if (P.kind == 2) {
-        const float *gv = ws.dvh + t0 * hs + (long)P.head * kD + c;
-        float gr[32];
+    for (int i = 0; i < NW; ++i) raw[i] = x[(seq0 + min(max(tb - 3 + i, 0), L - 1)) * P.ld + c];
 #pragma unroll
-        for (int r = 0; r < 32; ++r) gr[r] = gv[min(rb + r, n - 1) * hs];
-#pragma unroll
-        for (int r = 0; r < 32; ++r)
-            if (rb + r < n) ws.dy[(t0 + rb + r) * C_tot + P.ch0 + c] = gr[r] * silu_grad(conv_at(w, xw, r));
-        return;
-    }
-    float dsum[32];
-#pragma unroll
-    for (int r = 0; r < 32; ++r) dsum[r] = 0.f;
-    for (int jh = 0; jh < G; ++jh) {
-        const float *pj = (P.kind == 0 ? ws.dqp : ws.dkp) + t0 * hs + (long)(P.head * G + jh) * kD + c;
-#pragma unroll
-        for (int r = 0; r < 32; ++r) dsum[r] += pj[min(rb + r, n - 1) * hs];
-    }
-#pragma unroll
-    for (int r = 0; r < 32; ++r) {
-        if (rb + r < n) {
-            const float y = conv_at(w, xw, r);
-            zs[(rb + r) * kLK + c] = y * sigm(y);
-            ds[(rb + r) * kLK + c] = dsum[r];
-        }
-    }
-    __syncthreads();
-    {
-        const int r = t >> 2, pt = t & 3;
-        float ss = 0.f, sd = 0.f;
-        if (r < n)
-            for (int i = 0; i < 32; ++i) {
-                const float z = zs[r * kLK + pt * 32 + i];
-                ss = fmaf(z, z, ss);
-                sd = fmaf(z, ds[r * kLK + pt * 32 + i], sd);
-            }
-        ss += __shfl_xor(ss, 1, 64);
-        ss += __shfl_xor(ss, 2, 64);
-        sd += __shfl_xor(sd, 1, 64);
-        sd += __shfl_xor(sd, 2, 64);
-        if (pt == 0) {
-            nrm[r] = sqrtf(ss + 1e-6f);
-            zd[r] = sd;
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < 32; ++r) {
-        const int rr = rb + r;
-        if (rr < n) {
-            const float rn = nrm[rr];
-            const float dz = ds[rr * kLK + c] / rn - zs[rr * kLK + c] * zd[rr] / (rn * rn * rn);
-            ws.dy[(t0 + rr) * C_tot + P.ch0 + c] = dz * silu_grad(conv_at(w, xw, r));
-        }
+    for (int i = 0; i < NW; ++i) {
+        const int tau = tb - 3 + i;
+        float v = 0.f;
+        if (tau >= 0 && tau < L)
+            v = bf16_to_f32(raw[i]);
+        else if (tau < 0 && p.conv_state_in)
+            v = bf16_to_f32(p.conv_state_in[((long)s * 3 + 3 + tau) * C_tot + P.ch0 + c]);
+        xw[i] = v;
     }
 }
 
-// ---------------------------------------------------------------------------
-// 7. back through the conv
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kBT) void bwd_conv_kernel(BwdArgs p, BwdWs ws)
+__global__ __launch_bounds__(kBT) void bwd_dyconv_kernel(BwdArgs p, BwdWs ws)
 {
+    __shared__ float zs[kDyRows * kLK], ds[kDyRows * kLK];  // SiLU output, its gradient, then dy
+    __shared__ float nrm[kDyRows], zd[kDyRows];
     __shared__ float wpart[2][kD][4];
     const int cidx = blockIdx.x;
     const int4 ci = bchunk(p, ws, cidx);
     const int s = ci.x, n = ci.z, j = ci.w;
     const long C_tot = 2L * p.Hqk * kD + (long)p.Hv * kD;
     const Plane P = plane_of(p, blockIdx.y);
+    const int t = threadIdx.x, c = t & 127, rh = t >> 7;
+    const long ch = P.ch0 + c;
     if (n == 0) {  // an empty chunk slot contributes nothing to the weight gradient
-        if (threadIdx.x < kD)
-            for (int jj = 0; jj < 4; ++jj) ws.dwp[((long)cidx * C_tot + P.ch0 + threadIdx.x) * 4 + jj] = 0.f;
+        if (t < kD)
+            for (int jj = 0; jj < 4; ++jj) ws.dwp[((long)cidx * C_tot + P.ch0 + t) * 4 + jj] = 0.f;
         return;
     }
     const long seq0 = ci.y, t0 = seq0 + (long)j * kChunk;
-    const int L = bseq(p, ws, s).w;  // sequence length
+    const int L = bseq(p, ws, s).w;
+    const int m = min(n + 3, L - j * kChunk);  // rows of dy formed: the chunk's, and up to three after it
+    const int G = p.Hv / p.Hqk;
     const uint16_t *x = plane_src(p, P);
-    float *gx = (P.kind == 0 ? p.grad_q : P.kind == 1 ? p.grad_k : p.grad_v) + (long)P.head * kD;
-    const int t = threadIdx.x, c = t & 127, rh = t >> 7, rb = 32 * rh, tb = j * kChunk + rb;
-    const long ch = P.ch0 + c;
     float w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = bf16_to_f32(p.conv_w[ch * 4 + i]);
-    // dy of sequence positions tb .. tb + 34 (zero past the sequence), and the raw rows tb - 3 .. tb + 31
-    const float *dy = ws.dy + seq0 * C_tot + ch;
+    {
+        // ---- dy of rows rb .. rb + kDyHalf - 1 (those below m) of channel c
+        const int rb = kDyHalf * rh;
+        float xw[kDyWin];
+        x_window_n<kDyWin>(p, P, x, s, seq0, j * kChunk + rb, L, c, C_tot, xw);
+        const long hs = (long)p.Hv * kD;
+        float dsum[kDyHalf];
+        // rows past m read row m - 1 (in bounds) and are not used
+        if (P.kind == 2) {
+            const float *gv = ws.dvh + t0 * hs + (long)P.head * kD + c;
+#pragma unroll
+            for (int r = 0; r < kDyHalf; ++r) dsum[r] = gv[min(rb + r, m - 1) * hs];
+        } else {
+#pragma unroll
+            for (int r = 0; r < kDyHalf; ++r) dsum[r] = 0.f;
+            for (int jh = 0; jh < G; ++jh) {
+                const float *pj = (P.kind == 0 ? ws.dqp : ws.dkp) + t0 * hs + (long)(P.head * G + jh) * kD + c;
+#pragma unroll
+                for (int r = 0; r < kDyHalf; ++r) dsum[r] += pj[min(rb + r, m - 1) * hs];
+            }
+        }
+        // v: dy = dv^ SiLU'(y).  q, k: the SiLU output z and its gradient, for the norm
+#pragma unroll
+        for (int r = 0; r < kDyHalf; ++r) {
+            if (rb + r < m) {
+                float y = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y = fmaf(w[i], xw[r + i], y);
+                if (P.kind == 2) {
+                    ds[(rb + r) * kLK + c] = dsum[r] * silu_grad(y);
+                } else {
+                    zs[(rb + r) * kLK + c] = y * sigm(y);
+                    ds[(rb + r) * kLK + c] = dsum[r];
+                }
+            }
+        }
+        __syncthreads();
+        if (P.kind != 2) {
+            // ---- q, k: back through the L2 norm, row by row (four threads a row)
+            for (int r0 = 0; r0 < m; r0 += kBT / 4) {
+                const int r = r0 + (t >> 2), pt = t & 3;
+                float ss = 0.f, sd = 0.f;
+                if (r < m)
+                    for (int i = 0; i < 32; ++i) {
+                        const float z = zs[r * kLK + pt * 32 + i];
+                        ss = fmaf(z, z, ss);
+                        sd = fmaf(z, ds[r * kLK + pt * 32 + i], sd);
+                    }
+                ss += __shfl_xor(ss, 1, 64);
+                ss += __shfl_xor(ss, 2, 64);
+                sd += __shfl_xor(sd, 1, 64);
+                sd += __shfl_xor(sd, 2, 64);
+                if (pt == 0 && r < m) {
+                    nrm[r] = sqrtf(ss + 1e-6f);
+                    zd[r] = sd;
+                }
+            }
+            __syncthreads();
+            // dy = (dz / |z| - z <z, dz> / |z|^3) SiLU'(y), over ds in place
+#pragma unroll
+            for (int r = 0; r < kDyHalf; ++r) {
+                const int rr = rb + r;
+                if (rr < m) {
+                    float y = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) y = fmaf(w[i], xw[r + i], y);
+                    const float rn = nrm[rr];
+                    const float dz = ds[rr * kLK + c] / rn - zs[rr * kLK + c] * zd[rr] / (rn * rn * rn);
+                    ds[rr * kLK + c] = dz * silu_grad(y);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    // ---- back through the conv: thread (c, rh) takes rows 32 rh .. 32 rh + 31
+    float *gx = (P.kind == 0 ? p.grad_q : P.kind == 1 ? p.grad_k : p.grad_v) + (long)P.head * kD;
+    const int rb = 32 * rh, tb = j * kChunk + rb;
     float dw[kWin], xw[kWin];
 #pragma unroll
-    for (int i = 0; i < kWin; ++i) dw[i] = dy[(long)min(tb + i, L - 1) * C_tot];
-#pragma unroll
-    for (int i = 0; i < kWin; ++i) dw[i] = tb + i < L ? dw[i] : 0.f;
+    for (int i = 0; i < kWin; ++i) dw[i] = rb + i < m ? ds[(rb + i) * kLK + c] : 0.f;  // zero past the sequence
     x_window(p, P, x, s, seq0, tb, L, c, C_tot, xw);
     float gw[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1590,7 +1619,7 @@ __global__ __launch_bounds__(1024) void bwd_setup_kernel(BwdArgs p, BwdWs ws)
 }
 
 // Workspace carve-up: sizes in floats, each region 64-byte aligned
-constexpr int kBwdRegions = 21;  // two int4 tables and the nineteen float regions of BwdWs
+constexpr int kBwdRegions = 20;  // two int4 tables and the eighteen float regions of BwdWs
 struct BwdLayout {
     long off[kBwdRegions];
     long total;
@@ -1603,7 +1632,7 @@ BwdLayout bwd_layout(int N, int T_tot, int max_chunks, int Hqk, int Hv)
                             tok * Hqk * kD, tok * Hqk * kD, tok * Hv * kD, tok * Hv, tok * Hv,
                             chunks * Hv * 4096, chunks * Hv * 4096, chunks * Hv * kD * kD, chunks * Hv * kD * kD,
                             tok * Hv * kD, tok * Hv * kD, tok * Hv * kD, tok * Hv * kD, tok * Hv * kD,
-                            tok * Hv * kD, tok * C_tot, chunks * C_tot * 4, chunks * Hv * kSD, chunks * Hqk * 4096};
+                            tok * Hv * kD, chunks * C_tot * 4, chunks * Hv * kSD, chunks * Hqk * 4096};
     BwdLayout L{};
     long o = 0;
     for (int i = 0; i < kBwdRegions; ++i) {
@@ -1685,7 +1714,7 @@ hipError_t launch_backward(const uint16_t *q, const uint16_t *k, const uint16_t 
         ws.chunk_info = reinterpret_cast<int4 *>(base + L.off[0]);
         ws.seq_info = reinterpret_cast<int4 *>(base + L.off[1]);
         float **slots[kBwdRegions - 2] = {&ws.qh, &ws.kh, &ws.vh, &ws.gam, &ws.beta, &ws.X, &ws.P, &ws.Sc, &ws.dSc,
-                             &ws.vt, &ws.vn, &ws.dvn, &ws.dvh, &ws.dqp, &ws.dkp, &ws.dy, &ws.dwp, &ws.sdot, &ws.KK};
+                             &ws.vt, &ws.vn, &ws.dvn, &ws.dvh, &ws.dqp, &ws.dkp, &ws.dwp, &ws.sdot, &ws.KK};
         for (int i = 0; i < kBwdRegions - 2; ++i) *slots[i] = base + L.off[i + 2];
     } else {
         p.cu_seqlens = nullptr;  // nothing to tabulate: every sequence is empty
@@ -1710,8 +1739,7 @@ hipError_t launch_backward(const uint16_t *q, const uint16_t *k, const uint16_t 
     const long nw = C_tot * 4;
     if (chunks > 0) {
         hipLaunchKernelGGL(bwd_grad_kernel, dim3(chunks * Hv), dim3(kBT), 0, stream, p, ws);
-        hipLaunchKernelGGL(bwd_dy_kernel, dim3(chunks, planes), dim3(kBT), 0, stream, p, ws);
-        hipLaunchKernelGGL(bwd_conv_kernel, dim3(chunks, planes), dim3(kBT), 0, stream, p, ws);
+        hipLaunchKernelGGL(bwd_dyconv_kernel, dim3(chunks, planes), dim3(kBT), 0, stream, p, ws);
         hipLaunchKernelGGL(bwd_dw_kernel, dim3((nw + kBT - 1) / kBT), dim3(kBT), 0, stream, p, ws, nw, chunks);
     } else {
         hipLaunchKernelGGL(bwd_fill_kernel, dim3((nw + kBT - 1) / kBT), dim3(kBT), 0, stream, grad_conv_w, nw);
