@@ -290,7 +290,7 @@ TRAFFIC_KERNELS = {"prefill_chain": "chain_kernel", "prefill_prep": "prep_kernel
                    "decode_conv_shift": "conv_shift_qk_kernel<1>",
                    "decode_multi": "decode_tokens_kernel<4>", "decode_multi_conv_shift": "conv_shift_qk_kernel<4>"}
 BWD_KERNELS = ("bwd_prep_kernel", "bwd_local_kernel", "bwd_fwd_kernel", "bwd_chain_kernel", "bwd_grad_kernel",
-               "bwd_dy_kernel", "bwd_conv_kernel", "bwd_dw_kernel")
+               "bwd_dyconv_kernel", "bwd_dw_kernel")
 TRAFFIC_KERNELS.update({"backward_" + k_[4:-7]: k_ for k_ in BWD_KERNELS})
 
 
@@ -677,7 +677,7 @@ def bench_backward(hip, settle_ms, steps=10, warmup=3):
     tf = flop / (ms * 1e-3) / 1e12
     return {"metric": "training backward tokens/s (B=1, T=8192, 16QK/48V; all gradients, fp32)",
             "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms, "steps": steps,
-            "roofline": {"bound": "alu", "kernel": "whole backward (eight launches)", "achieved": tf,
+            "roofline": {"bound": "alu", "kernel": "whole backward (seven launches)", "achieved": tf,
                          "peak": PEAK_VALU_F32 / 1e12, "unit": "TFLOP/s", "frac": tf * 1e12 / PEAK_VALU_F32,
                          "traffic": None, "algorithmic_flop_per_call": flop}}
 
@@ -685,7 +685,7 @@ def bench_backward(hip, settle_ms, steps=10, warmup=3):
 def bench_backward_windows(hip):
     """The backward in a workspace short of the one-pass size: T = 8192 in
     512 MiB (the cost of the windows at the same length) and the native-context
-    length T = 262,144 (one pass: ~94 GB) in 3 GiB."""
+    length T = 262,144 (one pass: ~83 GB) in 3 GiB."""
     import numpy as np
     import torch
     from linear_attention_sequence_gdn_amd import inputs

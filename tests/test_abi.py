@@ -199,9 +199,9 @@ def test_backward_window_plan(L):
         tw = gdn.gdn_prefill_backward_windows(1, 8192, 16, 48, int(frac * need))
         assert tw >= prev and tw % 64 == 0
         prev = tw
-    # the native-context sequence: 262,144 tokens in about 3 GiB instead of the one-pass ~87 GiB
+    # the native-context sequence: 262,144 tokens in 3 GiB instead of the one-pass ~78 GiB
     one_pass = gdn.gdn_prefill_backward_workspace_size(1, 262144, 16, 48)
-    assert one_pass > 80 * 2**30
+    assert one_pass > 70 * 2**30
     assert gdn.gdn_prefill_backward_windows(1, 262144, 16, 48, 3 * 2**30) >= 4096
     # a batch whose sequences fit one at a time runs them whole
     one = gdn.gdn_prefill_backward_workspace_size(1, 200, 2, 6)
