@@ -86,6 +86,8 @@ struct BwdArgs {
     int nseg;                   // workgroups (segments) per sequence in the two sequential passes
     float *state_final;         // optional [N][Hv][128][128]: the state after each sequence's last
                                 // chunk, from the recomputed forward (NULL: not written)
+    bool forward_only;          // the recomputed forward for state_final alone: it stores no
+                                // per-chunk state, Vt or Vn
 };
 
 // Workspace (fp32).  tok = s*T + t; rows of a chunk beyond its length are
@@ -748,7 +750,7 @@ __global__ __launch_bounds__(kST) void bwd_fwd_kernel(BwdArgs p, BwdWs ws)
     for (int j = pl.j0; j < pl.hi; ++j) {
         const int cidx = sq.x + j, n = min(kChunk, sq.w - j * kChunk);
         const long t0 = (long)sq.z + (long)j * kChunk;
-        const bool own = j >= pl.lo;  // else a warm-up chunk: nothing stored
+        const bool own = j >= pl.lo && !p.forward_only;  // else a warm-up chunk: nothing stored
         float *sc = ws.Sc + ((long)cidx * Hv + h) * kD * kD + col0;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
@@ -1698,6 +1700,7 @@ hipError_t launch_backward(const uint16_t *q, const uint16_t *k, const uint16_t 
 {
     BwdArgs p{};
     p.state_final = state_final;
+    p.forward_only = forward_only;
     p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.conv_w = conv_w; p.conv_state_in = conv_state_in;
     p.state_in = state_in; p.grad_o = grad_o; p.grad_state_out = grad_state_out;
     p.grad_q = grad_q; p.grad_k = grad_k; p.grad_v = grad_v; p.grad_a = grad_a; p.grad_b = grad_b;
