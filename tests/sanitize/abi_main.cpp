@@ -49,6 +49,31 @@ int main()
     EXPECT((int)gdn_prefill_workspace_size(1, 64, 16, 48, 64, 128), 0);
     EXPECT((int)gdn_prefill_workspace_size(-1, 64, 16, 48, 128, 128), 0);
 
+    // the backward's window plan (host-only): a sweep of workspace sizes from
+    // nothing to the one-pass size, including the native-context length whose
+    // plan search walks thousands of window counts
+    {
+        const int wTs[] = {1, 64, 333, 8192, 262144};
+        for (int T : wTs)
+            for (auto &h : Hs) {
+                if (h[1] % h[0]) continue;
+                const size_t one = gdn_prefill_backward_workspace_size(1, T, h[0], h[1], 128, 128);
+                for (int k = 0; k <= 16; ++k) {
+                    int tw = -1;
+                    const int rc = gdn_prefill_backward_windows(1, T, h[0], h[1], 128, 128, one / 16 * k, &tw);
+                    if (rc == GDN_OK && (tw <= 0 || tw > T || (tw < T && tw % 64))) ++failures;
+                    if (rc != GDN_OK && rc != GDN_ERR_WORKSPACE_TOO_SMALL) ++failures;
+                }
+                int tw = -1;
+                EXPECT(gdn_prefill_backward_windows(2, T, h[0], h[1], 128, 128, 2 * one, &tw), GDN_OK);
+                if (tw != T) ++failures;
+            }
+        int tw = 0;
+        EXPECT(gdn_prefill_backward_windows(1, 64, 2, 6, 128, 128, 1 << 30, nullptr), GDN_ERR_INVALID_ARGUMENT);
+        EXPECT(gdn_prefill_backward_windows(1, 64, 3, 7, 128, 128, 1 << 30, &tw), GDN_ERR_UNSUPPORTED);
+        EXPECT(gdn_prefill_backward_windows(-1, 64, 2, 6, 128, 128, 1 << 30, &tw), GDN_ERR_INVALID_ARGUMENT);
+    }
+
     // the carved regions lie inside the workspace and do not overlap: each is
     // written in full inside an allocation of exactly the queried size
     const int carve[][4] = {{1, 1, 1, 1}, {3, 2, 2, 6}, {130, 4, 2, 8}, {129, 1, 16, 48}};
