@@ -1535,8 +1535,17 @@ __global__ __launch_bounds__(kBT) void bwd_dw_kernel(BwdArgs p, BwdWs ws, long n
 {
     const long e = (long)blockIdx.x * kBT + threadIdx.x;
     if (e >= n_elems) return;
+    // sixteen chunks' loads in flight at a time, added in chunk order
     float acc = 0.f;
-    for (int c = 0; c < n_chunks; ++c) acc += ws.dwp[(long)c * n_elems + e];
+    int c = 0;
+    for (; c + 16 <= n_chunks; c += 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = ws.dwp[(long)(c + u) * n_elems + e];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc += v[u];
+    }
+    for (; c < n_chunks; ++c) acc += ws.dwp[(long)c * n_elems + e];
     p.grad_conv_w[e] = acc;
 }
 
