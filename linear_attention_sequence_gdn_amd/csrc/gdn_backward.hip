@@ -1270,8 +1270,14 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
     __syncthreads();
     if (t < n) {
+        // column t below the diagonal, rows t .. n-1 in order (a fixed-count
+        // loop, so that its reads go out together; rows outside add nothing)
         float cs = 0.f;
-        for (int r = t; r < n; ++r) cs += Ym[r * kLN + t];
+#pragma unroll 16
+        for (int r = 0; r < 64; ++r) {
+            const float y = Ym[r * kLN + t];
+            cs = r >= t && r < n ? cs + y : cs;
+        }
         dbet[t] += cs;
     }
     __syncthreads();
@@ -1339,8 +1345,12 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     __syncthreads();
     if (t < n) {
-        float dg = 0.f;
-        for (int r = n - 1; r >= t; --r) dg += dgam[r];
+        float dg = 0.f;  // rows n-1 down to t, in that order
+#pragma unroll 16
+        for (int r = 63; r >= 0; --r) {
+            const float v = dgam[r];
+            dg = r >= t && r < n ? dg + v : dg;
+        }
         const long ti = (t0 + t) * Hv + h;
         p.grad_a[ti] = dg * (-p.gate_scale * sigm(p.a[ti]));
         p.grad_b[ti] = dbet[t] * bet[t] * (1.f - bet[t]);
